@@ -1,0 +1,175 @@
+"""fp64 CPU oracle for the causal long convolution -- TEST INFRASTRUCTURE ONLY.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
+``bench.py`` may import this package.  The GPU library never loads it, and it
+shares no code with the GPU library.
+
+It wraps ``oracle.c`` (plain C, fp64, OpenMP over rows), which computes
+(page "FlashFFTConv: Efficient Convolutions for Long Sequences with Tensor
+Cores", section 3.4):
+
+* ``conv_direct``  -- the causal convolution by its definition,
+  ``y[r, t] = sum_{s<=t} u[r, s] * k[h(r), t - s]``;
+* ``conv_fft``     -- the same through the convolution theorem with both
+  sequences zero-padded to 2N (iterative radix-2 FFT, no packing tricks);
+* ``conv_points``  -- single outputs by the definition (for sampled checks);
+* ``fft``          -- the radix-2 DFT itself, exposed for the oracle's pins.
+
+Inputs are the exact values stored in the I/O dtype (bf16 bit patterns are
+widened exactly); everything is evaluated in fp64.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+
+def build(force: bool = False) -> str:
+    """Compile oracle.c into liboracle.so with gcc (-O2 -fopenmp)."""
+    if (not force and os.path.exists(_LIB_PATH)
+            and os.path.getmtime(_LIB_PATH) >= os.path.getmtime(_SRC)):
+        return _LIB_PATH
+    tmp = _LIB_PATH + ".tmp%d" % os.getpid()
+    cmd = ["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c11",
+           "-Wall", "-o", tmp, _SRC, "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        build()
+        lib = ctypes.CDLL(_LIB_PATH)
+        d = ctypes.POINTER(ctypes.c_double)
+        lp = ctypes.POINTER(ctypes.c_long)
+        L = ctypes.c_long
+        lib.oracle_num_threads.restype = ctypes.c_int
+        lib.oracle_conv_direct.argtypes = [d, d, lp, d, L, L]
+        lib.oracle_conv_direct.restype = None
+        lib.oracle_conv_points.argtypes = [d, d, lp, L, lp, lp, L, d]
+        lib.oracle_conv_points.restype = None
+        lib.oracle_fft.argtypes = [d, d, L, ctypes.c_int]
+        lib.oracle_fft.restype = None
+        lib.oracle_kernel_spectrum.argtypes = [d, L, L, d, d]
+        lib.oracle_kernel_spectrum.restype = None
+        lib.oracle_conv_fft.argtypes = [d, d, lp, d, L, L, L]
+        lib.oracle_conv_fft.restype = ctypes.c_int
+        _lib = lib
+    return _lib
+
+
+def num_threads() -> int:
+    """Threads the oracle's OpenMP loops use."""
+    return int(_load().oracle_num_threads())
+
+
+def _dp(a):
+    return a.ctypes.data_as(ctypes.POINTER(ctypes.c_double))
+
+
+def _lp(a):
+    return a.ctypes.data_as(ctypes.POINTER(ctypes.c_long))
+
+
+def to_f64(a: np.ndarray, dtype: str) -> np.ndarray:
+    """Exact fp64 value of stored data.  ``dtype`` is 'f32', 'f16' or 'bf16'
+    (bf16 is carried as uint16 bit patterns)."""
+    if dtype == "bf16":
+        bits = np.asarray(a, dtype=np.uint16).astype(np.uint32) << 16
+        return bits.view(np.float32).astype(np.float64)
+    return np.asarray(a).astype(np.float64)
+
+
+def _rows(u, k, hidx):
+    u = np.ascontiguousarray(u, dtype=np.float64)
+    k = np.ascontiguousarray(k, dtype=np.float64)
+    R, N = u.shape
+    if k.ndim != 2 or k.shape[1] != N:
+        raise ValueError("kernel rows must have the same length as u rows")
+    if hidx is None:
+        hidx = np.arange(R) % k.shape[0]
+    hidx = np.ascontiguousarray(hidx, dtype=np.int64)
+    if hidx.shape != (R,) or (R and (hidx.min() < 0 or hidx.max() >= k.shape[0])):
+        raise ValueError("bad kernel row index")
+    return u, k, hidx, R, N
+
+
+def conv_direct(u, k, hidx=None) -> np.ndarray:
+    """y[r, t] = sum_{s<=t} u[r, s] k[hidx[r], t-s]  (fp64, O(N^2) per row).
+    ``u``: [R, N]; ``k``: [Hk, N]; default ``hidx[r] = r % Hk`` (the
+    [B][H][N] row order)."""
+    u, k, hidx, R, N = _rows(u, k, hidx)
+    y = np.empty((R, N), dtype=np.float64)
+    _load().oracle_conv_direct(_dp(u), _dp(k), _lp(hidx), _dp(y), R, N)
+    return y
+
+
+def conv_fft(u, k, hidx=None) -> np.ndarray:
+    """Same result via zero-padded (2N) radix-2 FFT convolution (fp64)."""
+    u, k, hidx, R, N = _rows(u, k, hidx)
+    if N & (N - 1):
+        raise ValueError("conv_fft needs a power-of-two N")
+    y = np.empty((R, N), dtype=np.float64)
+    rc = _load().oracle_conv_fft(_dp(u), _dp(k), _lp(hidx), _dp(y), R,
+                                 k.shape[0], N)
+    if rc != 0:
+        raise MemoryError("oracle_conv_fft: allocation failed")
+    return y
+
+
+def conv_points(u, k, rows, ts, hidx=None) -> np.ndarray:
+    """out[i] = y[rows[i], ts[i]] by the definition."""
+    u, k, hidx, R, N = _rows(u, k, hidx)
+    rows = np.ascontiguousarray(rows, dtype=np.int64)
+    ts = np.ascontiguousarray(ts, dtype=np.int64)
+    if rows.shape != ts.shape or rows.ndim != 1:
+        raise ValueError("rows and ts must be 1-D of equal length")
+    if len(rows) and (rows.min() < 0 or rows.max() >= R or ts.min() < 0
+                      or ts.max() >= N):
+        raise ValueError("sample index out of range")
+    out = np.empty(len(rows), dtype=np.float64)
+    _load().oracle_conv_points(_dp(u), _dp(k), _lp(hidx), N, _lp(rows),
+                               _lp(ts), len(rows), _dp(out))
+    return out
+
+
+def fft(x, inverse: bool = False) -> np.ndarray:
+    """Radix-2 DFT of a complex vector (power-of-two length).
+    forward: X[k] = sum_j x[j] e^{-2 pi i jk/n}; inverse includes 1/n."""
+    x = np.asarray(x, dtype=np.complex128)
+    n = x.shape[0]
+    if n < 1 or n & (n - 1):
+        raise ValueError("fft needs a power-of-two length")
+    re = np.ascontiguousarray(x.real, dtype=np.float64).copy()
+    im = np.ascontiguousarray(x.imag, dtype=np.float64).copy()
+    _load().oracle_fft(_dp(re), _dp(im), n, 1 if inverse else 0)
+    return re + 1j * im
+
+
+def kernel_spectrum(k) -> np.ndarray:
+    """FFT_2N of each zero-padded kernel row: [Hk, 2N] complex."""
+    k = np.ascontiguousarray(k, dtype=np.float64)
+    Hk, N = k.shape
+    kre = np.empty((Hk, 2 * N))
+    kim = np.empty((Hk, 2 * N))
+    _load().oracle_kernel_spectrum(_dp(k), Hk, N, _dp(kre), _dp(kim))
+    return kre + 1j * kim
+
+
+def rel_l2(y, y_ref) -> float:
+    """||y - y_ref||_2 / ||y_ref||_2 in fp64."""
+    y = np.asarray(y, dtype=np.float64)
+    y_ref = np.asarray(y_ref, dtype=np.float64)
+    num = float(np.sum((y - y_ref) ** 2))
+    den = float(np.sum(y_ref ** 2))
+    return (num / den) ** 0.5 if den > 0 else (0.0 if num == 0 else float("inf"))

@@ -1,0 +1,207 @@
+/*
+ * oracle.c -- plain fp64 CPU reference for the causal long convolution.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the product path may link, load or
+ * call this file; only the tests, the smoke check and the benchmark's CPU
+ * baseline leg use it.  It shares no code, header, table or constant with
+ * the GPU library.
+ *
+ * What it computes (page "FlashFFTConv: Efficient Convolutions for Long
+ * Sequences with Tensor Cores", section 3.4, "The FFT Convolution and Its
+ * Hardware Mismatch"):
+ *
+ *   convolution definition:  (u * k)[i] = sum_j u[j] k[i - j]
+ *   causal form used here:   y[b,h,t] = sum_{s=0..t} u[b,h,s] k[h,t-s],
+ *                            t in [0, N)   (kernel as long as the input)
+ *
+ * and, as an independent second route, the convolution theorem of the same
+ * section (u * k = F^-1(Fu . Fk)) with both sequences zero-padded to 2N so
+ * the circular result has no wrap-around, truncated back to N.  The FFT is
+ * the textbook iterative radix-2 Cooley-Tukey transform (bit reversal, then
+ * log2(L) butterfly stages).  Twiddles are taken from libm cos/sin of
+ * 2*pi*j/len for every index (no recurrence).  There is no real-to-complex
+ * packing and no matrix (Monarch) factoring here: this file deliberately
+ * computes the plain definitions so it can be checked by eye.
+ *
+ * All arithmetic is fp64.  Rows are independent; OpenMP splits them.
+ */
+#include <math.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+#ifndef M_PI
+#define M_PI 3.14159265358979323846
+#endif
+
+int oracle_num_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
+
+/* Direct causal convolution by the definition.  u and y are [R][N];
+ * kern is [Hk][N]; row r uses kernel row hidx[r].  O(N^2) per row. */
+void oracle_conv_direct(const double *u, const double *kern, const long *hidx,
+                        double *y, long R, long N)
+{
+    long r;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (r = 0; r < R; ++r) {
+        const double *ur = u + r * N;
+        const double *kr = kern + hidx[r] * N;
+        double *yr = y + r * N;
+        for (long t = 0; t < N; ++t) {
+            double acc = 0.0;
+            for (long s = 0; s <= t; ++s)
+                acc += ur[s] * kr[t - s];
+            yr[t] = acc;
+        }
+    }
+}
+
+/* Selected outputs by the definition: out[i] = y[rows[i], ts[i]]. */
+void oracle_conv_points(const double *u, const double *kern, const long *hidx,
+                        long N, const long *rows, const long *ts, long count,
+                        double *out)
+{
+    long i;
+#pragma omp parallel for schedule(dynamic, 16)
+    for (i = 0; i < count; ++i) {
+        const double *ur = u + rows[i] * N;
+        const double *kr = kern + hidx[rows[i]] * N;
+        long t = ts[i];
+        double acc = 0.0;
+        for (long s = 0; s <= t; ++s)
+            acc += ur[s] * kr[t - s];
+        out[i] = acc;
+    }
+}
+
+/* In-place iterative radix-2 DFT of length n (a power of two).
+ * sign = -1: X[k] = sum_j x[j] exp(-2 pi i jk/n)   (forward, unnormalised)
+ * sign = +1: x[j] = sum_k X[k] exp(+2 pi i jk/n)   (no 1/n here)          */
+static void fft_radix2(double *re, double *im, long n, int sign)
+{
+    /* bit-reversal permutation */
+    long j = 0;
+    for (long i = 1; i < n; ++i) {
+        long bit = n >> 1;
+        while (j & bit) {
+            j ^= bit;
+            bit >>= 1;
+        }
+        j ^= bit;
+        if (i < j) {
+            double t = re[i]; re[i] = re[j]; re[j] = t;
+            t = im[i]; im[i] = im[j]; im[j] = t;
+        }
+    }
+    /* butterfly stages */
+    for (long len = 2; len <= n; len <<= 1) {
+        long half = len >> 1;
+        for (long q = 0; q < half; ++q) {
+            double ang = sign * 2.0 * M_PI * (double)q / (double)len;
+            double wr = cos(ang), wi = sin(ang);
+            for (long b = 0; b < n; b += len) {
+                long p0 = b + q, p1 = b + q + half;
+                double xr = re[p1] * wr - im[p1] * wi;
+                double xi = re[p1] * wi + im[p1] * wr;
+                re[p1] = re[p0] - xr;
+                im[p1] = im[p0] - xi;
+                re[p0] += xr;
+                im[p0] += xi;
+            }
+        }
+    }
+}
+
+/* Exposed for the oracle's own pins.  inverse != 0 applies sign +1 and
+ * the 1/n normalisation, so oracle_fft(oracle_fft(x), inverse) == x. */
+void oracle_fft(double *re, double *im, long n, int inverse)
+{
+    fft_radix2(re, im, n, inverse ? +1 : -1);
+    if (inverse) {
+        double s = 1.0 / (double)n;
+        for (long i = 0; i < n; ++i) {
+            re[i] *= s;
+            im[i] *= s;
+        }
+    }
+}
+
+/* Spectrum of the zero-padded kernel rows: kre/kim are [Hk][2N]. */
+void oracle_kernel_spectrum(const double *kern, long Hk, long N,
+                            double *kre, double *kim)
+{
+    long L = 2 * N, h;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (h = 0; h < Hk; ++h) {
+        double *re = kre + h * L, *im = kim + h * L;
+        for (long t = 0; t < L; ++t) {
+            re[t] = t < N ? kern[h * N + t] : 0.0;
+            im[t] = 0.0;
+        }
+        fft_radix2(re, im, L, -1);
+    }
+}
+
+/* Causal convolution through the convolution theorem with 2N zero padding:
+ *   U = FFT_2N(pad(u)),  K = FFT_2N(pad(k)),  y = IFFT_2N(U.K)[0:N] (real).
+ * u, y: [R][N]; kern: [Hk][N]; row r uses kernel row hidx[r].
+ * The kernel spectra are computed once per call (Hk of them). */
+int oracle_conv_fft(const double *u, const double *kern, const long *hidx,
+                    double *y, long R, long Hk, long N)
+{
+    long L = 2 * N;
+    double *kre = (double *)malloc(sizeof(double) * (size_t)(Hk * L));
+    double *kim = (double *)malloc(sizeof(double) * (size_t)(Hk * L));
+    if (!kre || !kim) {
+        free(kre);
+        free(kim);
+        return -1;
+    }
+    oracle_kernel_spectrum(kern, Hk, N, kre, kim);
+    int fail = 0;
+#pragma omp parallel
+    {
+        double *re = (double *)malloc(sizeof(double) * (size_t)L);
+        double *im = (double *)malloc(sizeof(double) * (size_t)L);
+        if (!re || !im) {
+#pragma omp atomic write
+            fail = 1;
+        } else {
+            long r;
+#pragma omp for schedule(dynamic, 1)
+            for (r = 0; r < R; ++r) {
+                const double *ur = u + r * N;
+                const double *Kr = kre + hidx[r] * L, *Ki = kim + hidx[r] * L;
+                for (long t = 0; t < L; ++t) {
+                    re[t] = t < N ? ur[t] : 0.0;
+                    im[t] = 0.0;
+                }
+                fft_radix2(re, im, L, -1);
+                for (long f = 0; f < L; ++f) {
+                    double a = re[f], b = im[f];
+                    re[f] = a * Kr[f] - b * Ki[f];
+                    im[f] = a * Ki[f] + b * Kr[f];
+                }
+                fft_radix2(re, im, L, +1);
+                double s = 1.0 / (double)L;
+                double *yr = y + r * N;
+                for (long t = 0; t < N; ++t)
+                    yr[t] = re[t] * s;
+            }
+        }
+        free(re);
+        free(im);
+    }
+    free(kre);
+    free(kim);
+    return fail ? -1 : 0;
+}

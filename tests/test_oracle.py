@@ -1,0 +1,297 @@
+"""Pins for the fp64 CPU oracle (no GPU).
+
+The oracle is checked against things it does not compute itself: values
+worked by hand (tests/golden), closed forms, identities of the convolution
+and of the DFT, brute force on tiny inputs, and numpy's independent FFT.
+Each check is chosen so that a plausible slip in the oracle (a dropped term,
+a wrong sign or index, a reversed kernel, a missing normalisation, wrap-around
+from too little padding) fails at least one of them.
+"""
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+from tests.conftest import golden_path
+
+
+def _read_cases(name):
+    cases, cur = [], {}
+    with open(golden_path(name)) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            if line.startswith("case"):
+                if cur:
+                    cases.append(cur)
+                cur = {}
+                continue
+            key, vals = line.split(":", 1)
+            cur[key.strip()] = vals.split()
+    if cur:
+        cases.append(cur)
+    return cases
+
+
+# ---------------------------------------------------------------- golden
+
+def test_golden_hand_worked_convolutions():
+    for case in _read_cases("causal_conv_hand.txt"):
+        u = np.array([float(v) for v in case["u"]])[None, :]
+        k = np.array([float(v) for v in case["k"]])[None, :]
+        y = np.array([float(v) for v in case["y"]])
+        np.testing.assert_array_equal(oracle.conv_direct(u, k)[0], y)
+        n = u.shape[1]
+        if n & (n - 1) == 0:
+            np.testing.assert_allclose(oracle.conv_fft(u, k)[0], y,
+                                       atol=1e-12)
+
+
+def test_golden_hand_worked_dft():
+    case = _read_cases("dft_hand.txt")[0]
+    x = np.array([float(v) for v in case["x"]])
+    X = np.array([complex(*map(float, p.split(","))) for p in case["X"]])
+    np.testing.assert_allclose(oracle.fft(x), X, atol=1e-12)
+    np.testing.assert_allclose(oracle.fft(X, inverse=True), x, atol=1e-12)
+
+
+# ----------------------------------------------------------- brute force
+
+def _brute(u, k):
+    # direct double loop over all (t, s) pairs with the causal mask written
+    # as an explicit index test (a different loop shape from the oracle's)
+    n = len(u)
+    y = [0.0] * n
+    for s in range(n):
+        for j in range(n):
+            if s + j < n:
+                y[s + j] += u[s] * k[j]
+    return y
+
+
+@pytest.mark.parametrize("n", [1, 2, 3, 5, 8])
+def test_brute_force_tiny(n):
+    rng = np.random.default_rng(n)
+    u = rng.standard_normal((3, n))
+    k = rng.standard_normal((2, n))
+    hidx = np.array([1, 0, 1])
+    yd = oracle.conv_direct(u, k, hidx)
+    for r in range(3):
+        np.testing.assert_allclose(yd[r], _brute(u[r], k[hidx[r]]),
+                                   rtol=0, atol=1e-13)
+    if n & (n - 1) == 0:
+        np.testing.assert_allclose(oracle.conv_fft(u, k, hidx), yd,
+                                   rtol=0, atol=1e-12)
+
+
+def test_exhaustive_delta_basis_small():
+    # every (input delta, kernel delta) pair for N <= 16: y = delta at s + d
+    for n in (2, 4, 8, 16):
+        eye = np.eye(n)
+        for s in range(n):
+            u = np.repeat(eye[s][None, :], n, axis=0)
+            y_fft = oracle.conv_fft(u, eye, np.arange(n))
+            y_dir = oracle.conv_direct(u, eye, np.arange(n))
+            for d in range(n):
+                want = np.zeros(n)
+                if s + d < n:
+                    want[s + d] = 1.0
+                np.testing.assert_allclose(y_fft[d], want, atol=1e-12)
+                np.testing.assert_array_equal(y_dir[d], want)
+
+
+# --------------------------------------------------------------- identities
+
+@pytest.mark.parametrize("n", [256, 1024])
+def test_delta_identities(n):
+    rng = np.random.default_rng(7)
+    u = rng.standard_normal((2, n))
+    kd = np.zeros((3, n))
+    kd[0, 0] = 1.0                    # identity
+    kd[1, 5] = 1.0                    # delay by 5
+    kd[2, n - 1] = 1.0                # delay by n-1
+    for conv in (oracle.conv_direct, oracle.conv_fft):
+        y0 = conv(u, kd, [0, 0])
+        np.testing.assert_allclose(y0, u, atol=1e-12)
+        y5 = conv(u, kd, [1, 1])
+        want = np.zeros_like(u)
+        want[:, 5:] = u[:, :-5]
+        np.testing.assert_allclose(y5, want, atol=1e-12)
+        yl = conv(u, kd, [2, 2])
+        want = np.zeros_like(u)
+        want[:, n - 1] = u[:, 0]
+        np.testing.assert_allclose(yl, want, atol=1e-12)
+        # a delta input reproduces the kernel
+        ud = np.zeros((1, n))
+        ud[0, 0] = 1.0
+        kk = rng.standard_normal((1, n))
+        np.testing.assert_allclose(conv(ud, kk), kk, atol=1e-12)
+
+
+def test_closed_form_geometric_kernel():
+    # k[t] = r^t, u = 1  =>  y[t] = (1 - r^(t+1)) / (1 - r)
+    n, r = 1024, 0.99
+    t = np.arange(n)
+    k = (r ** t)[None, :]
+    u = np.ones((1, n))
+    want = (1 - r ** (t + 1)) / (1 - r)
+    for conv in (oracle.conv_direct, oracle.conv_fft):
+        np.testing.assert_allclose(conv(u, k)[0], want, rtol=1e-12)
+
+
+def test_closed_form_ramp():
+    # u = 1, k = 1  =>  y[t] = t + 1 (counts the causal window)
+    n = 512
+    y = oracle.conv_fft(np.ones((1, n)), np.ones((1, n)))[0]
+    np.testing.assert_allclose(y, np.arange(1, n + 1), rtol=1e-12)
+
+
+def test_linearity():
+    rng = np.random.default_rng(3)
+    n = 512
+    u1, u2 = rng.standard_normal((2, 1, n))
+    k1, k2 = rng.standard_normal((2, 1, n))
+    a, b = 1.75, -0.3
+    for conv in (oracle.conv_direct, oracle.conv_fft):
+        lhs = conv(a * u1 + b * u2, k1)
+        rhs = a * conv(u1, k1) + b * conv(u2, k1)
+        np.testing.assert_allclose(lhs, rhs, atol=1e-10)
+        lhs = conv(u1, a * k1 + b * k2)
+        rhs = a * conv(u1, k1) + b * conv(u1, k2)
+        np.testing.assert_allclose(lhs, rhs, atol=1e-10)
+
+
+def test_causality():
+    # changing u[s] may only change y[t] for t >= s; with padding to 2N the
+    # FFT route must not wrap the late inputs around onto early outputs
+    rng = np.random.default_rng(11)
+    n = 1024
+    u = rng.standard_normal((1, n))
+    k = rng.standard_normal((1, n))
+    base = oracle.conv_fft(u, k)
+    for s in (0, 1, 300, n - 1):
+        u2 = u.copy()
+        u2[0, s] += 10.0
+        y2 = oracle.conv_fft(u2, k)
+        np.testing.assert_allclose(y2[0, :s], base[0, :s], atol=1e-10)
+        assert np.abs(y2[0, s:] - base[0, s:]).max() > 1.0
+
+
+def test_commutes_in_u_and_k():
+    rng = np.random.default_rng(12)
+    n = 256
+    u = rng.standard_normal((1, n))
+    k = rng.standard_normal((1, n))
+    np.testing.assert_allclose(oracle.conv_fft(u, k), oracle.conv_fft(k, u),
+                               atol=1e-11)
+
+
+# ---------------------------------------------------------------- the DFT
+
+def _naive_dft(x):
+    n = len(x)
+    out = []
+    for kk in range(n):
+        acc = 0j
+        for j in range(n):
+            ang = -2.0 * math.pi * j * kk / n
+            acc += x[j] * complex(math.cos(ang), math.sin(ang))
+        out.append(acc)
+    return np.array(out)
+
+
+@pytest.mark.parametrize("n", [1, 2, 4, 8, 16, 32, 64])
+def test_fft_vs_naive_dft(n):
+    rng = np.random.default_rng(n)
+    x = rng.standard_normal(n) + 1j * rng.standard_normal(n)
+    np.testing.assert_allclose(oracle.fft(x), _naive_dft(list(x)),
+                               atol=1e-11 * max(1, n))
+
+
+def test_fft_round_trip_parseval_hermitian():
+    rng = np.random.default_rng(5)
+    n = 4096
+    x = rng.standard_normal(n)
+    X = oracle.fft(x)
+    np.testing.assert_allclose(oracle.fft(X, inverse=True).real, x,
+                               atol=1e-12)
+    # Parseval: sum |x|^2 = (1/n) sum |X|^2
+    assert abs(np.sum(x ** 2) - np.sum(np.abs(X) ** 2) / n) < 1e-9 * n
+    # Hermitian symmetry of a real input's spectrum
+    np.testing.assert_allclose(X[1:], np.conj(X[1:][::-1]), atol=1e-10)
+
+
+def test_fft_integer_bin_cosine():
+    n, m = 256, 17
+    j = np.arange(n)
+    X = oracle.fft(np.cos(2 * np.pi * m * j / n))
+    want = np.zeros(n, dtype=complex)
+    want[m] = want[n - m] = n / 2
+    np.testing.assert_allclose(X, want, atol=1e-9)
+
+
+def test_fft_matches_numpy():
+    rng = np.random.default_rng(9)
+    for n in (2, 128, 2048, 65536):
+        x = rng.standard_normal(n) + 1j * rng.standard_normal(n)
+        np.testing.assert_allclose(oracle.fft(x), np.fft.fft(x),
+                                   atol=1e-9 * np.sqrt(n))
+
+
+# ------------------------------------------- the two routes agree, and numpy
+
+@pytest.mark.parametrize("n", [2, 4, 16, 64, 256, 1024, 4096])
+def test_fft_route_matches_definition(n):
+    rng = np.random.default_rng(100 + n)
+    u = rng.standard_normal((4, n))
+    k = rng.standard_normal((3, n)) * np.exp(-0.01 * np.arange(n))
+    hidx = np.array([0, 1, 2, 1])
+    yd = oracle.conv_direct(u, k, hidx)
+    yf = oracle.conv_fft(u, k, hidx)
+    assert oracle.rel_l2(yf, yd) < 1e-12
+
+
+def test_fft_route_matches_numpy_rfft():
+    rng = np.random.default_rng(21)
+    n = 8192
+    u = rng.standard_normal((2, n))
+    k = rng.standard_normal((2, n))
+    L = 2 * n
+    want = np.fft.irfft(np.fft.rfft(u, L) * np.fft.rfft(k, L), L)[:, :n]
+    assert oracle.rel_l2(oracle.conv_fft(u, k), want) < 1e-12
+
+
+def test_kernel_spectrum_matches_numpy():
+    rng = np.random.default_rng(22)
+    k = rng.standard_normal((3, 512))
+    want = np.fft.fft(np.concatenate([k, np.zeros_like(k)], axis=1), axis=1)
+    np.testing.assert_allclose(oracle.kernel_spectrum(k), want, atol=1e-9)
+
+
+def test_points_match_full():
+    rng = np.random.default_rng(23)
+    n = 2048
+    u = rng.standard_normal((5, n))
+    k = rng.standard_normal((2, n))
+    hidx = np.array([0, 1, 0, 1, 1])
+    y = oracle.conv_direct(u, k, hidx)
+    rows = np.array([0, 4, 2, 3, 1, 1])
+    ts = np.array([0, n - 1, 1000, 7, 0, 2047])
+    np.testing.assert_array_equal(oracle.conv_points(u, k, rows, ts, hidx),
+                                  y[rows, ts])
+
+
+def test_rel_l2():
+    a = np.array([3.0, 4.0])
+    assert oracle.rel_l2(a, a) == 0.0
+    assert abs(oracle.rel_l2(a * 1.01, a) - 0.01) < 1e-12
+
+
+def test_exact_widening_of_stored_dtypes():
+    bits = np.array([0x3F80, 0xC000, 0x3E20, 0x0001], dtype=np.uint16)
+    np.testing.assert_array_equal(oracle.to_f64(bits, "bf16"),
+                                  [1.0, -2.0, 0.15625, 2.0 ** -133])
+    h = np.array([1.0, 0.5, -65504.0], dtype=np.float16)
+    np.testing.assert_array_equal(oracle.to_f64(h, "f16"), h.astype(float))
