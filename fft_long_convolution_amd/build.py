@@ -1,0 +1,48 @@
+"""Build libfftconv.so (HIP, gfx950) in-tree with hipcc.
+
+Usage: python -m fft_long_convolution_amd.build   (always recompiles)
+"""
+from __future__ import annotations
+
+import os
+import subprocess
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+LIB = os.path.join(HERE, "libfftconv.so")
+SOURCES = [os.path.join(HERE, "csrc", "fftconv_host.cpp"),
+           os.path.join(HERE, "csrc", "fftconv_kernels.hip")]
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+ARCH = os.environ.get("FFTCONV_ARCH", "gfx950")
+
+FLAGS = [
+    "-O3", "-std=c++17", "-fPIC", "-shared",
+    "--offload-arch=" + ARCH,
+    # keep hipcc from emitting packed fp32 VALU ops
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-Wall", "-Wno-unused-function",
+    "-I" + os.path.join(ROOT, "include"),
+]
+
+
+def build(verbose: bool = False) -> str:
+    tmp = LIB + ".tmp%d" % os.getpid()
+    cmd = [HIPCC] + FLAGS + ["-o", tmp] + SOURCES
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    err = "\n".join(l for l in (r.stderr or "").splitlines()
+                    if "packed-fp32-ops" not in l)
+    if r.returncode != 0:
+        raise RuntimeError("hipcc failed:\n" + err)
+    if verbose and err.strip():
+        print(err)
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    build(verbose=True)
+    print("built", LIB)
+    sys.exit(0)

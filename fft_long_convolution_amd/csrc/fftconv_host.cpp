@@ -1,0 +1,633 @@
+// Host side of libfftconv: planning (factorisation, launch shapes), the
+// fp64 construction of every DFT-matrix and twiddle table in the exact lane
+// layout the kernels consume, and the C ABI declared in include/fftconv.h.
+//
+// Method: page "FlashFFTConv: Efficient Convolutions for Long Sequences with
+// Tensor Cores", section 3.4 -- the convolution theorem with causal 2N
+// padding, the real-to-complex packing (one-stage decimation in time), the
+// order-p Monarch factorisation of the DFT, implicit zero padding, and the
+// kernel spectrum computed once per channel.  Plans follow the page's
+// "pre-select p offline per length" (section 3.4, cost-model heuristic) with
+// factors sized for gfx950: 8/16/32-point stages on 16x16 matrix-core
+// tiles, the whole row in one workgroup's LDS up to 16K points, and a
+// three-pass schedule through an fp32 workspace beyond that (the partial
+// fusion of the page's order-4 algorithm).
+#include <math.h>
+#include <stdint.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <complex>
+#include <functional>
+#include <mutex>
+#include <new>
+#include <vector>
+
+#include "../../include/fftconv.h"
+#include "fftconv_internal.h"
+
+using namespace fftconv;
+
+namespace {
+
+constexpr size_t kMinN = 256;
+constexpr size_t kMaxN = 4194304;
+constexpr int kFusedMaxM = 16384;
+
+bool is_pow2(size_t v) { return v && !(v & (v - 1)); }
+int ilog2(size_t v) {
+    int r = 0;
+    while ((size_t(1) << r) < v) ++r;
+    return r;
+}
+
+// ---------------------------------------------------------------- planning
+
+struct Shape {
+    size_t N = 0, M = 0;
+    int p = 0;
+    int f[kMaxStages] = {0};
+    int path = 0;        // 0 fused, 1 multi-pass
+    int n_outer = 0;     // multi-pass: outer factors f[0..n_outer)
+    int Min = 0, Qo = 1; // multi-pass slab length and slab count
+    int ct = 0;          // outer-pass batch columns per tile
+    int thr_fused = 64, thr_outer = 256, thr_inner = 512;
+    int lds_fused = 0, lds_outer = 0, lds_inner = 0;
+    fftconv_dtype dtype = FFTCONV_F32;
+};
+
+// Fused factorisations by log2(M): all but the last may be 8/16/32, the
+// last (the stage fused with the spectrum product) is 16 or 32.
+bool default_fused(int lg, std::vector<int>& out) {
+    switch (lg) {
+    case 8: out = {16, 16}; return true;
+    case 9: out = {32, 16}; return true;
+    case 10: out = {32, 32}; return true;
+    case 11: out = {8, 16, 16}; return true;
+    case 12: out = {16, 16, 16}; return true;
+    case 13: out = {32, 16, 16}; return true;
+    case 14: out = {32, 32, 16}; return true;
+    default: return false;
+    }
+}
+
+// Search for exactly p fused factors (radix exponents 3..5, last 4..5),
+// preferring larger leading factors.
+bool search_factors(int lg, int p, std::vector<int>& out) {
+    if (p < 2 || p > kMaxStages) return false;
+    std::vector<int> e(p, 0);
+    // enumerate exponents in descending-lexicographic order
+    std::function<bool(int, int)> rec = [&](int i, int left) -> bool {
+        if (i == p - 1) {
+            if (left == 4 || left == 5) { e[i] = left; return true; }
+            return false;
+        }
+        for (int x = 5; x >= 3; --x) {
+            if (left - x < 4 + 3 * (p - 2 - i)) continue;
+            e[i] = x;
+            if (rec(i + 1, left - x)) return true;
+        }
+        return false;
+    };
+    if (!rec(0, lg)) return false;
+    out.clear();
+    for (int i = 0; i < p; ++i) out.push_back(1 << e[i]);
+    return true;
+}
+
+fftconv_status make_shape(size_t N, int p, fftconv_dtype dtype, Shape& s) {
+    if (dtype != FFTCONV_F32 && dtype != FFTCONV_F16 && dtype != FFTCONV_BF16)
+        return FFTCONV_ERR_UNSUPPORTED;
+    if (!is_pow2(N) || N < kMinN || N > kMaxN) return FFTCONV_ERR_UNSUPPORTED;
+    if (p < 0 || p == 1 || p > kMaxStages) return FFTCONV_ERR_UNSUPPORTED;
+    s = Shape();
+    s.N = N;
+    s.M = N;
+    s.dtype = dtype;
+    const int lg = ilog2(N);
+    std::vector<int> fac;
+    if (s.M <= (size_t)kFusedMaxM) {
+        s.path = 0;
+        if (!default_fused(lg, fac)) return FFTCONV_ERR_UNSUPPORTED;
+        if (p != 0 && p != (int)fac.size() && !search_factors(lg, p, fac))
+            return FFTCONV_ERR_UNSUPPORTED;
+        // every stage must leave >= 16 columns and the pairing >= 4 blocks
+        for (int x : fac)
+            if ((int)(s.M / x) < 16) return FFTCONV_ERR_UNSUPPORTED;
+        if ((int)(s.M / fac.back()) < 4) return FFTCONV_ERR_UNSUPPORTED;
+        const int waves = s.M <= 1024 ? 1 : (s.M <= 4096 ? 4 : 8);
+        s.thr_fused = 64 * waves;
+        s.lds_fused = (int)(s.M * 8 + waves * 32 * 8);
+    } else {
+        s.path = 1;
+        std::vector<int> outer, inner;
+        if (lg <= 18) {
+            s.Min = 4096;
+            inner = {16, 16, 16};
+        } else {
+            s.Min = 8192;
+            inner = {32, 16, 16};
+        }
+        s.Qo = (int)(s.M / s.Min);
+        switch (ilog2(s.Qo)) {
+        case 3: outer = {8}; break;
+        case 4: outer = {16}; break;
+        case 5: outer = {32}; break;
+        case 6: outer = {8, 8}; break;
+        case 7: outer = {16, 8}; break;
+        case 8: outer = {16, 16}; break;
+        case 9: outer = {32, 16}; break;
+        case 10: outer = {32, 32}; break;
+        default: return FFTCONV_ERR_UNSUPPORTED;
+        }
+        if (p != 0 && p != (int)(outer.size() + inner.size()))
+            return FFTCONV_ERR_UNSUPPORTED;
+        s.n_outer = (int)outer.size();
+        fac = outer;
+        fac.insert(fac.end(), inner.begin(), inner.end());
+        s.ct = s.Qo >= 256 ? 16 : 4096 / s.Qo;
+        if (s.ct > s.Min) s.ct = s.Min;
+        s.thr_outer = 256;
+        s.thr_inner = 512;
+        s.lds_outer = s.Qo * s.ct * 8;
+        s.lds_inner = 2 * s.Min * 8 + (s.thr_inner / 64) * 32 * 8;
+    }
+    s.p = (int)fac.size();
+    for (int i = 0; i < s.p; ++i) s.f[i] = fac[i];
+    return FFTCONV_OK;
+}
+
+size_t kf_entry_bytes(fftconv_dtype dt) { return dt == FFTCONV_F32 ? 16 : 8; }
+
+double mfma_flops_per_row(const Shape& s) {
+    // real flops of the complex DFT-matrix products (8 per complex MAC):
+    // forward stage 1 contracts half its digits, the last inverse stage
+    // produces half its outputs.
+    double f = 0;
+    for (int i = 0; i < s.p; ++i) {
+        const double per = 8.0 * (double)s.M * s.f[i];
+        f += (i == 0) ? per : 2.0 * per;
+    }
+    return f;
+}
+
+void fill_info(const Shape& s, fftconv_plan_info* info) {
+    memset(info, 0, sizeof(*info));
+    info->N = s.N;
+    info->M = s.M;
+    info->order = s.p;
+    for (int i = 0; i < s.p; ++i) info->factors[i] = s.f[i];
+    info->path = s.path;
+    info->outer_factors = s.n_outer;
+    info->dtype = s.dtype;
+    info->spectrum_bytes_per_channel = s.M * kf_entry_bytes(s.dtype);
+    info->workspace_bytes_per_row = s.path ? s.M * 8 : 0;
+    info->mfma_flops_per_row = mfma_flops_per_row(s);
+}
+
+// ------------------------------------------------------- table construction
+
+enum MatKind { MAT_REG, MAT_MID_FWD, MAT_MID_INV };
+
+int mid_perm(int slot, int n) { return slot < n / 2 ? slot : 3 * n / 2 - 1 - slot; }
+
+uint16_t f32_to_f16_bits(float f) {
+    _Float16 h = (_Float16)f;
+    uint16_t b;
+    memcpy(&b, &h, 2);
+    return b;
+}
+
+// A-operand tiles of one stage's real-embedded DFT matrix, [MT][KS][lane]
+// with 8 halves (f16 plans) or 1 float (fp32 plans) per lane.
+// inverse: exponent sign +; half_in: only the first n/2 input digits;
+// half_out: only the first n/2 output digits.
+std::vector<uint8_t> build_matrix(int n, bool inverse, bool half_in,
+                                  bool half_out, MatKind kind, bool f32) {
+    const int nin = half_in ? n / 2 : n;
+    const int nout = half_out ? n / 2 : n;
+    const int KS = f32 ? nin / 2 : (nin <= 16 ? 1 : nin / 16);
+    const int MT = nout / 8 > 0 ? nout / 8 : 1;
+    const int per = f32 ? 1 : 8;
+    const size_t esz = f32 ? 4 : 2;
+    std::vector<uint8_t> out((size_t)MT * KS * 64 * per * esz, 0);
+    const double sgn = inverse ? 1.0 : -1.0;
+    const double scale = 1.0 / sqrt((double)n);
+    for (int mt = 0; mt < MT; ++mt)
+        for (int ks = 0; ks < KS; ++ks)
+            for (int lane = 0; lane < 64; ++lane) {
+                const int g = lane >> 4, x = lane & 15;
+                const int row = 16 * mt + x;
+                const int oslot = row >> 1, c = row & 1;
+                for (int j = 0; j < per; ++j) {
+                    int islot, d;
+                    bool chain = (kind == MAT_MID_INV);
+                    if (!f32) {
+                        if (chain) {
+                            islot = 16 * ks + 8 * (j >> 2) + 2 * g + ((j >> 1) & 1);
+                        } else {
+                            islot = 16 * ks + 4 * g + (j >> 1);
+                        }
+                        d = j & 1;
+                    } else {
+                        if (chain) {
+                            islot = 8 * (ks >> 2) + 2 * g + ((ks & 3) >> 1);
+                            d = ks & 1;
+                        } else {
+                            islot = 2 * ks + (g >> 1);
+                            d = g & 1;
+                        }
+                    }
+                    double val = 0.0;
+                    const bool ok = oslot < nout && (chain || islot < nin);
+                    if (ok) {
+                        const int ko = (kind == MAT_MID_FWD) ? mid_perm(oslot, n) : oslot;
+                        const int ni = chain ? mid_perm(islot, n) : islot;
+                        const long long e = ((long long)ko * ni) % n;
+                        const double ang = sgn * 2.0 * M_PI * (double)e / (double)n;
+                        const double wr = cos(ang) * scale, wi = sin(ang) * scale;
+                        if (c == 0) val = (d == 0) ? wr : -wi;
+                        else val = (d == 0) ? wi : wr;
+                    }
+                    const size_t idx = (((size_t)(mt * KS + ks) * 64 + lane) * per + j);
+                    if (f32) {
+                        float fv = (float)val;
+                        memcpy(&out[idx * 4], &fv, 4);
+                    } else {
+                        uint16_t hv = f32_to_f16_bits((float)val);
+                        memcpy(&out[idx * 2], &hv, 2);
+                    }
+                }
+            }
+    return out;
+}
+
+// W_S^{k c} for k < n, c < S/n, laid out [k][c] (fp64 -> fp32).
+std::vector<float> build_twiddles(int n, long long S) {
+    const long long s = S / n;
+    std::vector<float> t((size_t)S * 2);
+    for (long long k = 0; k < n; ++k)
+        for (long long c = 0; c < s; ++c) {
+            const long long e = (k * c) % S;
+            const double ang = -2.0 * M_PI * (double)e / (double)S;
+            t[(size_t)(k * s + c) * 2] = (float)cos(ang);
+            t[(size_t)(k * s + c) * 2 + 1] = (float)sin(ang);
+        }
+    return t;
+}
+
+// Position of lower bin part q for the digit list fac[0..cnt) with
+// in-place strides str[0..cnt) (divided by the unit 'unit').
+std::vector<int> build_digrev(const int* fac, const long long* str, int cnt,
+                              long long unit) {
+    long long Q = 1;
+    for (int i = 0; i < cnt; ++i) Q *= fac[i];
+    std::vector<int> r((size_t)Q);
+    for (long long q = 0; q < Q; ++q) {
+        long long rem = q, pos = 0;
+        for (int i = 0; i < cnt; ++i) {
+            const long long dgt = rem % fac[i];
+            rem /= fac[i];
+            pos += dgt * (str[i] / unit);
+        }
+        r[(size_t)q] = (int)pos;
+    }
+    return r;
+}
+
+}  // namespace
+
+// --------------------------------------------------------------- the plan
+
+struct fftconv_plan_s {
+    Shape s;
+    int device = 0;
+    std::vector<void*> allocs;
+    FwdParams fused{};      // path 0
+    FwdParams outer{};      // path 1, outer passes
+    FwdParams inner{};      // path 1, inner pass
+};
+
+namespace {
+
+hipError_t upload(fftconv_plan_s* pl, const void* host, size_t bytes, void** dev) {
+    void* d = nullptr;
+    hipError_t e = hipMalloc(&d, bytes ? bytes : 16);
+    if (e != hipSuccess) return e;
+    pl->allocs.push_back(d);
+    e = hipMemcpy(d, host, bytes, hipMemcpyHostToDevice);
+    *dev = d;
+    return e;
+}
+
+void free_plan(fftconv_plan_s* pl) {
+    if (!pl) return;
+    for (void* p : pl->allocs) (void)hipFree(p);
+    delete pl;
+}
+
+fftconv_status build_device_tables(fftconv_plan_s* pl) {
+    const Shape& s = pl->s;
+    const bool f32 = s.dtype == FFTCONV_F32;
+    long long S[kMaxStages], str[kMaxStages];
+    {
+        long long blk = (long long)s.M;
+        for (int i = 0; i < s.p; ++i) {
+            S[i] = blk;
+            str[i] = blk / s.f[i];
+            blk = str[i];
+        }
+    }
+    // regular stages: twiddles + matrices
+    StageDev reg[kMaxStages];
+    memset(reg, 0, sizeof(reg));
+    for (int i = 0; i < s.p - 1; ++i) {
+        const int n = s.f[i];
+        const bool outermost = (i == 0);
+        std::vector<float> tw = build_twiddles(n, S[i]);
+        void *dtw = nullptr, *dmf = nullptr, *dmi = nullptr;
+        if (upload(pl, tw.data(), tw.size() * 4, &dtw) != hipSuccess) return FFTCONV_ERR_HIP;
+        std::vector<uint8_t> mf = build_matrix(n, false, outermost, false, MAT_REG, f32);
+        std::vector<uint8_t> mi = build_matrix(n, true, false, outermost, MAT_REG, f32);
+        if (upload(pl, mf.data(), mf.size(), &dmf) != hipSuccess) return FFTCONV_ERR_HIP;
+        if (upload(pl, mi.data(), mi.size(), &dmi) != hipSuccess) return FFTCONV_ERR_HIP;
+        reg[i].n = n;
+        reg[i].tw = (const float2*)dtw;
+        reg[i].mat_f = dmf;
+        reg[i].mat_i = dmi;
+        reg[i].tw_stride = (int)str[i];
+    }
+    // middle stage
+    MidDev mid{};
+    {
+        const int n = s.f[s.p - 1];
+        std::vector<uint8_t> mf = build_matrix(n, false, false, false, MAT_MID_FWD, f32);
+        std::vector<uint8_t> mi = build_matrix(n, true, false, false, MAT_MID_INV, f32);
+        void *dmf = nullptr, *dmi = nullptr, *ddr = nullptr;
+        if (upload(pl, mf.data(), mf.size(), &dmf) != hipSuccess) return FFTCONV_ERR_HIP;
+        if (upload(pl, mi.data(), mi.size(), &dmi) != hipSuccess) return FFTCONV_ERR_HIP;
+        const int first = s.path ? s.n_outer : 0;
+        std::vector<int> dr = build_digrev(s.f + first, str + first,
+                                           s.p - 1 - first, n);
+        if (upload(pl, dr.data(), dr.size() * 4, &ddr) != hipSuccess) return FFTCONV_ERR_HIP;
+        mid.n = n;
+        mid.slab = s.path ? s.Min : (int)s.M;
+        mid.Q = mid.slab / n;
+        mid.digrev = (const int*)ddr;
+        mid.mat_f = dmf;
+        mid.mat_i = dmi;
+    }
+    if (s.path == 0) {
+        FwdParams& P = pl->fused;
+        memset(&P, 0, sizeof(P));
+        P.M = (int)s.M;
+        P.N = (int)s.N;
+        P.nst = s.p - 1;
+        P.outer_half = 1;
+        for (int i = 0; i < P.nst; ++i) {
+            P.st[i] = reg[i];
+            P.st[i].Sb = (int)S[i];
+            P.st[i].sb = (int)str[i];
+            P.st[i].Cb = 1;
+            P.st[i].tw_mul = 1;
+            P.st[i].ncols = (int)(s.M / s.f[i]);
+        }
+        P.mid = mid;
+        P.Qo = 1;
+        P.threads = s.thr_fused;
+    } else {
+        FwdParams& O = pl->outer;
+        memset(&O, 0, sizeof(O));
+        O.M = (int)s.M;
+        O.N = (int)s.N;
+        O.nst = s.n_outer;
+        O.outer_half = 1;
+        for (int i = 0; i < s.n_outer; ++i) {
+            O.st[i] = reg[i];
+            O.st[i].Sb = (int)(S[i] / s.Min);
+            O.st[i].sb = (int)(str[i] / s.Min);
+            O.st[i].Cb = s.ct;
+            O.st[i].tw_mul = s.Min;
+            O.st[i].ncols = s.Qo * s.ct / s.f[i];
+        }
+        O.Qo = s.Qo;
+        O.ct = s.ct;
+        O.threads = s.thr_outer;
+        FwdParams& I = pl->inner;
+        memset(&I, 0, sizeof(I));
+        I.M = (int)s.M;
+        I.N = (int)s.N;
+        I.nst = s.p - 1 - s.n_outer;
+        I.outer_half = 0;
+        for (int i = 0; i < I.nst; ++i) {
+            const int gi = s.n_outer + i;
+            I.st[i] = reg[gi];
+            I.st[i].Sb = (int)S[gi];
+            I.st[i].sb = (int)str[gi];
+            I.st[i].Cb = 1;
+            I.st[i].tw_mul = 1;
+            I.st[i].ncols = 2 * s.Min / s.f[gi];
+        }
+        I.mid = mid;
+        I.Qo = s.Qo;
+        I.nunits = s.Qo / 2 + 1;
+        I.threads = s.thr_inner;
+        std::vector<int> dro = build_digrev(s.f, str, s.n_outer, s.Min);
+        void* d = nullptr;
+        if (upload(pl, dro.data(), dro.size() * 4, &d) != hipSuccess) return FFTCONV_ERR_HIP;
+        I.digrev_o = (const int*)d;
+        O.digrev_o = (const int*)d;
+    }
+    return FFTCONV_OK;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+bool overlap(const void* a, size_t na, const void* b, size_t nb) {
+    const uintptr_t a0 = (uintptr_t)a, b0 = (uintptr_t)b;
+    return a0 < b0 + nb && b0 < a0 + na;
+}
+
+}  // namespace
+
+// ------------------------------------------------------------------ C ABI
+
+extern "C" {
+
+const char* fftconv_version(void) { return "fftconv-gfx950 0.1"; }
+
+const char* fftconv_status_string(fftconv_status st) {
+    switch (st) {
+    case FFTCONV_OK: return "ok";
+    case FFTCONV_ERR_INVALID_ARG: return "invalid argument";
+    case FFTCONV_ERR_UNSUPPORTED: return "unsupported length, order or dtype";
+    case FFTCONV_ERR_ALIGNMENT: return "tensor pointer not 16-byte aligned";
+    case FFTCONV_ERR_WORKSPACE: return "workspace missing or too small";
+    case FFTCONV_ERR_HIP: return "HIP runtime error";
+    }
+    return "unknown status";
+}
+
+fftconv_status fftconv_plan_query(size_t N, int p, fftconv_dtype dtype,
+                                  fftconv_plan_info* info) {
+    if (!info) return FFTCONV_ERR_INVALID_ARG;
+    Shape s;
+    fftconv_status st = make_shape(N, p, dtype, s);
+    if (st != FFTCONV_OK) return st;
+    fill_info(s, info);
+    return FFTCONV_OK;
+}
+
+fftconv_status fftconv_plan(size_t N, int p, fftconv_dtype dtype,
+                            fftconv_plan_t* out) {
+    if (!out) return FFTCONV_ERR_INVALID_ARG;
+    *out = nullptr;
+    Shape s;
+    fftconv_status st = make_shape(N, p, dtype, s);
+    if (st != FFTCONV_OK) return st;
+    fftconv_plan_s* pl = new (std::nothrow) fftconv_plan_s();
+    if (!pl) return FFTCONV_ERR_HIP;
+    pl->s = s;
+    if (hipGetDevice(&pl->device) != hipSuccess) {
+        delete pl;
+        return FFTCONV_ERR_HIP;
+    }
+    st = build_device_tables(pl);
+    if (st != FFTCONV_OK) {
+        free_plan(pl);
+        return st;
+    }
+    *out = pl;
+    return FFTCONV_OK;
+}
+
+fftconv_status fftconv_plan_get_info(fftconv_plan_t plan,
+                                     fftconv_plan_info* info) {
+    if (!plan || !info) return FFTCONV_ERR_INVALID_ARG;
+    fill_info(plan->s, info);
+    return FFTCONV_OK;
+}
+
+void fftconv_plan_destroy(fftconv_plan_t plan) { free_plan(plan); }
+
+size_t fftconv_spectrum_bytes(fftconv_plan_t plan, size_t H) {
+    if (!plan) return 0;
+    return H * plan->s.M * kf_entry_bytes(plan->s.dtype);
+}
+
+size_t fftconv_workspace_bytes(fftconv_plan_t plan, size_t B, size_t H) {
+    if (!plan || plan->s.path == 0) return 0;
+    return B * H * plan->s.M * 8;
+}
+
+fftconv_status fftconv_kernel_spectrum(fftconv_plan_t plan, const float* k,
+                                       size_t H, void* k_f, void* stream) {
+    if (!plan) return FFTCONV_ERR_INVALID_ARG;
+    if (H == 0) return FFTCONV_OK;
+    if (!k || !k_f) return FFTCONV_ERR_INVALID_ARG;
+    if (!aligned16(k) || !aligned16(k_f)) return FFTCONV_ERR_ALIGNMENT;
+    const Shape& s = plan->s;
+    if (overlap(k, H * s.N * 4, k_f, fftconv_spectrum_bytes(plan, H)))
+        return FFTCONV_ERR_INVALID_ARG;
+    if (H > 0x7fffffff) return FFTCONV_ERR_UNSUPPORTED;
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess) return FFTCONV_ERR_HIP;
+    if (dev != plan->device) return FFTCONV_ERR_INVALID_ARG;
+    hipStream_t st = (hipStream_t)stream;
+    const long long L = 2LL * (long long)s.N;
+    const size_t per_ch = (size_t)L * sizeof(float2) * 2;
+    size_t hc = (size_t)512 << 20;
+    hc = hc / per_ch;
+    if (hc < 1) hc = 1;
+    if (hc > H) hc = H;
+    void* X = nullptr;
+    if (hipMallocAsync(&X, hc * per_ch, st) != hipSuccess) return FFTCONV_ERR_HIP;
+    float2* X0 = (float2*)X;
+    float2* X1 = X0 + hc * L;
+    hipError_t e = hipSuccess;
+    const int io = (int)s.dtype;
+    for (size_t h0 = 0; h0 < H && e == hipSuccess; h0 += hc) {
+        const int cnt = (int)((H - h0) < hc ? (H - h0) : hc);
+        e = launch_kpad(k + h0 * s.N, X0, cnt, (int)s.N, st);
+        float2 *a = X0, *b = X1;
+        for (long long Ns = 1; Ns < L && e == hipSuccess; Ns *= 2) {
+            e = launch_stockham(a, b, cnt, (int)L, (int)Ns, st);
+            float2* t = a;
+            a = b;
+            b = t;
+        }
+        if (e != hipSuccess) break;
+        SpecParams sp{};
+        sp.M = (int)s.M;
+        sp.N = (int)s.N;
+        sp.L = (int)L;
+        sp.p = s.p;
+        for (int i = 0; i < s.p; ++i) sp.factors[i] = s.f[i];
+        sp.h0 = (int)h0;
+        sp.hcount = cnt;
+        sp.X = a;
+        sp.kf = k_f;
+        e = launch_alphabeta(io, sp, st);
+    }
+    hipError_t e2 = hipFreeAsync(X, st);
+    if (e != hipSuccess || e2 != hipSuccess) return FFTCONV_ERR_HIP;
+    return FFTCONV_OK;
+}
+
+fftconv_status fftconv_forward(fftconv_plan_t plan, const void* u,
+                               const void* k_f, void* y, size_t B, size_t H,
+                               size_t N, void* workspace,
+                               size_t workspace_bytes, void* stream) {
+    if (!plan) return FFTCONV_ERR_INVALID_ARG;
+    const Shape& s = plan->s;
+    if (N != s.N) return FFTCONV_ERR_INVALID_ARG;
+    const size_t rows = B * H;
+    if (B != 0 && rows / B != H) return FFTCONV_ERR_INVALID_ARG;
+    if (rows == 0) return FFTCONV_OK;
+    if (!u || !k_f || !y) return FFTCONV_ERR_INVALID_ARG;
+    if (!aligned16(u) || !aligned16(y) || !aligned16(k_f)) return FFTCONV_ERR_ALIGNMENT;
+    if (rows > 0x7fffffffULL || H > 0x7fffffffULL) return FFTCONV_ERR_UNSUPPORTED;
+    const size_t esz = s.dtype == FFTCONV_F32 ? 4 : 2;
+    const size_t io_bytes = rows * N * esz;
+    const size_t kf_bytes = fftconv_spectrum_bytes(plan, H);
+    if (overlap(y, io_bytes, u, io_bytes) || overlap(y, io_bytes, k_f, kf_bytes))
+        return FFTCONV_ERR_INVALID_ARG;
+    const size_t ws_need = fftconv_workspace_bytes(plan, B, H);
+    if (ws_need) {
+        if (!workspace || workspace_bytes < ws_need) return FFTCONV_ERR_WORKSPACE;
+        if (!aligned16(workspace)) return FFTCONV_ERR_ALIGNMENT;
+        if (overlap(workspace, ws_need, y, io_bytes) ||
+            overlap(workspace, ws_need, u, io_bytes) ||
+            overlap(workspace, ws_need, k_f, kf_bytes))
+            return FFTCONV_ERR_INVALID_ARG;
+    }
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess) return FFTCONV_ERR_HIP;
+    if (dev != plan->device) return FFTCONV_ERR_INVALID_ARG;
+    hipStream_t st = (hipStream_t)stream;
+    const int io = (int)s.dtype;
+    hipError_t e;
+    if (s.path == 0) {
+        FwdParams P = plan->fused;
+        P.rows = (long long)rows;
+        P.H = (int)H;
+        P.u = u;
+        P.y = y;
+        P.kf = k_f;
+        e = launch_fused(io, P, s.lds_fused, st);
+    } else {
+        FwdParams O = plan->outer, I = plan->inner;
+        O.rows = I.rows = (long long)rows;
+        O.H = I.H = (int)H;
+        O.u = I.u = u;
+        O.y = I.y = y;
+        O.kf = I.kf = k_f;
+        O.ws = I.ws = (float2*)workspace;
+        e = launch_outer_fwd(io, O, s.lds_outer, st);
+        if (e == hipSuccess) e = launch_inner(io, I, s.lds_inner, st);
+        if (e == hipSuccess) e = launch_outer_inv(io, O, s.lds_outer, st);
+    }
+    return e == hipSuccess ? FFTCONV_OK : FFTCONV_ERR_HIP;
+}
+
+}  // extern "C"

@@ -1,0 +1,117 @@
+// Internal declarations shared by the host planner (fftconv_host.cpp) and
+// the gfx950 kernels (fftconv_kernels.hip).  Not part of the public ABI.
+//
+// Transform conventions (page "FlashFFTConv: Efficient Convolutions for
+// Long Sequences with Tensor Cores", section 3.4):
+//  * A row u[0:N] is packed into M = N complex points z[m] = u[2m] + i u[2m+1]
+//    for m < N/2; z[m] = 0 for m >= N/2 is the causal zero padding, never
+//    stored and never multiplied ("Implicit zero-padding").
+//  * The M-point DFT is factored M = N_1 * ... * N_p (order-p Monarch).
+//    Forward stage i (decimation in frequency, in place): within blocks of
+//    S_i = N_i * ... * N_p points, each of the s_i = S_i / N_i columns gets an
+//    N_i-point DFT over elements spaced s_i apart, followed by the twiddle
+//    W_{S_i}^{k c} (k = output digit, c = column).  After stage p, position
+//    pos = sum_i k_i s_i holds bin k = k_1 + N_1 k_2 + N_1 N_2 k_3 + ...
+//  * Every stage DFT is scaled by 1/sqrt(N_i), so the whole transform is
+//    unitary and fp16 operands cannot overflow.
+//  * The inverse mirrors the stages (conjugate twiddle before each inverse
+//    DFT), taking digit-reversed positions back to natural order.
+//  * Between the transforms, bin k and its mirror bin (M - k) mod M are
+//    combined as Z'[k] = alpha_k Z[k] + beta_k conj(Z[-k]); alpha/beta fold
+//    the real-FFT unpack, the product with the kernel spectrum and the
+//    repack of the one-stage decimation in time.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fftconv {
+
+enum IoType : int { IO_F32 = 0, IO_F16 = 1, IO_BF16 = 2 };
+
+constexpr int kMaxStages = 8;
+constexpr int kWaveSize = 64;
+
+// One regular (non-middle) Monarch stage, as seen by a kernel that keeps a
+// "line" of complex points in LDS.  The line is made of outer units; each
+// outer unit holds Cb consecutive batch columns (Cb = 1 unless several
+// independent columns of a larger transform are processed together).
+//   LDS index of (block b, digit d, column c, batch cb)
+//        = ((b * Sb + d * sb + c) * Cb + cb)
+//   twiddle index = d * tw_stride + c * tw_mul + tw_off + cb
+struct StageDev {
+    int n;          // radix N_i (8, 16 or 32)
+    int Sb;         // block size in outer units
+    int sb;         // stride between digits in outer units (= Sb / n)
+    int Cb;         // batch columns per outer unit
+    int ncols;      // number of n-point DFT columns on the line
+    int tw_stride;  // s_i of the full transform
+    int tw_mul;     // multiplier of c in the twiddle column
+    int pad;
+    const float2* tw;    // W_{S_i}^{k c}, S_i entries laid out [k][c], or null
+    const void* mat_f;   // forward DFT matrix tiles (A operand, per lane)
+    const void* mat_i;   // inverse DFT matrix tiles (A operand, per lane)
+};
+
+// The last (innermost) stage, fused with the bin pairing and the first
+// inverse stage.
+struct MidDev {
+    int n;          // radix N_p (16 or 32)
+    int Q;          // blocks per slab (slab length / n)
+    int slab;       // slab length in points
+    int pad;
+    const int* digrev;   // block position of lower bin part q, [Q]
+    const void* mat_f;   // forward matrix, rows permuted to pair bins in-lane
+    const void* mat_i;   // inverse matrix, K ordered like the accumulators
+};
+
+struct FwdParams {
+    // geometry
+    int M;              // packed transform length (= N)
+    int N;              // sequence length
+    int nst;            // regular stages handled by this kernel
+    int outer_half;     // stage 0 is the outermost stage (zero half)
+    StageDev st[kMaxStages];
+    MidDev mid;
+    // rows
+    long long rows;     // B * H
+    int H;
+    int Qo;             // multi-pass: number of slabs (outer product)
+    int ct;             // multi-pass outer passes: batch columns per tile
+    int nunits;         // multi-pass inner pass: units per row
+    int threads;        // threads per workgroup
+    const int* digrev_o;   // multi-pass: slab index of outer bin part, [Qo]
+    // data
+    const void* u;
+    void* y;
+    const void* kf;     // alpha/beta, [H][M] entries
+    float2* ws;         // multi-pass workspace, [rows][M]
+};
+
+// Spectrum (alpha/beta) construction.
+struct SpecParams {
+    int M, N, L;
+    int p;
+    int factors[kMaxStages];
+    int h0, hcount;     // channel chunk
+    const float2* X;    // [hcount][L] fp32 spectra of the padded kernels
+    void* kf;           // [H][M] alpha/beta
+};
+
+// Launchers (defined in fftconv_kernels.hip).  Return hipSuccess or the
+// launch error.
+hipError_t launch_fused(int io, const FwdParams& p, int lds_bytes,
+                        hipStream_t s);
+hipError_t launch_outer_fwd(int io, const FwdParams& p, int lds_bytes,
+                            hipStream_t s);
+hipError_t launch_inner(int io, const FwdParams& p, int lds_bytes,
+                        hipStream_t s);
+hipError_t launch_outer_inv(int io, const FwdParams& p, int lds_bytes,
+                            hipStream_t s);
+hipError_t launch_kpad(const float* k, float2* X, int hcount, int N,
+                       hipStream_t s);
+hipError_t launch_stockham(const float2* in, float2* out, int hcount, int L,
+                           int Ns, hipStream_t s);
+hipError_t launch_alphabeta(int io, const SpecParams& p, hipStream_t s);
+
+}  // namespace fftconv

@@ -1,0 +1,745 @@
+// gfx950 (CDNA4) kernels of the causal FFT long convolution.
+//
+// Every DFT stage is a small dense complex matrix product on the matrix
+// cores (v_mfma_f32_16x16x32_f16 for 16-bit I/O plans, v_mfma_f32_16x16x4_f32
+// for fp32 plans), the Monarch factorisation of the FFT described on the
+// page "FlashFFTConv: Efficient Convolutions for Long Sequences with Tensor
+// Cores", section 3.4 ("The Monarch FFT Decomposition", Algorithm 1 and its
+// order-3/4 generalisations).  Data between stages lives in LDS as fp32
+// complex; each stage rounds its operand to the matrix-core type once and
+// accumulates in fp32.  Twiddles and the spectrum product are fp32 VALU work.
+//
+// Complex N-point DFTs are embedded as real 2N x 2N matrices
+//     [re_out]   [ Re W  -Im W ] [re_in]
+//     [im_out] = [ Im W   Re W ] [im_in]
+// with re/im interleaved along both the rows and the contraction index, so a
+// lane always holds the real and imaginary part of the same point.
+//
+// Matrix-core operand layouts used here (16x16 output tiles, 64 lanes,
+// lane = 16*g + x):
+//   A operand: lane (g, x) holds row x, contraction slots owned by group g
+//   B operand: lane (g, x) holds column x, contraction slots owned by g
+//   C result : lane (g, x) holds rows 4g..4g+3 of column x
+// Which contraction index sits in which (g, slot) is a free choice as long
+// as the matrix tables (built on the host) use the same one.
+#include "fftconv_internal.h"
+
+namespace fftconv {
+
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float2 cmul(float2 a, float2 b) {
+    return make_float2(a.x * b.x - a.y * b.y, a.x * b.y + a.y * b.x);
+}
+// a * conj(b)
+__device__ __forceinline__ float2 cmulc(float2 a, float2 b) {
+    return make_float2(a.x * b.x + a.y * b.y, a.y * b.x - a.x * b.y);
+}
+
+// ---------------------------------------------------------------------------
+// Matrix-core traits.
+//  gather decode: K-step ks, lane group g, slot j <-> input digit nn, part d
+//    f16: nn = 16 ks + 4 g + (j >> 1), d = j & 1     (8 halves per lane)
+//    f32: nn = 2 ks + (g >> 1),        d = g & 1     (1 float per lane)
+//  chain decode (operand taken straight from accumulators z[mt][e], which
+//  hold output slot 8 mt + 2 g + e):
+//    f16: K-step ks takes z[2ks + (j>>2)][(j>>1)&1], part j&1
+//    f32: K-step ks takes z[ks>>2][(ks&3)>>1], part ks&1
+// ---------------------------------------------------------------------------
+struct MfF16 {
+    typedef half8 AB;
+    static constexpr int ksteps(int nin) { return nin <= 16 ? 1 : nin / 16; }
+    static __device__ __forceinline__ floatx4 mma(const AB& a, const AB& b,
+                                                  floatx4 c) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+    }
+    template <class F>
+    static __device__ __forceinline__ AB gather(int ks, int g, int nin,
+                                                F&& get) {
+        AB b;
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+            const int nn = 16 * ks + 4 * g + jj;
+            float2 v = make_float2(0.f, 0.f);
+            if (nn < nin) v = get(nn);
+            b[2 * jj] = (_Float16)v.x;
+            b[2 * jj + 1] = (_Float16)v.y;
+        }
+        return b;
+    }
+    template <int MT>
+    static __device__ __forceinline__ AB chain(int ks,
+                                               const float2 (&z)[MT][2]) {
+        AB b;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const float2 v = z[2 * ks + (j >> 2)][(j >> 1) & 1];
+            b[j] = (_Float16)((j & 1) ? v.y : v.x);
+        }
+        return b;
+    }
+};
+
+struct MfF32 {
+    typedef float AB;
+    static constexpr int ksteps(int nin) { return nin / 2; }
+    static __device__ __forceinline__ floatx4 mma(const AB& a, const AB& b,
+                                                  floatx4 c) {
+        return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+    }
+    template <class F>
+    static __device__ __forceinline__ AB gather(int ks, int g, int nin,
+                                                F&& get) {
+        const int nn = 2 * ks + (g >> 1);
+        float2 v = make_float2(0.f, 0.f);
+        if (nn < nin) v = get(nn);
+        return (g & 1) ? v.y : v.x;
+    }
+    template <int MT>
+    static __device__ __forceinline__ AB chain(int ks,
+                                               const float2 (&z)[MT][2]) {
+        const float2 v = z[ks >> 2][(ks & 3) >> 1];
+        return (ks & 1) ? v.y : v.x;
+    }
+};
+
+// ---------------------------------------------------------------------------
+// One regular Monarch stage over an LDS line (in place).
+//  forward: gather digits nn (only the lower half when HALF: the causal zero
+//           padding), DFT, multiply output digit k by W_{S}^{k c}, scatter.
+//  inverse: gather digits k and multiply by conj(W_S^{k c}), inverse DFT,
+//           scatter (only the lower half of the outputs when HALF).
+// ---------------------------------------------------------------------------
+template <class MF, int N, bool INV, bool HALF>
+__device__ __forceinline__ void run_stage(float2* __restrict__ line,
+                                          int line_len, const StageDev& d,
+                                          int tw_off, int wave, int nwaves,
+                                          int lane) {
+    constexpr int NIN = (HALF && !INV) ? N / 2 : N;
+    constexpr int NOUT = (HALF && INV) ? N / 2 : N;
+    constexpr int KS = MF::ksteps(NIN);
+    constexpr int MT = NOUT / 8 > 0 ? NOUT / 8 : 1;
+    const int g = lane >> 4, x = lane & 15;
+    const typename MF::AB* mat =
+        (const typename MF::AB*)(INV ? d.mat_i : d.mat_f);
+    typename MF::AB A[MT][KS];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) A[mt][ks] = mat[(mt * KS + ks) * 64 + lane];
+
+    const int ntiles = (line_len / N) >> 4;
+    const int cs = d.sb * d.Cb;
+    const float2* __restrict__ tw = d.tw;
+    for (int t = wave; t < ntiles; t += nwaves) {
+        const int q = (t << 4) + x;
+        const int cb = q % d.Cb;
+        const int r1 = q / d.Cb;
+        const int c = r1 % d.sb;
+        const int b = r1 / d.sb;
+        const int base = (b * d.Sb + c) * d.Cb + cb;
+        const int twc = c * d.tw_mul + tw_off + cb;
+        typename MF::AB B[KS];
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            B[ks] = MF::gather(ks, g, NIN, [&](int nn) {
+                float2 v = line[base + nn * cs];
+                if (INV) v = cmulc(v, tw[nn * d.tw_stride + twc]);
+                return v;
+            });
+        }
+        floatx4 acc[MT];
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+            acc[mt] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks)
+                acc[mt] = MF::mma(A[mt][ks], B[ks], acc[mt]);
+        }
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+                const int slot = 8 * mt + 2 * g + e;
+                if (slot < NOUT) {
+                    float2 v = make_float2(acc[mt][2 * e], acc[mt][2 * e + 1]);
+                    if (!INV) v = cmul(v, tw[slot * d.tw_stride + twc]);
+                    line[base + slot * cs] = v;
+                }
+            }
+    }
+}
+
+template <class MF, bool INV>
+__device__ __forceinline__ void dispatch_stage(bool half, const StageDev& d,
+                                               float2* line, int line_len,
+                                               int tw_off, int wave,
+                                               int nwaves, int lane) {
+    if (half) {
+        if (d.n == 32) run_stage<MF, 32, INV, true>(line, line_len, d, tw_off, wave, nwaves, lane);
+        else if (d.n == 16) run_stage<MF, 16, INV, true>(line, line_len, d, tw_off, wave, nwaves, lane);
+        else run_stage<MF, 8, INV, true>(line, line_len, d, tw_off, wave, nwaves, lane);
+    } else {
+        if (d.n == 32) run_stage<MF, 32, INV, false>(line, line_len, d, tw_off, wave, nwaves, lane);
+        else if (d.n == 16) run_stage<MF, 16, INV, false>(line, line_len, d, tw_off, wave, nwaves, lane);
+        else run_stage<MF, 8, INV, false>(line, line_len, d, tw_off, wave, nwaves, lane);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Spectrum coefficients: one entry per packed bin = (alpha, beta).
+// ---------------------------------------------------------------------------
+template <int IO>
+__device__ __forceinline__ void load_ab(const void* kf, long long idx,
+                                        float2& a, float2& b) {
+    if (IO == IO_F32) {
+        const float4 v = ((const float4*)kf)[idx];
+        a = make_float2(v.x, v.y);
+        b = make_float2(v.z, v.w);
+    } else {
+        const uint2 w = ((const uint2*)kf)[idx];
+        const _Float16* h = (const _Float16*)&w;
+        a = make_float2((float)h[0], (float)h[1]);
+        b = make_float2((float)h[2], (float)h[3]);
+    }
+}
+
+// out = a*z + b*conj(p)
+__device__ __forceinline__ float2 pair_combine(float2 a, float2 z, float2 b,
+                                               float2 p) {
+    return make_float2(a.x * z.x - a.y * z.y + b.x * p.x + b.y * p.y,
+                       a.x * z.y + a.y * z.x + b.y * p.x - b.x * p.y);
+}
+
+// ---------------------------------------------------------------------------
+// The innermost stage fused with the bin pairing and the first inverse
+// stage (the forward DFT, the product with the kernel spectrum and the
+// start of the inverse stay in registers, as in Algorithm 1 of the page).
+//
+// Bins of block b (lower part q) pair with bins of the block whose lower
+// part is -q (mod Q); digit k pairs with n-1-k, except in the q = 0 block
+// where it pairs with -k (mod n).  The forward matrix rows are permuted
+// (slot s -> digit s for s < n/2, 3n/2-1-s otherwise) so that partner
+// digits sit in the same lane, M-tile mt <-> mt + MT/2.  A lane processes a
+// "lane slot": one block in column 0 of the MFMA tile and its partner in
+// column 1.  Unit types:
+//   0: one slab whose outer bin part is 0 (the only type for a fused row):
+//      lane slot 0 = (q=0, q=Q/2), lane slot j = (j, Q-j)
+//   1: one slab whose outer part is half the outer range: (j, Q-1-j)
+//   2: two slabs with mirrored outer parts: (j in slab 0, Q-1-j in slab 1)
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ int mid_perm(int slot, int n) {
+    return slot < (n >> 1) ? slot : (3 * n / 2 - 1 - slot);
+}
+
+template <class MF, int IO, int N>
+__device__ __forceinline__ void run_middle(float2* __restrict__ line,
+                                           const MidDev& d, int utype,
+                                           int sigA, int sigB,
+                                           const void* kf, long long kfrow,
+                                           int wave, int nwaves, int lane,
+                                           float2* scratch) {
+    constexpr int MT = N / 8;
+    constexpr int KS = MF::ksteps(N);
+    const int g = lane >> 4, x = lane & 15;
+    typedef typename MF::AB AB;
+    const AB* mf = (const AB*)d.mat_f;
+    const AB* mi = (const AB*)d.mat_i;
+    AB Af[MT][KS], Ai[MT][KS];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            Af[mt][ks] = mf[(mt * KS + ks) * 64 + lane];
+            Ai[mt][ks] = mi[(mt * KS + ks) * 64 + lane];
+        }
+    const int Q = d.Q;
+    const int LS = (utype == 2) ? Q : (Q >> 1);
+    const int steps = (LS + 15) >> 4;
+    for (int st = wave; st < steps; st += nwaves) {
+        const int ls_raw = (st << 4) + x;
+        const bool valid = ls_raw < LS;
+        const int ls = valid ? ls_raw : LS - 1;
+        const bool special = valid && utype == 0 && ls == 0;
+        int qA = ls, qB, sA = 0, sB = 0;
+        if (utype == 0) {
+            qB = (ls == 0) ? (Q >> 1) : (Q - ls);
+        } else {
+            qB = Q - 1 - ls;
+            if (utype == 2) sB = 1;
+        }
+        const int bA = d.digrev[qA], bB = d.digrev[qB];
+        const int offA = sA * d.slab + bA * N;
+        const int offB = sB * d.slab + bB * N;
+        const long long pA = kfrow + (long long)sigA * d.slab + bA * N;
+        const long long pB =
+            kfrow + (long long)(sB ? sigB : sigA) * d.slab + bB * N;
+
+        AB BA[KS], BB[KS];
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            BA[ks] = MF::gather(ks, g, N, [&](int nn) { return line[offA + nn]; });
+            BB[ks] = MF::gather(ks, g, N, [&](int nn) { return line[offB + nn]; });
+        }
+        float2 za[MT][2], zb[MT][2];
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+            floatx4 ca = floatx4{0.f, 0.f, 0.f, 0.f};
+            floatx4 cb = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                ca = MF::mma(Af[mt][ks], BA[ks], ca);
+                cb = MF::mma(Af[mt][ks], BB[ks], cb);
+            }
+            za[mt][0] = make_float2(ca[0], ca[1]);
+            za[mt][1] = make_float2(ca[2], ca[3]);
+            zb[mt][0] = make_float2(cb[0], cb[1]);
+            zb[mt][1] = make_float2(cb[2], cb[3]);
+        }
+        float2 ra[MT][2], rb[MT][2];
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+                const int slot = 8 * mt + 2 * g + e;
+                const int k = mid_perm(slot, N);
+                const int pm = (mt + MT / 2) % MT;
+                float2 aa, ba, ab, bb;
+                load_ab<IO>(kf, pA + k, aa, ba);
+                load_ab<IO>(kf, pB + k, ab, bb);
+                ra[mt][e] = pair_combine(aa, za[mt][e], ba, zb[pm][e]);
+                rb[mt][e] = pair_combine(ab, zb[mt][e], bb, za[pm][e]);
+                if (special) {
+                    // column 1 holds q = Q/2, its own mirror block
+                    rb[mt][e] = pair_combine(ab, zb[mt][e], bb, zb[pm][e]);
+                }
+            }
+        if (special) {
+            // column 0 holds q = 0: digit k pairs with -k (mod N), which
+            // lives in another lane group; exchange through LDS.
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+                for (int e = 0; e < 2; ++e)
+                    scratch[mid_perm(8 * mt + 2 * g + e, N)] = za[mt][e];
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+                for (int e = 0; e < 2; ++e) {
+                    const int k = mid_perm(8 * mt + 2 * g + e, N);
+                    const float2 pz = scratch[(N - k) & (N - 1)];
+                    float2 aa, ba;
+                    load_ab<IO>(kf, pA + k, aa, ba);
+                    ra[mt][e] = pair_combine(aa, za[mt][e], ba, pz);
+                }
+        }
+        AB CA[KS], CB[KS];
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            CA[ks] = MF::template chain<MT>(ks, ra);
+            CB[ks] = MF::template chain<MT>(ks, rb);
+        }
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+            floatx4 oa = floatx4{0.f, 0.f, 0.f, 0.f};
+            floatx4 ob = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                oa = MF::mma(Ai[mt][ks], CA[ks], oa);
+                ob = MF::mma(Ai[mt][ks], CB[ks], ob);
+            }
+            if (valid) {
+#pragma unroll
+                for (int e = 0; e < 2; ++e) {
+                    const int slot = 8 * mt + 2 * g + e;
+                    line[offA + slot] = make_float2(oa[2 * e], oa[2 * e + 1]);
+                    line[offB + slot] = make_float2(ob[2 * e], ob[2 * e + 1]);
+                }
+            }
+        }
+    }
+}
+
+template <class MF, int IO>
+__device__ __forceinline__ void dispatch_middle(const MidDev& d, float2* line,
+                                                int utype, int sigA, int sigB,
+                                                const void* kf,
+                                                long long kfrow, int wave,
+                                                int nwaves, int lane,
+                                                float2* scratch) {
+    if (d.n == 32)
+        run_middle<MF, IO, 32>(line, d, utype, sigA, sigB, kf, kfrow, wave, nwaves, lane, scratch);
+    else
+        run_middle<MF, IO, 16>(line, d, utype, sigA, sigB, kf, kfrow, wave, nwaves, lane, scratch);
+}
+
+// ---------------------------------------------------------------------------
+// I/O element conversions.  16-bit rows move as 16-byte vectors.
+// ---------------------------------------------------------------------------
+template <int IO>
+__device__ __forceinline__ float io_to_f32(uint16_t v) {
+    if (IO == IO_BF16) return __uint_as_float(((uint32_t)v) << 16);
+    return (float)__builtin_bit_cast(_Float16, v);
+}
+template <int IO>
+__device__ __forceinline__ uint16_t f32_to_io(float f) {
+    if (IO == IO_BF16) return __builtin_bit_cast(uint16_t, (__bf16)f);
+    return __builtin_bit_cast(uint16_t, (_Float16)f);
+}
+
+// z[m] = u[2m] + i u[2m+1] for m in [0, cnt): 'src' points at u[2*m0].
+// Points land at line[(m - m0) * stride] within each run of 'run' points.
+template <int IO>
+__device__ __forceinline__ void load_points(const void* src, float2* dst,
+                                            int npts, int tid, int nthr) {
+    if (IO == IO_F32) {
+        const float4* s = (const float4*)src;
+        for (int j = tid; j < (npts >> 1); j += nthr) {
+            const float4 v = s[j];
+            dst[2 * j] = make_float2(v.x, v.y);
+            dst[2 * j + 1] = make_float2(v.z, v.w);
+        }
+    } else {
+        const uint4* s = (const uint4*)src;
+        for (int j = tid; j < (npts >> 2); j += nthr) {
+            const uint4 v = s[j];
+            const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                dst[4 * j + i] = make_float2(io_to_f32<IO>((uint16_t)(w[i] & 0xffffu)),
+                                             io_to_f32<IO>((uint16_t)(w[i] >> 16)));
+        }
+    }
+}
+
+template <int IO>
+__device__ __forceinline__ void store_points(const float2* src, void* dst,
+                                             int npts, int tid, int nthr) {
+    if (IO == IO_F32) {
+        float4* o = (float4*)dst;
+        for (int j = tid; j < (npts >> 1); j += nthr) {
+            const float2 a = src[2 * j], b = src[2 * j + 1];
+            o[j] = make_float4(a.x, a.y, b.x, b.y);
+        }
+    } else {
+        uint4* o = (uint4*)dst;
+        for (int j = tid; j < (npts >> 2); j += nthr) {
+            uint32_t w[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float2 a = src[4 * j + i];
+                w[i] = (uint32_t)f32_to_io<IO>(a.x) | ((uint32_t)f32_to_io<IO>(a.y) << 16);
+            }
+            o[j] = make_uint4(w[0], w[1], w[2], w[3]);
+        }
+    }
+}
+
+template <int IO>
+__device__ __forceinline__ const char* io_ptr(const void* base, long long elem) {
+    return (const char*)base + elem * (IO == IO_F32 ? 4 : 2);
+}
+
+// ---------------------------------------------------------------------------
+// Fused path: one workgroup holds a whole row's M packed points in LDS.
+// ---------------------------------------------------------------------------
+template <class MF, int IO>
+__global__ void __launch_bounds__(512) fused_kernel(FwdParams P) {
+    extern __shared__ float2 smem[];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int nwaves = blockDim.x >> 6;
+    float2* line = smem;
+    float2* scratch = smem + P.M + wave * 32;
+    for (long long row = blockIdx.x; row < P.rows; row += gridDim.x) {
+        const int h = (int)(row % P.H);
+        load_points<IO>(io_ptr<IO>(P.u, row * P.N), line, P.N >> 1,
+                        threadIdx.x, blockDim.x);
+        __syncthreads();
+        for (int i = 0; i < P.nst; ++i) {
+            dispatch_stage<MF, false>(i == 0 && P.outer_half, P.st[i], line,
+                                      P.M, 0, wave, nwaves, lane);
+            __syncthreads();
+        }
+        dispatch_middle<MF, IO>(P.mid, line, 0, 0, 0, P.kf,
+                                (long long)h * P.M, wave, nwaves, lane,
+                                scratch);
+        __syncthreads();
+        for (int i = P.nst - 1; i >= 0; --i) {
+            dispatch_stage<MF, true>(i == 0 && P.outer_half, P.st[i], line,
+                                     P.M, 0, wave, nwaves, lane);
+            __syncthreads();
+        }
+        store_points<IO>(line, (void*)io_ptr<IO>(P.y, row * P.N), P.N >> 1,
+                         threadIdx.x, blockDim.x);
+        __syncthreads();
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Multi-pass path (rows too long for one workgroup's LDS).
+//  outer pass (forward): a tile of ct columns c2 of the [Qo][slab] view of
+//    a row; the outer stages run over the Qo outer digits; result to the
+//    fp32 workspace at the in-place positions.
+//  inner pass: one unit (slab or mirrored slab pair) per workgroup; inner
+//    stages, pairing with the spectrum, inverse inner stages; in place.
+//  outer pass (inverse): inverse outer stages per column tile, then y.
+// ---------------------------------------------------------------------------
+template <class MF, int IO>
+__global__ void __launch_bounds__(512) outer_fwd_kernel(FwdParams P) {
+    extern __shared__ float2 smem[];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int nwaves = blockDim.x >> 6;
+    const long long row = blockIdx.x;
+    const int c0 = blockIdx.y * P.ct;
+    const int slab = P.M / P.Qo;
+    float2* line = smem;
+    // the nonzero half of the outer digits: n_o < Qo/2
+    for (int no = 0; no < (P.Qo >> 1); ++no)
+        load_points<IO>(io_ptr<IO>(P.u, row * P.N + 2LL * ((long long)no * slab + c0)),
+                        line + no * P.ct, P.ct, threadIdx.x, blockDim.x);
+    __syncthreads();
+    for (int i = 0; i < P.nst; ++i) {
+        dispatch_stage<MF, false>(i == 0, P.st[i], line, P.Qo * P.ct, c0,
+                                  wave, nwaves, lane);
+        __syncthreads();
+    }
+    float2* ws = P.ws + row * (long long)P.M;
+    const int per = P.ct >> 1;   // float4 (two points) per outer digit
+    for (int j = threadIdx.x; j < P.Qo * per; j += blockDim.x) {
+        const int no = j / per, c = (j - no * per) * 2;
+        const float2 a = line[no * P.ct + c], b = line[no * P.ct + c + 1];
+        *(float4*)(ws + (long long)no * slab + c0 + c) = make_float4(a.x, a.y, b.x, b.y);
+    }
+}
+
+template <class MF, int IO>
+__global__ void __launch_bounds__(512) inner_kernel(FwdParams P) {
+    extern __shared__ float2 smem[];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int nwaves = blockDim.x >> 6;
+    const long long row = blockIdx.x;
+    const int unit = blockIdx.y;
+    const int h = (int)(row % P.H);
+    const int slab = P.M / P.Qo;
+    const int utype = unit == 0 ? 0 : (unit == 1 ? 1 : 2);
+    const int qoA = unit == 0 ? 0 : (unit == 1 ? (P.Qo >> 1) : unit - 1);
+    const int sigA = P.digrev_o[qoA];
+    const int sigB = utype == 2 ? P.digrev_o[P.Qo - qoA] : sigA;
+    const int nslab = utype == 2 ? 2 : 1;
+    float2* line = smem;
+    float2* scratch = smem + 2 * slab + wave * 32;
+    float2* ws = P.ws + row * (long long)P.M;
+    for (int s = 0; s < nslab; ++s) {
+        const float4* src = (const float4*)(ws + (long long)(s ? sigB : sigA) * slab);
+        for (int j = threadIdx.x; j < (slab >> 1); j += blockDim.x) {
+            const float4 v = src[j];
+            line[s * slab + 2 * j] = make_float2(v.x, v.y);
+            line[s * slab + 2 * j + 1] = make_float2(v.z, v.w);
+        }
+    }
+    __syncthreads();
+    const int len = nslab * slab;
+    for (int i = 0; i < P.nst; ++i) {
+        dispatch_stage<MF, false>(false, P.st[i], line, len, 0, wave, nwaves, lane);
+        __syncthreads();
+    }
+    dispatch_middle<MF, IO>(P.mid, line, utype, sigA, sigB, P.kf,
+                            (long long)h * P.M, wave, nwaves, lane, scratch);
+    __syncthreads();
+    for (int i = P.nst - 1; i >= 0; --i) {
+        dispatch_stage<MF, true>(false, P.st[i], line, len, 0, wave, nwaves, lane);
+        __syncthreads();
+    }
+    for (int s = 0; s < nslab; ++s) {
+        float4* dst = (float4*)(ws + (long long)(s ? sigB : sigA) * slab);
+        for (int j = threadIdx.x; j < (slab >> 1); j += blockDim.x) {
+            const float2 a = line[s * slab + 2 * j], b = line[s * slab + 2 * j + 1];
+            dst[j] = make_float4(a.x, a.y, b.x, b.y);
+        }
+    }
+}
+
+template <class MF, int IO>
+__global__ void __launch_bounds__(512) outer_inv_kernel(FwdParams P) {
+    extern __shared__ float2 smem[];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int nwaves = blockDim.x >> 6;
+    const long long row = blockIdx.x;
+    const int c0 = blockIdx.y * P.ct;
+    const int slab = P.M / P.Qo;
+    float2* line = smem;
+    const float2* ws = P.ws + row * (long long)P.M;
+    const int per = P.ct >> 1;
+    for (int j = threadIdx.x; j < P.Qo * per; j += blockDim.x) {
+        const int no = j / per, c = (j - no * per) * 2;
+        const float4 v = *(const float4*)(ws + (long long)no * slab + c0 + c);
+        line[no * P.ct + c] = make_float2(v.x, v.y);
+        line[no * P.ct + c + 1] = make_float2(v.z, v.w);
+    }
+    __syncthreads();
+    for (int i = P.nst - 1; i >= 0; --i) {
+        dispatch_stage<MF, true>(i == 0, P.st[i], line, P.Qo * P.ct, c0,
+                                 wave, nwaves, lane);
+        __syncthreads();
+    }
+    for (int no = 0; no < (P.Qo >> 1); ++no)
+        store_points<IO>(line + no * P.ct,
+                         (void*)io_ptr<IO>(P.y, row * P.N + 2LL * ((long long)no * slab + c0)),
+                         P.ct, threadIdx.x, blockDim.x);
+}
+
+// ---------------------------------------------------------------------------
+// Kernel spectrum (untimed, once per channel): an accurate fp32 radix-2
+// Stockham FFT of the zero-padded kernel, then alpha/beta per packed bin.
+// ---------------------------------------------------------------------------
+__global__ void kpad_kernel(const float* __restrict__ k, float2* __restrict__ X,
+                            int hcount, int N) {
+    const long long L = 2LL * N;
+    const long long total = hcount * L;
+    for (long long i = blockIdx.x * (long long)blockDim.x + threadIdx.x; i < total;
+         i += (long long)gridDim.x * blockDim.x) {
+        const long long h = i / L, t = i - h * L;
+        X[i] = make_float2(t < N ? k[h * N + t] : 0.f, 0.f);
+    }
+}
+
+// One radix-2 Stockham pass: sub-transforms of length Ns are combined into
+// length 2Ns; natural-order output after log2(L) passes.
+__global__ void stockham_kernel(const float2* __restrict__ in,
+                                float2* __restrict__ out, int hcount, int L,
+                                int Ns) {
+    const long long half = L >> 1;
+    const long long total = hcount * half;
+    for (long long i = blockIdx.x * (long long)blockDim.x + threadIdx.x; i < total;
+         i += (long long)gridDim.x * blockDim.x) {
+        const long long h = i / half, j = i - h * half;
+        const float2* a = in + h * L;
+        float2* o = out + h * L;
+        const int k = (int)(j % Ns);
+        double sn, cs;
+        sincospi(-(double)k / (double)Ns, &sn, &cs);
+        const float2 u0 = a[j];
+        const float2 u1 = cmul(a[j + half], make_float2((float)cs, (float)sn));
+        const long long dst = (j / Ns) * 2 * Ns + k;
+        o[dst] = make_float2(u0.x + u1.x, u0.y + u1.y);
+        o[dst + Ns] = make_float2(u0.x - u1.x, u0.y - u1.y);
+    }
+}
+
+// alpha_k = ((1 - s) K[k] + (1 + s) K[k+M]) / 2,  beta_k = i c (K[k] - K[k+M]) / 2
+// with s + i c = e^{i(pi/2 - 2 pi k/L)}... i.e. s = sin(2 pi k/L), c = cos(2 pi k/L);
+// stored at the in-place position of bin k.
+template <int IO>
+__global__ void alphabeta_kernel(SpecParams P) {
+    const long long total = (long long)P.hcount * P.M;
+    for (long long i = blockIdx.x * (long long)blockDim.x + threadIdx.x; i < total;
+         i += (long long)gridDim.x * blockDim.x) {
+        const long long hl = i / P.M;
+        const int pos = (int)(i - hl * P.M);
+        // bin of position: digits k_1..k_p, most significant first
+        int rem = pos, S = P.M, mul = 1, kb = 0;
+        for (int f = 0; f < P.p; ++f) {
+            const int n = P.factors[f];
+            const int s = S / n;
+            const int dgt = rem / s;
+            rem -= dgt * s;
+            kb += dgt * mul;
+            mul *= n;
+            S = s;
+        }
+        const float2* X = P.X + hl * P.L;
+        const float2 K1 = X[kb], K2 = X[kb + P.M];
+        double sn, cs;
+        sincospi(2.0 * (double)kb / (double)P.L, &sn, &cs);
+        const float s = (float)sn, c = (float)cs;
+        const float2 al = make_float2(0.5f * ((1.f - s) * K1.x + (1.f + s) * K2.x),
+                                      0.5f * ((1.f - s) * K1.y + (1.f + s) * K2.y));
+        const float2 dlt = make_float2(K1.x - K2.x, K1.y - K2.y);
+        const float2 be = make_float2(-0.5f * c * dlt.y, 0.5f * c * dlt.x);
+        const long long o = (long long)(P.h0 + hl) * P.M + pos;
+        if (IO == IO_F32) {
+            ((float4*)P.kf)[o] = make_float4(al.x, al.y, be.x, be.y);
+        } else {
+            _Float16 hv[4] = {(_Float16)al.x, (_Float16)al.y, (_Float16)be.x, (_Float16)be.y};
+            ((uint2*)P.kf)[o] = *(const uint2*)hv;
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Launchers
+// ---------------------------------------------------------------------------
+template <class K>
+static hipError_t set_lds(K kern, int bytes) {
+    if (bytes <= 64 * 1024) return hipSuccess;
+    return hipFuncSetAttribute((const void*)kern,
+                               hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+}
+
+#define FFTCONV_LAUNCH(KERNEL, GRID)                                          \
+    do {                                                                      \
+        hipError_t e_;                                                        \
+        const dim3 blk(p.threads);                                            \
+        switch (io) {                                                         \
+        case IO_F32:                                                          \
+            e_ = set_lds(KERNEL<MfF32, IO_F32>, lds);                         \
+            if (e_ != hipSuccess) return e_;                                  \
+            hipLaunchKernelGGL((KERNEL<MfF32, IO_F32>), GRID, blk, lds, s, p); \
+            break;                                                            \
+        case IO_F16:                                                          \
+            e_ = set_lds(KERNEL<MfF16, IO_F16>, lds);                         \
+            if (e_ != hipSuccess) return e_;                                  \
+            hipLaunchKernelGGL((KERNEL<MfF16, IO_F16>), GRID, blk, lds, s, p); \
+            break;                                                            \
+        default:                                                              \
+            e_ = set_lds(KERNEL<MfF16, IO_BF16>, lds);                        \
+            if (e_ != hipSuccess) return e_;                                  \
+            hipLaunchKernelGGL((KERNEL<MfF16, IO_BF16>), GRID, blk, lds, s, p); \
+            break;                                                            \
+        }                                                                     \
+        return hipGetLastError();                                             \
+    } while (0)
+
+hipError_t launch_fused(int io, const FwdParams& p, int lds, hipStream_t s) {
+    FFTCONV_LAUNCH(fused_kernel, dim3((unsigned)p.rows));
+}
+
+hipError_t launch_outer_fwd(int io, const FwdParams& p, int lds, hipStream_t s) {
+    const int slab = p.M / p.Qo;
+    FFTCONV_LAUNCH(outer_fwd_kernel, dim3((unsigned)p.rows, slab / p.ct));
+}
+
+hipError_t launch_inner(int io, const FwdParams& p, int lds, hipStream_t s) {
+    FFTCONV_LAUNCH(inner_kernel, dim3((unsigned)p.rows, p.nunits));
+}
+
+hipError_t launch_outer_inv(int io, const FwdParams& p, int lds, hipStream_t s) {
+    const int slab = p.M / p.Qo;
+    FFTCONV_LAUNCH(outer_inv_kernel, dim3((unsigned)p.rows, slab / p.ct));
+}
+
+hipError_t launch_kpad(const float* k, float2* X, int hcount, int N, hipStream_t s) {
+    hipLaunchKernelGGL(kpad_kernel, dim3(1024), dim3(256), 0, s, k, X, hcount, N);
+    return hipGetLastError();
+}
+
+hipError_t launch_stockham(const float2* in, float2* out, int hcount, int L,
+                           int Ns, hipStream_t s) {
+    hipLaunchKernelGGL(stockham_kernel, dim3(2048), dim3(256), 0, s, in, out,
+                       hcount, L, Ns);
+    return hipGetLastError();
+}
+
+hipError_t launch_alphabeta(int io, const SpecParams& p, hipStream_t s) {
+    if (io == IO_F32)
+        hipLaunchKernelGGL(alphabeta_kernel<IO_F32>, dim3(2048), dim3(256), 0, s, p);
+    else
+        hipLaunchKernelGGL(alphabeta_kernel<IO_F16>, dim3(2048), dim3(256), 0, s, p);
+    return hipGetLastError();
+}
+
+}  // namespace fftconv

@@ -1,0 +1,192 @@
+"""ctypes binding over libfftconv.so (the C ABI in include/fftconv.h).
+
+Argument marshalling only: every step of the convolution runs in the HIP
+library.  PyTorch supplies device memory (tensors) and the current stream.
+If the library is not built, calls raise -- there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libfftconv.so")
+
+STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported", 3: "alignment",
+          4: "workspace", 5: "hip error"}
+DTYPES = {"f32": 0, "f16": 1, "bf16": 2}
+
+_lib = None
+
+
+class FFTConvError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__("%s: %s (status %d)" % (what, STATUS.get(status, "?"),
+                                                 status))
+
+
+class PlanInfo(ctypes.Structure):
+    _fields_ = [("N", ctypes.c_size_t), ("M", ctypes.c_size_t),
+                ("order", ctypes.c_int), ("factors", ctypes.c_int * 8),
+                ("path", ctypes.c_int), ("outer_factors", ctypes.c_int),
+                ("dtype", ctypes.c_int),
+                ("spectrum_bytes_per_channel", ctypes.c_size_t),
+                ("workspace_bytes_per_row", ctypes.c_size_t),
+                ("mfma_flops_per_row", ctypes.c_double)]
+
+    def as_dict(self) -> dict:
+        return {"N": self.N, "M": self.M, "order": self.order,
+                "factors": list(self.factors[:self.order]),
+                "path": "fused" if self.path == 0 else "multipass",
+                "outer_factors": self.outer_factors,
+                "dtype": {v: k for k, v in DTYPES.items()}[self.dtype],
+                "spectrum_bytes_per_channel": self.spectrum_bytes_per_channel,
+                "workspace_bytes_per_row": self.workspace_bytes_per_row,
+                "mfma_flops_per_row": self.mfma_flops_per_row}
+
+
+def lib() -> ctypes.CDLL:
+    """Open libfftconv.so (built in-tree by fft_long_convolution_amd.build)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                "libfftconv.so is not built; run "
+                "'python -m fft_long_convolution_amd.build'")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, sz, i = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int
+        L.fftconv_plan.argtypes = [sz, i, i, ctypes.POINTER(vp)]
+        L.fftconv_plan.restype = i
+        L.fftconv_plan_query.argtypes = [sz, i, i, ctypes.POINTER(PlanInfo)]
+        L.fftconv_plan_query.restype = i
+        L.fftconv_plan_get_info.argtypes = [vp, ctypes.POINTER(PlanInfo)]
+        L.fftconv_plan_get_info.restype = i
+        L.fftconv_plan_destroy.argtypes = [vp]
+        L.fftconv_plan_destroy.restype = None
+        L.fftconv_spectrum_bytes.argtypes = [vp, sz]
+        L.fftconv_spectrum_bytes.restype = sz
+        L.fftconv_workspace_bytes.argtypes = [vp, sz, sz]
+        L.fftconv_workspace_bytes.restype = sz
+        L.fftconv_kernel_spectrum.argtypes = [vp, vp, sz, vp, vp]
+        L.fftconv_kernel_spectrum.restype = i
+        L.fftconv_forward.argtypes = [vp, vp, vp, vp, sz, sz, sz, vp, sz, vp]
+        L.fftconv_forward.restype = i
+        L.fftconv_status_string.argtypes = [i]
+        L.fftconv_status_string.restype = ctypes.c_char_p
+        L.fftconv_version.argtypes = []
+        L.fftconv_version.restype = ctypes.c_char_p
+        _lib = L
+    return _lib
+
+
+def plan_query(N: int, p: int = 0, dtype: str = "bf16") -> dict:
+    """What fftconv_plan(N, p, dtype) would build (no device needed)."""
+    info = PlanInfo()
+    st = lib().fftconv_plan_query(N, p, DTYPES[dtype], ctypes.byref(info))
+    if st != 0:
+        raise FFTConvError(st, "fftconv_plan_query(N=%d, p=%d)" % (N, p))
+    return info.as_dict()
+
+
+def _torch_dtype(dtype: str):
+    import torch
+    return {"f32": torch.float32, "f16": torch.float16,
+            "bf16": torch.bfloat16}[dtype]
+
+
+def _stream_handle(stream):
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+class FFTConv:
+    """Causal FFT long convolution for one (N, order, dtype) plan.
+
+    >>> conv = FFTConv(1024, dtype="bf16")
+    >>> k_f = conv.kernel_spectrum(k)          # k: [H, N] fp32, once
+    >>> y = conv.forward(u, k_f)               # u: [B, H, N] bf16
+    """
+
+    def __init__(self, N: int, p: int = 0, dtype: str = "bf16"):
+        if dtype not in DTYPES:
+            raise ValueError("dtype must be one of %s" % list(DTYPES))
+        import torch
+        if not torch.cuda.is_available():
+            raise RuntimeError("FFTConv needs a ROCm GPU")
+        self.N, self.dtype = N, dtype
+        h = ctypes.c_void_p()
+        st = lib().fftconv_plan(N, p, DTYPES[dtype], ctypes.byref(h))
+        if st != 0:
+            raise FFTConvError(st, "fftconv_plan(N=%d, p=%d, %s)" % (N, p, dtype))
+        self._plan = h
+        info = PlanInfo()
+        lib().fftconv_plan_get_info(h, ctypes.byref(info))
+        self.info = info.as_dict()
+        self.device = torch.cuda.current_device()
+
+    def close(self):
+        if getattr(self, "_plan", None):
+            lib().fftconv_plan_destroy(self._plan)
+            self._plan = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def spectrum_bytes(self, H: int) -> int:
+        return int(lib().fftconv_spectrum_bytes(self._plan, H))
+
+    def workspace_bytes(self, B: int, H: int) -> int:
+        return int(lib().fftconv_workspace_bytes(self._plan, B, H))
+
+    def kernel_spectrum(self, k, out=None, stream=None):
+        """k: [H, N] fp32 CUDA tensor -> opaque k_f (uint8 CUDA tensor)."""
+        import torch
+        if k.dtype != torch.float32 or k.dim() != 2 or k.shape[1] != self.N:
+            raise ValueError("k must be fp32 [H, %d]" % self.N)
+        k = k.contiguous()
+        H = k.shape[0]
+        nb = self.spectrum_bytes(H)
+        if out is None:
+            out = torch.empty(nb, dtype=torch.uint8, device=k.device)
+        elif out.numel() * out.element_size() < nb:
+            raise ValueError("k_f buffer too small")
+        st = lib().fftconv_kernel_spectrum(self._plan, k.data_ptr(), H,
+                                           out.data_ptr(),
+                                           _stream_handle(stream))
+        if st != 0:
+            raise FFTConvError(st, "fftconv_kernel_spectrum")
+        return out
+
+    def forward(self, u, k_f, out=None, workspace=None, stream=None):
+        """u: [B, H, N] CUDA tensor of the plan dtype -> y (same shape)."""
+        import torch
+        if u.dim() != 3 or u.shape[2] != self.N:
+            raise ValueError("u must be [B, H, %d]" % self.N)
+        if u.dtype != _torch_dtype(self.dtype):
+            raise ValueError("u dtype must be %s" % self.dtype)
+        u = u.contiguous()
+        B, H, N = u.shape
+        if out is None:
+            out = torch.empty_like(u)
+        elif out.shape != u.shape or out.dtype != u.dtype:
+            raise ValueError("out must match u")
+        need = self.workspace_bytes(B, H)
+        ws_ptr, ws_bytes = None, 0
+        if need:
+            if workspace is None:
+                workspace = torch.empty(need, dtype=torch.uint8,
+                                        device=u.device)
+            ws_ptr = workspace.data_ptr()
+            ws_bytes = workspace.numel() * workspace.element_size()
+        st = lib().fftconv_forward(self._plan, u.data_ptr(), k_f.data_ptr(),
+                                   out.data_ptr(), B, H, N, ws_ptr, ws_bytes,
+                                   _stream_handle(stream))
+        if st != 0:
+            raise FFTConvError(st, "fftconv_forward")
+        return out

@@ -1,0 +1,148 @@
+/*
+ * fftconv.h -- C ABI of the MI355X (gfx950) causal FFT long-convolution
+ * library (libfftconv.so).
+ *
+ * The operation (page "FlashFFTConv: Efficient Convolutions for Long
+ * Sequences with Tensor Cores", section 3.4, convolution definition and the
+ * convolution theorem with causal zero padding to 2N):
+ *
+ *     y[b,h,t] = sum_{s=0..t} u[b,h,s] * k[h,t-s],   t in [0, N)
+ *
+ * computed as the first N outputs of the 2N-point circular convolution of
+ * the zero-padded sequences.  Internally the real 2N-point transforms are
+ * packed into N-point complex ones (the one-stage decimation in time of
+ * section 3.4, "The real-valued FFT optimization"), the zero half of the
+ * padded input is never read or computed ("Implicit zero-padding for causal
+ * convolutions"), and every DFT is an order-p Monarch factorisation
+ * ("The Monarch FFT Decomposition"): small dense DFT-matrix products on the
+ * matrix cores with twiddle multiplies between them.
+ *
+ * Conventions for every call:
+ *  - All tensor pointers are DEVICE pointers (memory from hipMalloc or a
+ *    torch CUDA tensor on the same device); sizes are element counts.
+ *  - The caller owns u, k, k_f, y and the workspace.  A plan owns only its
+ *    own device tables.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *    Launching calls are asynchronous on that stream; they never
+ *    synchronise the host.  Faults inside kernels surface at the caller's
+ *    next synchronisation.
+ *  - Every argument is validated before anything is launched; on error the
+ *    call returns a non-OK status, launches nothing and writes nothing.
+ *    Nothing throws across this interface.
+ *  - A plan is immutable after creation and may be used from several host
+ *    threads and streams at once.
+ */
+#ifndef FFTCONV_H
+#define FFTCONV_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum fftconv_status {
+    FFTCONV_OK = 0,
+    FFTCONV_ERR_INVALID_ARG = 1,  /* null pointer, size mismatch, overlap   */
+    FFTCONV_ERR_UNSUPPORTED = 2,  /* N, order or dtype not supported        */
+    FFTCONV_ERR_ALIGNMENT = 3,    /* a tensor pointer is not 16-B aligned   */
+    FFTCONV_ERR_WORKSPACE = 4,    /* workspace missing or too small         */
+    FFTCONV_ERR_HIP = 5           /* the HIP runtime reported an error      */
+} fftconv_status;
+
+/* I/O element type of u and y.  k is always fp32. */
+typedef enum fftconv_dtype {
+    FFTCONV_F32 = 0,
+    FFTCONV_F16 = 1,
+    FFTCONV_BF16 = 2
+} fftconv_dtype;
+
+typedef struct fftconv_plan_s *fftconv_plan_t;
+
+/* Description of what a plan does (filled without touching the device). */
+typedef struct fftconv_plan_info {
+    size_t N;                 /* sequence length                            */
+    size_t M;                 /* packed complex transform length (= N)     */
+    int order;                /* number of Monarch factors p                */
+    int factors[8];           /* N_1 (outermost, sees the zero half) ...    */
+    int path;                 /* 0 = fused (one launch per call),
+                                 1 = multi-pass through the workspace       */
+    int outer_factors;        /* multi-pass: factors done in the outer pass */
+    fftconv_dtype dtype;
+    size_t spectrum_bytes_per_channel;
+    size_t workspace_bytes_per_row;
+    double mfma_flops_per_row; /* algorithmic matrix-core flops per row     */
+} fftconv_plan_info;
+
+/* Create a plan for length N, Monarch order p and I/O dtype.
+ *  N: a power of two in [256, 4194304] (section 3.4 discusses lengths up to
+ *     4M; section 4.2's tables span 256..4M).
+ *  p: 0 picks the default factorisation for N; p >= 2 requests exactly p
+ *     factors (each of 8, 16 or 32; the last one 16 or 32) and returns
+ *     FFTCONV_ERR_UNSUPPORTED when N cannot be split that way.
+ * Builds the DFT matrices and twiddle tables in fp64 on the host, rounds
+ * them to the kernel's operand types and uploads them synchronously.
+ * On success *out receives the plan; on failure *out is set to NULL. */
+fftconv_status fftconv_plan(size_t N, int p, fftconv_dtype dtype,
+                            fftconv_plan_t *out);
+
+/* Describe the plan fftconv_plan(N, p, dtype) would build, without
+ * allocating anything on the device. */
+fftconv_status fftconv_plan_query(size_t N, int p, fftconv_dtype dtype,
+                                  fftconv_plan_info *info);
+
+/* Describe an existing plan. */
+fftconv_status fftconv_plan_get_info(fftconv_plan_t plan,
+                                     fftconv_plan_info *info);
+
+/* Free a plan's device tables.  NULL is accepted. */
+void fftconv_plan_destroy(fftconv_plan_t plan);
+
+/* Bytes of the k_f buffer for H channels (caller allocates). */
+size_t fftconv_spectrum_bytes(fftconv_plan_t plan, size_t H);
+
+/* Bytes of the workspace fftconv_forward needs for B x H rows (0 on the
+ * fused path; the caller allocates it). */
+size_t fftconv_workspace_bytes(fftconv_plan_t plan, size_t B, size_t H);
+
+/* Kernel spectrum, computed once per channel and reused for every batch
+ * row (section 2, Equation 1: "Fk is often precomputed").
+ *  k:   device, fp32, [H][N] contiguous (the causal kernel taps k[h, t]).
+ *  k_f: device, fftconv_spectrum_bytes(plan, H) bytes, 16-B aligned.  Its
+ *       layout is private to plans with the same N, factorisation and
+ *       dtype: it holds, per packed frequency bin, the two coefficients
+ *       that combine the bin and its mirror bin with the kernel's
+ *       spectrum (the real-FFT unpack, pointwise product and repack folded
+ *       together), stored in the order the kernels visit the bins.
+ * Asynchronous on `stream`; it allocates a temporary fp32 transform
+ * buffer with stream-ordered allocation (hipMallocAsync). */
+fftconv_status fftconv_kernel_spectrum(fftconv_plan_t plan, const float *k,
+                                       size_t H, void *k_f, void *stream);
+
+/* Causal long convolution y = (u * k)[0:N] for all B x H rows.
+ *  u: device, plan dtype, [B][H][N] contiguous, 16-B aligned.
+ *  k_f: device, from fftconv_kernel_spectrum with the same plan and H.
+ *  y: device, plan dtype, [B][H][N], 16-B aligned; must not overlap u or
+ *     k_f (checked: FFTCONV_ERR_INVALID_ARG).
+ *  N: must equal the plan's N.
+ *  workspace, workspace_bytes: device scratch of at least
+ *     fftconv_workspace_bytes(plan, B, H) bytes, 16-B aligned (may be NULL
+ *     with size 0 when that is 0); too small -> FFTCONV_ERR_WORKSPACE.
+ * Asynchronous on `stream`, no host synchronisation.  B*H == 0 is a valid
+ * no-op.  The calling thread's current HIP device must be the plan's. */
+fftconv_status fftconv_forward(fftconv_plan_t plan, const void *u,
+                               const void *k_f, void *y, size_t B, size_t H,
+                               size_t N, void *workspace,
+                               size_t workspace_bytes, void *stream);
+
+/* Static, human-readable text for a status code. */
+const char *fftconv_status_string(fftconv_status status);
+
+/* Version string of the library build. */
+const char *fftconv_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FFTCONV_H */

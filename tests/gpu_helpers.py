@@ -1,0 +1,60 @@
+"""Shared helpers for the GPU parity tests: run the HIP library on seeded
+workload rows and compare with the fp64 oracle."""
+from __future__ import annotations
+
+import numpy as np
+
+import oracle
+from fft_long_convolution_amd import inputs
+
+TOL = {"f32": 1e-5, "f16": 2e-3, "bf16": 2e-3}
+
+
+def to_torch(a: np.ndarray, dtype: str, device="cuda"):
+    import torch
+    if dtype == "bf16":
+        t = torch.from_numpy(a.view(np.int16).copy()).view(torch.bfloat16)
+    else:
+        t = torch.from_numpy(np.ascontiguousarray(a))
+    return t.to(device)
+
+
+def from_torch(t, dtype: str) -> np.ndarray:
+    import torch
+    t = t.detach().cpu()
+    if dtype == "bf16":
+        return t.view(torch.int16).numpy().view(np.uint16)
+    return t.numpy()
+
+
+def run_gpu(w: inputs.Workload, conv=None, p: int = 0):
+    """GPU result for all rows of workload w, as fp64 [rows, N]."""
+    import torch
+    from fft_long_convolution_amd.fftconv import FFTConv
+    if conv is None:
+        conv = FFTConv(w.N, p=p, dtype=w.dtype)
+    u = inputs.input_rows(w)
+    k = inputs.kernel_rows(w)
+    ud = to_torch(u, w.dtype).view(w.B, w.H, w.N)
+    kd = torch.from_numpy(k).cuda()
+    kf = conv.kernel_spectrum(kd)
+    y = conv.forward(ud, kf)
+    torch.cuda.synchronize()
+    y64 = oracle.to_f64(from_torch(y, w.dtype).reshape(w.rows, w.N), w.dtype)
+    return y64, u, k
+
+
+def oracle_rows(w: inputs.Workload, u: np.ndarray, k: np.ndarray):
+    """fp64 oracle for the same rows (FFT route; direct when N is small)."""
+    u64 = oracle.to_f64(u, w.dtype).reshape(w.rows, w.N)
+    k64 = k.astype(np.float64)
+    hidx = np.arange(w.rows) % w.H
+    if w.N <= 512:
+        return oracle.conv_direct(u64, k64, hidx)
+    return oracle.conv_fft(u64, k64, hidx)
+
+
+def parity(w: inputs.Workload, p: int = 0):
+    y, u, k = run_gpu(w, p=p)
+    ref = oracle_rows(w, u, k)
+    return oracle.rel_l2(y, ref), y, ref
