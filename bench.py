@@ -1,0 +1,192 @@
+#!/usr/bin/env python3
+"""Benchmark of the causal FFT long convolution on one MI355X.
+
+A step is one fftconv_forward over the whole batch (the full hot path:
+load + pack, forward Monarch stages, spectrum product, inverse stages,
+unpack + store).  The kernel spectrum is computed once before timing, as the
+method precomputes it per channel.  Default workload: the Hyena-shaped
+B=64, H=768, N=1024 bf16 convolution.
+
+Prints one JSON line: throughput in outputs/s (B*H*N per step), the
+roofline of the dominant kernel, and the fp64 CPU oracle timed on the host
+as a baseline.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = ("FFT-conv B*H*N outputs/sec and % of HBM/MFMA roofline, "
+          "N=1K..4M, 1 GPU")
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+MFMA_PEAK_TFLOPS = {"f16": 2500.0, "bf16": 2500.0, "f32": 157.3}
+ROTATE_BYTES = 1 << 30          # > 4x the 256 MB Infinity Cache
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="hyena_bf16_n1k")
+    ap.add_argument("--no-cpu", action="store_true",
+                    help="skip the CPU oracle baseline")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="target CPU time of the oracle sample")
+    return ap.parse_args()
+
+
+def to_torch(a, dtype, torch):
+    if dtype == "bf16":
+        return torch.from_numpy(a.view(np.int16).copy()).view(torch.bfloat16)
+    return torch.from_numpy(np.ascontiguousarray(a))
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py: this build runs on exactly one GPU; a run on %d GPUs "
+              "is not part of it (rows would shard by channel with no "
+              "communication)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+    import torch
+    from fft_long_convolution_amd import inputs
+    from fft_long_convolution_amd.fftconv import FFTConv
+
+    w = inputs.WORKLOADS[args.workload]
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    conv = FFTConv(w.N, dtype=w.dtype)
+    info = conv.info
+
+    # ---- inputs (seeded, synthetic) resident in HBM before timing
+    t0 = time.time()
+    u_np = inputs.input_rows(w)
+    k_np = inputs.kernel_rows(w)
+    gen_s = time.time() - t0
+    u0 = to_torch(u_np, w.dtype, torch).view(w.B, w.H, w.N).to(dev)
+    k = torch.from_numpy(k_np).to(dev)
+    kf = conv.kernel_spectrum(k)
+    esz = 4 if w.dtype == "f32" else 2
+    set_bytes = 2 * w.rows * w.N * esz
+    nsets = max(1, min(8, -(-ROTATE_BYTES // set_bytes)))
+    us = [u0] + [u0.clone() for _ in range(nsets - 1)]
+    ys = [torch.empty_like(u0) for _ in range(nsets)]
+    wsb = conv.workspace_bytes(w.B, w.H)
+    ws = torch.empty(max(wsb, 16), dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+
+    # ---- warmup, then K timed steps, HIP events on the launch stream
+    stream = torch.cuda.current_stream()
+    for i in range(args.warmup):
+        conv.forward(us[i % nsets], kf, out=ys[i % nsets], workspace=ws)
+    torch.cuda.synchronize()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    for i in range(args.steps):
+        starts[i].record(stream)
+        conv.forward(us[i % nsets], kf, out=ys[i % nsets], workspace=ws)
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    per = [s.elapsed_time(e) for s, e in zip(starts, ends)]   # ms
+    ms_step = float(np.mean(per))
+    ms_med = float(np.median(per))
+    outputs = w.rows * w.N
+    value = outputs / (ms_step * 1e-3)
+
+    # ---- roofline of the dominant kernel (algorithmic bytes and flops)
+    kf_bytes = conv.spectrum_bytes(w.H)
+    alg_bytes = 2 * w.rows * w.N * esz + kf_bytes
+    achieved_gbs = alg_bytes / (ms_step * 1e-3) / 1e9
+    flops = info["mfma_flops_per_row"] * w.rows
+    achieved_tf = flops / (ms_step * 1e-3) / 1e12
+    t_hbm = alg_bytes / (HBM_PEAK_GBS * 1e9)
+    t_mfma = flops / (MFMA_PEAK_TFLOPS[w.dtype] * 1e12)
+    bound = "hbm" if t_hbm >= t_mfma else "mfma"
+    if bound == "hbm":
+        roof = {"bound": "hbm", "achieved": round(achieved_gbs, 1),
+                "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved_gbs / HBM_PEAK_GBS, 4)}
+    else:
+        roof = {"bound": "mfma", "achieved": round(achieved_tf, 2),
+                "peak": MFMA_PEAK_TFLOPS[w.dtype], "unit": "TFLOP/s",
+                "frac": round(achieved_tf / MFMA_PEAK_TFLOPS[w.dtype], 4)}
+    roof["traffic"] = None
+    roof["kernel"] = ("fused_kernel" if info["path"] == "fused"
+                      else "outer_fwd+inner+outer_inv")
+    roof["algorithmic_bytes"] = int(alg_bytes)
+    roof["mfma_flops"] = float(flops)
+    roof["mfma_frac"] = round(achieved_tf / MFMA_PEAK_TFLOPS[w.dtype], 4)
+
+    # ---- sampled correctness of the timed output against the oracle
+    import oracle
+    y_last = ys[(args.steps - 1) % nsets].view(w.rows, w.N)
+    rng = np.random.default_rng(7)
+    rows = rng.integers(0, w.rows, 48)
+    ts = rng.integers(0, w.N, 48)
+    ts[:4] = [0, w.N - 1, 1, w.N // 2]
+    sel_u = oracle.to_f64(u_np[rows], w.dtype)
+    sel_k = k_np.astype(np.float64)
+    got = y_last[torch.from_numpy(rows).to(dev), torch.from_numpy(ts).to(dev)]
+    got = got.float().cpu().numpy().astype(np.float64)
+    want = oracle.conv_points(sel_u, sel_k, np.arange(48), ts, rows % w.H)
+    scale = float(np.sqrt(np.mean(want ** 2))) or 1.0
+    sample_err = float(np.max(np.abs(got - want)) / scale)
+
+    # ---- CPU baseline: the fp64 oracle on a bounded sample of the rows
+    cpu = None
+    if not args.no_cpu:
+        cores = oracle.num_threads()
+        probe = min(w.rows, max(w.H, 64))
+        hidx = np.arange(w.rows) % w.H
+        t0 = time.perf_counter()
+        u_probe = oracle.to_f64(u_np[:probe], w.dtype)
+        oracle.conv_fft(u_probe, k_np[:min(w.H, probe)].astype(np.float64),
+                        hidx[:probe])
+        tp = time.perf_counter() - t0
+        n = int(min(w.rows, max(probe, probe * args.cpu_seconds / max(tp, 1e-6))))
+        n = max(probe, (n // w.H) * w.H) if n >= w.H else n
+        usel = oracle.to_f64(u_np[:n], w.dtype)
+        t0 = time.perf_counter()
+        oracle.conv_fft(usel, k_np.astype(np.float64), hidx[:n])
+        tc = time.perf_counter() - t0
+        cpu = {"value": round(n * w.N / tc, 1), "unit": "outputs/s",
+               "cores": cores, "kind": "oracle",
+               "sample": "%d of %d rows (B*H) at N=%d through the fp64 "
+                         "radix-2 FFT route of the oracle, kernel spectra "
+                         "included; %.1f s" % (n, w.rows, w.N, tc)}
+
+    line = {
+        "metric": METRIC, "value": round(value, 1), "unit": "outputs/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N,
+                   "io_dtype": w.dtype, "factors": info["factors"],
+                   "path": info["path"], "global_batch": w.B,
+                   "seq_len": w.N, "parallelism": "single-gpu"},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "timing": {"ms_median": round(ms_med, 5),
+                   "wall_ms_per_step": round(wall / args.steps * 1e3, 5),
+                   "buffer_sets": nsets,
+                   "sampled_max_err_over_rms": sample_err,
+                   "input_gen_s": round(gen_s, 2)},
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

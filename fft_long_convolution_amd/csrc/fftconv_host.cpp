@@ -15,6 +15,7 @@
 #include <math.h>
 #include <stdint.h>
 #include <stdio.h>
+#include <stdlib.h>
 #include <string.h>
 
 #include <complex>
@@ -295,6 +296,155 @@ std::vector<int> build_digrev(const int* fac, const long long* str, int cnt,
     return r;
 }
 
+
+// ----------------------------------------------- row-kernel tables (32 x NB)
+
+double emb(double wr, double wi, int c, int d) {
+    return c == 0 ? (d == 0 ? wr : -wi) : (d == 0 ? wi : wr);
+}
+int kmap32h(int kt, int x) { return kt == 0 ? x : (x == 0 ? 16 : 32 - x); }
+// n_b digit held by row y of tile t in the row kernel (mirror map for
+// NB = 32 so forward and inverse twiddle positions coincide).
+int nbmaph(int NB, int t, int y) { return NB == 32 ? kmap32h(t, y) : 16 * t + y; }
+
+// Inner forward stage (A operand, rows in mirror-pairing order) whose K
+// index follows the first stage's accumulator rows: K-step ks, group g,
+// slot j <-> n_b = nbmap(ks, 4g + j/2), part j&1.
+std::vector<uint8_t> row_f2a(int NB) {
+    const int KS = NB / 16, MT = NB / 8;
+    std::vector<uint8_t> out((size_t)MT * KS * 64 * 8 * 2);
+    const double sc = 1.0 / sqrt((double)NB);
+    for (int mt = 0; mt < MT; ++mt)
+        for (int ks = 0; ks < KS; ++ks)
+            for (int lane = 0; lane < 64; ++lane) {
+                const int g = lane >> 4, x = lane & 15;
+                const int row = 16 * mt + x, oslot = row >> 1, c = row & 1;
+                const int kb = mid_perm(oslot, NB);
+                for (int j = 0; j < 8; ++j) {
+                    const int nb = nbmaph(NB, ks, 4 * g + (j >> 1)), d = j & 1;
+                    const double ang = -2.0 * M_PI * (double)((kb * nb) % NB) / (double)NB;
+                    const double v = emb(cos(ang) * sc, sin(ang) * sc, c, d);
+                    const uint16_t hv = f32_to_f16_bits((float)v);
+                    memcpy(&out[((((size_t)(mt * KS + ks)) * 64 + lane) * 8 + j) * 2], &hv, 2);
+                }
+            }
+    return out;
+}
+
+uint16_t f32_to_bf16_bits(float f) {
+    uint32_t b;
+    memcpy(&b, &f, 4);
+    const uint32_t lsb = (b >> 16) & 1u;
+    return (uint16_t)((b + 0x7fffu + lsb) >> 16);
+}
+float bf16_bits_to_f32(uint16_t h) {
+    uint32_t b = (uint32_t)h << 16;
+    float f;
+    memcpy(&f, &b, 4);
+    return f;
+}
+
+// First stage as the B operand: K = (n_a < 16, part d), columns
+// (k_a tile, part c), k_a = kmap32(tile, x).  bf16 plans get a hi/lo split
+// so the bf16 input feeds the matrix core directly at ~2^-16 accuracy.
+std::vector<uint16_t> row_f1b(bool bf16) {
+    const int T = bf16 ? 8 : 4;
+    std::vector<uint16_t> out((size_t)T * 64 * 8);
+    const double sc = 1.0 / sqrt(32.0);
+    for (int tt = 0; tt < T; ++tt) {
+        const int jt = tt & 3;
+        const bool lo = tt >= 4;
+        for (int lane = 0; lane < 64; ++lane) {
+            const int g = lane >> 4, x = lane & 15;
+            const int kt = jt >> 1, c = jt & 1, ka = kmap32h(kt, x);
+            for (int j = 0; j < 8; ++j) {
+                const int na = 4 * g + (j >> 1), d = j & 1;
+                const double ang = -2.0 * M_PI * (double)((na * ka) % 32) / 32.0;
+                const double v = emb(cos(ang) * sc, sin(ang) * sc, c, d);
+                uint16_t bits;
+                if (bf16) {
+                    const uint16_t hi = f32_to_bf16_bits((float)v);
+                    bits = lo ? f32_to_bf16_bits((float)(v - (double)bf16_bits_to_f32(hi))) : hi;
+                } else {
+                    bits = f32_to_f16_bits((float)v);
+                }
+                out[((size_t)tt * 64 + lane) * 8 + j] = bits;
+            }
+        }
+    }
+    return out;
+}
+
+// Last inverse stage as the A operand: rows (n_a < 16, part c), K the
+// accumulator order of the preceding stage: k_a = kmap32(ks, 4g + j/2).
+std::vector<uint16_t> row_i1a() {
+    std::vector<uint16_t> out((size_t)4 * 64 * 8);
+    const double sc = 1.0 / sqrt(32.0);
+    for (int mt = 0; mt < 2; ++mt)
+        for (int ks = 0; ks < 2; ++ks)
+            for (int lane = 0; lane < 64; ++lane) {
+                const int g = lane >> 4, x = lane & 15;
+                const int row = 16 * mt + x, na = row >> 1, c = row & 1;
+                for (int j = 0; j < 8; ++j) {
+                    const int ka = kmap32h(ks, 4 * g + (j >> 1)), d = j & 1;
+                    const double ang = 2.0 * M_PI * (double)((na * ka) % 32) / 32.0;
+                    const double v = emb(cos(ang) * sc, sin(ang) * sc, c, d);
+                    out[(((size_t)(mt * 2 + ks)) * 64 + lane) * 8 + j] = f32_to_f16_bits((float)v);
+                }
+            }
+    return out;
+}
+
+// Inner inverse stage as the B operand: K in accumulator (chain) order of
+// the permuted inner forward stage, columns (n_b tile, part c).
+std::vector<uint16_t> row_i2b(int NB) {
+    const int KS = NB / 16, JT = 2 * (NB / 16);
+    std::vector<uint16_t> out((size_t)KS * JT * 64 * 8);
+    const double sc = 1.0 / sqrt((double)NB);
+    for (int ks = 0; ks < KS; ++ks)
+        for (int jt = 0; jt < JT; ++jt)
+            for (int lane = 0; lane < 64; ++lane) {
+                const int g = lane >> 4, x = lane & 15;
+                const int nt = jt >> 1, c = jt & 1, nb = nbmaph(NB, nt, x);
+                for (int j = 0; j < 8; ++j) {
+                    const int slot = 16 * ks + 8 * (j >> 2) + 2 * g + ((j >> 1) & 1);
+                    const int kb = mid_perm(slot, NB), d = j & 1;
+                    const double ang = 2.0 * M_PI * (double)((kb * nb) % NB) / (double)NB;
+                    const double v = emb(cos(ang) * sc, sin(ang) * sc, c, d);
+                    out[(((size_t)(ks * JT + jt)) * 64 + lane) * 8 + j] = f32_to_f16_bits((float)v);
+                }
+            }
+    return out;
+}
+
+// Per-lane twiddles W_M^{+-k_a n_b} at the positions each lane holds.
+std::vector<float> row_twiddles(int NB, bool inverse) {
+    const int M = 32 * NB, IT = NB / 16;
+    std::vector<float> out((size_t)64 * IT * 8 * 2);
+    for (int lane = 0; lane < 64; ++lane) {
+        const int g = lane >> 4, x = lane & 15;
+        for (int a = 0; a < IT; ++a)          // fwd: it;   inv: nt
+            for (int kt = 0; kt < 2; ++kt)
+                for (int r = 0; r < 4; ++r) {
+                    int ka, nb, idx;
+                    if (!inverse) {
+                        ka = kmap32h(kt, x);
+                        nb = nbmaph(NB, a, 4 * g + r);
+                        idx = lane * (IT * 8) + (a * 2 + kt) * 4 + r;
+                    } else {
+                        ka = kmap32h(kt, 4 * g + r);
+                        nb = nbmaph(NB, a, x);
+                        idx = lane * (IT * 8) + (kt * IT + a) * 4 + r;
+                    }
+                    const double ang = (inverse ? 2.0 : -2.0) * M_PI *
+                                       (double)(((long long)ka * nb) % M) / (double)M;
+                    out[(size_t)idx * 2] = (float)cos(ang);
+                    out[(size_t)idx * 2 + 1] = (float)sin(ang);
+                }
+    }
+    return out;
+}
+
 }  // namespace
 
 // --------------------------------------------------------------- the plan
@@ -306,6 +456,11 @@ struct fftconv_plan_s {
     FwdParams fused{};      // path 0
     FwdParams outer{};      // path 1, outer passes
     FwdParams inner{};      // path 1, inner pass
+    int num_cu = 256;
+    bool use_row = false;   // register-resident kernel for N = 32 x NB
+    int row_nb = 0;
+    int lds_row = 0;
+    RowParams row{};
 };
 
 namespace {
@@ -437,6 +592,37 @@ fftconv_status build_device_tables(fftconv_plan_s* pl) {
         if (upload(pl, dro.data(), dro.size() * 4, &d) != hipSuccess) return FFTCONV_ERR_HIP;
         I.digrev_o = (const int*)d;
         O.digrev_o = (const int*)d;
+    }
+    const char* kenv = getenv("FFTCONV_KERNEL");
+    const bool generic_only = kenv && strcmp(kenv, "generic") == 0;
+    if (s.path == 0 && s.p == 2 && s.f[0] == 32 && (s.f[1] == 16 || s.f[1] == 32) &&
+        s.dtype != FFTCONV_F32 && !generic_only) {
+        const int NB = s.f[1];
+        const bool bf = s.dtype == FFTCONV_BF16;
+        std::vector<uint16_t> f1b = row_f1b(bf), i1a = row_i1a(), i2b = row_i2b(NB);
+        std::vector<uint8_t> f2a = row_f2a(NB);
+        std::vector<float> twf = row_twiddles(NB, false), twi = row_twiddles(NB, true);
+        RowParams& R = pl->row;
+        void* d = nullptr;
+        if (upload(pl, f1b.data(), f1b.size() * 2, &d) != hipSuccess) return FFTCONV_ERR_HIP;
+        R.f1b = d;
+        if (upload(pl, i1a.data(), i1a.size() * 2, &d) != hipSuccess) return FFTCONV_ERR_HIP;
+        R.i1a = d;
+        if (upload(pl, i2b.data(), i2b.size() * 2, &d) != hipSuccess) return FFTCONV_ERR_HIP;
+        R.i2b = d;
+        if (upload(pl, f2a.data(), f2a.size(), &d) != hipSuccess) return FFTCONV_ERR_HIP;
+        R.f2a = d;
+        if (upload(pl, twf.data(), twf.size() * 4, &d) != hipSuccess) return FFTCONV_ERR_HIP;
+        R.twf = (const float2*)d;
+        if (upload(pl, twi.data(), twi.size() * 4, &d) != hipSuccess) return FFTCONV_ERR_HIP;
+        R.twi = (const float2*)d;
+        R.N = (int)s.N;
+        pl->use_row = true;
+        pl->row_nb = NB;
+        pl->lds_row = (int)s.M * 16 + ((bf ? 8 : 4) + 4) * 64 * 16 + 4 * 16 * NB * 8;
+        hipDeviceProp_t prop;
+        if (hipGetDeviceProperties(&prop, pl->device) == hipSuccess && prop.multiProcessorCount > 0)
+            pl->num_cu = prop.multiProcessorCount;
     }
     return FFTCONV_OK;
 }
@@ -607,7 +793,25 @@ fftconv_status fftconv_forward(fftconv_plan_t plan, const void* u,
     hipStream_t st = (hipStream_t)stream;
     const int io = (int)s.dtype;
     hipError_t e;
-    if (s.path == 0) {
+    if (plan->use_row) {
+        RowParams R = plan->row;
+        R.B = (int)B;
+        R.H = (int)H;
+        // work items = (channel, batch range); about one workgroup per CU
+        const long long G = 2LL * plan->num_cu;   // two workgroups per CU
+        R.rwg = (int)B;
+        R.nbc = 1;
+        while ((long long)H * R.nbc < 2 * G && R.rwg > 4) {
+            R.rwg = (R.rwg + 1) / 2;
+            R.nbc = (int)((B + R.rwg - 1) / R.rwg);
+        }
+        const long long items = (long long)H * R.nbc;
+        R.grid = (int)(items < G ? items : G);
+        R.u = u;
+        R.y = y;
+        R.kf = k_f;
+        e = launch_row(io, plan->row_nb, R, plan->lds_row, st);
+    } else if (s.path == 0) {
         FwdParams P = plan->fused;
         P.rows = (long long)rows;
         P.H = (int)H;

@@ -98,6 +98,25 @@ struct SpecParams {
     void* kf;           // [H][M] alpha/beta
 };
 
+// Register-resident row kernel (N = 32 * NB, NB = 16 or 32, 16-bit I/O).
+struct RowParams {
+    int B, H, N;
+    int nbc;            // workgroups per channel
+    int rwg;            // batch entries per work item
+    int grid;           // persistent workgroups
+    const void* u;
+    void* y;
+    const void* kf;     // alpha/beta, [H][M] (4 x f16 each)
+    const void* f1b;    // first stage, B-operand tiles [hi 4][lo 4][64]
+    const void* i1a;    // last inverse stage, A-operand tiles [2][2][64]
+    const void* f2a;    // inner forward stage, A-operand tiles
+    const void* i2b;    // inner inverse stage, B-operand tiles
+    const float2* twf;  // per-lane forward twiddles
+    const float2* twi;  // per-lane inverse twiddles
+};
+hipError_t launch_row(int io, int nb, const RowParams& p, int lds_bytes,
+                      hipStream_t s);
+
 // Launchers (defined in fftconv_kernels.hip).  Return hipSuccess or the
 // launch error.
 hipError_t launch_fused(int io, const FwdParams& p, int lds_bytes,

@@ -1,0 +1,396 @@
+// Register-resident fused kernel for rows of N = 32 * NB (NB = 16 or 32):
+// the whole row -- load, four Monarch DFT stages, twiddles, the spectrum
+// product with mirror-bin pairing, store -- stays in one wavefront's
+// registers (page "FlashFFTConv: Efficient Convolutions for Long Sequences
+// with Tensor Cores", section 3.4, Algorithm 1: matrix products with the
+// twiddle and kernel multiplies done in the accumulators, register reuse of
+// appendix A.2).
+//
+// Packed row z[m] = u[2m] + i u[2m+1], m = NB*n_a + n_b (n_a < 16 nonzero:
+// the causal zero half is never touched).  Bins k = k_a + 32 k_b.
+//
+// The four matrix-core products alternate the role of the data so that the
+// index the next stage contracts is always the one held inside a lane:
+//   F1  C[n_b][(c,k_a)] = data(A: rows n_b, K n_a) x F32       (k_a -> lanes)
+//   F2  C[(k_b,c)][k_a] = F_NB x data(B: K n_b, cols k_a)      (k_b in-lane)
+//   I2  C[k_a][(c,n_b)] = data(A: rows k_a, K k_b) x F_NB^-1   (k_a in-lane)
+//   I1  C[(n_a,c)][n_b] = F32^-1 x data(B: K k_a, cols n_b)    (n_a < 16)
+// Real and imaginary parts of a point always sit in the same lane (the
+// complex index goes to rows, or to separate column tiles).  Lane x holds
+// k_a = x and its mirror 32-x (lane 0: 0 and 16), and the F_NB row order
+// keeps k_b and NB-1-k_b in one lane group, so bin k and bin -k meet in the
+// same lane; only the k_a = 0 column needs an LDS exchange.
+#include "fftconv_internal.h"
+
+namespace fftconv {
+
+typedef _Float16 rhalf8 __attribute__((ext_vector_type(8)));
+typedef __bf16 rbf8 __attribute__((ext_vector_type(8)));
+typedef float rfloat4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ uint32_t pk_f16(float a, float b) {
+    _Float16 h[2] = {(_Float16)a, (_Float16)b};
+    return __builtin_bit_cast(uint32_t, h);
+}
+
+template <int IO>
+__device__ __forceinline__ uint32_t pk_io(float a, float b) {
+    if (IO == IO_BF16) {
+        __bf16 h[2] = {(__bf16)a, (__bf16)b};
+        return __builtin_bit_cast(uint32_t, h);
+    }
+    return pk_f16(a, b);
+}
+
+__device__ __forceinline__ rfloat4 mma_f16(uint4 a, uint4 b, rfloat4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(
+        __builtin_bit_cast(rhalf8, a), __builtin_bit_cast(rhalf8, b), c, 0, 0, 0);
+}
+__device__ __forceinline__ rfloat4 mma_bf16(uint4 a, uint4 b, rfloat4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+        __builtin_bit_cast(rbf8, a), __builtin_bit_cast(rbf8, b), c, 0, 0, 0);
+}
+
+__device__ __forceinline__ float2 cmul2(float2 a, float2 b) {
+    return make_float2(a.x * b.x - a.y * b.y, a.x * b.y + a.y * b.x);
+}
+
+// a*z + b*conj(p)
+__device__ __forceinline__ float2 pair2(float4 ab, float2 z, float2 p) {
+    return make_float2(ab.x * z.x - ab.y * z.y + ab.z * p.x + ab.w * p.y,
+                       ab.x * z.y + ab.y * z.x + ab.w * p.x - ab.z * p.y);
+}
+
+__device__ __forceinline__ int rmid_perm(int slot, int n) {
+    return slot < (n >> 1) ? slot : (3 * n / 2 - 1 - slot);
+}
+__device__ __forceinline__ int kmap32(int kt, int x) {
+    return kt == 0 ? x : (x == 0 ? 16 : 32 - x);
+}
+// n_b held by row y of tile t.  For NB = 32 the n_b digit uses the same
+// mirror map as k_a, which makes the forward and inverse twiddle positions
+// of every lane coincide (one register table, conjugated for the inverse).
+template <int NB>
+__device__ __forceinline__ int nbmap(int t, int y) {
+    return NB == 32 ? kmap32(t, y) : 16 * t + y;
+}
+
+// Rows are processed channel-major: a work item is (channel h, a range of
+// batch entries); the spectrum coefficients of h are staged in LDS once per
+// item (lane-major, so every lane reads its own consecutive 16-byte entries)
+// and the next item's coefficients are prefetched into registers while the
+// current item runs.  Each wave walks its rows with a DEPTH-deep ring of
+// input loads in flight.  The grid is persistent (about one workgroup per
+// compute unit).  The inner-stage tables and the twiddles stay in
+// registers; the first/last stage tables are read from LDS.
+constexpr int kRowDepth = 2;
+
+typedef _Float16 rhalf2 __attribute__((ext_vector_type(2)));
+typedef __bf16 rbf2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ uint32_t pk2(float a, float b) {
+    rhalf2 v;
+    v.x = (_Float16)a;
+    v.y = (_Float16)b;
+    return __builtin_bit_cast(uint32_t, v);
+}
+template <int IO>
+__device__ __forceinline__ uint32_t pk2io(float a, float b) {
+    if (IO == IO_BF16) {
+        rbf2 v;
+        v.x = (__bf16)a;
+        v.y = (__bf16)b;
+        return __builtin_bit_cast(uint32_t, v);
+    }
+    return pk2(a, b);
+}
+
+template <int IO, int NB>
+__global__ void __launch_bounds__(256, 2) row_kernel(RowParams P) {
+    constexpr int M = 32 * NB;
+    constexpr int IT = NB / 16;    // n_b tiles
+    constexpr int MT2 = NB / 8;    // k_b slot tiles
+    constexpr int KS2 = NB / 16;   // K-steps over n_b / k_b
+    constexpr int NT = NB / 16;    // n_b tiles of the inverse
+    constexpr bool BF = (IO == IO_BF16);
+    constexpr int F1T = BF ? 8 : 4;
+    constexpr int E = M / 256;     // spectrum entries per thread
+    constexpr int D = kRowDepth;
+
+    extern __shared__ float4 s_ab[];                 // [NSLOT][64]
+    uint4* s_f1b = (uint4*)(s_ab + M);               // [F1T][64]
+    uint4* s_i1a = s_f1b + F1T * 64;                 // [4][64]
+    float2* s_scr = (float2*)(s_i1a + 4 * 64);       // [4 waves][16][NB]
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    // wave index as a scalar: branches on it stay uniform (scalar branches)
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int g = lane >> 4, x = lane & 15;
+    const int nitems = P.H * P.nbc;
+    const int G = gridDim.x;
+
+    for (int i = tid; i < F1T * 64; i += 256) s_f1b[i] = ((const uint4*)P.f1b)[i];
+    for (int i = tid; i < 4 * 64; i += 256) s_i1a[i] = ((const uint4*)P.i1a)[i];
+    uint4 f2a[MT2][KS2];
+    uint4 i2b[KS2][2 * NT];
+#pragma unroll
+    for (int mt = 0; mt < MT2; ++mt)
+#pragma unroll
+        for (int ks = 0; ks < KS2; ++ks)
+            f2a[mt][ks] = ((const uint4*)P.f2a)[(mt * KS2 + ks) * 64 + lane];
+#pragma unroll
+    for (int ks = 0; ks < KS2; ++ks)
+#pragma unroll
+        for (int jt = 0; jt < 2 * NT; ++jt)
+            i2b[ks][jt] = ((const uint4*)P.i2b)[(ks * 2 * NT + jt) * 64 + lane];
+    constexpr bool SYM = (NB == 32);
+    float2 twf[IT][2][4], twi[SYM ? 1 : 2][SYM ? 1 : NT][4];
+#pragma unroll
+    for (int it = 0; it < IT; ++it)
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                twf[it][kt][r] = P.twf[lane * (IT * 8) + (it * 2 + kt) * 4 + r];
+    if (!SYM) {
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    twi[SYM ? 0 : kt][SYM ? 0 : nt][r] = P.twi[lane * (NT * 8) + (kt * NT + nt) * 4 + r];
+    }
+
+    // rows of work item 'item' handled by this wave: b = b0 + wave + 4 r
+    auto item_rows = [&](int item, int& h, int& b0, int& n) {
+        h = item / P.nbc;
+        const int bc = item - h * P.nbc;
+        b0 = bc * P.rwg;
+        const int b1 = min(P.B, b0 + P.rwg);
+        const int first = b0 + wave;
+        n = first < b1 ? (b1 - first + 3) / 4 : 0;
+    };
+    auto load_row = [&](uint32_t (&dst)[IT][4], int h, int b) {
+        const uint32_t* u =
+            (const uint32_t*)P.u + ((long long)b * P.H + h) * (M / 2);
+#pragma unroll
+        for (int it = 0; it < IT; ++it)
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) dst[it][jj] = u[NB * (4 * g + jj) + nbmap<NB>(it, x)];
+    };
+
+    // ring slot k holds rows k, k+D, k+2D, ... of the current item, then
+    // row k of the next item: slots are fixed per row, so no register
+    // copies (and no full drains of the load queue) are needed
+    uint32_t ring[D][IT][4];
+    int ch = 0, cb0 = 0, cn = 0;
+    if (blockIdx.x < nitems) item_rows(blockIdx.x, ch, cb0, cn);
+#pragma unroll
+    for (int k = 0; k < D; ++k)
+        if (k < cn) load_row(ring[k], ch, cb0 + wave + 4 * k);
+    uint2 abn[E];
+    if (blockIdx.x < nitems) {
+        const uint2* kf = (const uint2*)P.kf + (long long)(blockIdx.x / P.nbc) * M;
+#pragma unroll
+        for (int q = 0; q < E; ++q) abn[q] = kf[tid + 256 * q];
+    }
+    // mirror exchange of the k_a = 0 column: every lane writes its column-0
+    // bins and reads back bin -k_b of the same column (used by lanes x = 0)
+    // layout [k_b][x]: the 16 lanes of a group touch consecutive words
+    float2* scr = s_scr + wave * 16 * NB + x;
+
+    for (int item = blockIdx.x; item < nitems; item += G) {
+        int h, b0, n;
+        item_rows(item, h, b0, n);
+        int nh = 0, nb0 = 0, nn = 0;
+        if (item + G < nitems) item_rows(item + G, nh, nb0, nn);
+        __syncthreads();   // every wave is done with the previous item's table
+#pragma unroll
+        for (int q = 0; q < E; ++q) {
+            // bin (k_a, k_b) at position NB*k_a + k_b -> its lane and slot
+            const int pos = tid + 256 * q;
+            const int ka = pos / NB, kb = pos - ka * NB;
+            const int kt = ka < 16 ? 0 : 1;
+            const int xx = ka < 16 ? ka : (ka == 16 ? 0 : 32 - ka);
+            const int sl = kb < NB / 2 ? kb : (3 * NB / 2 - 1 - kb);
+            const int mt = sl >> 3, gg = (sl >> 1) & 3, e = sl & 1;
+            const _Float16* hv = (const _Float16*)&abn[q];
+            s_ab[((kt * MT2 + mt) * 2 + e) * 64 + gg * 16 + xx] =
+                make_float4((float)hv[0], (float)hv[1], (float)hv[2], (float)hv[3]);
+        }
+        __syncthreads();
+        if (item + G < nitems) {
+            const uint2* kf = (const uint2*)P.kf + (long long)((item + G) / P.nbc) * M;
+#pragma unroll
+            for (int q = 0; q < E; ++q) abn[q] = kf[tid + 256 * q];
+        }
+        auto row_body = [&](uint32_t (&cur)[IT][4], const long long row) {
+            // ---- F1: 32-point DFT over n_a (16 nonzero), k_a to the lanes
+            uint4 b2[KS2][2];
+#pragma unroll
+            for (int it = 0; it < IT; ++it) {
+                const uint4 a = make_uint4(cur[it][0], cur[it][1], cur[it][2], cur[it][3]);
+                rfloat4 c1[4];
+#pragma unroll
+                for (int jt = 0; jt < 4; ++jt) {
+                    rfloat4 acc = {0.f, 0.f, 0.f, 0.f};
+                    if (BF) {
+                        acc = mma_bf16(a, s_f1b[jt * 64 + lane], acc);
+                        acc = mma_bf16(a, s_f1b[(4 + jt) * 64 + lane], acc);
+                    } else {
+                        acc = mma_f16(a, s_f1b[jt * 64 + lane], acc);
+                    }
+                    c1[jt] = acc;
+                }
+                // twiddle W_M^{k_a n_b}; pack as F2's B operand (K = n_b)
+#pragma unroll
+                for (int kt = 0; kt < 2; ++kt) {
+                    uint32_t w[4];
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const float2 v = cmul2(make_float2(c1[2 * kt][r], c1[2 * kt + 1][r]),
+                                               twf[it][kt][r]);
+                        w[r] = pk2(v.x, v.y);
+                    }
+                    b2[it][kt] = make_uint4(w[0], w[1], w[2], w[3]);
+                }
+            }
+            // ---- F2: NB-point DFT over n_b, k_b in-lane (rows permuted)
+            float2 z[2][MT2][2];
+#pragma unroll
+            for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+                for (int mt = 0; mt < MT2; ++mt) {
+                    rfloat4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int ks = 0; ks < KS2; ++ks) acc = mma_f16(f2a[mt][ks], b2[ks][kt], acc);
+                    z[kt][mt][0] = make_float2(acc[0], acc[1]);
+                    z[kt][mt][1] = make_float2(acc[2], acc[3]);
+                }
+            // ---- mirror partner of every bin
+            // column 0 (k_a = 0, lane x = 0) pairs k_b with -k_b (mod NB),
+            // which another lane group holds: exchange through LDS
+#pragma unroll
+            for (int mt = 0; mt < MT2; ++mt)
+#pragma unroll
+                for (int e = 0; e < 2; ++e)
+                    scr[16 * rmid_perm(8 * mt + 2 * g + e, NB)] = z[0][mt][e];
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            float2 zq[MT2][2];
+#pragma unroll
+            for (int mt = 0; mt < MT2; ++mt)
+#pragma unroll
+                for (int e = 0; e < 2; ++e) {
+                    const int kb = rmid_perm(8 * mt + 2 * g + e, NB);
+                    zq[mt][e] = scr[16 * ((NB - kb) & (NB - 1))];
+                }
+            // ---- spectrum product: Z'[k] = alpha Z[k] + beta conj(Z[-k])
+            // partner of (k_a, k_b) for k_a != 0: (-k_a, NB-1-k_b), i.e. the
+            // other column tile and M-tile mt +- MT2/2; lane 0's second
+            // column (k_a = 16) is its own mirror
+            const bool l0 = (x == 0);
+            uint4 a2[2][KS2];
+#pragma unroll
+            for (int kt = 0; kt < 2; ++kt) {
+                float2 zp[MT2][2];
+#pragma unroll
+                for (int mt = 0; mt < MT2; ++mt)
+#pragma unroll
+                    for (int e = 0; e < 2; ++e) {
+                        const int pm = (mt + MT2 / 2) % MT2;
+                        const float4 ab = s_ab[((kt * MT2 + mt) * 2 + e) * 64 + lane];
+                        float2 p;
+                        if (kt == 0) {
+                            p = l0 ? zq[mt][e] : z[1][pm][e];
+                        } else {
+                            p = l0 ? z[1][pm][e] : z[0][pm][e];
+                        }
+                        zp[mt][e] = pair2(ab, z[kt][mt][e], p);
+                    }
+                // I2's A operand (K = k_b in accumulator order)
+#pragma unroll
+                for (int ks = 0; ks < KS2; ++ks) {
+                    uint32_t w[4];
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const float2 v = zp[2 * ks + (q >> 1)][q & 1];
+                        w[q] = pk2(v.x, v.y);
+                    }
+                    a2[kt][ks] = make_uint4(w[0], w[1], w[2], w[3]);
+                }
+            }
+            // ---- I2: inverse NB-point DFT over k_b (data as A), k_a in-lane
+            uint4 b1v[2][NT];
+#pragma unroll
+            for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+                for (int nt = 0; nt < NT; ++nt) {
+                    rfloat4 re = {0.f, 0.f, 0.f, 0.f}, im = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int ks = 0; ks < KS2; ++ks) {
+                        re = mma_f16(a2[kt][ks], i2b[ks][2 * nt], re);
+                        im = mma_f16(a2[kt][ks], i2b[ks][2 * nt + 1], im);
+                    }
+                    // conj twiddle W_M^{-k_a n_b}; pack as I1's B operand
+                    uint32_t w[4];
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        float2 t;
+                        if (SYM) {
+                            t = twf[kt][nt][r];
+                            t.y = -t.y;
+                        } else {
+                            t = twi[SYM ? 0 : kt][SYM ? 0 : nt][r];
+                        }
+                        const float2 v = cmul2(make_float2(re[r], im[r]), t);
+                        w[r] = pk2(v.x, v.y);
+                    }
+                    b1v[kt][nt] = make_uint4(w[0], w[1], w[2], w[3]);
+                }
+            // ---- I1: inverse 32-point DFT over k_a, only n_a < 16 (t < N)
+            uint32_t* yrow = (uint32_t*)P.y + row * (long long)(M / 2);
+#pragma unroll
+            for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+                for (int nt = 0; nt < NT; ++nt) {
+                    rfloat4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int ks = 0; ks < 2; ++ks)
+                        acc = mma_f16(s_i1a[(mt * 2 + ks) * 64 + lane], b1v[ks][nt], acc);
+#pragma unroll
+                    for (int e = 0; e < 2; ++e) {
+                        const int na = 8 * mt + 2 * g + e;
+                        yrow[NB * na + nbmap<NB>(nt, x)] = pk2io<IO>(acc[2 * e], acc[2 * e + 1]);
+                    }
+                }
+        };
+        for (int r0 = 0; r0 < n; r0 += D) {
+#pragma unroll
+            for (int k = 0; k < D; ++k) {
+                const int r = r0 + k;
+                if (r < n) {
+                    row_body(ring[k], (long long)(b0 + wave + 4 * r) * P.H + h);
+                    if (r + D < n) load_row(ring[k], h, b0 + wave + 4 * (r + D));
+                    else if (k < nn) load_row(ring[k], nh, nb0 + wave + 4 * k);
+                }
+            }
+        }
+    }
+}
+
+hipError_t launch_row(int io, int nb, const RowParams& p, int lds, hipStream_t s) {
+    const dim3 grid((unsigned)p.grid), blk(256);
+    if (io == IO_BF16) {
+        if (nb == 32) hipLaunchKernelGGL((row_kernel<IO_BF16, 32>), grid, blk, lds, s, p);
+        else hipLaunchKernelGGL((row_kernel<IO_BF16, 16>), grid, blk, lds, s, p);
+    } else {
+        if (nb == 32) hipLaunchKernelGGL((row_kernel<IO_F16, 32>), grid, blk, lds, s, p);
+        else hipLaunchKernelGGL((row_kernel<IO_F16, 16>), grid, blk, lds, s, p);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace fftconv

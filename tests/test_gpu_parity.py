@@ -53,3 +53,26 @@ def test_length_sweep(N, dtype):
     err, _, _ = parity(w)
     _say("sweep", N, dtype, "rel_l2", err)
     assert err < TOL[dtype]
+
+
+@pytest.mark.parametrize("N,dtype", [(512, "bf16"), (1024, "bf16"),
+                                     (1024, "f16")])
+def test_generic_kernel_at_row_lengths(N, dtype, monkeypatch):
+    # lengths 32*16 and 32*32 normally run the register-resident row
+    # kernel; the LDS-staged kernel must agree with the oracle there too
+    monkeypatch.setenv("FFTCONV_KERNEL", "generic")
+    w = inputs.Workload("generic", 60 + N.bit_length(), 4, 7, N, dtype,
+                        "normal", "decay", "generic kernel")
+    err, _, _ = parity(w)
+    _say("generic", N, dtype, "rel_l2", err)
+    assert err < TOL[dtype]
+
+
+@pytest.mark.parametrize("B,H", [(1, 1), (3, 2), (5, 9), (64, 3), (33, 4)])
+def test_row_kernel_batch_shapes(B, H):
+    # batch sizes that leave workgroups and waves partly empty
+    w = inputs.Workload("rowshape", 70 + B, B, H, 1024, "bf16", "normal",
+                        "decay", "row kernel shapes")
+    err, _, _ = parity(w)
+    _say("row shapes", B, H, "rel_l2", err)
+    assert err < TOL["bf16"]
