@@ -417,10 +417,11 @@ std::vector<uint16_t> row_i2b(int NB) {
     return out;
 }
 
-// Per-lane twiddles W_M^{+-k_a n_b} at the positions each lane holds.
-std::vector<float> row_twiddles(int NB, bool inverse) {
+// Per-lane twiddles W_M^{+-k_a n_b} at the positions each lane holds,
+// as packed f16 (re, im) pairs.
+std::vector<uint16_t> row_twiddles(int NB, bool inverse) {
     const int M = 32 * NB, IT = NB / 16;
-    std::vector<float> out((size_t)64 * IT * 8 * 2);
+    std::vector<uint16_t> out((size_t)64 * IT * 8 * 2);
     for (int lane = 0; lane < 64; ++lane) {
         const int g = lane >> 4, x = lane & 15;
         for (int a = 0; a < IT; ++a)          // fwd: it;   inv: nt
@@ -438,8 +439,8 @@ std::vector<float> row_twiddles(int NB, bool inverse) {
                     }
                     const double ang = (inverse ? 2.0 : -2.0) * M_PI *
                                        (double)(((long long)ka * nb) % M) / (double)M;
-                    out[(size_t)idx * 2] = (float)cos(ang);
-                    out[(size_t)idx * 2 + 1] = (float)sin(ang);
+                    out[(size_t)idx * 2] = f32_to_f16_bits((float)cos(ang));
+                    out[(size_t)idx * 2 + 1] = f32_to_f16_bits((float)sin(ang));
                 }
     }
     return out;
@@ -601,7 +602,7 @@ fftconv_status build_device_tables(fftconv_plan_s* pl) {
         const bool bf = s.dtype == FFTCONV_BF16;
         std::vector<uint16_t> f1b = row_f1b(bf), i1a = row_i1a(), i2b = row_i2b(NB);
         std::vector<uint8_t> f2a = row_f2a(NB);
-        std::vector<float> twf = row_twiddles(NB, false), twi = row_twiddles(NB, true);
+        std::vector<uint16_t> twf = row_twiddles(NB, false), twi = row_twiddles(NB, true);
         RowParams& R = pl->row;
         void* d = nullptr;
         if (upload(pl, f1b.data(), f1b.size() * 2, &d) != hipSuccess) return FFTCONV_ERR_HIP;
@@ -612,14 +613,14 @@ fftconv_status build_device_tables(fftconv_plan_s* pl) {
         R.i2b = d;
         if (upload(pl, f2a.data(), f2a.size(), &d) != hipSuccess) return FFTCONV_ERR_HIP;
         R.f2a = d;
-        if (upload(pl, twf.data(), twf.size() * 4, &d) != hipSuccess) return FFTCONV_ERR_HIP;
-        R.twf = (const float2*)d;
-        if (upload(pl, twi.data(), twi.size() * 4, &d) != hipSuccess) return FFTCONV_ERR_HIP;
-        R.twi = (const float2*)d;
+        if (upload(pl, twf.data(), twf.size() * 2, &d) != hipSuccess) return FFTCONV_ERR_HIP;
+        R.twf = (const uint32_t*)d;
+        if (upload(pl, twi.data(), twi.size() * 2, &d) != hipSuccess) return FFTCONV_ERR_HIP;
+        R.twi = (const uint32_t*)d;
         R.N = (int)s.N;
         pl->use_row = true;
         pl->row_nb = NB;
-        pl->lds_row = (int)s.M * 16 + ((bf ? 8 : 4) + 4) * 64 * 16 + 4 * 16 * NB * 8;
+        pl->lds_row = ((bf ? 8 : 4) + 4) * 64 * 16 + (int)s.M * 8 + 4 * 16 * NB * 4;
         hipDeviceProp_t prop;
         if (hipGetDeviceProperties(&prop, pl->device) == hipSuccess && prop.multiProcessorCount > 0)
             pl->num_cu = prop.multiProcessorCount;

@@ -111,8 +111,8 @@ struct RowParams {
     const void* i1a;    // last inverse stage, A-operand tiles [2][2][64]
     const void* f2a;    // inner forward stage, A-operand tiles
     const void* i2b;    // inner inverse stage, B-operand tiles
-    const float2* twf;  // per-lane forward twiddles
-    const float2* twi;  // per-lane inverse twiddles
+    const uint32_t* twf;  // per-lane forward twiddles (packed f16 re, im)
+    const uint32_t* twi;  // per-lane inverse twiddles (packed f16 re, im)
 };
 hipError_t launch_row(int io, int nb, const RowParams& p, int lds_bytes,
                       hipStream_t s);

@@ -92,7 +92,11 @@ __device__ __forceinline__ uint32_t pk2(float a, float b) {
     rhalf2 v;
     v.x = (_Float16)a;
     v.y = (_Float16)b;
-    return __builtin_bit_cast(uint32_t, v);
+    uint32_t r = __builtin_bit_cast(uint32_t, v);
+    // opaque to the optimiser: keeps the single packed conversion instead of
+    // two scalar ones feeding half-selects of the following packed ops
+    asm("" : "+v"(r));
+    return r;
 }
 template <int IO>
 __device__ __forceinline__ uint32_t pk2io(float a, float b) {
@@ -103,6 +107,33 @@ __device__ __forceinline__ uint32_t pk2io(float a, float b) {
         return __builtin_bit_cast(uint32_t, v);
     }
     return pk2(a, b);
+}
+
+// Packed-f16 complex arithmetic (re in the low half, im in the high half).
+// The operands of the next matrix product are f16 anyway; doing the twiddle
+// and spectrum products in packed f16 halves their vector-ALU cost.
+__device__ __forceinline__ rhalf2 as_h2(uint32_t v) { return __builtin_bit_cast(rhalf2, v); }
+__device__ __forceinline__ uint32_t as_u32(rhalf2 v) { return __builtin_bit_cast(uint32_t, v); }
+// d * t
+__device__ __forceinline__ rhalf2 hmul(rhalf2 d, rhalf2 t) {
+    const rhalf2 dxx = {d.x, d.x}, dyy = {d.y, d.y};
+    const rhalf2 tn = {-t.y, t.x};
+    return __builtin_elementwise_fma(dyy, tn, dxx * t);
+}
+// d * conj(t)
+__device__ __forceinline__ rhalf2 hmulc(rhalf2 d, rhalf2 t) {
+    const rhalf2 dxx = {d.x, d.x}, dyy = {d.y, d.y};
+    const rhalf2 tc = {t.x, -t.y}, tn = {t.y, t.x};
+    return __builtin_elementwise_fma(dyy, tn, dxx * tc);
+}
+// a*z + b*conj(p)
+__device__ __forceinline__ rhalf2 hpair(rhalf2 a, rhalf2 z, rhalf2 b, rhalf2 p) {
+    const rhalf2 zxx = {z.x, z.x}, zyy = {z.y, z.y};
+    const rhalf2 pxx = {p.x, p.x}, pyy = {p.y, p.y};
+    const rhalf2 an = {-a.y, a.x}, bn = {b.y, -b.x};
+    rhalf2 r = __builtin_elementwise_fma(zyy, an, zxx * a);
+    r = __builtin_elementwise_fma(pxx, b, r);
+    return __builtin_elementwise_fma(pyy, bn, r);
 }
 
 template <int IO, int NB>
@@ -117,10 +148,11 @@ __global__ void __launch_bounds__(256, 2) row_kernel(RowParams P) {
     constexpr int E = M / 256;     // spectrum entries per thread
     constexpr int D = kRowDepth;
 
-    extern __shared__ float4 s_ab[];                 // [NSLOT][64]
-    uint4* s_f1b = (uint4*)(s_ab + M);               // [F1T][64]
+    extern __shared__ uint4 s_lds[];
+    uint4* s_f1b = s_lds;                            // [F1T][64]
     uint4* s_i1a = s_f1b + F1T * 64;                 // [4][64]
-    float2* s_scr = (float2*)(s_i1a + 4 * 64);       // [4 waves][16][NB]
+    uint2* s_ab = (uint2*)(s_i1a + 4 * 64);          // [bins per lane][64]
+    uint32_t* s_scr = (uint32_t*)(s_ab + M);         // [4 waves][NB][16]
 
     const int tid = threadIdx.x, lane = tid & 63;
     // wave index as a scalar: branches on it stay uniform (scalar branches)
@@ -144,7 +176,7 @@ __global__ void __launch_bounds__(256, 2) row_kernel(RowParams P) {
         for (int jt = 0; jt < 2 * NT; ++jt)
             i2b[ks][jt] = ((const uint4*)P.i2b)[(ks * 2 * NT + jt) * 64 + lane];
     constexpr bool SYM = (NB == 32);
-    float2 twf[IT][2][4], twi[SYM ? 1 : 2][SYM ? 1 : NT][4];
+    uint32_t twf[IT][2][4], twi[SYM ? 1 : 2][SYM ? 1 : NT][4];
 #pragma unroll
     for (int it = 0; it < IT; ++it)
 #pragma unroll
@@ -198,7 +230,7 @@ __global__ void __launch_bounds__(256, 2) row_kernel(RowParams P) {
     // mirror exchange of the k_a = 0 column: every lane writes its column-0
     // bins and reads back bin -k_b of the same column (used by lanes x = 0)
     // layout [k_b][x]: the 16 lanes of a group touch consecutive words
-    float2* scr = s_scr + wave * 16 * NB + x;
+    uint32_t* scr = s_scr + wave * 16 * NB + x;
 
     for (int item = blockIdx.x; item < nitems; item += G) {
         int h, b0, n;
@@ -215,9 +247,7 @@ __global__ void __launch_bounds__(256, 2) row_kernel(RowParams P) {
             const int xx = ka < 16 ? ka : (ka == 16 ? 0 : 32 - ka);
             const int sl = kb < NB / 2 ? kb : (3 * NB / 2 - 1 - kb);
             const int mt = sl >> 3, gg = (sl >> 1) & 3, e = sl & 1;
-            const _Float16* hv = (const _Float16*)&abn[q];
-            s_ab[((kt * MT2 + mt) * 2 + e) * 64 + gg * 16 + xx] =
-                make_float4((float)hv[0], (float)hv[1], (float)hv[2], (float)hv[3]);
+            s_ab[((kt * MT2 + mt) * 2 + e) * 64 + gg * 16 + xx] = abn[q];
         }
         __syncthreads();
         if (item + G < nitems) {
@@ -243,21 +273,19 @@ __global__ void __launch_bounds__(256, 2) row_kernel(RowParams P) {
                     }
                     c1[jt] = acc;
                 }
-                // twiddle W_M^{k_a n_b}; pack as F2's B operand (K = n_b)
+                // twiddle W_M^{k_a n_b} (packed f16); F2's B operand (K = n_b)
 #pragma unroll
                 for (int kt = 0; kt < 2; ++kt) {
                     uint32_t w[4];
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        const float2 v = cmul2(make_float2(c1[2 * kt][r], c1[2 * kt + 1][r]),
-                                               twf[it][kt][r]);
-                        w[r] = pk2(v.x, v.y);
-                    }
+                    for (int r = 0; r < 4; ++r)
+                        w[r] = as_u32(hmul(as_h2(pk2(c1[2 * kt][r], c1[2 * kt + 1][r])),
+                                           as_h2(twf[it][kt][r])));
                     b2[it][kt] = make_uint4(w[0], w[1], w[2], w[3]);
                 }
             }
             // ---- F2: NB-point DFT over n_b, k_b in-lane (rows permuted)
-            float2 z[2][MT2][2];
+            uint32_t z[2][MT2][2];
 #pragma unroll
             for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
@@ -265,8 +293,8 @@ __global__ void __launch_bounds__(256, 2) row_kernel(RowParams P) {
                     rfloat4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                     for (int ks = 0; ks < KS2; ++ks) acc = mma_f16(f2a[mt][ks], b2[ks][kt], acc);
-                    z[kt][mt][0] = make_float2(acc[0], acc[1]);
-                    z[kt][mt][1] = make_float2(acc[2], acc[3]);
+                    z[kt][mt][0] = pk2(acc[0], acc[1]);
+                    z[kt][mt][1] = pk2(acc[2], acc[3]);
                 }
             // ---- mirror partner of every bin
             // column 0 (k_a = 0, lane x = 0) pairs k_b with -k_b (mod NB),
@@ -279,7 +307,7 @@ __global__ void __launch_bounds__(256, 2) row_kernel(RowParams P) {
             __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
             __builtin_amdgcn_wave_barrier();
             __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-            float2 zq[MT2][2];
+            uint32_t zq[MT2][2];
 #pragma unroll
             for (int mt = 0; mt < MT2; ++mt)
 #pragma unroll
@@ -295,32 +323,27 @@ __global__ void __launch_bounds__(256, 2) row_kernel(RowParams P) {
             uint4 a2[2][KS2];
 #pragma unroll
             for (int kt = 0; kt < 2; ++kt) {
-                float2 zp[MT2][2];
+                uint32_t zp[MT2][2];
 #pragma unroll
                 for (int mt = 0; mt < MT2; ++mt)
 #pragma unroll
                     for (int e = 0; e < 2; ++e) {
                         const int pm = (mt + MT2 / 2) % MT2;
-                        const float4 ab = s_ab[((kt * MT2 + mt) * 2 + e) * 64 + lane];
-                        float2 p;
+                        const uint2 ab = s_ab[((kt * MT2 + mt) * 2 + e) * 64 + lane];
+                        uint32_t p;
                         if (kt == 0) {
                             p = l0 ? zq[mt][e] : z[1][pm][e];
                         } else {
                             p = l0 ? z[1][pm][e] : z[0][pm][e];
                         }
-                        zp[mt][e] = pair2(ab, z[kt][mt][e], p);
+                        zp[mt][e] = as_u32(hpair(as_h2(ab.x), as_h2(z[kt][mt][e]),
+                                                 as_h2(ab.y), as_h2(p)));
                     }
                 // I2's A operand (K = k_b in accumulator order)
 #pragma unroll
-                for (int ks = 0; ks < KS2; ++ks) {
-                    uint32_t w[4];
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        const float2 v = zp[2 * ks + (q >> 1)][q & 1];
-                        w[q] = pk2(v.x, v.y);
-                    }
-                    a2[kt][ks] = make_uint4(w[0], w[1], w[2], w[3]);
-                }
+                for (int ks = 0; ks < KS2; ++ks)
+                    a2[kt][ks] = make_uint4(zp[2 * ks][0], zp[2 * ks][1],
+                                            zp[2 * ks + 1][0], zp[2 * ks + 1][1]);
             }
             // ---- I2: inverse NB-point DFT over k_b (data as A), k_a in-lane
             uint4 b1v[2][NT];
@@ -338,15 +361,9 @@ __global__ void __launch_bounds__(256, 2) row_kernel(RowParams P) {
                     uint32_t w[4];
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
-                        float2 t;
-                        if (SYM) {
-                            t = twf[kt][nt][r];
-                            t.y = -t.y;
-                        } else {
-                            t = twi[SYM ? 0 : kt][SYM ? 0 : nt][r];
-                        }
-                        const float2 v = cmul2(make_float2(re[r], im[r]), t);
-                        w[r] = pk2(v.x, v.y);
+                        const rhalf2 v = as_h2(pk2(re[r], im[r]));
+                        w[r] = SYM ? as_u32(hmulc(v, as_h2(twf[kt][nt][r])))
+                                   : as_u32(hmul(v, as_h2(twi[SYM ? 0 : kt][SYM ? 0 : nt][r])));
                     }
                     b1v[kt][nt] = make_uint4(w[0], w[1], w[2], w[3]);
                 }
