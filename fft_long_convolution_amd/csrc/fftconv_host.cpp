@@ -172,6 +172,18 @@ double mfma_flops_per_row(const Shape& s) {
     return f;
 }
 
+bool generic_forced() {
+    const char* kenv = getenv("FFTCONV_KERNEL");
+    return kenv && strcmp(kenv, "generic") == 0;
+}
+
+// The register-resident kernel covers N = 32 x NB (NB = 16, 32) with 16-bit
+// I/O; FFTCONV_KERNEL=generic keeps such plans on the LDS-staged kernel.
+bool row_kernel_applies(const Shape& s) {
+    return s.path == 0 && s.p == 2 && s.f[0] == 32 && (s.f[1] == 16 || s.f[1] == 32) &&
+           s.dtype != FFTCONV_F32 && !generic_forced();
+}
+
 void fill_info(const Shape& s, fftconv_plan_info* info) {
     memset(info, 0, sizeof(*info));
     info->N = s.N;
@@ -184,6 +196,7 @@ void fill_info(const Shape& s, fftconv_plan_info* info) {
     info->spectrum_bytes_per_channel = s.M * kf_entry_bytes(s.dtype);
     info->workspace_bytes_per_row = s.path ? s.M * 8 : 0;
     info->mfma_flops_per_row = mfma_flops_per_row(s);
+    info->kernel_variant = s.path ? 2 : (row_kernel_applies(s) ? 1 : 0);
 }
 
 // ------------------------------------------------------- table construction
@@ -594,10 +607,7 @@ fftconv_status build_device_tables(fftconv_plan_s* pl) {
         I.digrev_o = (const int*)d;
         O.digrev_o = (const int*)d;
     }
-    const char* kenv = getenv("FFTCONV_KERNEL");
-    const bool generic_only = kenv && strcmp(kenv, "generic") == 0;
-    if (s.path == 0 && s.p == 2 && s.f[0] == 32 && (s.f[1] == 16 || s.f[1] == 32) &&
-        s.dtype != FFTCONV_F32 && !generic_only) {
+    if (row_kernel_applies(s)) {
         const int NB = s.f[1];
         const bool bf = s.dtype == FFTCONV_BF16;
         std::vector<uint16_t> f1b = row_f1b(bf), i1a = row_i1a(), i2b = row_i2b(NB);

@@ -33,7 +33,8 @@ class PlanInfo(ctypes.Structure):
                 ("dtype", ctypes.c_int),
                 ("spectrum_bytes_per_channel", ctypes.c_size_t),
                 ("workspace_bytes_per_row", ctypes.c_size_t),
-                ("mfma_flops_per_row", ctypes.c_double)]
+                ("mfma_flops_per_row", ctypes.c_double),
+                ("kernel_variant", ctypes.c_int)]
 
     def as_dict(self) -> dict:
         return {"N": self.N, "M": self.M, "order": self.order,
@@ -43,7 +44,10 @@ class PlanInfo(ctypes.Structure):
                 "dtype": {v: k for k, v in DTYPES.items()}[self.dtype],
                 "spectrum_bytes_per_channel": self.spectrum_bytes_per_channel,
                 "workspace_bytes_per_row": self.workspace_bytes_per_row,
-                "mfma_flops_per_row": self.mfma_flops_per_row}
+                "mfma_flops_per_row": self.mfma_flops_per_row,
+                "kernel": {0: "fused_kernel", 1: "row_kernel",
+                           2: "outer_fwd_kernel+inner_kernel+outer_inv_kernel"
+                           }[self.kernel_variant]}
 
 
 def lib() -> ctypes.CDLL:

@@ -72,6 +72,10 @@ typedef struct fftconv_plan_info {
     size_t spectrum_bytes_per_channel;
     size_t workspace_bytes_per_row;
     double mfma_flops_per_row; /* algorithmic matrix-core flops per row     */
+    int kernel_variant;       /* 0 = LDS-staged fused kernel,
+                                 1 = register-resident row kernel (N = 32*16
+                                     or 32*32, 16-bit I/O),
+                                 2 = three-pass (outer, inner, outer)       */
 } fftconv_plan_info;
 
 /* Create a plan for length N, Monarch order p and I/O dtype.

@@ -76,3 +76,75 @@ def test_row_kernel_batch_shapes(B, H):
     err, _, _ = parity(w)
     _say("row shapes", B, H, "rel_l2", err)
     assert err < TOL["bf16"]
+
+
+def _plan_and_spectrum(N, dtype, H=3):
+    import torch
+    from fft_long_convolution_amd.fftconv import FFTConv
+    conv = FFTConv(N, dtype=dtype)
+    k = torch.from_numpy(inputs.kernel_rows(
+        inputs.Workload("edge", 90, 1, H, N, dtype, "normal", "decay", ""))).cuda()
+    return conv, conv.kernel_spectrum(k)
+
+
+def test_empty_batch_is_a_noop():
+    import torch
+    conv, kf = _plan_and_spectrum(1024, "bf16")
+    u = torch.empty(0, 3, 1024, dtype=torch.bfloat16, device="cuda")
+    y = conv.forward(u, kf)
+    torch.cuda.synchronize()
+    assert y.shape == (0, 3, 1024)
+
+
+def test_error_paths():
+    import torch
+    from fft_long_convolution_amd import fftconv as fc
+    conv, kf = _plan_and_spectrum(1024, "bf16")
+    L = fc.lib()
+    u = torch.randn(2, 3, 1024, device="cuda").to(torch.bfloat16)
+    y = torch.empty_like(u)
+    s = None
+    # wrong N
+    assert L.fftconv_forward(conv._plan, u.data_ptr(), kf.data_ptr(),
+                             y.data_ptr(), 2, 3, 512, None, 0, s) == 1
+    # misaligned input pointer
+    assert L.fftconv_forward(conv._plan, u.data_ptr() + 2, kf.data_ptr(),
+                             y.data_ptr(), 2, 3, 1024, None, 0, s) == 3
+    # output overlapping the input
+    assert L.fftconv_forward(conv._plan, u.data_ptr(), kf.data_ptr(),
+                             u.data_ptr() + 1024, 2, 3, 1024, None, 0, s) == 1
+    # null spectrum
+    assert L.fftconv_forward(conv._plan, u.data_ptr(), None, y.data_ptr(),
+                             2, 3, 1024, None, 0, s) == 1
+    # multi-pass plan with a missing / short workspace
+    conv2, kf2 = _plan_and_spectrum(32768, "bf16", H=1)
+    u2 = torch.randn(1, 1, 32768, device="cuda").to(torch.bfloat16)
+    y2 = torch.empty_like(u2)
+    need = conv2.workspace_bytes(1, 1)
+    assert need == 32768 * 8
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    assert L.fftconv_forward(conv2._plan, u2.data_ptr(), kf2.data_ptr(),
+                             y2.data_ptr(), 1, 1, 32768, None, 0, s) == 4
+    assert L.fftconv_forward(conv2._plan, u2.data_ptr(), kf2.data_ptr(),
+                             y2.data_ptr(), 1, 1, 32768, ws.data_ptr(),
+                             need - 16, s) == 4
+    assert L.fftconv_forward(conv2._plan, u2.data_ptr(), kf2.data_ptr(),
+                             y2.data_ptr(), 1, 1, 32768, ws.data_ptr(),
+                             need, s) == 0
+    torch.cuda.synchronize()
+    with pytest.raises(fc.FFTConvError):
+        fc.FFTConv(1000, dtype="bf16")
+
+
+@pytest.mark.parametrize("N", [1024, 8192, 65536])
+def test_deterministic_and_stream(N):
+    import torch
+    conv, kf = _plan_and_spectrum(N, "bf16")
+    u = torch.randn(4, 3, N, device="cuda").to(torch.bfloat16)
+    y1 = conv.forward(u, kf)
+    st = torch.cuda.Stream()
+    st.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(st):
+        y2 = conv.forward(u, kf)
+    torch.cuda.synchronize()
+    assert torch.equal(y1.view(torch.int16), y2.view(torch.int16))
