@@ -471,6 +471,7 @@ struct fftconv_plan_s {
     FwdParams outer{};      // path 1, outer passes
     FwdParams inner{};      // path 1, inner pass
     int num_cu = 256;
+    long long row_max_channels = 1;   // channels whose spectra fit the row LDS
     bool use_row = false;   // register-resident kernel for N = 32 x NB
     int row_nb = 0;
     int lds_row = 0;
@@ -630,7 +631,11 @@ fftconv_status build_device_tables(fftconv_plan_s* pl) {
         R.N = (int)s.N;
         pl->use_row = true;
         pl->row_nb = NB;
-        pl->lds_row = ((bf ? 8 : 4) + 4) * 64 * 16 + (int)s.M * 8 + 4 * 16 * NB * 4;
+        // fixed part: first/last stage tables + exchange scratch; the rest
+        // of a 64 KB budget (two workgroups per CU) holds spectra
+        const int fixed = ((bf ? 8 : 4) + 4) * 64 * 16 + 4 * 16 * NB * 4;
+        pl->row_max_channels = (64 * 1024 - fixed) / ((int)s.M * 8);
+        pl->lds_row = fixed + (int)pl->row_max_channels * (int)s.M * 8;
         hipDeviceProp_t prop;
         if (hipGetDeviceProperties(&prop, pl->device) == hipSuccess && prop.multiProcessorCount > 0)
             pl->num_cu = prop.multiProcessorCount;
@@ -808,16 +813,15 @@ fftconv_status fftconv_forward(fftconv_plan_t plan, const void* u,
         RowParams R = plan->row;
         R.B = (int)B;
         R.H = (int)H;
-        // work items = (channel, batch range); about one workgroup per CU
-        const long long G = 2LL * plan->num_cu;   // two workgroups per CU
-        R.rwg = (int)B;
-        R.nbc = 1;
-        while ((long long)H * R.nbc < 2 * G && R.rwg > 4) {
-            R.rwg = (R.rwg + 1) / 2;
-            R.nbc = (int)((B + R.rwg - 1) / R.rwg);
-        }
-        const long long items = (long long)H * R.nbc;
-        R.grid = (int)(items < G ? items : G);
+        // two persistent workgroups per CU, each a contiguous channel-major
+        // slice of rows; the slice's channels' spectra must fit the LDS
+        const long long rows_all = (long long)B * (long long)H;
+        long long G = 2LL * plan->num_cu;
+        long long per = (rows_all + G - 1) / G;
+        const long long max_ch = plan->row_max_channels;
+        while ((per + B - 1) / B + 1 > max_ch && per > 1) per = (per + 1) / 2;
+        R.rows_per_wg = per;
+        R.grid = (int)((rows_all + per - 1) / per);
         R.u = u;
         R.y = y;
         R.kf = k_f;

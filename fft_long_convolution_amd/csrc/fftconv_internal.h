@@ -101,9 +101,8 @@ struct SpecParams {
 // Register-resident row kernel (N = 32 * NB, NB = 16 or 32, 16-bit I/O).
 struct RowParams {
     int B, H, N;
-    int nbc;            // workgroups per channel
-    int rwg;            // batch entries per work item
-    int grid;           // persistent workgroups
+    long long rows_per_wg;   // contiguous slice of channel-major rows
+    int grid;                // workgroups
     const void* u;
     void* y;
     const void* kf;     // alpha/beta, [H][M] (4 x f16 each)

@@ -75,14 +75,16 @@ __device__ __forceinline__ int nbmap(int t, int y) {
     return NB == 32 ? kmap32(t, y) : 16 * t + y;
 }
 
-// Rows are processed channel-major: a work item is (channel h, a range of
-// batch entries); the spectrum coefficients of h are staged in LDS once per
-// item (lane-major, so every lane reads its own consecutive 16-byte entries)
-// and the next item's coefficients are prefetched into registers while the
-// current item runs.  Each wave walks its rows with a DEPTH-deep ring of
-// input loads in flight.  The grid is persistent (about one workgroup per
-// compute unit).  The inner-stage tables and the twiddles stay in
-// registers; the first/last stage tables are read from LDS.
+// Schedule: rows are taken in channel-major order (index = h*B + b) and each
+// workgroup owns one contiguous slice of that order.  The spectrum
+// coefficients of every channel the slice touches are staged in LDS once at
+// the start (lane-major, so every lane reads its own consecutive entries);
+// after that the row loop has no barriers.  Each wave walks every 4th row of
+// the slice with a DEPTH-deep ring of input loads in flight; refills are
+// unconditional (past the end they re-read the last row), so every row issues
+// the same memory operations and the wait counts stay exact.  The inner-stage
+// tables and the twiddles stay in registers for the whole kernel; the
+// first/last stage tables are read from LDS.
 constexpr int kRowDepth = 2;
 
 typedef _Float16 rhalf2 __attribute__((ext_vector_type(2)));
@@ -145,21 +147,22 @@ __global__ void __launch_bounds__(256, 2) row_kernel(RowParams P) {
     constexpr int NT = NB / 16;    // n_b tiles of the inverse
     constexpr bool BF = (IO == IO_BF16);
     constexpr int F1T = BF ? 8 : 4;
-    constexpr int E = M / 256;     // spectrum entries per thread
     constexpr int D = kRowDepth;
 
     extern __shared__ uint4 s_lds[];
     uint4* s_f1b = s_lds;                            // [F1T][64]
     uint4* s_i1a = s_f1b + F1T * 64;                 // [4][64]
-    uint2* s_ab = (uint2*)(s_i1a + 4 * 64);          // [bins per lane][64]
-    uint32_t* s_scr = (uint32_t*)(s_ab + M);         // [4 waves][NB][16]
+    uint32_t* s_scr = (uint32_t*)(s_i1a + 4 * 64);   // [4 waves][NB][16]
+    uint2* s_ab = (uint2*)(s_scr + 4 * NB * 16);     // [channels][bins per lane][64]
 
     const int tid = threadIdx.x, lane = tid & 63;
     // wave index as a scalar: branches on it stay uniform (scalar branches)
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int g = lane >> 4, x = lane & 15;
-    const int nitems = P.H * P.nbc;
-    const int G = gridDim.x;
+    const long long total = (long long)P.B * P.H;
+    const long long r0 = (long long)blockIdx.x * P.rows_per_wg;
+    const long long r1 = min(total, r0 + P.rows_per_wg);
+    const int h_lo = (int)(r0 / P.B);
 
     for (int i = tid; i < F1T * 64; i += 256) s_f1b[i] = ((const uint4*)P.f1b)[i];
     for (int i = tid; i < 4 * 64; i += 256) s_i1a[i] = ((const uint4*)P.i1a)[i];
@@ -194,16 +197,34 @@ __global__ void __launch_bounds__(256, 2) row_kernel(RowParams P) {
                     twi[SYM ? 0 : kt][SYM ? 0 : nt][r] = P.twi[lane * (NT * 8) + (kt * NT + nt) * 4 + r];
     }
 
-    // rows of work item 'item' handled by this wave: b = b0 + wave + 4 r
-    auto item_rows = [&](int item, int& h, int& b0, int& n) {
-        h = item / P.nbc;
-        const int bc = item - h * P.nbc;
-        b0 = bc * P.rwg;
-        const int b1 = min(P.B, b0 + P.rwg);
-        const int first = b0 + wave;
-        n = first < b1 ? (b1 - first + 3) / 4 : 0;
+    // ---- spectrum coefficients of every channel of this slice -> LDS
+    if (r0 < r1) {
+        const int h_hi = (int)((r1 - 1) / P.B);
+        const int nch = h_hi - h_lo + 1;
+        for (int i = tid; i < nch * M; i += 256) {
+            const int c = i / M, pos = i - c * M;
+            // bin (k_a, k_b) at position NB*k_a + k_b -> its lane and slot
+            const int ka = pos / NB, kb = pos - ka * NB;
+            const int kt = ka < 16 ? 0 : 1;
+            const int xx = ka < 16 ? ka : (ka == 16 ? 0 : 32 - ka);
+            const int sl = kb < NB / 2 ? kb : (3 * NB / 2 - 1 - kb);
+            const int mt = sl >> 3, gg = (sl >> 1) & 3, e = sl & 1;
+            s_ab[(long long)c * M + ((kt * MT2 + mt) * 2 + e) * 64 + gg * 16 + xx] =
+                ((const uint2*)P.kf)[(long long)(h_lo + c) * M + pos];
+        }
+    }
+    __syncthreads();
+
+    // this wave's rows: slice positions wave, wave+4, ...
+    const long long nrow = r1 > r0 + wave ? (r1 - r0 - wave + 3) / 4 : 0;
+    auto row_of = [&](long long m, int& h, int& b) {
+        long long idx = r0 + wave + 4 * (m < nrow ? m : nrow - 1);
+        h = (int)(idx / P.B);
+        b = (int)(idx - (long long)h * P.B);
     };
-    auto load_row = [&](uint32_t (&dst)[IT][4], int h, int b) {
+    auto load_row = [&](uint32_t (&dst)[IT][4], long long m) {
+        int h, b;
+        row_of(m, h, b);
         const uint32_t* u =
             (const uint32_t*)P.u + ((long long)b * P.H + h) * (M / 2);
 #pragma unroll
@@ -212,50 +233,21 @@ __global__ void __launch_bounds__(256, 2) row_kernel(RowParams P) {
             for (int jj = 0; jj < 4; ++jj) dst[it][jj] = u[NB * (4 * g + jj) + nbmap<NB>(it, x)];
     };
 
-    // ring slot k holds rows k, k+D, k+2D, ... of the current item, then
-    // row k of the next item: slots are fixed per row, so no register
-    // copies (and no full drains of the load queue) are needed
     uint32_t ring[D][IT][4];
-    int ch = 0, cb0 = 0, cn = 0;
-    if (blockIdx.x < nitems) item_rows(blockIdx.x, ch, cb0, cn);
+    if (nrow > 0) {
 #pragma unroll
-    for (int k = 0; k < D; ++k)
-        if (k < cn) load_row(ring[k], ch, cb0 + wave + 4 * k);
-    uint2 abn[E];
-    if (blockIdx.x < nitems) {
-        const uint2* kf = (const uint2*)P.kf + (long long)(blockIdx.x / P.nbc) * M;
-#pragma unroll
-        for (int q = 0; q < E; ++q) abn[q] = kf[tid + 256 * q];
+        for (int k = 0; k < D; ++k) load_row(ring[k], k);
     }
     // mirror exchange of the k_a = 0 column: every lane writes its column-0
     // bins and reads back bin -k_b of the same column (used by lanes x = 0)
-    // layout [k_b][x]: the 16 lanes of a group touch consecutive words
     uint32_t* scr = s_scr + wave * 16 * NB + x;
 
-    for (int item = blockIdx.x; item < nitems; item += G) {
-        int h, b0, n;
-        item_rows(item, h, b0, n);
-        int nh = 0, nb0 = 0, nn = 0;
-        if (item + G < nitems) item_rows(item + G, nh, nb0, nn);
-        __syncthreads();   // every wave is done with the previous item's table
-#pragma unroll
-        for (int q = 0; q < E; ++q) {
-            // bin (k_a, k_b) at position NB*k_a + k_b -> its lane and slot
-            const int pos = tid + 256 * q;
-            const int ka = pos / NB, kb = pos - ka * NB;
-            const int kt = ka < 16 ? 0 : 1;
-            const int xx = ka < 16 ? ka : (ka == 16 ? 0 : 32 - ka);
-            const int sl = kb < NB / 2 ? kb : (3 * NB / 2 - 1 - kb);
-            const int mt = sl >> 3, gg = (sl >> 1) & 3, e = sl & 1;
-            s_ab[((kt * MT2 + mt) * 2 + e) * 64 + gg * 16 + xx] = abn[q];
-        }
-        __syncthreads();
-        if (item + G < nitems) {
-            const uint2* kf = (const uint2*)P.kf + (long long)((item + G) / P.nbc) * M;
-#pragma unroll
-            for (int q = 0; q < E; ++q) abn[q] = kf[tid + 256 * q];
-        }
-        auto row_body = [&](uint32_t (&cur)[IT][4], const long long row) {
+    {
+        auto row_body = [&](uint32_t (&cur)[IT][4], const long long m) {
+            int h, b;
+            row_of(m, h, b);
+            const long long row = (long long)b * P.H + h;
+            const int abbase = (h - h_lo) * M;
             // ---- F1: 32-point DFT over n_a (16 nonzero), k_a to the lanes
             uint4 b2[KS2][2];
 #pragma unroll
@@ -329,7 +321,7 @@ __global__ void __launch_bounds__(256, 2) row_kernel(RowParams P) {
 #pragma unroll
                     for (int e = 0; e < 2; ++e) {
                         const int pm = (mt + MT2 / 2) % MT2;
-                        const uint2 ab = s_ab[((kt * MT2 + mt) * 2 + e) * 64 + lane];
+                        const uint2 ab = s_ab[abbase + ((kt * MT2 + mt) * 2 + e) * 64 + lane];
                         uint32_t p;
                         if (kt == 0) {
                             p = l0 ? zq[mt][e] : z[1][pm][e];
@@ -384,14 +376,12 @@ __global__ void __launch_bounds__(256, 2) row_kernel(RowParams P) {
                     }
                 }
         };
-        for (int r0 = 0; r0 < n; r0 += D) {
+        for (long long m0 = 0; m0 < nrow; m0 += D) {
 #pragma unroll
             for (int k = 0; k < D; ++k) {
-                const int r = r0 + k;
-                if (r < n) {
-                    row_body(ring[k], (long long)(b0 + wave + 4 * r) * P.H + h);
-                    if (r + D < n) load_row(ring[k], h, b0 + wave + 4 * (r + D));
-                    else if (k < nn) load_row(ring[k], nh, nb0 + wave + 4 * k);
+                if (m0 + k < nrow) {
+                    row_body(ring[k], m0 + k);
+                    load_row(ring[k], m0 + k + D);
                 }
             }
         }
