@@ -54,6 +54,7 @@ struct Shape {
     int ct = 0;          // outer-pass batch columns per tile
     int thr_fused = 64, thr_outer = 256, thr_inner = 512;
     int lds_fused = 0, lds_outer = 0, lds_inner = 0;
+    int wide_P = 0;      // > 0: fused P x 32 x 32 kernel (P/2 waves per row)
     fftconv_dtype dtype = FFTCONV_F32;
 };
 
@@ -96,6 +97,8 @@ bool search_factors(int lg, int p, std::vector<int>& out) {
     return true;
 }
 
+bool generic_forced();
+
 fftconv_status make_shape(size_t N, int p, fftconv_dtype dtype, Shape& s) {
     if (dtype != FFTCONV_F32 && dtype != FFTCONV_F16 && dtype != FFTCONV_BF16)
         return FFTCONV_ERR_UNSUPPORTED;
@@ -110,6 +113,13 @@ fftconv_status make_shape(size_t N, int p, fftconv_dtype dtype, Shape& s) {
     if (s.M <= (size_t)kFusedMaxM) {
         s.path = 0;
         if (!default_fused(lg, fac)) return FFTCONV_ERR_UNSUPPORTED;
+        // 16-bit I/O at N = 4K..16K: order 3 as P x 32 x 32 on the
+        // one-workgroup-per-row kernel
+        if (dtype != FFTCONV_F32 && lg >= 12 && lg <= 14 && (p == 0 || p == 3) &&
+            !generic_forced()) {
+            s.wide_P = 1 << (lg - 10);
+            fac = {s.wide_P, 32, 32};
+        }
         if (p != 0 && p != (int)fac.size() && !search_factors(lg, p, fac))
             return FFTCONV_ERR_UNSUPPORTED;
         // every stage must leave >= 16 columns and the pairing >= 4 blocks
@@ -196,7 +206,7 @@ void fill_info(const Shape& s, fftconv_plan_info* info) {
     info->spectrum_bytes_per_channel = s.M * kf_entry_bytes(s.dtype);
     info->workspace_bytes_per_row = s.path ? s.M * 8 : 0;
     info->mfma_flops_per_row = mfma_flops_per_row(s);
-    info->kernel_variant = s.path ? 2 : (row_kernel_applies(s) ? 1 : 0);
+    info->kernel_variant = s.path ? 2 : (s.wide_P ? 3 : (row_kernel_applies(s) ? 1 : 0));
 }
 
 // ------------------------------------------------------- table construction
@@ -459,6 +469,67 @@ std::vector<uint16_t> row_twiddles(int NB, bool inverse) {
     return out;
 }
 
+
+// ------------------------------------------- wide-kernel tables (P x 32 x 32)
+
+// First engine stage as the B operand over all 32 n_a (two K-steps), scaled
+// so that the outer P-point stage, this stage and the next one together are
+// unitary: 1/sqrt(32 P).
+std::vector<uint16_t> wide_f1b(int P) {
+    std::vector<uint16_t> out((size_t)8 * 64 * 8);
+    const double sc = 1.0 / sqrt(32.0 * P);
+    for (int ks = 0; ks < 2; ++ks)
+        for (int jt = 0; jt < 4; ++jt)
+            for (int lane = 0; lane < 64; ++lane) {
+                const int g = lane >> 4, x = lane & 15;
+                const int kt = jt >> 1, c = jt & 1, ka = kmap32h(kt, x);
+                for (int j = 0; j < 8; ++j) {
+                    const int na = 16 * ks + 4 * g + (j >> 1), d = j & 1;
+                    const double ang = -2.0 * M_PI * (double)((na * ka) % 32) / 32.0;
+                    const double v = emb(cos(ang) * sc, sin(ang) * sc, c, d);
+                    out[(((size_t)(ks * 4 + jt)) * 64 + lane) * 8 + j] = f32_to_f16_bits((float)v);
+                }
+            }
+    return out;
+}
+
+// Last inverse engine stage as the A operand producing all 32 n_a.
+std::vector<uint16_t> wide_i1a(int P) {
+    std::vector<uint16_t> out((size_t)8 * 64 * 8);
+    const double sc = 1.0 / sqrt(32.0 * P);
+    for (int mt = 0; mt < 4; ++mt)
+        for (int ks = 0; ks < 2; ++ks)
+            for (int lane = 0; lane < 64; ++lane) {
+                const int g = lane >> 4, x = lane & 15;
+                const int row = 16 * mt + x, na = row >> 1, c = row & 1;
+                for (int j = 0; j < 8; ++j) {
+                    const int ka = kmap32h(ks, 4 * g + (j >> 1)), d = j & 1;
+                    const double ang = 2.0 * M_PI * (double)((na * ka) % 32) / 32.0;
+                    const double v = emb(cos(ang) * sc, sin(ang) * sc, c, d);
+                    out[(((size_t)(mt * 2 + ks)) * 64 + lane) * 8 + j] = f32_to_f16_bits((float)v);
+                }
+            }
+    return out;
+}
+
+// Outer-stage twiddles W_M^{n' k1}, k1 = 1..P/2, for the columns each
+// thread owns: n_b = t & 31, n_a = CPT (t >> 5) + j.
+std::vector<uint16_t> wide_outer_twiddles(int P) {
+    const int T = 32 * P, CPT = 1024 / T, M = 1024 * P;
+    std::vector<uint16_t> out((size_t)(P / 2) * T * CPT * 2);
+    for (int k1 = 1; k1 <= P / 2; ++k1)
+        for (int t = 0; t < T; ++t)
+            for (int j = 0; j < CPT; ++j) {
+                const int nb = t & 31, na = CPT * (t >> 5) + j;
+                const long long np = 32LL * na + nb;
+                const double ang = -2.0 * M_PI * (double)((np * k1) % M) / (double)M;
+                const size_t idx = (((size_t)(k1 - 1) * T + t) * CPT + j) * 2;
+                out[idx] = f32_to_f16_bits((float)cos(ang));
+                out[idx + 1] = f32_to_f16_bits((float)sin(ang));
+            }
+    return out;
+}
+
 }  // namespace
 
 // --------------------------------------------------------------- the plan
@@ -476,6 +547,9 @@ struct fftconv_plan_s {
     int row_nb = 0;
     int lds_row = 0;
     RowParams row{};
+    int lds_wide = 0;
+    int wide_wgs_per_cu = 1;
+    WideParams wide{};
 };
 
 namespace {
@@ -636,10 +710,39 @@ fftconv_status build_device_tables(fftconv_plan_s* pl) {
         const int fixed = ((bf ? 8 : 4) + 4) * 64 * 16 + 4 * 16 * NB * 4;
         pl->row_max_channels = (64 * 1024 - fixed) / ((int)s.M * 8);
         pl->lds_row = fixed + (int)pl->row_max_channels * (int)s.M * 8;
-        hipDeviceProp_t prop;
-        if (hipGetDeviceProperties(&prop, pl->device) == hipSuccess && prop.multiProcessorCount > 0)
-            pl->num_cu = prop.multiProcessorCount;
     }
+    if (s.wide_P) {
+        const int P = s.wide_P;
+        std::vector<uint16_t> f1b = wide_f1b(P), i1a = wide_i1a(P), i2b = row_i2b(32);
+        std::vector<uint8_t> f2a = row_f2a(32);
+        std::vector<uint16_t> twf = row_twiddles(32, false), two = wide_outer_twiddles(P);
+        WideParams& W = pl->wide;
+        void* d = nullptr;
+        if (upload(pl, f1b.data(), f1b.size() * 2, &d) != hipSuccess) return FFTCONV_ERR_HIP;
+        W.f1b = d;
+        if (upload(pl, i1a.data(), i1a.size() * 2, &d) != hipSuccess) return FFTCONV_ERR_HIP;
+        W.i1a = d;
+        if (upload(pl, i2b.data(), i2b.size() * 2, &d) != hipSuccess) return FFTCONV_ERR_HIP;
+        W.i2b = d;
+        if (upload(pl, f2a.data(), f2a.size(), &d) != hipSuccess) return FFTCONV_ERR_HIP;
+        W.f2a = d;
+        if (upload(pl, twf.data(), twf.size() * 2, &d) != hipSuccess) return FFTCONV_ERR_HIP;
+        W.twf = (const uint32_t*)d;
+        if (upload(pl, two.data(), two.size() * 2, &d) != hipSuccess) return FFTCONV_ERR_HIP;
+        W.two = (const uint32_t*)d;
+        W.N = (int)s.N;
+        // stage tables (16 KB) + outer twiddles + one row of f16 points +
+        // the k_b exchange
+        pl->lds_wide = 16 * 1024 + (P / 2) * 4096 + (int)s.M * 4 + 39 * 16 * 4;
+        // two waves per SIMD (256 registers each), LDS permitting
+        const int by_waves = 8 / (P / 2);
+        const int by_lds = (160 * 1024) / pl->lds_wide;
+        pl->wide_wgs_per_cu = by_waves < by_lds ? by_waves : by_lds;
+        if (pl->wide_wgs_per_cu < 1) pl->wide_wgs_per_cu = 1;
+    }
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, pl->device) == hipSuccess && prop.multiProcessorCount > 0)
+        pl->num_cu = prop.multiProcessorCount;
     return FFTCONV_OK;
 }
 
@@ -759,6 +862,18 @@ fftconv_status fftconv_kernel_spectrum(fftconv_plan_t plan, const float* k,
             b = t;
         }
         if (e != hipSuccess) break;
+        if (s.wide_P) {
+            WideCoefParams wp{};
+            wp.M = (int)s.M;
+            wp.L = (int)L;
+            wp.P = s.wide_P;
+            wp.h0 = (int)h0;
+            wp.hcount = cnt;
+            wp.X = a;
+            wp.kf = k_f;
+            e = launch_wide_coef(wp, st);
+            continue;
+        }
         SpecParams sp{};
         sp.M = (int)s.M;
         sp.N = (int)s.N;
@@ -826,6 +941,21 @@ fftconv_status fftconv_forward(fftconv_plan_t plan, const void* u,
         R.y = y;
         R.kf = k_f;
         e = launch_row(io, plan->row_nb, R, plan->lds_row, st);
+    } else if (s.wide_P) {
+        WideParams W = plan->wide;
+        W.B = (int)B;
+        W.H = (int)H;
+        // persistent workgroups striding over the channel-major rows; a
+        // multiple of 8 so every XCD gets the same share
+        const long long rows_all = (long long)B * (long long)H;
+        long long G = (long long)plan->wide_wgs_per_cu * plan->num_cu;
+        G = G < 8 ? 8 : G & ~7LL;
+        const long long need = (rows_all + 7) & ~7LL;
+        W.grid = (int)(G < need ? G : need);
+        W.u = u;
+        W.y = y;
+        W.kf = k_f;
+        e = launch_wide(io, s.wide_P, W, plan->lds_wide, st);
     } else if (s.path == 0) {
         FwdParams P = plan->fused;
         P.rows = (long long)rows;

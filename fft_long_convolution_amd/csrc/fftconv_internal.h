@@ -116,6 +116,32 @@ struct RowParams {
 hipError_t launch_row(int io, int nb, const RowParams& p, int lds_bytes,
                       hipStream_t s);
 
+// Fused kernel for N = P * 1024 (P = 4, 8, 16, 16-bit I/O): one workgroup
+// of P/2 wavefronts per row (fftconv_wide.hip).
+struct WideParams {
+    int B, H, N;
+    int grid;                // persistent workgroups, a multiple of 8
+    const void* u;
+    void* y;
+    const void* kf;          // coefficients, [H][P/2][2][2][4][64][2] (4 x f16)
+    const void* f1b;         // 32-point stage over n_a, B tiles [ks 2][jt 4][64]
+    const void* i1a;         // its inverse, A tiles [mt 4][ks 2][64]
+    const void* f2a;         // 32-point stage over n_b, A tiles [mt 4][ks 2][64]
+    const void* i2b;         // its inverse, B tiles [ks 2][jt 4][64]
+    const uint32_t* twf;     // per-lane W_1024 twiddles (packed f16)
+    const uint32_t* two;     // outer twiddles W_M^{n' k1}, [k1-1][thread][column]
+};
+hipError_t launch_wide(int io, int P, const WideParams& p, int lds_bytes,
+                       hipStream_t s);
+
+struct WideCoefParams {
+    int M, L, P;
+    int h0, hcount;
+    const float2* X;         // [hcount][L] fp32 spectra of the padded kernels
+    void* kf;
+};
+hipError_t launch_wide_coef(const WideCoefParams& p, hipStream_t s);
+
 // Launchers (defined in fftconv_kernels.hip).  Return hipSuccess or the
 // launch error.
 hipError_t launch_fused(int io, const FwdParams& p, int lds_bytes,

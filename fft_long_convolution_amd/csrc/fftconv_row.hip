@@ -20,60 +20,9 @@
 // k_a = x and its mirror 32-x (lane 0: 0 and 16), and the F_NB row order
 // keeps k_b and NB-1-k_b in one lane group, so bin k and bin -k meet in the
 // same lane; only the k_a = 0 column needs an LDS exchange.
-#include "fftconv_internal.h"
+#include "fftconv_mfma.h"
 
 namespace fftconv {
-
-typedef _Float16 rhalf8 __attribute__((ext_vector_type(8)));
-typedef __bf16 rbf8 __attribute__((ext_vector_type(8)));
-typedef float rfloat4 __attribute__((ext_vector_type(4)));
-
-__device__ __forceinline__ uint32_t pk_f16(float a, float b) {
-    _Float16 h[2] = {(_Float16)a, (_Float16)b};
-    return __builtin_bit_cast(uint32_t, h);
-}
-
-template <int IO>
-__device__ __forceinline__ uint32_t pk_io(float a, float b) {
-    if (IO == IO_BF16) {
-        __bf16 h[2] = {(__bf16)a, (__bf16)b};
-        return __builtin_bit_cast(uint32_t, h);
-    }
-    return pk_f16(a, b);
-}
-
-__device__ __forceinline__ rfloat4 mma_f16(uint4 a, uint4 b, rfloat4 c) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_f16(
-        __builtin_bit_cast(rhalf8, a), __builtin_bit_cast(rhalf8, b), c, 0, 0, 0);
-}
-__device__ __forceinline__ rfloat4 mma_bf16(uint4 a, uint4 b, rfloat4 c) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-        __builtin_bit_cast(rbf8, a), __builtin_bit_cast(rbf8, b), c, 0, 0, 0);
-}
-
-__device__ __forceinline__ float2 cmul2(float2 a, float2 b) {
-    return make_float2(a.x * b.x - a.y * b.y, a.x * b.y + a.y * b.x);
-}
-
-// a*z + b*conj(p)
-__device__ __forceinline__ float2 pair2(float4 ab, float2 z, float2 p) {
-    return make_float2(ab.x * z.x - ab.y * z.y + ab.z * p.x + ab.w * p.y,
-                       ab.x * z.y + ab.y * z.x + ab.w * p.x - ab.z * p.y);
-}
-
-__device__ __forceinline__ int rmid_perm(int slot, int n) {
-    return slot < (n >> 1) ? slot : (3 * n / 2 - 1 - slot);
-}
-__device__ __forceinline__ int kmap32(int kt, int x) {
-    return kt == 0 ? x : (x == 0 ? 16 : 32 - x);
-}
-// n_b held by row y of tile t.  For NB = 32 the n_b digit uses the same
-// mirror map as k_a, which makes the forward and inverse twiddle positions
-// of every lane coincide (one register table, conjugated for the inverse).
-template <int NB>
-__device__ __forceinline__ int nbmap(int t, int y) {
-    return NB == 32 ? kmap32(t, y) : 16 * t + y;
-}
 
 // Schedule: rows are taken in channel-major order (index = h*B + b) and each
 // workgroup owns one contiguous slice of that order.  The spectrum
@@ -86,57 +35,6 @@ __device__ __forceinline__ int nbmap(int t, int y) {
 // tables and the twiddles stay in registers for the whole kernel; the
 // first/last stage tables are read from LDS.
 constexpr int kRowDepth = 2;
-
-typedef _Float16 rhalf2 __attribute__((ext_vector_type(2)));
-typedef __bf16 rbf2 __attribute__((ext_vector_type(2)));
-
-__device__ __forceinline__ uint32_t pk2(float a, float b) {
-    rhalf2 v;
-    v.x = (_Float16)a;
-    v.y = (_Float16)b;
-    uint32_t r = __builtin_bit_cast(uint32_t, v);
-    // opaque to the optimiser: keeps the single packed conversion instead of
-    // two scalar ones feeding half-selects of the following packed ops
-    asm("" : "+v"(r));
-    return r;
-}
-template <int IO>
-__device__ __forceinline__ uint32_t pk2io(float a, float b) {
-    if (IO == IO_BF16) {
-        rbf2 v;
-        v.x = (__bf16)a;
-        v.y = (__bf16)b;
-        return __builtin_bit_cast(uint32_t, v);
-    }
-    return pk2(a, b);
-}
-
-// Packed-f16 complex arithmetic (re in the low half, im in the high half).
-// The operands of the next matrix product are f16 anyway; doing the twiddle
-// and spectrum products in packed f16 halves their vector-ALU cost.
-__device__ __forceinline__ rhalf2 as_h2(uint32_t v) { return __builtin_bit_cast(rhalf2, v); }
-__device__ __forceinline__ uint32_t as_u32(rhalf2 v) { return __builtin_bit_cast(uint32_t, v); }
-// d * t
-__device__ __forceinline__ rhalf2 hmul(rhalf2 d, rhalf2 t) {
-    const rhalf2 dxx = {d.x, d.x}, dyy = {d.y, d.y};
-    const rhalf2 tn = {-t.y, t.x};
-    return __builtin_elementwise_fma(dyy, tn, dxx * t);
-}
-// d * conj(t)
-__device__ __forceinline__ rhalf2 hmulc(rhalf2 d, rhalf2 t) {
-    const rhalf2 dxx = {d.x, d.x}, dyy = {d.y, d.y};
-    const rhalf2 tc = {t.x, -t.y}, tn = {t.y, t.x};
-    return __builtin_elementwise_fma(dyy, tn, dxx * tc);
-}
-// a*z + b*conj(p)
-__device__ __forceinline__ rhalf2 hpair(rhalf2 a, rhalf2 z, rhalf2 b, rhalf2 p) {
-    const rhalf2 zxx = {z.x, z.x}, zyy = {z.y, z.y};
-    const rhalf2 pxx = {p.x, p.x}, pyy = {p.y, p.y};
-    const rhalf2 an = {-a.y, a.x}, bn = {b.y, -b.x};
-    rhalf2 r = __builtin_elementwise_fma(zyy, an, zxx * a);
-    r = __builtin_elementwise_fma(pxx, b, r);
-    return __builtin_elementwise_fma(pyy, bn, r);
-}
 
 template <int IO, int NB>
 __global__ void __launch_bounds__(256, 2) row_kernel(RowParams P) {

@@ -45,7 +45,7 @@ class PlanInfo(ctypes.Structure):
                 "spectrum_bytes_per_channel": self.spectrum_bytes_per_channel,
                 "workspace_bytes_per_row": self.workspace_bytes_per_row,
                 "mfma_flops_per_row": self.mfma_flops_per_row,
-                "kernel": {0: "fused_kernel", 1: "row_kernel",
+                "kernel": {0: "fused_kernel", 1: "row_kernel", 3: "wide_kernel",
                            2: "outer_fwd_kernel+inner_kernel+outer_inv_kernel"
                            }[self.kernel_variant]}
 

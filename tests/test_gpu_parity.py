@@ -56,10 +56,12 @@ def test_length_sweep(N, dtype):
 
 
 @pytest.mark.parametrize("N,dtype", [(512, "bf16"), (1024, "bf16"),
-                                     (1024, "f16")])
+                                     (1024, "f16"), (4096, "bf16"),
+                                     (8192, "f16"), (16384, "bf16")])
 def test_generic_kernel_at_row_lengths(N, dtype, monkeypatch):
-    # lengths 32*16 and 32*32 normally run the register-resident row
-    # kernel; the LDS-staged kernel must agree with the oracle there too
+    # lengths 32*16, 32*32 and P*32*32 normally run the register-resident
+    # row and wide kernels; the LDS-staged kernel must agree with the oracle
+    # there too
     monkeypatch.setenv("FFTCONV_KERNEL", "generic")
     w = inputs.Workload("generic", 60 + N.bit_length(), 4, 7, N, dtype,
                         "normal", "decay", "generic kernel")
@@ -76,6 +78,20 @@ def test_row_kernel_batch_shapes(B, H):
     err, _, _ = parity(w)
     _say("row shapes", B, H, "rel_l2", err)
     assert err < TOL["bf16"]
+
+
+@pytest.mark.parametrize("N,dtype,B,H", [
+    (4096, "f16", 1, 1), (4096, "bf16", 7, 3), (8192, "f16", 1, 1),
+    (8192, "f16", 5, 9), (8192, "bf16", 33, 2), (16384, "f16", 3, 1),
+    (16384, "bf16", 2, 7)])
+def test_wide_kernel_batch_shapes(N, dtype, B, H):
+    # row counts that leave the persistent workgroups' slices ragged and
+    # cross channel boundaries inside a slice
+    w = inputs.Workload("wideshape", 80 + N.bit_length() + B, B, H, N, dtype,
+                        "normal", "decay", "wide kernel shapes")
+    err, _, _ = parity(w)
+    _say("wide shapes", N, dtype, B, H, "rel_l2", err)
+    assert err < TOL[dtype]
 
 
 def _plan_and_spectrum(N, dtype, H=3):

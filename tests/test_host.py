@@ -40,8 +40,10 @@ def test_plan_query_every_length(lg, dtype):
     N = 1 << lg
     info = fc.plan_query(N, 0, dtype)
     prod = 1
-    for f in info["factors"]:
-        assert f in (8, 16, 32)
+    for i, f in enumerate(info["factors"]):
+        # the one-workgroup-per-row kernel has a vector-ALU outer stage of
+        # radix 4..16 in front of its 32 x 32 engine
+        assert f in ((4, 8, 16) if info["kernel"] == "wide_kernel" and i == 0 else (8, 16, 32))
         prod *= f
     assert prod == N and info["M"] == N
     assert info["factors"][-1] in (16, 32)
@@ -57,14 +59,22 @@ def test_plan_query_every_length(lg, dtype):
 
 def test_default_orders_follow_length():
     assert fc.plan_query(1024)["factors"] == [32, 32]
-    assert fc.plan_query(8192)["factors"] == [32, 16, 16]
+    # 16-bit I/O at 4K..16K: P x 32 x 32 on the wide kernel
+    for lg, P in ((12, 4), (13, 8), (14, 16)):
+        for dt in ("f16", "bf16"):
+            info = fc.plan_query(1 << lg, 0, dt)
+            assert info["factors"] == [P, 32, 32]
+            assert info["kernel"] == "wide_kernel"
+    assert fc.plan_query(8192, 0, "f32")["factors"] == [32, 16, 16]
+    assert fc.plan_query(8192, 0, "f32")["kernel"] == "fused_kernel"
     assert fc.plan_query(65536)["order"] == 4
     assert fc.plan_query(1 << 22)["order"] == 5
 
 
 def test_requested_order():
     assert fc.plan_query(1024, 3)["factors"] == [8, 8, 16]
-    assert fc.plan_query(8192, 3)["factors"] == [32, 16, 16]
+    assert fc.plan_query(8192, 3)["factors"] == [8, 32, 32]
+    assert fc.plan_query(8192, 3, "f32")["factors"] == [32, 16, 16]
     for N, p in ((256, 3), (4096, 2)):   # needs a radix outside 8..32
         with pytest.raises(fc.FFTConvError) as e:
             fc.plan_query(N, p)
