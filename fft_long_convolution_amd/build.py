@@ -14,7 +14,8 @@ LIB = os.path.join(HERE, "libfftconv.so")
 SOURCES = [os.path.join(HERE, "csrc", "fftconv_host.cpp"),
            os.path.join(HERE, "csrc", "fftconv_kernels.hip"),
            os.path.join(HERE, "csrc", "fftconv_row.hip"),
-           os.path.join(HERE, "csrc", "fftconv_wide.hip")]
+           os.path.join(HERE, "csrc", "fftconv_wide.hip"),
+           os.path.join(HERE, "csrc", "fftconv_mp.hip")]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = os.environ.get("FFTCONV_ARCH", "gfx950")
 

@@ -55,6 +55,8 @@ struct Shape {
     int thr_fused = 64, thr_outer = 256, thr_inner = 512;
     int lds_fused = 0, lds_outer = 0, lds_inner = 0;
     int wide_P = 0;      // > 0: fused P x 32 x 32 kernel (P/2 waves per row)
+    int mp_P1 = 0;       // > 0: multi-pass with outer levels P1 [x mp_P2] and
+    int mp_P2 = 1;       //      4096-point inner slabs (4 x 32 x 32)
     fftconv_dtype dtype = FFTCONV_F32;
 };
 
@@ -129,6 +131,23 @@ fftconv_status make_shape(size_t N, int p, fftconv_dtype dtype, Shape& s) {
         const int waves = s.M <= 1024 ? 1 : (s.M <= 4096 ? 4 : 8);
         s.thr_fused = 64 * waves;
         s.lds_fused = (int)(s.M * 8 + waves * 32 * 8);
+    } else if (dtype != FFTCONV_F32 && !generic_forced()) {
+        s.path = 1;
+        const int Po = (int)(s.M / 4096);
+        switch (Po) {
+        case 8: case 16: case 32: s.mp_P1 = Po; s.mp_P2 = 1; break;
+        case 64: s.mp_P1 = 8; s.mp_P2 = 8; break;
+        case 128: s.mp_P1 = 16; s.mp_P2 = 8; break;
+        case 256: s.mp_P1 = 16; s.mp_P2 = 16; break;
+        case 512: s.mp_P1 = 32; s.mp_P2 = 16; break;
+        case 1024: s.mp_P1 = 32; s.mp_P2 = 32; break;
+        default: return FFTCONV_ERR_UNSUPPORTED;
+        }
+        fac = {s.mp_P1};
+        if (s.mp_P2 > 1) fac.push_back(s.mp_P2);
+        fac.insert(fac.end(), {4, 32, 32});
+        if (p != 0 && p != (int)fac.size()) return FFTCONV_ERR_UNSUPPORTED;
+        s.n_outer = s.mp_P2 > 1 ? 2 : 1;
     } else {
         s.path = 1;
         std::vector<int> outer, inner;
@@ -204,9 +223,9 @@ void fill_info(const Shape& s, fftconv_plan_info* info) {
     info->outer_factors = s.n_outer;
     info->dtype = s.dtype;
     info->spectrum_bytes_per_channel = s.M * kf_entry_bytes(s.dtype);
-    info->workspace_bytes_per_row = s.path ? s.M * 8 : 0;
+    info->workspace_bytes_per_row = s.path ? s.M * (s.mp_P1 ? 4 : 8) : 0;
     info->mfma_flops_per_row = mfma_flops_per_row(s);
-    info->kernel_variant = s.path ? 2 : (s.wide_P ? 3 : (row_kernel_applies(s) ? 1 : 0));
+    info->kernel_variant = s.mp_P1 ? 4 : s.path ? 2 : (s.wide_P ? 3 : (row_kernel_applies(s) ? 1 : 0));
 }
 
 // ------------------------------------------------------- table construction
@@ -530,6 +549,35 @@ std::vector<uint16_t> wide_outer_twiddles(int P) {
     return out;
 }
 
+// Inner-pass twiddles W_4096^{n' m}, m = 1..4, for the columns each thread
+// owns (as in the wide kernel with 256 threads: n_b = t & 31,
+// n_a = 4 (t >> 5) + j).
+std::vector<uint16_t> mp_inner_twiddles() {
+    const int T = 256, CPT = 4, Mi = 4096;
+    std::vector<uint16_t> out((size_t)4 * T * CPT * 2);
+    for (int m = 1; m <= 4; ++m)
+        for (int t = 0; t < T; ++t)
+            for (int j = 0; j < CPT; ++j) {
+                const long long np = 32LL * (CPT * (t >> 5) + j) + (t & 31);
+                const double ang = -2.0 * M_PI * (double)((np * m) % Mi) / (double)Mi;
+                const size_t idx = (((size_t)(m - 1) * T + t) * CPT + j) * 2;
+                out[idx] = f32_to_f16_bits((float)cos(ang));
+                out[idx + 1] = f32_to_f16_bits((float)sin(ang));
+            }
+    return out;
+}
+
+// Column-pass twiddle bases W_n^c, c < count, fp32 (computed in fp64).
+std::vector<float> col_twiddles(long long n, long long count) {
+    std::vector<float> out((size_t)count * 2);
+    for (long long c = 0; c < count; ++c) {
+        const double ang = -2.0 * M_PI * (double)c / (double)n;
+        out[(size_t)c * 2] = (float)cos(ang);
+        out[(size_t)c * 2 + 1] = (float)sin(ang);
+    }
+    return out;
+}
+
 }  // namespace
 
 // --------------------------------------------------------------- the plan
@@ -550,6 +598,10 @@ struct fftconv_plan_s {
     int lds_wide = 0;
     int wide_wgs_per_cu = 1;
     WideParams wide{};
+    int lds_mp = 0;
+    MpInnerParams mp{};
+    const float2* mp_tw1 = nullptr;   // W_M^c, c < M / P1
+    const float2* mp_tw2 = nullptr;   // W_{M/P1}^c, c < 4096 (two levels)
 };
 
 namespace {
@@ -570,8 +622,11 @@ void free_plan(fftconv_plan_s* pl) {
     delete pl;
 }
 
+fftconv_status build_mp_tables(fftconv_plan_s* pl);
+
 fftconv_status build_device_tables(fftconv_plan_s* pl) {
     const Shape& s = pl->s;
+    if (s.mp_P1) return build_mp_tables(pl);
     const bool f32 = s.dtype == FFTCONV_F32;
     long long S[kMaxStages], str[kMaxStages];
     {
@@ -746,6 +801,46 @@ fftconv_status build_device_tables(fftconv_plan_s* pl) {
     return FFTCONV_OK;
 }
 
+fftconv_status build_mp_tables(fftconv_plan_s* pl) {
+    const Shape& s = pl->s;
+    std::vector<uint16_t> f1b = wide_f1b(4), i1a = wide_i1a(4), i2b = row_i2b(32);
+    std::vector<uint8_t> f2a = row_f2a(32);
+    std::vector<uint16_t> twf = row_twiddles(32, false), two = mp_inner_twiddles();
+    MpInnerParams& I = pl->mp;
+    void* d = nullptr;
+    if (upload(pl, f1b.data(), f1b.size() * 2, &d) != hipSuccess) return FFTCONV_ERR_HIP;
+    I.f1b = d;
+    if (upload(pl, i1a.data(), i1a.size() * 2, &d) != hipSuccess) return FFTCONV_ERR_HIP;
+    I.i1a = d;
+    if (upload(pl, i2b.data(), i2b.size() * 2, &d) != hipSuccess) return FFTCONV_ERR_HIP;
+    I.i2b = d;
+    if (upload(pl, f2a.data(), f2a.size(), &d) != hipSuccess) return FFTCONV_ERR_HIP;
+    I.f2a = d;
+    if (upload(pl, twf.data(), twf.size() * 2, &d) != hipSuccess) return FFTCONV_ERR_HIP;
+    I.twf = (const uint32_t*)d;
+    if (upload(pl, two.data(), two.size() * 2, &d) != hipSuccess) return FFTCONV_ERR_HIP;
+    I.two = (const uint32_t*)d;
+    I.M = (int)s.M;
+    I.Po = (int)(s.M / 4096);
+    I.P1 = s.mp_P1;
+    I.P2 = s.mp_P2;
+    std::vector<float> t1 = col_twiddles((long long)s.M, (long long)s.M / s.mp_P1);
+    if (upload(pl, t1.data(), t1.size() * 4, &d) != hipSuccess) return FFTCONV_ERR_HIP;
+    pl->mp_tw1 = (const float2*)d;
+    if (s.mp_P2 > 1) {
+        std::vector<float> t2 = col_twiddles((long long)s.M / s.mp_P1, 4096);
+        if (upload(pl, t2.data(), t2.size() * 4, &d) != hipSuccess) return FFTCONV_ERR_HIP;
+        pl->mp_tw2 = (const float2*)d;
+    }
+    // stage tables (16 KB) + inner twiddles (16 KB) + two slabs of f16
+    // points (32 KB) + the k_b exchange
+    pl->lds_mp = 16 * 1024 + 16 * 1024 + 8 * 1024 * 4 + 39 * 16 * 4;
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, pl->device) == hipSuccess && prop.multiProcessorCount > 0)
+        pl->num_cu = prop.multiProcessorCount;
+    return FFTCONV_OK;
+}
+
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
 bool overlap(const void* a, size_t na, const void* b, size_t nb) {
@@ -822,7 +917,7 @@ size_t fftconv_spectrum_bytes(fftconv_plan_t plan, size_t H) {
 
 size_t fftconv_workspace_bytes(fftconv_plan_t plan, size_t B, size_t H) {
     if (!plan || plan->s.path == 0) return 0;
-    return B * H * plan->s.M * 8;
+    return B * H * plan->s.M * (plan->s.mp_P1 ? 4 : 8);
 }
 
 fftconv_status fftconv_kernel_spectrum(fftconv_plan_t plan, const float* k,
@@ -862,6 +957,18 @@ fftconv_status fftconv_kernel_spectrum(fftconv_plan_t plan, const float* k,
             b = t;
         }
         if (e != hipSuccess) break;
+        if (s.mp_P1) {
+            MpCoefParams mp{};
+            mp.M = (int)s.M;
+            mp.L = (int)L;
+            mp.Po = (int)(s.M / 4096);
+            mp.h0 = (int)h0;
+            mp.hcount = cnt;
+            mp.X = a;
+            mp.kf = k_f;
+            e = launch_mp_coef(mp, st);
+            continue;
+        }
         if (s.wide_P) {
             WideCoefParams wp{};
             wp.M = (int)s.M;
@@ -941,6 +1048,35 @@ fftconv_status fftconv_forward(fftconv_plan_t plan, const void* u,
         R.y = y;
         R.kf = k_f;
         e = launch_row(io, plan->row_nb, R, plan->lds_row, st);
+    } else if (s.mp_P1) {
+        const long long rows_all = (long long)B * (long long)H;
+        MpColParams C1{};
+        C1.rows = rows_all;
+        C1.M = (int)s.M;
+        C1.S = (int)(s.M / s.mp_P1);
+        C1.tw = plan->mp_tw1;
+        C1.u = u;
+        C1.y = y;
+        C1.ws = workspace;
+        MpColParams C2 = C1;
+        C2.S = 4096;
+        C2.tw = plan->mp_tw2;
+        MpInnerParams I = plan->mp;
+        I.B = (int)B;
+        I.H = (int)H;
+        I.ws = workspace;
+        I.kf = k_f;
+        const long long units = rows_all * (I.Po / 2);
+        if (units > 0x7fffffffLL) return FFTCONV_ERR_UNSUPPORTED;
+        long long G = 2LL * plan->num_cu;
+        G = G < 8 ? 8 : G & ~7LL;
+        const long long need = (units + 7) & ~7LL;
+        I.grid = (int)(G < need ? G : need);
+        e = launch_mp_col(io, s.mp_P1, 0, C1, st);
+        if (e == hipSuccess && s.mp_P2 > 1) e = launch_mp_col(io, s.mp_P2, 1, C2, st);
+        if (e == hipSuccess) e = launch_mp_inner(io, I, plan->lds_mp, st);
+        if (e == hipSuccess && s.mp_P2 > 1) e = launch_mp_col(io, s.mp_P2, 2, C2, st);
+        if (e == hipSuccess) e = launch_mp_col(io, s.mp_P1, 3, C1, st);
     } else if (s.wide_P) {
         WideParams W = plan->wide;
         W.B = (int)B;

@@ -142,6 +142,43 @@ struct WideCoefParams {
 };
 hipError_t launch_wide_coef(const WideCoefParams& p, hipStream_t s);
 
+// Multi-pass path for N >= 32K, 16-bit I/O (fftconv_mp.hip): column passes
+// over the outer factor P_o = P1 [* P2] and an inner pass over units of two
+// 4096-point slabs; f16 complex workspace [rows][M].
+struct MpColParams {
+    long long rows;
+    int M;
+    int S;                 // columns per block (spacing of the P inputs)
+    const float2* tw;      // W_{P S}^c, c < S
+    const void* u;
+    void* y;
+    void* ws;
+};
+hipError_t launch_mp_col(int io, int P, int mode, const MpColParams& p, hipStream_t s);
+
+struct MpInnerParams {
+    int B, H, M;
+    int Po, P1, P2;        // outer factor and its levels (P2 = 1: one level)
+    int grid;              // persistent workgroups, a multiple of 8
+    void* ws;
+    const void* kf;        // coefficients, [H][P_o/2][4][2][2][4][64][2] (4 x f16)
+    const void* f1b;
+    const void* i1a;
+    const void* f2a;
+    const void* i2b;
+    const uint32_t* twf;
+    const uint32_t* two;   // W_4096^{n' m}, m = 1..4, [m-1][thread][column]
+};
+hipError_t launch_mp_inner(int io, const MpInnerParams& p, int lds_bytes, hipStream_t s);
+
+struct MpCoefParams {
+    int M, L, Po;
+    int h0, hcount;
+    const float2* X;       // [hcount][L] fp32 spectra of the padded kernels
+    void* kf;
+};
+hipError_t launch_mp_coef(const MpCoefParams& p, hipStream_t s);
+
 // Launchers (defined in fftconv_kernels.hip).  Return hipSuccess or the
 // launch error.
 hipError_t launch_fused(int io, const FwdParams& p, int lds_bytes,

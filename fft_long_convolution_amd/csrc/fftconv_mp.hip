@@ -1,0 +1,458 @@
+// Multi-pass path for N >= 32K with 16-bit I/O (page "FlashFFTConv:
+// Efficient Convolutions for Long Sequences with Tensor Cores", sections
+// 3.2 and 3.4: beyond what one workgroup holds, the outer Monarch factors
+// are applied in passes through HBM and the inner factors stay fused).
+//
+// M = P_o * 4096 with P_o = P1 (one outer level) or P1 * P2 (two levels),
+// an f16 complex workspace [row][M]:
+//   column pass, level 1: P1-point DFT over points spaced M/P1 apart (half
+//     of them zero: the causal padding), twiddle W_M^{c k1}, u -> workspace;
+//   column pass, level 2: P2-point DFT over points spaced 4096 apart inside
+//     each level-1 block, twiddle W_{M/P1}^{c k2}, in place;
+//   inner pass: slabs of 4096 points (outer bin k_o at slab
+//     sigma(k_o) = (k_o mod P1) P2 + k_o / P1) go through the 4 x 32 x 32
+//     engine in units of two slabs: the slab of k_o and the slab of its
+//     mirror P_o - k_o, or slabs 0 and P_o/2 together;
+//   inverse column passes in the opposite order, the last one writing y.
+// Column passes compute in fp32 and store f16.  Each outer stage carries
+// 1/sqrt(P) so the workspace stays O(|u|).
+//
+// Mirror pairing across slabs.  With S_B the slab of P_o - k_o, the data
+// conj(S_B[c]) W_4096^c transforms to conj(Z[-k]) at the position where the
+// slab of k_o has Z[k]; in the inner outer stage that is the 4-point DFT of
+// conj(S_B) taken at output (j + 1) mod 4 with twiddle W_4096^{n'(j + 1)}.
+// Slab P_o/2 pairs with itself the same way (its conjugated copy fills
+// sub-rows 2 and 3 of the pairing), slab 0 pairs like a fused row.
+#include "fftconv_engine.h"
+
+namespace fftconv {
+
+using namespace eng;
+
+namespace {
+
+__device__ __forceinline__ rfloat2 f2_from_h2(uint32_t v) {
+    const rhalf2 h = as_h2(v);
+    const rfloat2 r = {(float)h.x, (float)h.y};
+    return r;
+}
+template <int IO>
+__device__ __forceinline__ rfloat2 f2_from_io(uint32_t v) {
+    if constexpr (IO == IO_BF16) {
+        const rfloat2 r = {__uint_as_float(v << 16), __uint_as_float(v & 0xffff0000u)};
+        return r;
+    } else {
+        return f2_from_h2(v);
+    }
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------------------
+// Column passes.  One thread per column c of a block: MODE 0 reads u (first
+// level, P/2 nonzero inputs) and writes the workspace; MODE 1 is a forward
+// level in place; MODE 2 an inverse level in place; MODE 3 the last inverse
+// level, writing the P/2 outputs t < N to y.
+template <int IO, int P, int MODE>
+__global__ void __launch_bounds__(256) mp_col_kernel(MpColParams prm) {
+    const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
+    const long long per_row = (long long)prm.M / P;   // columns of a row
+    const long long row = i / per_row;
+    if (row >= prm.rows) return;
+    const int rem = (int)(i - row * per_row);
+    const int blk = rem / prm.S, c = rem - blk * prm.S;
+    const float sc = rsqrtf((float)P);
+    const float2 tt = prm.tw[c];   // W_{P S}^c
+    const rfloat2 t1 = {tt.x, tt.y};
+
+    rfloat2 v[P];
+    uint32_t* ws = (uint32_t*)prm.ws + row * (long long)prm.M + (long long)blk * P * prm.S + c;
+    if constexpr (MODE == 0) {
+        const uint32_t* u = (const uint32_t*)prm.u + row * (long long)(prm.M / 2) + c;
+        rfloat2 xin[P / 2];
+#pragma unroll
+        for (int n = 0; n < P / 2; ++n) xin[n] = f2_from_io<IO>(u[(long long)n * prm.S]) * sc;
+        dft_half_in<P>(xin, v);
+    } else if constexpr (MODE == 1) {
+#pragma unroll
+        for (int n = 0; n < P; ++n) v[n] = f2_from_h2(ws[(long long)n * prm.S]) * sc;
+        dft_small<P, false>(v);
+    } else {
+        // conjugate twiddles, then the inverse DFT
+        rfloat2 w = {1.f, 0.f};
+#pragma unroll
+        for (int k = 0; k < P; ++k) {
+            const rfloat2 a = f2_from_h2(ws[(long long)k * prm.S]) * sc;
+            v[k] = k == 0 ? a : fmulc(a, w);
+            w = fmul(w, t1);
+        }
+    }
+    if constexpr (MODE <= 1) {
+        rfloat2 w = {1.f, 0.f};
+#pragma unroll
+        for (int k = 0; k < P; ++k) {
+            const rfloat2 a = k == 0 ? v[k] : fmul(v[k], w);
+            ws[(long long)k * prm.S] = pk2(a.x, a.y);
+            w = fmul(w, t1);
+        }
+    } else if constexpr (MODE == 2) {
+        dft_small<P, true>(v);
+#pragma unroll
+        for (int n = 0; n < P; ++n) ws[(long long)n * prm.S] = pk2(v[n].x, v[n].y);
+    } else {
+        rfloat2 z[P / 2];
+        idft_half_out<P>(v, z);
+        uint32_t* y = (uint32_t*)prm.y + row * (long long)(prm.M / 2) + c;
+#pragma unroll
+        for (int n = 0; n < P / 2; ++n) y[(long long)n * prm.S] = pk2io<IO>(z[n].x, z[n].y);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Inner pass: persistent workgroups of four waves, one unit (two 4096-point
+// slabs, eight 1024-point regions) at a time.
+//   pair unit (slabs of k_o and P_o - k_o):  wave j holds region 2j = slab
+//     A sub-row j (4-point DFT output j, twiddle w_j) and region 2j + 1 =
+//     conj(slab B output 3 - j) w_{j+1}; the pairing is element-wise.
+//   self unit (slabs 0 and P_o/2): regions 0..3 are slab 0 laid out like a
+//     fused row of the wide kernel (wave 0: sub-rows 0 and 2 pair within
+//     themselves, wave 1: sub-row 1 and conj(sub-row 3) w_1); regions 4..7
+//     are slab P_o/2 sub-rows 0, 1 with conj(output 3) w_1 and
+//     conj(output 2) w_2.
+template <int IO>
+__global__ void __launch_bounds__(256, 2) mp_inner_kernel(MpInnerParams prm) {
+    constexpr int Q = 1024, T = 256, CPT = 4, SLAB = 4096;
+    typedef Outer<IO> O;
+    typedef typename O::V C;
+
+    extern __shared__ uint4 s_lds[];
+    uint4* s_f1b = s_lds;                              // [ks 2][jt 4][64]
+    uint4* s_i1a = s_f1b + 8 * 64;                     // [mt 4][ks 2][64]
+    uint32_t* s_two = (uint32_t*)(s_i1a + 8 * 64);     // [m - 1][thread][column], m = 1..4
+    uint32_t* s_buf = s_two + 4 * Q;                   // [8 regions][Q]
+    uint32_t* s_scr = s_buf + 8 * Q;                   // [39 k_b slots][16 x]
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int g = lane >> 4, x = lane & 15;
+    const int upr = prm.Po / 2;                        // units per row
+    const int total = prm.B * prm.H * upr;
+    // unit index (h * upr + q) * B + b: the B units that share spectrum
+    // coefficients are neighbours, and the G / 8 workgroups of an XCD take
+    // a contiguous block of indices at a time (as in the wide kernel)
+    const int G = gridDim.x;
+    const int first = (blockIdx.x & 7) * (G >> 3) + (blockIdx.x >> 3);
+    if (first >= total) return;
+
+    for (int i = tid; i < 8 * 64; i += T) {
+        s_f1b[i] = ((const uint4*)prm.f1b)[i];
+        s_i1a[i] = ((const uint4*)prm.i1a)[i];
+    }
+    for (int i = tid; i < Q; i += T) ((uint4*)s_two)[i] = ((const uint4*)prm.two)[i];
+    Regs E;
+    load_regs(E, prm.f2a, prm.i2b, prm.twf, lane);
+
+    const int nb = tid & 31, na0 = CPT * (tid >> 5);
+    const int it_o = nb < 16 ? 0 : 1, x_o = nb < 16 ? nb : (nb == 16 ? 0 : 32 - nb);
+    const int oa0 = eng_addr(na0, it_o, x_o);
+    const int lofs = 32 * na0 + nb;
+    auto load_two = [&](uint32_t (&tw)[4][CPT]) {
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            const uint4 v = *(const uint4*)(s_two + (m * T + tid) * CPT);
+            tw[m][0] = v.x;
+            tw[m][1] = v.y;
+            tw[m][2] = v.z;
+            tw[m][3] = v.w;
+        }
+    };
+    auto sigma = [&](int ko) { return (ko % prm.P1) * prm.P2 + ko / prm.P1; };
+    // unit -> (row, q, slabs)
+    auto unit_rows = [&](int idx, long long& row, int& h, int& q, int& sa, int& sb) {
+        const int hq = idx / prm.B, b = idx - hq * prm.B;
+        h = hq / upr;
+        q = hq - h * upr;
+        row = (long long)b * prm.H + h;
+        sa = sigma(q);
+        sb = sigma(q == 0 ? prm.Po / 2 : prm.Po - q);
+    };
+    uint32_t xin[2][4][CPT];   // [slab][n1][column]
+    auto load_in = [&](int idx) {
+        long long row;
+        int h, q, sa, sb;
+        unit_rows(idx, row, h, q, sa, sb);
+        const uint32_t* base = (const uint32_t*)prm.ws + row * (long long)prm.M;
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+            const uint32_t* sl = base + (long long)(s ? sb : sa) * SLAB + lofs;
+#pragma unroll
+            for (int n1 = 0; n1 < 4; ++n1)
+#pragma unroll
+                for (int j = 0; j < CPT; ++j) xin[s][n1][j] = sl[n1 * Q + 32 * j];
+        }
+    };
+    load_in(first);
+    __syncthreads();
+
+    uint32_t* scr = s_scr + x;
+    const int i1_base = (16 * (g >> 1) + x) * 4 + 2 * (g & 1);
+
+    const int steps = (total - first - 1) / G + 1;
+    for (int step = 0; step < steps; ++step) {
+        const int idx = first + step * G;
+        long long row;
+        int h, q, sa, sb;
+        unit_rows(idx, row, h, q, sa, sb);
+        const bool self = (q == 0);
+        const int inext = step + 1 < steps ? idx + G : idx;
+        // ---------------- inner outer stage: 4-point DFTs of both slabs
+        {
+            uint32_t tw[4][CPT];
+            load_two(tw);
+            uint32_t V[8][CPT];
+#pragma unroll
+            for (int j = 0; j < CPT; ++j) {
+                C a[4], b[4];
+#pragma unroll
+                for (int n1 = 0; n1 < 4; ++n1) {
+                    a[n1] = O::from_h2(xin[0][n1][j]);
+                    b[n1] = O::from_h2(xin[1][n1][j]);
+                }
+                dft_small<4, false>(a);
+                dft_small<4, false>(b);
+                if (self) {
+                    V[0][j] = O::to_h2(a[0]);
+                    V[1][j] = O::to_h2(O::mul(a[2], tw[1][j]));
+                    V[2][j] = O::to_h2(O::mul(a[1], tw[0][j]));
+                    V[3][j] = O::to_h2(O::mul(cnj(a[3]), tw[0][j]));
+                    V[4][j] = O::to_h2(b[0]);
+                    V[5][j] = O::to_h2(O::mul(cnj(b[3]), tw[0][j]));
+                    V[6][j] = O::to_h2(O::mul(b[1], tw[0][j]));
+                    V[7][j] = O::to_h2(O::mul(cnj(b[2]), tw[1][j]));
+                } else {
+                    V[0][j] = O::to_h2(a[0]);
+#pragma unroll
+                    for (int m = 1; m < 4; ++m) V[2 * m][j] = O::to_h2(O::mul(a[m], tw[m - 1][j]));
+#pragma unroll
+                    for (int m = 0; m < 4; ++m) V[2 * m + 1][j] = O::to_h2(O::mul(cnj(b[3 - m]), tw[m][j]));
+                }
+            }
+#pragma unroll
+            for (int s = 0; s < 8; ++s)
+                *(uint4*)(s_buf + s * Q + oa0) = make_uint4(V[s][0], V[s][1], V[s][2], V[s][3]);
+        }
+        __syncthreads();
+
+        // ---------------- engine: regions 2*wave and 2*wave + 1
+        {
+            const uint4* cf = (const uint4*)prm.kf + (((long long)h * upr + q) * 4 + wave) * 1024;
+            uint4 cfr[2][2][4];   // [region][kt][mt]
+#pragma unroll
+            for (int s = 0; s < 2; ++s)
+#pragma unroll
+                for (int mt = 0; mt < 4; ++mt) cfr[s][0][mt] = cf[(s * 2) * 256 + mt * 64 + lane];
+            uint32_t z[2][2][4][2];
+            forward(s_buf + (2 * wave) * Q, s_f1b, E, lane, z[0]);
+#pragma unroll
+            for (int s = 0; s < 2; ++s)
+#pragma unroll
+                for (int mt = 0; mt < 4; ++mt) cfr[s][1][mt] = cf[(s * 2 + 1) * 256 + mt * 64 + lane];
+            __builtin_amdgcn_sched_barrier(0);
+            forward(s_buf + (2 * wave + 1) * Q, s_f1b, E, lane, z[1]);
+            __builtin_amdgcn_sched_barrier(0);
+
+            uint4 a2[2][2][2];
+            if (self && wave == 0) {
+                uint32_t zq[4][2];
+                self_exchange(z[0], scr, g, zq);
+#pragma unroll
+                for (int kt = 0; kt < 2; ++kt) {
+                    pair_self(kt, x == 0, z[0], z[1], zq, cfr[0][kt], cfr[1][kt], a2[0][kt], a2[1][kt]);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            } else {
+#pragma unroll
+                for (int kt = 0; kt < 2; ++kt) {
+                    pair_elem(kt, z[0], z[1], cfr[0][kt], cfr[1][kt], a2[0][kt], a2[1][kt]);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            }
+            // next unit's input (after the coefficient loads: the load
+            // counter retires in order)
+            load_in(inext);
+
+            inverse(a2[0], s_i1a, E, lane, i1_base, s_buf + (2 * wave) * Q);
+            __builtin_amdgcn_sched_barrier(0);
+            inverse(a2[1], s_i1a, E, lane, i1_base, s_buf + (2 * wave + 1) * Q);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        __syncthreads();
+
+        // ---------------- inverse inner outer stage, back to the workspace
+        {
+            uint32_t tw[4][CPT];
+            load_two(tw);
+            uint32_t R[8][CPT];
+#pragma unroll
+            for (int s = 0; s < 8; ++s) {
+                const uint4 v = *(const uint4*)(s_buf + s * Q + oa0);
+                R[s][0] = v.x;
+                R[s][1] = v.y;
+                R[s][2] = v.z;
+                R[s][3] = v.w;
+            }
+            uint32_t* base = (uint32_t*)prm.ws + row * (long long)prm.M;
+            uint32_t* sla = base + (long long)sa * SLAB + lofs;
+            uint32_t* slb = base + (long long)sb * SLAB + lofs;
+#pragma unroll
+            for (int j = 0; j < CPT; ++j) {
+                C a[4], b[4];
+                if (self) {
+                    a[0] = O::from_h2(R[0][j]);
+                    a[2] = O::mulc(O::from_h2(R[1][j]), tw[1][j]);
+                    a[1] = O::mulc(O::from_h2(R[2][j]), tw[0][j]);
+                    a[3] = cnj(O::mulc(O::from_h2(R[3][j]), tw[0][j]));
+                    b[0] = O::from_h2(R[4][j]);
+                    b[1] = O::mulc(O::from_h2(R[6][j]), tw[0][j]);
+                    b[3] = cnj(O::mulc(O::from_h2(R[5][j]), tw[0][j]));
+                    b[2] = cnj(O::mulc(O::from_h2(R[7][j]), tw[1][j]));
+                } else {
+                    a[0] = O::from_h2(R[0][j]);
+#pragma unroll
+                    for (int m = 1; m < 4; ++m) a[m] = O::mulc(O::from_h2(R[2 * m][j]), tw[m - 1][j]);
+#pragma unroll
+                    for (int m = 0; m < 4; ++m) b[3 - m] = cnj(O::mulc(O::from_h2(R[2 * m + 1][j]), tw[m][j]));
+                }
+                dft_small<4, true>(a);
+                dft_small<4, true>(b);
+#pragma unroll
+                for (int n1 = 0; n1 < 4; ++n1) {
+                    sla[n1 * Q + 32 * j] = O::to_h2(a[n1]);
+                    slb[n1 * Q + 32 * j] = O::to_h2(b[n1]);
+                }
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Spectrum coefficients in the inner pass's engine order:
+// [h][q < P_o/2][wave 4][region 2][kt 2][mt 4][lane 64][e 2], each
+// (alpha, beta) as packed f16.  Region 0 of a wave holds its bin k; region 1
+// holds conj(alpha_{-k}), conj(beta_{-k}) for the element-wise pairs, or,
+// for wave 0 of the self unit, its own bin P_o (2 + 4 k').
+__global__ void mp_coef_kernel(MpCoefParams P) {
+    const int upr = P.Po / 2;
+    const long long per_ch = (long long)upr * 8192;
+    const long long total = (long long)P.hcount * per_ch;
+    for (long long i = blockIdx.x * (long long)blockDim.x + threadIdx.x; i < total;
+         i += (long long)gridDim.x * blockDim.x) {
+        const long long hl = i / per_ch;
+        const int rem = (int)(i - hl * per_ch);
+        const int e = rem & 1;
+        const int lane = (rem >> 1) & 63;
+        const int mt = (rem >> 7) & 3;
+        const int kt = (rem >> 9) & 1;
+        const int reg = (rem >> 10) & 1;
+        const int wave = (rem >> 11) & 3;
+        const int q = rem >> 13;
+        const int gg = lane >> 4, xx = lane & 15;
+        const long long kp = kmap32(kt, xx) + 32 * rmid_perm(8 * mt + 2 * gg + e, 32);
+        long long k;
+        bool conj_neg = false;
+        if (q == 0 && wave == 0) {
+            k = (long long)P.Po * ((reg ? 2 : 0) + 4 * kp);
+        } else {
+            long long ko = q, j = wave;
+            if (q == 0) {
+                if (wave == 1) {
+                    ko = 0;
+                    j = 1;
+                } else {
+                    ko = P.Po / 2;
+                    j = wave - 2;
+                }
+            }
+            k = ko + (long long)P.Po * (j + 4 * kp);
+            conj_neg = (reg == 1);
+        }
+        if (conj_neg) k = (P.M - k) % P.M;
+        const float2* X = P.X + hl * P.L;
+        const float2 K1 = X[k], K2 = X[k + P.M];
+        double sn, cs;
+        sincospi(2.0 * (double)k / (double)P.L, &sn, &cs);
+        const float s = (float)sn, c = (float)cs;
+        float2 al = make_float2(0.5f * ((1.f - s) * K1.x + (1.f + s) * K2.x),
+                                0.5f * ((1.f - s) * K1.y + (1.f + s) * K2.y));
+        const float2 dlt = make_float2(K1.x - K2.x, K1.y - K2.y);
+        float2 be = make_float2(-0.5f * c * dlt.y, 0.5f * c * dlt.x);
+        if (conj_neg) {
+            al.y = -al.y;
+            be.y = -be.y;
+        }
+        _Float16 hv[4] = {(_Float16)al.x, (_Float16)al.y, (_Float16)be.x, (_Float16)be.y};
+        ((uint2*)P.kf)[(long long)(P.h0 + hl) * per_ch + rem] = *(const uint2*)hv;
+    }
+}
+
+// ---------------------------------------------------------------------------
+namespace {
+
+template <int IO, int P>
+hipError_t col_launch(int mode, const MpColParams& p, hipStream_t s) {
+    const long long threads = p.rows * (long long)(p.M / P);
+    const dim3 grid((unsigned)((threads + 255) / 256)), blk(256);
+    switch (mode) {
+    case 0: hipLaunchKernelGGL((mp_col_kernel<IO, P, 0>), grid, blk, 0, s, p); break;
+    case 1: hipLaunchKernelGGL((mp_col_kernel<IO, P, 1>), grid, blk, 0, s, p); break;
+    case 2: hipLaunchKernelGGL((mp_col_kernel<IO, P, 2>), grid, blk, 0, s, p); break;
+    default: hipLaunchKernelGGL((mp_col_kernel<IO, P, 3>), grid, blk, 0, s, p); break;
+    }
+    return hipGetLastError();
+}
+
+template <int IO>
+hipError_t col_dispatch(int P, int mode, const MpColParams& p, hipStream_t s) {
+    switch (P) {
+    case 2: return col_launch<IO, 2>(mode, p, s);
+    case 4: return col_launch<IO, 4>(mode, p, s);
+    case 8: return col_launch<IO, 8>(mode, p, s);
+    case 16: return col_launch<IO, 16>(mode, p, s);
+    case 32: return col_launch<IO, 32>(mode, p, s);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace
+
+hipError_t launch_mp_col(int io, int P, int mode, const MpColParams& p, hipStream_t s) {
+    if (p.rows <= 0) return hipSuccess;
+    return io == IO_BF16 ? col_dispatch<IO_BF16>(P, mode, p, s) : col_dispatch<IO_F16>(P, mode, p, s);
+}
+
+hipError_t launch_mp_inner(int io, const MpInnerParams& p, int lds, hipStream_t s) {
+    const dim3 grid((unsigned)p.grid), blk(256);
+    if (io == IO_BF16) {
+        if (lds > 64 * 1024) {
+            hipError_t e = hipFuncSetAttribute((const void*)mp_inner_kernel<IO_BF16>,
+                                               hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+            if (e != hipSuccess) return e;
+        }
+        hipLaunchKernelGGL(mp_inner_kernel<IO_BF16>, grid, blk, lds, s, p);
+    } else {
+        if (lds > 64 * 1024) {
+            hipError_t e = hipFuncSetAttribute((const void*)mp_inner_kernel<IO_F16>,
+                                               hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+            if (e != hipSuccess) return e;
+        }
+        hipLaunchKernelGGL(mp_inner_kernel<IO_F16>, grid, blk, lds, s, p);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_mp_coef(const MpCoefParams& p, hipStream_t s) {
+    hipLaunchKernelGGL(mp_coef_kernel, dim3(2048), dim3(256), 0, s, p);
+    return hipGetLastError();
+}
+
+}  // namespace fftconv

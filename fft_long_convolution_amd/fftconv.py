@@ -46,6 +46,7 @@ class PlanInfo(ctypes.Structure):
                 "workspace_bytes_per_row": self.workspace_bytes_per_row,
                 "mfma_flops_per_row": self.mfma_flops_per_row,
                 "kernel": {0: "fused_kernel", 1: "row_kernel", 3: "wide_kernel",
+                           4: "mp_col_kernel+mp_inner_kernel",
                            2: "outer_fwd_kernel+inner_kernel+outer_inv_kernel"
                            }[self.kernel_variant]}
 

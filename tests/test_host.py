@@ -40,17 +40,28 @@ def test_plan_query_every_length(lg, dtype):
     N = 1 << lg
     info = fc.plan_query(N, 0, dtype)
     prod = 1
-    for i, f in enumerate(info["factors"]):
-        # the one-workgroup-per-row kernel has a vector-ALU outer stage of
-        # radix 4..16 in front of its 32 x 32 engine
-        assert f in ((4, 8, 16) if info["kernel"] == "wide_kernel" and i == 0 else (8, 16, 32))
+    fac = info["factors"]
+    for i, f in enumerate(fac):
+        if info["kernel"] == "wide_kernel" and i == 0:
+            # vector-ALU outer stage of radix 4..16 before the 32 x 32 engine
+            assert f in (4, 8, 16)
+        elif info["kernel"].startswith("mp_") and i == len(fac) - 3:
+            # multi-pass: 4096-point inner slabs, 4 x 32 x 32
+            assert f == 4
+        else:
+            assert f in (8, 16, 32)
         prod *= f
     assert prod == N and info["M"] == N
     assert info["factors"][-1] in (16, 32)
     assert info["path"] == ("fused" if N <= 16384 else "multipass")
     entry = 16 if dtype == "f32" else 8
     assert info["spectrum_bytes_per_channel"] == N * entry
-    assert info["workspace_bytes_per_row"] == (0 if N <= 16384 else 8 * N)
+    # workspace: f16 complex on the 16-bit multi-pass path, fp32 otherwise
+    ws = 0 if N <= 16384 else (8 * N if dtype == "f32" else 4 * N)
+    assert info["workspace_bytes_per_row"] == ws
+    if N > 16384 and dtype != "f32":
+        assert info["kernel"] == "mp_col_kernel+mp_inner_kernel"
+        assert fac[-3:] == [4, 32, 32]
     # matrix-core flops: 16 M (N_1/2 + sum_{i>1} N_i) per row
     f = info["factors"]
     want = 16.0 * N * (f[0] / 2 + sum(f[1:]))
