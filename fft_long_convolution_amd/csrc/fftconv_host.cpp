@@ -624,6 +624,8 @@ void free_plan(fftconv_plan_s* pl) {
 
 fftconv_status build_mp_tables(fftconv_plan_s* pl);
 
+constexpr size_t kMpChunkBytes = (size_t)256 << 20;
+
 fftconv_status build_device_tables(fftconv_plan_s* pl) {
     const Shape& s = pl->s;
     if (s.mp_P1) return build_mp_tables(pl);
@@ -760,10 +762,11 @@ fftconv_status build_device_tables(fftconv_plan_s* pl) {
         R.N = (int)s.N;
         pl->use_row = true;
         pl->row_nb = NB;
-        // fixed part: first/last stage tables + exchange scratch; the rest
-        // of a 64 KB budget (two workgroups per CU) holds spectra
-        const int fixed = ((bf ? 8 : 4) + 4) * 64 * 16 + 4 * 16 * NB * 4;
-        pl->row_max_channels = (64 * 1024 - fixed) / ((int)s.M * 8);
+        // fixed part: first/last stage tables, claim counter, exchange
+        // scratch of eight waves; the rest of a 128 KB budget (one
+        // workgroup per CU) holds spectra
+        const int fixed = ((bf ? 8 : 4) + 4) * 64 * 16 + 16 + 8 * 16 * NB * 4;
+        pl->row_max_channels = (128 * 1024 - fixed) / ((int)s.M * 8);
         pl->lds_row = fixed + (int)pl->row_max_channels * (int)s.M * 8;
     }
     if (s.wide_P) {
@@ -843,6 +846,17 @@ fftconv_status build_mp_tables(fftconv_plan_s* pl) {
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
+// Channels per chunk of the multi-pass path: the passes run chunk by chunk
+// so the chunk's workspace (B * hc * M f16 complex) stays in the 256 MB
+// Infinity Cache between the pass that writes it and the one that reads it.
+size_t mp_chunk_channels(const Shape& s, size_t B, size_t H) {
+    const size_t per_ch = (B ? B : 1) * s.M * 4;
+    size_t hc = kMpChunkBytes / per_ch;
+    if (hc < 1) hc = 1;
+    if (hc > H) hc = H;
+    return hc;
+}
+
 bool overlap(const void* a, size_t na, const void* b, size_t nb) {
     const uintptr_t a0 = (uintptr_t)a, b0 = (uintptr_t)b;
     return a0 < b0 + nb && b0 < a0 + na;
@@ -917,7 +931,8 @@ size_t fftconv_spectrum_bytes(fftconv_plan_t plan, size_t H) {
 
 size_t fftconv_workspace_bytes(fftconv_plan_t plan, size_t B, size_t H) {
     if (!plan || plan->s.path == 0) return 0;
-    return B * H * plan->s.M * (plan->s.mp_P1 ? 4 : 8);
+    if (plan->s.mp_P1) return B * mp_chunk_channels(plan->s, B, H) * plan->s.M * 4;
+    return B * H * plan->s.M * 8;
 }
 
 fftconv_status fftconv_kernel_spectrum(fftconv_plan_t plan, const float* k,
@@ -1035,10 +1050,10 @@ fftconv_status fftconv_forward(fftconv_plan_t plan, const void* u,
         RowParams R = plan->row;
         R.B = (int)B;
         R.H = (int)H;
-        // two persistent workgroups per CU, each a contiguous channel-major
+        // one persistent workgroup per CU, each a contiguous channel-major
         // slice of rows; the slice's channels' spectra must fit the LDS
         const long long rows_all = (long long)B * (long long)H;
-        long long G = 2LL * plan->num_cu;
+        long long G = plan->num_cu;
         long long per = (rows_all + G - 1) / G;
         const long long max_ch = plan->row_max_channels;
         while ((per + B - 1) / B + 1 > max_ch && per > 1) per = (per + 1) / 2;
@@ -1049,9 +1064,9 @@ fftconv_status fftconv_forward(fftconv_plan_t plan, const void* u,
         R.kf = k_f;
         e = launch_row(io, plan->row_nb, R, plan->lds_row, st);
     } else if (s.mp_P1) {
-        const long long rows_all = (long long)B * (long long)H;
+        const size_t hc_max = mp_chunk_channels(s, B, H);
         MpColParams C1{};
-        C1.rows = rows_all;
+        C1.H = (int)H;
         C1.M = (int)s.M;
         C1.S = (int)(s.M / s.mp_P1);
         C1.tw = plan->mp_tw1;
@@ -1066,17 +1081,24 @@ fftconv_status fftconv_forward(fftconv_plan_t plan, const void* u,
         I.H = (int)H;
         I.ws = workspace;
         I.kf = k_f;
-        const long long units = rows_all * (I.Po / 2);
-        if (units > 0x7fffffffLL) return FFTCONV_ERR_UNSUPPORTED;
-        long long G = 2LL * plan->num_cu;
-        G = G < 8 ? 8 : G & ~7LL;
-        const long long need = (units + 7) & ~7LL;
-        I.grid = (int)(G < need ? G : need);
-        e = launch_mp_col(io, s.mp_P1, 0, C1, st);
-        if (e == hipSuccess && s.mp_P2 > 1) e = launch_mp_col(io, s.mp_P2, 1, C2, st);
-        if (e == hipSuccess) e = launch_mp_inner(io, I, plan->lds_mp, st);
-        if (e == hipSuccess && s.mp_P2 > 1) e = launch_mp_col(io, s.mp_P2, 2, C2, st);
-        if (e == hipSuccess) e = launch_mp_col(io, s.mp_P1, 3, C1, st);
+        if ((long long)B * (long long)hc_max * (I.Po / 2) > 0x7fffffffLL) return FFTCONV_ERR_UNSUPPORTED;
+        e = hipSuccess;
+        for (size_t h0 = 0; h0 < H && e == hipSuccess; h0 += hc_max) {
+            const size_t hc = H - h0 < hc_max ? H - h0 : hc_max;
+            C1.h0 = C2.h0 = I.h0 = (int)h0;
+            C1.hc = C2.hc = I.hc = (int)hc;
+            C1.rows = C2.rows = (long long)B * (long long)hc;
+            const long long units = C1.rows * (I.Po / 2);
+            long long G = 2LL * plan->num_cu;
+            G = G < 8 ? 8 : G & ~7LL;
+            const long long need = (units + 7) & ~7LL;
+            I.grid = (int)(G < need ? G : need);
+            e = launch_mp_col(io, s.mp_P1, 0, C1, st);
+            if (e == hipSuccess && s.mp_P2 > 1) e = launch_mp_col(io, s.mp_P2, 1, C2, st);
+            if (e == hipSuccess) e = launch_mp_inner(io, I, plan->lds_mp, st);
+            if (e == hipSuccess && s.mp_P2 > 1) e = launch_mp_col(io, s.mp_P2, 2, C2, st);
+            if (e == hipSuccess) e = launch_mp_col(io, s.mp_P1, 3, C1, st);
+        }
     } else if (s.wide_P) {
         WideParams W = plan->wide;
         W.B = (int)B;

@@ -146,7 +146,8 @@ hipError_t launch_wide_coef(const WideCoefParams& p, hipStream_t s);
 // over the outer factor P_o = P1 [* P2] and an inner pass over units of two
 // 4096-point slabs; f16 complex workspace [rows][M].
 struct MpColParams {
-    long long rows;
+    long long rows;        // B * hc rows of the chunk: local row r -> channel
+    int H, h0, hc;         //   h0 + r % hc of batch r / hc; workspace row r
     int M;
     int S;                 // columns per block (spacing of the P inputs)
     const float2* tw;      // W_{P S}^c, c < S
@@ -158,6 +159,7 @@ hipError_t launch_mp_col(int io, int P, int mode, const MpColParams& p, hipStrea
 
 struct MpInnerParams {
     int B, H, M;
+    int h0, hc;            // channel chunk (workspace rows b * hc + h - h0)
     int Po, P1, P2;        // outer factor and its levels (P2 = 1: one level)
     int grid;              // persistent workgroups, a multiple of 8
     void* ws;

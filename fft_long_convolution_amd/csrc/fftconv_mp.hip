@@ -14,7 +14,8 @@
 //     engine in units of two slabs: the slab of k_o and the slab of its
 //     mirror P_o - k_o, or slabs 0 and P_o/2 together;
 //   inverse column passes in the opposite order, the last one writing y.
-// Column passes compute in fp32 and store f16.  Each outer stage carries
+// Column passes compute in fp32 and store f16.  Streams (input, workspace,
+// output) use non-temporal loads and stores; L2 keeps the coefficients.  Each outer stage carries
 // 1/sqrt(P) so the workspace stays O(|u|).
 //
 // Mirror pairing across slabs.  With S_B the slab of P_o - k_o, the data
@@ -61,6 +62,9 @@ __global__ void __launch_bounds__(256) mp_col_kernel(MpColParams prm) {
     if (row >= prm.rows) return;
     const int rem = (int)(i - row * per_row);
     const int blk = rem / prm.S, c = rem - blk * prm.S;
+    // input/output row in memory: batch row / hc, channel h0 + row % hc
+    const long long bq = row / prm.hc;
+    const long long mrow = bq * prm.H + prm.h0 + (row - bq * prm.hc);
     const float sc = rsqrtf((float)P);
     const float2 tt = prm.tw[c];   // W_{P S}^c
     const rfloat2 t1 = {tt.x, tt.y};
@@ -68,21 +72,22 @@ __global__ void __launch_bounds__(256) mp_col_kernel(MpColParams prm) {
     rfloat2 v[P];
     uint32_t* ws = (uint32_t*)prm.ws + row * (long long)prm.M + (long long)blk * P * prm.S + c;
     if constexpr (MODE == 0) {
-        const uint32_t* u = (const uint32_t*)prm.u + row * (long long)(prm.M / 2) + c;
+        const uint32_t* u = (const uint32_t*)prm.u + mrow * (long long)(prm.M / 2) + c;
         rfloat2 xin[P / 2];
 #pragma unroll
-        for (int n = 0; n < P / 2; ++n) xin[n] = f2_from_io<IO>(u[(long long)n * prm.S]) * sc;
+        for (int n = 0; n < P / 2; ++n)
+            xin[n] = f2_from_io<IO>(__builtin_nontemporal_load(&u[(long long)n * prm.S])) * sc;
         dft_half_in<P>(xin, v);
     } else if constexpr (MODE == 1) {
 #pragma unroll
-        for (int n = 0; n < P; ++n) v[n] = f2_from_h2(ws[(long long)n * prm.S]) * sc;
+        for (int n = 0; n < P; ++n) v[n] = f2_from_h2(__builtin_nontemporal_load(&ws[(long long)n * prm.S])) * sc;
         dft_small<P, false>(v);
     } else {
         // conjugate twiddles, then the inverse DFT
         rfloat2 w = {1.f, 0.f};
 #pragma unroll
         for (int k = 0; k < P; ++k) {
-            const rfloat2 a = f2_from_h2(ws[(long long)k * prm.S]) * sc;
+            const rfloat2 a = f2_from_h2(__builtin_nontemporal_load(&ws[(long long)k * prm.S])) * sc;
             v[k] = k == 0 ? a : fmulc(a, w);
             w = fmul(w, t1);
         }
@@ -92,19 +97,19 @@ __global__ void __launch_bounds__(256) mp_col_kernel(MpColParams prm) {
 #pragma unroll
         for (int k = 0; k < P; ++k) {
             const rfloat2 a = k == 0 ? v[k] : fmul(v[k], w);
-            ws[(long long)k * prm.S] = pk2(a.x, a.y);
+            __builtin_nontemporal_store(pk2(a.x, a.y), &ws[(long long)k * prm.S]);
             w = fmul(w, t1);
         }
     } else if constexpr (MODE == 2) {
         dft_small<P, true>(v);
 #pragma unroll
-        for (int n = 0; n < P; ++n) ws[(long long)n * prm.S] = pk2(v[n].x, v[n].y);
+        for (int n = 0; n < P; ++n) __builtin_nontemporal_store(pk2(v[n].x, v[n].y), &ws[(long long)n * prm.S]);
     } else {
         rfloat2 z[P / 2];
         idft_half_out<P>(v, z);
-        uint32_t* y = (uint32_t*)prm.y + row * (long long)(prm.M / 2) + c;
+        uint32_t* y = (uint32_t*)prm.y + mrow * (long long)(prm.M / 2) + c;
 #pragma unroll
-        for (int n = 0; n < P / 2; ++n) y[(long long)n * prm.S] = pk2io<IO>(z[n].x, z[n].y);
+        for (int n = 0; n < P / 2; ++n) __builtin_nontemporal_store(pk2io<IO>(z[n].x, z[n].y), &y[(long long)n * prm.S]);
     }
 }
 
@@ -136,8 +141,8 @@ __global__ void __launch_bounds__(256, 2) mp_inner_kernel(MpInnerParams prm) {
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int g = lane >> 4, x = lane & 15;
     const int upr = prm.Po / 2;                        // units per row
-    const int total = prm.B * prm.H * upr;
-    // unit index (h * upr + q) * B + b: the B units that share spectrum
+    const int total = prm.B * prm.hc * upr;
+    // unit index (hl * upr + q) * B + b: the B units that share spectrum
     // coefficients are neighbours, and the G / 8 workgroups of an XCD take
     // a contiguous block of indices at a time (as in the wide kernel)
     const int G = gridDim.x;
@@ -168,11 +173,14 @@ __global__ void __launch_bounds__(256, 2) mp_inner_kernel(MpInnerParams prm) {
     };
     auto sigma = [&](int ko) { return (ko % prm.P1) * prm.P2 + ko / prm.P1; };
     // unit -> (row, q, slabs)
+    // row is the workspace row of the unit (b * hc + local channel), h the
+    // channel (its spectrum coefficients)
     auto unit_rows = [&](int idx, long long& row, int& h, int& q, int& sa, int& sb) {
         const int hq = idx / prm.B, b = idx - hq * prm.B;
-        h = hq / upr;
-        q = hq - h * upr;
-        row = (long long)b * prm.H + h;
+        const int hl = hq / upr;
+        q = hq - hl * upr;
+        h = prm.h0 + hl;
+        row = (long long)b * prm.hc + hl;
         sa = sigma(q);
         sb = sigma(q == 0 ? prm.Po / 2 : prm.Po - q);
     };
@@ -188,7 +196,7 @@ __global__ void __launch_bounds__(256, 2) mp_inner_kernel(MpInnerParams prm) {
 #pragma unroll
             for (int n1 = 0; n1 < 4; ++n1)
 #pragma unroll
-                for (int j = 0; j < CPT; ++j) xin[s][n1][j] = sl[n1 * Q + 32 * j];
+                for (int j = 0; j < CPT; ++j) xin[s][n1][j] = __builtin_nontemporal_load(&sl[n1 * Q + 32 * j]);
         }
     };
     load_in(first);
@@ -327,8 +335,8 @@ __global__ void __launch_bounds__(256, 2) mp_inner_kernel(MpInnerParams prm) {
                 dft_small<4, true>(b);
 #pragma unroll
                 for (int n1 = 0; n1 < 4; ++n1) {
-                    sla[n1 * Q + 32 * j] = O::to_h2(a[n1]);
-                    slb[n1 * Q + 32 * j] = O::to_h2(b[n1]);
+                    __builtin_nontemporal_store(O::to_h2(a[n1]), &sla[n1 * Q + 32 * j]);
+                    __builtin_nontemporal_store(O::to_h2(b[n1]), &slb[n1 * Q + 32 * j]);
                 }
             }
         }

@@ -25,19 +25,24 @@
 namespace fftconv {
 
 // Schedule: rows are taken in channel-major order (index = h*B + b) and each
-// workgroup owns one contiguous slice of that order.  The spectrum
-// coefficients of every channel the slice touches are staged in LDS once at
-// the start (lane-major, so every lane reads its own consecutive entries);
-// after that the row loop has no barriers.  Each wave walks every 4th row of
-// the slice with a DEPTH-deep ring of input loads in flight; refills are
-// unconditional (past the end they re-read the last row), so every row issues
-// the same memory operations and the wait counts stay exact.  The inner-stage
-// tables and the twiddles stay in registers for the whole kernel; the
-// first/last stage tables are read from LDS.
+// workgroup (one per CU, eight waves: two per SIMD) owns one contiguous slice
+// of that order.  The spectrum coefficients of every channel the slice
+// touches are staged in LDS once at the start (lane-major, so every lane
+// reads its own consecutive entries); after that the row loop has no
+// barriers.  Waves claim rows of the slice one at a time from an LDS
+// counter, DEPTH claims ahead of the row being computed: a wave that the
+// SIMD's arbitration favours simply takes more rows, so the waves of a CU
+// finish together.  Refills are unconditional (a claim past the end re-reads
+// the last row), so every row issues the same memory operations and the wait
+// counts stay exact.  The inner-stage tables and the twiddles stay in
+// registers for the whole kernel; the first/last stage tables are read from
+// LDS.  Input and output rows are touched once: non-temporal loads and
+// stores keep them from displacing the spectra in L2.
 constexpr int kRowDepth = 2;
+constexpr int kRowWaves = 8;
 
 template <int IO, int NB>
-__global__ void __launch_bounds__(256, 2) row_kernel(RowParams P) {
+__global__ void __launch_bounds__(64 * kRowWaves, 1) row_kernel(RowParams P) {
     constexpr int M = 32 * NB;
     constexpr int IT = NB / 16;    // n_b tiles
     constexpr int MT2 = NB / 8;    // k_b slot tiles
@@ -50,8 +55,9 @@ __global__ void __launch_bounds__(256, 2) row_kernel(RowParams P) {
     extern __shared__ uint4 s_lds[];
     uint4* s_f1b = s_lds;                            // [F1T][64]
     uint4* s_i1a = s_f1b + F1T * 64;                 // [4][64]
-    uint32_t* s_scr = (uint32_t*)(s_i1a + 4 * 64);   // [4 waves][NB][16]
-    uint2* s_ab = (uint2*)(s_scr + 4 * NB * 16);     // [channels][bins per lane][64]
+    uint32_t* s_ctr = (uint32_t*)(s_i1a + 4 * 64);   // row claim counter (16 B)
+    uint32_t* s_scr = s_ctr + 4;                     // [waves][NB][16]
+    uint2* s_ab = (uint2*)(s_scr + kRowWaves * NB * 16);   // [channels][bins per lane][64]
 
     const int tid = threadIdx.x, lane = tid & 63;
     // wave index as a scalar: branches on it stay uniform (scalar branches)
@@ -62,8 +68,10 @@ __global__ void __launch_bounds__(256, 2) row_kernel(RowParams P) {
     const long long r1 = min(total, r0 + P.rows_per_wg);
     const int h_lo = (int)(r0 / P.B);
 
-    for (int i = tid; i < F1T * 64; i += 256) s_f1b[i] = ((const uint4*)P.f1b)[i];
-    for (int i = tid; i < 4 * 64; i += 256) s_i1a[i] = ((const uint4*)P.i1a)[i];
+    constexpr int TH = 64 * kRowWaves;
+    for (int i = tid; i < F1T * 64; i += TH) s_f1b[i] = ((const uint4*)P.f1b)[i];
+    for (int i = tid; i < 4 * 64; i += TH) s_i1a[i] = ((const uint4*)P.i1a)[i];
+    if (tid == 0) s_ctr[0] = 0;
     uint4 f2a[MT2][KS2];
     uint4 i2b[KS2][2 * NT];
 #pragma unroll
@@ -99,7 +107,7 @@ __global__ void __launch_bounds__(256, 2) row_kernel(RowParams P) {
     if (r0 < r1) {
         const int h_hi = (int)((r1 - 1) / P.B);
         const int nch = h_hi - h_lo + 1;
-        for (int i = tid; i < nch * M; i += 256) {
+        for (int i = tid; i < nch * M; i += TH) {
             const int c = i / M, pos = i - c * M;
             // bin (k_a, k_b) at position NB*k_a + k_b -> its lane and slot
             const int ka = pos / NB, kb = pos - ka * NB;
@@ -113,35 +121,45 @@ __global__ void __launch_bounds__(256, 2) row_kernel(RowParams P) {
     }
     __syncthreads();
 
-    // this wave's rows: slice positions wave, wave+4, ...
-    const long long nrow = r1 > r0 + wave ? (r1 - r0 - wave + 3) / 4 : 0;
-    auto row_of = [&](long long m, int& h, int& b) {
-        long long idx = r0 + wave + 4 * (m < nrow ? m : nrow - 1);
+    // rows of the slice are claimed one at a time (slice position c)
+    const int nslice = (int)(r1 - r0);
+    auto claim = [&]() {
+        uint32_t c = 0;
+        if (lane == 0) c = atomicAdd(s_ctr, 1u);
+        return (int)__builtin_amdgcn_readfirstlane(c);
+    };
+    auto row_of = [&](int c, int& h, int& b) {
+        const long long idx = r0 + (c < nslice ? c : nslice - 1);
         h = (int)(idx / P.B);
         b = (int)(idx - (long long)h * P.B);
     };
-    auto load_row = [&](uint32_t (&dst)[IT][4], long long m) {
+    auto load_row = [&](uint32_t (&dst)[IT][4], int c) {
         int h, b;
-        row_of(m, h, b);
+        row_of(c, h, b);
         const uint32_t* u =
             (const uint32_t*)P.u + ((long long)b * P.H + h) * (M / 2);
 #pragma unroll
         for (int it = 0; it < IT; ++it)
 #pragma unroll
-            for (int jj = 0; jj < 4; ++jj) dst[it][jj] = u[NB * (4 * g + jj) + nbmap<NB>(it, x)];
+            for (int jj = 0; jj < 4; ++jj)
+                dst[it][jj] = __builtin_nontemporal_load(&u[NB * (4 * g + jj) + nbmap<NB>(it, x)]);
     };
 
     uint32_t ring[D][IT][4];
-    if (nrow > 0) {
+    int cl[D];
+    if (nslice > 0) {
 #pragma unroll
-        for (int k = 0; k < D; ++k) load_row(ring[k], k);
+        for (int k = 0; k < D; ++k) {
+            cl[k] = claim();
+            load_row(ring[k], cl[k]);
+        }
     }
     // mirror exchange of the k_a = 0 column: every lane writes its column-0
     // bins and reads back bin -k_b of the same column (used by lanes x = 0)
     uint32_t* scr = s_scr + wave * 16 * NB + x;
 
     {
-        auto row_body = [&](uint32_t (&cur)[IT][4], const long long m) {
+        auto row_body = [&](uint32_t (&cur)[IT][4], const int m) {
             int h, b;
             row_of(m, h, b);
             const long long row = (long long)b * P.H + h;
@@ -270,32 +288,43 @@ __global__ void __launch_bounds__(256, 2) row_kernel(RowParams P) {
 #pragma unroll
                     for (int e = 0; e < 2; ++e) {
                         const int na = 8 * mt + 2 * g + e;
-                        yrow[NB * na + nbmap<NB>(nt, x)] = pk2io<IO>(acc[2 * e], acc[2 * e + 1]);
+                        __builtin_nontemporal_store(pk2io<IO>(acc[2 * e], acc[2 * e + 1]),
+                                                    &yrow[NB * na + nbmap<NB>(nt, x)]);
                     }
                 }
         };
-        for (long long m0 = 0; m0 < nrow; m0 += D) {
+        // claims grow monotonically and the ring is consumed in claim
+        // order, so the first claim past the end ends the wave's work
+        bool more = nslice > 0;
+        while (more) {
 #pragma unroll
             for (int k = 0; k < D; ++k) {
-                if (m0 + k < nrow) {
-                    row_body(ring[k], m0 + k);
-                    load_row(ring[k], m0 + k + D);
+                if (more && cl[k] < nslice) {
+                    row_body(ring[k], cl[k]);
+                    cl[k] = claim();
+                    load_row(ring[k], cl[k]);
+                } else {
+                    more = false;
                 }
             }
         }
     }
 }
 
-hipError_t launch_row(int io, int nb, const RowParams& p, int lds, hipStream_t s) {
-    const dim3 grid((unsigned)p.grid), blk(256);
-    if (io == IO_BF16) {
-        if (nb == 32) hipLaunchKernelGGL((row_kernel<IO_BF16, 32>), grid, blk, lds, s, p);
-        else hipLaunchKernelGGL((row_kernel<IO_BF16, 16>), grid, blk, lds, s, p);
-    } else {
-        if (nb == 32) hipLaunchKernelGGL((row_kernel<IO_F16, 32>), grid, blk, lds, s, p);
-        else hipLaunchKernelGGL((row_kernel<IO_F16, 16>), grid, blk, lds, s, p);
+template <int IO, int NB>
+static hipError_t launch_row_t(const RowParams& p, int lds, hipStream_t s) {
+    if (lds > 64 * 1024) {
+        const hipError_t e = hipFuncSetAttribute((const void*)row_kernel<IO, NB>,
+                                                 hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+        if (e != hipSuccess) return e;
     }
+    hipLaunchKernelGGL((row_kernel<IO, NB>), dim3((unsigned)p.grid), dim3(64 * kRowWaves), lds, s, p);
     return hipGetLastError();
+}
+
+hipError_t launch_row(int io, int nb, const RowParams& p, int lds, hipStream_t s) {
+    if (io == IO_BF16) return nb == 32 ? launch_row_t<IO_BF16, 32>(p, lds, s) : launch_row_t<IO_BF16, 16>(p, lds, s);
+    return nb == 32 ? launch_row_t<IO_F16, 32>(p, lds, s) : launch_row_t<IO_F16, 16>(p, lds, s);
 }
 
 }  // namespace fftconv

@@ -17,6 +17,9 @@
 //  3. Outer inverse (all threads): conjugate twiddle and the P-point
 //     inverse DFT, only the n1 < P/2 outputs (t < N), store.
 //
+// Input and output rows are touched once and go through non-temporal
+// loads and stores, which keeps L2 for the spectrum coefficients.
+//
 // Mirror pairing.  Bin k pairs with -k.  For 0 < k1 < P/2 the partner bins
 // live in sub-row P - k1.  That sub-row is pushed through the engine as
 // w_k1 * conj(A_{P-k1}) -- the same twiddle as sub-row k1 -- which returns
@@ -101,7 +104,7 @@ __global__ void __launch_bounds__(32 * P, 2) wide_kernel(WideParams prm) {
         for (int n1 = 0; n1 < HALF; ++n1) {
             const uint32_t* un = u + n1 * Q + lofs;
 #pragma unroll
-            for (int j = 0; j < CPT; ++j) uin[n1][j] = un[32 * j];
+            for (int j = 0; j < CPT; ++j) uin[n1][j] = __builtin_nontemporal_load(&un[32 * j]);
         }
     };
     load_u(first);
@@ -242,7 +245,8 @@ __global__ void __launch_bounds__(32 * P, 2) wide_kernel(WideParams prm) {
                 }
                 idft_half_out<P>(Bv, zo);
 #pragma unroll
-                for (int n1 = 0; n1 < HALF; ++n1) yrow[n1 * Q + lofs + 32 * j] = O::to_io(zo[n1]);
+                for (int n1 = 0; n1 < HALF; ++n1)
+                    __builtin_nontemporal_store(O::to_io(zo[n1]), &yrow[n1 * Q + lofs + 32 * j]);
             }
         }
     }
