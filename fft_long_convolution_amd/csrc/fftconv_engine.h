@@ -243,6 +243,26 @@ __device__ __forceinline__ int eng_addr(int na, int it, int x) {
 }
 
 
+// Dynamic distribution of rows (or units) over persistent workgroups.  The
+// grid (G workgroups, a multiple of 8) splits into the 8 groups that share
+// an XCD (consecutive dispatch ids go to consecutive XCDs).  Group x owns
+// the indices whose position within each block of G falls in
+// [x G/8, (x + 1) G/8) -- neighbouring indices share spectrum coefficients,
+// which then stay in that XCD's L2 -- and its workgroups claim them in
+// order from their own counter (ctr[32 x], a 128-byte line each).  A
+// workgroup that the CU's arbitration favours simply claims more.
+struct XcdClaim {
+    uint32_t* ctr;
+    int G, gx, x;
+    __device__ __forceinline__ XcdClaim(uint32_t* c, int grid, int bid)
+        : ctr(c + 32 * (bid & 7)), G(grid), gx(grid >> 3), x(bid & 7) {}
+    // next index of this group (monotonic; >= total means done)
+    __device__ __forceinline__ long long next() const {
+        const uint32_t k = atomicAdd(ctr, 1u);
+        return (long long)(k / gx) * G + (long long)x * gx + (k % gx);
+    }
+};
+
 // Stage tables the engine keeps in registers for the whole kernel.
 struct Regs {
     uint4 f2a[4][2];        // stage over n_b, A tiles

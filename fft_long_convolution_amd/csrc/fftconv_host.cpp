@@ -791,7 +791,7 @@ fftconv_status build_device_tables(fftconv_plan_s* pl) {
         W.N = (int)s.N;
         // stage tables (16 KB) + outer twiddles + one row of f16 points +
         // the k_b exchange
-        pl->lds_wide = 16 * 1024 + (P / 2) * 4096 + (int)s.M * 4 + 39 * 16 * 4;
+        pl->lds_wide = 16 * 1024 + (P / 2) * 4096 + (int)s.M * 4 + 39 * 16 * 4 + 16;
         // two waves per SIMD (256 registers each), LDS permitting
         const int by_waves = 8 / (P / 2);
         const int by_lds = (160 * 1024) / pl->lds_wide;
@@ -837,7 +837,7 @@ fftconv_status build_mp_tables(fftconv_plan_s* pl) {
     }
     // stage tables (16 KB) + inner twiddles (16 KB) + two slabs of f16
     // points (32 KB) + the k_b exchange
-    pl->lds_mp = 16 * 1024 + 16 * 1024 + 8 * 1024 * 4 + 39 * 16 * 4;
+    pl->lds_mp = 16 * 1024 + 16 * 1024 + 8 * 1024 * 4 + 39 * 16 * 4 + 16;
     hipDeviceProp_t prop;
     if (hipGetDeviceProperties(&prop, pl->device) == hipSuccess && prop.multiProcessorCount > 0)
         pl->num_cu = prop.multiProcessorCount;
@@ -930,8 +930,12 @@ size_t fftconv_spectrum_bytes(fftconv_plan_t plan, size_t H) {
 }
 
 size_t fftconv_workspace_bytes(fftconv_plan_t plan, size_t B, size_t H) {
-    if (!plan || plan->s.path == 0) return 0;
-    if (plan->s.mp_P1) return B * mp_chunk_channels(plan->s, B, H) * plan->s.M * 4;
+    if (!plan) return 0;
+    // wide kernel: the row-claim counters only
+    if (plan->s.wide_P) return kClaimBytes;
+    if (plan->s.path == 0) return 0;
+    // multi-pass: one channel chunk of f16 complex rows, then the counters
+    if (plan->s.mp_P1) return B * mp_chunk_channels(plan->s, B, H) * plan->s.M * 4 + kClaimBytes;
     return B * H * plan->s.M * 8;
 }
 
@@ -1073,6 +1077,7 @@ fftconv_status fftconv_forward(fftconv_plan_t plan, const void* u,
         C1.u = u;
         C1.y = y;
         C1.ws = workspace;
+        C1.ctr = (uint32_t*)((char*)workspace + (ws_need - kClaimBytes));
         MpColParams C2 = C1;
         C2.S = 4096;
         C2.tw = plan->mp_tw2;
@@ -1080,6 +1085,7 @@ fftconv_status fftconv_forward(fftconv_plan_t plan, const void* u,
         I.B = (int)B;
         I.H = (int)H;
         I.ws = workspace;
+        I.ctr = C1.ctr;
         I.kf = k_f;
         if ((long long)B * (long long)hc_max * (I.Po / 2) > 0x7fffffffLL) return FFTCONV_ERR_UNSUPPORTED;
         e = hipSuccess;
@@ -1113,7 +1119,9 @@ fftconv_status fftconv_forward(fftconv_plan_t plan, const void* u,
         W.u = u;
         W.y = y;
         W.kf = k_f;
-        e = launch_wide(io, s.wide_P, W, plan->lds_wide, st);
+        W.ctr = (uint32_t*)workspace;
+        e = launch_claim_reset(W.ctr, st);
+        if (e == hipSuccess) e = launch_wide(io, s.wide_P, W, plan->lds_wide, st);
     } else if (s.path == 0) {
         FwdParams P = plan->fused;
         P.rows = (long long)rows;

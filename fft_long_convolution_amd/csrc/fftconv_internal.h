@@ -118,9 +118,15 @@ hipError_t launch_row(int io, int nb, const RowParams& p, int lds_bytes,
 
 // Fused kernel for N = P * 1024 (P = 4, 8, 16, 16-bit I/O): one workgroup
 // of P/2 wavefronts per row (fftconv_wide.hip).
+// Row-claim counters of one call: 8 XCD groups, one 128-byte line each.
+constexpr int kClaimWords = 256;
+constexpr size_t kClaimBytes = kClaimWords * 4;
+hipError_t launch_claim_reset(uint32_t* ctr, hipStream_t s);
+
 struct WideParams {
     int B, H, N;
     int grid;                // persistent workgroups, a multiple of 8
+    uint32_t* ctr;           // claim counters (workspace, cleared per call)
     const void* u;
     void* y;
     const void* kf;          // coefficients, [H][P/2][2][2][4][64][2] (4 x f16)
@@ -154,6 +160,7 @@ struct MpColParams {
     const void* u;
     void* y;
     void* ws;
+    uint32_t* ctr;         // first pass: clears the inner pass's counters
 };
 hipError_t launch_mp_col(int io, int P, int mode, const MpColParams& p, hipStream_t s);
 
@@ -162,6 +169,7 @@ struct MpInnerParams {
     int h0, hc;            // channel chunk (workspace rows b * hc + h - h0)
     int Po, P1, P2;        // outer factor and its levels (P2 = 1: one level)
     int grid;              // persistent workgroups, a multiple of 8
+    uint32_t* ctr;         // claim counters (end of the workspace)
     void* ws;
     const void* kf;        // coefficients, [H][P_o/2][4][2][2][4][64][2] (4 x f16)
     const void* f1b;

@@ -57,6 +57,8 @@ __device__ __forceinline__ rfloat2 f2_from_io(uint32_t v) {
 template <int IO, int P, int MODE>
 __global__ void __launch_bounds__(256) mp_col_kernel(MpColParams prm) {
     const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
+    // the first pass of a chunk clears the inner pass's claim counters
+    if (MODE == 0 && blockIdx.x == 0 && threadIdx.x < kClaimWords) prm.ctr[threadIdx.x] = 0u;
     const long long per_row = (long long)prm.M / P;   // columns of a row
     const long long row = i / per_row;
     if (row >= prm.rows) return;
@@ -136,6 +138,7 @@ __global__ void __launch_bounds__(256, 2) mp_inner_kernel(MpInnerParams prm) {
     uint32_t* s_two = (uint32_t*)(s_i1a + 8 * 64);     // [m - 1][thread][column], m = 1..4
     uint32_t* s_buf = s_two + 4 * Q;                   // [8 regions][Q]
     uint32_t* s_scr = s_buf + 8 * Q;                   // [39 k_b slots][16 x]
+    int* s_claim = (int*)(s_scr + 39 * 16);            // [2] claimed unit indices
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -143,17 +146,20 @@ __global__ void __launch_bounds__(256, 2) mp_inner_kernel(MpInnerParams prm) {
     const int upr = prm.Po / 2;                        // units per row
     const int total = prm.B * prm.hc * upr;
     // unit index (hl * upr + q) * B + b: the B units that share spectrum
-    // coefficients are neighbours, and the G / 8 workgroups of an XCD take
-    // a contiguous block of indices at a time (as in the wide kernel)
-    const int G = gridDim.x;
-    const int first = (blockIdx.x & 7) * (G >> 3) + (blockIdx.x >> 3);
-    if (first >= total) return;
+    // coefficients are neighbours; units are claimed one ahead from the
+    // counters of this workgroup's XCD group (as in the wide kernel)
+    const XcdClaim claimer(prm.ctr, gridDim.x, blockIdx.x);
 
     for (int i = tid; i < 8 * 64; i += T) {
         s_f1b[i] = ((const uint4*)prm.f1b)[i];
         s_i1a[i] = ((const uint4*)prm.i1a)[i];
     }
     for (int i = tid; i < Q; i += T) ((uint4*)s_two)[i] = ((const uint4*)prm.two)[i];
+    if (tid == 0) {
+        const long long c0 = claimer.next(), c1 = claimer.next();
+        s_claim[0] = (int)(c0 < total ? c0 : total);
+        s_claim[1] = (int)(c1 < total ? c1 : total);
+    }
     Regs E;
     load_regs(E, prm.f2a, prm.i2b, prm.twf, lane);
 
@@ -199,20 +205,20 @@ __global__ void __launch_bounds__(256, 2) mp_inner_kernel(MpInnerParams prm) {
                 for (int j = 0; j < CPT; ++j) xin[s][n1][j] = __builtin_nontemporal_load(&sl[n1 * Q + 32 * j]);
         }
     };
-    load_in(first);
     __syncthreads();
+    int cur = s_claim[0], nxt = s_claim[1];
+    if (cur >= total) return;   // uniform over the workgroup
+    load_in(cur);
 
     uint32_t* scr = s_scr + x;
     const int i1_base = (16 * (g >> 1) + x) * 4 + 2 * (g & 1);
 
-    const int steps = (total - first - 1) / G + 1;
-    for (int step = 0; step < steps; ++step) {
-        const int idx = first + step * G;
+    while (cur < total) {
         long long row;
         int h, q, sa, sb;
-        unit_rows(idx, row, h, q, sa, sb);
+        unit_rows(cur, row, h, q, sa, sb);
         const bool self = (q == 0);
-        const int inext = step + 1 < steps ? idx + G : idx;
+        const int inext = nxt < total ? nxt : cur;
         // ---------------- inner outer stage: 4-point DFTs of both slabs
         {
             uint32_t tw[4][CPT];
@@ -249,6 +255,11 @@ __global__ void __launch_bounds__(256, 2) mp_inner_kernel(MpInnerParams prm) {
             for (int s = 0; s < 8; ++s)
                 *(uint4*)(s_buf + s * Q + oa0) = make_uint4(V[s][0], V[s][1], V[s][2], V[s][3]);
         }
+        // claim the row after next now: the atomic returns long before the
+        // value is published, and it is older than the loads it must not
+        // delay
+        long long c2 = 0;
+        if (tid == 0) c2 = claimer.next();
         __syncthreads();
 
         // ---------------- engine: regions 2*wave and 2*wave + 1
@@ -285,8 +296,9 @@ __global__ void __launch_bounds__(256, 2) mp_inner_kernel(MpInnerParams prm) {
                     __builtin_amdgcn_sched_barrier(0);
                 }
             }
-            // next unit's input (after the coefficient loads: the load
-            // counter retires in order)
+            // publish the unit after next; then the next unit's input (after
+            // the coefficient loads: the load counter retires in order)
+            if (tid == 0) s_claim[0] = (int)(c2 < total ? c2 : total);
             load_in(inext);
 
             inverse(a2[0], s_i1a, E, lane, i1_base, s_buf + (2 * wave) * Q);
@@ -295,7 +307,7 @@ __global__ void __launch_bounds__(256, 2) mp_inner_kernel(MpInnerParams prm) {
             __builtin_amdgcn_sched_barrier(0);
         }
         __syncthreads();
-
+        const int nn = s_claim[0];
         // ---------------- inverse inner outer stage, back to the workspace
         {
             uint32_t tw[4][CPT];
@@ -340,6 +352,8 @@ __global__ void __launch_bounds__(256, 2) mp_inner_kernel(MpInnerParams prm) {
                 }
             }
         }
+        cur = nxt;
+        nxt = nn;
     }
 }
 

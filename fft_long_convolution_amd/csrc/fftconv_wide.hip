@@ -45,25 +45,27 @@ __global__ void __launch_bounds__(32 * P, 2) wide_kernel(WideParams prm) {
     uint32_t* s_two = (uint32_t*)(s_i1a + 8 * 64);     // [k1 - 1][thread][column]
     uint32_t* s_buf = s_two + HALF * Q;                // [P sub-rows][Q]
     uint32_t* s_scr = s_buf + M;                       // [39 k_b slots][16 x]
+    int* s_claim = (int*)(s_scr + 39 * 16);            // [2] claimed row indices
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int g = lane >> 4, x = lane & 15;
     const int total = prm.B * prm.H;
-    // Rows are taken in channel-major order (index h * B + b).  At step t
-    // the grid covers indices [t G, (t + 1) G), and the G / 8 workgroups
-    // that share an XCD (consecutive dispatch ids go to consecutive XCDs)
-    // take a contiguous block of them: the few channels in flight on an XCD
-    // at a time keep their spectrum coefficients in that XCD's L2.
-    const int G = gridDim.x;
-    const int first = (blockIdx.x & 7) * (G >> 3) + (blockIdx.x >> 3);
-    if (first >= total) return;   // uniform over the workgroup
+    // Rows are taken in channel-major order (index h * B + b), claimed one
+    // row ahead by thread 0 from the counters of this workgroup's XCD group
+    // and published through LDS at the row's barriers.
+    const XcdClaim claimer(prm.ctr, gridDim.x, blockIdx.x);
 
     for (int i = tid; i < 8 * 64; i += T) {
         s_f1b[i] = ((const uint4*)prm.f1b)[i];
         s_i1a[i] = ((const uint4*)prm.i1a)[i];
     }
     for (int i = tid; i < HALF * Q / 4; i += T) ((uint4*)s_two)[i] = ((const uint4*)prm.two)[i];
+    if (tid == 0) {
+        const long long c0 = claimer.next(), c1 = claimer.next();
+        s_claim[0] = (int)(c0 < total ? c0 : total);
+        s_claim[1] = (int)(c1 < total ? c1 : total);
+    }
     Regs E;
     load_regs(E, prm.f2a, prm.i2b, prm.twf, lane);
 
@@ -107,19 +109,19 @@ __global__ void __launch_bounds__(32 * P, 2) wide_kernel(WideParams prm) {
             for (int j = 0; j < CPT; ++j) uin[n1][j] = __builtin_nontemporal_load(&un[32 * j]);
         }
     };
-    load_u(first);
     __syncthreads();
+    int cur = s_claim[0], nxt = s_claim[1];
+    if (cur >= total) return;   // uniform over the workgroup
+    load_u(cur);
 
     uint32_t* scr = s_scr + x;
     const int i1_base = (16 * (g >> 1) + x) * 4 + 2 * (g & 1);
 
-    const int steps = (total - first - 1) / G + 1;
-    for (int step = 0; step < steps; ++step) {
-        const int idx = first + step * G;
-        const int h = idx / prm.B, b = idx - h * prm.B;
+    while (cur < total) {
+        const int h = cur / prm.B, b = cur - h * prm.B;
         const long long mrow = (long long)b * prm.H + h;
-        // next row of this workgroup (the last one re-reads its own row)
-        const int inext = step + 1 < steps ? idx + G : idx;
+        // next row of this workgroup (past the end: re-read this row)
+        const int inext = nxt < total ? nxt : cur;
         // ---------------- outer forward stage
         {
             typedef Outer<IO> O;
@@ -154,6 +156,11 @@ __global__ void __launch_bounds__(32 * P, 2) wide_kernel(WideParams prm) {
                 }
             }
         }
+        // claim the row after next now: the atomic returns long before the
+        // value is published, and it is older than the loads it must not
+        // delay
+        long long c2 = 0;
+        if (tid == 0) c2 = claimer.next();
         __syncthreads();
 
         // ---------------- engine: sub-rows 2*wave and 2*wave + 1
@@ -194,9 +201,10 @@ __global__ void __launch_bounds__(32 * P, 2) wide_kernel(WideParams prm) {
                     __builtin_amdgcn_sched_barrier(0);
                 }
             }
-            // next row's input: issued only now, because the load counter
-            // retires in order and the coefficient loads above must not
-            // wait behind it
+            // publish the row after next; then the next row's input, issued
+            // only now because the load counter retires in order and the
+            // coefficient loads above must not wait behind it
+            if (tid == 0) s_claim[0] = (int)(c2 < total ? c2 : total);
             load_u(inext);
 
             // ---------------- inverse 1024-point DFT of both sub-rows
@@ -206,7 +214,7 @@ __global__ void __launch_bounds__(32 * P, 2) wide_kernel(WideParams prm) {
             __builtin_amdgcn_sched_barrier(0);
         }
         __syncthreads();
-
+        const int nn = s_claim[0];
         // ---------------- outer inverse stage and store
         {
             uint32_t R[P][CPT];
@@ -249,7 +257,18 @@ __global__ void __launch_bounds__(32 * P, 2) wide_kernel(WideParams prm) {
                     __builtin_nontemporal_store(O::to_io(zo[n1]), &yrow[n1 * Q + lofs + 32 * j]);
             }
         }
+        cur = nxt;
+        nxt = nn;
     }
+}
+
+// Clears the row-claim counters of one call (a kernel rather than a memset,
+// so the call can be captured in a graph).
+__global__ void claim_reset_kernel(uint32_t* ctr) { ctr[threadIdx.x] = 0u; }
+
+hipError_t launch_claim_reset(uint32_t* ctr, hipStream_t s) {
+    hipLaunchKernelGGL(claim_reset_kernel, dim3(1), dim3(kClaimWords), 0, s, ctr);
+    return hipGetLastError();
 }
 
 hipError_t launch_wide(int io, int P, const WideParams& p, int lds, hipStream_t s) {
