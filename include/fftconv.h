@@ -75,15 +75,22 @@ typedef struct fftconv_plan_info {
     int kernel_variant;       /* 0 = LDS-staged fused kernel,
                                  1 = register-resident row kernel (N = 32*16
                                      or 32*32, 16-bit I/O),
-                                 2 = three-pass (outer, inner, outer)       */
+                                 2 = three-pass, LDS-staged (fp32 I/O),
+                                 3 = one-workgroup-per-row kernel
+                                     (N = P*1024, P = 4, 8, 16, 16-bit I/O),
+                                 4 = column passes + slab-pair inner pass
+                                     (N >= 32K, 16-bit I/O)                */
 } fftconv_plan_info;
 
 /* Create a plan for length N, Monarch order p and I/O dtype.
  *  N: a power of two in [256, 4194304] (section 3.4 discusses lengths up to
  *     4M; section 4.2's tables span 256..4M).
  *  p: 0 picks the default factorisation for N; p >= 2 requests exactly p
- *     factors (each of 8, 16 or 32; the last one 16 or 32) and returns
- *     FFTCONV_ERR_UNSUPPORTED when N cannot be split that way.
+ *     factors and returns FFTCONV_ERR_UNSUPPORTED when N cannot be split
+ *     that way.  For the LDS-staged kernels the factors are 8, 16 or 32 (the
+ *     last one 16 or 32); 16-bit plans at N = 4K..16K use P x 32 x 32
+ *     (P = N/1024, p = 3) and at N >= 32K the outer levels followed by
+ *     4 x 32 x 32, whose order is fixed by N.
  * Builds the DFT matrices and twiddle tables in fp64 on the host, rounds
  * them to the kernel's operand types and uploads them synchronously.
  * On success *out receives the plan; on failure *out is set to NULL. */
@@ -105,8 +112,13 @@ void fftconv_plan_destroy(fftconv_plan_t plan);
 /* Bytes of the k_f buffer for H channels (caller allocates). */
 size_t fftconv_spectrum_bytes(fftconv_plan_t plan, size_t H);
 
-/* Bytes of the workspace fftconv_forward needs for B x H rows (0 on the
- * fused path; the caller allocates it). */
+/* Bytes of the workspace fftconv_forward needs for B x H rows; the caller
+ * allocates it.  0 for the row and LDS-staged fused kernels; 1 KB of work
+ * counters for the one-workgroup-per-row kernel; for the 16-bit multi-pass
+ * path one channel chunk of f16 complex rows (at most 256 MB unless a single
+ * channel is larger) plus the counters; B*H rows of fp32 complex for the
+ * fp32 multi-pass path.  A call owns its workspace until it completes: two
+ * calls in flight at once need two workspaces. */
 size_t fftconv_workspace_bytes(fftconv_plan_t plan, size_t B, size_t H);
 
 /* Kernel spectrum, computed once per channel and reused for every batch
