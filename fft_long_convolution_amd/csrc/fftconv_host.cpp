@@ -1099,11 +1099,32 @@ fftconv_status fftconv_forward(fftconv_plan_t plan, const void* u,
             G = G < 8 ? 8 : G & ~7LL;
             const long long need = (units + 7) & ~7LL;
             I.grid = (int)(G < need ? G : need);
-            e = launch_mp_col(io, s.mp_P1, 0, C1, st);
-            if (e == hipSuccess && s.mp_P2 > 1) e = launch_mp_col(io, s.mp_P2, 1, C2, st);
-            if (e == hipSuccess) e = launch_mp_inner(io, I, plan->lds_mp, st);
-            if (e == hipSuccess && s.mp_P2 > 1) e = launch_mp_col(io, s.mp_P2, 2, C2, st);
-            if (e == hipSuccess) e = launch_mp_col(io, s.mp_P1, 3, C1, st);
+            if (s.mp_P2 > 1) {
+                // both outer levels in one pass each way
+                MpCol2Params D{};
+                D.rows = C1.rows;
+                D.H = C1.H;
+                D.h0 = C1.h0;
+                D.hc = C1.hc;
+                D.M = C1.M;
+                D.tw1 = C1.tw;
+                D.tw2 = C2.tw;
+                D.u = u;
+                D.y = y;
+                D.ws = workspace;
+                D.ctr = C1.ctr;
+                // persistent workgroups, two per CU, a multiple of 16 (the
+                // tile count is a multiple of 64)
+                D.grid = (int)std::min<long long>(mp_col2_tiles(s.mp_P2, D.rows),
+                                                  std::max<long long>(16, (2LL * plan->num_cu) & ~15LL));
+                e = launch_mp_col2(io, s.mp_P1, s.mp_P2, false, D, st);
+                if (e == hipSuccess) e = launch_mp_inner(io, I, plan->lds_mp, st);
+                if (e == hipSuccess) e = launch_mp_col2(io, s.mp_P1, s.mp_P2, true, D, st);
+            } else {
+                e = launch_mp_col(io, s.mp_P1, 0, C1, st);
+                if (e == hipSuccess) e = launch_mp_inner(io, I, plan->lds_mp, st);
+                if (e == hipSuccess) e = launch_mp_col(io, s.mp_P1, 3, C1, st);
+            }
         }
     } else if (s.wide_P) {
         WideParams W = plan->wide;

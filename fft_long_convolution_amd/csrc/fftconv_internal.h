@@ -164,6 +164,23 @@ struct MpColParams {
 };
 hipError_t launch_mp_col(int io, int P, int mode, const MpColParams& p, hipStream_t s);
 
+// Both outer levels of a two-level plan in one pass (tiles of 512 / P2
+// columns with all P1 * P2 outer points; the level-1 results stay in LDS).
+struct MpCol2Params {
+    long long rows;        // B * hc rows of the chunk (as MpColParams)
+    int H, h0, hc;
+    int M;
+    int grid;              // persistent workgroups (<= tiles)
+    const float2* tw1;     // W_M^c, c < M / P1
+    const float2* tw2;     // W_{M/P1}^c, c < 4096
+    const void* u;
+    void* y;
+    void* ws;
+    uint32_t* ctr;         // forward pass: clears the inner pass's counters
+};
+long long mp_col2_tiles(int P2, long long rows);
+hipError_t launch_mp_col2(int io, int P1, int P2, bool inv, const MpCol2Params& p, hipStream_t s);
+
 struct MpInnerParams {
     int B, H, M;
     int h0, hc;            // channel chunk (workspace rows b * hc + h - h0)

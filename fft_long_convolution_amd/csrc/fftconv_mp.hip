@@ -116,6 +116,208 @@ __global__ void __launch_bounds__(256) mp_col_kernel(MpColParams prm) {
 }
 
 // ---------------------------------------------------------------------------
+// Both outer levels in one pass (two-level plans).  A tile is TC = 512 / P2
+// consecutive columns c of a row with all P1 * P2 outer points of each; the
+// level-1 results stay in LDS (f16, as the workspace would hold them), so
+// only the level-2 results travel through HBM; the inverse mirrors it.
+//   forward: task (c, n2): P1-point DFT over n1 of z[(P2 n1 + n2) 4096 + c]
+//     (P1/2 nonzero), twiddle W_M^{(n2 4096 + c) k1} -> LDS (k1, n2, c);
+//     task (c, k1): P2-point DFT over n2, twiddle W_{M/P1}^{c k2} ->
+//     workspace [k1][k2][c] (slab k1 P2 + k2);
+//   inverse: the same in reverse, only the n1 < P1/2 outputs (t < N) to y.
+// Workgroups of 256 threads (two per CU) are persistent: every global load
+// of the next tile (data and twiddles) is issued before the current tile's
+// second level, so HBM reads overlap the arithmetic and the stores.
+constexpr int kCol2Threads = 256;
+constexpr int col2_cols(int P2) { return 512 / P2; }
+
+template <int IO, int P1, int P2, bool INV>
+__global__ void __launch_bounds__(kCol2Threads, 2) mp_col2_kernel(MpCol2Params prm) {
+    constexpr int TC = col2_cols(P2), SLAB = 4096, TPR = SLAB / TC;
+    constexpr int NT = kCol2Threads;
+    constexpr int L1T = P2 * TC / NT;             // level-1 tasks per thread (2)
+    constexpr int L2T = P1 * TC / NT;             // level-2 tasks per thread (2 or 4)
+    static_assert(P2 <= P1 && P1 <= 2 * P2 && TC >= 16, "outer factor pair");
+    // LDS word of (k1, n2, c); n2 is rotated by k1 so that level-2 tasks of
+    // one wave (several k1) hit different banks
+    __shared__ uint32_t s_t[P1 * P2 * TC];
+    auto lidx = [](int k1, int n2, int c) { return (k1 * P2 + ((n2 + k1) & (P2 - 1))) * TC + c; };
+    const int tid = threadIdx.x;
+    const long long M2 = (long long)P2 * SLAB, M = (long long)P1 * M2;
+    const long long ntiles = prm.rows * TPR;
+    const float sc1 = rsqrtf((float)P1), sc2 = rsqrtf((float)P2);
+    // the first pass of a chunk clears the inner pass's claim counters
+    if (!INV && blockIdx.x == 0 && tid < kClaimWords) prm.ctr[tid] = 0u;
+
+    // Tiles 2k and 2k+1 share 128-byte lines (64 bytes each): they go to
+    // workgroups b and b + 8, which sit on the same XCD (blocks are dealt to
+    // the 8 XCDs round-robin), so one L2 fetch serves both.  The grid is a
+    // multiple of 16.
+    const int bid = blockIdx.x;
+    const long long tile0 = (bid & ~15) + 2 * (bid & 7) + ((bid >> 3) & 1);
+    auto row_of = [&](long long t, int& c0) {
+        const long long r = t / TPR;
+        c0 = (int)(t - r * TPR) * TC;
+        return r;
+    };
+    auto mem_row = [&](long long r) {
+        const long long bq = r / prm.hc;
+        return bq * prm.H + prm.h0 + (r - bq * prm.hc);
+    };
+
+    if constexpr (!INV) {
+        uint32_t raw[L1T][P1 / 2];
+        float2 tw1[L1T], tw2[L2T];
+        auto fetch = [&](long long t) {
+            int c0;
+            const long long r = row_of(t, c0);
+            const uint32_t* u = (const uint32_t*)prm.u + mem_row(r) * (M / 2) + c0;
+#pragma unroll
+            for (int i = 0; i < L1T; ++i) {
+                const int task = tid + i * NT;
+                const long long col = (long long)(task / TC) * SLAB + task % TC;
+#pragma unroll
+                for (int n1 = 0; n1 < P1 / 2; ++n1)
+                    raw[i][n1] = __builtin_nontemporal_load(&u[(long long)n1 * M2 + col]);
+                tw1[i] = prm.tw1[col + c0];
+            }
+#pragma unroll
+            for (int j = 0; j < L2T; ++j) tw2[j] = prm.tw2[c0 + (tid + j * NT) % TC];
+        };
+        long long t = tile0;
+        if (t < ntiles) fetch(t);
+#pragma unroll 1
+        for (; t < ntiles; t += gridDim.x) {
+            int c0;
+            const long long r = row_of(t, c0);
+            // level 1: P1-point DFT of the P1/2 nonzero inputs, twiddle, to LDS
+#pragma unroll
+            for (int i = 0; i < L1T; ++i) {
+                // one task at a time: interleaved tasks would not fit the registers
+                __builtin_amdgcn_sched_barrier(0);
+                const int task = tid + i * NT, c = task % TC, n2 = task / TC;
+                rfloat2 xin[P1 / 2], v[P1];
+#pragma unroll
+                for (int n1 = 0; n1 < P1 / 2; ++n1) xin[n1] = f2_from_io<IO>(raw[i][n1]) * sc1;
+                dft_half_in<P1>(xin, v);
+                const rfloat2 t1 = {tw1[i].x, tw1[i].y};
+                rfloat2 w = t1;
+                s_t[lidx(0, n2, c)] = pk2(v[0].x, v[0].y);
+#pragma unroll
+                for (int k1 = 1; k1 < P1; ++k1) {
+                    const rfloat2 a = fmul(v[k1], w);
+                    s_t[lidx(k1, n2, c)] = pk2(a.x, a.y);
+                    w = fmul(w, t1);
+                }
+            }
+            float2 tw2c[L2T];
+#pragma unroll
+            for (int j = 0; j < L2T; ++j) tw2c[j] = tw2[j];
+            __syncthreads();
+            if (t + gridDim.x < ntiles) fetch(t + gridDim.x);
+            // level 2: P2-point DFT over n2, twiddle, to the workspace
+            uint32_t* ws = (uint32_t*)prm.ws + r * M + c0;
+#pragma unroll
+            for (int j = 0; j < L2T; ++j) {
+                // one task at a time: interleaved tasks would not fit the registers
+                __builtin_amdgcn_sched_barrier(0);
+                const int task = tid + j * NT, c = task % TC, k1 = task / TC;
+                rfloat2 v[P2];
+#pragma unroll
+                for (int m = 0; m < P2; ++m) v[m] = f2_from_h2(s_t[lidx(k1, m, c)]) * sc2;
+                dft_small<P2, false>(v);
+                const rfloat2 t2 = {tw2c[j].x, tw2c[j].y};
+                rfloat2 w = t2;
+                uint32_t* o = ws + (long long)k1 * M2 + c;
+                __builtin_nontemporal_store(pk2(v[0].x, v[0].y), &o[0]);
+#pragma unroll
+                for (int k2 = 1; k2 < P2; ++k2) {
+                    const rfloat2 a = fmul(v[k2], w);
+                    __builtin_nontemporal_store(pk2(a.x, a.y), &o[(long long)k2 * SLAB]);
+                    w = fmul(w, t2);
+                }
+            }
+            __syncthreads();
+        }
+    } else {
+        uint32_t raw[L2T][P2];
+        float2 tw1[L1T], tw2[L2T];
+        auto fetch = [&](long long t) {
+            int c0;
+            const long long r = row_of(t, c0);
+            const uint32_t* ws = (const uint32_t*)prm.ws + r * M + c0;
+#pragma unroll
+            for (int j = 0; j < L2T; ++j) {
+                const int task = tid + j * NT, c = task % TC, k1 = task / TC;
+                const uint32_t* in = ws + (long long)k1 * M2 + c;
+#pragma unroll
+                for (int k2 = 0; k2 < P2; ++k2) raw[j][k2] = __builtin_nontemporal_load(&in[(long long)k2 * SLAB]);
+                tw2[j] = prm.tw2[c0 + c];
+            }
+#pragma unroll
+            for (int i = 0; i < L1T; ++i) {
+                const int task = tid + i * NT;
+                tw1[i] = prm.tw1[(long long)(task / TC) * SLAB + c0 + task % TC];
+            }
+        };
+        long long t = tile0;
+        if (t < ntiles) fetch(t);
+#pragma unroll 1
+        for (; t < ntiles; t += gridDim.x) {
+            int c0;
+            const long long r = row_of(t, c0);
+            // inverse level 2: conjugate twiddle, P2-point inverse DFT, to LDS
+#pragma unroll
+            for (int j = 0; j < L2T; ++j) {
+                // one task at a time: interleaved tasks would not fit the registers
+                __builtin_amdgcn_sched_barrier(0);
+                const int task = tid + j * NT, c = task % TC, k1 = task / TC;
+                const rfloat2 t2 = {tw2[j].x, tw2[j].y};
+                rfloat2 v[P2], w = t2;
+                v[0] = f2_from_h2(raw[j][0]) * sc2;
+#pragma unroll
+                for (int k2 = 1; k2 < P2; ++k2) {
+                    v[k2] = fmulc(f2_from_h2(raw[j][k2]) * sc2, w);
+                    w = fmul(w, t2);
+                }
+                dft_small<P2, true>(v);
+#pragma unroll
+                for (int m = 0; m < P2; ++m) s_t[lidx(k1, m, c)] = pk2(v[m].x, v[m].y);
+            }
+            float2 tw1c[L1T];
+#pragma unroll
+            for (int i = 0; i < L1T; ++i) tw1c[i] = tw1[i];
+            __syncthreads();
+            if (t + gridDim.x < ntiles) fetch(t + gridDim.x);
+            // inverse level 1: conjugate twiddle, P1-point inverse DFT, the
+            // P1/2 outputs t < N to y
+            uint32_t* y = (uint32_t*)prm.y + mem_row(r) * (M / 2) + c0;
+#pragma unroll
+            for (int i = 0; i < L1T; ++i) {
+                // one task at a time: interleaved tasks would not fit the registers
+                __builtin_amdgcn_sched_barrier(0);
+                const int task = tid + i * NT, c = task % TC, n2 = task / TC;
+                const rfloat2 t1 = {tw1c[i].x, tw1c[i].y};
+                rfloat2 v[P1], w = t1;
+                v[0] = f2_from_h2(s_t[lidx(0, n2, c)]) * sc1;
+#pragma unroll
+                for (int k1 = 1; k1 < P1; ++k1) {
+                    v[k1] = fmulc(f2_from_h2(s_t[lidx(k1, n2, c)]) * sc1, w);
+                    w = fmul(w, t1);
+                }
+                rfloat2 z[P1 / 2];
+                idft_half_out<P1>(v, z);
+                uint32_t* o = y + (long long)n2 * SLAB + c;
+#pragma unroll
+                for (int n1 = 0; n1 < P1 / 2; ++n1)
+                    __builtin_nontemporal_store(pk2io<IO>(z[n1].x, z[n1].y), &o[(long long)n1 * M2]);
+            }
+            __syncthreads();
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Inner pass: persistent workgroups of four waves, one unit (two 4096-point
 // slabs, eight 1024-point regions) at a time.
 //   pair unit (slabs of k_o and P_o - k_o):  wave j holds region 2j = slab
@@ -450,6 +652,34 @@ hipError_t col_dispatch(int P, int mode, const MpColParams& p, hipStream_t s) {
 hipError_t launch_mp_col(int io, int P, int mode, const MpColParams& p, hipStream_t s) {
     if (p.rows <= 0) return hipSuccess;
     return io == IO_BF16 ? col_dispatch<IO_BF16>(P, mode, p, s) : col_dispatch<IO_F16>(P, mode, p, s);
+}
+
+template <int IO, int P1, int P2>
+hipError_t col2_launch(bool inv, const MpCol2Params& p, hipStream_t s) {
+    const dim3 grid((unsigned)p.grid), blk(kCol2Threads);
+    if (inv) hipLaunchKernelGGL((mp_col2_kernel<IO, P1, P2, true>), grid, blk, 0, s, p);
+    else hipLaunchKernelGGL((mp_col2_kernel<IO, P1, P2, false>), grid, blk, 0, s, p);
+    return hipGetLastError();
+}
+
+template <int IO>
+hipError_t col2_dispatch(int P1, int P2, bool inv, const MpCol2Params& p, hipStream_t s) {
+    switch (P1 * 64 + P2) {
+    case 8 * 64 + 8: return col2_launch<IO, 8, 8>(inv, p, s);
+    case 16 * 64 + 8: return col2_launch<IO, 16, 8>(inv, p, s);
+    case 16 * 64 + 16: return col2_launch<IO, 16, 16>(inv, p, s);
+    case 32 * 64 + 16: return col2_launch<IO, 32, 16>(inv, p, s);
+    case 32 * 64 + 32: return col2_launch<IO, 32, 32>(inv, p, s);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+long long mp_col2_tiles(int P2, long long rows) { return rows * (4096 / col2_cols(P2)); }
+
+hipError_t launch_mp_col2(int io, int P1, int P2, bool inv, const MpCol2Params& p, hipStream_t s) {
+    if (p.rows <= 0) return hipSuccess;
+    if (p.grid <= 0 || p.grid % 16 || P2 > P1 || P1 > 2 * P2) return hipErrorInvalidValue;
+    return io == IO_BF16 ? col2_dispatch<IO_BF16>(P1, P2, inv, p, s) : col2_dispatch<IO_F16>(P1, P2, inv, p, s);
 }
 
 hipError_t launch_mp_inner(int io, const MpInnerParams& p, int lds, hipStream_t s) {

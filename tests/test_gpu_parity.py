@@ -94,6 +94,19 @@ def test_wide_kernel_batch_shapes(N, dtype, B, H):
     assert err < TOL[dtype]
 
 
+@pytest.mark.parametrize("N,dtype,B,H", [
+    (262144, "f16", 1, 3), (262144, "bf16", 2, 1), (524288, "bf16", 1, 2),
+    (1048576, "f16", 1, 2), (2097152, "bf16", 1, 1), (4194304, "f16", 1, 1)])
+def test_two_level_multipass(N, dtype, B, H):
+    # every factor pair of the two outer levels (8x8, 16x8, 16x16, 32x16,
+    # 32x32) through the passes that keep level 1 in LDS
+    w = inputs.Workload("twolevel", 100 + N.bit_length() + B, B, H, N, dtype,
+                        "normal", "decay", "two-level multi-pass")
+    err, _, _ = parity(w)
+    _say("two-level", N, dtype, B, H, "rel_l2", err)
+    assert err < TOL[dtype]
+
+
 def _plan_and_spectrum(N, dtype, H=3):
     import torch
     from fft_long_convolution_amd.fftconv import FFTConv
