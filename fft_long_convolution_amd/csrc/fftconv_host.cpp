@@ -762,11 +762,12 @@ fftconv_status build_device_tables(fftconv_plan_s* pl) {
         R.N = (int)s.N;
         pl->use_row = true;
         pl->row_nb = NB;
-        // fixed part: first/last stage tables, claim counter, exchange
-        // scratch of eight waves; the rest of a 128 KB budget (one
+        // fixed part: the four stage tables, claim counter, exchange
+        // scratch of every wave; the rest of a 144 KB budget (one
         // workgroup per CU) holds spectra
-        const int fixed = ((bf ? 8 : 4) + 4) * 64 * 16 + 16 + 8 * 16 * NB * 4;
-        pl->row_max_channels = (128 * 1024 - fixed) / ((int)s.M * 8);
+        const int tables = (bf ? 8 : 4) + 4 + (NB / 8) * (NB / 16) + (NB / 16) * 2 * (NB / 16);
+        const int fixed = tables * 64 * 16 + 16 + kRowWaves * 16 * NB * 4;
+        pl->row_max_channels = (144 * 1024 - fixed) / ((int)s.M * 8);
         pl->lds_row = fixed + (int)pl->row_max_channels * (int)s.M * 8;
     }
     if (s.wide_P) {

@@ -115,6 +115,8 @@ struct RowParams {
 };
 hipError_t launch_row(int io, int nb, const RowParams& p, int lds_bytes,
                       hipStream_t s);
+// Waves per row-kernel workgroup (one workgroup per CU).
+constexpr int kRowWaves = 16;
 
 // Fused kernel for N = P * 1024 (P = 4, 8, 16, 16-bit I/O): one workgroup
 // of P/2 wavefronts per row (fftconv_wide.hip).

@@ -25,7 +25,8 @@
 namespace fftconv {
 
 // Schedule: rows are taken in channel-major order (index = h*B + b) and each
-// workgroup (one per CU, eight waves: two per SIMD) owns one contiguous slice
+// workgroup (one per CU, sixteen waves: four per SIMD, so that one wave's
+// matrix products overlap another's vector arithmetic) owns one contiguous slice
 // of that order.  The spectrum coefficients of every channel the slice
 // touches are staged in LDS once at the start (lane-major, so every lane
 // reads its own consecutive entries); after that the row loop has no
@@ -34,12 +35,11 @@ namespace fftconv {
 // SIMD's arbitration favours simply takes more rows, so the waves of a CU
 // finish together.  Refills are unconditional (a claim past the end re-reads
 // the last row), so every row issues the same memory operations and the wait
-// counts stay exact.  The inner-stage tables and the twiddles stay in
-// registers for the whole kernel; the first/last stage tables are read from
-// LDS.  Input and output rows are touched once: non-temporal loads and
+// counts stay exact.  The twiddles stay in registers for the whole kernel;
+// the four stage tables are read from LDS at each use (keeping them in
+// registers would halve the waves per SIMD).  Input and output rows are touched once: non-temporal loads and
 // stores keep them from displacing the spectra in L2.
 constexpr int kRowDepth = 2;
-constexpr int kRowWaves = 8;
 
 template <int IO, int NB>
 __global__ void __launch_bounds__(64 * kRowWaves, 1) row_kernel(RowParams P) {
@@ -55,7 +55,9 @@ __global__ void __launch_bounds__(64 * kRowWaves, 1) row_kernel(RowParams P) {
     extern __shared__ uint4 s_lds[];
     uint4* s_f1b = s_lds;                            // [F1T][64]
     uint4* s_i1a = s_f1b + F1T * 64;                 // [4][64]
-    uint32_t* s_ctr = (uint32_t*)(s_i1a + 4 * 64);   // row claim counter (16 B)
+    uint4* s_f2a = s_i1a + 4 * 64;                   // [MT2][KS2][64]
+    uint4* s_i2b = s_f2a + MT2 * KS2 * 64;           // [KS2][2 NT][64]
+    uint32_t* s_ctr = (uint32_t*)(s_i2b + KS2 * 2 * NT * 64);   // row claim counter (16 B)
     uint32_t* s_scr = s_ctr + 4;                     // [waves][NB][16]
     uint2* s_ab = (uint2*)(s_scr + kRowWaves * NB * 16);   // [channels][bins per lane][64]
 
@@ -71,19 +73,9 @@ __global__ void __launch_bounds__(64 * kRowWaves, 1) row_kernel(RowParams P) {
     constexpr int TH = 64 * kRowWaves;
     for (int i = tid; i < F1T * 64; i += TH) s_f1b[i] = ((const uint4*)P.f1b)[i];
     for (int i = tid; i < 4 * 64; i += TH) s_i1a[i] = ((const uint4*)P.i1a)[i];
+    for (int i = tid; i < MT2 * KS2 * 64; i += TH) s_f2a[i] = ((const uint4*)P.f2a)[i];
+    for (int i = tid; i < KS2 * 2 * NT * 64; i += TH) s_i2b[i] = ((const uint4*)P.i2b)[i];
     if (tid == 0) s_ctr[0] = 0;
-    uint4 f2a[MT2][KS2];
-    uint4 i2b[KS2][2 * NT];
-#pragma unroll
-    for (int mt = 0; mt < MT2; ++mt)
-#pragma unroll
-        for (int ks = 0; ks < KS2; ++ks)
-            f2a[mt][ks] = ((const uint4*)P.f2a)[(mt * KS2 + ks) * 64 + lane];
-#pragma unroll
-    for (int ks = 0; ks < KS2; ++ks)
-#pragma unroll
-        for (int jt = 0; jt < 2 * NT; ++jt)
-            i2b[ks][jt] = ((const uint4*)P.i2b)[(ks * 2 * NT + jt) * 64 + lane];
     constexpr bool SYM = (NB == 32);
     uint32_t twf[IT][2][4], twi[SYM ? 1 : 2][SYM ? 1 : NT][4];
 #pragma unroll
@@ -200,7 +192,7 @@ __global__ void __launch_bounds__(64 * kRowWaves, 1) row_kernel(RowParams P) {
                 for (int mt = 0; mt < MT2; ++mt) {
                     rfloat4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                    for (int ks = 0; ks < KS2; ++ks) acc = mma_f16(f2a[mt][ks], b2[ks][kt], acc);
+                    for (int ks = 0; ks < KS2; ++ks) acc = mma_f16(s_f2a[(mt * KS2 + ks) * 64 + lane], b2[ks][kt], acc);
                     z[kt][mt][0] = pk2(acc[0], acc[1]);
                     z[kt][mt][1] = pk2(acc[2], acc[3]);
                 }
@@ -262,8 +254,8 @@ __global__ void __launch_bounds__(64 * kRowWaves, 1) row_kernel(RowParams P) {
                     rfloat4 re = {0.f, 0.f, 0.f, 0.f}, im = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                     for (int ks = 0; ks < KS2; ++ks) {
-                        re = mma_f16(a2[kt][ks], i2b[ks][2 * nt], re);
-                        im = mma_f16(a2[kt][ks], i2b[ks][2 * nt + 1], im);
+                        re = mma_f16(a2[kt][ks], s_i2b[(ks * 2 * NT + 2 * nt) * 64 + lane], re);
+                        im = mma_f16(a2[kt][ks], s_i2b[(ks * 2 * NT + 2 * nt + 1) * 64 + lane], im);
                     }
                     // conj twiddle W_M^{-k_a n_b}; pack as I1's B operand
                     uint32_t w[4];
