@@ -154,12 +154,15 @@ def main():
     outputs = w.rows * w.N
     value = outputs / (ms_step * 1e-3)
 
-    # ---- roofline of the dominant kernel (algorithmic bytes and flops per
-    # launch over the launch's own duration: median of single bracketed
-    # launches, the figure a kernel trace reports)
+    # ---- roofline of the dominant kernel: algorithmic bytes and flops per
+    # forward call over its average duration in the timed region (HIP events
+    # on the launch stream around K back-to-back calls; a kernel trace's
+    # average agrees up to the gaps between launches).  Individually
+    # bracketed launches (ms_median_single_launch) also carry the events' own
+    # overhead.
     kf_bytes = conv.spectrum_bytes(w.H)
     alg_bytes = 2 * w.rows * w.N * esz + kf_bytes
-    ms_kernel = ms_med
+    ms_kernel = ms_step
     achieved_gbs = alg_bytes / (ms_kernel * 1e-3) / 1e9
     flops = info["mfma_flops_per_row"] * w.rows
     achieved_tf = flops / (ms_kernel * 1e-3) / 1e12

@@ -56,17 +56,21 @@ __device__ __forceinline__ rfloat2 f2_from_io(uint32_t v) {
 // level, writing the P/2 outputs t < N to y.
 template <int IO, int P, int MODE>
 __global__ void __launch_bounds__(256) mp_col_kernel(MpColParams prm) {
-    const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
     // the first pass of a chunk clears the inner pass's claim counters
     if (MODE == 0 && blockIdx.x == 0 && threadIdx.x < kClaimWords) prm.ctr[threadIdx.x] = 0u;
-    const long long per_row = (long long)prm.M / P;   // columns of a row
-    const long long row = i / per_row;
+    // M / P columns per row and S are powers of two and M / P is a multiple
+    // of the block size, so the row is uniform over the block: shifts, and
+    // one 32-bit division per block, instead of per-thread 64-bit divisions
+    const int lg_row = __builtin_ctz((unsigned)prm.M) - __builtin_ctz((unsigned)P);
+    const int lg_s = __builtin_ctz((unsigned)prm.S);
+    const unsigned i0 = blockIdx.x * 256u;
+    const long long row = (long long)(i0 >> lg_row);
     if (row >= prm.rows) return;
-    const int rem = (int)(i - row * per_row);
-    const int blk = rem / prm.S, c = rem - blk * prm.S;
+    const int rem = (int)(i0 & ((1u << lg_row) - 1u)) + (int)threadIdx.x;
+    const int blk = rem >> lg_s, c = rem & (prm.S - 1);
     // input/output row in memory: batch row / hc, channel h0 + row % hc
-    const long long bq = row / prm.hc;
-    const long long mrow = bq * prm.H + prm.h0 + (row - bq * prm.hc);
+    const unsigned bq = (unsigned)row / (unsigned)prm.hc;
+    const long long mrow = (long long)bq * prm.H + prm.h0 + ((unsigned)row - bq * (unsigned)prm.hc);
     const float sc = rsqrtf((float)P);
     const float2 tt = prm.tw[c];   // W_{P S}^c
     const rfloat2 t1 = {tt.x, tt.y};
@@ -161,8 +165,8 @@ __global__ void __launch_bounds__(kCol2Threads, 2) mp_col2_kernel(MpCol2Params p
         return r;
     };
     auto mem_row = [&](long long r) {
-        const long long bq = r / prm.hc;
-        return bq * prm.H + prm.h0 + (r - bq * prm.hc);
+        const unsigned bq = (unsigned)r / (unsigned)prm.hc;
+        return (long long)bq * prm.H + prm.h0 + ((unsigned)r - bq * (unsigned)prm.hc);
     };
 
     if constexpr (!INV) {
@@ -379,14 +383,16 @@ __global__ void __launch_bounds__(256, 2) mp_inner_kernel(MpInnerParams prm) {
             tw[m][3] = v.w;
         }
     };
-    auto sigma = [&](int ko) { return (ko % prm.P1) * prm.P2 + ko / prm.P1; };
+    // P1 and the units per row are powers of two: shifts and masks
+    const int lg_p1 = __builtin_ctz((unsigned)prm.P1), lg_upr = __builtin_ctz((unsigned)upr);
+    auto sigma = [&](int ko) { return (ko & (prm.P1 - 1)) * prm.P2 + (ko >> lg_p1); };
     // unit -> (row, q, slabs)
     // row is the workspace row of the unit (b * hc + local channel), h the
     // channel (its spectrum coefficients)
     auto unit_rows = [&](int idx, long long& row, int& h, int& q, int& sa, int& sb) {
-        const int hq = idx / prm.B, b = idx - hq * prm.B;
-        const int hl = hq / upr;
-        q = hq - hl * upr;
+        const int hq = (int)((unsigned)idx / (unsigned)prm.B), b = idx - hq * prm.B;
+        const int hl = hq >> lg_upr;
+        q = hq & (upr - 1);
         h = prm.h0 + hl;
         row = (long long)b * prm.hc + hl;
         sa = sigma(q);
@@ -651,6 +657,12 @@ hipError_t col_dispatch(int P, int mode, const MpColParams& p, hipStream_t s) {
 
 hipError_t launch_mp_col(int io, int P, int mode, const MpColParams& p, hipStream_t s) {
     if (p.rows <= 0) return hipSuccess;
+    // the kernel's index math: power-of-two M and S, whole blocks per row,
+    // 32-bit thread indices
+    const long long per_row = (long long)p.M / (P > 0 ? P : 1);
+    if (P <= 0 || (p.M & (p.M - 1)) || (p.S & (p.S - 1)) || per_row % 256 ||
+        p.rows * per_row > (1LL << 32))
+        return hipErrorInvalidValue;
     return io == IO_BF16 ? col_dispatch<IO_BF16>(P, mode, p, s) : col_dispatch<IO_F16>(P, mode, p, s);
 }
 

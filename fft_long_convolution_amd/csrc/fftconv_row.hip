@@ -120,10 +120,20 @@ __global__ void __launch_bounds__(64 * kRowWaves, 1) row_kernel(RowParams P) {
         if (lane == 0) c = atomicAdd(s_ctr, 1u);
         return (int)__builtin_amdgcn_readfirstlane(c);
     };
+    // slice position -> (channel, batch) by stepping from the slice's first
+    // row: a slice spans only the few channels whose spectra fit the LDS, so
+    // this takes a handful of scalar steps where a 64-bit division would take
+    // over a hundred
+    const int b_lo = (int)(r0 - (long long)h_lo * P.B);
     auto row_of = [&](int c, int& h, int& b) {
-        const long long idx = r0 + (c < nslice ? c : nslice - 1);
-        h = (int)(idx / P.B);
-        b = (int)(idx - (long long)h * P.B);
+        int off = b_lo + (c < nslice ? c : nslice - 1);
+        int hh = h_lo;
+        while (off >= P.B) {
+            off -= P.B;
+            ++hh;
+        }
+        h = hh;
+        b = off;
     };
     auto load_row = [&](uint32_t (&dst)[IT][4], int c) {
         int h, b;
