@@ -46,7 +46,11 @@ class PlanInfo(ctypes.Structure):
                 "workspace_bytes_per_row": self.workspace_bytes_per_row,
                 "mfma_flops_per_row": self.mfma_flops_per_row,
                 "kernel": {0: "fused_kernel", 1: "row_kernel", 3: "wide_kernel",
-                           4: "mp_col_kernel+mp_inner_kernel",
+                           # one outer level: per-column passes; two: both
+                           # levels in one column pass each way
+                           4: ("mp_col2_kernel+mp_inner_kernel"
+                               if self.outer_factors > 1 else
+                               "mp_col_kernel+mp_inner_kernel"),
                            2: "outer_fwd_kernel+inner_kernel+outer_inv_kernel"
                            }[self.kernel_variant]}
 
