@@ -567,6 +567,64 @@ std::vector<uint16_t> mp_inner_twiddles() {
     return out;
 }
 
+// Matrix-core two-level forward pass (P1 = P2 = 32): A operands of a
+// 32-point DFT (scaled 1/sqrt(32)) over the first nin inputs, as hi/lo
+// pairs of 16-bit values (bf16 or f16), [mt 4][ks][hi/lo][lane][8]:
+// lane (g, x) holds real row 16 mt + x (output digit and re/im) and real
+// columns 32 ks + 8 g .. + 7 (input digit and re/im).
+std::vector<uint16_t> col2m_dft_a(bool bf16, int nin) {
+    const int KS = nin * 2 / 32;
+    std::vector<uint16_t> out((size_t)4 * KS * 2 * 64 * 8);
+    const double sc = 1.0 / sqrt(32.0);
+    for (int mt = 0; mt < 4; ++mt)
+        for (int ks = 0; ks < KS; ++ks)
+            for (int lane = 0; lane < 64; ++lane)
+                for (int i = 0; i < 8; ++i) {
+                    const int g = lane >> 4, x = lane & 15;
+                    const int R = 16 * mt + x, kk = 32 * ks + 8 * g + i;
+                    const int o = R >> 1, ro = R & 1, n = kk >> 1, ki = kk & 1;
+                    const double ang = -2.0 * M_PI * (double)((o * n) % 32) / 32.0;
+                    const double fr = cos(ang) * sc, fi = sin(ang) * sc;
+                    const double v = ro == 0 ? (ki == 0 ? fr : -fi) : (ki == 0 ? fi : fr);
+                    uint16_t hi, lo;
+                    if (bf16) {
+                        hi = f32_to_bf16_bits((float)v);
+                        lo = f32_to_bf16_bits((float)(v - (double)bf16_bits_to_f32(hi)));
+                    } else {
+                        hi = f32_to_f16_bits((float)v);
+                        _Float16 hh;
+                        memcpy(&hh, &hi, 2);
+                        lo = f32_to_f16_bits((float)(v - (double)(float)hh));
+                    }
+                    for (int hl = 0; hl < 2; ++hl)
+                        out[((((size_t)(mt * KS + ks) * 2 + hl) * 64 + lane) * 8) + i] = hl ? lo : hi;
+                }
+    return out;
+}
+
+// Twiddles of the matrix-core forward pass (fp32 pairs, computed in fp64):
+// [W_1024^{n2 k1}: 32 x 32][W_M^{32 i k1}: 128 x 32][W_M^{c k1}: 32 x 32]
+// [W_M^{1024 i k2}: 128 x 32][W_M^{32 c k2}: 32 x 32]
+std::vector<float> col2m_twiddles(long long M) {
+    std::vector<float> out;
+    auto put = [&](long long num, long long den) {
+        const double ang = -2.0 * M_PI * (double)(num % den) / (double)den;
+        out.push_back((float)cos(ang));
+        out.push_back((float)sin(ang));
+    };
+    for (int n2 = 0; n2 < 32; ++n2)
+        for (int k = 0; k < 32; ++k) put((long long)n2 * k, 1024);
+    for (int i = 0; i < 128; ++i)
+        for (int k = 0; k < 32; ++k) put(32LL * i * k, M);
+    for (int c = 0; c < 32; ++c)
+        for (int k = 0; k < 32; ++k) put((long long)c * k, M);
+    for (int i = 0; i < 128; ++i)
+        for (int k = 0; k < 32; ++k) put(1024LL * i * k, M);
+    for (int c = 0; c < 32; ++c)
+        for (int k = 0; k < 32; ++k) put(32LL * c * k, M);
+    return out;
+}
+
 // Column-pass twiddle bases W_n^c, c < count, fp32 (computed in fp64).
 std::vector<float> col_twiddles(long long n, long long count) {
     std::vector<float> out((size_t)count * 2);
@@ -600,6 +658,9 @@ struct fftconv_plan_s {
     WideParams wide{};
     int lds_mp = 0;
     MpInnerParams mp{};
+    const uint4* mp2m_a1 = nullptr;   // matrix-core forward pass (4M): level-1 A operands
+    const uint4* mp2m_a2 = nullptr;   //   level-2 A operands
+    const float2* mp2m_tm = nullptr;  //   twiddle tables
     const float2* mp_tw1 = nullptr;   // W_M^c, c < M / P1
     const float2* mp_tw2 = nullptr;   // W_{M/P1}^c, c < 4096 (two levels)
 };
@@ -835,6 +896,16 @@ fftconv_status build_mp_tables(fftconv_plan_s* pl) {
         std::vector<float> t2 = col_twiddles((long long)s.M / s.mp_P1, 4096);
         if (upload(pl, t2.data(), t2.size() * 4, &d) != hipSuccess) return FFTCONV_ERR_HIP;
         pl->mp_tw2 = (const float2*)d;
+    }
+    if (s.mp_P1 == 32 && s.mp_P2 == 32) {
+        std::vector<uint16_t> a1 = col2m_dft_a(s.dtype == FFTCONV_BF16, 16), a2 = col2m_dft_a(false, 32);
+        std::vector<float> tm = col2m_twiddles((long long)s.M);
+        if (upload(pl, a1.data(), a1.size() * 2, &d) != hipSuccess) return FFTCONV_ERR_HIP;
+        pl->mp2m_a1 = (const uint4*)d;
+        if (upload(pl, a2.data(), a2.size() * 2, &d) != hipSuccess) return FFTCONV_ERR_HIP;
+        pl->mp2m_a2 = (const uint4*)d;
+        if (upload(pl, tm.data(), tm.size() * 4, &d) != hipSuccess) return FFTCONV_ERR_HIP;
+        pl->mp2m_tm = (const float2*)d;
     }
     // stage tables (16 KB) + inner twiddles (16 KB) + two slabs of f16
     // points (32 KB) + the k_b exchange
@@ -1118,7 +1189,18 @@ fftconv_status fftconv_forward(fftconv_plan_t plan, const void* u,
                 // tile count is a multiple of 64)
                 D.grid = (int)std::min<long long>(mp_col2_tiles(s.mp_P2, D.rows),
                                                   std::max<long long>(16, (2LL * plan->num_cu) & ~15LL));
-                e = launch_mp_col2(io, s.mp_P1, s.mp_P2, false, D, st);
+                if (plan->mp2m_a1) {
+                    // P1 = P2 = 32: the forward pass on the matrix cores,
+                    // one workgroup per CU
+                    MpCol2Params F = D;
+                    F.a1 = plan->mp2m_a1;
+                    F.a2 = plan->mp2m_a2;
+                    F.tm = plan->mp2m_tm;
+                    F.grid = (int)std::min<long long>(D.rows * 128, plan->num_cu);
+                    e = launch_mp_col2m_fwd(io, F, st);
+                } else {
+                    e = launch_mp_col2(io, s.mp_P1, s.mp_P2, false, D, st);
+                }
                 if (e == hipSuccess) e = launch_mp_inner(io, I, plan->lds_mp, st);
                 if (e == hipSuccess) e = launch_mp_col2(io, s.mp_P1, s.mp_P2, true, D, st);
             } else {

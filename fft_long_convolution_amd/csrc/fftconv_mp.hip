@@ -47,6 +47,14 @@ __device__ __forceinline__ rfloat2 f2_from_io(uint32_t v) {
     }
 }
 
+// Exchange between 16-lane rows: the odd rows of a trade places with the
+// even rows of c (rows 1 <-> 0 and 3 <-> 2).
+__device__ __forceinline__ void swap16(uint32_t& a, uint32_t& c) {
+    const auto r = __builtin_amdgcn_permlane16_swap(a, c, false, false);
+    a = r[0];
+    c = r[1];
+}
+
 }  // namespace
 
 // ---------------------------------------------------------------------------
@@ -318,6 +326,212 @@ __global__ void __launch_bounds__(kCol2Threads, 2) mp_col2_kernel(MpCol2Params p
             }
             __syncthreads();
         }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Forward two-level column pass on the matrix cores, P1 = P2 = 32 (M = 4M).
+// A tile is 32 columns c (c0 .. c0 + 31 of the 4096-point slab) with all
+// 1024 outer points; one workgroup of eight waves per CU holds it in LDS.
+//   level 1: for each (n2, c) the 32-point DFT over n1 (16 nonzero inputs)
+//     as 16 x 16 x 32 products (A = DFT matrix as a hi/lo pair, B = 16
+//     tasks); twiddle W_M^{(4096 n2 + c0 + c) k1} = W_1024^{n2 k1} x
+//     W_M^{(c0 + c) k1} from LDS tables; to LDS as f16;
+//   level 2: for each (k1, c) the 32-point DFT over n2; twiddle
+//     W_M^{32 (c0 + c) k2}; to the workspace [k1][k2][c] as f16.
+// Every DFT entry is a hi/lo pair of 16-bit values, so the products are as
+// accurate as fp32 arithmetic; the roundings are the same two f16 stores as
+// in the vector-ALU pass.  Loads and stores cover whole 128-byte lines: lane
+// groups g and g + 1 take the two 16-column halves of a row, and one
+// exchange between 16-lane rows rearranges them into (or out of) operands.
+// The intermediate is stored [k1][c][n2] with the 16-byte granule n2 / 4
+// xor-ed with c % 8 (conflict-free 128-bit accesses).
+template <int IO>
+__global__ void __launch_bounds__(512, 2) mp_col2m_fwd_kernel(MpCol2Params prm) {
+    constexpr int SLAB = 4096, TC = 32, TPR = SLAB / TC;
+    constexpr long long M2 = 32LL * SLAB, M = 32LL * M2;
+    extern __shared__ uint4 s_lds[];
+    uint4* s_mid = s_lds;                                   // 8192 granules
+    float2* s_tw1 = (float2*)(s_mid + 8192);                // [k1][c]
+    float2* s_tw2 = s_tw1 + 1024;                           // [k2][c]
+    float2* s_twn = s_tw2 + 1024;                           // [n2][k1]
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int g = lane >> 4, x = lane & 15;
+    const long long ntiles = prm.rows * TPR;
+    if (blockIdx.x == 0 && tid < kClaimWords) prm.ctr[tid] = 0u;
+
+    uint4 a1[4][2], a2[4][2][2];
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+#pragma unroll
+        for (int hl = 0; hl < 2; ++hl) a1[mt][hl] = prm.a1[(mt * 2 + hl) * 64 + lane];
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+            for (int hl = 0; hl < 2; ++hl) a2[mt][ks][hl] = prm.a2[((mt * 2 + ks) * 2 + hl) * 64 + lane];
+    }
+    const float2* g_twn = prm.tm;
+    const float2* g_1 = g_twn + 1024;
+    const float2* g_1b = g_1 + 4096;
+    const float2* g_2 = g_1b + 1024;
+    const float2* g_2b = g_2 + 4096;
+    for (int i = tid; i < 1024; i += 512) s_twn[i] = g_twn[i];
+
+    auto mma = [](uint4 a, uint4 b, rfloat4 c) {
+        return IO == IO_BF16 ? mma_bf16(a, b, c) : mma_f16(a, b, c);
+    };
+    auto cmulf = [](float2 a, float2 b) { return make_float2(a.x * b.x - a.y * b.y, a.x * b.y + a.y * b.x); };
+    auto mid = [](int k1, int c, int gr) { return (k1 * 32 + c) * 8 + (gr ^ (c & 7)); };
+    auto tile_of = [&](long long t, int& c0) {
+        const long long r = t / TPR;
+        c0 = (int)(t - r * TPR) * TC;
+        return r;
+    };
+    // per-tile twiddle tables, [k][c] (lanes of a group read 16 columns c of
+    // one k: distinct banks): entry (k, c) = G[c0 / 32][k] Gb[c][k]
+    float2 tg[2][2];   // loaded operands of this thread's two entries
+    auto tw_load = [&](const float2* G, const float2* Gb, int c0) {
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+            const int e = tid + 512 * q, k = e >> 5, c = e & 31;
+            tg[q][0] = G[(c0 >> 5) * 32 + k];
+            tg[q][1] = Gb[c * 32 + k];
+        }
+    };
+    auto tw_store = [&](float2* T) {
+#pragma unroll
+        for (int q = 0; q < 2; ++q) T[tid + 512 * q] = cmulf(tg[q][0], tg[q][1]);
+    };
+    // next tile's input: wave w takes n2 = 4 w + j; lane (g, x) loads rows
+    // n1 = 8 (g / 2) + r of column 16 (g % 2) + x
+    uint32_t raw[4][8];
+    auto fetch = [&](long long t) {
+        int c0;
+        const long long r = tile_of(t, c0);
+        const unsigned bq = (unsigned)r / (unsigned)prm.hc;
+        const long long mrow = (long long)bq * prm.H + prm.h0 + ((unsigned)r - bq * (unsigned)prm.hc);
+        const uint32_t* u = (const uint32_t*)prm.u + mrow * (M / 2) + (long long)(8 * (g >> 1)) * M2 +
+                            (long long)(4 * wave) * SLAB + c0 + 16 * (g & 1) + x;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int q = 0; q < 8; ++q) raw[j][q] = __builtin_nontemporal_load(&u[q * M2 + j * SLAB]);
+    };
+
+    long long t = blockIdx.x;
+    if (t < ntiles) {
+        int c0;
+        tile_of(t, c0);
+        tw_load(g_1, g_1b, c0);
+        tw_store(s_tw1);
+        fetch(t);
+    }
+    __syncthreads();
+#pragma unroll 1
+    for (; t < ntiles; t += gridDim.x) {
+        int c0;
+        const long long r = tile_of(t, c0);
+        tw_load(g_2, g_2b, c0);       // level-2 table of this tile, stored below
+        // ---------------- level 1
+        {
+            uint4 bop[4][2];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+#pragma unroll
+                for (int q = 0; q < 4; ++q) swap16(raw[j][q], raw[j][q + 4]);
+                bop[j][0] = make_uint4(raw[j][0], raw[j][1], raw[j][2], raw[j][3]);
+                bop[j][1] = make_uint4(raw[j][4], raw[j][5], raw[j][6], raw[j][7]);
+            }
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt) {
+                rfloat4 cc[2][4];
+#pragma unroll
+                for (int h = 0; h < 2; ++h)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        rfloat4 acc = {0.f, 0.f, 0.f, 0.f};
+                        acc = mma(a1[mt][0], bop[j][h], acc);
+                        cc[h][j] = mma(a1[mt][1], bop[j][h], acc);
+                    }
+#pragma unroll
+                for (int e = 0; e < 2; ++e) {
+                    const int k1 = 8 * mt + 2 * g + e;
+                    float2 tn[4];
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) tn[j] = s_twn[(4 * wave + j) * 32 + k1];
+#pragma unroll
+                    for (int h = 0; h < 2; ++h) {
+                        const int c = 16 * h + x;
+                        const float2 t1 = s_tw1[k1 * 32 + c];
+                        uint32_t v[4];
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) {
+                            const float2 tw = cmulf(tn[j], t1);
+                            const float2 a = cmulf(make_float2(cc[h][j][2 * e], cc[h][j][2 * e + 1]), tw);
+                            v[j] = pk2(a.x, a.y);
+                        }
+                        s_mid[mid(k1, c, wave)] = make_uint4(v[0], v[1], v[2], v[3]);
+                    }
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+        tw_store(s_tw2);
+        __syncthreads();
+        const long long tn_ = t + gridDim.x;
+        if (tn_ < ntiles) {
+            int c0n;
+            tile_of(tn_, c0n);
+            tw_load(g_1, g_1b, c0n);   // older than the input loads: no wait on them
+            fetch(tn_);
+        }
+        // ---------------- level 2: wave w takes k1 = 4 w + j
+        {
+            uint32_t* ws = (uint32_t*)prm.ws + r * M + c0 + 16 * (g & 1) + x;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int k1 = 4 * wave + j;
+                uint4 b[2][2];
+#pragma unroll
+                for (int h = 0; h < 2; ++h)
+#pragma unroll
+                    for (int ks = 0; ks < 2; ++ks) b[h][ks] = s_mid[mid(k1, 16 * h + x, 4 * ks + g)];
+#pragma unroll
+                for (int mt = 0; mt < 4; ++mt) {
+                    uint32_t o[2][2];
+#pragma unroll
+                    for (int h = 0; h < 2; ++h) {
+                        rfloat4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                        for (int ks = 0; ks < 2; ++ks) {
+                            acc = mma_f16(a2[mt][ks][0], b[h][ks], acc);
+                            acc = mma_f16(a2[mt][ks][1], b[h][ks], acc);
+                        }
+                        const int c = 16 * h + x;
+#pragma unroll
+                        for (int e = 0; e < 2; ++e) {
+                            const float2 a = cmulf(make_float2(acc[2 * e], acc[2 * e + 1]),
+                                                   s_tw2[(8 * mt + 2 * g + e) * 32 + c]);
+                            o[h][e] = pk2(a.x, a.y);
+                        }
+                    }
+                    // lane group g holds k2 = 8 mt + 2 g + e of both halves:
+                    // exchange so each store covers a whole line of row
+                    // k2 = 8 mt + 4 (g / 2) + e (+ 2 for the second value)
+#pragma unroll
+                    for (int e = 0; e < 2; ++e) {
+                        swap16(o[0][e], o[1][e]);
+                        const int k2 = 8 * mt + 4 * (g >> 1) + e;
+                        __builtin_nontemporal_store(o[0][e], &ws[(long long)k1 * M2 + (long long)k2 * SLAB]);
+                        __builtin_nontemporal_store(o[1][e], &ws[(long long)k1 * M2 + (long long)(k2 + 2) * SLAB]);
+                    }
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+        if (tn_ < ntiles) tw_store(s_tw1);
+        __syncthreads();
     }
 }
 
@@ -692,6 +906,21 @@ hipError_t launch_mp_col2(int io, int P1, int P2, bool inv, const MpCol2Params& 
     if (p.rows <= 0) return hipSuccess;
     if (p.grid <= 0 || p.grid % 16 || P2 > P1 || P1 > 2 * P2) return hipErrorInvalidValue;
     return io == IO_BF16 ? col2_dispatch<IO_BF16>(P1, P2, inv, p, s) : col2_dispatch<IO_F16>(P1, P2, inv, p, s);
+}
+
+template <int IO>
+static hipError_t col2m_fwd_t(const MpCol2Params& p, hipStream_t s) {
+    const hipError_t e = hipFuncSetAttribute((const void*)mp_col2m_fwd_kernel<IO>,
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, kCol2mLds);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((mp_col2m_fwd_kernel<IO>), dim3((unsigned)p.grid), dim3(512), kCol2mLds, s, p);
+    return hipGetLastError();
+}
+
+hipError_t launch_mp_col2m_fwd(int io, const MpCol2Params& p, hipStream_t s) {
+    if (p.rows <= 0) return hipSuccess;
+    if (p.grid <= 0 || p.M != 4194304 || !p.a1 || !p.a2 || !p.tm) return hipErrorInvalidValue;
+    return io == IO_BF16 ? col2m_fwd_t<IO_BF16>(p, s) : col2m_fwd_t<IO_F16>(p, s);
 }
 
 hipError_t launch_mp_inner(int io, const MpInnerParams& p, int lds, hipStream_t s) {
