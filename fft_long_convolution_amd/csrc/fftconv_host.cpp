@@ -567,23 +567,24 @@ std::vector<uint16_t> mp_inner_twiddles() {
     return out;
 }
 
-// Matrix-core two-level forward pass (P1 = P2 = 32): A operands of a
-// 32-point DFT (scaled 1/sqrt(32)) over the first nin inputs, as hi/lo
-// pairs of 16-bit values (bf16 or f16), [mt 4][ks][hi/lo][lane][8]:
+// Matrix-core two-level passes (P1 = P2 = 32): A operands of a 32-point
+// DFT (scaled 1/sqrt(32); inverse: exponent sign +) over the first nin
+// inputs and nout outputs, as hi/lo pairs of 16-bit values (bf16 or f16),
+// [mt][ks][hi/lo][lane][8]:
 // lane (g, x) holds real row 16 mt + x (output digit and re/im) and real
 // columns 32 ks + 8 g .. + 7 (input digit and re/im).
-std::vector<uint16_t> col2m_dft_a(bool bf16, int nin) {
-    const int KS = nin * 2 / 32;
-    std::vector<uint16_t> out((size_t)4 * KS * 2 * 64 * 8);
+std::vector<uint16_t> col2m_dft_a(bool bf16, int nin, int nout = 32, bool inverse = false) {
+    const int KS = nin * 2 / 32, MT = nout * 2 / 16;
+    std::vector<uint16_t> out((size_t)MT * KS * 2 * 64 * 8);
     const double sc = 1.0 / sqrt(32.0);
-    for (int mt = 0; mt < 4; ++mt)
+    for (int mt = 0; mt < MT; ++mt)
         for (int ks = 0; ks < KS; ++ks)
             for (int lane = 0; lane < 64; ++lane)
                 for (int i = 0; i < 8; ++i) {
                     const int g = lane >> 4, x = lane & 15;
                     const int R = 16 * mt + x, kk = 32 * ks + 8 * g + i;
                     const int o = R >> 1, ro = R & 1, n = kk >> 1, ki = kk & 1;
-                    const double ang = -2.0 * M_PI * (double)((o * n) % 32) / 32.0;
+                    const double ang = (inverse ? 2.0 : -2.0) * M_PI * (double)((o * n) % 32) / 32.0;
                     const double fr = cos(ang) * sc, fi = sin(ang) * sc;
                     const double v = ro == 0 ? (ki == 0 ? fr : -fi) : (ki == 0 ? fi : fr);
                     uint16_t hi, lo;
@@ -660,6 +661,8 @@ struct fftconv_plan_s {
     MpInnerParams mp{};
     const uint4* mp2m_a1 = nullptr;   // matrix-core forward pass (4M): level-1 A operands
     const uint4* mp2m_a2 = nullptr;   //   level-2 A operands
+    const uint4* mp2m_ia1 = nullptr;  // inverse pass: level-1 inverse A operands
+    const uint4* mp2m_ia2 = nullptr;  //   level-2 inverse A operands
     const float2* mp2m_tm = nullptr;  //   twiddle tables
     const float2* mp_tw1 = nullptr;   // W_M^c, c < M / P1
     const float2* mp_tw2 = nullptr;   // W_{M/P1}^c, c < 4096 (two levels)
@@ -906,6 +909,11 @@ fftconv_status build_mp_tables(fftconv_plan_s* pl) {
         pl->mp2m_a2 = (const uint4*)d;
         if (upload(pl, tm.data(), tm.size() * 4, &d) != hipSuccess) return FFTCONV_ERR_HIP;
         pl->mp2m_tm = (const float2*)d;
+        std::vector<uint16_t> ia1 = col2m_dft_a(false, 32, 16, true), ia2 = col2m_dft_a(false, 32, 32, true);
+        if (upload(pl, ia1.data(), ia1.size() * 2, &d) != hipSuccess) return FFTCONV_ERR_HIP;
+        pl->mp2m_ia1 = (const uint4*)d;
+        if (upload(pl, ia2.data(), ia2.size() * 2, &d) != hipSuccess) return FFTCONV_ERR_HIP;
+        pl->mp2m_ia2 = (const uint4*)d;
     }
     // stage tables (16 KB) + inner twiddles (16 KB) + two slabs of f16
     // points (32 KB) + the k_b exchange
@@ -1202,7 +1210,18 @@ fftconv_status fftconv_forward(fftconv_plan_t plan, const void* u,
                     e = launch_mp_col2(io, s.mp_P1, s.mp_P2, false, D, st);
                 }
                 if (e == hipSuccess) e = launch_mp_inner(io, I, plan->lds_mp, st);
-                if (e == hipSuccess) e = launch_mp_col2(io, s.mp_P1, s.mp_P2, true, D, st);
+                if (e == hipSuccess) {
+                    if (plan->mp2m_ia1) {
+                        MpCol2Params F = D;
+                        F.a1 = plan->mp2m_ia1;
+                        F.a2 = plan->mp2m_ia2;
+                        F.tm = plan->mp2m_tm;
+                        F.grid = (int)std::min<long long>(D.rows * 128, plan->num_cu);
+                        e = launch_mp_col2m_inv(io, F, st);
+                    } else {
+                        e = launch_mp_col2(io, s.mp_P1, s.mp_P2, true, D, st);
+                    }
+                }
             } else {
                 e = launch_mp_col(io, s.mp_P1, 0, C1, st);
                 if (e == hipSuccess) e = launch_mp_inner(io, I, plan->lds_mp, st);

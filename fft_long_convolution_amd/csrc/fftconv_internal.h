@@ -180,8 +180,9 @@ struct MpCol2Params {
     void* ws;
     uint32_t* ctr;         // forward pass: clears the inner pass's counters
     // matrix-core forward pass (P1 = P2 = 32)
-    const uint4* a1;       // level-1 DFT A operands, [mt 4][hi/lo 2][64]
-    const uint4* a2;       // level-2 DFT A operands, [mt 4][ks 2][hi/lo 2][64]
+    const uint4* a1;       // forward level-1 DFT A operands, [mt 4][hi/lo 2][64];
+                           // inverse: level-1 inverse DFT, [mt 2][ks 2][hi/lo 2][64]
+    const uint4* a2;       // level-2 (inverse) DFT A operands, [mt 4][ks 2][hi/lo 2][64]
     const float2* tm;      // [W_1024^{n2 k1} 1024][W_M^{32 i k1} 128 x 32][W_M^{c k1} 32 x 32]
                            // [W_M^{1024 i k2} 128 x 32][W_M^{32 c k2} 32 x 32]
 };
@@ -190,6 +191,7 @@ long long mp_col2_tiles(int P2, long long rows);
 // workgroup of 512 threads per CU, 152 KB LDS).
 constexpr int kCol2mLds = 128 * 1024 + 3 * 8 * 1024;
 hipError_t launch_mp_col2m_fwd(int io, const MpCol2Params& p, hipStream_t s);
+hipError_t launch_mp_col2m_inv(int io, const MpCol2Params& p, hipStream_t s);
 hipError_t launch_mp_col2(int io, int P1, int P2, bool inv, const MpCol2Params& p, hipStream_t s);
 
 struct MpInnerParams {

@@ -55,6 +55,18 @@ __device__ __forceinline__ void swap16(uint32_t& a, uint32_t& c) {
     c = r[1];
 }
 
+// 16-byte load through a buffer descriptor (base in scalar registers, a
+// per-lane byte offset, a scalar byte offset): the compiler keeps no 64-bit
+// per-lane address to hoist out of a loop.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* base, int bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, bytes, 0x00020000);
+}
+__device__ __forceinline__ uint4 buf_ld16(__amdgpu_buffer_rsrc_t r, unsigned voff, int soff) {
+    typedef unsigned v4u __attribute__((ext_vector_type(4)));
+    const v4u v = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+
 }  // namespace
 
 // ---------------------------------------------------------------------------
@@ -536,6 +548,218 @@ __global__ void __launch_bounds__(512, 2) mp_col2m_fwd_kernel(MpCol2Params prm) 
 }
 
 // ---------------------------------------------------------------------------
+// Inverse two-level column pass on the matrix cores, P1 = P2 = 32: the
+// mirror of the forward pass.
+//   level 2: for each (k1, c) the workspace values over k2 times the
+//     conjugate twiddle W_M^{-32 (c0 + c) k2} (fp32, rounded once to f16 for
+//     the operand), the inverse 32-point DFT over k2, the conjugate twiddle
+//     W_1024^{-n2 k1} W_M^{-(c0 + c) k1}; to LDS [n2][c][k1] as f16;
+//   level 1: for each (n2, c) the inverse DFT over k1, only n1 < 16 (t < N),
+//     to y.
+template <int IO>
+__global__ void __launch_bounds__(512, 2) mp_col2m_inv_kernel(MpCol2Params prm) {
+    constexpr int SLAB = 4096, TC = 32, TPR = SLAB / TC;
+    constexpr long long M2 = 32LL * SLAB, M = 32LL * M2;
+    extern __shared__ uint4 s_lds[];
+    uint4* s_mid = s_lds;                                   // [n2][c][k1 granules]
+    float2* s_tw1 = (float2*)(s_mid + 8192);                // [k1][c]
+    float2* s_tw2 = s_tw1 + 1024;                           // [k2][c]
+    float2* s_twn = s_tw2 + 1024;                           // [n2][k1]
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int g = lane >> 4, x = lane & 15;
+    const long long ntiles = prm.rows * TPR;
+
+    const float2* g_twn = prm.tm;
+    const float2* g_1 = g_twn + 1024;
+    const float2* g_1b = g_1 + 4096;
+    const float2* g_2 = g_1b + 1024;
+    const float2* g_2b = g_2 + 4096;
+    for (int i = tid; i < 1024; i += 512) s_twn[i] = g_twn[i];
+    const __amdgpu_buffer_rsrc_t rs_a1 = buf_rsrc(prm.a1, 2 * 2 * 2 * 64 * 16);
+    const __amdgpu_buffer_rsrc_t rs_a2 = buf_rsrc(prm.a2, 4 * 2 * 2 * 64 * 16);
+
+    auto cmulf = [](float2 a, float2 b) { return make_float2(a.x * b.x - a.y * b.y, a.x * b.y + a.y * b.x); };
+    auto cmulcf = [](float2 a, float2 b) { return make_float2(a.x * b.x + a.y * b.y, a.y * b.x - a.x * b.y); };
+    auto mid = [](int n2, int c, int gr) { return (n2 * 32 + c) * 8 + (gr ^ (c & 7)); };
+    auto tile_of = [&](long long t, int& c0) {
+        const long long r = t / TPR;
+        c0 = (int)(t - r * TPR) * TC;
+        return r;
+    };
+    // per-tile twiddle tables [k][c], both built for the next tile during
+    // level 1
+    float2 tg[2][2][2];
+    auto tw_load = [&](int c0) {
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+            const int e = tid + 512 * q, k = e >> 5, c = e & 31;
+            tg[0][q][0] = g_1[(c0 >> 5) * 32 + k];
+            tg[0][q][1] = g_1b[c * 32 + k];
+            tg[1][q][0] = g_2[(c0 >> 5) * 32 + k];
+            tg[1][q][1] = g_2b[c * 32 + k];
+        }
+    };
+    auto tw_store = [&]() {
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+            s_tw1[tid + 512 * q] = cmulf(tg[0][q][0], tg[0][q][1]);
+            s_tw2[tid + 512 * q] = cmulf(tg[1][q][0], tg[1][q][1]);
+        }
+    };
+    // next tile's workspace values: wave w takes k1 = 4 w + j; lane (g, x)
+    // loads k2 = 16 ks + 8 (g / 2) + q of column 16 (g % 2) + x
+    uint32_t raw[4][16];
+    // (a wave-uniform base per row block and a 32-bit lane offset: no
+    // 64-bit per-lane addresses to keep)
+    const unsigned lofs = (unsigned)(8 * (g >> 1) * SLAB + 16 * (g & 1) + x);
+    auto fetch = [&](long long t) {
+        int c0;
+        const long long r = tile_of(t, c0);
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int q = 0; q < 16; ++q) {
+                const uint32_t* wb = (const uint32_t*)prm.ws + r * M + (long long)(4 * wave + j) * M2 +
+                                     (long long)((q >> 3) * 16 + (q & 7)) * SLAB + c0;
+                raw[j][q] = __builtin_nontemporal_load(&wb[lofs]);
+            }
+    };
+
+    long long t = blockIdx.x;
+    if (t < ntiles) {
+        int c0;
+        tile_of(t, c0);
+        tw_load(c0);
+        tw_store();
+        fetch(t);
+    }
+    __syncthreads();
+#pragma unroll 1
+    for (; t < ntiles; t += gridDim.x) {
+        int c0;
+        const long long r = tile_of(t, c0);
+        // ---------------- inverse level 2: wave w takes k1 = 4 w + j
+        {
+            // conjugate input twiddles (each lane's own row k2 and column),
+            // then the exchange into operands of both column halves
+            uint4 bop[4][2][2];   // [j][h][ks]
+            const int cl = 16 * (g & 1) + x;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+#pragma unroll
+                for (int q = 0; q < 16; ++q) {
+                    const int k2 = (q >> 3) * 16 + 8 * (g >> 1) + (q & 7);
+                    const rfloat2 d = f2_from_h2(raw[j][q]);
+                    const float2 v = cmulcf(make_float2(d.x, d.y), s_tw2[k2 * 32 + cl]);
+                    raw[j][q] = pk2(v.x, v.y);
+                }
+#pragma unroll
+                for (int ks = 0; ks < 2; ++ks) {
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) swap16(raw[j][8 * ks + q], raw[j][8 * ks + q + 4]);
+                    bop[j][0][ks] = make_uint4(raw[j][8 * ks], raw[j][8 * ks + 1], raw[j][8 * ks + 2], raw[j][8 * ks + 3]);
+                    bop[j][1][ks] = make_uint4(raw[j][8 * ks + 4], raw[j][8 * ks + 5], raw[j][8 * ks + 6], raw[j][8 * ks + 7]);
+                }
+            }
+            // the level-2 A operands one M-tile at a time (L2-resident): all
+            // of them beside the operands of four tasks would not fit
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt) {
+                uint4 a2[2][2];
+#pragma unroll
+                for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+                    for (int hl = 0; hl < 2; ++hl) a2[ks][hl] = buf_ld16(rs_a2, lane * 16, (((mt * 2 + ks) * 2 + hl) * 64) * 16);
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const int c = 16 * h + x;
+                    uint32_t v[2][4];
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const int k1 = 4 * wave + j;
+                        rfloat4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                        for (int ks = 0; ks < 2; ++ks) {
+                            acc = mma_f16(a2[ks][0], bop[j][h][ks], acc);
+                            acc = mma_f16(a2[ks][1], bop[j][h][ks], acc);
+                        }
+                        const float2 t1 = s_tw1[k1 * 32 + c];
+#pragma unroll
+                        for (int e = 0; e < 2; ++e) {
+                            const int n2 = 8 * mt + 2 * g + e;
+                            const float2 tw = cmulf(s_twn[n2 * 32 + k1], t1);
+                            const float2 a = cmulcf(make_float2(acc[2 * e], acc[2 * e + 1]), tw);
+                            v[e][j] = pk2(a.x, a.y);
+                        }
+                    }
+#pragma unroll
+                    for (int e = 0; e < 2; ++e)
+                        s_mid[mid(8 * mt + 2 * g + e, c, wave)] = make_uint4(v[e][0], v[e][1], v[e][2], v[e][3]);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            }
+        }
+        __syncthreads();
+        const long long tn_ = t + gridDim.x;
+        uint4 a1[2][2][2];
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+                for (int hl = 0; hl < 2; ++hl) a1[mt][ks][hl] = buf_ld16(rs_a1, lane * 16, (((mt * 2 + ks) * 2 + hl) * 64) * 16);
+        if (tn_ < ntiles) {
+            int c0n;
+            tile_of(tn_, c0n);
+            tw_load(c0n);
+            fetch(tn_);
+        }
+        // ---------------- inverse level 1: wave w takes n2 = 4 w + j
+        {
+            const unsigned bq = (unsigned)r / (unsigned)prm.hc;
+            const long long mrow = (long long)bq * prm.H + prm.h0 + ((unsigned)r - bq * (unsigned)prm.hc);
+            uint32_t* y = (uint32_t*)prm.y + mrow * (M / 2) + c0 + 16 * (g & 1) + x;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int n2 = 4 * wave + j;
+                uint4 b[2][2];
+#pragma unroll
+                for (int h = 0; h < 2; ++h)
+#pragma unroll
+                    for (int ks = 0; ks < 2; ++ks) b[h][ks] = s_mid[mid(n2, 16 * h + x, 4 * ks + g)];
+#pragma unroll
+                for (int mt = 0; mt < 2; ++mt) {
+                    uint32_t o[2][2];
+#pragma unroll
+                    for (int h = 0; h < 2; ++h) {
+                        rfloat4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                        for (int ks = 0; ks < 2; ++ks) {
+                            acc = mma_f16(a1[mt][ks][0], b[h][ks], acc);
+                            acc = mma_f16(a1[mt][ks][1], b[h][ks], acc);
+                        }
+#pragma unroll
+                        for (int e = 0; e < 2; ++e) o[h][e] = pk2io<IO>(acc[2 * e], acc[2 * e + 1]);
+                    }
+                    // rows n1 = 8 mt + 4 (g / 2) + e and + 2, whole lines
+#pragma unroll
+                    for (int e = 0; e < 2; ++e) {
+                        swap16(o[0][e], o[1][e]);
+                        const int n1 = 8 * mt + 4 * (g >> 1) + e;
+                        __builtin_nontemporal_store(o[0][e], &y[(long long)n1 * M2 + (long long)n2 * SLAB]);
+                        __builtin_nontemporal_store(o[1][e], &y[(long long)(n1 + 2) * M2 + (long long)n2 * SLAB]);
+                    }
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+        if (tn_ < ntiles) tw_store();
+        __syncthreads();
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Inner pass: persistent workgroups of four waves, one unit (two 4096-point
 // slabs, eight 1024-point regions) at a time.
 //   pair unit (slabs of k_o and P_o - k_o):  wave j holds region 2j = slab
@@ -921,6 +1145,21 @@ hipError_t launch_mp_col2m_fwd(int io, const MpCol2Params& p, hipStream_t s) {
     if (p.rows <= 0) return hipSuccess;
     if (p.grid <= 0 || p.M != 4194304 || !p.a1 || !p.a2 || !p.tm) return hipErrorInvalidValue;
     return io == IO_BF16 ? col2m_fwd_t<IO_BF16>(p, s) : col2m_fwd_t<IO_F16>(p, s);
+}
+
+template <int IO>
+static hipError_t col2m_inv_t(const MpCol2Params& p, hipStream_t s) {
+    const hipError_t e = hipFuncSetAttribute((const void*)mp_col2m_inv_kernel<IO>,
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, kCol2mLds);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((mp_col2m_inv_kernel<IO>), dim3((unsigned)p.grid), dim3(512), kCol2mLds, s, p);
+    return hipGetLastError();
+}
+
+hipError_t launch_mp_col2m_inv(int io, const MpCol2Params& p, hipStream_t s) {
+    if (p.rows <= 0) return hipSuccess;
+    if (p.grid <= 0 || p.M != 4194304 || !p.a1 || !p.a2 || !p.tm) return hipErrorInvalidValue;
+    return io == IO_BF16 ? col2m_inv_t<IO_BF16>(p, s) : col2m_inv_t<IO_F16>(p, s);
 }
 
 hipError_t launch_mp_inner(int io, const MpInnerParams& p, int lds, hipStream_t s) {
