@@ -553,14 +553,20 @@ std::vector<uint16_t> wide_outer_twiddles(int P) {
 // owns (as in the wide kernel with 256 threads: n_b = t & 31,
 // n_a = 4 (t >> 5) + j).
 std::vector<uint16_t> mp_inner_twiddles() {
-    const int T = 256, CPT = 4, Mi = 4096;
-    std::vector<uint16_t> out((size_t)4 * T * CPT * 2);
-    for (int m = 1; m <= 4; ++m)
-        for (int t = 0; t < T; ++t)
-            for (int j = 0; j < CPT; ++j) {
-                const long long np = 32LL * (CPT * (t >> 5) + j) + (t & 31);
+    // W_4096^{n' m} for m = 0..4, n' = 32 n_a + n_b < 1024 (packed f16),
+    // [m][engine position of (n_a, n_b)]: the position of the 32 x 32
+    // engine's LDS layout, 4 consecutive n_a per 16-byte word
+    const int Q = 1024, Mi = 4096;
+    std::vector<uint16_t> out((size_t)5 * Q * 2);
+    for (int m = 0; m <= 4; ++m)
+        for (int na = 0; na < 32; ++na)
+            for (int nb = 0; nb < 32; ++nb) {
+                const int it = nb < 16 ? 0 : 1;
+                const int xx = nb < 16 ? nb : (nb == 16 ? 0 : 32 - nb);
+                const int pos = (((it * 2 + (na >> 4)) * 64 + 16 * ((na >> 2) & 3) + xx) << 2) + (na & 3);
+                const int np = 32 * na + nb;
                 const double ang = -2.0 * M_PI * (double)((np * m) % Mi) / (double)Mi;
-                const size_t idx = (((size_t)(m - 1) * T + t) * CPT + j) * 2;
+                const size_t idx = ((size_t)m * Q + pos) * 2;
                 out[idx] = f32_to_f16_bits((float)cos(ang));
                 out[idx + 1] = f32_to_f16_bits((float)sin(ang));
             }
@@ -915,9 +921,9 @@ fftconv_status build_mp_tables(fftconv_plan_s* pl) {
         if (upload(pl, ia2.data(), ia2.size() * 2, &d) != hipSuccess) return FFTCONV_ERR_HIP;
         pl->mp2m_ia2 = (const uint4*)d;
     }
-    // stage tables (16 KB) + inner twiddles (16 KB) + two slabs of f16
-    // points (32 KB) + the k_b exchange
-    pl->lds_mp = 16 * 1024 + 16 * 1024 + 8 * 1024 * 4 + 39 * 16 * 4 + 16;
+    // stage tables (16 KB) + inner twiddles (20 KB) + two slabs of f16
+    // points (32 KB) + the k_b exchange + claims + outer-stage operands
+    pl->lds_mp = 16 * 1024 + 20 * 1024 + 8 * 1024 * 4 + 39 * 16 * 4 + 16 + 4 * 64 * 8;
     hipDeviceProp_t prop;
     if (hipGetDeviceProperties(&prop, pl->device) == hipSuccess && prop.multiProcessorCount > 0)
         pl->num_cu = prop.multiProcessorCount;

@@ -207,7 +207,7 @@ struct MpInnerParams {
     const void* f2a;
     const void* i2b;
     const uint32_t* twf;
-    const uint32_t* two;   // W_4096^{n' m}, m = 1..4, [m-1][thread][column]
+    const uint32_t* two;   // W_4096^{n' m}, m = 0..4, [m][engine position of n'] (packed f16)
 };
 hipError_t launch_mp_inner(int io, const MpInnerParams& p, int lds_bytes, hipStream_t s);
 
