@@ -47,10 +47,13 @@ class PlanInfo(ctypes.Structure):
                 "mfma_flops_per_row": self.mfma_flops_per_row,
                 "kernel": {0: "fused_kernel", 1: "row_kernel", 3: "wide_kernel",
                            # one outer level: per-column passes; two: both
-                           # levels in one column pass each way
-                           4: ("mp_col2_kernel+mp_inner_kernel"
-                               if self.outer_factors > 1 else
-                               "mp_col_kernel+mp_inner_kernel"),
+                           # levels in one column pass each way (on the
+                           # matrix cores when both are 32)
+                           4: ("mp_col_kernel+mp_inner_kernel"
+                               if self.outer_factors <= 1 else
+                               "mp_col2m_fwd_kernel+mp_inner_kernel+mp_col2m_inv_kernel"
+                               if list(self.factors[:2]) == [32, 32] else
+                               "mp_col2_kernel+mp_inner_kernel"),
                            2: "outer_fwd_kernel+inner_kernel+outer_inv_kernel"
                            }[self.kernel_variant]}
 

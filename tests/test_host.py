@@ -63,8 +63,12 @@ def test_plan_query_every_length(lg, dtype):
         # one outer level up to P_o = 32 (N = 128K), two above
         two = N > 131072
         assert info["outer_factors"] == (2 if two else 1)
-        assert info["kernel"] == ("mp_col2_kernel+mp_inner_kernel" if two else
-                                  "mp_col_kernel+mp_inner_kernel")
+        if not two:
+            assert info["kernel"] == "mp_col_kernel+mp_inner_kernel"
+        elif fac[:2] == [32, 32]:
+            assert info["kernel"] == "mp_col2m_fwd_kernel+mp_inner_kernel+mp_col2m_inv_kernel"
+        else:
+            assert info["kernel"] == "mp_col2_kernel+mp_inner_kernel"
         assert fac[-3:] == [4, 32, 32]
     # matrix-core flops: 16 M (N_1/2 + sum_{i>1} N_i) per row
     f = info["factors"]
