@@ -15,6 +15,7 @@ from __future__ import annotations
 
 import argparse
 import json
+import math
 import os
 import sys
 import time
@@ -60,8 +61,10 @@ def measured_traffic(workload: str):
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=100)
-    ap.add_argument("--warmup", type=int, default=20)
+    # default (flag not given): sized from a short estimate so that warmup
+    # covers >= 0.3 s of work (clocks settle) and the timed region ~1 s
+    ap.add_argument("--steps", type=int, default=None)
+    ap.add_argument("--warmup", type=int, default=None)
     ap.add_argument("--workload", default="hyena_bf16_n1k")
     ap.add_argument("--no-cpu", action="store_true",
                     help="skip the CPU oracle baseline")
@@ -97,11 +100,11 @@ def main():
         esz = 4 if w.dtype == "f32" else 2
         a = torch.ones(w.rows * w.N * esz // 4, dtype=torch.float32, device=dev)
         b = torch.empty_like(a)
-        for _ in range(args.steps):
+        for _ in range(args.steps or 100):
             b.copy_(a)
         torch.cuda.synchronize()
         print(json.dumps({"copy_calibration_bytes_each_way": a.numel() * 4,
-                          "copies": args.steps}))
+                          "copies": args.steps or 100}))
         return
     conv = FFTConv(w.N, dtype=w.dtype)
     info = conv.info
@@ -126,6 +129,22 @@ def main():
     # ---- warmup, then K timed steps between two HIP events recorded on the
     # stream the kernels are launched on (launches back to back)
     stream = torch.cuda.current_stream()
+    if args.steps is None or args.warmup is None:
+        # estimate the step time (these calls are untimed warmup too)
+        for i in range(3):
+            conv.forward(us[i % nsets], kf, out=ys[i % nsets], workspace=ws)
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for i in range(10):
+            conv.forward(us[i % nsets], kf, out=ys[i % nsets], workspace=ws)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        est = max(e0.elapsed_time(e1) / 10, 1e-3)
+        if args.warmup is None:
+            args.warmup = max(20, int(math.ceil(300.0 / est)))
+        if args.steps is None:
+            args.steps = max(100, int(math.ceil(1000.0 / est)))
     for i in range(args.warmup):
         conv.forward(us[i % nsets], kf, out=ys[i % nsets], workspace=ws)
     torch.cuda.synchronize()

@@ -113,4 +113,12 @@ __device__ __forceinline__ rhalf2 hpair(rhalf2 a, rhalf2 z, rhalf2 b, rhalf2 p) 
     return __builtin_elementwise_fma(byy, pn, r);
 }
 
+// Exchange between 16-lane rows: the odd rows of a trade places with the
+// even rows of c (rows 1 <-> 0 and 3 <-> 2).
+__device__ __forceinline__ void swap16(uint32_t& a, uint32_t& c) {
+    const auto r = __builtin_amdgcn_permlane16_swap(a, c, false, false);
+    a = r[0];
+    c = r[1];
+}
+
 }  // namespace fftconv

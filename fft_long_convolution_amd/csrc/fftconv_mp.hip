@@ -47,14 +47,6 @@ __device__ __forceinline__ rfloat2 f2_from_io(uint32_t v) {
     }
 }
 
-// Exchange between 16-lane rows: the odd rows of a trade places with the
-// even rows of c (rows 1 <-> 0 and 3 <-> 2).
-__device__ __forceinline__ void swap16(uint32_t& a, uint32_t& c) {
-    const auto r = __builtin_amdgcn_permlane16_swap(a, c, false, false);
-    a = r[0];
-    c = r[1];
-}
-
 // 16-byte load through a buffer descriptor (base in scalar registers, a
 // per-lane byte offset, a scalar byte offset): the compiler keeps no 64-bit
 // per-lane address to hoist out of a loop.

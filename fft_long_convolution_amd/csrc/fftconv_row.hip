@@ -140,11 +140,21 @@ __global__ void __launch_bounds__(64 * kRowWaves, 1) row_kernel(RowParams P) {
         row_of(c, h, b);
         const uint32_t* u =
             (const uint32_t*)P.u + ((long long)b * P.H + h) * (M / 2);
+        if constexpr (NB == 32) {
+            // whole 128-byte rows per load: lane groups g and g + 1 take the
+            // two halves of rows 8 (g / 2) + q; the exchange into the
+            // operand layout happens where the row is consumed
 #pragma unroll
-        for (int it = 0; it < IT; ++it)
+            for (int q = 0; q < 8; ++q)
+                dst[q >> 2][q & 3] = __builtin_nontemporal_load(
+                    &u[NB * (8 * (g >> 1) + q) + ((g & 1) ? kmap32(1, x) : x)]);
+        } else {
 #pragma unroll
-            for (int jj = 0; jj < 4; ++jj)
-                dst[it][jj] = __builtin_nontemporal_load(&u[NB * (4 * g + jj) + nbmap<NB>(it, x)]);
+            for (int it = 0; it < IT; ++it)
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj)
+                    dst[it][jj] = __builtin_nontemporal_load(&u[NB * (4 * g + jj) + nbmap<NB>(it, x)]);
+        }
     };
 
     uint32_t ring[D][IT][4];
@@ -166,6 +176,10 @@ __global__ void __launch_bounds__(64 * kRowWaves, 1) row_kernel(RowParams P) {
             row_of(m, h, b);
             const long long row = (long long)b * P.H + h;
             const int abbase = (h - h_lo) * M;
+            if constexpr (NB == 32) {
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj) swap16(cur[0][jj], cur[1][jj]);
+            }
             // ---- F1: 32-point DFT over n_a (16 nonzero), k_a to the lanes
             uint4 b2[KS2][2];
 #pragma unroll
@@ -280,7 +294,8 @@ __global__ void __launch_bounds__(64 * kRowWaves, 1) row_kernel(RowParams P) {
             // ---- I1: inverse 32-point DFT over k_a, only n_a < 16 (t < N)
             uint32_t* yrow = (uint32_t*)P.y + row * (long long)(M / 2);
 #pragma unroll
-            for (int mt = 0; mt < 2; ++mt)
+            for (int mt = 0; mt < 2; ++mt) {
+                uint32_t o[NT][2];
 #pragma unroll
                 for (int nt = 0; nt < NT; ++nt) {
                     rfloat4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -288,12 +303,25 @@ __global__ void __launch_bounds__(64 * kRowWaves, 1) row_kernel(RowParams P) {
                     for (int ks = 0; ks < 2; ++ks)
                         acc = mma_f16(s_i1a[(mt * 2 + ks) * 64 + lane], b1v[ks][nt], acc);
 #pragma unroll
-                    for (int e = 0; e < 2; ++e) {
-                        const int na = 8 * mt + 2 * g + e;
-                        __builtin_nontemporal_store(pk2io<IO>(acc[2 * e], acc[2 * e + 1]),
-                                                    &yrow[NB * na + nbmap<NB>(nt, x)]);
-                    }
+                    for (int e = 0; e < 2; ++e) o[nt][e] = pk2io<IO>(acc[2 * e], acc[2 * e + 1]);
                 }
+                if constexpr (NB == 32) {
+                    // rows n_a = 8 mt + 4 (g / 2) + e (+ 2): whole lines
+#pragma unroll
+                    for (int e = 0; e < 2; ++e) {
+                        swap16(o[0][e], o[1][e]);
+                        const int na = 8 * mt + 4 * (g >> 1) + e, w = (g & 1) ? kmap32(1, x) : x;
+                        __builtin_nontemporal_store(o[0][e], &yrow[NB * na + w]);
+                        __builtin_nontemporal_store(o[1][e], &yrow[NB * (na + 2) + w]);
+                    }
+                } else {
+#pragma unroll
+                    for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+                        for (int e = 0; e < 2; ++e)
+                            __builtin_nontemporal_store(o[nt][e], &yrow[NB * (8 * mt + 2 * g + e) + nbmap<NB>(nt, x)]);
+                }
+            }
         };
         // claims grow monotonically and the ring is consumed in claim
         // order, so the first claim past the end ends the wave's work
