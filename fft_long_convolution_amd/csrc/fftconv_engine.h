@@ -457,5 +457,33 @@ __device__ __forceinline__ void inverse(const uint4 (&a2)[2][2], const uint4* s_
     }
 }
 
+// Conversions and buffer-descriptor loads shared by the multi-pass kernels.
+__device__ __forceinline__ rfloat2 f2_from_h2(uint32_t v) {
+    const rhalf2 h = as_h2(v);
+    const rfloat2 r = {(float)h.x, (float)h.y};
+    return r;
+}
+template <int IO>
+__device__ __forceinline__ rfloat2 f2_from_io(uint32_t v) {
+    if constexpr (IO == IO_BF16) {
+        const rfloat2 r = {__uint_as_float(v << 16), __uint_as_float(v & 0xffff0000u)};
+        return r;
+    } else {
+        return f2_from_h2(v);
+    }
+}
+
+// 16-byte load through a buffer descriptor (base in scalar registers, a
+// per-lane byte offset, a scalar byte offset): the compiler keeps no 64-bit
+// per-lane address to hoist out of a loop.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* base, int bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, bytes, 0x00020000);
+}
+__device__ __forceinline__ uint4 buf_ld16(__amdgpu_buffer_rsrc_t r, unsigned voff, int soff) {
+    typedef unsigned v4u __attribute__((ext_vector_type(4)));
+    const v4u v = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+
 }  // namespace eng
 }  // namespace fftconv
