@@ -13,7 +13,12 @@ Cores", section 3.4):
 * ``conv_fft``     -- the same through the convolution theorem with both
   sequences zero-padded to 2N (iterative radix-2 FFT, no packing tricks);
 * ``conv_points``  -- single outputs by the definition (for sampled checks);
-* ``fft``          -- the radix-2 DFT itself, exposed for the oracle's pins.
+* ``fft``          -- the radix-2 DFT itself, exposed for the oracle's pins;
+* ``gated_direct`` / ``gated_fft`` / ``gated_points`` -- the gated
+  convolution ``y = v * ((u * w) conv k)`` (elementwise gates on the input
+  and on the output; same page, section 3 "Technical Approach",
+  "Domain-Specific Optimizations", gating operation fusion), by the same
+  three routes.
 
 Inputs are the exact values stored in the I/O dtype (bf16 bit patterns are
 widened exactly); everything is evaluated in fp64.
@@ -141,6 +146,38 @@ def conv_points(u, k, rows, ts, hidx=None) -> np.ndarray:
     _load().oracle_conv_points(_dp(u), _dp(k), _lp(hidx), N, _lp(rows),
                                _lp(ts), len(rows), _dp(out))
     return out
+
+
+def _gates(u, w, v):
+    u = np.asarray(u, dtype=np.float64)
+    w = np.asarray(w, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    if w.shape != u.shape or v.shape != u.shape:
+        raise ValueError("gates must have the shape of u")
+    return u, w, v
+
+
+def gated_direct(u, w, v, k, hidx=None) -> np.ndarray:
+    """y[r, t] = v[r, t] * sum_{s<=t} u[r, s] w[r, s] k[hidx[r], t-s]: the
+    input gate multiplies u before the convolution, the output gate
+    multiplies its result (fp64; the products of stored 16-bit values are
+    exact in fp64)."""
+    u, w, v = _gates(u, w, v)
+    return v * conv_direct(u * w, k, hidx)
+
+
+def gated_fft(u, w, v, k, hidx=None) -> np.ndarray:
+    """The gated convolution with the convolution by the 2N-point FFT route."""
+    u, w, v = _gates(u, w, v)
+    return v * conv_fft(u * w, k, hidx)
+
+
+def gated_points(u, w, v, k, rows, ts, hidx=None) -> np.ndarray:
+    """out[i] = y[rows[i], ts[i]] of the gated convolution by the definition."""
+    u, w, v = _gates(u, w, v)
+    rows = np.asarray(rows, dtype=np.int64)
+    ts = np.asarray(ts, dtype=np.int64)
+    return v[rows, ts] * conv_points(u * w, k, rows, ts, hidx)
 
 
 def fft(x, inverse: bool = False) -> np.ndarray:

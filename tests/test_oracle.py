@@ -295,3 +295,78 @@ def test_exact_widening_of_stored_dtypes():
                                   [1.0, -2.0, 0.15625, 2.0 ** -133])
     h = np.array([1.0, 0.5, -65504.0], dtype=np.float16)
     np.testing.assert_array_equal(oracle.to_f64(h, "f16"), h.astype(float))
+
+
+# ----------------------------------------------------------------- gated
+
+def test_golden_hand_worked_gated():
+    for case in _read_cases("gated_conv_hand.txt"):
+        u, w, v, k = (np.array([float(x) for x in case[key]])[None, :]
+                      for key in ("u", "w", "v", "k"))
+        y = np.array([float(x) for x in case["y"]])
+        np.testing.assert_array_equal(oracle.gated_direct(u, w, v, k)[0], y)
+
+
+def _brute_gated(u, w, v, k):
+    # explicit triple product per (t, s) pair, gates applied term by term
+    n = len(u)
+    y = [0.0] * n
+    for t in range(n):
+        acc = 0.0
+        for s in range(t + 1):
+            acc += u[s] * w[s] * k[t - s]
+        y[t] = v[t] * acc
+    return y
+
+
+@pytest.mark.parametrize("n", [1, 2, 4, 7, 8])
+def test_gated_brute_force_tiny(n):
+    rng = np.random.default_rng(100 + n)
+    u, w, v = (rng.standard_normal((3, n)) for _ in range(3))
+    k = rng.standard_normal((2, n))
+    hidx = np.array([0, 1, 1])
+    yd = oracle.gated_direct(u, w, v, k, hidx)
+    for r in range(3):
+        np.testing.assert_allclose(yd[r], _brute_gated(u[r], w[r], v[r], k[hidx[r]]),
+                                   rtol=0, atol=1e-13)
+    if n & (n - 1) == 0:
+        np.testing.assert_allclose(oracle.gated_fft(u, w, v, k, hidx), yd,
+                                   rtol=0, atol=1e-12)
+
+
+def test_gated_special_cases():
+    rng = np.random.default_rng(7)
+    u = rng.standard_normal((2, 16))
+    k = rng.standard_normal((2, 16))
+    one = np.ones_like(u)
+    # unit gates: the plain convolution
+    np.testing.assert_array_equal(oracle.gated_direct(u, one, one, k),
+                                  oracle.conv_direct(u, k))
+    # a zero output gate zeroes the output; a zero input gate zeroes it too
+    assert not oracle.gated_direct(u, one, np.zeros_like(u), k).any()
+    assert not oracle.gated_direct(u, np.zeros_like(u), one, k).any()
+    # constant gates scale: w = a, v = b gives a * b * (u * k)
+    a, b = 0.75, -2.0
+    np.testing.assert_allclose(oracle.gated_direct(u, a * one, b * one, k),
+                               a * b * oracle.conv_direct(u, k), rtol=1e-14)
+    # the input gate acts before the convolution: gating u by a delta at s0
+    # keeps only u[s0] k[t - s0] (t >= s0)
+    s0 = 5
+    wd = np.zeros_like(u)
+    wd[:, s0] = 1.0
+    yd = oracle.gated_direct(u, wd, one, k)
+    for r in range(2):
+        want = np.zeros(16)
+        want[s0:] = u[r, s0] * k[r, :16 - s0]
+        np.testing.assert_allclose(yd[r], want, atol=1e-14)
+
+
+def test_gated_points_match_full():
+    rng = np.random.default_rng(11)
+    u, w, v = (rng.standard_normal((4, 32)) for _ in range(3))
+    k = rng.standard_normal((2, 32))
+    full = oracle.gated_direct(u, w, v, k)
+    rows = np.array([0, 3, 2, 1, 3])
+    ts = np.array([0, 31, 7, 16, 1])
+    np.testing.assert_allclose(oracle.gated_points(u, w, v, k, rows, ts),
+                               full[rows, ts], rtol=0, atol=1e-12)
