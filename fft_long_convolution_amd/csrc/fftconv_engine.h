@@ -204,6 +204,11 @@ struct Outer {
         if constexpr (IO == IO_BF16) return pk2io<IO_BF16>(a.x, a.y);
         else return as_u32(a);
     }
+    // element-wise product with a packed pair of I/O values (a gate):
+    // exact in fp32 for bf16, one rounding in packed f16 for f16
+    static __device__ __forceinline__ V emul(V a, uint32_t g) {
+        return a * from_io(g);
+    }
     // a * t and a * conj(t), t a packed-f16 twiddle
     static __device__ __forceinline__ V mul(V a, uint32_t t) {
         if constexpr (IO == IO_BF16) {

@@ -666,6 +666,7 @@ struct fftconv_plan_s {
     int lds_mp = 0;
     MpInnerParams mp{};
     const uint4* mp2m_a1 = nullptr;   // matrix-core forward pass (4M): level-1 A operands
+    const uint4* mp2m_a1h = nullptr;  // the same in f16 (gated rows)
     const uint4* mp2m_a2 = nullptr;   //   level-2 A operands
     const uint4* mp2m_ia1 = nullptr;  // inverse pass: level-1 inverse A operands
     const uint4* mp2m_ia2 = nullptr;  //   level-2 inverse A operands
@@ -819,6 +820,13 @@ fftconv_status build_device_tables(fftconv_plan_s* pl) {
         void* d = nullptr;
         if (upload(pl, f1b.data(), f1b.size() * 2, &d) != hipSuccess) return FFTCONV_ERR_HIP;
         R.f1b = d;
+        R.f1h = d;
+        if (bf) {
+            // gated rows feed u (.) w to the first stage as f16
+            std::vector<uint16_t> f1h = row_f1b(false);
+            if (upload(pl, f1h.data(), f1h.size() * 2, &d) != hipSuccess) return FFTCONV_ERR_HIP;
+            R.f1h = d;
+        }
         if (upload(pl, i1a.data(), i1a.size() * 2, &d) != hipSuccess) return FFTCONV_ERR_HIP;
         R.i1a = d;
         if (upload(pl, i2b.data(), i2b.size() * 2, &d) != hipSuccess) return FFTCONV_ERR_HIP;
@@ -911,6 +919,13 @@ fftconv_status build_mp_tables(fftconv_plan_s* pl) {
         std::vector<float> tm = col2m_twiddles((long long)s.M);
         if (upload(pl, a1.data(), a1.size() * 2, &d) != hipSuccess) return FFTCONV_ERR_HIP;
         pl->mp2m_a1 = (const uint4*)d;
+        pl->mp2m_a1h = pl->mp2m_a1;
+        if (s.dtype == FFTCONV_BF16) {
+            // gated rows feed u (.) w to level 1 as f16
+            std::vector<uint16_t> a1h = col2m_dft_a(false, 16);
+            if (upload(pl, a1h.data(), a1h.size() * 2, &d) != hipSuccess) return FFTCONV_ERR_HIP;
+            pl->mp2m_a1h = (const uint4*)d;
+        }
         if (upload(pl, a2.data(), a2.size() * 2, &d) != hipSuccess) return FFTCONV_ERR_HIP;
         pl->mp2m_a2 = (const uint4*)d;
         if (upload(pl, tm.data(), tm.size() * 4, &d) != hipSuccess) return FFTCONV_ERR_HIP;
@@ -1103,10 +1118,16 @@ fftconv_status fftconv_kernel_spectrum(fftconv_plan_t plan, const float* k,
     return FFTCONV_OK;
 }
 
-fftconv_status fftconv_forward(fftconv_plan_t plan, const void* u,
-                               const void* k_f, void* y, size_t B, size_t H,
-                               size_t N, void* workspace,
-                               size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Shared body of the plain and the gated forward call; w and v are both
+// null (plain) or both set (gated), which the callers guarantee.
+fftconv_status forward_impl(fftconv_plan_t plan, const void* u, const void* w,
+                            const void* v, const void* k_f, void* y, size_t B,
+                            size_t H, size_t N, void* workspace,
+                            size_t workspace_bytes, void* stream) {
     if (!plan) return FFTCONV_ERR_INVALID_ARG;
     const Shape& s = plan->s;
     if (N != s.N) return FFTCONV_ERR_INVALID_ARG;
@@ -1115,11 +1136,14 @@ fftconv_status fftconv_forward(fftconv_plan_t plan, const void* u,
     if (rows == 0) return FFTCONV_OK;
     if (!u || !k_f || !y) return FFTCONV_ERR_INVALID_ARG;
     if (!aligned16(u) || !aligned16(y) || !aligned16(k_f)) return FFTCONV_ERR_ALIGNMENT;
+    if (w && (!aligned16(w) || !aligned16(v))) return FFTCONV_ERR_ALIGNMENT;
     if (rows > 0x7fffffffULL || H > 0x7fffffffULL) return FFTCONV_ERR_UNSUPPORTED;
     const size_t esz = s.dtype == FFTCONV_F32 ? 4 : 2;
     const size_t io_bytes = rows * N * esz;
     const size_t kf_bytes = fftconv_spectrum_bytes(plan, H);
     if (overlap(y, io_bytes, u, io_bytes) || overlap(y, io_bytes, k_f, kf_bytes))
+        return FFTCONV_ERR_INVALID_ARG;
+    if (w && (overlap(y, io_bytes, w, io_bytes) || overlap(y, io_bytes, v, io_bytes)))
         return FFTCONV_ERR_INVALID_ARG;
     const size_t ws_need = fftconv_workspace_bytes(plan, B, H);
     if (ws_need) {
@@ -1128,6 +1152,9 @@ fftconv_status fftconv_forward(fftconv_plan_t plan, const void* u,
         if (overlap(workspace, ws_need, y, io_bytes) ||
             overlap(workspace, ws_need, u, io_bytes) ||
             overlap(workspace, ws_need, k_f, kf_bytes))
+            return FFTCONV_ERR_INVALID_ARG;
+        if (w && (overlap(workspace, ws_need, w, io_bytes) ||
+                  overlap(workspace, ws_need, v, io_bytes)))
             return FFTCONV_ERR_INVALID_ARG;
     }
     int dev = -1;
@@ -1152,6 +1179,8 @@ fftconv_status fftconv_forward(fftconv_plan_t plan, const void* u,
         R.u = u;
         R.y = y;
         R.kf = k_f;
+        R.w = w;
+        R.v = v;
         e = launch_row(io, plan->row_nb, R, plan->lds_row, st);
     } else if (s.mp_P1) {
         const size_t hc_max = mp_chunk_channels(s, B, H);
@@ -1162,6 +1191,8 @@ fftconv_status fftconv_forward(fftconv_plan_t plan, const void* u,
         C1.tw = plan->mp_tw1;
         C1.u = u;
         C1.y = y;
+        C1.w = w;
+        C1.v = v;
         C1.ws = workspace;
         C1.ctr = (uint32_t*)((char*)workspace + (ws_need - kClaimBytes));
         MpColParams C2 = C1;
@@ -1197,6 +1228,8 @@ fftconv_status fftconv_forward(fftconv_plan_t plan, const void* u,
                 D.tw2 = C2.tw;
                 D.u = u;
                 D.y = y;
+                D.w = w;
+                D.v = v;
                 D.ws = workspace;
                 D.ctr = C1.ctr;
                 // persistent workgroups, two per CU, a multiple of 16 (the
@@ -1207,7 +1240,7 @@ fftconv_status fftconv_forward(fftconv_plan_t plan, const void* u,
                     // P1 = P2 = 32: the forward pass on the matrix cores,
                     // one workgroup per CU
                     MpCol2Params F = D;
-                    F.a1 = plan->mp2m_a1;
+                    F.a1 = w ? plan->mp2m_a1h : plan->mp2m_a1;
                     F.a2 = plan->mp2m_a2;
                     F.tm = plan->mp2m_tm;
                     F.grid = (int)std::min<long long>(D.rows * 128, plan->num_cu);
@@ -1248,6 +1281,8 @@ fftconv_status fftconv_forward(fftconv_plan_t plan, const void* u,
         W.u = u;
         W.y = y;
         W.kf = k_f;
+        W.w = w;
+        W.v = v;
         W.ctr = (uint32_t*)workspace;
         e = launch_claim_reset(W.ctr, st);
         if (e == hipSuccess) e = launch_wide(io, s.wide_P, W, plan->lds_wide, st);
@@ -1258,6 +1293,8 @@ fftconv_status fftconv_forward(fftconv_plan_t plan, const void* u,
         P.u = u;
         P.y = y;
         P.kf = k_f;
+        P.w = w;
+        P.v = v;
         e = launch_fused(io, P, s.lds_fused, st);
     } else {
         FwdParams O = plan->outer, I = plan->inner;
@@ -1265,6 +1302,8 @@ fftconv_status fftconv_forward(fftconv_plan_t plan, const void* u,
         O.H = I.H = (int)H;
         O.u = I.u = u;
         O.y = I.y = y;
+        O.w = I.w = w;
+        O.v = I.v = v;
         O.kf = I.kf = k_f;
         O.ws = I.ws = (float2*)workspace;
         e = launch_outer_fwd(io, O, s.lds_outer, st);
@@ -1272,6 +1311,28 @@ fftconv_status fftconv_forward(fftconv_plan_t plan, const void* u,
         if (e == hipSuccess) e = launch_outer_inv(io, O, s.lds_outer, st);
     }
     return e == hipSuccess ? FFTCONV_OK : FFTCONV_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+fftconv_status fftconv_forward(fftconv_plan_t plan, const void* u,
+                               const void* k_f, void* y, size_t B, size_t H,
+                               size_t N, void* workspace,
+                               size_t workspace_bytes, void* stream) {
+    return forward_impl(plan, u, nullptr, nullptr, k_f, y, B, H, N, workspace,
+                        workspace_bytes, stream);
+}
+
+fftconv_status fftconv_forward_gated(fftconv_plan_t plan, const void* u,
+                                     const void* w, const void* v,
+                                     const void* k_f, void* y, size_t B,
+                                     size_t H, size_t N, void* workspace,
+                                     size_t workspace_bytes, void* stream) {
+    if (B * H != 0 && (!w || !v)) return FFTCONV_ERR_INVALID_ARG;
+    return forward_impl(plan, u, w, v, k_f, y, B, H, N, workspace,
+                        workspace_bytes, stream);
 }
 
 }  // extern "C"

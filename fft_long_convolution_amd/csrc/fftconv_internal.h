@@ -86,6 +86,8 @@ struct FwdParams {
     void* y;
     const void* kf;     // alpha/beta, [H][M] entries
     float2* ws;         // multi-pass workspace, [rows][M]
+    const void* w;      // input gate (layout of u) or null
+    const void* v;      // output gate (layout of y) or null
 };
 
 // Spectrum (alpha/beta) construction.
@@ -105,8 +107,11 @@ struct RowParams {
     int grid;                // workgroups
     const void* u;
     void* y;
+    const void* w;      // input gate (layout of u) or null
+    const void* v;      // output gate (layout of y) or null
     const void* kf;     // alpha/beta, [H][M] (4 x f16 each)
     const void* f1b;    // first stage, B-operand tiles [hi 4][lo 4][64]
+    const void* f1h;    // first stage in f16 [4][64] (gated rows)
     const void* i1a;    // last inverse stage, A-operand tiles [2][2][64]
     const void* f2a;    // inner forward stage, A-operand tiles
     const void* i2b;    // inner inverse stage, B-operand tiles
@@ -115,8 +120,10 @@ struct RowParams {
 };
 hipError_t launch_row(int io, int nb, const RowParams& p, int lds_bytes,
                       hipStream_t s);
-// Waves per row-kernel workgroup (one workgroup per CU).
+// Waves per row-kernel workgroup (one workgroup per CU); the LDS layout is
+// sized for kRowWaves.
 constexpr int kRowWaves = 16;
+constexpr int kRowWavesGated = 12;
 
 // Fused kernel for N = P * 1024 (P = 4, 8, 16, 16-bit I/O): one workgroup
 // of P/2 wavefronts per row (fftconv_wide.hip).
@@ -131,6 +138,8 @@ struct WideParams {
     uint32_t* ctr;           // claim counters (workspace, cleared per call)
     const void* u;
     void* y;
+    const void* w;           // input gate (layout of u) or null
+    const void* v;           // output gate (layout of y) or null
     const void* kf;          // coefficients, [H][P/2][2][2][4][64][2] (4 x f16)
     const void* f1b;         // 32-point stage over n_a, B tiles [ks 2][jt 4][64]
     const void* i1a;         // its inverse, A tiles [mt 4][ks 2][64]
@@ -161,6 +170,8 @@ struct MpColParams {
     const float2* tw;      // W_{P S}^c, c < S
     const void* u;
     void* y;
+    const void* w;         // input gate (layout of u) or null
+    const void* v;         // output gate (layout of y) or null
     void* ws;
     uint32_t* ctr;         // first pass: clears the inner pass's counters
 };
@@ -177,6 +188,8 @@ struct MpCol2Params {
     const float2* tw2;     // W_{M/P1}^c, c < 4096
     const void* u;
     void* y;
+    const void* w;         // input gate (layout of u) or null
+    const void* v;         // output gate (layout of y) or null
     void* ws;
     uint32_t* ctr;         // forward pass: clears the inner pass's counters
     // matrix-core forward pass (P1 = P2 = 32)

@@ -391,49 +391,90 @@ __device__ __forceinline__ uint16_t f32_to_io(float f) {
     return __builtin_bit_cast(uint16_t, (_Float16)f);
 }
 
-// z[m] = u[2m] + i u[2m+1] for m in [0, cnt): 'src' points at u[2*m0].
-// Points land at line[(m - m0) * stride] within each run of 'run' points.
+// z[m] = u[2m] + i u[2m+1] for m in [0, npts): 'src' points at u[2*m0].
+// With a gate g (same layout as u, or null) the points are of u (.) g,
+// each product formed in fp32 (exact for 16-bit inputs).
 template <int IO>
-__device__ __forceinline__ void load_points(const void* src, float2* dst,
-                                            int npts, int tid, int nthr) {
+__device__ __forceinline__ void load_points(const void* src, const void* gsrc,
+                                            float2* dst, int npts, int tid,
+                                            int nthr) {
     if (IO == IO_F32) {
         const float4* s = (const float4*)src;
+        const float4* gs = (const float4*)gsrc;
         for (int j = tid; j < (npts >> 1); j += nthr) {
-            const float4 v = s[j];
+            float4 v = s[j];
+            if (gs) {
+                const float4 g = gs[j];
+                v = make_float4(v.x * g.x, v.y * g.y, v.z * g.z, v.w * g.w);
+            }
             dst[2 * j] = make_float2(v.x, v.y);
             dst[2 * j + 1] = make_float2(v.z, v.w);
         }
     } else {
         const uint4* s = (const uint4*)src;
+        const uint4* gs = (const uint4*)gsrc;
         for (int j = tid; j < (npts >> 2); j += nthr) {
             const uint4 v = s[j];
             const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+            float2 pt[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i)
-                dst[4 * j + i] = make_float2(io_to_f32<IO>((uint16_t)(w[i] & 0xffffu)),
-                                             io_to_f32<IO>((uint16_t)(w[i] >> 16)));
+                pt[i] = make_float2(io_to_f32<IO>((uint16_t)(w[i] & 0xffffu)),
+                                    io_to_f32<IO>((uint16_t)(w[i] >> 16)));
+            if (gs) {
+                const uint4 gv = gs[j];
+                const uint32_t gw[4] = {gv.x, gv.y, gv.z, gv.w};
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    pt[i].x *= io_to_f32<IO>((uint16_t)(gw[i] & 0xffffu));
+                    pt[i].y *= io_to_f32<IO>((uint16_t)(gw[i] >> 16));
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) dst[4 * j + i] = pt[i];
         }
     }
 }
 
+// y[2m], y[2m+1] = Re, Im of the points; with a gate g (same layout as y,
+// or null) each output is multiplied by g in fp32 before the one rounding
+// to the I/O type.
 template <int IO>
-__device__ __forceinline__ void store_points(const float2* src, void* dst,
-                                             int npts, int tid, int nthr) {
+__device__ __forceinline__ void store_points(const float2* src, const void* gsrc,
+                                             void* dst, int npts, int tid,
+                                             int nthr) {
     if (IO == IO_F32) {
         float4* o = (float4*)dst;
+        const float4* gs = (const float4*)gsrc;
         for (int j = tid; j < (npts >> 1); j += nthr) {
             const float2 a = src[2 * j], b = src[2 * j + 1];
-            o[j] = make_float4(a.x, a.y, b.x, b.y);
+            float4 r = make_float4(a.x, a.y, b.x, b.y);
+            if (gs) {
+                const float4 g = gs[j];
+                r = make_float4(r.x * g.x, r.y * g.y, r.z * g.z, r.w * g.w);
+            }
+            o[j] = r;
         }
     } else {
         uint4* o = (uint4*)dst;
+        const uint4* gs = (const uint4*)gsrc;
         for (int j = tid; j < (npts >> 2); j += nthr) {
+            float2 pt[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) pt[i] = src[4 * j + i];
+            if (gs) {
+                const uint4 gv = gs[j];
+                const uint32_t gw[4] = {gv.x, gv.y, gv.z, gv.w};
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    pt[i].x *= io_to_f32<IO>((uint16_t)(gw[i] & 0xffffu));
+                    pt[i].y *= io_to_f32<IO>((uint16_t)(gw[i] >> 16));
+                }
+            }
             uint32_t w[4];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const float2 a = src[4 * j + i];
-                w[i] = (uint32_t)f32_to_io<IO>(a.x) | ((uint32_t)f32_to_io<IO>(a.y) << 16);
-            }
+            for (int i = 0; i < 4; ++i)
+                w[i] = (uint32_t)f32_to_io<IO>(pt[i].x) | ((uint32_t)f32_to_io<IO>(pt[i].y) << 16);
             o[j] = make_uint4(w[0], w[1], w[2], w[3]);
         }
     }
@@ -442,6 +483,11 @@ __device__ __forceinline__ void store_points(const float2* src, void* dst,
 template <int IO>
 __device__ __forceinline__ const char* io_ptr(const void* base, long long elem) {
     return (const char*)base + elem * (IO == IO_F32 ? 4 : 2);
+}
+// the same for an optional gate (null stays null)
+template <int IO>
+__device__ __forceinline__ const char* gate_ptr(const void* base, long long elem) {
+    return base ? io_ptr<IO>(base, elem) : nullptr;
 }
 
 // ---------------------------------------------------------------------------
@@ -456,8 +502,8 @@ __global__ void __launch_bounds__(512) fused_kernel(FwdParams P) {
     float2* scratch = smem + P.M + wave * 32;
     for (long long row = blockIdx.x; row < P.rows; row += gridDim.x) {
         const int h = (int)(row % P.H);
-        load_points<IO>(io_ptr<IO>(P.u, row * P.N), line, P.N >> 1,
-                        threadIdx.x, blockDim.x);
+        load_points<IO>(io_ptr<IO>(P.u, row * P.N), gate_ptr<IO>(P.w, row * P.N),
+                        line, P.N >> 1, threadIdx.x, blockDim.x);
         __syncthreads();
         for (int i = 0; i < P.nst; ++i) {
             dispatch_stage<MF, false>(i == 0 && P.outer_half, P.st[i], line,
@@ -473,7 +519,8 @@ __global__ void __launch_bounds__(512) fused_kernel(FwdParams P) {
                                      P.M, 0, wave, nwaves, lane);
             __syncthreads();
         }
-        store_points<IO>(line, (void*)io_ptr<IO>(P.y, row * P.N), P.N >> 1,
+        store_points<IO>(line, gate_ptr<IO>(P.v, row * P.N),
+                         (void*)io_ptr<IO>(P.y, row * P.N), P.N >> 1,
                          threadIdx.x, blockDim.x);
         __syncthreads();
     }
@@ -498,9 +545,11 @@ __global__ void __launch_bounds__(512) outer_fwd_kernel(FwdParams P) {
     const int slab = P.M / P.Qo;
     float2* line = smem;
     // the nonzero half of the outer digits: n_o < Qo/2
-    for (int no = 0; no < (P.Qo >> 1); ++no)
-        load_points<IO>(io_ptr<IO>(P.u, row * P.N + 2LL * ((long long)no * slab + c0)),
+    for (int no = 0; no < (P.Qo >> 1); ++no) {
+        const long long e0 = row * P.N + 2LL * ((long long)no * slab + c0);
+        load_points<IO>(io_ptr<IO>(P.u, e0), gate_ptr<IO>(P.w, e0),
                         line + no * P.ct, P.ct, threadIdx.x, blockDim.x);
+    }
     __syncthreads();
     for (int i = 0; i < P.nst; ++i) {
         dispatch_stage<MF, false>(i == 0, P.st[i], line, P.Qo * P.ct, c0,
@@ -586,10 +635,11 @@ __global__ void __launch_bounds__(512) outer_inv_kernel(FwdParams P) {
                                  wave, nwaves, lane);
         __syncthreads();
     }
-    for (int no = 0; no < (P.Qo >> 1); ++no)
-        store_points<IO>(line + no * P.ct,
-                         (void*)io_ptr<IO>(P.y, row * P.N + 2LL * ((long long)no * slab + c0)),
-                         P.ct, threadIdx.x, blockDim.x);
+    for (int no = 0; no < (P.Qo >> 1); ++no) {
+        const long long e0 = row * P.N + 2LL * ((long long)no * slab + c0);
+        store_points<IO>(line + no * P.ct, gate_ptr<IO>(P.v, e0),
+                         (void*)io_ptr<IO>(P.y, e0), P.ct, threadIdx.x, blockDim.x);
+    }
 }
 
 // ---------------------------------------------------------------------------

@@ -113,6 +113,31 @@ __device__ __forceinline__ rhalf2 hpair(rhalf2 a, rhalf2 z, rhalf2 b, rhalf2 p) 
     return __builtin_elementwise_fma(byy, pn, r);
 }
 
+// Gates (element-wise products with a second tensor of the I/O layout).
+// u (.) w of two packed 16-bit I/O pairs, as packed f16: each product is
+// exact in fp32 (or formed by the correctly rounded packed f16 multiply)
+// and rounded once.
+template <int IO>
+__device__ __forceinline__ uint32_t gate_in(uint32_t u, uint32_t w) {
+    if constexpr (IO == IO_BF16) {
+        return pk2(__uint_as_float(u << 16) * __uint_as_float(w << 16),
+                   __uint_as_float(u & 0xffff0000u) * __uint_as_float(w & 0xffff0000u));
+    } else {
+        return as_u32(as_h2(u) * as_h2(w));
+    }
+}
+// the low and high values of a packed 16-bit I/O pair in fp32
+template <int IO>
+__device__ __forceinline__ float io_lo(uint32_t v) {
+    if constexpr (IO == IO_BF16) return __uint_as_float(v << 16);
+    else return (float)as_h2(v).x;
+}
+template <int IO>
+__device__ __forceinline__ float io_hi(uint32_t v) {
+    if constexpr (IO == IO_BF16) return __uint_as_float(v & 0xffff0000u);
+    else return (float)as_h2(v).y;
+}
+
 // Exchange between 16-lane rows: the odd rows of a trade places with the
 // even rows of c (rows 1 <-> 0 and 3 <-> 2).
 __device__ __forceinline__ void swap16(uint32_t& a, uint32_t& c) {

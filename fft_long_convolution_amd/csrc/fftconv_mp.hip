@@ -65,6 +65,13 @@ __global__ void __launch_bounds__(256) mp_col_kernel(MpColParams prm) {
 #pragma unroll
         for (int n = 0; n < P / 2; ++n)
             xin[n] = f2_from_io<IO>(__builtin_nontemporal_load(&u[(long long)n * prm.S])) * sc;
+        if (prm.w) {
+            // input gate: u (.) w, exact in fp32
+            const uint32_t* w = (const uint32_t*)prm.w + mrow * (long long)(prm.M / 2) + c;
+#pragma unroll
+            for (int n = 0; n < P / 2; ++n)
+                xin[n] = xin[n] * f2_from_io<IO>(__builtin_nontemporal_load(&w[(long long)n * prm.S]));
+        }
         dft_half_in<P>(xin, v);
     } else if constexpr (MODE == 1) {
 #pragma unroll
@@ -95,6 +102,13 @@ __global__ void __launch_bounds__(256) mp_col_kernel(MpColParams prm) {
     } else {
         rfloat2 z[P / 2];
         idft_half_out<P>(v, z);
+        if (prm.v) {
+            // output gate, in fp32 before the one rounding to the I/O type
+            const uint32_t* g = (const uint32_t*)prm.v + mrow * (long long)(prm.M / 2) + c;
+#pragma unroll
+            for (int n = 0; n < P / 2; ++n)
+                z[n] = z[n] * f2_from_io<IO>(__builtin_nontemporal_load(&g[(long long)n * prm.S]));
+        }
         uint32_t* y = (uint32_t*)prm.y + mrow * (long long)(prm.M / 2) + c;
 #pragma unroll
         for (int n = 0; n < P / 2; ++n) __builtin_nontemporal_store(pk2io<IO>(z[n].x, z[n].y), &y[(long long)n * prm.S]);
@@ -114,10 +128,15 @@ __global__ void __launch_bounds__(256) mp_col_kernel(MpColParams prm) {
 // Workgroups of 256 threads (two per CU) are persistent: every global load
 // of the next tile (data and twiddles) is issued before the current tile's
 // second level, so HBM reads overlap the arithmetic and the stores.
+// Gated rows (G): the forward pass multiplies u by the input gate, fetched
+// for the current tile as its level 1 starts; the inverse pass fetches the
+// output gate of each level-1 task as the task starts and multiplies the
+// fp32 results before the store; it issues the next tile's prefetch after
+// level 1, so that the gate's loads never wait behind it.
 constexpr int kCol2Threads = 256;
 constexpr int col2_cols(int P2) { return 512 / P2; }
 
-template <int IO, int P1, int P2, bool INV>
+template <int IO, int P1, int P2, bool INV, bool G>
 __global__ void __launch_bounds__(kCol2Threads, 2) mp_col2_kernel(MpCol2Params prm) {
     constexpr int TC = col2_cols(P2), SLAB = 4096, TPR = SLAB / TC;
     constexpr int NT = kCol2Threads;
@@ -176,6 +195,18 @@ __global__ void __launch_bounds__(kCol2Threads, 2) mp_col2_kernel(MpCol2Params p
         for (; t < ntiles; t += gridDim.x) {
             int c0;
             const long long r = row_of(t, c0);
+            uint32_t graw[G ? L1T : 1][P1 / 2];   // input gate of this tile
+            if constexpr (G) {
+                const uint32_t* w = (const uint32_t*)prm.w + mem_row(r) * (M / 2) + c0;
+#pragma unroll
+                for (int i = 0; i < L1T; ++i) {
+                    const int task = tid + i * NT;
+                    const long long col = (long long)(task / TC) * SLAB + task % TC;
+#pragma unroll
+                    for (int n1 = 0; n1 < P1 / 2; ++n1)
+                        graw[i][n1] = __builtin_nontemporal_load(&w[(long long)n1 * M2 + col]);
+                }
+            }
             // level 1: P1-point DFT of the P1/2 nonzero inputs, twiddle, to LDS
 #pragma unroll
             for (int i = 0; i < L1T; ++i) {
@@ -184,7 +215,10 @@ __global__ void __launch_bounds__(kCol2Threads, 2) mp_col2_kernel(MpCol2Params p
                 const int task = tid + i * NT, c = task % TC, n2 = task / TC;
                 rfloat2 xin[P1 / 2], v[P1];
 #pragma unroll
-                for (int n1 = 0; n1 < P1 / 2; ++n1) xin[n1] = f2_from_io<IO>(raw[i][n1]) * sc1;
+                for (int n1 = 0; n1 < P1 / 2; ++n1) {
+                    xin[n1] = f2_from_io<IO>(raw[i][n1]) * sc1;
+                    if constexpr (G) xin[n1] = xin[n1] * f2_from_io<IO>(graw[i][n1]);
+                }
                 dft_half_in<P1>(xin, v);
                 const rfloat2 t1 = {tw1[i].x, tw1[i].y};
                 rfloat2 w = t1;
@@ -274,7 +308,9 @@ __global__ void __launch_bounds__(kCol2Threads, 2) mp_col2_kernel(MpCol2Params p
 #pragma unroll
             for (int i = 0; i < L1T; ++i) tw1c[i] = tw1[i];
             __syncthreads();
-            if (t + gridDim.x < ntiles) fetch(t + gridDim.x);
+            if constexpr (!G) {
+                if (t + gridDim.x < ntiles) fetch(t + gridDim.x);
+            }
             // inverse level 1: conjugate twiddle, P1-point inverse DFT, the
             // P1/2 outputs t < N to y
             uint32_t* y = (uint32_t*)prm.y + mem_row(r) * (M / 2) + c0;
@@ -283,6 +319,14 @@ __global__ void __launch_bounds__(kCol2Threads, 2) mp_col2_kernel(MpCol2Params p
                 // one task at a time: interleaved tasks would not fit the registers
                 __builtin_amdgcn_sched_barrier(0);
                 const int task = tid + i * NT, c = task % TC, n2 = task / TC;
+                uint32_t graw[G ? P1 / 2 : 1];   // output gate of this task
+                if constexpr (G) {
+                    const uint32_t* gv = (const uint32_t*)prm.v + mem_row(r) * (M / 2) + c0 +
+                                         (long long)n2 * SLAB + c;
+#pragma unroll
+                    for (int n1 = 0; n1 < P1 / 2; ++n1)
+                        graw[n1] = __builtin_nontemporal_load(&gv[(long long)n1 * M2]);
+                }
                 const rfloat2 t1 = {tw1c[i].x, tw1c[i].y};
                 rfloat2 v[P1], w = t1;
                 v[0] = f2_from_h2(s_t[lidx(0, n2, c)]) * sc1;
@@ -293,10 +337,17 @@ __global__ void __launch_bounds__(kCol2Threads, 2) mp_col2_kernel(MpCol2Params p
                 }
                 rfloat2 z[P1 / 2];
                 idft_half_out<P1>(v, z);
+                if constexpr (G) {
+#pragma unroll
+                    for (int n1 = 0; n1 < P1 / 2; ++n1) z[n1] = z[n1] * f2_from_io<IO>(graw[n1]);
+                }
                 uint32_t* o = y + (long long)n2 * SLAB + c;
 #pragma unroll
                 for (int n1 = 0; n1 < P1 / 2; ++n1)
                     __builtin_nontemporal_store(pk2io<IO>(z[n1].x, z[n1].y), &o[(long long)n1 * M2]);
+            }
+            if constexpr (G) {
+                if (t + gridDim.x < ntiles) fetch(t + gridDim.x);
             }
             __syncthreads();
         }
@@ -320,7 +371,10 @@ __global__ void __launch_bounds__(kCol2Threads, 2) mp_col2_kernel(MpCol2Params p
 // exchange between 16-lane rows rearranges them into (or out of) operands.
 // The intermediate is stored [k1][c][n2] with the 16-byte granule n2 / 4
 // xor-ed with c % 8 (conflict-free 128-bit accesses).
-template <int IO>
+// Gated rows (G): the input gate of the tile is fetched as the tile starts
+// (the prefetch of u is already in) and u (.) w enters level 1 as f16, with
+// f16 hi/lo DFT operands for both I/O types.
+template <int IO, bool G>
 __global__ void __launch_bounds__(512, 2) mp_col2m_fwd_kernel(MpCol2Params prm) {
     constexpr int SLAB = 4096, TC = 32, TPR = SLAB / TC;
     constexpr long long M2 = 32LL * SLAB, M = 32LL * M2;
@@ -353,7 +407,7 @@ __global__ void __launch_bounds__(512, 2) mp_col2m_fwd_kernel(MpCol2Params prm) 
     for (int i = tid; i < 1024; i += 512) s_twn[i] = g_twn[i];
 
     auto mma = [](uint4 a, uint4 b, rfloat4 c) {
-        return IO == IO_BF16 ? mma_bf16(a, b, c) : mma_f16(a, b, c);
+        return (IO == IO_BF16 && !G) ? mma_bf16(a, b, c) : mma_f16(a, b, c);
     };
     auto cmulf = [](float2 a, float2 b) { return make_float2(a.x * b.x - a.y * b.y, a.x * b.y + a.y * b.x); };
     auto mid = [](int k1, int c, int gr) { return (k1 * 32 + c) * 8 + (gr ^ (c & 7)); };
@@ -363,14 +417,14 @@ __global__ void __launch_bounds__(512, 2) mp_col2m_fwd_kernel(MpCol2Params prm) 
         return r;
     };
     // per-tile twiddle tables, [k][c] (lanes of a group read 16 columns c of
-    // one k: distinct banks): entry (k, c) = G[c0 / 32][k] Gb[c][k]
+    // one k: distinct banks): entry (k, c) = Ta[c0 / 32][k] Tb[c][k]
     float2 tg[2][2];   // loaded operands of this thread's two entries
-    auto tw_load = [&](const float2* G, const float2* Gb, int c0) {
+    auto tw_load = [&](const float2* Ta, const float2* Tb, int c0) {
 #pragma unroll
         for (int q = 0; q < 2; ++q) {
             const int e = tid + 512 * q, k = e >> 5, c = e & 31;
-            tg[q][0] = G[(c0 >> 5) * 32 + k];
-            tg[q][1] = Gb[c * 32 + k];
+            tg[q][0] = Ta[(c0 >> 5) * 32 + k];
+            tg[q][1] = Tb[c * 32 + k];
         }
     };
     auto tw_store = [&](float2* T) {
@@ -380,18 +434,19 @@ __global__ void __launch_bounds__(512, 2) mp_col2m_fwd_kernel(MpCol2Params prm) 
     // next tile's input: wave w takes n2 = 4 w + j; lane (g, x) loads rows
     // n1 = 8 (g / 2) + r of column 16 (g % 2) + x
     uint32_t raw[4][8];
-    auto fetch = [&](long long t) {
+    auto fetch_into = [&](uint32_t (&dst)[4][8], const void* base, long long t) {
         int c0;
         const long long r = tile_of(t, c0);
         const unsigned bq = (unsigned)r / (unsigned)prm.hc;
         const long long mrow = (long long)bq * prm.H + prm.h0 + ((unsigned)r - bq * (unsigned)prm.hc);
-        const uint32_t* u = (const uint32_t*)prm.u + mrow * (M / 2) + (long long)(8 * (g >> 1)) * M2 +
+        const uint32_t* u = (const uint32_t*)base + mrow * (M / 2) + (long long)(8 * (g >> 1)) * M2 +
                             (long long)(4 * wave) * SLAB + c0 + 16 * (g & 1) + x;
 #pragma unroll
         for (int j = 0; j < 4; ++j)
 #pragma unroll
-            for (int q = 0; q < 8; ++q) raw[j][q] = __builtin_nontemporal_load(&u[q * M2 + j * SLAB]);
+            for (int q = 0; q < 8; ++q) dst[j][q] = __builtin_nontemporal_load(&u[q * M2 + j * SLAB]);
     };
+    auto fetch = [&](long long t) { fetch_into(raw, prm.u, t); };
 
     long long t = blockIdx.x;
     if (t < ntiles) {
@@ -407,6 +462,14 @@ __global__ void __launch_bounds__(512, 2) mp_col2m_fwd_kernel(MpCol2Params prm) 
         int c0;
         const long long r = tile_of(t, c0);
         tw_load(g_2, g_2b, c0);       // level-2 table of this tile, stored below
+        if constexpr (G) {
+            uint32_t graw[4][8];
+            fetch_into(graw, prm.w, t);
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+#pragma unroll
+                for (int q = 0; q < 8; ++q) raw[j][q] = gate_in<IO>(raw[j][q], graw[j][q]);
+        }
         // ---------------- level 1
         {
             uint4 bop[4][2];
@@ -518,7 +581,12 @@ __global__ void __launch_bounds__(512, 2) mp_col2m_fwd_kernel(MpCol2Params prm) 
 //     W_1024^{-n2 k1} W_M^{-(c0 + c) k1}; to LDS [n2][c][k1] as f16;
 //   level 1: for each (n2, c) the inverse DFT over k1, only n1 < 16 (t < N),
 //     to y.
-template <int IO>
+// Gated rows (G): the output gate of the tile is fetched, at the stores'
+// addresses, before level 1 and multiplies the fp32 results before the one
+// rounding to the I/O type; the next tile's workspace values are then
+// fetched after level 1 so that both sets of registers are never live
+// together.
+template <int IO, bool G>
 __global__ void __launch_bounds__(512, 2) mp_col2m_inv_kernel(MpCol2Params prm) {
     constexpr int SLAB = 4096, TC = 32, TPR = SLAB / TC;
     constexpr long long M2 = 32LL * SLAB, M = 32LL * M2;
@@ -664,6 +732,25 @@ __global__ void __launch_bounds__(512, 2) mp_col2m_inv_kernel(MpCol2Params prm) 
         }
         __syncthreads();
         const long long tn_ = t + gridDim.x;
+        const unsigned bq = (unsigned)r / (unsigned)prm.hc;
+        const long long mrow = (long long)bq * prm.H + prm.h0 + ((unsigned)r - bq * (unsigned)prm.hc);
+        // output gate at the stores' addresses: [j][mt][e][row n1, n1 + 2]
+        uint32_t graw[G ? 4 : 1][2][2][2];
+        if constexpr (G) {
+            const uint32_t* gv = (const uint32_t*)prm.v + mrow * (M / 2) + c0 + 16 * (g & 1) + x;
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+#pragma unroll
+                for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+                    for (int e = 0; e < 2; ++e)
+#pragma unroll
+                        for (int p2 = 0; p2 < 2; ++p2) {
+                            const int n1 = 8 * mt + 4 * (g >> 1) + e + 2 * p2;
+                            graw[j][mt][e][p2] = __builtin_nontemporal_load(
+                                &gv[(long long)n1 * M2 + (long long)(4 * wave + j) * SLAB]);
+                        }
+        }
         uint4 a1[2][2][2];
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt)
@@ -671,7 +758,7 @@ __global__ void __launch_bounds__(512, 2) mp_col2m_inv_kernel(MpCol2Params prm) 
             for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
                 for (int hl = 0; hl < 2; ++hl) a1[mt][ks][hl] = buf_ld16(rs_a1, lane * 16, (((mt * 2 + ks) * 2 + hl) * 64) * 16);
-        if (tn_ < ntiles) {
+        if (!G && tn_ < ntiles) {
             int c0n;
             tile_of(tn_, c0n);
             tw_load(c0n);
@@ -679,8 +766,6 @@ __global__ void __launch_bounds__(512, 2) mp_col2m_inv_kernel(MpCol2Params prm) 
         }
         // ---------------- inverse level 1: wave w takes n2 = 4 w + j
         {
-            const unsigned bq = (unsigned)r / (unsigned)prm.hc;
-            const long long mrow = (long long)bq * prm.H + prm.h0 + ((unsigned)r - bq * (unsigned)prm.hc);
             uint32_t* y = (uint32_t*)prm.y + mrow * (M / 2) + c0 + 16 * (g & 1) + x;
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
@@ -693,6 +778,12 @@ __global__ void __launch_bounds__(512, 2) mp_col2m_inv_kernel(MpCol2Params prm) 
 #pragma unroll
                 for (int mt = 0; mt < 2; ++mt) {
                     uint32_t o[2][2];
+                    if constexpr (G) {
+                        // back to the layout of the results (the exchange
+                        // below is its own inverse)
+#pragma unroll
+                        for (int e = 0; e < 2; ++e) swap16(graw[j][mt][e][0], graw[j][mt][e][1]);
+                    }
 #pragma unroll
                     for (int h = 0; h < 2; ++h) {
                         rfloat4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -702,7 +793,13 @@ __global__ void __launch_bounds__(512, 2) mp_col2m_inv_kernel(MpCol2Params prm) 
                             acc = mma_f16(a1[mt][ks][1], b[h][ks], acc);
                         }
 #pragma unroll
-                        for (int e = 0; e < 2; ++e) o[h][e] = pk2io<IO>(acc[2 * e], acc[2 * e + 1]);
+                        for (int e = 0; e < 2; ++e) {
+                            if constexpr (G)
+                                o[h][e] = pk2io<IO>(acc[2 * e] * io_lo<IO>(graw[j][mt][e][h]),
+                                                    acc[2 * e + 1] * io_hi<IO>(graw[j][mt][e][h]));
+                            else
+                                o[h][e] = pk2io<IO>(acc[2 * e], acc[2 * e + 1]);
+                        }
                     }
                     // rows n1 = 8 mt + 4 (g / 2) + e and + 2, whole lines
 #pragma unroll
@@ -715,6 +812,12 @@ __global__ void __launch_bounds__(512, 2) mp_col2m_inv_kernel(MpCol2Params prm) 
                 }
                 __builtin_amdgcn_sched_barrier(0);
             }
+        }
+        if (G && tn_ < ntiles) {
+            int c0n;
+            tile_of(tn_, c0n);
+            tw_load(c0n);
+            fetch(tn_);
         }
         if (tn_ < ntiles) tw_store();
         __syncthreads();
@@ -825,8 +928,19 @@ hipError_t launch_mp_col(int io, int P, int mode, const MpColParams& p, hipStrea
 template <int IO, int P1, int P2>
 hipError_t col2_launch(bool inv, const MpCol2Params& p, hipStream_t s) {
     const dim3 grid((unsigned)p.grid), blk(kCol2Threads);
-    if (inv) hipLaunchKernelGGL((mp_col2_kernel<IO, P1, P2, true>), grid, blk, 0, s, p);
-    else hipLaunchKernelGGL((mp_col2_kernel<IO, P1, P2, false>), grid, blk, 0, s, p);
+    // 32 x 32 plans take the matrix-core passes; only their plain variant
+    // of this kernel is kept
+    if constexpr (P1 == 32 && P2 == 32) {
+        if (p.w) return hipErrorInvalidValue;
+        if (inv) hipLaunchKernelGGL((mp_col2_kernel<IO, P1, P2, true, false>), grid, blk, 0, s, p);
+        else hipLaunchKernelGGL((mp_col2_kernel<IO, P1, P2, false, false>), grid, blk, 0, s, p);
+    } else if (p.w) {
+        if (inv) hipLaunchKernelGGL((mp_col2_kernel<IO, P1, P2, true, true>), grid, blk, 0, s, p);
+        else hipLaunchKernelGGL((mp_col2_kernel<IO, P1, P2, false, true>), grid, blk, 0, s, p);
+    } else {
+        if (inv) hipLaunchKernelGGL((mp_col2_kernel<IO, P1, P2, true, false>), grid, blk, 0, s, p);
+        else hipLaunchKernelGGL((mp_col2_kernel<IO, P1, P2, false, false>), grid, blk, 0, s, p);
+    }
     return hipGetLastError();
 }
 
@@ -850,34 +964,36 @@ hipError_t launch_mp_col2(int io, int P1, int P2, bool inv, const MpCol2Params& 
     return io == IO_BF16 ? col2_dispatch<IO_BF16>(P1, P2, inv, p, s) : col2_dispatch<IO_F16>(P1, P2, inv, p, s);
 }
 
-template <int IO>
+template <int IO, bool G>
 static hipError_t col2m_fwd_t(const MpCol2Params& p, hipStream_t s) {
-    const hipError_t e = hipFuncSetAttribute((const void*)mp_col2m_fwd_kernel<IO>,
+    const hipError_t e = hipFuncSetAttribute((const void*)mp_col2m_fwd_kernel<IO, G>,
                                              hipFuncAttributeMaxDynamicSharedMemorySize, kCol2mLds);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((mp_col2m_fwd_kernel<IO>), dim3((unsigned)p.grid), dim3(512), kCol2mLds, s, p);
+    hipLaunchKernelGGL((mp_col2m_fwd_kernel<IO, G>), dim3((unsigned)p.grid), dim3(512), kCol2mLds, s, p);
     return hipGetLastError();
 }
 
 hipError_t launch_mp_col2m_fwd(int io, const MpCol2Params& p, hipStream_t s) {
     if (p.rows <= 0) return hipSuccess;
     if (p.grid <= 0 || p.M != 4194304 || !p.a1 || !p.a2 || !p.tm) return hipErrorInvalidValue;
-    return io == IO_BF16 ? col2m_fwd_t<IO_BF16>(p, s) : col2m_fwd_t<IO_F16>(p, s);
+    if (p.w) return io == IO_BF16 ? col2m_fwd_t<IO_BF16, true>(p, s) : col2m_fwd_t<IO_F16, true>(p, s);
+    return io == IO_BF16 ? col2m_fwd_t<IO_BF16, false>(p, s) : col2m_fwd_t<IO_F16, false>(p, s);
 }
 
-template <int IO>
+template <int IO, bool G>
 static hipError_t col2m_inv_t(const MpCol2Params& p, hipStream_t s) {
-    const hipError_t e = hipFuncSetAttribute((const void*)mp_col2m_inv_kernel<IO>,
+    const hipError_t e = hipFuncSetAttribute((const void*)mp_col2m_inv_kernel<IO, G>,
                                              hipFuncAttributeMaxDynamicSharedMemorySize, kCol2mLds);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((mp_col2m_inv_kernel<IO>), dim3((unsigned)p.grid), dim3(512), kCol2mLds, s, p);
+    hipLaunchKernelGGL((mp_col2m_inv_kernel<IO, G>), dim3((unsigned)p.grid), dim3(512), kCol2mLds, s, p);
     return hipGetLastError();
 }
 
 hipError_t launch_mp_col2m_inv(int io, const MpCol2Params& p, hipStream_t s) {
     if (p.rows <= 0) return hipSuccess;
     if (p.grid <= 0 || p.M != 4194304 || !p.a1 || !p.a2 || !p.tm) return hipErrorInvalidValue;
-    return io == IO_BF16 ? col2m_inv_t<IO_BF16>(p, s) : col2m_inv_t<IO_F16>(p, s);
+    if (p.v) return io == IO_BF16 ? col2m_inv_t<IO_BF16, true>(p, s) : col2m_inv_t<IO_F16, true>(p, s);
+    return io == IO_BF16 ? col2m_inv_t<IO_BF16, false>(p, s) : col2m_inv_t<IO_F16, false>(p, s);
 }
 
 hipError_t launch_mp_coef(const MpCoefParams& p, hipStream_t s) {

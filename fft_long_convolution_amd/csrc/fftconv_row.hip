@@ -39,22 +39,34 @@ namespace fftconv {
 // the four stage tables are read from LDS at each use (keeping them in
 // registers would halve the waves per SIMD).  Input and output rows are touched once: non-temporal loads and
 // stores keep them from displacing the spectra in L2.
+//
+// Gated rows (y = v (.) ((u (.) w) * k)): the input gate rides in a second
+// ring beside u and multiplies it as the row is consumed; the product feeds
+// the first stage as f16 (for bf16 rows too: rounding it to bf16 would cost
+// as much as the whole error budget).  The output gate is fetched at the
+// start of the row, with the stores' addresses, and multiplies the fp32
+// accumulators before the one rounding to the I/O type.  The extra registers
+// take the workgroup down to twelve waves.
 constexpr int kRowDepth = 2;
 
-template <int IO, int NB>
-__global__ void __launch_bounds__(64 * kRowWaves, 1) row_kernel(RowParams P) {
+template <int IO, int NB, bool G>
+__global__ void __launch_bounds__(64 * (G ? kRowWavesGated : kRowWaves), 1)
+row_kernel(RowParams P) {
+    constexpr int WAVES = G ? kRowWavesGated : kRowWaves;
     constexpr int M = 32 * NB;
     constexpr int IT = NB / 16;    // n_b tiles
     constexpr int MT2 = NB / 8;    // k_b slot tiles
     constexpr int KS2 = NB / 16;   // K-steps over n_b / k_b
     constexpr int NT = NB / 16;    // n_b tiles of the inverse
     constexpr bool BF = (IO == IO_BF16);
-    constexpr int F1T = BF ? 8 : 4;
+    constexpr int F1R = BF ? 8 : 4;       // first-stage region (plan layout)
+    constexpr bool BFA = BF && !G;        // bf16 first-stage operands
+    constexpr int F1T = BFA ? 8 : 4;      // first-stage tiles used
     constexpr int D = kRowDepth;
 
     extern __shared__ uint4 s_lds[];
-    uint4* s_f1b = s_lds;                            // [F1T][64]
-    uint4* s_i1a = s_f1b + F1T * 64;                 // [4][64]
+    uint4* s_f1b = s_lds;                            // [F1R][64]
+    uint4* s_i1a = s_f1b + F1R * 64;                 // [4][64]
     uint4* s_f2a = s_i1a + 4 * 64;                   // [MT2][KS2][64]
     uint4* s_i2b = s_f2a + MT2 * KS2 * 64;           // [KS2][2 NT][64]
     uint32_t* s_ctr = (uint32_t*)(s_i2b + KS2 * 2 * NT * 64);   // row claim counter (16 B)
@@ -70,8 +82,9 @@ __global__ void __launch_bounds__(64 * kRowWaves, 1) row_kernel(RowParams P) {
     const long long r1 = min(total, r0 + P.rows_per_wg);
     const int h_lo = (int)(r0 / P.B);
 
-    constexpr int TH = 64 * kRowWaves;
-    for (int i = tid; i < F1T * 64; i += TH) s_f1b[i] = ((const uint4*)P.f1b)[i];
+    constexpr int TH = 64 * WAVES;
+    const uint4* f1src = (const uint4*)(G ? P.f1h : P.f1b);
+    for (int i = tid; i < F1T * 64; i += TH) s_f1b[i] = f1src[i];
     for (int i = tid; i < 4 * 64; i += TH) s_i1a[i] = ((const uint4*)P.i1a)[i];
     for (int i = tid; i < MT2 * KS2 * 64; i += TH) s_f2a[i] = ((const uint4*)P.f2a)[i];
     for (int i = tid; i < KS2 * 2 * NT * 64; i += TH) s_i2b[i] = ((const uint4*)P.i2b)[i];
@@ -135,11 +148,11 @@ __global__ void __launch_bounds__(64 * kRowWaves, 1) row_kernel(RowParams P) {
         h = hh;
         b = off;
     };
-    auto load_row = [&](uint32_t (&dst)[IT][4], int c) {
+    auto load_row = [&](uint32_t (&dst)[IT][4], const void* base, int c) {
         int h, b;
         row_of(c, h, b);
         const uint32_t* u =
-            (const uint32_t*)P.u + ((long long)b * P.H + h) * (M / 2);
+            (const uint32_t*)base + ((long long)b * P.H + h) * (M / 2);
         if constexpr (NB == 32) {
             // whole 128-byte rows per load: lane groups g and g + 1 take the
             // two halves of rows 8 (g / 2) + q; the exchange into the
@@ -158,12 +171,14 @@ __global__ void __launch_bounds__(64 * kRowWaves, 1) row_kernel(RowParams P) {
     };
 
     uint32_t ring[D][IT][4];
+    uint32_t wring[G ? D : 1][IT][4];   // input gate rows (gated only)
     int cl[D];
     if (nslice > 0) {
 #pragma unroll
         for (int k = 0; k < D; ++k) {
             cl[k] = claim();
-            load_row(ring[k], cl[k]);
+            load_row(ring[k], P.u, cl[k]);
+            if constexpr (G) load_row(wring[k], P.w, cl[k]);
         }
     }
     // mirror exchange of the k_a = 0 column: every lane writes its column-0
@@ -171,14 +186,45 @@ __global__ void __launch_bounds__(64 * kRowWaves, 1) row_kernel(RowParams P) {
     uint32_t* scr = s_scr + wave * 16 * NB + x;
 
     {
-        auto row_body = [&](uint32_t (&cur)[IT][4], const int m) {
+        auto row_body = [&](uint32_t (&cur)[IT][4], uint32_t (&wcur)[IT][4], const int m) {
             int h, b;
             row_of(m, h, b);
             const long long row = (long long)b * P.H + h;
             const int abbase = (h - h_lo) * M;
+            // output gate at the stores' addresses: [mt][nt][e] is the word
+            // stored from o[nt][e] of tile mt (for NB = 32 after the
+            // exchange, which is undone below)
+            uint32_t vg[G ? 2 : 1][NT][2];
+            if constexpr (G) {
+                const uint32_t* vrow = (const uint32_t*)P.v + row * (long long)(M / 2);
+#pragma unroll
+                for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+                    for (int e = 0; e < 2; ++e) {
+                        if constexpr (NB == 32) {
+                            const int na = 8 * mt + 4 * (g >> 1) + e, w = (g & 1) ? kmap32(1, x) : x;
+                            vg[mt][0][e] = __builtin_nontemporal_load(&vrow[NB * na + w]);
+                            vg[mt][1][e] = __builtin_nontemporal_load(&vrow[NB * (na + 2) + w]);
+                        } else {
+#pragma unroll
+                            for (int nt = 0; nt < NT; ++nt)
+                                vg[mt][nt][e] = __builtin_nontemporal_load(
+                                    &vrow[NB * (8 * mt + 2 * g + e) + nbmap<NB>(nt, x)]);
+                        }
+                    }
+            }
             if constexpr (NB == 32) {
 #pragma unroll
-                for (int jj = 0; jj < 4; ++jj) swap16(cur[0][jj], cur[1][jj]);
+                for (int jj = 0; jj < 4; ++jj) {
+                    swap16(cur[0][jj], cur[1][jj]);
+                    if constexpr (G) swap16(wcur[0][jj], wcur[1][jj]);
+                }
+            }
+            if constexpr (G) {
+#pragma unroll
+                for (int it = 0; it < IT; ++it)
+#pragma unroll
+                    for (int jj = 0; jj < 4; ++jj) cur[it][jj] = gate_in<IO>(cur[it][jj], wcur[it][jj]);
             }
             // ---- F1: 32-point DFT over n_a (16 nonzero), k_a to the lanes
             uint4 b2[KS2][2];
@@ -189,7 +235,7 @@ __global__ void __launch_bounds__(64 * kRowWaves, 1) row_kernel(RowParams P) {
 #pragma unroll
                 for (int jt = 0; jt < 4; ++jt) {
                     rfloat4 acc = {0.f, 0.f, 0.f, 0.f};
-                    if (BF) {
+                    if (BFA) {
                         acc = mma_bf16(a, s_f1b[jt * 64 + lane], acc);
                         acc = mma_bf16(a, s_f1b[(4 + jt) * 64 + lane], acc);
                     } else {
@@ -296,6 +342,10 @@ __global__ void __launch_bounds__(64 * kRowWaves, 1) row_kernel(RowParams P) {
 #pragma unroll
             for (int mt = 0; mt < 2; ++mt) {
                 uint32_t o[NT][2];
+                if constexpr (G && NB == 32) {
+#pragma unroll
+                    for (int e = 0; e < 2; ++e) swap16(vg[mt][0][e], vg[mt][1][e]);
+                }
 #pragma unroll
                 for (int nt = 0; nt < NT; ++nt) {
                     rfloat4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -303,7 +353,13 @@ __global__ void __launch_bounds__(64 * kRowWaves, 1) row_kernel(RowParams P) {
                     for (int ks = 0; ks < 2; ++ks)
                         acc = mma_f16(s_i1a[(mt * 2 + ks) * 64 + lane], b1v[ks][nt], acc);
 #pragma unroll
-                    for (int e = 0; e < 2; ++e) o[nt][e] = pk2io<IO>(acc[2 * e], acc[2 * e + 1]);
+                    for (int e = 0; e < 2; ++e) {
+                        if constexpr (G)
+                            o[nt][e] = pk2io<IO>(acc[2 * e] * io_lo<IO>(vg[mt][nt][e]),
+                                                 acc[2 * e + 1] * io_hi<IO>(vg[mt][nt][e]));
+                        else
+                            o[nt][e] = pk2io<IO>(acc[2 * e], acc[2 * e + 1]);
+                    }
                 }
                 if constexpr (NB == 32) {
                     // rows n_a = 8 mt + 4 (g / 2) + e (+ 2): whole lines
@@ -330,9 +386,10 @@ __global__ void __launch_bounds__(64 * kRowWaves, 1) row_kernel(RowParams P) {
 #pragma unroll
             for (int k = 0; k < D; ++k) {
                 if (more && cl[k] < nslice) {
-                    row_body(ring[k], cl[k]);
+                    row_body(ring[k], wring[G ? k : 0], cl[k]);
                     cl[k] = claim();
-                    load_row(ring[k], cl[k]);
+                    load_row(ring[k], P.u, cl[k]);
+                    if constexpr (G) load_row(wring[k], P.w, cl[k]);
                 } else {
                     more = false;
                 }
@@ -341,20 +398,27 @@ __global__ void __launch_bounds__(64 * kRowWaves, 1) row_kernel(RowParams P) {
     }
 }
 
-template <int IO, int NB>
+template <int IO, int NB, bool G>
 static hipError_t launch_row_t(const RowParams& p, int lds, hipStream_t s) {
     if (lds > 64 * 1024) {
-        const hipError_t e = hipFuncSetAttribute((const void*)row_kernel<IO, NB>,
+        const hipError_t e = hipFuncSetAttribute((const void*)row_kernel<IO, NB, G>,
                                                  hipFuncAttributeMaxDynamicSharedMemorySize, lds);
         if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL((row_kernel<IO, NB>), dim3((unsigned)p.grid), dim3(64 * kRowWaves), lds, s, p);
+    hipLaunchKernelGGL((row_kernel<IO, NB, G>), dim3((unsigned)p.grid),
+                       dim3(64 * (G ? kRowWavesGated : kRowWaves)), lds, s, p);
     return hipGetLastError();
 }
 
+template <bool G>
+static hipError_t launch_row_g(int io, int nb, const RowParams& p, int lds, hipStream_t s) {
+    if (io == IO_BF16)
+        return nb == 32 ? launch_row_t<IO_BF16, 32, G>(p, lds, s) : launch_row_t<IO_BF16, 16, G>(p, lds, s);
+    return nb == 32 ? launch_row_t<IO_F16, 32, G>(p, lds, s) : launch_row_t<IO_F16, 16, G>(p, lds, s);
+}
+
 hipError_t launch_row(int io, int nb, const RowParams& p, int lds, hipStream_t s) {
-    if (io == IO_BF16) return nb == 32 ? launch_row_t<IO_BF16, 32>(p, lds, s) : launch_row_t<IO_BF16, 16>(p, lds, s);
-    return nb == 32 ? launch_row_t<IO_F16, 32>(p, lds, s) : launch_row_t<IO_F16, 16>(p, lds, s);
+    return p.w ? launch_row_g<true>(io, nb, p, lds, s) : launch_row_g<false>(io, nb, p, lds, s);
 }
 
 }  // namespace fftconv

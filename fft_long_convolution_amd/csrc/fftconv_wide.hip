@@ -20,6 +20,12 @@
 // Input and output rows are touched once and go through non-temporal
 // loads and stores, which keeps L2 for the spectrum coefficients.
 //
+// Gated rows (y = v (.) ((u (.) w) * k)): the input gate is prefetched with
+// u and multiplies it in the outer forward stage; the output gate is
+// fetched as the outer inverse stage starts and multiplies its results
+// before the store (fp32 for bf16 rows, packed f16 for f16 rows, as the
+// stage itself computes).
+//
 // Mirror pairing.  Bin k pairs with -k.  For 0 < k1 < P/2 the partner bins
 // live in sub-row P - k1.  That sub-row is pushed through the engine as
 // w_k1 * conj(A_{P-k1}) -- the same twiddle as sub-row k1 -- which returns
@@ -34,7 +40,7 @@ namespace fftconv {
 
 using namespace eng;
 
-template <int IO, int P>
+template <int IO, int P, bool G>
 __global__ void __launch_bounds__(32 * P, 2) wide_kernel(WideParams prm) {
     constexpr int Q = 1024, M = P * Q, HALF = P / 2, T = 32 * P;
     constexpr int CPT = Q / T;   // outer-stage columns per thread
@@ -99,14 +105,25 @@ __global__ void __launch_bounds__(32 * P, 2) wide_kernel(WideParams prm) {
     // on a per-n1 scalar base
     const int lofs = 32 * na0 + nb;
     uint32_t uin[HALF][CPT];
+    uint32_t win[G ? HALF : 1][CPT];   // input gate (gated only)
     auto load_u = [&](int idx) {
         const int hh = idx / prm.B, bb = idx - hh * prm.B;
-        const uint32_t* u = (const uint32_t*)prm.u + ((long long)bb * prm.H + hh) * (M / 2);
+        const long long off = ((long long)bb * prm.H + hh) * (M / 2);
+        const uint32_t* u = (const uint32_t*)prm.u + off;
 #pragma unroll
         for (int n1 = 0; n1 < HALF; ++n1) {
             const uint32_t* un = u + n1 * Q + lofs;
 #pragma unroll
             for (int j = 0; j < CPT; ++j) uin[n1][j] = __builtin_nontemporal_load(&un[32 * j]);
+        }
+        if constexpr (G) {
+            const uint32_t* w = (const uint32_t*)prm.w + off;
+#pragma unroll
+            for (int n1 = 0; n1 < HALF; ++n1) {
+                const uint32_t* wn = w + n1 * Q + lofs;
+#pragma unroll
+                for (int j = 0; j < CPT; ++j) win[n1][j] = __builtin_nontemporal_load(&wn[32 * j]);
+            }
         }
     };
     __syncthreads();
@@ -133,7 +150,10 @@ __global__ void __launch_bounds__(32 * P, 2) wide_kernel(WideParams prm) {
             for (int j = 0; j < CPT; ++j) {
                 C xin[HALF], A[P];
 #pragma unroll
-                for (int n1 = 0; n1 < HALF; ++n1) xin[n1] = O::from_io(uin[n1][j]);
+                for (int n1 = 0; n1 < HALF; ++n1) {
+                    xin[n1] = O::from_io(uin[n1][j]);
+                    if constexpr (G) xin[n1] = O::emul(xin[n1], win[n1][j]);
+                }
                 dft_half_in<P>(xin, A);
                 V[0][j] = O::to_h2(A[0]);
                 V[1][j] = O::to_h2(O::mul(A[HALF], two[HALF - 1][j]));
@@ -217,6 +237,15 @@ __global__ void __launch_bounds__(32 * P, 2) wide_kernel(WideParams prm) {
         const int nn = s_claim[0];
         // ---------------- outer inverse stage and store
         {
+            uint32_t vin[G ? HALF : 1][CPT];   // output gate (gated only)
+            if constexpr (G) {
+                const uint32_t* vr = (const uint32_t*)prm.v + mrow * (M / 2);
+#pragma unroll
+                for (int n1 = 0; n1 < HALF; ++n1)
+#pragma unroll
+                    for (int j = 0; j < CPT; ++j)
+                        vin[n1][j] = __builtin_nontemporal_load(&vr[n1 * Q + lofs + 32 * j]);
+            }
             uint32_t R[P][CPT];
 #pragma unroll
             for (int s = 0; s < P; ++s) {
@@ -253,8 +282,10 @@ __global__ void __launch_bounds__(32 * P, 2) wide_kernel(WideParams prm) {
                 }
                 idft_half_out<P>(Bv, zo);
 #pragma unroll
-                for (int n1 = 0; n1 < HALF; ++n1)
+                for (int n1 = 0; n1 < HALF; ++n1) {
+                    if constexpr (G) zo[n1] = O::emul(zo[n1], vin[n1][j]);
                     __builtin_nontemporal_store(O::to_io(zo[n1]), &yrow[n1 * Q + lofs + 32 * j]);
+                }
             }
         }
         cur = nxt;
@@ -271,17 +302,18 @@ hipError_t launch_claim_reset(uint32_t* ctr, hipStream_t s) {
     return hipGetLastError();
 }
 
-hipError_t launch_wide(int io, int P, const WideParams& p, int lds, hipStream_t s) {
+template <bool G>
+static hipError_t launch_wide_g(int io, int P, const WideParams& p, int lds, hipStream_t s) {
     const dim3 grid((unsigned)p.grid), blk((unsigned)(32 * P));
 #define FFTCONV_WIDE(IOT, PP)                                                              \
     do {                                                                                   \
         if (lds > 64 * 1024) {                                                             \
-            hipError_t e_ = hipFuncSetAttribute((const void*)wide_kernel<IOT, PP>,         \
+            hipError_t e_ = hipFuncSetAttribute((const void*)wide_kernel<IOT, PP, G>,      \
                                                 hipFuncAttributeMaxDynamicSharedMemorySize, \
                                                 lds);                                      \
             if (e_ != hipSuccess) return e_;                                               \
         }                                                                                  \
-        hipLaunchKernelGGL((wide_kernel<IOT, PP>), grid, blk, lds, s, p);                  \
+        hipLaunchKernelGGL((wide_kernel<IOT, PP, G>), grid, blk, lds, s, p);               \
     } while (0)
     if (io == IO_BF16) {
         if (P == 4) FFTCONV_WIDE(IO_BF16, 4);
@@ -294,6 +326,10 @@ hipError_t launch_wide(int io, int P, const WideParams& p, int lds, hipStream_t 
     }
 #undef FFTCONV_WIDE
     return hipGetLastError();
+}
+
+hipError_t launch_wide(int io, int P, const WideParams& p, int lds, hipStream_t s) {
+    return p.w ? launch_wide_g<true>(io, P, p, lds, s) : launch_wide_g<false>(io, P, p, lds, s);
 }
 
 // Spectrum coefficients in the wide kernel's engine order:

@@ -84,6 +84,9 @@ def lib() -> ctypes.CDLL:
         L.fftconv_kernel_spectrum.restype = i
         L.fftconv_forward.argtypes = [vp, vp, vp, vp, sz, sz, sz, vp, sz, vp]
         L.fftconv_forward.restype = i
+        L.fftconv_forward_gated.argtypes = [vp, vp, vp, vp, vp, vp, sz, sz,
+                                            sz, vp, sz, vp]
+        L.fftconv_forward_gated.restype = i
         L.fftconv_status_string.argtypes = [i]
         L.fftconv_status_string.restype = ctypes.c_char_p
         L.fftconv_version.argtypes = []
@@ -175,14 +178,12 @@ class FFTConv:
             raise FFTConvError(st, "fftconv_kernel_spectrum")
         return out
 
-    def forward(self, u, k_f, out=None, workspace=None, stream=None):
-        """u: [B, H, N] CUDA tensor of the plan dtype -> y (same shape)."""
+    def _prepare(self, u, out, workspace):
         import torch
         if u.dim() != 3 or u.shape[2] != self.N:
             raise ValueError("u must be [B, H, %d]" % self.N)
         if u.dtype != _torch_dtype(self.dtype):
             raise ValueError("u dtype must be %s" % self.dtype)
-        u = u.contiguous()
         B, H, N = u.shape
         if out is None:
             out = torch.empty_like(u)
@@ -196,9 +197,37 @@ class FFTConv:
                                         device=u.device)
             ws_ptr = workspace.data_ptr()
             ws_bytes = workspace.numel() * workspace.element_size()
+        return out, ws_ptr, ws_bytes
+
+    def forward(self, u, k_f, out=None, workspace=None, stream=None):
+        """u: [B, H, N] CUDA tensor of the plan dtype -> y (same shape)."""
+        u = u.contiguous()
+        out, ws_ptr, ws_bytes = self._prepare(u, out, workspace)
+        B, H, N = u.shape
         st = lib().fftconv_forward(self._plan, u.data_ptr(), k_f.data_ptr(),
                                    out.data_ptr(), B, H, N, ws_ptr, ws_bytes,
                                    _stream_handle(stream))
         if st != 0:
             raise FFTConvError(st, "fftconv_forward")
+        return out
+
+    def forward_gated(self, u, w, v, k_f, out=None, workspace=None,
+                      stream=None):
+        """y = v * conv(u * w, k): u, w, v are [B, H, N] CUDA tensors of the
+        plan dtype; returns y (same shape)."""
+        u = u.contiguous()
+        w = w.contiguous()
+        v = v.contiguous()
+        if w.shape != u.shape or v.shape != u.shape:
+            raise ValueError("gates must have the shape of u")
+        if w.dtype != u.dtype or v.dtype != u.dtype:
+            raise ValueError("gates must have the dtype of u")
+        out, ws_ptr, ws_bytes = self._prepare(u, out, workspace)
+        B, H, N = u.shape
+        st = lib().fftconv_forward_gated(
+            self._plan, u.data_ptr(), w.data_ptr(), v.data_ptr(),
+            k_f.data_ptr(), out.data_ptr(), B, H, N, ws_ptr, ws_bytes,
+            _stream_handle(stream))
+        if st != 0:
+            raise FFTConvError(st, "fftconv_forward_gated")
         return out

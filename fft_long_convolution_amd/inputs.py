@@ -153,6 +153,21 @@ def input_rows(w: Workload, rows=None) -> np.ndarray:
     return out
 
 
+def gate_rows(w: Workload, which: str, rows=None) -> np.ndarray:
+    """Gate rows of the gated convolution (r = b*H + h) in the storage
+    dtype: which = "w" (input gate) or "v" (output gate), each N(0,1) --
+    in H3/Hyena-style layers both gates are linear projections of the
+    layer input, Gaussian-like at initialisation."""
+    stream = {"w": 4, "v": 5}[which]
+    rows = np.arange(w.rows) if rows is None else np.asarray(rows, np.int64)
+    dt = {"f32": np.float32, "f16": np.float16, "bf16": np.uint16}[w.dtype]
+    out = np.empty((len(rows), w.N), dtype=dt)
+    for i, r in enumerate(rows):
+        out[i] = cast_io(_rng(w.wid, stream, int(r)).standard_normal(w.N),
+                         w.dtype)
+    return out
+
+
 def shrink(w: Workload, B: int | None = None, H: int | None = None,
            N: int | None = None) -> Workload:
     """Same generator recipe at a smaller shape (parity cases that the

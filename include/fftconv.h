@@ -151,6 +151,29 @@ fftconv_status fftconv_forward(fftconv_plan_t plan, const void *u,
                                size_t N, void *workspace,
                                size_t workspace_bytes, void *stream);
 
+/* Gated causal long convolution, y = v (.) ((u (.) w) * k)[0:N], for all
+ * B x H rows: the input gate w multiplies u element-wise before the
+ * convolution and the output gate v multiplies its result (page
+ * "FlashFFTConv: Efficient Convolutions for Long Sequences with Tensor
+ * Cores", section 3, "Domain-Specific Optimizations": the gating of
+ * H3/Hyena-style layers fused into the convolution kernel, so neither
+ * u (.) w nor the ungated result makes a round trip through HBM).
+ *  u, w, v: device, plan dtype, [B][H][N] contiguous, 16-B aligned; both
+ *     gates are required (a tensor of ones stands for an absent gate).
+ *  y: as in fftconv_forward; must not overlap u, w, v or k_f (checked:
+ *     FFTCONV_ERR_INVALID_ARG).  w and v may alias u or each other.
+ *  All other arguments, the workspace and the error behaviour are those of
+ *  fftconv_forward.  Products are formed in fp32 (exact for 16-bit
+ *  inputs); with 16-bit I/O the gated input enters the first transform
+ *  stage as f16, and the output gate multiplies the fp32 result before the
+ *  one rounding to the I/O type (f16 rows of N = 4K..16K multiply in
+ *  packed f16, as that stage computes). */
+fftconv_status fftconv_forward_gated(fftconv_plan_t plan, const void *u,
+                                     const void *w, const void *v,
+                                     const void *k_f, void *y, size_t B,
+                                     size_t H, size_t N, void *workspace,
+                                     size_t workspace_bytes, void *stream);
+
 /* Static, human-readable text for a status code. */
 const char *fftconv_status_string(fftconv_status status);
 

@@ -58,3 +58,38 @@ def parity(w: inputs.Workload, p: int = 0):
     y, u, k = run_gpu(w, p=p)
     ref = oracle_rows(w, u, k)
     return oracle.rel_l2(y, ref), y, ref
+
+
+def run_gpu_gated(w: inputs.Workload, conv=None, p: int = 0):
+    """GPU gated result v * conv(u * w, k) for all rows, as fp64."""
+    import torch
+    from fft_long_convolution_amd.fftconv import FFTConv
+    if conv is None:
+        conv = FFTConv(w.N, p=p, dtype=w.dtype)
+    u = inputs.input_rows(w)
+    gw = inputs.gate_rows(w, "w")
+    gv = inputs.gate_rows(w, "v")
+    k = inputs.kernel_rows(w)
+    dev = [to_torch(a, w.dtype).view(w.B, w.H, w.N) for a in (u, gw, gv)]
+    kf = conv.kernel_spectrum(torch.from_numpy(k).cuda())
+    y = conv.forward_gated(dev[0], dev[1], dev[2], kf)
+    torch.cuda.synchronize()
+    y64 = oracle.to_f64(from_torch(y, w.dtype).reshape(w.rows, w.N), w.dtype)
+    return y64, (u, gw, gv), k
+
+
+def oracle_gated_rows(w: inputs.Workload, ins, k: np.ndarray):
+    """fp64 oracle of the gated convolution for the same rows."""
+    u64, w64, v64 = (oracle.to_f64(a, w.dtype).reshape(w.rows, w.N)
+                     for a in ins)
+    k64 = k.astype(np.float64)
+    hidx = np.arange(w.rows) % w.H
+    if w.N <= 512:
+        return oracle.gated_direct(u64, w64, v64, k64, hidx)
+    return oracle.gated_fft(u64, w64, v64, k64, hidx)
+
+
+def parity_gated(w: inputs.Workload, p: int = 0):
+    y, ins, k = run_gpu_gated(w, p=p)
+    ref = oracle_gated_rows(w, ins, k)
+    return oracle.rel_l2(y, ref), y, ref

@@ -119,6 +119,8 @@ def test_bad_dtype_and_order():
 def test_null_plan_is_rejected_without_device():
     L = fc.lib()
     assert L.fftconv_forward(None, 16, 16, 16, 1, 1, 256, None, 0, None) == 1
+    assert L.fftconv_forward_gated(None, 16, 16, 16, 16, 16, 1, 1, 256, None,
+                                   0, None) == 1
     assert L.fftconv_kernel_spectrum(None, 16, 1, 16, None) == 1
     assert L.fftconv_spectrum_bytes(None, 4) == 0
     assert L.fftconv_workspace_bytes(None, 1, 1) == 0

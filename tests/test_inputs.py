@@ -78,3 +78,16 @@ def test_workload_shapes(name):
     w = inputs.WORKLOADS[name]
     assert w.N & (w.N - 1) == 0 and w.N >= 256
     assert w.dtype in ("f32", "f16", "bf16")
+
+
+def test_gate_rows():
+    w = inputs.shrink(inputs.WORKLOADS["hyena_bf16_n1k"], B=2, H=4)
+    gw = inputs.gate_rows(w, "w")
+    gv = inputs.gate_rows(w, "v")
+    assert gw.shape == (8, 1024) and gw.dtype == np.uint16
+    # reproducible, row-independent, and distinct from u and from each other
+    np.testing.assert_array_equal(inputs.gate_rows(w, "w", [5])[0], gw[5])
+    u = inputs.input_rows(w)
+    assert not np.array_equal(gw, gv) and not np.array_equal(gw, u)
+    x = (gv.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    assert abs(x.mean()) < 0.05 and abs(x.std() - 1.0) < 0.05
