@@ -10,6 +10,10 @@ B=64, H=768, N=1024 bf16 convolution.
 Prints one JSON line: throughput in outputs/s (B*H*N per step), the
 roofline of the dominant kernel, and the fp64 CPU oracle timed on the host
 as a baseline.
+
+--gated times the gated form y = v * ((u * w) conv k) instead (one
+fftconv_forward_gated per step; the gates are seeded N(0,1) tensors of the
+shape of u, resident in HBM like u).
 """
 from __future__ import annotations
 
@@ -66,6 +70,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=None)
     ap.add_argument("--warmup", type=int, default=None)
     ap.add_argument("--workload", default="hyena_bf16_n1k")
+    ap.add_argument("--gated", action="store_true",
+                    help="time the gated convolution v * ((u * w) conv k)")
     ap.add_argument("--no-cpu", action="store_true",
                     help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
@@ -113,18 +119,32 @@ def main():
     t0 = time.time()
     u_np = inputs.input_rows(w)
     k_np = inputs.kernel_rows(w)
+    g_np = ([inputs.gate_rows(w, "w"), inputs.gate_rows(w, "v")]
+            if args.gated else [])
     gen_s = time.time() - t0
     u0 = to_torch(u_np, w.dtype, torch).view(w.B, w.H, w.N).to(dev)
+    g0 = [to_torch(a, w.dtype, torch).view(w.B, w.H, w.N).to(dev) for a in g_np]
     k = torch.from_numpy(k_np).to(dev)
     kf = conv.kernel_spectrum(k)
     esz = 4 if w.dtype == "f32" else 2
-    set_bytes = 2 * w.rows * w.N * esz
+    # streams per step: u, y (+ the two gates)
+    nstream = 4 if args.gated else 2
+    set_bytes = nstream * w.rows * w.N * esz
     nsets = max(1, min(8, -(-ROTATE_BYTES // set_bytes)))
     us = [u0] + [u0.clone() for _ in range(nsets - 1)]
+    gs = [g0] + [[g.clone() for g in g0] for _ in range(nsets - 1)]
     ys = [torch.empty_like(u0) for _ in range(nsets)]
     wsb = conv.workspace_bytes(w.B, w.H)
     ws = torch.empty(max(wsb, 16), dtype=torch.uint8, device=dev)
     torch.cuda.synchronize()
+
+    def step(i):
+        j = i % nsets
+        if args.gated:
+            conv.forward_gated(us[j], gs[j][0], gs[j][1], kf, out=ys[j],
+                               workspace=ws)
+        else:
+            conv.forward(us[j], kf, out=ys[j], workspace=ws)
 
     # ---- warmup, then K timed steps between two HIP events recorded on the
     # stream the kernels are launched on (launches back to back)
@@ -132,12 +152,12 @@ def main():
     if args.steps is None or args.warmup is None:
         # estimate the step time (these calls are untimed warmup too)
         for i in range(3):
-            conv.forward(us[i % nsets], kf, out=ys[i % nsets], workspace=ws)
+            step(i)
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
         e0.record(stream)
         for i in range(10):
-            conv.forward(us[i % nsets], kf, out=ys[i % nsets], workspace=ws)
+            step(i)
         e1.record(stream)
         torch.cuda.synchronize()
         est = max(e0.elapsed_time(e1) / 10, 1e-3)
@@ -146,7 +166,7 @@ def main():
         if args.steps is None:
             args.steps = max(100, int(math.ceil(1000.0 / est)))
     for i in range(args.warmup):
-        conv.forward(us[i % nsets], kf, out=ys[i % nsets], workspace=ws)
+        step(i)
     torch.cuda.synchronize()
     ev0 = torch.cuda.Event(enable_timing=True)
     ev1 = torch.cuda.Event(enable_timing=True)
@@ -154,7 +174,7 @@ def main():
     wall0 = time.perf_counter()
     ev0.record(stream)
     for i in range(args.steps):
-        conv.forward(us[i % nsets], kf, out=ys[i % nsets], workspace=ws)
+        step(i)
     ev1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
@@ -165,7 +185,7 @@ def main():
         a = torch.cuda.Event(enable_timing=True)
         b = torch.cuda.Event(enable_timing=True)
         a.record(stream)
-        conv.forward(us[i % nsets], kf, out=ys[i % nsets], workspace=ws)
+        step(i)
         b.record(stream)
         per.append((a, b))
     torch.cuda.synchronize()
@@ -180,7 +200,7 @@ def main():
     # bracketed launches (ms_median_single_launch) also carry the events' own
     # overhead.
     kf_bytes = conv.spectrum_bytes(w.H)
-    alg_bytes = 2 * w.rows * w.N * esz + kf_bytes
+    alg_bytes = nstream * w.rows * w.N * esz + kf_bytes
     ms_kernel = ms_step
     achieved_gbs = alg_bytes / (ms_kernel * 1e-3) / 1e9
     flops = info["mfma_flops_per_row"] * w.rows
@@ -196,7 +216,7 @@ def main():
         roof = {"bound": "mfma", "achieved": round(achieved_tf, 2),
                 "peak": MFMA_PEAK_TFLOPS[w.dtype], "unit": "TFLOP/s",
                 "frac": round(achieved_tf / MFMA_PEAK_TFLOPS[w.dtype], 4)}
-    roof["traffic"] = measured_traffic(w.name)
+    roof["traffic"] = measured_traffic(w.name + ("_gated" if args.gated else ""))
     roof["kernel"] = info["kernel"]
     roof["algorithmic_bytes"] = int(alg_bytes)
     roof["mfma_flops"] = float(flops)
@@ -214,7 +234,12 @@ def main():
     sel_k = k_np.astype(np.float64)
     got = y_last[torch.from_numpy(rows).to(dev), torch.from_numpy(ts).to(dev)]
     got = got.float().cpu().numpy().astype(np.float64)
-    want = oracle.conv_points(sel_u, sel_k, np.arange(48), ts, rows % w.H)
+    if args.gated:
+        sel_w, sel_v = (oracle.to_f64(a[rows], w.dtype) for a in g_np)
+        want = oracle.gated_points(sel_u, sel_w, sel_v, sel_k, np.arange(48),
+                                   ts, rows % w.H)
+    else:
+        want = oracle.conv_points(sel_u, sel_k, np.arange(48), ts, rows % w.H)
     scale = float(np.sqrt(np.mean(want ** 2))) or 1.0
     sample_err = float(np.max(np.abs(got - want)) / scale)
 
@@ -225,24 +250,28 @@ def main():
         hidx = np.arange(w.rows) % w.H
         # probe a slice of about 4M outputs, then size the sample to the
         # requested CPU time (whole rows; at most the whole workload)
+        def cpu_run(n):
+            uh, inv = np.unique(hidx[:n], return_inverse=True)
+            usel = oracle.to_f64(u_np[:n], w.dtype)
+            ksel = k_np[uh].astype(np.float64)
+            gsel = [oracle.to_f64(a[:n], w.dtype) for a in g_np]
+            t0 = time.perf_counter()
+            if args.gated:
+                oracle.gated_fft(usel, gsel[0], gsel[1], ksel, inv)
+            else:
+                oracle.conv_fft(usel, ksel, inv)
+            return time.perf_counter() - t0
         probe = int(min(w.rows, max(1, (1 << 22) // w.N)))
-        t0 = time.perf_counter()
-        uh, inv = np.unique(hidx[:probe], return_inverse=True)
-        oracle.conv_fft(oracle.to_f64(u_np[:probe], w.dtype),
-                        k_np[uh].astype(np.float64), inv)
-        tp = time.perf_counter() - t0
+        tp = cpu_run(probe)
         n = int(min(w.rows, max(probe, probe * args.cpu_seconds / max(tp, 1e-6))))
-        uh, inv = np.unique(hidx[:n], return_inverse=True)
-        usel = oracle.to_f64(u_np[:n], w.dtype)
-        ksel = k_np[uh].astype(np.float64)
-        t0 = time.perf_counter()
-        oracle.conv_fft(usel, ksel, inv)
-        tc = time.perf_counter() - t0
+        tc = cpu_run(n)
         cpu = {"value": round(n * w.N / tc, 1), "unit": "outputs/s",
                "cores": cores, "kind": "oracle",
                "sample": "%d of %d rows (B*H) at N=%d through the fp64 "
-                         "radix-2 FFT route of the oracle, kernel spectra "
-                         "included; %.1f s" % (n, w.rows, w.N, tc)}
+                         "radix-2 FFT route of the oracle%s, kernel spectra "
+                         "included; %.1f s" % (n, w.rows, w.N,
+                                               " with both gates" if args.gated else "",
+                                               tc)}
 
     line = {
         "metric": METRIC, "value": round(value, 1), "unit": "outputs/s",
@@ -250,7 +279,9 @@ def main():
         "ms_per_step": round(ms_step, 5), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": w.dtype,
         "data": "synthetic",
-        "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N,
+        "config": {"workload": w.name + (" gated" if args.gated else ""),
+                   "op": "gated" if args.gated else "plain",
+                   "B": w.B, "H": w.H, "N": w.N,
                    "io_dtype": w.dtype, "factors": info["factors"],
                    "path": info["path"], "global_batch": w.B,
                    "seq_len": w.N, "parallelism": "single-gpu"},
