@@ -14,6 +14,14 @@ Cores", section 3.4):
   sequences zero-padded to 2N (iterative radix-2 FFT, no packing tricks);
 * ``conv_points``  -- single outputs by the definition (for sampled checks);
 * ``fft``          -- the radix-2 DFT itself, exposed for the oracle's pins;
+* ``op_direct`` / ``op_fft`` / ``op_points`` -- the operator family of
+  ``oracle.c`` by kind: "causal" (the convolution above), "causal_adjoint"
+  (its transpose, ``y[s] = sum_{t>=s} u[t] k[t-s]``, the input gradient),
+  "circular" (``y[t] = sum_s u[s] k[(t-s) mod N]``, the non-causal
+  convolution with an FFT of size N) and "circular_adjoint";
+* ``kgrad_direct`` / ``kgrad_fft`` / ``kgrad_points`` -- the kernel
+  gradient ``dk[h][j] = sum_{rows of h} sum_t dy[t] u[t-j]`` (t-j mod N for
+  the circular kinds);
 * ``gated_direct`` / ``gated_fft`` / ``gated_points`` -- the gated
   convolution ``y = v * ((u * w) conv k)`` (elementwise gates on the input
   and on the output; same page, section 3 "Technical Approach",
@@ -69,6 +77,19 @@ def _load():
         lib.oracle_kernel_spectrum.restype = None
         lib.oracle_conv_fft.argtypes = [d, d, lp, d, L, L, L]
         lib.oracle_conv_fft.restype = ctypes.c_int
+        I = ctypes.c_int
+        lib.oracle_op_direct.argtypes = [d, d, lp, d, L, L, I]
+        lib.oracle_op_direct.restype = None
+        lib.oracle_op_points.argtypes = [d, d, lp, L, lp, lp, L, I, d]
+        lib.oracle_op_points.restype = None
+        lib.oracle_op_fft.argtypes = [d, d, lp, d, L, L, L, I]
+        lib.oracle_op_fft.restype = ctypes.c_int
+        lib.oracle_kgrad_direct.argtypes = [d, d, lp, d, L, L, L, I]
+        lib.oracle_kgrad_direct.restype = None
+        lib.oracle_kgrad_fft.argtypes = [d, d, lp, d, L, L, L, I]
+        lib.oracle_kgrad_fft.restype = ctypes.c_int
+        lib.oracle_kgrad_points.argtypes = [d, d, lp, L, L, lp, lp, L, I, d]
+        lib.oracle_kgrad_points.restype = None
         _lib = lib
     return _lib
 
@@ -145,6 +166,113 @@ def conv_points(u, k, rows, ts, hidx=None) -> np.ndarray:
     out = np.empty(len(rows), dtype=np.float64)
     _load().oracle_conv_points(_dp(u), _dp(k), _lp(hidx), N, _lp(rows),
                                _lp(ts), len(rows), _dp(out))
+    return out
+
+
+KINDS = {"causal": 0, "causal_adjoint": 1, "circular": 2,
+         "circular_adjoint": 3}
+
+
+def _kind(kind: str) -> int:
+    if kind not in KINDS:
+        raise ValueError("unknown operator kind %r" % (kind,))
+    return KINDS[kind]
+
+
+def op_direct(u, k, kind: str, hidx=None) -> np.ndarray:
+    """Operator ``kind`` by its definition (fp64, O(N^2) per row)."""
+    kd = _kind(kind)
+    u, k, hidx, R, N = _rows(u, k, hidx)
+    y = np.empty((R, N), dtype=np.float64)
+    _load().oracle_op_direct(_dp(u), _dp(k), _lp(hidx), _dp(y), R, N, kd)
+    return y
+
+
+def op_fft(u, k, kind: str, hidx=None) -> np.ndarray:
+    """Operator ``kind`` through the convolution theorem (2N zero padding
+    for the causal kinds, size N for the circular ones; the adjoints use the
+    conjugate kernel spectrum)."""
+    kd = _kind(kind)
+    u, k, hidx, R, N = _rows(u, k, hidx)
+    if N & (N - 1):
+        raise ValueError("op_fft needs a power-of-two N")
+    y = np.empty((R, N), dtype=np.float64)
+    if _load().oracle_op_fft(_dp(u), _dp(k), _lp(hidx), _dp(y), R,
+                             k.shape[0], N, kd) != 0:
+        raise MemoryError("oracle_op_fft: allocation failed")
+    return y
+
+
+def op_points(u, k, kind: str, rows, ts, hidx=None) -> np.ndarray:
+    """out[i] = y[rows[i], ts[i]] of operator ``kind`` by the definition."""
+    kd = _kind(kind)
+    u, k, hidx, R, N = _rows(u, k, hidx)
+    rows = np.ascontiguousarray(rows, dtype=np.int64)
+    ts = np.ascontiguousarray(ts, dtype=np.int64)
+    if rows.shape != ts.shape or rows.ndim != 1:
+        raise ValueError("rows and ts must be 1-D of equal length")
+    if len(rows) and (rows.min() < 0 or rows.max() >= R or ts.min() < 0
+                      or ts.max() >= N):
+        raise ValueError("sample index out of range")
+    out = np.empty(len(rows), dtype=np.float64)
+    _load().oracle_op_points(_dp(u), _dp(k), _lp(hidx), N, _lp(rows),
+                             _lp(ts), len(rows), kd, _dp(out))
+    return out
+
+
+def _grad_rows(u, dy, Hk, hidx):
+    u = np.ascontiguousarray(u, dtype=np.float64)
+    dy = np.ascontiguousarray(dy, dtype=np.float64)
+    if u.shape != dy.shape or u.ndim != 2:
+        raise ValueError("u and dy must be [R, N] of the same shape")
+    R, N = u.shape
+    if hidx is None:
+        hidx = np.arange(R) % Hk
+    hidx = np.ascontiguousarray(hidx, dtype=np.int64)
+    if hidx.shape != (R,) or (R and (hidx.min() < 0 or hidx.max() >= Hk)):
+        raise ValueError("bad kernel row index")
+    return u, dy, hidx, R, N
+
+
+def kgrad_direct(u, dy, Hk: int, kind: str = "causal", hidx=None) -> np.ndarray:
+    """Kernel gradient dk [Hk, N] of operator ``kind`` (its own kind or its
+    adjoint give the same gradient of the forward kernel) by the
+    definition: dk[h][j] = sum over rows r of channel h of
+    sum_t dy[r][t] u[r][t-j]."""
+    kd = _kind(kind)
+    u, dy, hidx, R, N = _grad_rows(u, dy, Hk, hidx)
+    dk = np.empty((Hk, N), dtype=np.float64)
+    _load().oracle_kgrad_direct(_dp(u), _dp(dy), _lp(hidx), _dp(dk), R, Hk,
+                                N, kd)
+    return dk
+
+
+def kgrad_fft(u, dy, Hk: int, kind: str = "causal", hidx=None) -> np.ndarray:
+    """The kernel gradient through the convolution theorem:
+    IFFT(sum_r conj(FFT u_r) . FFT dy_r)[0:N]."""
+    kd = _kind(kind)
+    u, dy, hidx, R, N = _grad_rows(u, dy, Hk, hidx)
+    if N & (N - 1):
+        raise ValueError("kgrad_fft needs a power-of-two N")
+    dk = np.empty((Hk, N), dtype=np.float64)
+    if _load().oracle_kgrad_fft(_dp(u), _dp(dy), _lp(hidx), _dp(dk), R, Hk,
+                                N, kd) != 0:
+        raise MemoryError("oracle_kgrad_fft: allocation failed")
+    return dk
+
+
+def kgrad_points(u, dy, Hk: int, hs, js, kind: str = "causal",
+                 hidx=None) -> np.ndarray:
+    """out[i] = dk[hs[i], js[i]] by the definition."""
+    kd = _kind(kind)
+    u, dy, hidx, R, N = _grad_rows(u, dy, Hk, hidx)
+    hs = np.ascontiguousarray(hs, dtype=np.int64)
+    js = np.ascontiguousarray(js, dtype=np.int64)
+    if hs.shape != js.shape or hs.ndim != 1:
+        raise ValueError("hs and js must be 1-D of equal length")
+    out = np.empty(len(hs), dtype=np.float64)
+    _load().oracle_kgrad_points(_dp(u), _dp(dy), _lp(hidx), R, N, _lp(hs),
+                                _lp(js), len(hs), kd, _dp(out))
     return out
 
 

@@ -23,6 +23,25 @@
  * packing and no matrix (Monarch) factoring here: this file deliberately
  * computes the plain definitions so it can be checked by eye.
  *
+ * Further operators of the same family (same page, section 3: the
+ * non-causal convolutions of its benchmark tables use an FFT of size N, a
+ * circular convolution; training needs the gradients of the causal one,
+ * which section 3.3 writes as products with the conjugate spectra):
+ *
+ *   kind 0  causal             y[t] = sum_{s<=t} u[s] k[t-s]
+ *   kind 1  causal adjoint     y[s] = sum_{t>=s} u[t] k[t-s]
+ *                              (the transpose of kind 0: du from dy)
+ *   kind 2  circular           y[t] = sum_s u[s] k[(t-s) mod N]
+ *   kind 3  circular adjoint   y[s] = sum_t u[t] k[(t-s) mod N]
+ *
+ *   kernel gradient  dk[h][j] = sum_{rows r of channel h} sum_t
+ *                               dy[r][t] u[r][t-j]   (t-j taken mod N for
+ *                               the circular kinds, t-j >= 0 otherwise)
+ *
+ * each by its definition and, independently, through the convolution
+ * theorem (2N zero padding for the causal kinds, size N for the circular
+ * ones; the adjoints multiply by the conjugate spectrum).
+ *
  * All arithmetic is fp64.  Rows are independent; OpenMP splits them.
  */
 #include <math.h>
@@ -204,4 +223,232 @@ int oracle_conv_fft(const double *u, const double *kern, const long *hidx,
     free(kre);
     free(kim);
     return fail ? -1 : 0;
+}
+
+
+/* ---------------------------------------------------------------------
+ * The operator family (kinds 0..3 above) and the kernel gradient.
+ * ------------------------------------------------------------------- */
+
+/* k index of the term pairing output position a with input position b of
+ * operator `kind`, or -1 when the term is absent. */
+static long op_tap(int kind, long a, long b, long N)
+{
+    switch (kind) {
+    case 0: return b <= a ? a - b : -1;              /* y[a] += u[b] k[a-b] */
+    case 1: return b >= a ? b - a : -1;              /* y[a] += u[b] k[b-a] */
+    case 2: return ((a - b) % N + N) % N;            /* k[(a-b) mod N]      */
+    default: return ((b - a) % N + N) % N;           /* k[(b-a) mod N]      */
+    }
+}
+
+/* Operator `kind` by its definition; u, y [R][N], kern [Hk][N]. */
+void oracle_op_direct(const double *u, const double *kern, const long *hidx,
+                      double *y, long R, long N, int kind)
+{
+    long r;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (r = 0; r < R; ++r) {
+        const double *ur = u + r * N;
+        const double *kr = kern + hidx[r] * N;
+        for (long a = 0; a < N; ++a) {
+            double acc = 0.0;
+            for (long b = 0; b < N; ++b) {
+                long j = op_tap(kind, a, b, N);
+                if (j >= 0)
+                    acc += ur[b] * kr[j];
+            }
+            y[r * N + a] = acc;
+        }
+    }
+}
+
+/* Single outputs out[i] = y[rows[i]][ts[i]] of operator `kind`. */
+void oracle_op_points(const double *u, const double *kern, const long *hidx,
+                      long N, const long *rows, const long *ts, long n,
+                      int kind, double *out)
+{
+    long i;
+#pragma omp parallel for schedule(dynamic, 16)
+    for (i = 0; i < n; ++i) {
+        const double *ur = u + rows[i] * N;
+        const double *kr = kern + hidx[rows[i]] * N;
+        double acc = 0.0;
+        for (long b = 0; b < N; ++b) {
+            long j = op_tap(kind, ts[i], b, N);
+            if (j >= 0)
+                acc += ur[b] * kr[j];
+        }
+        out[i] = acc;
+    }
+}
+
+/* Operator `kind` through the convolution theorem: transform length
+ * L = 2N (zero padded) for the causal kinds, N for the circular ones;
+ * Y = U . K (kinds 0, 2) or U . conj(K) (kinds 1, 3); y = IFFT(Y)[0:N]. */
+int oracle_op_fft(const double *u, const double *kern, const long *hidx,
+                  double *y, long R, long Hk, long N, int kind)
+{
+    const long L = kind < 2 ? 2 * N : N;
+    const double csign = (kind == 1 || kind == 3) ? -1.0 : 1.0;
+    double *kre = (double *)malloc(sizeof(double) * (size_t)(Hk * L));
+    double *kim = (double *)malloc(sizeof(double) * (size_t)(Hk * L));
+    if (!kre || !kim) {
+        free(kre);
+        free(kim);
+        return -1;
+    }
+    long h;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (h = 0; h < Hk; ++h) {
+        for (long t = 0; t < L; ++t) {
+            kre[h * L + t] = t < N ? kern[h * N + t] : 0.0;
+            kim[h * L + t] = 0.0;
+        }
+        fft_radix2(kre + h * L, kim + h * L, L, -1);
+    }
+    int fail = 0;
+#pragma omp parallel
+    {
+        double *re = (double *)malloc(sizeof(double) * (size_t)L);
+        double *im = (double *)malloc(sizeof(double) * (size_t)L);
+        if (!re || !im) {
+#pragma omp atomic write
+            fail = 1;
+        } else {
+            long r;
+#pragma omp for schedule(dynamic, 1)
+            for (r = 0; r < R; ++r) {
+                const double *Kr = kre + hidx[r] * L, *Ki = kim + hidx[r] * L;
+                for (long t = 0; t < L; ++t) {
+                    re[t] = t < N ? u[r * N + t] : 0.0;
+                    im[t] = 0.0;
+                }
+                fft_radix2(re, im, L, -1);
+                for (long f = 0; f < L; ++f) {
+                    double a = re[f], b = im[f], c = Kr[f], d = csign * Ki[f];
+                    re[f] = a * c - b * d;
+                    im[f] = a * d + b * c;
+                }
+                fft_radix2(re, im, L, +1);
+                for (long t = 0; t < N; ++t)
+                    y[r * N + t] = re[t] / (double)L;
+            }
+        }
+        free(re);
+        free(im);
+    }
+    free(kre);
+    free(kim);
+    return fail ? -1 : 0;
+}
+
+/* Kernel gradient by its definition: dk [Hk][N] (overwritten). Causal
+ * kinds (0, 1 -- the gradient of kind 0): dk[h][j] = sum_r sum_{t>=j}
+ * dy[r][t] u[r][t-j]; circular kinds (2, 3): t-j taken mod N. */
+void oracle_kgrad_direct(const double *u, const double *dy, const long *hidx,
+                         double *dk, long R, long Hk, long N, int kind)
+{
+    long h;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (h = 0; h < Hk; ++h) {
+        for (long j = 0; j < N; ++j)
+            dk[h * N + j] = 0.0;
+        for (long r = 0; r < R; ++r) {
+            if (hidx[r] != h)
+                continue;
+            const double *ur = u + r * N, *dr = dy + r * N;
+            for (long j = 0; j < N; ++j) {
+                double acc = 0.0;
+                for (long t = 0; t < N; ++t) {
+                    long s = t - j;
+                    if (kind >= 2)
+                        s = (s % N + N) % N;
+                    else if (s < 0)
+                        continue;
+                    acc += dr[t] * ur[s];
+                }
+                dk[h * N + j] += acc;
+            }
+        }
+    }
+}
+
+/* Kernel gradient through the convolution theorem: per row
+ * G = conj(FFT(u)) . FFT(dy) (length 2N zero padded for the causal kinds,
+ * N for the circular ones), summed over the rows of each channel, then
+ * dk = IFFT(G)[0:N]. */
+int oracle_kgrad_fft(const double *u, const double *dy, const long *hidx,
+                     double *dk, long R, long Hk, long N, int kind)
+{
+    const long L = kind < 2 ? 2 * N : N;
+    int fail = 0;
+    long h;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (h = 0; h < Hk; ++h) {
+        double *gre = (double *)calloc((size_t)L, sizeof(double));
+        double *gim = (double *)calloc((size_t)L, sizeof(double));
+        double *are = (double *)malloc(sizeof(double) * (size_t)L);
+        double *aim = (double *)malloc(sizeof(double) * (size_t)L);
+        double *bre = (double *)malloc(sizeof(double) * (size_t)L);
+        double *bim = (double *)malloc(sizeof(double) * (size_t)L);
+        if (!gre || !gim || !are || !aim || !bre || !bim) {
+#pragma omp atomic write
+            fail = 1;
+        } else {
+            for (long r = 0; r < R; ++r) {
+                if (hidx[r] != h)
+                    continue;
+                for (long t = 0; t < L; ++t) {
+                    are[t] = t < N ? u[r * N + t] : 0.0;
+                    bre[t] = t < N ? dy[r * N + t] : 0.0;
+                    aim[t] = bim[t] = 0.0;
+                }
+                fft_radix2(are, aim, L, -1);
+                fft_radix2(bre, bim, L, -1);
+                for (long f = 0; f < L; ++f) {
+                    /* conj(A) . B */
+                    gre[f] += are[f] * bre[f] + aim[f] * bim[f];
+                    gim[f] += are[f] * bim[f] - aim[f] * bre[f];
+                }
+            }
+            fft_radix2(gre, gim, L, +1);
+            for (long j = 0; j < N; ++j)
+                dk[h * N + j] = gre[j] / (double)L;
+        }
+        free(gre);
+        free(gim);
+        free(are);
+        free(aim);
+        free(bre);
+        free(bim);
+    }
+    return fail ? -1 : 0;
+}
+
+/* Single kernel-gradient entries out[i] = dk[hs[i]][js[i]] by the
+ * definition. */
+void oracle_kgrad_points(const double *u, const double *dy, const long *hidx,
+                         long R, long N, const long *hs, const long *js,
+                         long n, int kind, double *out)
+{
+    long i;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (i = 0; i < n; ++i) {
+        double acc = 0.0;
+        for (long r = 0; r < R; ++r) {
+            if (hidx[r] != hs[i])
+                continue;
+            const double *ur = u + r * N, *dr = dy + r * N;
+            for (long t = 0; t < N; ++t) {
+                long s = t - js[i];
+                if (kind >= 2)
+                    s = (s % N + N) % N;
+                else if (s < 0)
+                    continue;
+                acc += dr[t] * ur[s];
+            }
+        }
+        out[i] = acc;
+    }
 }

@@ -370,3 +370,148 @@ def test_gated_points_match_full():
     ts = np.array([0, 31, 7, 16, 1])
     np.testing.assert_allclose(oracle.gated_points(u, w, v, k, rows, ts),
                                full[rows, ts], rtol=0, atol=1e-12)
+
+
+# ------------------------------------------- circular, adjoints, gradients
+
+def test_golden_hand_worked_operators():
+    (case,) = _read_cases("ops_hand.txt")
+    f = lambda key: np.array([float(x) for x in case[key]])[None, :]
+    u, k, dy = f("u"), f("k"), f("dy")
+    for kind in ("circular", "causal_adjoint", "circular_adjoint"):
+        np.testing.assert_array_equal(oracle.op_direct(u, k, kind), f(kind))
+        np.testing.assert_allclose(oracle.op_fft(u, k, kind), f(kind),
+                                   atol=1e-14)
+    np.testing.assert_array_equal(oracle.kgrad_direct(u, dy, 1, "causal"),
+                                  f("kgrad_causal"))
+    np.testing.assert_array_equal(oracle.kgrad_direct(u, dy, 1, "circular"),
+                                  f("kgrad_circular"))
+    np.testing.assert_allclose(oracle.kgrad_fft(u, dy, 1, "causal"),
+                               f("kgrad_causal"), atol=1e-14)
+    np.testing.assert_allclose(oracle.kgrad_fft(u, dy, 1, "circular"),
+                               f("kgrad_circular"), atol=1e-14)
+
+
+def _brute_op(u, k, kind):
+    # the definitions with the sum index running over the kernel taps
+    n = len(u)
+    y = [0.0] * n
+    for a in range(n):
+        for j in range(n):
+            if kind == "circular":
+                y[a] += k[j] * u[(a - j) % n]
+            elif kind == "circular_adjoint":
+                y[a] += k[j] * u[(a + j) % n]
+            elif kind == "causal_adjoint":
+                if a + j < n:
+                    y[a] += k[j] * u[a + j]
+            else:
+                if a - j >= 0:
+                    y[a] += k[j] * u[a - j]
+    return y
+
+
+@pytest.mark.parametrize("kind", list(oracle.KINDS))
+@pytest.mark.parametrize("n", [1, 2, 4, 8])
+def test_operators_brute_force_and_fft(kind, n):
+    rng = np.random.default_rng(300 + n)
+    u = rng.standard_normal((3, n))
+    k = rng.standard_normal((2, n))
+    hidx = np.array([1, 0, 1])
+    yd = oracle.op_direct(u, k, kind, hidx)
+    for r in range(3):
+        np.testing.assert_allclose(yd[r], _brute_op(u[r], k[hidx[r]], kind),
+                                   atol=1e-13)
+    np.testing.assert_allclose(oracle.op_fft(u, k, kind, hidx), yd,
+                               atol=1e-12)
+    rows = np.array([0, 2, 1, 2])
+    ts = np.array([0, n - 1, n // 2, 0])
+    np.testing.assert_allclose(oracle.op_points(u, k, kind, rows, ts, hidx),
+                               yd[rows, ts], atol=1e-13)
+
+
+def test_adjoint_identities():
+    # <A u, y> = <u, A^T y> for the causal and the circular operator
+    rng = np.random.default_rng(17)
+    N = 64
+    u, y = rng.standard_normal((2, 5, N))
+    k = rng.standard_normal((5, N))
+    for kind in ("causal", "circular"):
+        lhs = np.sum(oracle.op_fft(u, k, kind) * y)
+        rhs = np.sum(u * oracle.op_fft(y, k, kind + "_adjoint"))
+        assert abs(lhs - rhs) < 1e-10 * (abs(lhs) + 1)
+
+
+def test_circular_special_cases():
+    rng = np.random.default_rng(23)
+    N = 32
+    u = rng.standard_normal((2, N))
+    # a delta kernel at m is a circular shift by m
+    for m in (0, 1, 7, N - 1):
+        d = np.zeros((1, N))
+        d[0, m] = 1.0
+        np.testing.assert_allclose(oracle.op_fft(u, d, "circular", [0, 0]),
+                                   np.roll(u, m, axis=1), atol=1e-13)
+    # with u and k both confined to the first half there is no wrap-around:
+    # the circular result is the causal one
+    uh = u.copy()
+    uh[:, N // 2:] = 0.0
+    kh = rng.standard_normal((1, N))
+    kh[:, N // 2:] = 0.0
+    np.testing.assert_allclose(oracle.op_direct(uh, kh, "circular", [0, 0]),
+                               oracle.conv_direct(uh, kh, [0, 0]), atol=1e-13)
+    # a constant kernel sums the whole row into every output
+    c = np.full((1, N), 0.5)
+    y = oracle.op_direct(u, c, "circular", [0, 0])
+    np.testing.assert_allclose(y, 0.5 * u.sum(axis=1, keepdims=True) *
+                               np.ones((1, N)), atol=1e-12)
+
+
+def test_circular_against_numpy_fft():
+    rng = np.random.default_rng(29)
+    N = 128
+    u = rng.standard_normal((3, N))
+    k = rng.standard_normal((3, N))
+    want = np.fft.irfft(np.fft.rfft(u) * np.fft.rfft(k), n=N)
+    np.testing.assert_allclose(oracle.op_fft(u, k, "circular"), want,
+                               atol=1e-12)
+    want = np.fft.irfft(np.fft.rfft(u) * np.conj(np.fft.rfft(k)), n=N)
+    np.testing.assert_allclose(oracle.op_fft(u, k, "circular_adjoint"), want,
+                               atol=1e-12)
+
+
+def test_kernel_gradient_is_the_derivative():
+    # L(k) = <dy, A_k u> is linear in k, so dL/dk[j] = L(e_j) exactly;
+    # L(e_j) goes through the operator's definition, not the gradient code
+    rng = np.random.default_rng(31)
+    N, B, H = 16, 3, 2
+    u = rng.standard_normal((B * H, N))
+    dy = rng.standard_normal((B * H, N))
+    for kind in ("causal", "circular"):
+        dk = oracle.kgrad_direct(u, dy, H, kind)
+        for h in range(H):
+            for j in range(N):
+                e = np.zeros((H, N))
+                e[h, j] = 1.0
+                want = np.sum(dy * oracle.op_direct(u, e, kind))
+                assert abs(dk[h, j] - want) < 1e-12
+        np.testing.assert_allclose(oracle.kgrad_fft(u, dy, H, kind), dk,
+                                   atol=1e-12)
+        hs = np.array([0, 1, 1, 0])
+        js = np.array([0, N - 1, 3, 9])
+        np.testing.assert_allclose(oracle.kgrad_points(u, dy, H, hs, js, kind),
+                                   dk[hs, js], atol=1e-12)
+
+
+def test_kernel_gradient_against_numpy_fft():
+    rng = np.random.default_rng(37)
+    N, B, H = 64, 4, 3
+    u = rng.standard_normal((B * H, N))
+    dy = rng.standard_normal((B * H, N))
+    hidx = np.arange(B * H) % H
+    for kind, L in (("causal", 2 * N), ("circular", N)):
+        g = np.conj(np.fft.fft(u, n=L)) * np.fft.fft(dy, n=L)
+        want = np.stack([np.fft.ifft(g[hidx == h].sum(axis=0)).real[:N]
+                         for h in range(H)])
+        np.testing.assert_allclose(oracle.kgrad_fft(u, dy, H, kind), want,
+                                   atol=1e-11)
