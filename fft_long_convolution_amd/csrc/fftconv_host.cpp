@@ -1042,7 +1042,14 @@ size_t fftconv_workspace_bytes(fftconv_plan_t plan, size_t B, size_t H) {
 
 fftconv_status fftconv_kernel_spectrum(fftconv_plan_t plan, const float* k,
                                        size_t H, void* k_f, void* stream) {
+    return fftconv_kernel_spectrum_kind(plan, k, H, FFTCONV_CAUSAL, k_f, stream);
+}
+
+fftconv_status fftconv_kernel_spectrum_kind(fftconv_plan_t plan, const float* k,
+                                            size_t H, fftconv_kernel_kind kind,
+                                            void* k_f, void* stream) {
     if (!plan) return FFTCONV_ERR_INVALID_ARG;
+    if ((int)kind < 0 || (int)kind > 3) return FFTCONV_ERR_INVALID_ARG;
     if (H == 0) return FFTCONV_OK;
     if (!k || !k_f) return FFTCONV_ERR_INVALID_ARG;
     if (!aligned16(k) || !aligned16(k_f)) return FFTCONV_ERR_ALIGNMENT;
@@ -1068,7 +1075,7 @@ fftconv_status fftconv_kernel_spectrum(fftconv_plan_t plan, const float* k,
     const int io = (int)s.dtype;
     for (size_t h0 = 0; h0 < H && e == hipSuccess; h0 += hc) {
         const int cnt = (int)((H - h0) < hc ? (H - h0) : hc);
-        e = launch_kpad(k + h0 * s.N, X0, cnt, (int)s.N, st);
+        e = launch_kpad(k + h0 * s.N, X0, cnt, (int)s.N, (int)kind, st);
         float2 *a = X0, *b = X1;
         for (long long Ns = 1; Ns < L && e == hipSuccess; Ns *= 2) {
             e = launch_stockham(a, b, cnt, (int)L, (int)Ns, st);

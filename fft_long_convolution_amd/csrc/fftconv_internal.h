@@ -242,7 +242,7 @@ hipError_t launch_inner(int io, const FwdParams& p, int lds_bytes,
                         hipStream_t s);
 hipError_t launch_outer_inv(int io, const FwdParams& p, int lds_bytes,
                             hipStream_t s);
-hipError_t launch_kpad(const float* k, float2* X, int hcount, int N,
+hipError_t launch_kpad(const float* k, float2* X, int hcount, int N, int kind,
                        hipStream_t s);
 hipError_t launch_stockham(const float2* in, float2* out, int hcount, int L,
                            int Ns, hipStream_t s);

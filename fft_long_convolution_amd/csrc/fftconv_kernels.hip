@@ -646,14 +646,35 @@ __global__ void __launch_bounds__(512) outer_inv_kernel(FwdParams P) {
 // Kernel spectrum (untimed, once per channel): an accurate fp32 radix-2
 // Stockham FFT of the zero-padded kernel, then alpha/beta per packed bin.
 // ---------------------------------------------------------------------------
+// The 2N-periodic kernel c whose circular convolution with the zero-padded
+// input gives the operator of `kind` on outputs t < N:
+//   0 causal            c[t] = k[t] (t < N), 0 above
+//   1 causal adjoint    c[0] = k[0], c[2N - j] = k[j] (0 < j < N), 0 else
+//                       (y[s] = sum_{t>=s} u[t] k[t-s])
+//   2 circular          c[t] = k[t mod N]  (y[t] = sum_s u[s] k[(t-s) mod N])
+//   3 circular adjoint  c[t] = k[(-t) mod N]
 __global__ void kpad_kernel(const float* __restrict__ k, float2* __restrict__ X,
-                            int hcount, int N) {
+                            int hcount, int N, int kind) {
     const long long L = 2LL * N;
     const long long total = hcount * L;
     for (long long i = blockIdx.x * (long long)blockDim.x + threadIdx.x; i < total;
          i += (long long)gridDim.x * blockDim.x) {
-        const long long h = i / L, t = i - h * L;
-        X[i] = make_float2(t < N ? k[h * N + t] : 0.f, 0.f);
+        const long long h = i / L;
+        const int t = (int)(i - h * L);
+        const float* kr = k + h * N;
+        float v = 0.f;
+        if (kind == 0) {
+            if (t < N) v = kr[t];
+        } else if (kind == 1) {
+            if (t == 0) v = kr[0];
+            else if (t > N) v = kr[2 * N - t];
+        } else if (kind == 2) {
+            v = kr[t & (N - 1)];
+        } else {
+            const int m = t & (N - 1);
+            v = kr[m == 0 ? 0 : N - m];
+        }
+        X[i] = make_float2(v, 0.f);
     }
 }
 
@@ -772,8 +793,9 @@ hipError_t launch_outer_inv(int io, const FwdParams& p, int lds, hipStream_t s) 
     FFTCONV_LAUNCH(outer_inv_kernel, dim3((unsigned)p.rows, slab / p.ct));
 }
 
-hipError_t launch_kpad(const float* k, float2* X, int hcount, int N, hipStream_t s) {
-    hipLaunchKernelGGL(kpad_kernel, dim3(1024), dim3(256), 0, s, k, X, hcount, N);
+hipError_t launch_kpad(const float* k, float2* X, int hcount, int N, int kind,
+                       hipStream_t s) {
+    hipLaunchKernelGGL(kpad_kernel, dim3(1024), dim3(256), 0, s, k, X, hcount, N, kind);
     return hipGetLastError();
 }
 

@@ -58,6 +58,11 @@ class PlanInfo(ctypes.Structure):
                            }[self.kernel_variant]}
 
 
+# fftconv_kernel_kind values of the C header
+KERNEL_KINDS = {"causal": 0, "causal_adjoint": 1, "circular": 2,
+                "circular_adjoint": 3}
+
+
 def lib() -> ctypes.CDLL:
     """Open libfftconv.so (built in-tree by fft_long_convolution_amd.build)."""
     global _lib
@@ -82,6 +87,8 @@ def lib() -> ctypes.CDLL:
         L.fftconv_workspace_bytes.restype = sz
         L.fftconv_kernel_spectrum.argtypes = [vp, vp, sz, vp, vp]
         L.fftconv_kernel_spectrum.restype = i
+        L.fftconv_kernel_spectrum_kind.argtypes = [vp, vp, sz, i, vp, vp]
+        L.fftconv_kernel_spectrum_kind.restype = i
         L.fftconv_forward.argtypes = [vp, vp, vp, vp, sz, sz, sz, vp, sz, vp]
         L.fftconv_forward.restype = i
         L.fftconv_forward_gated.argtypes = [vp, vp, vp, vp, vp, vp, sz, sz,
@@ -159,8 +166,10 @@ class FFTConv:
     def workspace_bytes(self, B: int, H: int) -> int:
         return int(lib().fftconv_workspace_bytes(self._plan, B, H))
 
-    def kernel_spectrum(self, k, out=None, stream=None):
-        """k: [H, N] fp32 CUDA tensor -> opaque k_f (uint8 CUDA tensor)."""
+    def kernel_spectrum(self, k, out=None, stream=None, kind="causal"):
+        """k: [H, N] fp32 CUDA tensor -> opaque k_f (uint8 CUDA tensor).
+        kind: "causal", "causal_adjoint", "circular" or "circular_adjoint"
+        (the operator fftconv_forward then computes)."""
         import torch
         if k.dtype != torch.float32 or k.dim() != 2 or k.shape[1] != self.N:
             raise ValueError("k must be fp32 [H, %d]" % self.N)
@@ -171,11 +180,14 @@ class FFTConv:
             out = torch.empty(nb, dtype=torch.uint8, device=k.device)
         elif out.numel() * out.element_size() < nb:
             raise ValueError("k_f buffer too small")
-        st = lib().fftconv_kernel_spectrum(self._plan, k.data_ptr(), H,
-                                           out.data_ptr(),
-                                           _stream_handle(stream))
+        if kind not in KERNEL_KINDS:
+            raise ValueError("unknown kernel kind %r" % (kind,))
+        st = lib().fftconv_kernel_spectrum_kind(self._plan, k.data_ptr(), H,
+                                                KERNEL_KINDS[kind],
+                                                out.data_ptr(),
+                                                _stream_handle(stream))
         if st != 0:
-            raise FFTConvError(st, "fftconv_kernel_spectrum")
+            raise FFTConvError(st, "fftconv_kernel_spectrum_kind")
         return out
 
     def _prepare(self, u, out, workspace):

@@ -135,6 +135,35 @@ size_t fftconv_workspace_bytes(fftconv_plan_t plan, size_t B, size_t H);
 fftconv_status fftconv_kernel_spectrum(fftconv_plan_t plan, const float *k,
                                        size_t H, void *k_f, void *stream);
 
+/* Which operator a spectrum makes fftconv_forward (and the gated call)
+ * compute, for kernel taps k[h, 0:N] (page "FlashFFTConv: Efficient
+ * Convolutions for Long Sequences with Tensor Cores": the convolution
+ * definition and theorem of section 3.3; the non-causal convolutions of its
+ * benchmark tables use an FFT of size N, i.e. a circular convolution; the
+ * gradients multiply by the conjugate spectrum):
+ *   FFTCONV_CAUSAL            y[t] = sum_{s<=t} u[s] k[t-s]
+ *   FFTCONV_CAUSAL_ADJOINT    y[s] = sum_{t>=s} u[t] k[t-s]
+ *                             (the transpose: du from dy)
+ *   FFTCONV_CIRCULAR          y[t] = sum_s u[s] k[(t-s) mod N]
+ *   FFTCONV_CIRCULAR_ADJOINT  y[s] = sum_t u[t] k[(t-s) mod N]
+ * Every kind runs the same kernels at the same cost: each is the first N
+ * outputs of a 2N-point circular convolution of the zero-padded input with
+ * a 2N-periodic kernel built from k (k followed by zeros; k[0] and the
+ * reversed taps; k twice; k reversed twice). */
+typedef enum fftconv_kernel_kind {
+    FFTCONV_CAUSAL = 0,
+    FFTCONV_CAUSAL_ADJOINT = 1,
+    FFTCONV_CIRCULAR = 2,
+    FFTCONV_CIRCULAR_ADJOINT = 3
+} fftconv_kernel_kind;
+
+/* fftconv_kernel_spectrum for the operator `kind` (FFTCONV_CAUSAL gives
+ * exactly fftconv_kernel_spectrum).  Arguments, layout and errors as
+ * there; an unknown kind -> FFTCONV_ERR_INVALID_ARG. */
+fftconv_status fftconv_kernel_spectrum_kind(fftconv_plan_t plan, const float *k,
+                                            size_t H, fftconv_kernel_kind kind,
+                                            void *k_f, void *stream);
+
 /* Causal long convolution y = (u * k)[0:N] for all B x H rows.
  *  u: device, plan dtype, [B][H][N] contiguous, 16-B aligned.
  *  k_f: device, from fftconv_kernel_spectrum with the same plan and H.

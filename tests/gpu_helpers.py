@@ -93,3 +93,31 @@ def parity_gated(w: inputs.Workload, p: int = 0):
     y, ins, k = run_gpu_gated(w, p=p)
     ref = oracle_gated_rows(w, ins, k)
     return oracle.rel_l2(y, ref), y, ref
+
+
+def run_gpu_op(w: inputs.Workload, kind: str, conv=None):
+    """GPU result of operator ``kind`` (a spectrum of that kind fed to the
+    plain forward call) for all rows, as fp64."""
+    import torch
+    from fft_long_convolution_amd.fftconv import FFTConv
+    if conv is None:
+        conv = FFTConv(w.N, dtype=w.dtype)
+    u = inputs.input_rows(w)
+    k = inputs.kernel_rows(w)
+    ud = to_torch(u, w.dtype).view(w.B, w.H, w.N)
+    kf = conv.kernel_spectrum(torch.from_numpy(k).cuda(), kind=kind)
+    y = conv.forward(ud, kf)
+    torch.cuda.synchronize()
+    y64 = oracle.to_f64(from_torch(y, w.dtype).reshape(w.rows, w.N), w.dtype)
+    return y64, u, k
+
+
+def parity_op(w: inputs.Workload, kind: str):
+    y, u, k = run_gpu_op(w, kind)
+    u64 = oracle.to_f64(u, w.dtype).reshape(w.rows, w.N)
+    hidx = np.arange(w.rows) % w.H
+    if w.N <= 512:
+        ref = oracle.op_direct(u64, k.astype(np.float64), kind, hidx)
+    else:
+        ref = oracle.op_fft(u64, k.astype(np.float64), kind, hidx)
+    return oracle.rel_l2(y, ref), y, ref
