@@ -57,6 +57,7 @@ struct Shape {
     int wide_P = 0;      // > 0: fused P x 32 x 32 kernel (P/2 waves per row)
     int mp_P1 = 0;       // > 0: multi-pass with outer levels P1 [x mp_P2] and
     int mp_P2 = 1;       //      4096-point inner slabs (4 x 32 x 32)
+    bool grad = false;   // the kernel-gradient plan: LDS-staged kernels only
     fftconv_dtype dtype = FFTCONV_F32;
 };
 
@@ -101,7 +102,11 @@ bool search_factors(int lg, int p, std::vector<int>& out) {
 
 bool generic_forced();
 
-fftconv_status make_shape(size_t N, int p, fftconv_dtype dtype, Shape& s) {
+// grad: the shape of the kernel-gradient passes, which hold two lines (u
+// and dy) per workgroup: LDS-staged kernels only, fused up to M = 8192 and
+// multi-pass slabs of at most 4096 points above.
+fftconv_status make_shape(size_t N, int p, fftconv_dtype dtype, Shape& s,
+                          bool grad = false) {
     if (dtype != FFTCONV_F32 && dtype != FFTCONV_F16 && dtype != FFTCONV_BF16)
         return FFTCONV_ERR_UNSUPPORTED;
     if (!is_pow2(N) || N < kMinN || N > kMaxN) return FFTCONV_ERR_UNSUPPORTED;
@@ -112,13 +117,14 @@ fftconv_status make_shape(size_t N, int p, fftconv_dtype dtype, Shape& s) {
     s.dtype = dtype;
     const int lg = ilog2(N);
     std::vector<int> fac;
-    if (s.M <= (size_t)kFusedMaxM) {
+    s.grad = grad;
+    if (s.M <= (size_t)(grad ? 8192 : kFusedMaxM)) {
         s.path = 0;
         if (!default_fused(lg, fac)) return FFTCONV_ERR_UNSUPPORTED;
         // 16-bit I/O at N = 4K..16K: order 3 as P x 32 x 32 on the
         // one-workgroup-per-row kernel
         if (dtype != FFTCONV_F32 && lg >= 12 && lg <= 14 && (p == 0 || p == 3) &&
-            !generic_forced()) {
+            !generic_forced() && !grad) {
             s.wide_P = 1 << (lg - 10);
             fac = {s.wide_P, 32, 32};
         }
@@ -131,7 +137,7 @@ fftconv_status make_shape(size_t N, int p, fftconv_dtype dtype, Shape& s) {
         const int waves = s.M <= 1024 ? 1 : (s.M <= 4096 ? 4 : 8);
         s.thr_fused = 64 * waves;
         s.lds_fused = (int)(s.M * 8 + waves * 32 * 8);
-    } else if (dtype != FFTCONV_F32 && !generic_forced()) {
+    } else if (dtype != FFTCONV_F32 && !generic_forced() && !grad) {
         s.path = 1;
         const int Po = (int)(s.M / 4096);
         switch (Po) {
@@ -151,7 +157,10 @@ fftconv_status make_shape(size_t N, int p, fftconv_dtype dtype, Shape& s) {
     } else {
         s.path = 1;
         std::vector<int> outer, inner;
-        if (lg <= 18) {
+        if (grad && lg <= 14) {
+            s.Min = 2048;
+            inner = {8, 16, 16};
+        } else if (lg <= 18 || grad) {
             s.Min = 4096;
             inner = {16, 16, 16};
         } else {
@@ -210,7 +219,7 @@ bool generic_forced() {
 // I/O; FFTCONV_KERNEL=generic keeps such plans on the LDS-staged kernel.
 bool row_kernel_applies(const Shape& s) {
     return s.path == 0 && s.p == 2 && s.f[0] == 32 && (s.f[1] == 16 || s.f[1] == 32) &&
-           s.dtype != FFTCONV_F32 && !generic_forced();
+           s.dtype != FFTCONV_F32 && !generic_forced() && !s.grad;
 }
 
 void fill_info(const Shape& s, fftconv_plan_info* info) {
@@ -673,6 +682,7 @@ struct fftconv_plan_s {
     const float2* mp2m_tm = nullptr;  //   twiddle tables
     const float2* mp_tw1 = nullptr;   // W_M^c, c < M / P1
     const float2* mp_tw2 = nullptr;   // W_{M/P1}^c, c < 4096 (two levels)
+    fftconv_plan_s* grad = nullptr;   // LDS-staged plan of the kernel gradient
 };
 
 namespace {
@@ -689,6 +699,7 @@ hipError_t upload(fftconv_plan_s* pl, const void* host, size_t bytes, void** dev
 
 void free_plan(fftconv_plan_s* pl) {
     if (!pl) return;
+    free_plan(pl->grad);
     for (void* p : pl->allocs) (void)hipFree(p);
     delete pl;
 }
@@ -945,6 +956,46 @@ fftconv_status build_mp_tables(fftconv_plan_s* pl) {
     return FFTCONV_OK;
 }
 
+// The kernel-gradient plan of a plan: the same N and dtype on the
+// LDS-staged kernels (two lines per workgroup), whose accumulators must fit
+// the kernels' fixed number of lane-slot steps per wave (two for a 16-point
+// innermost stage, one for a 32-point one).
+
+fftconv_status build_grad_plan(fftconv_plan_s* pl) {
+    Shape g;
+    fftconv_status st = make_shape(pl->s.N, 0, pl->s.dtype, g, true);
+    if (st != FFTCONV_OK) return st;
+    const int nm = g.f[g.p - 1];
+    const int slab = g.path ? g.Min : (int)g.M;
+    const int Q = slab / nm;
+    const int LS = g.path ? Q : Q / 2;
+    const int waves = (g.path ? g.thr_inner : g.thr_fused) / 64;
+    if ((LS + 15) / 16 > (nm == 32 ? 1 : 2) * waves) return FFTCONV_ERR_UNSUPPORTED;
+    fftconv_plan_s* gp = new (std::nothrow) fftconv_plan_s();
+    if (!gp) return FFTCONV_ERR_HIP;
+    gp->s = g;
+    gp->device = pl->device;
+    st = build_device_tables(gp);
+    if (st != FFTCONV_OK) {
+        free_plan(gp);
+        return st;
+    }
+    pl->grad = gp;
+    return FFTCONV_OK;
+}
+
+size_t kgrad_workspace_bytes(const fftconv_plan_s* pl, size_t B, size_t H) {
+    const Shape& g = pl->grad->s;
+    if (g.path == 0) return 0;
+    // outer-transformed rows of u and dy, and one result row per channel
+    return (2 * B * H + H) * g.M * 8;
+}
+
+int kgrad_lds(const Shape& g) {
+    return g.path ? 4 * g.Min * 8 + (g.thr_inner / 64) * 64 * 8
+                  : (int)g.M * 2 * 8 + (g.thr_fused / 64) * 64 * 8;
+}
+
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
 // Channels per chunk of the multi-pass path: the passes run chunk by chunk
@@ -1008,6 +1059,7 @@ fftconv_status fftconv_plan(size_t N, int p, fftconv_dtype dtype,
         return FFTCONV_ERR_HIP;
     }
     st = build_device_tables(pl);
+    if (st == FFTCONV_OK) st = build_grad_plan(pl);
     if (st != FFTCONV_OK) {
         free_plan(pl);
         return st;
@@ -1028,6 +1080,13 @@ void fftconv_plan_destroy(fftconv_plan_t plan) { free_plan(plan); }
 size_t fftconv_spectrum_bytes(fftconv_plan_t plan, size_t H) {
     if (!plan) return 0;
     return H * plan->s.M * kf_entry_bytes(plan->s.dtype);
+}
+
+size_t fftconv_backward_workspace_bytes(fftconv_plan_t plan, size_t B, size_t H) {
+    if (!plan || !plan->grad) return 0;
+    const size_t a = fftconv_workspace_bytes(plan, B, H);
+    const size_t b = kgrad_workspace_bytes(plan, B, H);
+    return a > b ? a : b;
 }
 
 size_t fftconv_workspace_bytes(fftconv_plan_t plan, size_t B, size_t H) {
@@ -1340,6 +1399,106 @@ fftconv_status fftconv_forward_gated(fftconv_plan_t plan, const void* u,
     if (B * H != 0 && (!w || !v)) return FFTCONV_ERR_INVALID_ARG;
     return forward_impl(plan, u, w, v, k_f, y, B, H, N, workspace,
                         workspace_bytes, stream);
+}
+
+fftconv_status fftconv_backward(fftconv_plan_t plan, const void* u,
+                                const void* dy, const void* k_f_adj, void* du,
+                                float* dk, size_t B, size_t H, size_t N,
+                                void* workspace, size_t workspace_bytes,
+                                void* stream) {
+    if (!plan || !plan->grad) return FFTCONV_ERR_INVALID_ARG;
+    const Shape& s = plan->s;
+    if (N != s.N) return FFTCONV_ERR_INVALID_ARG;
+    if (!du && !dk) return FFTCONV_ERR_INVALID_ARG;
+    const size_t rows = B * H;
+    if (B != 0 && rows / B != H) return FFTCONV_ERR_INVALID_ARG;
+    if (rows > 0x7fffffffULL || H > 0x7fffffffULL) return FFTCONV_ERR_UNSUPPORTED;
+    const size_t esz = s.dtype == FFTCONV_F32 ? 4 : 2;
+    const size_t io_bytes = rows * N * esz, dk_bytes = H * N * 4;
+    if (dk) {
+        if (!aligned16(dk)) return FFTCONV_ERR_ALIGNMENT;
+        if (rows && (!u || !dy)) return FFTCONV_ERR_INVALID_ARG;
+        if (rows && (!aligned16(u) || !aligned16(dy))) return FFTCONV_ERR_ALIGNMENT;
+        if (overlap(dk, dk_bytes, u, io_bytes) || overlap(dk, dk_bytes, dy, io_bytes))
+            return FFTCONV_ERR_INVALID_ARG;
+        if (du && overlap(dk, dk_bytes, du, io_bytes)) return FFTCONV_ERR_INVALID_ARG;
+        if (k_f_adj && overlap(dk, dk_bytes, k_f_adj, fftconv_spectrum_bytes(plan, H)))
+            return FFTCONV_ERR_INVALID_ARG;
+    }
+    if (du && rows && u && overlap(du, io_bytes, u, io_bytes)) return FFTCONV_ERR_INVALID_ARG;
+    const size_t ws_need = fftconv_backward_workspace_bytes(plan, B, H);
+    if (rows && ws_need) {
+        if (!workspace || workspace_bytes < ws_need) return FFTCONV_ERR_WORKSPACE;
+        if (!aligned16(workspace)) return FFTCONV_ERR_ALIGNMENT;
+        if ((u && overlap(workspace, ws_need, u, io_bytes)) ||
+            (dk && overlap(workspace, ws_need, dk, dk_bytes)))
+            return FFTCONV_ERR_INVALID_ARG;
+    }
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess) return FFTCONV_ERR_HIP;
+    if (dev != plan->device) return FFTCONV_ERR_INVALID_ARG;
+    hipStream_t st = (hipStream_t)stream;
+    // du = the adjoint operator applied to dy (the forward kernels with the
+    // conjugate spectrum); validated like any forward call
+    if (du) {
+        const fftconv_status fs = forward_impl(plan, dy, nullptr, nullptr, k_f_adj, du, B, H,
+                                               N, workspace, workspace_bytes, stream);
+        if (fs != FFTCONV_OK) return fs;
+    }
+    if (!dk || H == 0) return FFTCONV_OK;
+    const fftconv_plan_s* gp = plan->grad;
+    const Shape& g = gp->s;
+    const int io = (int)s.dtype;
+    hipError_t e;
+    if (rows == 0) {
+        // an empty batch contributes nothing: dk = 0
+        return launch_scale_f32(dk, (long long)(H * N), 0.f, st) == hipSuccess
+                   ? FFTCONV_OK : FFTCONV_ERR_HIP;
+    }
+    KgradParams K{};
+    K.B = (int)B;
+    K.H = (int)H;
+    K.scale = (float)g.M;
+    K.u = u;
+    K.dy = dy;
+    K.dk = dk;
+    const int lds = kgrad_lds(g);
+    if (g.path == 0) {
+        K.f = gp->fused;
+        e = launch_kgrad_fused(io, K, lds, st);
+    } else {
+        float2* wsu = (float2*)workspace;
+        float2* wsd = wsu + rows * g.M;
+        float2* wsg = wsd + rows * g.M;
+        FwdParams O = gp->outer;
+        O.rows = (long long)rows;
+        O.H = (int)H;
+        O.u = u;
+        O.ws = wsu;
+        e = launch_outer_fwd(io, O, g.lds_outer, st);
+        if (e == hipSuccess) {
+            O.u = dy;
+            O.ws = wsd;
+            e = launch_outer_fwd(io, O, g.lds_outer, st);
+        }
+        if (e == hipSuccess) {
+            K.f = gp->inner;
+            K.wsu = wsu;
+            K.wsd = wsd;
+            K.wsg = wsg;
+            e = launch_kgrad_inner(io, K, lds, st);
+        }
+        if (e == hipSuccess) {
+            FwdParams OI = gp->outer;
+            OI.rows = (long long)H;
+            OI.H = (int)H;
+            OI.ws = wsg;
+            OI.y = dk;
+            e = launch_outer_inv_f32out(io, OI, g.lds_outer, st);
+        }
+        if (e == hipSuccess) e = launch_scale_f32(dk, (long long)(H * N), (float)g.M, st);
+    }
+    return e == hipSuccess ? FFTCONV_OK : FFTCONV_ERR_HIP;
 }
 
 }  // extern "C"

@@ -90,6 +90,30 @@ struct FwdParams {
     const void* v;      // output gate (layout of y) or null
 };
 
+// Kernel gradient of the causal convolution (LDS-staged kernels of a plan
+// built for it): dk[h][j] = sum_b sum_{t>=j} dy[b,h,t] u[b,h,t-j].
+struct KgradParams {
+    FwdParams f;        // stages: the whole transform (fused) or the inner
+                        // slabs (multi-pass: f.digrev_o, f.Qo, f.nunits)
+    int B, H;
+    float scale;        // sqrt(M): the unitary transforms' lost factor
+    const void* u;      // [B][H][N], plan dtype (fused)
+    const void* dy;
+    float* dk;          // [H][N] fp32 (fused)
+    const float2* wsu;  // multi-pass: outer-transformed rows [B*H][M]
+    const float2* wsd;
+    float2* wsg;        // multi-pass: per-channel result rows [H][M]
+};
+hipError_t launch_kgrad_fused(int io, const KgradParams& p, int lds_bytes,
+                              hipStream_t s);
+hipError_t launch_kgrad_inner(int io, const KgradParams& p, int lds_bytes,
+                              hipStream_t s);
+// outer inverse pass writing fp32 (the kernel gradient) whatever the plan's
+// I/O type, and an in-place scale of n floats
+hipError_t launch_outer_inv_f32out(int io, const FwdParams& p, int lds_bytes,
+                                   hipStream_t s);
+hipError_t launch_scale_f32(float* x, long long n, float a, hipStream_t s);
+
 // Spectrum (alpha/beta) construction.
 struct SpecParams {
     int M, N, L;

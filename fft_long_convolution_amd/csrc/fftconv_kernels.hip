@@ -643,6 +643,349 @@ __global__ void __launch_bounds__(512) outer_inv_kernel(FwdParams P) {
 }
 
 // ---------------------------------------------------------------------------
+// Kernel gradient of the causal convolution,
+//   dk[h][j] = sum_b sum_{t>=j} dy[b,h,t] u[b,h,t-j],
+// whose 2N-point spectrum is G = sum_b conj(U_b) . DY_b (page "FlashFFTConv:
+// Efficient Convolutions for Long Sequences with Tensor Cores", section 3:
+// the backward pass of an FFT convolution multiplies by conjugate spectra,
+// and the input spectra are recomputed instead of stored).
+// In the packed form (z = u_even + i u_odd, Z its M-point DFT), bins k and
+// -k give E = (Z[k] + conj Z[-k]) / 2, O = (Z[k] - conj Z[-k]) / (2i) and
+// U[k] = E + w O, U[k + M] = E - w O with w = W_2N^k; the real result's
+// packed spectrum is Z_g[k] = (G[k] + G[k+M]) / 2 + i conj(w) (G[k] - G[k+M]) / 2.
+// Z_g is linear in G, so it is accumulated over the batch directly, in the
+// registers of the lane that owns the bin pair (the lane slots of the
+// innermost stage, which already hold bins k and -k together), and then
+// goes through the inverse stages like a product spectrum.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float2 kg_bin(float2 a, float2 ap, float2 d, float2 dp,
+                                         float2 w) {
+    const float2 c = make_float2(ap.x, -ap.y), f = make_float2(dp.x, -dp.y);
+    // E = (Z + conj Z-) / 2, O = -i (Z - conj Z-) / 2
+    const float2 eu = make_float2(0.5f * (a.x + c.x), 0.5f * (a.y + c.y));
+    const float2 ou = make_float2(0.5f * (a.y - c.y), -0.5f * (a.x - c.x));
+    const float2 ed = make_float2(0.5f * (d.x + f.x), 0.5f * (d.y + f.y));
+    const float2 od = make_float2(0.5f * (d.y - f.y), -0.5f * (d.x - f.x));
+    const float2 wu = cmul(w, ou), wd = cmul(w, od);
+    const float2 up = make_float2(eu.x + wu.x, eu.y + wu.y);
+    const float2 um = make_float2(eu.x - wu.x, eu.y - wu.y);
+    const float2 dpl = make_float2(ed.x + wd.x, ed.y + wd.y);
+    const float2 dmi = make_float2(ed.x - wd.x, ed.y - wd.y);
+    // G+ = conj(U+) DY+, G- = conj(U-) DY-
+    const float2 gp = cmulc(dpl, up), gm = cmulc(dmi, um);
+    const float2 eg = make_float2(0.5f * (gp.x + gm.x), 0.5f * (gp.y + gm.y));
+    const float2 og = cmulc(make_float2(0.5f * (gp.x - gm.x), 0.5f * (gp.y - gm.y)), w);
+    return make_float2(eg.x - og.y, eg.y + og.x);
+}
+
+// W_2N^bin = exp(-i pi bin / M)
+__device__ __forceinline__ float2 kg_w(int bin, int M) {
+    float sn, cs;
+    sincospif(-(float)bin / (float)M, &sn, &cs);
+    return make_float2(cs, sn);
+}
+
+// Lane-slot geometry of the innermost stage (as in run_middle).
+struct KgSlot {
+    int ls, qA, qB, offA, offB;
+    bool valid, special;
+};
+__device__ __forceinline__ KgSlot kg_slot(const MidDev& d, int utype, int st, int x) {
+    const int Q = d.Q;
+    const int LS = (utype == 2) ? Q : (Q >> 1);
+    KgSlot k;
+    const int ls_raw = (st << 4) + x;
+    k.valid = ls_raw < LS;
+    k.ls = k.valid ? ls_raw : LS - 1;
+    k.special = k.valid && utype == 0 && k.ls == 0;
+    k.qA = k.ls;
+    int sB = 0;
+    if (utype == 0) {
+        k.qB = (k.ls == 0) ? (Q >> 1) : (Q - k.ls);
+    } else {
+        k.qB = Q - 1 - k.ls;
+        if (utype == 2) sB = 1;
+    }
+    k.offA = d.digrev[k.qA] * d.n;
+    k.offB = sB * d.slab + d.digrev[k.qB] * d.n;
+    return k;
+}
+
+// Forward innermost stage of the u line and the dy line, and the
+// accumulation of Z_g for every bin of this wave's lane slots.  Bins:
+// k = ko + Qo (q + Q digit) (ko the outer part of the slab, Qo the number
+// of slabs; 0 and 1 on a fused row).
+template <class MF, int N, int SPW>
+__device__ __forceinline__ void kgrad_middle(const float2* __restrict__ lu,
+                                             const float2* __restrict__ ld,
+                                             const MidDev& d, int utype, int koA,
+                                             int koB, int Qo, int M, int wave,
+                                             int nwaves, int lane, float2* scru,
+                                             float2* scrd,
+                                             float2 (&accA)[SPW][N / 8][2],
+                                             float2 (&accB)[SPW][N / 8][2]) {
+    constexpr int MT = N / 8;
+    constexpr int KS = MF::ksteps(N);
+    const int g = lane >> 4, x = lane & 15;
+    typedef typename MF::AB AB;
+    const AB* mf = (const AB*)d.mat_f;
+    AB Af[MT][KS];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) Af[mt][ks] = mf[(mt * KS + ks) * 64 + lane];
+    const int Q = d.Q;
+    const int LS = (utype == 2) ? Q : (Q >> 1);
+    const int steps = (LS + 15) >> 4;
+#pragma unroll
+    for (int sp = 0; sp < SPW; ++sp) {
+        const int st = wave + sp * nwaves;
+        if (st >= steps) break;
+        const KgSlot ks_ = kg_slot(d, utype, st, x);
+        float2 z[4][MT][2];   // u of A, u of B, dy of A, dy of B
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            const float2* src = (v & 2) ? ld : lu;
+            const int off = (v & 1) ? ks_.offB : ks_.offA;
+            AB Bv[KS];
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks)
+                Bv[ks] = MF::gather(ks, g, N, [&](int nn) { return src[off + nn]; });
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) {
+                floatx4 c = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks) c = MF::mma(Af[mt][ks], Bv[ks], c);
+                z[v][mt][0] = make_float2(c[0], c[1]);
+                z[v][mt][1] = make_float2(c[2], c[3]);
+            }
+        }
+        if (ks_.special) {
+            // block q = 0 pairs digit k with -k (mod N), held by another
+            // lane group: exchange the u and dy values through LDS
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+                for (int e = 0; e < 2; ++e) {
+                    const int k = mid_perm(8 * mt + 2 * g + e, N);
+                    scru[k] = z[0][mt][e];
+                    scrd[k] = z[2][mt][e];
+                }
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        }
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+                const int k = mid_perm(8 * mt + 2 * g + e, N);
+                const int pm = (mt + MT / 2) % MT;
+                const float2 wA = kg_w(koA + Qo * (ks_.qA + Q * k), M);
+                const float2 wB = kg_w(koB + Qo * (ks_.qB + Q * k), M);
+                float2 cA, cB;
+                if (ks_.special) {
+                    const int km = (N - k) & (N - 1);
+                    cA = kg_bin(z[0][mt][e], scru[km], z[2][mt][e], scrd[km], wA);
+                    // block q = Q/2 is its own mirror block
+                    cB = kg_bin(z[1][mt][e], z[1][pm][e], z[3][mt][e], z[3][pm][e], wB);
+                } else {
+                    cA = kg_bin(z[0][mt][e], z[1][pm][e], z[2][mt][e], z[3][pm][e], wA);
+                    cB = kg_bin(z[1][mt][e], z[0][pm][e], z[3][mt][e], z[2][pm][e], wB);
+                }
+                accA[sp][mt][e].x += cA.x;
+                accA[sp][mt][e].y += cA.y;
+                accB[sp][mt][e].x += cB.x;
+                accB[sp][mt][e].y += cB.y;
+            }
+    }
+}
+
+// Inverse innermost stage of the accumulated spectrum (times `pre`), into
+// the line at the lane slots' positions.
+template <class MF, int N, int SPW>
+__device__ __forceinline__ void kgrad_final(float2* __restrict__ line, const MidDev& d,
+                                            int utype, int wave, int nwaves, int lane,
+                                            float pre, float2 (&accA)[SPW][N / 8][2],
+                                            float2 (&accB)[SPW][N / 8][2]) {
+    constexpr int MT = N / 8;
+    constexpr int KS = MF::ksteps(N);
+    const int g = lane >> 4, x = lane & 15;
+    typedef typename MF::AB AB;
+    const AB* mi = (const AB*)d.mat_i;
+    const int Q = d.Q;
+    const int LS = (utype == 2) ? Q : (Q >> 1);
+    const int steps = (LS + 15) >> 4;
+#pragma unroll
+    for (int sp = 0; sp < SPW; ++sp) {
+        const int st = wave + sp * nwaves;
+        if (st >= steps) break;
+        const KgSlot ks_ = kg_slot(d, utype, st, x);
+        float2 ra[MT][2], rb[MT][2];
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+                ra[mt][e] = make_float2(accA[sp][mt][e].x * pre, accA[sp][mt][e].y * pre);
+                rb[mt][e] = make_float2(accB[sp][mt][e].x * pre, accB[sp][mt][e].y * pre);
+            }
+        AB CA[KS], CB[KS];
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            CA[ks] = MF::template chain<MT>(ks, ra);
+            CB[ks] = MF::template chain<MT>(ks, rb);
+        }
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+            floatx4 oa = floatx4{0.f, 0.f, 0.f, 0.f};
+            floatx4 ob = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                const AB a = mi[(mt * KS + ks) * 64 + lane];
+                oa = MF::mma(a, CA[ks], oa);
+                ob = MF::mma(a, CB[ks], ob);
+            }
+            if (ks_.valid) {
+#pragma unroll
+                for (int e = 0; e < 2; ++e) {
+                    const int slot = 8 * mt + 2 * g + e;
+                    line[ks_.offA + slot] = make_float2(oa[2 * e], oa[2 * e + 1]);
+                    line[ks_.offB + slot] = make_float2(ob[2 * e], ob[2 * e + 1]);
+                }
+            }
+        }
+    }
+}
+
+// lane-slot steps per wave (checked by the host): two for 16-point
+// innermost stages, one for 32-point ones (registers)
+constexpr int kg_spw(int nm) { return nm == 32 ? 1 : 2; }
+
+// Fused: one workgroup per channel, looping over the batch; two lines
+// (u and dy) in LDS.  dk = `post` x the inverse of the accumulated spectrum.
+template <class MF, int IO, int NM>
+__global__ void __launch_bounds__(512) kgrad_fused_kernel(KgradParams P) {
+    extern __shared__ float2 smem[];
+    const FwdParams& F = P.f;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int nwaves = blockDim.x >> 6;
+    float2* la = smem;
+    float2* lb = smem + F.M;
+    float2* scr = smem + 2 * F.M + wave * 64;
+    const int h = blockIdx.x;
+    constexpr int SPW = kg_spw(NM);
+    float2 accA[SPW][NM / 8][2], accB[SPW][NM / 8][2];
+#pragma unroll
+    for (int sp = 0; sp < SPW; ++sp)
+#pragma unroll
+        for (int mt = 0; mt < NM / 8; ++mt)
+#pragma unroll
+            for (int e = 0; e < 2; ++e) accA[sp][mt][e] = accB[sp][mt][e] = make_float2(0.f, 0.f);
+    for (int b = 0; b < P.B; ++b) {
+        const long long row = (long long)b * P.H + h;
+        load_points<IO>(io_ptr<IO>(P.u, row * F.N), nullptr, la, F.N >> 1, threadIdx.x, blockDim.x);
+        load_points<IO>(io_ptr<IO>(P.dy, row * F.N), nullptr, lb, F.N >> 1, threadIdx.x, blockDim.x);
+        __syncthreads();
+        for (int i = 0; i < F.nst; ++i) {
+            dispatch_stage<MF, false>(i == 0 && F.outer_half, F.st[i], la, F.M, 0, wave, nwaves, lane);
+            dispatch_stage<MF, false>(i == 0 && F.outer_half, F.st[i], lb, F.M, 0, wave, nwaves, lane);
+            __syncthreads();
+        }
+        kgrad_middle<MF, NM, SPW>(la, lb, F.mid, 0, 0, 0, 1, F.M, wave, nwaves, lane, scr,
+                                     scr + 32, accA, accB);
+        __syncthreads();
+    }
+    const float pre = rsqrtf((float)F.M);
+    kgrad_final<MF, NM, SPW>(la, F.mid, 0, wave, nwaves, lane, pre, accA, accB);
+    __syncthreads();
+    for (int i = F.nst - 1; i >= 0; --i) {
+        dispatch_stage<MF, true>(i == 0 && F.outer_half, F.st[i], la, F.M, 0, wave, nwaves, lane);
+        __syncthreads();
+    }
+    const float post = P.scale;
+    float2* o = (float2*)(P.dk + (long long)h * F.N);
+    for (int j = threadIdx.x; j < (F.N >> 1); j += blockDim.x)
+        o[j] = make_float2(la[j].x * post, la[j].y * post);
+}
+
+// Multi-pass inner pass: one workgroup per (channel, unit of slabs), looping
+// over the batch; the outer-transformed rows of u and dy come from the
+// workspace, the result (inverse inner stages done) goes to the channel's
+// workspace row for the outer inverse pass.
+template <class MF, int IO, int NM>
+__global__ void __launch_bounds__(512) kgrad_inner_kernel(KgradParams P) {
+    extern __shared__ float2 smem[];
+    const FwdParams& F = P.f;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int nwaves = blockDim.x >> 6;
+    const int h = blockIdx.x, unit = blockIdx.y;
+    const int slab = F.M / F.Qo;
+    const int utype = unit == 0 ? 0 : (unit == 1 ? 1 : 2);
+    const int qoA = unit == 0 ? 0 : (unit == 1 ? (F.Qo >> 1) : unit - 1);
+    const int sigA = F.digrev_o[qoA];
+    const int sigB = utype == 2 ? F.digrev_o[F.Qo - qoA] : sigA;
+    const int nslab = utype == 2 ? 2 : 1;
+    const int koA = qoA, koB = utype == 2 ? F.Qo - qoA : qoA;
+    const int len = nslab * slab;
+    float2* la = smem;
+    float2* lb = smem + 2 * slab;
+    float2* scr = smem + 4 * slab + wave * 64;
+    constexpr int SPW = kg_spw(NM);
+    float2 accA[SPW][NM / 8][2], accB[SPW][NM / 8][2];
+#pragma unroll
+    for (int sp = 0; sp < SPW; ++sp)
+#pragma unroll
+        for (int mt = 0; mt < NM / 8; ++mt)
+#pragma unroll
+            for (int e = 0; e < 2; ++e) accA[sp][mt][e] = accB[sp][mt][e] = make_float2(0.f, 0.f);
+    for (int b = 0; b < P.B; ++b) {
+        const long long row = (long long)b * P.H + h;
+        for (int sl = 0; sl < nslab; ++sl) {
+            const long long off = row * (long long)F.M + (long long)(sl ? sigB : sigA) * slab;
+            const float4* su = (const float4*)(P.wsu + off);
+            const float4* sd = (const float4*)(P.wsd + off);
+            for (int j = threadIdx.x; j < (slab >> 1); j += blockDim.x) {
+                const float4 a = su[j], c = sd[j];
+                la[sl * slab + 2 * j] = make_float2(a.x, a.y);
+                la[sl * slab + 2 * j + 1] = make_float2(a.z, a.w);
+                lb[sl * slab + 2 * j] = make_float2(c.x, c.y);
+                lb[sl * slab + 2 * j + 1] = make_float2(c.z, c.w);
+            }
+        }
+        __syncthreads();
+        for (int i = 0; i < F.nst; ++i) {
+            dispatch_stage<MF, false>(false, F.st[i], la, len, 0, wave, nwaves, lane);
+            dispatch_stage<MF, false>(false, F.st[i], lb, len, 0, wave, nwaves, lane);
+            __syncthreads();
+        }
+        kgrad_middle<MF, NM, SPW>(la, lb, F.mid, utype, koA, koB, F.Qo, F.M, wave, nwaves,
+                                     lane, scr, scr + 32, accA, accB);
+        __syncthreads();
+    }
+    const float pre = rsqrtf((float)F.M);
+    kgrad_final<MF, NM, SPW>(la, F.mid, utype, wave, nwaves, lane, pre, accA, accB);
+    __syncthreads();
+    for (int i = F.nst - 1; i >= 0; --i) {
+        dispatch_stage<MF, true>(false, F.st[i], la, len, 0, wave, nwaves, lane);
+        __syncthreads();
+    }
+    for (int sl = 0; sl < nslab; ++sl) {
+        float4* dst = (float4*)(P.wsg + (long long)h * F.M + (long long)(sl ? sigB : sigA) * slab);
+        for (int j = threadIdx.x; j < (slab >> 1); j += blockDim.x) {
+            const float2 a = la[sl * slab + 2 * j], c = la[sl * slab + 2 * j + 1];
+            dst[j] = make_float4(a.x, a.y, c.x, c.y);
+        }
+    }
+}
+
+// x *= a; a = 0 writes zeros (whatever x held)
+__global__ void scale_f32_kernel(float* x, long long n, float a) {
+    for (long long i = blockIdx.x * (long long)blockDim.x + threadIdx.x; i < n;
+         i += (long long)gridDim.x * blockDim.x)
+        x[i] = a == 0.f ? 0.f : x[i] * a;
+}
+
+// ---------------------------------------------------------------------------
 // Kernel spectrum (untimed, once per channel): an accurate fp32 radix-2
 // Stockham FFT of the zero-padded kernel, then alpha/beta per packed bin.
 // ---------------------------------------------------------------------------
@@ -811,6 +1154,77 @@ hipError_t launch_alphabeta(int io, const SpecParams& p, hipStream_t s) {
         hipLaunchKernelGGL(alphabeta_kernel<IO_F32>, dim3(2048), dim3(256), 0, s, p);
     else
         hipLaunchKernelGGL(alphabeta_kernel<IO_F16>, dim3(2048), dim3(256), 0, s, p);
+    return hipGetLastError();
+}
+
+
+#define FFTCONV_KG_LAUNCH(KERNEL, GRID)                                                  \
+    do {                                                                                 \
+        const dim3 blk(p.f.threads), grid = (GRID);                                      \
+        hipError_t e_;                                                                   \
+        if (p.f.mid.n != 16 && p.f.mid.n != 32) return hipErrorInvalidValue;           \
+        switch (io * 2 + (p.f.mid.n == 32 ? 1 : 0)) {                                    \
+        case IO_F32 * 2:                                                                 \
+            e_ = set_lds(KERNEL<MfF32, IO_F32, 16>, lds);                                \
+            if (e_ != hipSuccess) return e_;                                             \
+            hipLaunchKernelGGL((KERNEL<MfF32, IO_F32, 16>), grid, blk, lds, s, p);       \
+            break;                                                                       \
+        case IO_F32 * 2 + 1:                                                             \
+            e_ = set_lds(KERNEL<MfF32, IO_F32, 32>, lds);                                \
+            if (e_ != hipSuccess) return e_;                                             \
+            hipLaunchKernelGGL((KERNEL<MfF32, IO_F32, 32>), grid, blk, lds, s, p);       \
+            break;                                                                       \
+        case IO_F16 * 2:                                                                 \
+            e_ = set_lds(KERNEL<MfF16, IO_F16, 16>, lds);                                \
+            if (e_ != hipSuccess) return e_;                                             \
+            hipLaunchKernelGGL((KERNEL<MfF16, IO_F16, 16>), grid, blk, lds, s, p);       \
+            break;                                                                       \
+        case IO_F16 * 2 + 1:                                                             \
+            e_ = set_lds(KERNEL<MfF16, IO_F16, 32>, lds);                                \
+            if (e_ != hipSuccess) return e_;                                             \
+            hipLaunchKernelGGL((KERNEL<MfF16, IO_F16, 32>), grid, blk, lds, s, p);       \
+            break;                                                                       \
+        case IO_BF16 * 2:                                                                \
+            e_ = set_lds(KERNEL<MfF16, IO_BF16, 16>, lds);                               \
+            if (e_ != hipSuccess) return e_;                                             \
+            hipLaunchKernelGGL((KERNEL<MfF16, IO_BF16, 16>), grid, blk, lds, s, p);      \
+            break;                                                                       \
+        default:                                                                         \
+            e_ = set_lds(KERNEL<MfF16, IO_BF16, 32>, lds);                               \
+            if (e_ != hipSuccess) return e_;                                             \
+            hipLaunchKernelGGL((KERNEL<MfF16, IO_BF16, 32>), grid, blk, lds, s, p);      \
+            break;                                                                       \
+        }                                                                                \
+        return hipGetLastError();                                                        \
+    } while (0)
+
+hipError_t launch_kgrad_fused(int io, const KgradParams& p, int lds, hipStream_t s) {
+    FFTCONV_KG_LAUNCH(kgrad_fused_kernel, dim3((unsigned)p.H));
+}
+
+hipError_t launch_kgrad_inner(int io, const KgradParams& p, int lds, hipStream_t s) {
+    FFTCONV_KG_LAUNCH(kgrad_inner_kernel, dim3((unsigned)p.H, (unsigned)p.f.nunits));
+}
+
+hipError_t launch_outer_inv_f32out(int io, const FwdParams& p, int lds, hipStream_t s) {
+    const int slab = p.M / p.Qo;
+    const dim3 grid((unsigned)p.rows, slab / p.ct), blk(p.threads);
+    hipError_t e;
+    if (io == IO_F32) {
+        e = set_lds(outer_inv_kernel<MfF32, IO_F32>, lds);
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL((outer_inv_kernel<MfF32, IO_F32>), grid, blk, lds, s, p);
+    } else {
+        e = set_lds(outer_inv_kernel<MfF16, IO_F32>, lds);
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL((outer_inv_kernel<MfF16, IO_F32>), grid, blk, lds, s, p);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_scale_f32(float* x, long long n, float a, hipStream_t s) {
+    if (n <= 0) return hipSuccess;
+    hipLaunchKernelGGL(scale_f32_kernel, dim3(1024), dim3(256), 0, s, x, n, a);
     return hipGetLastError();
 }
 

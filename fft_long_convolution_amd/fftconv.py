@@ -94,6 +94,11 @@ def lib() -> ctypes.CDLL:
         L.fftconv_forward_gated.argtypes = [vp, vp, vp, vp, vp, vp, sz, sz,
                                             sz, vp, sz, vp]
         L.fftconv_forward_gated.restype = i
+        L.fftconv_backward_workspace_bytes.argtypes = [vp, sz, sz]
+        L.fftconv_backward_workspace_bytes.restype = sz
+        L.fftconv_backward.argtypes = [vp, vp, vp, vp, vp, vp, sz, sz, sz,
+                                       vp, sz, vp]
+        L.fftconv_backward.restype = i
         L.fftconv_status_string.argtypes = [i]
         L.fftconv_status_string.restype = ctypes.c_char_p
         L.fftconv_version.argtypes = []
@@ -243,3 +248,46 @@ class FFTConv:
         if st != 0:
             raise FFTConvError(st, "fftconv_forward_gated")
         return out
+
+    def backward_workspace_bytes(self, B: int, H: int) -> int:
+        return int(lib().fftconv_backward_workspace_bytes(self._plan, B, H))
+
+    def backward(self, u, dy, k_f_adj, need_du=True, need_dk=True,
+                 workspace=None, stream=None):
+        """Gradients of the causal convolution: returns (du, dk) for
+        dy = dL/dy ([B, H, N], plan dtype); k_f_adj from
+        kernel_spectrum(k, kind="causal_adjoint").  du has u's shape and
+        dtype, dk is fp32 [H, N]; either may be skipped (None)."""
+        import torch
+        if dy.dim() != 3 or dy.shape[2] != self.N:
+            raise ValueError("dy must be [B, H, %d]" % self.N)
+        if dy.dtype != _torch_dtype(self.dtype):
+            raise ValueError("dy dtype must be %s" % self.dtype)
+        if not (need_du or need_dk):
+            raise ValueError("nothing to compute")
+        dy = dy.contiguous()
+        B, H, N = dy.shape
+        if need_dk:
+            if u is None or u.shape != dy.shape or u.dtype != dy.dtype:
+                raise ValueError("u must match dy")
+            u = u.contiguous()
+        du = torch.empty_like(dy) if need_du else None
+        dk = (torch.empty(H, N, dtype=torch.float32, device=dy.device)
+              if need_dk else None)
+        need = self.backward_workspace_bytes(B, H)
+        ws_ptr, ws_bytes = None, 0
+        if need:
+            if workspace is None:
+                workspace = torch.empty(need, dtype=torch.uint8,
+                                        device=dy.device)
+            ws_ptr = workspace.data_ptr()
+            ws_bytes = workspace.numel() * workspace.element_size()
+        st = lib().fftconv_backward(
+            self._plan, u.data_ptr() if need_dk else None, dy.data_ptr(),
+            k_f_adj.data_ptr() if need_du else None,
+            du.data_ptr() if need_du else None,
+            dk.data_ptr() if need_dk else None, B, H, N, ws_ptr, ws_bytes,
+            _stream_handle(stream))
+        if st != 0:
+            raise FFTConvError(st, "fftconv_backward")
+        return du, dk

@@ -158,7 +158,7 @@ def gate_rows(w: Workload, which: str, rows=None) -> np.ndarray:
     dtype: which = "w" (input gate) or "v" (output gate), each N(0,1) --
     in H3/Hyena-style layers both gates are linear projections of the
     layer input, Gaussian-like at initialisation."""
-    stream = {"w": 4, "v": 5}[which]
+    stream = {"w": 4, "v": 5, "dy": 6}[which]
     rows = np.arange(w.rows) if rows is None else np.asarray(rows, np.int64)
     dt = {"f32": np.float32, "f16": np.float16, "bf16": np.uint16}[w.dtype]
     out = np.empty((len(rows), w.N), dtype=dt)
@@ -166,6 +166,12 @@ def gate_rows(w: Workload, which: str, rows=None) -> np.ndarray:
         out[i] = cast_io(_rng(w.wid, stream, int(r)).standard_normal(w.N),
                          w.dtype)
     return out
+
+
+def dy_rows(w: Workload, rows=None) -> np.ndarray:
+    """Output-gradient rows dL/dy for the backward pass (r = b*H + h), N(0,1)
+    in the storage dtype (a loss with Gaussian sensitivities)."""
+    return gate_rows(w, "dy", rows)
 
 
 def shrink(w: Workload, B: int | None = None, H: int | None = None,

@@ -203,6 +203,37 @@ fftconv_status fftconv_forward_gated(fftconv_plan_t plan, const void *u,
                                      size_t H, size_t N, void *workspace,
                                      size_t workspace_bytes, void *stream);
 
+/* Bytes of the workspace fftconv_backward needs for B x H rows (the
+ * larger of the forward call's and the kernel gradient's: 0 up to N = 8192,
+ * else two B*H x N and one H x N fp32 complex rows). */
+size_t fftconv_backward_workspace_bytes(fftconv_plan_t plan, size_t B, size_t H);
+
+/* Backward pass of the causal convolution y = (u * k)[0:N] (page
+ * "FlashFFTConv: Efficient Convolutions for Long Sequences with Tensor
+ * Cores", section 3: the gradients of an FFT convolution are products with
+ * conjugate spectra, and the spectra of the inputs are recomputed rather
+ * than kept from the forward pass):
+ *   du[b,h,s] = sum_{t>=s} dy[b,h,t] k[h,t-s]
+ *   dk[h,j]   = sum_b sum_{t>=j} dy[b,h,t] u[b,h,t-j]
+ *  u, dy: device, plan dtype, [B][H][N], 16-B aligned (u only needed for dk).
+ *  k_f_adj: from fftconv_kernel_spectrum_kind(..., FFTCONV_CAUSAL_ADJOINT)
+ *     of the same plan and k (only needed for du).
+ *  du: device, plan dtype, [B][H][N], or NULL to skip the input gradient.
+ *  dk: device, fp32, [H][N], 16-B aligned, overwritten (not accumulated),
+ *     or NULL to skip the kernel gradient; not both NULL.
+ *  workspace: fftconv_backward_workspace_bytes(plan, B, H) bytes.
+ * du runs the forward kernels on dy with the adjoint spectrum (the same
+ * cost as a forward call); dk runs the LDS-staged kernels on u and dy,
+ * accumulating conj(U) DY over the batch per channel in registers, then
+ * one inverse transform per channel.  B = 0 gives dk = 0.  The input
+ * gradient of the other kinds is fftconv_forward with the matching adjoint
+ * spectrum.  Errors as fftconv_forward. */
+fftconv_status fftconv_backward(fftconv_plan_t plan, const void *u,
+                                const void *dy, const void *k_f_adj, void *du,
+                                float *dk, size_t B, size_t H, size_t N,
+                                void *workspace, size_t workspace_bytes,
+                                void *stream);
+
 /* Static, human-readable text for a status code. */
 const char *fftconv_status_string(fftconv_status status);
 

@@ -121,3 +121,37 @@ def parity_op(w: inputs.Workload, kind: str):
     else:
         ref = oracle.op_fft(u64, k.astype(np.float64), kind, hidx)
     return oracle.rel_l2(y, ref), y, ref
+
+
+def run_gpu_backward(w: inputs.Workload, conv=None):
+    """GPU (du, dk) of the causal convolution for dy = inputs.dy_rows, as
+    fp64 [rows, N] and [H, N]."""
+    import torch
+    from fft_long_convolution_amd.fftconv import FFTConv
+    if conv is None:
+        conv = FFTConv(w.N, dtype=w.dtype)
+    u = inputs.input_rows(w)
+    dy = inputs.dy_rows(w)
+    k = inputs.kernel_rows(w)
+    ud = to_torch(u, w.dtype).view(w.B, w.H, w.N)
+    dyd = to_torch(dy, w.dtype).view(w.B, w.H, w.N)
+    kfa = conv.kernel_spectrum(torch.from_numpy(k).cuda(), kind="causal_adjoint")
+    du, dk = conv.backward(ud, dyd, kfa)
+    torch.cuda.synchronize()
+    du64 = oracle.to_f64(from_torch(du, w.dtype).reshape(w.rows, w.N), w.dtype)
+    dk64 = dk.cpu().numpy().astype(np.float64)
+    return du64, dk64, u, dy, k
+
+
+def oracle_backward(w: inputs.Workload, u, dy, k):
+    u64 = oracle.to_f64(u, w.dtype).reshape(w.rows, w.N)
+    dy64 = oracle.to_f64(dy, w.dtype).reshape(w.rows, w.N)
+    hidx = np.arange(w.rows) % w.H
+    k64 = k.astype(np.float64)
+    if w.N <= 512:
+        du = oracle.op_direct(dy64, k64, "causal_adjoint", hidx)
+        dk = oracle.kgrad_direct(u64, dy64, w.H, "causal", hidx)
+    else:
+        du = oracle.op_fft(dy64, k64, "causal_adjoint", hidx)
+        dk = oracle.kgrad_fft(u64, dy64, w.H, "causal", hidx)
+    return du, dk

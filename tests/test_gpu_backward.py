@@ -1,0 +1,100 @@
+"""GPU parity of the backward pass of the causal convolution through the C
+ABI entry point fftconv_backward: the input gradient (the forward kernels
+with the adjoint spectrum) and the kernel gradient (LDS-staged kernels
+accumulating conj(U) DY per channel), against the fp64 oracle's
+definitions and convolution-theorem routes.  dk is fp32 for every I/O
+type; its bar is the I/O type's (the inputs' quantisation is exact in the
+oracle, the error is the transforms').
+"""
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+from fft_long_convolution_amd import inputs
+from tests.gpu_helpers import TOL, from_torch, oracle_backward, run_gpu_backward, to_torch
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.mark.parametrize("N,dtype,B,H", [
+    (256, "f32", 1, 4), (256, "bf16", 3, 5), (512, "f16", 4, 3),
+    (1024, "bf16", 5, 3), (1024, "f32", 2, 2), (2048, "f16", 3, 2),
+    (4096, "bf16", 2, 3), (8192, "f16", 3, 2), (16384, "bf16", 2, 3),
+    (32768, "f32", 1, 2), (65536, "f16", 2, 1), (262144, "bf16", 1, 2),
+    (1048576, "f16", 1, 1), (4194304, "bf16", 1, 1)])
+def test_backward(N, dtype, B, H):
+    # fused kernel-gradient kernel up to N = 8192 (two lines per
+    # workgroup), multi-pass (outer passes + accumulating inner pass +
+    # outer inverse) above; the input gradient through every forward family
+    w = inputs.Workload("bwd", 240 + N.bit_length() + B, B, H, N, dtype,
+                        "normal", "decay", "backward")
+    du, dk, u, dy, k = run_gpu_backward(w)
+    rdu, rdk = oracle_backward(w, u, dy, k)
+    edu, edk = oracle.rel_l2(du, rdu), oracle.rel_l2(dk, rdk)
+    _say("backward", N, dtype, B, H, "du rel_l2", edu, "dk rel_l2", edk)
+    assert edu < TOL[dtype]
+    assert edk < TOL[dtype]
+
+
+def test_backward_pieces_and_errors():
+    import torch
+    from fft_long_convolution_amd import fftconv as fc
+    w = inputs.Workload("bwdp", 250, 3, 2, 1024, "bf16", "normal", "decay", "")
+    conv = fc.FFTConv(1024, dtype="bf16")
+    u = to_torch(inputs.input_rows(w), "bf16").view(3, 2, 1024)
+    dy = to_torch(inputs.dy_rows(w), "bf16").view(3, 2, 1024)
+    kfa = conv.kernel_spectrum(torch.from_numpy(inputs.kernel_rows(w)).cuda(),
+                               kind="causal_adjoint")
+    du_all, dk_all = conv.backward(u, dy, kfa)
+    du_only, none1 = conv.backward(None, dy, kfa, need_dk=False)
+    none2, dk_only = conv.backward(u, dy, None, need_du=False)
+    torch.cuda.synchronize()
+    assert none1 is None and none2 is None
+    assert torch.equal(du_all.view(torch.int16), du_only.view(torch.int16))
+    assert torch.equal(dk_all, dk_only)
+    # an empty batch: dk = 0
+    e = torch.empty(0, 2, 1024, dtype=torch.bfloat16, device="cuda")
+    _, dk0 = conv.backward(e, e, None, need_du=False)
+    torch.cuda.synchronize()
+    assert dk0.shape == (2, 1024) and not dk0.any()
+    L = fc.lib()
+    dk = torch.empty(2, 1024, device="cuda")
+    # nothing requested, dk overlapping u, misaligned dk
+    assert L.fftconv_backward(conv._plan, u.data_ptr(), dy.data_ptr(), None,
+                              None, None, 3, 2, 1024, None, 0, None) == 1
+    assert L.fftconv_backward(conv._plan, u.data_ptr(), dy.data_ptr(), None,
+                              None, u.data_ptr(), 3, 2, 1024, None, 0,
+                              None) == 1
+    assert L.fftconv_backward(conv._plan, u.data_ptr(), dy.data_ptr(), None,
+                              None, dk.data_ptr() + 4, 3, 2, 1024, None, 0,
+                              None) == 3
+    # a multi-pass kernel gradient needs its workspace
+    conv2 = fc.FFTConv(32768, dtype="f16")
+    u2 = torch.randn(1, 1, 32768, device="cuda").half()
+    dk2 = torch.empty(1, 32768, device="cuda")
+    need = conv2.backward_workspace_bytes(1, 1)
+    assert need >= 3 * 32768 * 8
+    assert L.fftconv_backward(conv2._plan, u2.data_ptr(), u2.data_ptr(), None,
+                              None, dk2.data_ptr(), 1, 1, 32768, None, 0,
+                              None) == 4
+    torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("name", ["hyena_bf16_n1k", "m2bert_f16_n8k",
+                                  "audio_bf16_n64k"])
+def test_backward_full_size(name):
+    w = inputs.WORKLOADS[name]
+    _say("backward full-size", name)
+    du, dk, u, dy, k = run_gpu_backward(w)
+    rdu, rdk = oracle_backward(w, u, dy, k)
+    edu, edk = oracle.rel_l2(du, rdu), oracle.rel_l2(dk, rdk)
+    _say("  du rel_l2", edu, "dk rel_l2", edk)
+    assert edu < TOL[w.dtype]
+    assert edk < TOL[w.dtype]

@@ -121,6 +121,10 @@ def test_null_plan_is_rejected_without_device():
     assert L.fftconv_forward(None, 16, 16, 16, 1, 1, 256, None, 0, None) == 1
     assert L.fftconv_forward_gated(None, 16, 16, 16, 16, 16, 1, 1, 256, None,
                                    0, None) == 1
+    assert L.fftconv_backward(None, 16, 16, 16, 16, 16, 1, 1, 256, None, 0,
+                              None) == 1
+    assert L.fftconv_backward_workspace_bytes(None, 1, 1) == 0
+    assert L.fftconv_kernel_spectrum_kind(None, 16, 1, 0, 16, None) == 1
     assert L.fftconv_kernel_spectrum(None, 16, 1, 16, None) == 1
     assert L.fftconv_spectrum_bytes(None, 4) == 0
     assert L.fftconv_workspace_bytes(None, 1, 1) == 0
