@@ -13,7 +13,9 @@ as a baseline.
 
 --gated times the gated form y = v * ((u * w) conv k) instead (one
 fftconv_forward_gated per step; the gates are seeded N(0,1) tensors of the
-shape of u, resident in HBM like u).
+shape of u, resident in HBM like u).  --circular times the non-causal
+(circular) convolution, --backward one fftconv_backward (du and dk of the
+causal convolution for a seeded N(0,1) dy).
 """
 from __future__ import annotations
 
@@ -72,6 +74,10 @@ def parse():
     ap.add_argument("--workload", default="hyena_bf16_n1k")
     ap.add_argument("--gated", action="store_true",
                     help="time the gated convolution v * ((u * w) conv k)")
+    ap.add_argument("--circular", action="store_true",
+                    help="time the non-causal (circular) convolution")
+    ap.add_argument("--backward", action="store_true",
+                    help="time the backward pass (du and dk)")
     ap.add_argument("--no-cpu", action="store_true",
                     help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
@@ -112,6 +118,12 @@ def main():
         print(json.dumps({"copy_calibration_bytes_each_way": a.numel() * 4,
                           "copies": args.steps or 100}))
         return
+    if args.gated + args.circular + args.backward > 1:
+        print("bench.py: choose one of --gated, --circular, --backward",
+              file=sys.stderr)
+        sys.exit(2)
+    op = ("gated" if args.gated else "circular" if args.circular
+          else "backward" if args.backward else "plain")
     conv = FFTConv(w.N, dtype=w.dtype)
     info = conv.info
 
@@ -119,30 +131,42 @@ def main():
     t0 = time.time()
     u_np = inputs.input_rows(w)
     k_np = inputs.kernel_rows(w)
-    g_np = ([inputs.gate_rows(w, "w"), inputs.gate_rows(w, "v")]
-            if args.gated else [])
+    if op == "gated":
+        g_np = [inputs.gate_rows(w, "w"), inputs.gate_rows(w, "v")]
+    elif op == "backward":
+        g_np = [inputs.dy_rows(w)]
+    else:
+        g_np = []
     gen_s = time.time() - t0
     u0 = to_torch(u_np, w.dtype, torch).view(w.B, w.H, w.N).to(dev)
     g0 = [to_torch(a, w.dtype, torch).view(w.B, w.H, w.N).to(dev) for a in g_np]
     k = torch.from_numpy(k_np).to(dev)
-    kf = conv.kernel_spectrum(k)
+    kind = {"circular": "circular", "backward": "causal_adjoint"}.get(op, "causal")
+    kf = conv.kernel_spectrum(k, kind=kind)
     esz = 4 if w.dtype == "f32" else 2
-    # streams per step: u, y (+ the two gates)
-    nstream = 4 if args.gated else 2
+    # [B][H][N] streams per step: u and y, + the two gates (gated), or u, dy
+    # and du (backward, which also writes the fp32 [H][N] dk)
+    nstream = {"gated": 4, "backward": 3}.get(op, 2)
     set_bytes = nstream * w.rows * w.N * esz
     nsets = max(1, min(8, -(-ROTATE_BYTES // set_bytes)))
     us = [u0] + [u0.clone() for _ in range(nsets - 1)]
     gs = [g0] + [[g.clone() for g in g0] for _ in range(nsets - 1)]
     ys = [torch.empty_like(u0) for _ in range(nsets)]
-    wsb = conv.workspace_bytes(w.B, w.H)
+    dks = ([torch.empty(w.H, w.N, dtype=torch.float32, device=dev)
+            for _ in range(nsets)] if op == "backward" else [])
+    wsb = (conv.backward_workspace_bytes(w.B, w.H) if op == "backward"
+           else conv.workspace_bytes(w.B, w.H))
     ws = torch.empty(max(wsb, 16), dtype=torch.uint8, device=dev)
     torch.cuda.synchronize()
 
     def step(i):
         j = i % nsets
-        if args.gated:
+        if op == "gated":
             conv.forward_gated(us[j], gs[j][0], gs[j][1], kf, out=ys[j],
                                workspace=ws)
+        elif op == "backward":
+            conv.backward(us[j], gs[j][0], kf, workspace=ws, out_du=ys[j],
+                          out_dk=dks[j])
         else:
             conv.forward(us[j], kf, out=ys[j], workspace=ws)
 
@@ -201,9 +225,13 @@ def main():
     # overhead.
     kf_bytes = conv.spectrum_bytes(w.H)
     alg_bytes = nstream * w.rows * w.N * esz + kf_bytes
+    if op == "backward":
+        alg_bytes += w.H * w.N * 4
     ms_kernel = ms_step
     achieved_gbs = alg_bytes / (ms_kernel * 1e-3) / 1e9
-    flops = info["mfma_flops_per_row"] * w.rows
+    # matrix-core flops: one forward call's; the backward counts two (du is
+    # one forward call, dk two forward transforms per row)
+    flops = info["mfma_flops_per_row"] * w.rows * (2 if op == "backward" else 1)
     achieved_tf = flops / (ms_kernel * 1e-3) / 1e12
     t_hbm = alg_bytes / (HBM_PEAK_GBS * 1e9)
     t_mfma = flops / (MFMA_PEAK_TFLOPS[w.dtype] * 1e12)
@@ -216,8 +244,8 @@ def main():
         roof = {"bound": "mfma", "achieved": round(achieved_tf, 2),
                 "peak": MFMA_PEAK_TFLOPS[w.dtype], "unit": "TFLOP/s",
                 "frac": round(achieved_tf / MFMA_PEAK_TFLOPS[w.dtype], 4)}
-    roof["traffic"] = measured_traffic(w.name + ("_gated" if args.gated else ""))
-    roof["kernel"] = info["kernel"]
+    roof["traffic"] = measured_traffic(w.name + ("" if op == "plain" else "_" + op))
+    roof["kernel"] = info["kernel"] + ("+kgrad" if op == "backward" else "")
     roof["algorithmic_bytes"] = int(alg_bytes)
     roof["mfma_flops"] = float(flops)
     roof["mfma_frac"] = round(achieved_tf / MFMA_PEAK_TFLOPS[w.dtype], 4)
@@ -234,30 +262,57 @@ def main():
     sel_k = k_np.astype(np.float64)
     got = y_last[torch.from_numpy(rows).to(dev), torch.from_numpy(ts).to(dev)]
     got = got.float().cpu().numpy().astype(np.float64)
-    if args.gated:
+    if op == "gated":
         sel_w, sel_v = (oracle.to_f64(a[rows], w.dtype) for a in g_np)
         want = oracle.gated_points(sel_u, sel_w, sel_v, sel_k, np.arange(48),
                                    ts, rows % w.H)
+    elif op == "circular":
+        want = oracle.op_points(sel_u, sel_k, "circular", np.arange(48), ts,
+                                rows % w.H)
+    elif op == "backward":
+        sel_dy = oracle.to_f64(g_np[0][rows], w.dtype)
+        want = oracle.op_points(sel_dy, sel_k, "causal_adjoint", np.arange(48),
+                                ts, rows % w.H)
     else:
         want = oracle.conv_points(sel_u, sel_k, np.arange(48), ts, rows % w.H)
     scale = float(np.sqrt(np.mean(want ** 2))) or 1.0
     sample_err = float(np.max(np.abs(got - want)) / scale)
+    if op == "backward":
+        # dk at a few taps of two channels (all batch rows of each)
+        hs_sel = np.unique(rng.integers(0, w.H, 2))
+        rsel = np.array([b * w.H + h for h in hs_sel for b in range(w.B)])
+        hloc = np.repeat(np.arange(len(hs_sel)), w.B)
+        js = rng.integers(0, w.N, 8)
+        js[:2] = [0, w.N - 1]
+        hq = np.repeat(np.arange(len(hs_sel)), len(js))
+        jq = np.tile(js, len(hs_sel))
+        want_k = oracle.kgrad_points(oracle.to_f64(u_np[rsel], w.dtype),
+                                     oracle.to_f64(g_np[0][rsel], w.dtype),
+                                     len(hs_sel), hq, jq, "causal", hloc)
+        dk_last = dks[(args.steps - 1) % nsets].cpu().numpy().astype(np.float64)
+        got_k = dk_last[hs_sel[hq], jq]
+        sk = float(np.sqrt(np.mean(want_k ** 2))) or 1.0
+        sample_err = max(sample_err, float(np.max(np.abs(got_k - want_k)) / sk))
 
     # ---- CPU baseline: the fp64 oracle on a bounded sample of the rows
     cpu = None
     if not args.no_cpu:
         cores = oracle.num_threads()
         hidx = np.arange(w.rows) % w.H
-        # probe a slice of about 4M outputs, then size the sample to the
-        # requested CPU time (whole rows; at most the whole workload)
+
         def cpu_run(n):
             uh, inv = np.unique(hidx[:n], return_inverse=True)
             usel = oracle.to_f64(u_np[:n], w.dtype)
             ksel = k_np[uh].astype(np.float64)
             gsel = [oracle.to_f64(a[:n], w.dtype) for a in g_np]
             t0 = time.perf_counter()
-            if args.gated:
+            if op == "gated":
                 oracle.gated_fft(usel, gsel[0], gsel[1], ksel, inv)
+            elif op == "circular":
+                oracle.op_fft(usel, ksel, "circular", inv)
+            elif op == "backward":
+                oracle.op_fft(gsel[0], ksel, "causal_adjoint", inv)
+                oracle.kgrad_fft(usel, gsel[0], len(uh), "causal", inv)
             else:
                 oracle.conv_fft(usel, ksel, inv)
             return time.perf_counter() - t0
@@ -265,13 +320,14 @@ def main():
         tp = cpu_run(probe)
         n = int(min(w.rows, max(probe, probe * args.cpu_seconds / max(tp, 1e-6))))
         tc = cpu_run(n)
+        what = {"gated": " with both gates", "circular": " (circular kind)",
+                "backward": " (du by the adjoint and dk by the gradient "
+                            "routes)"}.get(op, "")
         cpu = {"value": round(n * w.N / tc, 1), "unit": "outputs/s",
                "cores": cores, "kind": "oracle",
                "sample": "%d of %d rows (B*H) at N=%d through the fp64 "
                          "radix-2 FFT route of the oracle%s, kernel spectra "
-                         "included; %.1f s" % (n, w.rows, w.N,
-                                               " with both gates" if args.gated else "",
-                                               tc)}
+                         "included; %.1f s" % (n, w.rows, w.N, what, tc)}
 
     line = {
         "metric": METRIC, "value": round(value, 1), "unit": "outputs/s",
@@ -279,8 +335,8 @@ def main():
         "ms_per_step": round(ms_step, 5), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": w.dtype,
         "data": "synthetic",
-        "config": {"workload": w.name + (" gated" if args.gated else ""),
-                   "op": "gated" if args.gated else "plain",
+        "config": {"workload": w.name + ("" if op == "plain" else " " + op),
+                   "op": op,
                    "B": w.B, "H": w.H, "N": w.N,
                    "io_dtype": w.dtype, "factors": info["factors"],
                    "path": info["path"], "global_batch": w.B,

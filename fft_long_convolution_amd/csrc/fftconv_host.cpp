@@ -984,9 +984,25 @@ fftconv_status build_grad_plan(fftconv_plan_s* pl) {
     return FFTCONV_OK;
 }
 
+// Batch slices of the fused kernel-gradient pass: enough workgroups to
+// give every SIMD a few waves (each slice is a workgroup per channel).
+int kgrad_splits(const fftconv_plan_s* pl, size_t B, size_t H) {
+    const Shape& g = pl->grad->s;
+    if (g.path != 0 || B <= 1 || H == 0) return 1;
+    const long long waves = g.thr_fused / 64;
+    const long long want = 4LL * 4 * pl->num_cu;   // waves: four per SIMD
+    long long n = (want + H * waves - 1) / (H * waves);
+    if (n > (long long)B) n = (long long)B;
+    if (n > 64) n = 64;
+    return n < 1 ? 1 : (int)n;
+}
+
 size_t kgrad_workspace_bytes(const fftconv_plan_s* pl, size_t B, size_t H) {
     const Shape& g = pl->grad->s;
-    if (g.path == 0) return 0;
+    if (g.path == 0) {
+        const int ns = kgrad_splits(pl, B, H);
+        return ns > 1 ? (size_t)ns * H * g.N * 4 : 0;
+    }
     // outer-transformed rows of u and dy, and one result row per channel
     return (2 * B * H + H) * g.M * 8;
 }
@@ -1465,7 +1481,11 @@ fftconv_status fftconv_backward(fftconv_plan_t plan, const void* u,
     const int lds = kgrad_lds(g);
     if (g.path == 0) {
         K.f = gp->fused;
-        e = launch_kgrad_fused(io, K, lds, st);
+        const int ns = kgrad_splits(plan, B, H);
+        K.wsg = (float2*)workspace;
+        e = launch_kgrad_fused(io, K, ns, lds, st);
+        if (e == hipSuccess && ns > 1)
+            e = launch_kgrad_reduce((const float*)workspace, dk, (long long)(H * N), ns, st);
     } else {
         float2* wsu = (float2*)workspace;
         float2* wsd = wsu + rows * g.M;

@@ -99,13 +99,18 @@ struct KgradParams {
     float scale;        // sqrt(M): the unitary transforms' lost factor
     const void* u;      // [B][H][N], plan dtype (fused)
     const void* dy;
-    float* dk;          // [H][N] fp32 (fused)
+    float* dk;          // [H][N] fp32 (fused, one batch slice)
     const float2* wsu;  // multi-pass: outer-transformed rows [B*H][M]
     const float2* wsd;
-    float2* wsg;        // multi-pass: per-channel result rows [H][M]
+    float2* wsg;        // multi-pass: per-channel result rows [H][M];
+                        // fused with several slices: partial dk rows
 };
-hipError_t launch_kgrad_fused(int io, const KgradParams& p, int lds_bytes,
+// fused: grid H x nsplit batch slices; with nsplit > 1 the slices write
+// partial rows to wsg ([nsplit][H][N] fp32) for launch_kgrad_reduce
+hipError_t launch_kgrad_fused(int io, const KgradParams& p, int nsplit, int lds_bytes,
                               hipStream_t s);
+hipError_t launch_kgrad_reduce(const float* part, float* dk, long long n, int nsplit,
+                               hipStream_t s);
 hipError_t launch_kgrad_inner(int io, const KgradParams& p, int lds_bytes,
                               hipStream_t s);
 // outer inverse pass writing fp32 (the kernel gradient) whatever the plan's

@@ -861,8 +861,10 @@ __device__ __forceinline__ void kgrad_final(float2* __restrict__ line, const Mid
 // innermost stages, one for 32-point ones (registers)
 constexpr int kg_spw(int nm) { return nm == 32 ? 1 : 2; }
 
-// Fused: one workgroup per channel, looping over the batch; two lines
-// (u and dy) in LDS.  dk = `post` x the inverse of the accumulated spectrum.
+// Fused: one workgroup per (channel, slice of the batch), looping over its
+// rows; two lines (u and dy) in LDS.  Writes `post` x the inverse of the
+// accumulated spectrum to dk (one slice) or to the slice's partial row
+// (several slices, summed by kgrad_reduce_kernel: the inverse is linear).
 template <class MF, int IO, int NM>
 __global__ void __launch_bounds__(512) kgrad_fused_kernel(KgradParams P) {
     extern __shared__ float2 smem[];
@@ -873,6 +875,8 @@ __global__ void __launch_bounds__(512) kgrad_fused_kernel(KgradParams P) {
     float2* lb = smem + F.M;
     float2* scr = smem + 2 * F.M + wave * 64;
     const int h = blockIdx.x;
+    const int b0 = (int)(((long long)P.B * blockIdx.y) / gridDim.y);
+    const int b1 = (int)(((long long)P.B * (blockIdx.y + 1)) / gridDim.y);
     constexpr int SPW = kg_spw(NM);
     float2 accA[SPW][NM / 8][2], accB[SPW][NM / 8][2];
 #pragma unroll
@@ -881,7 +885,7 @@ __global__ void __launch_bounds__(512) kgrad_fused_kernel(KgradParams P) {
         for (int mt = 0; mt < NM / 8; ++mt)
 #pragma unroll
             for (int e = 0; e < 2; ++e) accA[sp][mt][e] = accB[sp][mt][e] = make_float2(0.f, 0.f);
-    for (int b = 0; b < P.B; ++b) {
+    for (int b = b0; b < b1; ++b) {
         const long long row = (long long)b * P.H + h;
         load_points<IO>(io_ptr<IO>(P.u, row * F.N), nullptr, la, F.N >> 1, threadIdx.x, blockDim.x);
         load_points<IO>(io_ptr<IO>(P.dy, row * F.N), nullptr, lb, F.N >> 1, threadIdx.x, blockDim.x);
@@ -903,9 +907,27 @@ __global__ void __launch_bounds__(512) kgrad_fused_kernel(KgradParams P) {
         __syncthreads();
     }
     const float post = P.scale;
-    float2* o = (float2*)(P.dk + (long long)h * F.N);
+    float* dst = gridDim.y > 1 ? (float*)P.wsg + (long long)blockIdx.y * P.H * F.N : P.dk;
+    float2* o = (float2*)(dst + (long long)h * F.N);
     for (int j = threadIdx.x; j < (F.N >> 1); j += blockDim.x)
         o[j] = make_float2(la[j].x * post, la[j].y * post);
+}
+
+// dk = the sum of the slices' partial rows, [nsplit][H * N] -> [H * N]
+__global__ void kgrad_reduce_kernel(const float4* __restrict__ part, float4* __restrict__ dk,
+                                    long long n4, int nsplit) {
+    for (long long i = blockIdx.x * (long long)blockDim.x + threadIdx.x; i < n4;
+         i += (long long)gridDim.x * blockDim.x) {
+        float4 a = part[i];
+        for (int sidx = 1; sidx < nsplit; ++sidx) {
+            const float4 b = part[(long long)sidx * n4 + i];
+            a.x += b.x;
+            a.y += b.y;
+            a.z += b.z;
+            a.w += b.w;
+        }
+        dk[i] = a;
+    }
 }
 
 // Multi-pass inner pass: one workgroup per (channel, unit of slabs), looping
@@ -1198,8 +1220,16 @@ hipError_t launch_alphabeta(int io, const SpecParams& p, hipStream_t s) {
         return hipGetLastError();                                                        \
     } while (0)
 
-hipError_t launch_kgrad_fused(int io, const KgradParams& p, int lds, hipStream_t s) {
-    FFTCONV_KG_LAUNCH(kgrad_fused_kernel, dim3((unsigned)p.H));
+hipError_t launch_kgrad_fused(int io, const KgradParams& p, int nsplit, int lds, hipStream_t s) {
+    FFTCONV_KG_LAUNCH(kgrad_fused_kernel, dim3((unsigned)p.H, (unsigned)nsplit));
+}
+
+hipError_t launch_kgrad_reduce(const float* part, float* dk, long long n, int nsplit,
+                               hipStream_t s) {
+    if (n % 4) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(kgrad_reduce_kernel, dim3(2048), dim3(256), 0, s, (const float4*)part,
+                       (float4*)dk, n / 4, nsplit);
+    return hipGetLastError();
 }
 
 hipError_t launch_kgrad_inner(int io, const KgradParams& p, int lds, hipStream_t s) {

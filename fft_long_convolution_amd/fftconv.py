@@ -253,7 +253,7 @@ class FFTConv:
         return int(lib().fftconv_backward_workspace_bytes(self._plan, B, H))
 
     def backward(self, u, dy, k_f_adj, need_du=True, need_dk=True,
-                 workspace=None, stream=None):
+                 workspace=None, stream=None, out_du=None, out_dk=None):
         """Gradients of the causal convolution: returns (du, dk) for
         dy = dL/dy ([B, H, N], plan dtype); k_f_adj from
         kernel_spectrum(k, kind="causal_adjoint").  du has u's shape and
@@ -271,9 +271,16 @@ class FFTConv:
             if u is None or u.shape != dy.shape or u.dtype != dy.dtype:
                 raise ValueError("u must match dy")
             u = u.contiguous()
-        du = torch.empty_like(dy) if need_du else None
-        dk = (torch.empty(H, N, dtype=torch.float32, device=dy.device)
-              if need_dk else None)
+        du = dk = None
+        if need_du:
+            du = torch.empty_like(dy) if out_du is None else out_du
+            if du.shape != dy.shape or du.dtype != dy.dtype:
+                raise ValueError("out_du must match dy")
+        if need_dk:
+            dk = (torch.empty(H, N, dtype=torch.float32, device=dy.device)
+                  if out_dk is None else out_dk)
+            if dk.shape != (H, N) or dk.dtype != torch.float32:
+                raise ValueError("out_dk must be fp32 [H, N]")
         need = self.backward_workspace_bytes(B, H)
         ws_ptr, ws_bytes = None, 0
         if need:
