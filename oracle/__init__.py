@@ -22,6 +22,8 @@ Cores", section 3.4):
 * ``kgrad_direct`` / ``kgrad_fft`` / ``kgrad_points`` -- the kernel
   gradient ``dk[h][j] = sum_{rows of h} sum_t dy[t] u[t-j]`` (t-j mod N for
   the circular kinds);
+* ``lowpass_fft`` -- the frequency-sparse (band-limited) convolution: the
+  2N-point kernel spectrum zeroed beyond a cutoff frequency F;
 * ``gated_direct`` / ``gated_fft`` / ``gated_points`` -- the gated
   convolution ``y = v * ((u * w) conv k)`` (elementwise gates on the input
   and on the output; same page, section 3 "Technical Approach",
@@ -90,6 +92,8 @@ def _load():
         lib.oracle_kgrad_fft.restype = ctypes.c_int
         lib.oracle_kgrad_points.argtypes = [d, d, lp, L, L, lp, lp, L, I, d]
         lib.oracle_kgrad_points.restype = None
+        lib.oracle_lowpass_fft.argtypes = [d, d, lp, d, L, L, L, L]
+        lib.oracle_lowpass_fft.restype = ctypes.c_int
         _lib = lib
     return _lib
 
@@ -274,6 +278,21 @@ def kgrad_points(u, dy, Hk: int, hs, js, kind: str = "causal",
     _load().oracle_kgrad_points(_dp(u), _dp(dy), _lp(hidx), R, N, _lp(hs),
                                 _lp(js), len(hs), kd, _dp(out))
     return out
+
+
+def lowpass_fft(u, k, F: int, hidx=None) -> np.ndarray:
+    """Frequency-sparse causal convolution: IFFT_2N(U . K_F)[0:N] where the
+    kernel spectrum keeps only frequencies f with min(f, 2N - f) <= F."""
+    u, k, hidx, R, N = _rows(u, k, hidx)
+    if N & (N - 1):
+        raise ValueError("lowpass_fft needs a power-of-two N")
+    if F < 0:
+        raise ValueError("cutoff must be >= 0")
+    y = np.empty((R, N), dtype=np.float64)
+    if _load().oracle_lowpass_fft(_dp(u), _dp(k), _lp(hidx), _dp(y), R,
+                                  k.shape[0], N, int(F)) != 0:
+        raise MemoryError("oracle_lowpass_fft: allocation failed")
+    return y
 
 
 def _gates(u, w, v):

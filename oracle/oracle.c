@@ -42,6 +42,12 @@
  * theorem (2N zero padding for the causal kinds, size N for the circular
  * ones; the adjoints multiply by the conjugate spectrum).
  *
+ * Frequency-sparse (low-pass) convolution (same page, section 3:
+ * zeroing part of the kernel spectrum, a band limit that discards the high
+ * frequencies): the causal route above with the 2N-point kernel spectrum
+ * set to zero at every frequency f whose distance min(f, 2N - f) from
+ * zero exceeds the cutoff F.
+ *
  * All arithmetic is fp64.  Rows are independent; OpenMP splits them.
  */
 #include <math.h>
@@ -451,4 +457,63 @@ void oracle_kgrad_points(const double *u, const double *dy, const long *hidx,
         }
         out[i] = acc;
     }
+}
+
+
+/* Frequency-sparse causal convolution: y = IFFT_2N(U . K_F)[0:N] with
+ * K_F[f] = K[f] if min(f, 2N - f) <= F, else 0. */
+int oracle_lowpass_fft(const double *u, const double *kern, const long *hidx,
+                       double *y, long R, long Hk, long N, long F)
+{
+    const long L = 2 * N;
+    double *kre = (double *)malloc(sizeof(double) * (size_t)(Hk * L));
+    double *kim = (double *)malloc(sizeof(double) * (size_t)(Hk * L));
+    if (!kre || !kim) {
+        free(kre);
+        free(kim);
+        return -1;
+    }
+    oracle_kernel_spectrum(kern, Hk, N, kre, kim);
+    for (long h = 0; h < Hk; ++h)
+        for (long f = 0; f < L; ++f) {
+            long dist = f < L - f ? f : L - f;
+            if (dist > F) {
+                kre[h * L + f] = 0.0;
+                kim[h * L + f] = 0.0;
+            }
+        }
+    int fail = 0;
+#pragma omp parallel
+    {
+        double *re = (double *)malloc(sizeof(double) * (size_t)L);
+        double *im = (double *)malloc(sizeof(double) * (size_t)L);
+        if (!re || !im) {
+#pragma omp atomic write
+            fail = 1;
+        } else {
+            long r;
+#pragma omp for schedule(dynamic, 1)
+            for (r = 0; r < R; ++r) {
+                const double *Kr = kre + hidx[r] * L, *Ki = kim + hidx[r] * L;
+                for (long t = 0; t < L; ++t) {
+                    re[t] = t < N ? u[r * N + t] : 0.0;
+                    im[t] = 0.0;
+                }
+                fft_radix2(re, im, L, -1);
+                for (long f = 0; f < L; ++f) {
+                    double a = re[f], b = im[f];
+                    re[f] = a * Kr[f] - b * Ki[f];
+                    im[f] = a * Ki[f] + b * Kr[f];
+                }
+                fft_radix2(re, im, L, +1);
+                for (long t = 0; t < N; ++t)
+                    y[r * N + t] = re[t] / (double)L;
+            }
+        }
+        free(re);
+        free(im);
+    }
+    free(kre);
+    free(kim);
+    return fail ? -1 : 0;
 }

@@ -515,3 +515,58 @@ def test_kernel_gradient_against_numpy_fft():
                          for h in range(H)])
         np.testing.assert_allclose(oracle.kgrad_fft(u, dy, H, kind), want,
                                    atol=1e-11)
+
+
+# ------------------------------------------------- frequency-sparse (low-pass)
+
+def _dirichlet_kernel(c, F):
+    # the 2N-periodic kernel whose spectrum is that of c band-limited to
+    # |f| <= F, by circular convolution with the Dirichlet kernel
+    # D_F[j] = sin(pi (2F+1) j / L) / (L sin(pi j / L)), D_F[0] = (2F+1)/L
+    L = len(c)
+    j = np.arange(L)
+    D = np.empty(L)
+    D[0] = (2 * F + 1) / L
+    jj = j[1:]
+    D[1:] = np.sin(np.pi * (2 * F + 1) * jj / L) / (L * np.sin(np.pi * jj / L))
+    out = np.zeros(L)
+    for n in range(L):
+        out[n] = sum(c[m] * D[(n - m) % L] for m in range(L))
+    return out
+
+
+@pytest.mark.parametrize("N,F", [(8, 2), (16, 5), (16, 0), (32, 11)])
+def test_lowpass_time_domain(N, F):
+    # independent route: band-limit the padded kernel in time (Dirichlet),
+    # then the 2N-point circular convolution by its definition
+    rng = np.random.default_rng(400 + N + F)
+    u = rng.standard_normal((2, N))
+    k = rng.standard_normal((2, N))
+    L = 2 * N
+    want = np.zeros((2, N))
+    for r in range(2):
+        c = _dirichlet_kernel(np.concatenate([k[r], np.zeros(N)]), F)
+        up = np.concatenate([u[r], np.zeros(N)])
+        for t in range(N):
+            want[r, t] = sum(up[s] * c[(t - s) % L] for s in range(L))
+    np.testing.assert_allclose(oracle.lowpass_fft(u, k, F), want, atol=1e-12)
+
+
+def test_lowpass_special_cases():
+    rng = np.random.default_rng(41)
+    N = 64
+    u = rng.standard_normal((3, N))
+    k = rng.standard_normal((3, N))
+    # no band limit: the causal convolution
+    np.testing.assert_allclose(oracle.lowpass_fft(u, k, N), oracle.conv_direct(u, k),
+                               atol=1e-12)
+    # DC only: every output is sum(u) sum(k) / 2N
+    y0 = oracle.lowpass_fft(u, k, 0)
+    want = (u.sum(axis=1) * k.sum(axis=1) / (2 * N))[:, None] * np.ones((1, N))
+    np.testing.assert_allclose(y0, want, atol=1e-12)
+    # against numpy: the same band limit applied to numpy's spectra
+    L = 2 * N
+    f = np.arange(L)
+    mask = np.minimum(f, L - f) <= 9
+    want = np.fft.ifft(np.fft.fft(u, n=L) * np.fft.fft(k, n=L) * mask).real[:, :N]
+    np.testing.assert_allclose(oracle.lowpass_fft(u, k, 9), want, atol=1e-12)
