@@ -78,6 +78,9 @@ def parse():
                     help="time the non-causal (circular) convolution")
     ap.add_argument("--backward", action="store_true",
                     help="time the backward pass (du and dk)")
+    ap.add_argument("--lowpass", type=int, default=None, metavar="F",
+                    help="time the frequency-sparse convolution whose kernel "
+                         "spectrum keeps frequencies within F of zero")
     ap.add_argument("--no-cpu", action="store_true",
                     help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
@@ -118,12 +121,13 @@ def main():
         print(json.dumps({"copy_calibration_bytes_each_way": a.numel() * 4,
                           "copies": args.steps or 100}))
         return
-    if args.gated + args.circular + args.backward > 1:
-        print("bench.py: choose one of --gated, --circular, --backward",
-              file=sys.stderr)
+    if args.gated + args.circular + args.backward + (args.lowpass is not None) > 1:
+        print("bench.py: choose one of --gated, --circular, --backward, "
+              "--lowpass", file=sys.stderr)
         sys.exit(2)
     op = ("gated" if args.gated else "circular" if args.circular
-          else "backward" if args.backward else "plain")
+          else "backward" if args.backward
+          else "lowpass" if args.lowpass is not None else "plain")
     conv = FFTConv(w.N, dtype=w.dtype)
     info = conv.info
 
@@ -142,7 +146,10 @@ def main():
     g0 = [to_torch(a, w.dtype, torch).view(w.B, w.H, w.N).to(dev) for a in g_np]
     k = torch.from_numpy(k_np).to(dev)
     kind = {"circular": "circular", "backward": "causal_adjoint"}.get(op, "causal")
-    kf = conv.kernel_spectrum(k, kind=kind)
+    if op == "lowpass":
+        kf = conv.kernel_spectrum_lowpass(k, args.lowpass)
+    else:
+        kf = conv.kernel_spectrum(k, kind=kind)
     esz = 4 if w.dtype == "f32" else 2
     # [B][H][N] streams per step: u and y, + the two gates (gated), or u, dy
     # and du (backward, which also writes the fp32 [H][N] dk)
@@ -167,6 +174,8 @@ def main():
         elif op == "backward":
             conv.backward(us[j], gs[j][0], kf, workspace=ws, out_du=ys[j],
                           out_dk=dks[j])
+        elif op == "lowpass":
+            conv.forward_lowpass(us[j], kf, args.lowpass, out=ys[j], workspace=ws)
         else:
             conv.forward(us[j], kf, out=ys[j], workspace=ws)
 
@@ -273,6 +282,11 @@ def main():
         sel_dy = oracle.to_f64(g_np[0][rows], w.dtype)
         want = oracle.op_points(sel_dy, sel_k, "causal_adjoint", np.arange(48),
                                 ts, rows % w.H)
+    elif op == "lowpass":
+        # the band-limited route over the sampled rows, then the samples
+        uh, inv = np.unique(rows % w.H, return_inverse=True)
+        full = oracle.lowpass_fft(sel_u, sel_k[uh], args.lowpass, inv)
+        want = full[np.arange(48), ts]
     else:
         want = oracle.conv_points(sel_u, sel_k, np.arange(48), ts, rows % w.H)
     scale = float(np.sqrt(np.mean(want ** 2))) or 1.0
@@ -313,6 +327,8 @@ def main():
             elif op == "backward":
                 oracle.op_fft(gsel[0], ksel, "causal_adjoint", inv)
                 oracle.kgrad_fft(usel, gsel[0], len(uh), "causal", inv)
+            elif op == "lowpass":
+                oracle.lowpass_fft(usel, ksel, args.lowpass, inv)
             else:
                 oracle.conv_fft(usel, ksel, inv)
             return time.perf_counter() - t0
@@ -322,7 +338,8 @@ def main():
         tc = cpu_run(n)
         what = {"gated": " with both gates", "circular": " (circular kind)",
                 "backward": " (du by the adjoint and dk by the gradient "
-                            "routes)"}.get(op, "")
+                            "routes)",
+                "lowpass": " (band-limited spectrum)"}.get(op, "")
         cpu = {"value": round(n * w.N / tc, 1), "unit": "outputs/s",
                "cores": cores, "kind": "oracle",
                "sample": "%d of %d rows (B*H) at N=%d through the fp64 "
@@ -336,7 +353,7 @@ def main():
         "scaling": "weak", "vs_baseline": None, "dtype": w.dtype,
         "data": "synthetic",
         "config": {"workload": w.name + ("" if op == "plain" else " " + op),
-                   "op": op,
+                   "op": op, "cutoff": args.lowpass,
                    "B": w.B, "H": w.H, "N": w.N,
                    "io_dtype": w.dtype, "factors": info["factors"],
                    "path": info["path"], "global_batch": w.B,

@@ -448,7 +448,10 @@ std::vector<uint16_t> row_i1a() {
 
 // Inner inverse stage as the B operand: K in accumulator (chain) order of
 // the permuted inner forward stage, columns (n_b tile, part c).
-std::vector<uint16_t> row_i2b(int NB) {
+// K-step ks, half h of a lane's 8 values: M-tile 2 ks + h of the forward
+// accumulators, or ks + h KS with `split` (the row kernel: its K-step 1 then
+// holds exactly the tiles of the middle k_b, which a band limit zeroes).
+std::vector<uint16_t> row_i2b(int NB, bool split = false) {
     const int KS = NB / 16, JT = 2 * (NB / 16);
     std::vector<uint16_t> out((size_t)KS * JT * 64 * 8);
     const double sc = 1.0 / sqrt((double)NB);
@@ -458,7 +461,8 @@ std::vector<uint16_t> row_i2b(int NB) {
                 const int g = lane >> 4, x = lane & 15;
                 const int nt = jt >> 1, c = jt & 1, nb = nbmaph(NB, nt, x);
                 for (int j = 0; j < 8; ++j) {
-                    const int slot = 16 * ks + 8 * (j >> 2) + 2 * g + ((j >> 1) & 1);
+                    const int mt = split ? ks + KS * (j >> 2) : 2 * ks + (j >> 2);
+                    const int slot = 8 * mt + 2 * g + ((j >> 1) & 1);
                     const int kb = mid_perm(slot, NB), d = j & 1;
                     const double ang = 2.0 * M_PI * (double)((kb * nb) % NB) / (double)NB;
                     const double v = emb(cos(ang) * sc, sin(ang) * sc, c, d);
@@ -705,6 +709,13 @@ void free_plan(fftconv_plan_s* pl) {
 }
 
 fftconv_status build_mp_tables(fftconv_plan_s* pl);
+fftconv_status spectrum_impl(fftconv_plan_t plan, const float* k, size_t H,
+                             fftconv_kernel_kind kind, long long cutoff, void* k_f,
+                             void* stream);
+fftconv_status forward_impl(fftconv_plan_t plan, const void* u, const void* w,
+                            const void* v, const void* k_f, void* y, size_t B,
+                            size_t H, size_t N, void* workspace,
+                            size_t workspace_bytes, void* stream, int skip_hi);
 
 constexpr size_t kMpChunkBytes = (size_t)256 << 20;
 
@@ -824,7 +835,8 @@ fftconv_status build_device_tables(fftconv_plan_s* pl) {
     if (row_kernel_applies(s)) {
         const int NB = s.f[1];
         const bool bf = s.dtype == FFTCONV_BF16;
-        std::vector<uint16_t> f1b = row_f1b(bf), i1a = row_i1a(), i2b = row_i2b(NB);
+        std::vector<uint16_t> f1b = row_f1b(bf), i1a = row_i1a(), i2b = row_i2b(NB),
+                              i2bs = row_i2b(NB, true);
         std::vector<uint8_t> f2a = row_f2a(NB);
         std::vector<uint16_t> twf = row_twiddles(NB, false), twi = row_twiddles(NB, true);
         RowParams& R = pl->row;
@@ -842,6 +854,8 @@ fftconv_status build_device_tables(fftconv_plan_s* pl) {
         R.i1a = d;
         if (upload(pl, i2b.data(), i2b.size() * 2, &d) != hipSuccess) return FFTCONV_ERR_HIP;
         R.i2b = d;
+        if (upload(pl, i2bs.data(), i2bs.size() * 2, &d) != hipSuccess) return FFTCONV_ERR_HIP;
+        R.i2bs = d;
         if (upload(pl, f2a.data(), f2a.size(), &d) != hipSuccess) return FFTCONV_ERR_HIP;
         R.f2a = d;
         if (upload(pl, twf.data(), twf.size() * 2, &d) != hipSuccess) return FFTCONV_ERR_HIP;
@@ -1123,6 +1137,26 @@ fftconv_status fftconv_kernel_spectrum(fftconv_plan_t plan, const float* k,
 fftconv_status fftconv_kernel_spectrum_kind(fftconv_plan_t plan, const float* k,
                                             size_t H, fftconv_kernel_kind kind,
                                             void* k_f, void* stream) {
+    return spectrum_impl(plan, k, H, kind, -1, k_f, stream);
+}
+
+fftconv_status fftconv_kernel_spectrum_lowpass(fftconv_plan_t plan, const float* k,
+                                               size_t H, size_t cutoff, void* k_f,
+                                               void* stream) {
+    if (!plan) return FFTCONV_ERR_INVALID_ARG;
+    if (cutoff > plan->s.N) return FFTCONV_ERR_INVALID_ARG;
+    return spectrum_impl(plan, k, H, FFTCONV_CAUSAL, (long long)cutoff, k_f, stream);
+}
+
+}  // extern "C"
+
+namespace {
+
+// Kernel spectrum of operator `kind`, band-limited to frequencies within
+// `cutoff` of zero when cutoff >= 0.
+fftconv_status spectrum_impl(fftconv_plan_t plan, const float* k, size_t H,
+                             fftconv_kernel_kind kind, long long cutoff, void* k_f,
+                             void* stream) {
     if (!plan) return FFTCONV_ERR_INVALID_ARG;
     if ((int)kind < 0 || (int)kind > 3) return FFTCONV_ERR_INVALID_ARG;
     if (H == 0) return FFTCONV_OK;
@@ -1158,6 +1192,7 @@ fftconv_status fftconv_kernel_spectrum_kind(fftconv_plan_t plan, const float* k,
             a = b;
             b = t;
         }
+        if (e == hipSuccess && cutoff >= 0) e = launch_band_limit(a, cnt, (int)L, (int)cutoff, st);
         if (e != hipSuccess) break;
         if (s.mp_P1) {
             MpCoefParams mp{};
@@ -1200,16 +1235,12 @@ fftconv_status fftconv_kernel_spectrum_kind(fftconv_plan_t plan, const float* k,
     return FFTCONV_OK;
 }
 
-}  // extern "C"
-
-namespace {
-
 // Shared body of the plain and the gated forward call; w and v are both
 // null (plain) or both set (gated), which the callers guarantee.
 fftconv_status forward_impl(fftconv_plan_t plan, const void* u, const void* w,
                             const void* v, const void* k_f, void* y, size_t B,
                             size_t H, size_t N, void* workspace,
-                            size_t workspace_bytes, void* stream) {
+                            size_t workspace_bytes, void* stream, int skip_hi) {
     if (!plan) return FFTCONV_ERR_INVALID_ARG;
     const Shape& s = plan->s;
     if (N != s.N) return FFTCONV_ERR_INVALID_ARG;
@@ -1263,6 +1294,7 @@ fftconv_status forward_impl(fftconv_plan_t plan, const void* u, const void* w,
         R.kf = k_f;
         R.w = w;
         R.v = v;
+        R.skip_hi = skip_hi;
         e = launch_row(io, plan->row_nb, R, plan->lds_row, st);
     } else if (s.mp_P1) {
         const size_t hc_max = mp_chunk_channels(s, B, H);
@@ -1404,7 +1436,20 @@ fftconv_status fftconv_forward(fftconv_plan_t plan, const void* u,
                                size_t N, void* workspace,
                                size_t workspace_bytes, void* stream) {
     return forward_impl(plan, u, nullptr, nullptr, k_f, y, B, H, N, workspace,
-                        workspace_bytes, stream);
+                        workspace_bytes, stream, 0);
+}
+
+fftconv_status fftconv_forward_lowpass(fftconv_plan_t plan, const void* u,
+                                       const void* k_f, size_t cutoff, void* y,
+                                       size_t B, size_t H, size_t N, void* workspace,
+                                       size_t workspace_bytes, void* stream) {
+    if (!plan) return FFTCONV_ERR_INVALID_ARG;
+    if (cutoff > plan->s.N) return FFTCONV_ERR_INVALID_ARG;
+    // the row kernel at N = 32 x 32 skips the tiles of k_b = 8..23, whose
+    // packed bins k in [256, 768) all lie beyond a cutoff below M/4
+    const int skip = (plan->use_row && plan->row_nb == 32 && cutoff < plan->s.M / 4) ? 1 : 0;
+    return forward_impl(plan, u, nullptr, nullptr, k_f, y, B, H, N, workspace,
+                        workspace_bytes, stream, skip);
 }
 
 fftconv_status fftconv_forward_gated(fftconv_plan_t plan, const void* u,
@@ -1414,7 +1459,7 @@ fftconv_status fftconv_forward_gated(fftconv_plan_t plan, const void* u,
                                      size_t workspace_bytes, void* stream) {
     if (B * H != 0 && (!w || !v)) return FFTCONV_ERR_INVALID_ARG;
     return forward_impl(plan, u, w, v, k_f, y, B, H, N, workspace,
-                        workspace_bytes, stream);
+                        workspace_bytes, stream, 0);
 }
 
 fftconv_status fftconv_backward(fftconv_plan_t plan, const void* u,
@@ -1458,7 +1503,7 @@ fftconv_status fftconv_backward(fftconv_plan_t plan, const void* u,
     // conjugate spectrum); validated like any forward call
     if (du) {
         const fftconv_status fs = forward_impl(plan, dy, nullptr, nullptr, k_f_adj, du, B, H,
-                                               N, workspace, workspace_bytes, stream);
+                                               N, workspace, workspace_bytes, stream, 0);
         if (fs != FFTCONV_OK) return fs;
     }
     if (!dk || H == 0) return FFTCONV_OK;

@@ -132,6 +132,8 @@ struct SpecParams {
 // Register-resident row kernel (N = 32 * NB, NB = 16 or 32, 16-bit I/O).
 struct RowParams {
     int B, H, N;
+    int skip_hi;             // band limit below M/4 (NB = 32): skip the
+                             // matrix-core tiles of k_b = 8..23
     long long rows_per_wg;   // contiguous slice of channel-major rows
     int grid;                // workgroups
     const void* u;
@@ -144,6 +146,7 @@ struct RowParams {
     const void* i1a;    // last inverse stage, A-operand tiles [2][2][64]
     const void* f2a;    // inner forward stage, A-operand tiles
     const void* i2b;    // inner inverse stage, B-operand tiles
+    const void* i2bs;   // the same with the band-limited K-step grouping
     const uint32_t* twf;  // per-lane forward twiddles (packed f16 re, im)
     const uint32_t* twi;  // per-lane inverse twiddles (packed f16 re, im)
 };
@@ -273,6 +276,7 @@ hipError_t launch_outer_inv(int io, const FwdParams& p, int lds_bytes,
                             hipStream_t s);
 hipError_t launch_kpad(const float* k, float2* X, int hcount, int N, int kind,
                        hipStream_t s);
+hipError_t launch_band_limit(float2* X, int hcount, int L, int F, hipStream_t s);
 hipError_t launch_stockham(const float2* in, float2* out, int hcount, int L,
                            int Ns, hipStream_t s);
 hipError_t launch_alphabeta(int io, const SpecParams& p, hipStream_t s);

@@ -1043,6 +1043,17 @@ __global__ void kpad_kernel(const float* __restrict__ k, float2* __restrict__ X,
     }
 }
 
+// Band limit of kernel spectra: X[h][f] = 0 where min(f, L - f) > F.
+__global__ void band_limit_kernel(float2* __restrict__ X, int hcount, int L, int F) {
+    const long long total = (long long)hcount * L;
+    for (long long i = blockIdx.x * (long long)blockDim.x + threadIdx.x; i < total;
+         i += (long long)gridDim.x * blockDim.x) {
+        const int f = (int)(i % L);
+        const int dist = f < L - f ? f : L - f;
+        if (dist > F) X[i] = make_float2(0.f, 0.f);
+    }
+}
+
 // One radix-2 Stockham pass: sub-transforms of length Ns are combined into
 // length 2Ns; natural-order output after log2(L) passes.
 __global__ void stockham_kernel(const float2* __restrict__ in,
@@ -1161,6 +1172,11 @@ hipError_t launch_outer_inv(int io, const FwdParams& p, int lds, hipStream_t s) 
 hipError_t launch_kpad(const float* k, float2* X, int hcount, int N, int kind,
                        hipStream_t s) {
     hipLaunchKernelGGL(kpad_kernel, dim3(1024), dim3(256), 0, s, k, X, hcount, N, kind);
+    return hipGetLastError();
+}
+
+hipError_t launch_band_limit(float2* X, int hcount, int L, int F, hipStream_t s) {
+    hipLaunchKernelGGL(band_limit_kernel, dim3(1024), dim3(256), 0, s, X, hcount, L, F);
     return hipGetLastError();
 }
 

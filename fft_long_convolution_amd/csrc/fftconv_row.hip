@@ -49,7 +49,7 @@ namespace fftconv {
 // take the workgroup down to twelve waves.
 constexpr int kRowDepth = 2;
 
-template <int IO, int NB, bool G>
+template <int IO, int NB, bool G, bool SK>
 __global__ void __launch_bounds__(64 * (G ? kRowWavesGated : kRowWaves), 1)
 row_kernel(RowParams P) {
     constexpr int WAVES = G ? kRowWavesGated : kRowWaves;
@@ -76,6 +76,8 @@ row_kernel(RowParams P) {
     const int tid = threadIdx.x, lane = tid & 63;
     // wave index as a scalar: branches on it stay uniform (scalar branches)
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    // band limit below M/4: the M-tiles of k_b = 8..23 are all zero
+    constexpr bool skip_hi = SK && NB == 32;
     const int g = lane >> 4, x = lane & 15;
     const long long total = (long long)P.B * P.H;
     const long long r0 = (long long)blockIdx.x * P.rows_per_wg;
@@ -87,7 +89,8 @@ row_kernel(RowParams P) {
     for (int i = tid; i < F1T * 64; i += TH) s_f1b[i] = f1src[i];
     for (int i = tid; i < 4 * 64; i += TH) s_i1a[i] = ((const uint4*)P.i1a)[i];
     for (int i = tid; i < MT2 * KS2 * 64; i += TH) s_f2a[i] = ((const uint4*)P.f2a)[i];
-    for (int i = tid; i < KS2 * 2 * NT * 64; i += TH) s_i2b[i] = ((const uint4*)P.i2b)[i];
+    const uint4* i2src = (const uint4*)(skip_hi ? P.i2bs : P.i2b);
+    for (int i = tid; i < KS2 * 2 * NT * 64; i += TH) s_i2b[i] = i2src[i];
     if (tid == 0) s_ctr[0] = 0;
     constexpr bool SYM = (NB == 32);
     uint32_t twf[IT][2][4], twi[SYM ? 1 : 2][SYM ? 1 : NT][4];
@@ -255,11 +258,17 @@ row_kernel(RowParams P) {
                 }
             }
             // ---- F2: NB-point DFT over n_b, k_b in-lane (rows permuted)
+            // (under a band limit below M/4 the odd M-tiles -- k_b 8..23, the
+            // highest frequencies -- hold only zeroed bins: not computed)
             uint32_t z[2][MT2][2];
 #pragma unroll
             for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
                 for (int mt = 0; mt < MT2; ++mt) {
+                    if (skip_hi && (mt & 1)) {
+                        z[kt][mt][0] = z[kt][mt][1] = 0u;
+                        continue;
+                    }
                     rfloat4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                     for (int ks = 0; ks < KS2; ++ks) acc = mma_f16(s_f2a[(mt * KS2 + ks) * 64 + lane], b2[ks][kt], acc);
@@ -298,6 +307,10 @@ row_kernel(RowParams P) {
                 for (int mt = 0; mt < MT2; ++mt)
 #pragma unroll
                     for (int e = 0; e < 2; ++e) {
+                        if (skip_hi && (mt & 1)) {
+                            zp[mt][e] = 0u;
+                            continue;
+                        }
                         const int pm = (mt + MT2 / 2) % MT2;
                         const uint2 ab = s_ab[abbase + ((kt * MT2 + mt) * 2 + e) * 64 + lane];
                         uint32_t p;
@@ -309,11 +322,14 @@ row_kernel(RowParams P) {
                         zp[mt][e] = as_u32(hpair(as_h2(ab.x), as_h2(z[kt][mt][e]),
                                                  as_h2(ab.y), as_h2(p)));
                     }
-                // I2's A operand (K = k_b in accumulator order)
+                // I2's A operand (K = k_b in accumulator order): K-step ks
+                // holds M-tiles 2 ks and 2 ks + 1, or, band-limited, ks and
+                // ks + KS2 (then K-step 1 is all zero)
 #pragma unroll
-                for (int ks = 0; ks < KS2; ++ks)
-                    a2[kt][ks] = make_uint4(zp[2 * ks][0], zp[2 * ks][1],
-                                            zp[2 * ks + 1][0], zp[2 * ks + 1][1]);
+                for (int ks = 0; ks < KS2; ++ks) {
+                    const int m0 = skip_hi ? ks : 2 * ks, m1 = skip_hi ? ks + KS2 : 2 * ks + 1;
+                    a2[kt][ks] = make_uint4(zp[m0][0], zp[m0][1], zp[m1][0], zp[m1][1]);
+                }
             }
             // ---- I2: inverse NB-point DFT over k_b (data as A), k_a in-lane
             uint4 b1v[2][NT];
@@ -324,6 +340,7 @@ row_kernel(RowParams P) {
                     rfloat4 re = {0.f, 0.f, 0.f, 0.f}, im = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                     for (int ks = 0; ks < KS2; ++ks) {
+                        if (skip_hi && ks == 1) continue;
                         re = mma_f16(a2[kt][ks], s_i2b[(ks * 2 * NT + 2 * nt) * 64 + lane], re);
                         im = mma_f16(a2[kt][ks], s_i2b[(ks * 2 * NT + 2 * nt + 1) * 64 + lane], im);
                     }
@@ -398,14 +415,14 @@ row_kernel(RowParams P) {
     }
 }
 
-template <int IO, int NB, bool G>
+template <int IO, int NB, bool G, bool SK>
 static hipError_t launch_row_t(const RowParams& p, int lds, hipStream_t s) {
     if (lds > 64 * 1024) {
-        const hipError_t e = hipFuncSetAttribute((const void*)row_kernel<IO, NB, G>,
+        const hipError_t e = hipFuncSetAttribute((const void*)row_kernel<IO, NB, G, SK>,
                                                  hipFuncAttributeMaxDynamicSharedMemorySize, lds);
         if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL((row_kernel<IO, NB, G>), dim3((unsigned)p.grid),
+    hipLaunchKernelGGL((row_kernel<IO, NB, G, SK>), dim3((unsigned)p.grid),
                        dim3(64 * (G ? kRowWavesGated : kRowWaves)), lds, s, p);
     return hipGetLastError();
 }
@@ -413,12 +430,21 @@ static hipError_t launch_row_t(const RowParams& p, int lds, hipStream_t s) {
 template <bool G>
 static hipError_t launch_row_g(int io, int nb, const RowParams& p, int lds, hipStream_t s) {
     if (io == IO_BF16)
-        return nb == 32 ? launch_row_t<IO_BF16, 32, G>(p, lds, s) : launch_row_t<IO_BF16, 16, G>(p, lds, s);
-    return nb == 32 ? launch_row_t<IO_F16, 32, G>(p, lds, s) : launch_row_t<IO_F16, 16, G>(p, lds, s);
+        return nb == 32 ? launch_row_t<IO_BF16, 32, G, false>(p, lds, s)
+                        : launch_row_t<IO_BF16, 16, G, false>(p, lds, s);
+    return nb == 32 ? launch_row_t<IO_F16, 32, G, false>(p, lds, s)
+                    : launch_row_t<IO_F16, 16, G, false>(p, lds, s);
 }
 
 hipError_t launch_row(int io, int nb, const RowParams& p, int lds, hipStream_t s) {
-    return p.w ? launch_row_g<true>(io, nb, p, lds, s) : launch_row_g<false>(io, nb, p, lds, s);
+    if (p.w) return launch_row_g<true>(io, nb, p, lds, s);
+    if (p.skip_hi) {
+        // band-limited rows (N = 1024 only)
+        if (nb != 32) return hipErrorInvalidValue;
+        return io == IO_BF16 ? launch_row_t<IO_BF16, 32, false, true>(p, lds, s)
+                             : launch_row_t<IO_F16, 32, false, true>(p, lds, s);
+    }
+    return launch_row_g<false>(io, nb, p, lds, s);
 }
 
 }  // namespace fftconv

@@ -87,6 +87,11 @@ def lib() -> ctypes.CDLL:
         L.fftconv_workspace_bytes.restype = sz
         L.fftconv_kernel_spectrum.argtypes = [vp, vp, sz, vp, vp]
         L.fftconv_kernel_spectrum.restype = i
+        L.fftconv_kernel_spectrum_lowpass.argtypes = [vp, vp, sz, sz, vp, vp]
+        L.fftconv_kernel_spectrum_lowpass.restype = i
+        L.fftconv_forward_lowpass.argtypes = [vp, vp, vp, sz, vp, sz, sz, sz,
+                                              vp, sz, vp]
+        L.fftconv_forward_lowpass.restype = i
         L.fftconv_kernel_spectrum_kind.argtypes = [vp, vp, sz, i, vp, vp]
         L.fftconv_kernel_spectrum_kind.restype = i
         L.fftconv_forward.argtypes = [vp, vp, vp, vp, sz, sz, sz, vp, sz, vp]
@@ -170,6 +175,39 @@ class FFTConv:
 
     def workspace_bytes(self, B: int, H: int) -> int:
         return int(lib().fftconv_workspace_bytes(self._plan, B, H))
+
+    def kernel_spectrum_lowpass(self, k, cutoff: int, out=None, stream=None):
+        """Band-limited spectrum of the causal kernel k ([H, N] fp32): kept
+        at frequencies within `cutoff` of zero (of the 2N-point transform)."""
+        import torch
+        if k.dtype != torch.float32 or k.dim() != 2 or k.shape[1] != self.N:
+            raise ValueError("k must be fp32 [H, %d]" % self.N)
+        k = k.contiguous()
+        H = k.shape[0]
+        nb = self.spectrum_bytes(H)
+        if out is None:
+            out = torch.empty(nb, dtype=torch.uint8, device=k.device)
+        st = lib().fftconv_kernel_spectrum_lowpass(self._plan, k.data_ptr(), H,
+                                                   int(cutoff), out.data_ptr(),
+                                                   _stream_handle(stream))
+        if st != 0:
+            raise FFTConvError(st, "fftconv_kernel_spectrum_lowpass")
+        return out
+
+    def forward_lowpass(self, u, k_f, cutoff: int, out=None, workspace=None,
+                        stream=None):
+        """The frequency-sparse convolution (k_f from kernel_spectrum_lowpass
+        with the same cutoff)."""
+        u = u.contiguous()
+        out, ws_ptr, ws_bytes = self._prepare(u, out, workspace)
+        B, H, N = u.shape
+        st = lib().fftconv_forward_lowpass(self._plan, u.data_ptr(),
+                                           k_f.data_ptr(), int(cutoff),
+                                           out.data_ptr(), B, H, N, ws_ptr,
+                                           ws_bytes, _stream_handle(stream))
+        if st != 0:
+            raise FFTConvError(st, "fftconv_forward_lowpass")
+        return out
 
     def kernel_spectrum(self, k, out=None, stream=None, kind="causal"):
         """k: [H, N] fp32 CUDA tensor -> opaque k_f (uint8 CUDA tensor).

@@ -164,6 +164,19 @@ fftconv_status fftconv_kernel_spectrum_kind(fftconv_plan_t plan, const float *k,
                                             size_t H, fftconv_kernel_kind kind,
                                             void *k_f, void *stream);
 
+/* Frequency-sparse (band-limited) kernel spectrum (page "FlashFFTConv:
+ * Efficient Convolutions for Long Sequences with Tensor Cores", section 3:
+ * zeroing part of the frequency-domain kernel, the convolutional analogue
+ * of low-pass filtering, lets the kernels skip the matrix-product blocks
+ * whose bins are all zero).  The causal kernel's 2N-point spectrum is kept
+ * at frequencies f with min(f, 2N - f) <= cutoff and zeroed elsewhere
+ * (sparsity 1 - (2 cutoff + 1) / 2N for cutoff < N; cutoff = N keeps
+ * everything).  cutoff > N -> FFTCONV_ERR_INVALID_ARG; otherwise as
+ * fftconv_kernel_spectrum. */
+fftconv_status fftconv_kernel_spectrum_lowpass(fftconv_plan_t plan, const float *k,
+                                               size_t H, size_t cutoff, void *k_f,
+                                               void *stream);
+
 /* Causal long convolution y = (u * k)[0:N] for all B x H rows.
  *  u: device, plan dtype, [B][H][N] contiguous, 16-B aligned.
  *  k_f: device, from fftconv_kernel_spectrum with the same plan and H.
@@ -179,6 +192,18 @@ fftconv_status fftconv_forward(fftconv_plan_t plan, const void *u,
                                const void *k_f, void *y, size_t B, size_t H,
                                size_t N, void *workspace,
                                size_t workspace_bytes, void *stream);
+
+/* fftconv_forward for a spectrum from fftconv_kernel_spectrum_lowpass with
+ * the same cutoff: the frequency-sparse convolution.  Kernels may skip the
+ * blocks whose bins the cutoff zeroes (the register-resident kernel at
+ * N = 1024 skips half of its innermost matrix products and pairing work when
+ * cutoff < N/4); other kernels compute the zero bins.  A spectrum built with
+ * a larger cutoff (or none) is not valid here.  Arguments and errors as
+ * fftconv_forward; cutoff > N -> FFTCONV_ERR_INVALID_ARG. */
+fftconv_status fftconv_forward_lowpass(fftconv_plan_t plan, const void *u,
+                                       const void *k_f, size_t cutoff, void *y,
+                                       size_t B, size_t H, size_t N, void *workspace,
+                                       size_t workspace_bytes, void *stream);
 
 /* Gated causal long convolution, y = v (.) ((u (.) w) * k)[0:N], for all
  * B x H rows: the input gate w multiplies u element-wise before the

@@ -1,0 +1,72 @@
+"""GPU parity of the frequency-sparse (band-limited) convolution:
+fftconv_kernel_spectrum_lowpass + fftconv_forward_lowpass against the fp64
+oracle's band-limited FFT route.  At N = 1024 a cutoff below N/4 runs the
+register-resident kernel's variant that skips the matrix-core tiles of the
+zeroed bins; other lengths compute the zero bins."""
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+from fft_long_convolution_amd import inputs
+from tests.gpu_helpers import TOL, from_torch, to_torch
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def _run(w, cutoff):
+    import torch
+    from fft_long_convolution_amd.fftconv import FFTConv
+    conv = FFTConv(w.N, dtype=w.dtype)
+    u = inputs.input_rows(w)
+    k = inputs.kernel_rows(w)
+    kf = conv.kernel_spectrum_lowpass(torch.from_numpy(k).cuda(), cutoff)
+    y = conv.forward_lowpass(to_torch(u, w.dtype).view(w.B, w.H, w.N), kf, cutoff)
+    torch.cuda.synchronize()
+    got = oracle.to_f64(from_torch(y, w.dtype).reshape(w.rows, w.N), w.dtype)
+    ref = oracle.lowpass_fft(oracle.to_f64(u, w.dtype).reshape(w.rows, w.N),
+                             k.astype(np.float64), cutoff, np.arange(w.rows) % w.H)
+    return oracle.rel_l2(got, ref)
+
+
+@pytest.mark.parametrize("N,dtype,B,H,cutoff", [
+    (256, "f32", 1, 4, 40), (512, "f16", 3, 5, 100),
+    (1024, "bf16", 3, 5, 255), (1024, "f16", 64, 3, 128),
+    (1024, "bf16", 2, 7, 31), (1024, "bf16", 3, 5, 256),
+    (1024, "f16", 3, 5, 700), (8192, "bf16", 2, 3, 1000),
+    (65536, "f16", 1, 3, 20000), (4194304, "bf16", 1, 1, 500000)])
+def test_lowpass(N, dtype, B, H, cutoff):
+    w = inputs.Workload("lowpass", 260 + N.bit_length() + B, B, H, N, dtype,
+                        "normal", "decay", "band-limited")
+    err = _run(w, cutoff)
+    _say("lowpass", N, dtype, B, H, cutoff, "rel_l2", err)
+    assert err < TOL[dtype]
+
+
+def test_lowpass_full_size_hyena():
+    # 75% sparsity (cutoff 255 of N = 1024: 511 of 2048 frequencies kept)
+    err = _run(inputs.WORKLOADS["hyena_bf16_n1k"], 255)
+    _say("lowpass full-size hyena rel_l2", err)
+    assert err < TOL["bf16"]
+
+
+def test_lowpass_errors():
+    import torch
+    from fft_long_convolution_amd import fftconv as fc
+    conv = fc.FFTConv(1024, dtype="bf16")
+    L = fc.lib()
+    k = torch.randn(2, 1024, device="cuda")
+    kf = torch.empty(conv.spectrum_bytes(2), dtype=torch.uint8, device="cuda")
+    assert L.fftconv_kernel_spectrum_lowpass(conv._plan, k.data_ptr(), 2, 1025,
+                                             kf.data_ptr(), None) == 1
+    u = torch.randn(1, 2, 1024, device="cuda").to(torch.bfloat16)
+    y = torch.empty_like(u)
+    assert L.fftconv_forward_lowpass(conv._plan, u.data_ptr(), kf.data_ptr(), 1025,
+                                     y.data_ptr(), 1, 2, 1024, None, 0, None) == 1
+    torch.cuda.synchronize()
