@@ -717,7 +717,7 @@ fftconv_status forward_impl(fftconv_plan_t plan, const void* u, const void* w,
                             size_t H, size_t N, void* workspace,
                             size_t workspace_bytes, void* stream, int skip_hi);
 
-constexpr size_t kMpChunkBytes = (size_t)256 << 20;
+constexpr size_t kMpChunkBytes = (size_t)1024 << 20;
 
 fftconv_status build_device_tables(fftconv_plan_s* pl) {
     const Shape& s = pl->s;
@@ -1029,10 +1029,21 @@ int kgrad_lds(const Shape& g) {
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
 // Channels per chunk of the multi-pass path: the passes run chunk by chunk
-// so the chunk's workspace (B * hc * M f16 complex) stays in the 256 MB
-// Infinity Cache between the pass that writes it and the one that reads it.
+// to bound the workspace (B * hc * M f16 complex, at most 1 GB).  Every
+// chunk costs three launches with their ramp-up and tail; measured at
+// N = 4M, 256 MB chunks (small enough for the Infinity Cache) ran 5%
+// slower than 1 GB ones, so the cache does not decide the size.
+// Batch rows per chunk: all of them unless one channel's rows alone exceed
+// the bound (then the chunk is one channel of a slice of the batch).
+size_t mp_chunk_batch(const Shape& s, size_t B) {
+    size_t bc = kMpChunkBytes / (s.M * 4);
+    if (bc < 1) bc = 1;
+    return B < bc ? (B ? B : 1) : bc;
+}
+
 size_t mp_chunk_channels(const Shape& s, size_t B, size_t H) {
-    const size_t per_ch = (B ? B : 1) * s.M * 4;
+    B = mp_chunk_batch(s, B);
+    const size_t per_ch = B * s.M * 4;
     size_t hc = kMpChunkBytes / per_ch;
     if (hc < 1) hc = 1;
     if (hc > H) hc = H;
@@ -1125,7 +1136,9 @@ size_t fftconv_workspace_bytes(fftconv_plan_t plan, size_t B, size_t H) {
     if (plan->s.wide_P) return kClaimBytes;
     if (plan->s.path == 0) return 0;
     // multi-pass: one channel chunk of f16 complex rows, then the counters
-    if (plan->s.mp_P1) return B * mp_chunk_channels(plan->s, B, H) * plan->s.M * 4 + kClaimBytes;
+    if (plan->s.mp_P1)
+        return mp_chunk_batch(plan->s, B) * mp_chunk_channels(plan->s, B, H) * plan->s.M * 4 +
+               kClaimBytes;
     return B * H * plan->s.M * 8;
 }
 
@@ -1298,6 +1311,7 @@ fftconv_status forward_impl(fftconv_plan_t plan, const void* u, const void* w,
         e = launch_row(io, plan->row_nb, R, plan->lds_row, st);
     } else if (s.mp_P1) {
         const size_t hc_max = mp_chunk_channels(s, B, H);
+        const size_t bc_max = mp_chunk_batch(s, B);
         MpColParams C1{};
         C1.H = (int)H;
         C1.M = (int)s.M;
@@ -1318,13 +1332,24 @@ fftconv_status forward_impl(fftconv_plan_t plan, const void* u, const void* w,
         I.ws = workspace;
         I.ctr = C1.ctr;
         I.kf = k_f;
-        if ((long long)B * (long long)hc_max * (I.Po / 2) > 0x7fffffffLL) return FFTCONV_ERR_UNSUPPORTED;
+        if ((long long)bc_max * (long long)hc_max * (I.Po / 2) > 0x7fffffffLL)
+            return FFTCONV_ERR_UNSUPPORTED;
         e = hipSuccess;
+        // chunks of bc_max batch rows x hc_max channels: the passes address
+        // rows relative to the chunk's first batch row
+        const size_t row_bytes = H * N * esz;
+        for (size_t b0 = 0; b0 < B && e == hipSuccess; b0 += bc_max)
         for (size_t h0 = 0; h0 < H && e == hipSuccess; h0 += hc_max) {
+            const size_t bcur = B - b0 < bc_max ? B - b0 : bc_max;
             const size_t hc = H - h0 < hc_max ? H - h0 : hc_max;
+            C1.u = C2.u = (const char*)u + b0 * row_bytes;
+            C1.y = C2.y = (char*)y + b0 * row_bytes;
+            C1.w = C2.w = w ? (const char*)w + b0 * row_bytes : nullptr;
+            C1.v = C2.v = v ? (const char*)v + b0 * row_bytes : nullptr;
+            I.B = (int)bcur;
             C1.h0 = C2.h0 = I.h0 = (int)h0;
             C1.hc = C2.hc = I.hc = (int)hc;
-            C1.rows = C2.rows = (long long)B * (long long)hc;
+            C1.rows = C2.rows = (long long)bcur * (long long)hc;
             const long long units = C1.rows * (I.Po / 2);
             long long G = 2LL * plan->num_cu;
             G = G < 8 ? 8 : G & ~7LL;
@@ -1340,10 +1365,10 @@ fftconv_status forward_impl(fftconv_plan_t plan, const void* u, const void* w,
                 D.M = C1.M;
                 D.tw1 = C1.tw;
                 D.tw2 = C2.tw;
-                D.u = u;
-                D.y = y;
-                D.w = w;
-                D.v = v;
+                D.u = C1.u;
+                D.y = C1.y;
+                D.w = C1.w;
+                D.v = C1.v;
                 D.ws = workspace;
                 D.ctr = C1.ctr;
                 // persistent workgroups, two per CU, a multiple of 16 (the

@@ -9,7 +9,8 @@ import numpy as np
 import pytest
 
 from fft_long_convolution_amd import inputs
-from tests.gpu_helpers import TOL, oracle_rows, parity, run_gpu
+from tests.gpu_helpers import TOL, from_torch, oracle_rows, parity, run_gpu, to_torch
+import oracle
 
 pytestmark = pytest.mark.gpu
 
@@ -178,3 +179,33 @@ def test_deterministic_and_stream(N):
         y2 = conv.forward(u, kf)
     torch.cuda.synchronize()
     assert torch.equal(y1.view(torch.int16), y2.view(torch.int16))
+
+
+@pytest.mark.parametrize("N,B,dtype", [(1048576, 257, "f16"), (4194304, 65, "bf16")])
+def test_multipass_batch_chunks(N, B, dtype):
+    # one channel's rows exceed the 1 GB workspace chunk: the passes run over
+    # slices of the batch; rows on both sides of a slice boundary are checked
+    # by the definition
+    import torch
+    from fft_long_convolution_amd.fftconv import FFTConv
+    w = inputs.Workload("bchunk", 120 + N.bit_length(), B, 1, N, dtype,
+                        "normal", "decay", "batch chunks")
+    conv = FFTConv(N, dtype=dtype)
+    u = inputs.input_rows(w)
+    k = inputs.kernel_rows(w)
+    kf = conv.kernel_spectrum(torch.from_numpy(k).cuda())
+    y = conv.forward(to_torch(u, dtype).view(B, 1, N), kf)
+    torch.cuda.synchronize()
+    slice_rows = (1 << 30) // (N * 4)
+    rows = np.array([0, slice_rows - 1, slice_rows, B - 1])
+    got = oracle.to_f64(from_torch(y, dtype).reshape(B, N)[rows], dtype)
+    del y
+    rng = np.random.default_rng(5)
+    ts = np.concatenate([[0, N - 1], rng.integers(0, N, 30)])
+    rr = np.repeat(np.arange(len(rows)), len(ts))
+    tt = np.tile(ts, len(rows))
+    want = oracle.conv_points(oracle.to_f64(u[rows], dtype), k.astype(np.float64),
+                              rr, tt, np.zeros(len(rows), dtype=np.int64))
+    err = oracle.rel_l2(got[rr, tt], want)
+    _say("batch chunks", N, B, dtype, "sampled rel_l2", err)
+    assert err < 1.5 * TOL[dtype]
