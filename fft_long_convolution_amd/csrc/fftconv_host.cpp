@@ -1011,7 +1011,22 @@ int kgrad_splits(const fftconv_plan_s* pl, size_t B, size_t H) {
     return n < 1 ? 1 : (int)n;
 }
 
+// The row-engine kernel gradient (N = 1024, 16-bit I/O): batch slices per
+// channel so that the (channel, slice) waves cover the GPU a few times.
+bool kgrad_on_row(const fftconv_plan_s* pl) {
+    return pl->use_row && pl->row_nb == 32 && pl->s.dtype != FFTCONV_F32;
+}
+
+int kgrad_row_slices(const fftconv_plan_s* pl, size_t B, size_t H) {
+    if (B == 0 || H == 0) return 1;
+    long long n = (16LL * pl->num_cu + (long long)H - 1) / (long long)H;
+    if (n > (long long)B) n = (long long)B;
+    if (n > 64) n = 64;
+    return n < 1 ? 1 : (int)n;
+}
+
 size_t kgrad_workspace_bytes(const fftconv_plan_s* pl, size_t B, size_t H) {
+    if (kgrad_on_row(pl)) return (size_t)kgrad_row_slices(pl, B, H) * H * 64 * 32 * 4;
     const Shape& g = pl->grad->s;
     if (g.path == 0) {
         const int ns = kgrad_splits(pl, B, H);
@@ -1540,6 +1555,27 @@ fftconv_status fftconv_backward(fftconv_plan_t plan, const void* u,
         // an empty batch contributes nothing: dk = 0
         return launch_scale_f32(dk, (long long)(H * N), 0.f, st) == hipSuccess
                    ? FFTCONV_OK : FFTCONV_ERR_HIP;
+    }
+    if (kgrad_on_row(plan)) {
+        KgRowParams R{};
+        R.B = (int)B;
+        R.H = (int)H;
+        R.S = kgrad_row_slices(plan, B, H);
+        R.u = u;
+        R.dy = dy;
+        R.part = (float*)workspace;
+        R.dk = dk;
+        R.f1b = plan->row.f1b;
+        R.f2a = plan->row.f2a;
+        R.i2b = plan->row.i2b;
+        R.i1a = plan->row.i1a;
+        R.twf = plan->row.twf;
+        // accumulated 4 Z_g in unitary units: the inverse gets Z_g / sqrt(M),
+        // the output takes back the factor M (see the generic path)
+        R.pre = 0.25f / sqrtf((float)s.M);
+        R.post = (float)s.M;
+        e = launch_kgrad_row(io, R, st);
+        return e == hipSuccess ? FFTCONV_OK : FFTCONV_ERR_HIP;
     }
     KgradParams K{};
     K.B = (int)B;

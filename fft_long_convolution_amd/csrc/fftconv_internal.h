@@ -119,6 +119,25 @@ hipError_t launch_outer_inv_f32out(int io, const FwdParams& p, int lds_bytes,
                                    hipStream_t s);
 hipError_t launch_scale_f32(float* x, long long n, float a, hipStream_t s);
 
+// Kernel gradient on the row engine (N = 1024, 16-bit I/O,
+// fftconv_kgrad.hip): one wave per (channel, batch slice) accumulates the
+// packed gradient spectrum over its rows into part ([S][H][64 lanes][32]
+// fp32); one wave per channel sums the slices and inverts it into dk.
+struct KgRowParams {
+    int B, H, S;
+    const void* u;
+    const void* dy;
+    float* part;
+    float* dk;              // [H][1024] fp32
+    const void* f1b;        // the row plan's tables
+    const void* f2a;
+    const void* i2b;
+    const void* i1a;
+    const uint32_t* twf;
+    float pre, post;        // operand scale of the inverse, output scale
+};
+hipError_t launch_kgrad_row(int io, const KgRowParams& p, hipStream_t s);
+
 // Spectrum (alpha/beta) construction.
 struct SpecParams {
     int M, N, L;

@@ -1,0 +1,323 @@
+// Kernel gradient of the causal convolution on the register-resident
+// 32 x 32 engine (N = 1024, 16-bit I/O):
+//   dk[h][j] = sum_b sum_{t>=j} dy[b,h,t] u[b,h,t-j],
+// the inverse transform of G = sum_b conj(U_b) DY_b (page "FlashFFTConv:
+// Efficient Convolutions for Long Sequences with Tensor Cores", section 3:
+// the gradients of an FFT convolution multiply by conjugate spectra, and the
+// input spectra are recomputed in the backward pass instead of kept).
+//
+// kgrad_row_kernel: one wavefront per (channel, slice of the batch).  Each
+// row of u and of dy goes through the forward half of the row kernel (whole
+// 128-byte line loads, F1 with the twiddle, F2), which leaves bin
+// k = k_a + 32 k_b and its mirror -k in the same lane (the k_a = 0 column
+// through an LDS exchange).  With a = Z_u[k], c = conj Z_u[-k], d = Z_dy[k],
+// e = conj Z_dy[-k], E2 = a + c, O' = a - c, Ed2 = d + e, Od' = d - e and
+// w = W_2N^k, the packed spectrum of the real result is
+//   4 Z_g[k] = 2 conj(E2) d + conj(O') (Od' - conj(w)^2 Ed2):
+// the real-FFT unpack of both spectra, the products conj(U) DY at k and
+// k + M, and the repack, folded into three complex products (packed f16,
+// like the forward pairing).  The wave accumulates it
+// over its rows in fp32 registers and writes the lane's 16 bins to a
+// partial row.
+// kgrad_row_inv: one wavefront per channel sums the partial rows and runs
+// the inverse half of the engine (I2, twiddle, I1) into fp32 dk.
+#include "fftconv_mfma.h"
+
+namespace fftconv {
+
+constexpr int kKgWaves = 8;
+
+template <int IO>
+__global__ void __launch_bounds__(64 * kKgWaves, 1) kgrad_row_kernel(KgRowParams P) {
+    constexpr int NB = 32, IT = 2, MT2 = 4, KS2 = 2, M = 1024;
+    constexpr bool BF = (IO == IO_BF16);
+    constexpr int F1T = BF ? 8 : 4;
+    extern __shared__ uint4 s_lds[];
+    uint4* s_f1b = s_lds;                                   // [F1T][64]
+    uint4* s_f2a = s_f1b + F1T * 64;                        // [MT2][KS2][64]
+    uint32_t* s_scr = (uint32_t*)(s_f2a + MT2 * KS2 * 64);  // [waves][2][NB][16]
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int g = lane >> 4, x = lane & 15;
+    constexpr int TH = 64 * kKgWaves;
+    for (int i = tid; i < F1T * 64; i += TH) s_f1b[i] = ((const uint4*)P.f1b)[i];
+    for (int i = tid; i < MT2 * KS2 * 64; i += TH) s_f2a[i] = ((const uint4*)P.f2a)[i];
+    uint32_t twf[IT][2][4];
+#pragma unroll
+    for (int it = 0; it < IT; ++it)
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) twf[it][kt][r] = P.twf[lane * (IT * 8) + (it * 2 + kt) * 4 + r];
+    __syncthreads();
+    // no workgroup barrier below: a wave without a task may leave
+    const int task = blockIdx.x * kKgWaves + wave;
+    if (task >= P.H * P.S) return;
+    const int h = task / P.S, sl = task - h * P.S;
+    const int b0 = (int)((long long)P.B * sl / P.S), b1 = (int)((long long)P.B * (sl + 1) / P.S);
+
+    // conj(W_2N^k)^2 = exp(2 pi i k / M) of the lane's bins, packed f16
+    uint32_t wc[2][MT2][2];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int mt = 0; mt < MT2; ++mt)
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+                const int k = kmap32(kt, x) + 32 * rmid_perm(8 * mt + 2 * g + e, NB);
+                float sn, cs;
+                sincospif(2.f * (float)k / (float)M, &sn, &cs);
+                wc[kt][mt][e] = pk2(cs, sn);
+            }
+
+    auto load_row = [&](uint32_t (&dst)[IT][4], const void* base, int b) {
+        const uint32_t* r = (const uint32_t*)base + ((long long)b * P.H + h) * (M / 2);
+#pragma unroll
+        for (int q = 0; q < 8; ++q)
+            dst[q >> 2][q & 3] =
+                __builtin_nontemporal_load(&r[NB * (8 * (g >> 1) + q) + ((g & 1) ? kmap32(1, x) : x)]);
+    };
+    // F1 (with the twiddle) and F2 of one row: bins (kt, mt, e) as packed f16
+    auto forward = [&](uint32_t (&cur)[IT][4], uint32_t (&z)[2][MT2][2]) {
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) swap16(cur[0][jj], cur[1][jj]);
+        uint4 b2[KS2][2];
+#pragma unroll
+        for (int it = 0; it < IT; ++it) {
+            const uint4 a = make_uint4(cur[it][0], cur[it][1], cur[it][2], cur[it][3]);
+            rfloat4 c1[4];
+#pragma unroll
+            for (int jt = 0; jt < 4; ++jt) {
+                rfloat4 acc = {0.f, 0.f, 0.f, 0.f};
+                if (BF) {
+                    acc = mma_bf16(a, s_f1b[jt * 64 + lane], acc);
+                    acc = mma_bf16(a, s_f1b[(4 + jt) * 64 + lane], acc);
+                } else {
+                    acc = mma_f16(a, s_f1b[jt * 64 + lane], acc);
+                }
+                c1[jt] = acc;
+            }
+#pragma unroll
+            for (int kt = 0; kt < 2; ++kt) {
+                uint32_t w[4];
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    w[r] = as_u32(hmul(as_h2(pk2(c1[2 * kt][r], c1[2 * kt + 1][r])), as_h2(twf[it][kt][r])));
+                b2[it][kt] = make_uint4(w[0], w[1], w[2], w[3]);
+            }
+        }
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+            for (int mt = 0; mt < MT2; ++mt) {
+                rfloat4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int ks = 0; ks < KS2; ++ks) acc = mma_f16(s_f2a[(mt * KS2 + ks) * 64 + lane], b2[ks][kt], acc);
+                z[kt][mt][0] = pk2(acc[0], acc[1]);
+                z[kt][mt][1] = pk2(acc[2], acc[3]);
+            }
+    };
+    // bin -k_b of the k_a = 0 column, from the lane group that holds it
+    uint32_t* scr_u = s_scr + (wave * 2) * 16 * NB + x;
+    uint32_t* scr_d = scr_u + 16 * NB;
+    auto mirror0 = [&](const uint32_t (&z)[2][MT2][2], uint32_t* scr, uint32_t (&zq)[MT2][2]) {
+#pragma unroll
+        for (int mt = 0; mt < MT2; ++mt)
+#pragma unroll
+            for (int e = 0; e < 2; ++e) scr[16 * rmid_perm(8 * mt + 2 * g + e, NB)] = z[0][mt][e];
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+        for (int mt = 0; mt < MT2; ++mt)
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+                const int kb = rmid_perm(8 * mt + 2 * g + e, NB);
+                zq[mt][e] = scr[16 * ((NB - kb) & (NB - 1))];
+            }
+    };
+
+    float2 acc[2][MT2][2];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int mt = 0; mt < MT2; ++mt)
+#pragma unroll
+            for (int e = 0; e < 2; ++e) acc[kt][mt][e] = make_float2(0.f, 0.f);
+
+    const bool l0 = (x == 0);
+    uint32_t nu[IT][4], nd[IT][4];   // next row, in flight
+    if (b0 < b1) {
+        load_row(nu, P.u, b0);
+        load_row(nd, P.dy, b0);
+    }
+    for (int b = b0; b < b1; ++b) {
+        uint32_t cu[IT][4], cd[IT][4];
+#pragma unroll
+        for (int it = 0; it < IT; ++it)
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) {
+                cu[it][jj] = nu[it][jj];
+                cd[it][jj] = nd[it][jj];
+            }
+        // the next row (past the end: this row again, so every iteration
+        // issues the same loads)
+        const int bn = b + 1 < b1 ? b + 1 : b;
+        load_row(nu, P.u, bn);
+        load_row(nd, P.dy, bn);
+        uint32_t zu[2][MT2][2], zd[2][MT2][2], qu[MT2][2], qd[MT2][2];
+        forward(cu, zu);
+        forward(cd, zd);
+        mirror0(zu, scr_u, qu);
+        mirror0(zd, scr_d, qd);
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+            for (int mt = 0; mt < MT2; ++mt)
+#pragma unroll
+                for (int e = 0; e < 2; ++e) {
+                    const int pm = (mt + MT2 / 2) % MT2;
+                    uint32_t pu, pd;
+                    if (kt == 0) {
+                        pu = l0 ? qu[mt][e] : zu[1][pm][e];
+                        pd = l0 ? qd[mt][e] : zd[1][pm][e];
+                    } else {
+                        pu = l0 ? zu[1][pm][e] : zu[0][pm][e];
+                        pd = l0 ? zd[1][pm][e] : zd[0][pm][e];
+                    }
+                    const rhalf2 A = as_h2(zu[kt][mt][e]), Ap = as_h2(pu);
+                    const rhalf2 Dv = as_h2(zd[kt][mt][e]), Dp = as_h2(pd);
+                    const rhalf2 cAp = {Ap.x, -Ap.y}, cDp = {Dp.x, -Dp.y};
+                    const rhalf2 E2 = A + cAp, O2 = A - cAp;
+                    const rhalf2 Ed = Dv + cDp, Od = Dv - cDp;
+                    const rhalf2 T = Od - hmul(Ed, as_h2(wc[kt][mt][e]));
+                    const rhalf2 two = {(_Float16)2.f, (_Float16)2.f};
+                    const rhalf2 R = __builtin_elementwise_fma(hmulc(Dv, E2), two, hmulc(T, O2));
+                    acc[kt][mt][e].x += (float)R.x;
+                    acc[kt][mt][e].y += (float)R.y;
+                }
+    }
+    float4* o = (float4*)P.part + ((long long)(sl * P.H + h) * 64 + lane) * 8;
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int mt = 0; mt < MT2; ++mt)
+            o[kt * MT2 + mt] = make_float4(acc[kt][mt][0].x, acc[kt][mt][0].y, acc[kt][mt][1].x,
+                                           acc[kt][mt][1].y);
+}
+
+template <int IO>
+__global__ void __launch_bounds__(64 * kKgWaves, 1) kgrad_row_inv_kernel(KgRowParams P) {
+    constexpr int NB = 32, MT2 = 4, KS2 = 2, NT = 2, IT = 2;
+    extern __shared__ uint4 s_lds[];
+    uint4* s_i2b = s_lds;                       // [KS2][2 NT][64]
+    uint4* s_i1a = s_i2b + KS2 * 2 * NT * 64;   // [4][64]
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int g = lane >> 4, x = lane & 15;
+    constexpr int TH = 64 * kKgWaves;
+    for (int i = tid; i < KS2 * 2 * NT * 64; i += TH) s_i2b[i] = ((const uint4*)P.i2b)[i];
+    for (int i = tid; i < 4 * 64; i += TH) s_i1a[i] = ((const uint4*)P.i1a)[i];
+    uint32_t twf[IT][2][4];
+#pragma unroll
+    for (int it = 0; it < IT; ++it)
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) twf[it][kt][r] = P.twf[lane * (IT * 8) + (it * 2 + kt) * 4 + r];
+    __syncthreads();
+    const int h = blockIdx.x * kKgWaves + wave;
+    if (h >= P.H) return;
+    // the channel's accumulated spectrum (times 4), scaled by `pre` so that
+    // the f16 operands stay in range however concentrated it is
+    float4 s4[2 * MT2];
+#pragma unroll
+    for (int i = 0; i < 2 * MT2; ++i) s4[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int sl = 0; sl < P.S; ++sl) {
+        const float4* p = (const float4*)P.part + ((long long)(sl * P.H + h) * 64 + lane) * 8;
+#pragma unroll
+        for (int i = 0; i < 2 * MT2; ++i) {
+            const float4 v = p[i];
+            s4[i].x += v.x;
+            s4[i].y += v.y;
+            s4[i].z += v.z;
+            s4[i].w += v.w;
+        }
+    }
+    uint4 a2[2][KS2];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+        uint32_t zp[MT2][2];
+#pragma unroll
+        for (int mt = 0; mt < MT2; ++mt) {
+            const float4 v = s4[kt * MT2 + mt];
+            zp[mt][0] = pk2(v.x * P.pre, v.y * P.pre);
+            zp[mt][1] = pk2(v.z * P.pre, v.w * P.pre);
+        }
+#pragma unroll
+        for (int ks = 0; ks < KS2; ++ks)
+            a2[kt][ks] = make_uint4(zp[2 * ks][0], zp[2 * ks][1], zp[2 * ks + 1][0], zp[2 * ks + 1][1]);
+    }
+    // I2 and the conjugate twiddle, as the row kernel
+    uint4 b1v[2][NT];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+            rfloat4 re = {0.f, 0.f, 0.f, 0.f}, im = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < KS2; ++ks) {
+                re = mma_f16(a2[kt][ks], s_i2b[(ks * 2 * NT + 2 * nt) * 64 + lane], re);
+                im = mma_f16(a2[kt][ks], s_i2b[(ks * 2 * NT + 2 * nt + 1) * 64 + lane], im);
+            }
+            uint32_t w[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) w[r] = as_u32(hmulc(as_h2(pk2(re[r], im[r])), as_h2(twf[kt][nt][r])));
+            b1v[kt][nt] = make_uint4(w[0], w[1], w[2], w[3]);
+        }
+    // I1 into fp32 points (t even, t odd), whole lines as the row kernel
+    float2* dk = (float2*)(P.dk + (long long)h * (32 * NB));
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) {
+        float2 o[NT][2];
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+            rfloat4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) acc = mma_f16(s_i1a[(mt * 2 + ks) * 64 + lane], b1v[ks][nt], acc);
+#pragma unroll
+            for (int e = 0; e < 2; ++e) o[nt][e] = make_float2(acc[2 * e] * P.post, acc[2 * e + 1] * P.post);
+        }
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+            uint32_t ax = __float_as_uint(o[0][e].x), bx = __float_as_uint(o[1][e].x);
+            uint32_t ay = __float_as_uint(o[0][e].y), by = __float_as_uint(o[1][e].y);
+            swap16(ax, bx);
+            swap16(ay, by);
+            const int na = 8 * mt + 4 * (g >> 1) + e, w = (g & 1) ? kmap32(1, x) : x;
+            dk[NB * na + w] = make_float2(__uint_as_float(ax), __uint_as_float(ay));
+            dk[NB * (na + 2) + w] = make_float2(__uint_as_float(bx), __uint_as_float(by));
+        }
+    }
+}
+
+int kgrad_row_lds(int io) { return ((io == IO_BF16 ? 8 : 4) + 8) * 64 * 16 + kKgWaves * 2 * 32 * 16 * 4; }
+
+hipError_t launch_kgrad_row(int io, const KgRowParams& p, hipStream_t s) {
+    if (p.H <= 0 || p.S <= 0) return hipSuccess;
+    const unsigned tasks = (unsigned)(p.H * p.S);
+    const dim3 grid((tasks + kKgWaves - 1) / kKgWaves), blk(64 * kKgWaves);
+    const int lds = kgrad_row_lds(io);
+    if (io == IO_BF16) hipLaunchKernelGGL(kgrad_row_kernel<IO_BF16>, grid, blk, lds, s, p);
+    else hipLaunchKernelGGL(kgrad_row_kernel<IO_F16>, grid, blk, lds, s, p);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const dim3 grid2((unsigned)((p.H + kKgWaves - 1) / kKgWaves));
+    const int lds2 = (2 * 2 * 2 + 4) * 64 * 16;
+    if (io == IO_BF16) hipLaunchKernelGGL(kgrad_row_inv_kernel<IO_BF16>, grid2, blk, lds2, s, p);
+    else hipLaunchKernelGGL(kgrad_row_inv_kernel<IO_F16>, grid2, blk, lds2, s, p);
+    return hipGetLastError();
+}
+
+}  // namespace fftconv
