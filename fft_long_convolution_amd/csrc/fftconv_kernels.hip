@@ -391,93 +391,92 @@ __device__ __forceinline__ uint16_t f32_to_io(float f) {
     return __builtin_bit_cast(uint16_t, (_Float16)f);
 }
 
-// z[m] = u[2m] + i u[2m+1] for m in [0, npts): 'src' points at u[2*m0].
-// With a gate g (same layout as u, or null) the points are of u (.) g,
-// each product formed in fp32 (exact for 16-bit inputs).
+// Points move as 16-byte vectors: two fp32 points or four 16-bit ones.
+template <int IO>
+constexpr int pts_per_vec() { return IO == IO_F32 ? 2 : 4; }
+
+// Vector j of a run of points: z[m] = u[2m] + i u[2m+1] from `src` (at
+// u[2*m0]) into dst[pts_per_vec * j ...].  With a gate g (same layout as u,
+// or null) the points are of u (.) g, each product formed in fp32 (exact
+// for 16-bit inputs).
+template <int IO>
+__device__ __forceinline__ void load_vec(const void* src, const void* gsrc, float2* dst, int j) {
+    if (IO == IO_F32) {
+        float4 v = ((const float4*)src)[j];
+        if (gsrc) {
+            const float4 g = ((const float4*)gsrc)[j];
+            v = make_float4(v.x * g.x, v.y * g.y, v.z * g.z, v.w * g.w);
+        }
+        dst[2 * j] = make_float2(v.x, v.y);
+        dst[2 * j + 1] = make_float2(v.z, v.w);
+    } else {
+        const uint4 v = ((const uint4*)src)[j];
+        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+        float2 pt[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            pt[i] = make_float2(io_to_f32<IO>((uint16_t)(w[i] & 0xffffu)),
+                                io_to_f32<IO>((uint16_t)(w[i] >> 16)));
+        if (gsrc) {
+            const uint4 gv = ((const uint4*)gsrc)[j];
+            const uint32_t gw[4] = {gv.x, gv.y, gv.z, gv.w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                pt[i].x *= io_to_f32<IO>((uint16_t)(gw[i] & 0xffffu));
+                pt[i].y *= io_to_f32<IO>((uint16_t)(gw[i] >> 16));
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) dst[4 * j + i] = pt[i];
+    }
+}
+
+// Vector j of a run of outputs: y[2m], y[2m+1] = Re, Im of src[m]; with a
+// gate g (same layout as y, or null) each output is multiplied by g in fp32
+// before the one rounding to the I/O type.
+template <int IO>
+__device__ __forceinline__ void store_vec(const float2* src, const void* gsrc, void* dst, int j) {
+    if (IO == IO_F32) {
+        const float2 a = src[2 * j], b = src[2 * j + 1];
+        float4 r = make_float4(a.x, a.y, b.x, b.y);
+        if (gsrc) {
+            const float4 g = ((const float4*)gsrc)[j];
+            r = make_float4(r.x * g.x, r.y * g.y, r.z * g.z, r.w * g.w);
+        }
+        ((float4*)dst)[j] = r;
+    } else {
+        float2 pt[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) pt[i] = src[4 * j + i];
+        if (gsrc) {
+            const uint4 gv = ((const uint4*)gsrc)[j];
+            const uint32_t gw[4] = {gv.x, gv.y, gv.z, gv.w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                pt[i].x *= io_to_f32<IO>((uint16_t)(gw[i] & 0xffffu));
+                pt[i].y *= io_to_f32<IO>((uint16_t)(gw[i] >> 16));
+            }
+        }
+        uint32_t w[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            w[i] = (uint32_t)f32_to_io<IO>(pt[i].x) | ((uint32_t)f32_to_io<IO>(pt[i].y) << 16);
+        ((uint4*)dst)[j] = make_uint4(w[0], w[1], w[2], w[3]);
+    }
+}
+
+// A whole run of npts points with all threads of the workgroup.
 template <int IO>
 __device__ __forceinline__ void load_points(const void* src, const void* gsrc,
                                             float2* dst, int npts, int tid,
                                             int nthr) {
-    if (IO == IO_F32) {
-        const float4* s = (const float4*)src;
-        const float4* gs = (const float4*)gsrc;
-        for (int j = tid; j < (npts >> 1); j += nthr) {
-            float4 v = s[j];
-            if (gs) {
-                const float4 g = gs[j];
-                v = make_float4(v.x * g.x, v.y * g.y, v.z * g.z, v.w * g.w);
-            }
-            dst[2 * j] = make_float2(v.x, v.y);
-            dst[2 * j + 1] = make_float2(v.z, v.w);
-        }
-    } else {
-        const uint4* s = (const uint4*)src;
-        const uint4* gs = (const uint4*)gsrc;
-        for (int j = tid; j < (npts >> 2); j += nthr) {
-            const uint4 v = s[j];
-            const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-            float2 pt[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                pt[i] = make_float2(io_to_f32<IO>((uint16_t)(w[i] & 0xffffu)),
-                                    io_to_f32<IO>((uint16_t)(w[i] >> 16)));
-            if (gs) {
-                const uint4 gv = gs[j];
-                const uint32_t gw[4] = {gv.x, gv.y, gv.z, gv.w};
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    pt[i].x *= io_to_f32<IO>((uint16_t)(gw[i] & 0xffffu));
-                    pt[i].y *= io_to_f32<IO>((uint16_t)(gw[i] >> 16));
-                }
-            }
-#pragma unroll
-            for (int i = 0; i < 4; ++i) dst[4 * j + i] = pt[i];
-        }
-    }
+    for (int j = tid; j < npts / pts_per_vec<IO>(); j += nthr) load_vec<IO>(src, gsrc, dst, j);
 }
-
-// y[2m], y[2m+1] = Re, Im of the points; with a gate g (same layout as y,
-// or null) each output is multiplied by g in fp32 before the one rounding
-// to the I/O type.
 template <int IO>
 __device__ __forceinline__ void store_points(const float2* src, const void* gsrc,
                                              void* dst, int npts, int tid,
                                              int nthr) {
-    if (IO == IO_F32) {
-        float4* o = (float4*)dst;
-        const float4* gs = (const float4*)gsrc;
-        for (int j = tid; j < (npts >> 1); j += nthr) {
-            const float2 a = src[2 * j], b = src[2 * j + 1];
-            float4 r = make_float4(a.x, a.y, b.x, b.y);
-            if (gs) {
-                const float4 g = gs[j];
-                r = make_float4(r.x * g.x, r.y * g.y, r.z * g.z, r.w * g.w);
-            }
-            o[j] = r;
-        }
-    } else {
-        uint4* o = (uint4*)dst;
-        const uint4* gs = (const uint4*)gsrc;
-        for (int j = tid; j < (npts >> 2); j += nthr) {
-            float2 pt[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) pt[i] = src[4 * j + i];
-            if (gs) {
-                const uint4 gv = gs[j];
-                const uint32_t gw[4] = {gv.x, gv.y, gv.z, gv.w};
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    pt[i].x *= io_to_f32<IO>((uint16_t)(gw[i] & 0xffffu));
-                    pt[i].y *= io_to_f32<IO>((uint16_t)(gw[i] >> 16));
-                }
-            }
-            uint32_t w[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                w[i] = (uint32_t)f32_to_io<IO>(pt[i].x) | ((uint32_t)f32_to_io<IO>(pt[i].y) << 16);
-            o[j] = make_uint4(w[0], w[1], w[2], w[3]);
-        }
-    }
+    for (int j = tid; j < npts / pts_per_vec<IO>(); j += nthr) store_vec<IO>(src, gsrc, dst, j);
 }
 
 template <int IO>
@@ -544,11 +543,15 @@ __global__ void __launch_bounds__(512) outer_fwd_kernel(FwdParams P) {
     const int c0 = blockIdx.y * P.ct;
     const int slab = P.M / P.Qo;
     float2* line = smem;
-    // the nonzero half of the outer digits: n_o < Qo/2
-    for (int no = 0; no < (P.Qo >> 1); ++no) {
-        const long long e0 = row * P.N + 2LL * ((long long)no * slab + c0);
-        load_points<IO>(io_ptr<IO>(P.u, e0), gate_ptr<IO>(P.w, e0),
-                        line + no * P.ct, P.ct, threadIdx.x, blockDim.x);
+    // the nonzero half of the outer digits: n_o < Qo/2, every thread over
+    // (digit, vector) pairs -- a tile's run per digit is only ct points
+    {
+        const int per = P.ct / pts_per_vec<IO>();
+        for (int i = threadIdx.x; i < (P.Qo >> 1) * per; i += blockDim.x) {
+            const int no = i / per, j = i - no * per;
+            const long long e0 = row * P.N + 2LL * ((long long)no * slab + c0);
+            load_vec<IO>(io_ptr<IO>(P.u, e0), gate_ptr<IO>(P.w, e0), line + no * P.ct, j);
+        }
     }
     __syncthreads();
     for (int i = 0; i < P.nst; ++i) {
@@ -635,10 +638,13 @@ __global__ void __launch_bounds__(512) outer_inv_kernel(FwdParams P) {
                                  wave, nwaves, lane);
         __syncthreads();
     }
-    for (int no = 0; no < (P.Qo >> 1); ++no) {
-        const long long e0 = row * P.N + 2LL * ((long long)no * slab + c0);
-        store_points<IO>(line + no * P.ct, gate_ptr<IO>(P.v, e0),
-                         (void*)io_ptr<IO>(P.y, e0), P.ct, threadIdx.x, blockDim.x);
+    {
+        const int per = P.ct / pts_per_vec<IO>();
+        for (int i = threadIdx.x; i < (P.Qo >> 1) * per; i += blockDim.x) {
+            const int no = i / per, j = i - no * per;
+            const long long e0 = row * P.N + 2LL * ((long long)no * slab + c0);
+            store_vec<IO>(line + no * P.ct, gate_ptr<IO>(P.v, e0), (void*)io_ptr<IO>(P.y, e0), j);
+        }
     }
 }
 
