@@ -1025,8 +1025,20 @@ int kgrad_row_slices(const fftconv_plan_s* pl, size_t B, size_t H) {
     return n < 1 ? 1 : (int)n;
 }
 
+// The wide-engine kernel gradient (N = P x 1024, 16-bit I/O): a workgroup
+// per (channel, slice), two per CU.
+int kgrad_wide_slices(const fftconv_plan_s* pl, size_t B, size_t H) {
+    if (B == 0 || H == 0) return 1;
+    long long n = (4LL * pl->num_cu + (long long)H - 1) / (long long)H;
+    if (n > (long long)B) n = (long long)B;
+    if (n > 64) n = 64;
+    return n < 1 ? 1 : (int)n;
+}
+
 size_t kgrad_workspace_bytes(const fftconv_plan_s* pl, size_t B, size_t H) {
     if (kgrad_on_row(pl)) return (size_t)kgrad_row_slices(pl, B, H) * H * 64 * 32 * 4;
+    if (pl->s.wide_P)
+        return (size_t)kgrad_wide_slices(pl, B, H) * H * (pl->s.wide_P / 2) * 64 * 64 * 4;
     const Shape& g = pl->grad->s;
     if (g.path == 0) {
         const int ns = kgrad_splits(pl, B, H);
@@ -1575,6 +1587,26 @@ fftconv_status fftconv_backward(fftconv_plan_t plan, const void* u,
         R.pre = 0.25f / sqrtf((float)s.M);
         R.post = (float)s.M;
         e = launch_kgrad_row(io, R, st);
+        return e == hipSuccess ? FFTCONV_OK : FFTCONV_ERR_HIP;
+    }
+    if (s.wide_P) {
+        KgWideParams W{};
+        W.B = (int)B;
+        W.H = (int)H;
+        W.S = kgrad_wide_slices(plan, B, H);
+        W.u = u;
+        W.dy = dy;
+        W.part = (float*)workspace;
+        W.dk = dk;
+        W.f1b = plan->wide.f1b;
+        W.f2a = plan->wide.f2a;
+        W.i2b = plan->wide.i2b;
+        W.i1a = plan->wide.i1a;
+        W.twf = plan->wide.twf;
+        W.two = plan->wide.two;
+        W.pre = 0.25f / sqrtf((float)s.M);
+        W.post = (float)s.M;
+        e = launch_kgrad_wide(io, s.wide_P, W, st);
         return e == hipSuccess ? FFTCONV_OK : FFTCONV_ERR_HIP;
     }
     KgradParams K{};

@@ -138,6 +138,24 @@ struct KgRowParams {
 };
 hipError_t launch_kgrad_row(int io, const KgRowParams& p, hipStream_t s);
 
+// The same on the one-workgroup-per-row engine (N = P x 1024): a workgroup
+// per (channel, batch slice); part is [S][H][P/2 waves][64 lanes][64] fp32.
+struct KgWideParams {
+    int B, H, S;
+    const void* u;
+    const void* dy;
+    float* part;
+    float* dk;              // [H][N] fp32
+    const void* f1b;        // the wide plan's tables
+    const void* f2a;
+    const void* i2b;
+    const void* i1a;
+    const uint32_t* twf;
+    const uint32_t* two;
+    float pre, post;
+};
+hipError_t launch_kgrad_wide(int io, int P, const KgWideParams& p, hipStream_t s);
+
 // Spectrum (alpha/beta) construction.
 struct SpecParams {
     int M, N, L;

@@ -21,7 +21,7 @@
 // partial row.
 // kgrad_row_inv: one wavefront per channel sums the partial rows and runs
 // the inverse half of the engine (I2, twiddle, I1) into fp32 dk.
-#include "fftconv_mfma.h"
+#include "fftconv_engine.h"
 
 namespace fftconv {
 
@@ -318,6 +318,379 @@ hipError_t launch_kgrad_row(int io, const KgRowParams& p, hipStream_t s) {
     if (io == IO_BF16) hipLaunchKernelGGL(kgrad_row_inv_kernel<IO_BF16>, grid2, blk, lds2, s, p);
     else hipLaunchKernelGGL(kgrad_row_inv_kernel<IO_F16>, grid2, blk, lds2, s, p);
     return hipGetLastError();
+}
+
+
+// ---------------------------------------------------------------------------
+// The same on the one-workgroup-per-row engine (N = P x 1024, P = 4, 8, 16,
+// 16-bit I/O): a workgroup of P/2 waves per (channel, batch slice).  Each
+// row of u and of dy goes through the wide kernel's outer forward stage into
+// LDS and the engine's forward transform of the wave's two sub-rows.  For
+// waves w >= 1 the second sub-row holds conj(Z[-k]) where the first holds
+// Z[k] (k = w + P k'), so both contributions are element-wise:
+//   4 Z_g[k]        = 2 conj(E2) d + conj(O') (Od' - W Ed2)
+//   4 conj Z_g[-k]  = 2 conj(E2) e + conj(O') (Od' + W Ed2)
+// with a, c, d, e the two sub-rows of u and dy, E2 = a + c, O' = a - c,
+// Ed2 = d + e, Od' = d - e and W = exp(2 pi i k / M) -- the second one in the
+// conjugated form the inverse expects of that sub-row.  Wave 0's sub-rows
+// (k = P k' and P/2 + P k') pair within themselves as in the wide kernel.
+// kgrad_wide_inv_kernel sums the slices per channel, runs the engine's
+// inverse and the outer inverse stage, and writes fp32 dk.
+// ---------------------------------------------------------------------------
+using namespace eng;
+
+// 4 Z_g for one bin from its value and its mirror partner (not conjugated)
+// of u and dy; W = exp(2 pi i k / M)
+__device__ __forceinline__ rhalf2 kg_self(uint32_t a, uint32_t ap, uint32_t d, uint32_t dp, rhalf2 W) {
+    const rhalf2 A = as_h2(a), Ap = as_h2(ap), Dv = as_h2(d), Dp = as_h2(dp);
+    const rhalf2 cAp = {Ap.x, -Ap.y}, cDp = {Dp.x, -Dp.y};
+    const rhalf2 E2 = A + cAp, O2 = A - cAp, Ed = Dv + cDp, Od = Dv - cDp;
+    const rhalf2 T = Od - hmul(Ed, W);
+    const rhalf2 two = {(_Float16)2.f, (_Float16)2.f};
+    return __builtin_elementwise_fma(hmulc(Dv, E2), two, hmulc(T, O2));
+}
+
+template <int IO, int P>
+__global__ void __launch_bounds__(32 * P, 2) kgrad_wide_kernel(KgWideParams K) {
+    constexpr int Q = 1024, M = P * Q, HALF = P / 2, T = 32 * P;
+    constexpr int CPT = Q / T;
+    extern __shared__ uint4 s_lds[];
+    uint4* s_f1b = s_lds;                              // [ks 2][jt 4][64]
+    uint32_t* s_two = (uint32_t*)(s_f1b + 8 * 64);     // [k1 - 1][thread][column]
+    uint32_t* s_buf = s_two + HALF * Q;                // [P sub-rows][Q]
+    uint32_t* s_scr = s_buf + M;                       // [u, dy][39 k_b slots][16 x]
+    uint32_t* s_wb = s_scr + 2 * 39 * 16;              // [kt][mt][e][lane] exp(2 pi i k'/1024)
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int g = lane >> 4, x = lane & 15;
+    for (int i = tid; i < 8 * 64; i += T) s_f1b[i] = ((const uint4*)K.f1b)[i];
+    for (int i = tid; i < HALF * Q / 4; i += T) ((uint4*)s_two)[i] = ((const uint4*)K.two)[i];
+    Regs E;
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) E.f2a[mt][ks] = ((const uint4*)K.f2a)[(mt * 2 + ks) * 64 + lane];
+#pragma unroll
+    for (int it = 0; it < 2; ++it)
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) E.twf[it][kt][r] = K.twf[lane * 16 + (it * 2 + kt) * 4 + r];
+    __syncthreads();
+
+    const int h = blockIdx.x / K.S, sl = blockIdx.x - h * K.S;
+    const int b0 = (int)((long long)K.B * sl / K.S), b1 = (int)((long long)K.B * (sl + 1) / K.S);
+
+    // W = exp(2 pi i k / M) = exp(2 pi i k1 / M) exp(2 pi i k' / 1024): the
+    // lane's engine bins k' times a factor of the sub-row
+    if (wave == 0) {
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+                for (int e = 0; e < 2; ++e) {
+                    const int kp = kmap32(kt, x) + 32 * rmid_perm(8 * mt + 2 * g + e, 32);
+                    float sn, cs;
+                    sincospif(2.f * (float)kp / (float)Q, &sn, &cs);
+                    s_wb[((kt * 4 + mt) * 2 + e) * 64 + lane] = pk2(cs, sn);
+                }
+    }
+    __syncthreads();
+    // sub-row factors: wave w >= 1: k1 = w for both; wave 0: 1 and P/2
+    uint32_t wsub[2];
+    {
+        float sn, cs;
+        sincospif(2.f * (float)(wave == 0 ? HALF : wave) / (float)M, &sn, &cs);
+        const uint32_t f = pk2(cs, sn);
+        wsub[0] = wave == 0 ? pk2(1.f, 0.f) : f;
+        wsub[1] = f;
+    }
+
+    // ---- outer forward stage geometry (as the wide kernel)
+    const int nb = tid & 31, na0 = CPT * (tid >> 5);
+    const int it_o = nb < 16 ? 0 : 1, x_o = nb < 16 ? nb : (nb == 16 ? 0 : 32 - nb);
+    const int oa0 = eng_addr(na0, it_o, x_o);
+    const int lofs = 32 * na0 + nb;
+    auto load_in = [&](uint32_t (&dst)[HALF][CPT], const void* base, int b) {
+        const uint32_t* r = (const uint32_t*)base + ((long long)b * K.H + h) * (M / 2);
+#pragma unroll
+        for (int n1 = 0; n1 < HALF; ++n1)
+#pragma unroll
+            for (int j = 0; j < CPT; ++j) dst[n1][j] = __builtin_nontemporal_load(&r[n1 * Q + lofs + 32 * j]);
+    };
+    auto outer_fwd = [&](const uint32_t (&in)[HALF][CPT]) {
+        typedef Outer<IO> O;
+        typedef typename O::V C;
+        uint32_t V[P][CPT];
+#pragma unroll
+        for (int j = 0; j < CPT; ++j) {
+            C xin[HALF], A[P];
+#pragma unroll
+            for (int n1 = 0; n1 < HALF; ++n1) xin[n1] = O::from_io(in[n1][j]);
+            dft_half_in<P>(xin, A);
+            const uint32_t* tw = s_two + tid * CPT + j;
+            V[0][j] = O::to_h2(A[0]);
+            V[1][j] = O::to_h2(O::mul(A[HALF], tw[(HALF - 1) * T * CPT]));
+#pragma unroll
+            for (int k1 = 1; k1 < HALF; ++k1) {
+                const uint32_t t = tw[(k1 - 1) * T * CPT];
+                V[2 * k1][j] = O::to_h2(O::mul(A[k1], t));
+                V[2 * k1 + 1][j] = O::to_h2(O::mul(cnj(A[P - k1]), t));
+            }
+        }
+#pragma unroll
+        for (int sidx = 0; sidx < P; ++sidx) {
+            uint32_t* dst = s_buf + sidx * Q + oa0;
+            if constexpr (CPT == 2) {
+                *(uint2*)dst = make_uint2(V[sidx][0], V[sidx][1]);
+            } else {
+#pragma unroll
+                for (int q = 0; q < CPT / 4; ++q)
+                    *(uint4*)(dst + 64 * q) =
+                        make_uint4(V[sidx][4 * q], V[sidx][4 * q + 1], V[sidx][4 * q + 2], V[sidx][4 * q + 3]);
+            }
+        }
+    };
+
+    float2 acc[2][2][4][2];   // [sub][kt][mt][e]
+#pragma unroll
+    for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+                for (int e = 0; e < 2; ++e) acc[sb][kt][mt][e] = make_float2(0.f, 0.f);
+
+    uint32_t* scr_u = s_scr + x;
+    uint32_t* scr_d = s_scr + 39 * 16 + x;
+    for (int b = b0; b < b1; ++b) {
+        uint32_t zu[2][2][4][2], zd[2][2][4][2];   // [sub][kt][mt][e]
+        {
+            uint32_t in_u[HALF][CPT];
+            load_in(in_u, K.u, b);
+            outer_fwd(in_u);
+        }
+        __syncthreads();
+        forward(s_buf + (2 * wave) * Q, s_f1b, E, lane, zu[0]);
+        forward(s_buf + (2 * wave + 1) * Q, s_f1b, E, lane, zu[1]);
+        __syncthreads();
+        {
+            uint32_t in_d[HALF][CPT];
+            load_in(in_d, K.dy, b);
+            outer_fwd(in_d);
+        }
+        __syncthreads();
+        forward(s_buf + (2 * wave) * Q, s_f1b, E, lane, zd[0]);
+        forward(s_buf + (2 * wave + 1) * Q, s_f1b, E, lane, zd[1]);
+        if (wave != 0) {
+#pragma unroll
+            for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+                for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+                    for (int e = 0; e < 2; ++e) {
+                        const rhalf2 a = as_h2(zu[0][kt][mt][e]), c = as_h2(zu[1][kt][mt][e]);
+                        const rhalf2 d = as_h2(zd[0][kt][mt][e]), ee = as_h2(zd[1][kt][mt][e]);
+                        const rhalf2 W = hmul(as_h2(s_wb[((kt * 4 + mt) * 2 + e) * 64 + lane]), as_h2(wsub[0]));
+                        const rhalf2 E2 = a + c, O2 = a - c, Ed = d + ee, Od = d - ee;
+                        const rhalf2 WE = hmul(Ed, W);
+                        const rhalf2 two = {(_Float16)2.f, (_Float16)2.f};
+                        const rhalf2 RX = __builtin_elementwise_fma(hmulc(d, E2), two, hmulc(Od - WE, O2));
+                        const rhalf2 RY = __builtin_elementwise_fma(hmulc(ee, E2), two, hmulc(Od + WE, O2));
+                        acc[0][kt][mt][e].x += (float)RX.x;
+                        acc[0][kt][mt][e].y += (float)RX.y;
+                        acc[1][kt][mt][e].x += (float)RY.x;
+                        acc[1][kt][mt][e].y += (float)RY.y;
+                    }
+        } else {
+            // sub-row 0 pairs k' with -k' (the k_a = 0 column through LDS),
+            // sub-row 1 pairs k' with 1023 - k' (one lane over)
+            uint32_t qu[4][2], qd[4][2];
+            self_exchange(zu[0], scr_u, g, qu);
+            self_exchange(zd[0], scr_d, g, qd);
+            const bool l0 = (x == 0);
+#pragma unroll
+            for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+                for (int mt = 0; mt < 4; ++mt) {
+                    const int pm = (mt + 2) & 3;
+#pragma unroll
+                    for (int e = 0; e < 2; ++e) {
+                        uint32_t nu, nd;
+                        if (kt == 0) {
+                            nu = l0 ? qu[mt][e] : zu[0][1][pm][e];
+                            nd = l0 ? qd[mt][e] : zd[0][1][pm][e];
+                        } else {
+                            nu = l0 ? zu[0][1][pm][e] : zu[0][0][pm][e];
+                            nd = l0 ? zd[0][1][pm][e] : zd[0][0][pm][e];
+                        }
+                        const uint32_t ru = kt == 0 ? rot_up(zu[1][1][pm][e]) : rot_down(zu[1][0][pm][e]);
+                        const uint32_t rd = kt == 0 ? rot_up(zd[1][1][pm][e]) : rot_down(zd[1][0][pm][e]);
+                        const rhalf2 W0 = as_h2(s_wb[((kt * 4 + mt) * 2 + e) * 64 + lane]);
+                        const rhalf2 W1 = hmul(W0, as_h2(wsub[1]));
+                        const rhalf2 R0 = kg_self(zu[0][kt][mt][e], nu, zd[0][kt][mt][e], nd, W0);
+                        const rhalf2 R1 = kg_self(zu[1][kt][mt][e], ru, zd[1][kt][mt][e], rd, W1);
+                        acc[0][kt][mt][e].x += (float)R0.x;
+                        acc[0][kt][mt][e].y += (float)R0.y;
+                        acc[1][kt][mt][e].x += (float)R1.x;
+                        acc[1][kt][mt][e].y += (float)R1.y;
+                    }
+                }
+        }
+        __syncthreads();
+    }
+    float4* o = (float4*)K.part + (((long long)(sl * K.H + h) * HALF + wave) * 64 + lane) * 16;
+#pragma unroll
+    for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt)
+                o[(sb * 2 + kt) * 4 + mt] = make_float4(acc[sb][kt][mt][0].x, acc[sb][kt][mt][0].y,
+                                                        acc[sb][kt][mt][1].x, acc[sb][kt][mt][1].y);
+}
+
+template <int IO, int P>
+__global__ void __launch_bounds__(32 * P, 2) kgrad_wide_inv_kernel(KgWideParams K) {
+    constexpr int Q = 1024, M = P * Q, HALF = P / 2, T = 32 * P;
+    constexpr int CPT = Q / T;
+    extern __shared__ uint4 s_lds[];
+    uint4* s_i1a = s_lds;                              // [mt 4][ks 2][64]
+    uint32_t* s_two = (uint32_t*)(s_i1a + 8 * 64);
+    uint32_t* s_buf = s_two + HALF * Q;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int g = lane >> 4, x = lane & 15;
+    for (int i = tid; i < 8 * 64; i += T) s_i1a[i] = ((const uint4*)K.i1a)[i];
+    for (int i = tid; i < HALF * Q / 4; i += T) ((uint4*)s_two)[i] = ((const uint4*)K.two)[i];
+    Regs E;
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+        for (int jt = 0; jt < 4; ++jt) E.i2b[ks][jt] = ((const uint4*)K.i2b)[(ks * 4 + jt) * 64 + lane];
+#pragma unroll
+    for (int it = 0; it < 2; ++it)
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) E.twf[it][kt][r] = K.twf[lane * 16 + (it * 2 + kt) * 4 + r];
+    const int h = blockIdx.x;
+    // the channel's accumulated spectra of this wave's sub-rows
+    float4 s4[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) s4[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int sl = 0; sl < K.S; ++sl) {
+        const float4* pp = (const float4*)K.part + (((long long)(sl * K.H + h) * HALF + wave) * 64 + lane) * 16;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const float4 v = pp[i];
+            s4[i].x += v.x;
+            s4[i].y += v.y;
+            s4[i].z += v.z;
+            s4[i].w += v.w;
+        }
+    }
+    uint4 a2[2][2][2];   // [sub][kt][ks]
+#pragma unroll
+    for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt) {
+            uint32_t pz[4][2];
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt) {
+                const float4 v = s4[(sb * 2 + kt) * 4 + mt];
+                pz[mt][0] = pk2(v.x * K.pre, v.y * K.pre);
+                pz[mt][1] = pk2(v.z * K.pre, v.w * K.pre);
+            }
+            pack_a2(pz, a2[sb][kt]);
+        }
+    __syncthreads();   // tables in LDS
+    const int i1_base = (16 * (g >> 1) + x) * 4 + 2 * (g & 1);
+    inverse(a2[0], s_i1a, E, lane, i1_base, s_buf + (2 * wave) * Q);
+    inverse(a2[1], s_i1a, E, lane, i1_base, s_buf + (2 * wave + 1) * Q);
+    __syncthreads();
+    // outer inverse stage, fp32 output
+    const int nb = tid & 31, na0 = CPT * (tid >> 5);
+    const int it_o = nb < 16 ? 0 : 1, x_o = nb < 16 ? nb : (nb == 16 ? 0 : 32 - nb);
+    const int oa0 = eng_addr(na0, it_o, x_o);
+    const int lofs = 32 * na0 + nb;
+    typedef Outer<IO> O;
+    typedef typename O::V C;
+    uint32_t R[P][CPT];
+#pragma unroll
+    for (int sidx = 0; sidx < P; ++sidx) {
+        const uint32_t* src = s_buf + sidx * Q + oa0;
+        if constexpr (CPT == 2) {
+            const uint2 v = *(const uint2*)src;
+            R[sidx][0] = v.x;
+            R[sidx][1] = v.y;
+        } else {
+#pragma unroll
+            for (int q = 0; q < CPT / 4; ++q) {
+                const uint4 v = *(const uint4*)(src + 64 * q);
+                R[sidx][4 * q] = v.x;
+                R[sidx][4 * q + 1] = v.y;
+                R[sidx][4 * q + 2] = v.z;
+                R[sidx][4 * q + 3] = v.w;
+            }
+        }
+    }
+    float2* dk = (float2*)(K.dk + (long long)h * M);   // N = M reals per row
+#pragma unroll
+    for (int j = 0; j < CPT; ++j) {
+        const uint32_t* tw = s_two + tid * CPT + j;
+        C Bv[P], zo[HALF];
+        Bv[0] = O::from_h2(R[0][j]);
+        Bv[HALF] = O::mulc(O::from_h2(R[1][j]), tw[(HALF - 1) * T * CPT]);
+#pragma unroll
+        for (int k1 = 1; k1 < HALF; ++k1) {
+            const uint32_t t = tw[(k1 - 1) * T * CPT];
+            Bv[k1] = O::mulc(O::from_h2(R[2 * k1][j]), t);
+            Bv[P - k1] = cnj(O::mulc(O::from_h2(R[2 * k1 + 1][j]), t));
+        }
+        idft_half_out<P>(Bv, zo);
+#pragma unroll
+        for (int n1 = 0; n1 < HALF; ++n1)
+            dk[n1 * Q + lofs + 32 * j] = make_float2((float)zo[n1].x * K.post, (float)zo[n1].y * K.post);
+    }
+}
+
+int kgrad_wide_lds(int P) {
+    return 8 * 64 * 16 + (P / 2) * 1024 * 4 + P * 1024 * 4 + 2 * 39 * 16 * 4 + 16 * 64 * 4;
+}
+int kgrad_wide_inv_lds(int P) { return 8 * 64 * 16 + (P / 2) * 1024 * 4 + P * 1024 * 4; }
+
+template <int IO, int P>
+static hipError_t kgrad_wide_t(const KgWideParams& p, hipStream_t s) {
+    const int l1 = kgrad_wide_lds(P), l2 = kgrad_wide_inv_lds(P);
+    hipError_t e = hipFuncSetAttribute((const void*)kgrad_wide_kernel<IO, P>,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, l1);
+    if (e != hipSuccess) return e;
+    e = hipFuncSetAttribute((const void*)kgrad_wide_inv_kernel<IO, P>,
+                            hipFuncAttributeMaxDynamicSharedMemorySize, l2);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((kgrad_wide_kernel<IO, P>), dim3((unsigned)(p.H * p.S)), dim3(32 * P), l1, s, p);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((kgrad_wide_inv_kernel<IO, P>), dim3((unsigned)p.H), dim3(32 * P), l2, s, p);
+    return hipGetLastError();
+}
+
+hipError_t launch_kgrad_wide(int io, int P, const KgWideParams& p, hipStream_t s) {
+    if (p.H <= 0 || p.S <= 0) return hipSuccess;
+    if (io == IO_BF16) {
+        if (P == 4) return kgrad_wide_t<IO_BF16, 4>(p, s);
+        if (P == 8) return kgrad_wide_t<IO_BF16, 8>(p, s);
+        if (P == 16) return kgrad_wide_t<IO_BF16, 16>(p, s);
+    } else {
+        if (P == 4) return kgrad_wide_t<IO_F16, 4>(p, s);
+        if (P == 8) return kgrad_wide_t<IO_F16, 8>(p, s);
+        if (P == 16) return kgrad_wide_t<IO_F16, 16>(p, s);
+    }
+    return hipErrorInvalidValue;
 }
 
 }  // namespace fftconv

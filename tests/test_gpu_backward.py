@@ -27,13 +27,15 @@ def _say(*a):
     (256, "f32", 1, 4), (256, "bf16", 3, 5), (512, "f16", 4, 3),
     (1024, "bf16", 5, 3), (1024, "f16", 64, 4), (1024, "bf16", 1, 1),
     (1024, "f32", 2, 2), (2048, "f16", 3, 2),
-    (4096, "bf16", 2, 3), (8192, "f16", 3, 2), (16384, "bf16", 2, 3),
+    (4096, "bf16", 2, 3), (4096, "f16", 1, 1), (8192, "f16", 3, 2),
+    (8192, "bf16", 17, 5), (16384, "bf16", 2, 3), (16384, "f16", 4, 2),
     (32768, "f32", 1, 2), (65536, "f16", 2, 1), (262144, "bf16", 1, 2),
     (1048576, "f16", 1, 1), (4194304, "bf16", 1, 1)])
 def test_backward(N, dtype, B, H):
-    # the row engine at N = 1024 with 16-bit I/O (batch slices of one row up
-    # to more rows than slices), the LDS-staged kernel-gradient kernel
-    # elsewhere up to N = 8192 (two lines per workgroup), multi-pass (outer
+    # the row engine at N = 1024 and the wide engine at N = 4K..16K with
+    # 16-bit I/O (batch slices of one row up to more rows than slices), the
+    # LDS-staged kernel-gradient kernel elsewhere up to N = 8192 (two lines
+    # per workgroup), multi-pass (outer
     # passes + accumulating inner pass + outer inverse) above; the input
     # gradient through every forward family
     w = inputs.Workload("bwd", 240 + N.bit_length() + B, B, H, N, dtype,
