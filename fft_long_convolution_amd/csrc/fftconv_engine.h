@@ -294,6 +294,9 @@ __device__ __forceinline__ void load_regs(Regs& E, const void* f2a, const void* 
 }
 
 // Forward 1024-point DFT of one region (engine layout) into z[kt][mt][e].
+// SK (a band limit below M/4): the odd M-tiles of the second stage,
+// k_b = 8..23, hold only bins the limit zeroes -- not computed (zero).
+template <bool SK = false>
 __device__ __forceinline__ void forward(const uint32_t* region, const uint4* s_f1b, const Regs& E,
                                         int lane, uint32_t (&z)[2][4][2]) {
     const uint4* src = (const uint4*)region;
@@ -334,6 +337,10 @@ __device__ __forceinline__ void forward(const uint32_t* region, const uint4* s_f
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt) {
+            if (SK && (mt & 1)) {
+                z[kt][mt][0] = z[kt][mt][1] = 0u;
+                continue;
+            }
             rfloat4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks) acc = mma_f16(E.f2a[mt][ks], b2[ks][kt], acc);
@@ -343,16 +350,22 @@ __device__ __forceinline__ void forward(const uint32_t* region, const uint4* s_f
 }
 
 // Gather the spectrum-product results p[mt][e] of one column tile kt into
-// the inverse stage's A operands.
+// the inverse stage's A operands: K-step ks holds M-tiles 2 ks and 2 ks + 1,
+// or with SK ks and ks + 2 (K-step 1 is then all zero; the inverse table of
+// a band-limited call is grouped the same way).
+template <bool SK = false>
 __device__ __forceinline__ void pack_a2(const uint32_t (&p)[4][2], uint4 (&a2)[2]) {
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks)
-        a2[ks] = make_uint4(p[2 * ks][0], p[2 * ks][1], p[2 * ks + 1][0], p[2 * ks + 1][1]);
+    for (int ks = 0; ks < 2; ++ks) {
+        const int m0 = SK ? ks : 2 * ks, m1 = SK ? ks + 2 : 2 * ks + 1;
+        a2[ks] = make_uint4(p[m0][0], p[m0][1], p[m1][0], p[m1][1]);
+    }
 }
 
 // Element-wise spectrum product of a region pair whose second region holds
 // conj(Z[-k]) where the first holds Z[k]:
 //   X' = a0 X + b0 Y,  Y' = a1 Y + b1 X   (coefficients (a_e0, b_e0, a_e1, b_e1))
+template <bool SK = false>
 __device__ __forceinline__ void pair_elem(int kt, const uint32_t (&zX)[2][4][2],
                                           const uint32_t (&zY)[2][4][2], const uint4 (&cX)[4],
                                           const uint4 (&cY)[4], uint4 (&a2X)[2], uint4 (&a2Y)[2]) {
@@ -361,14 +374,18 @@ __device__ __forceinline__ void pair_elem(int kt, const uint32_t (&zX)[2][4][2],
     for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
         for (int e = 0; e < 2; ++e) {
+            if (SK && (mt & 1)) {
+                p0[mt][e] = p1[mt][e] = 0u;
+                continue;
+            }
             const rhalf2 zx = as_h2(zX[kt][mt][e]), zy = as_h2(zY[kt][mt][e]);
             const uint32_t al0 = e ? cX[mt].z : cX[mt].x, be0 = e ? cX[mt].w : cX[mt].y;
             const uint32_t al1 = e ? cY[mt].z : cY[mt].x, be1 = e ? cY[mt].w : cY[mt].y;
             p0[mt][e] = as_u32(hcmla(as_h2(al0), zx, as_h2(be0), zy));
             p1[mt][e] = as_u32(hcmla(as_h2(al1), zy, as_h2(be1), zx));
         }
-    pack_a2(p0, a2X);
-    pack_a2(p1, a2Y);
+    pack_a2<SK>(p0, a2X);
+    pack_a2<SK>(p1, a2Y);
 }
 
 // Self pairing: region X pairs k' with -k' (negation, the k_a = 0 column
@@ -395,6 +412,7 @@ __device__ __forceinline__ void self_exchange(const uint32_t (&zX)[2][4][2], uin
             zq[mt][e] = scr[16 * (32 - kb)];
         }
 }
+template <bool SK = false>
 __device__ __forceinline__ void pair_self(int kt, bool l0, const uint32_t (&zX)[2][4][2],
                                           const uint32_t (&zY)[2][4][2], const uint32_t (&zq)[4][2],
                                           const uint4 (&cX)[4], const uint4 (&cY)[4],
@@ -405,6 +423,10 @@ __device__ __forceinline__ void pair_self(int kt, bool l0, const uint32_t (&zX)[
         const int pm = (mt + 2) & 3;
 #pragma unroll
         for (int e = 0; e < 2; ++e) {
+            if (SK && (mt & 1)) {
+                p0[mt][e] = p1[mt][e] = 0u;
+                continue;
+            }
             // negation partner of X
             uint32_t pn;
             if (kt == 0) pn = l0 ? zq[mt][e] : zX[1][pm][e];
@@ -417,12 +439,13 @@ __device__ __forceinline__ void pair_self(int kt, bool l0, const uint32_t (&zX)[
             p1[mt][e] = as_u32(hpair(as_h2(al1), as_h2(zY[kt][mt][e]), as_h2(be1), as_h2(pr)));
         }
     }
-    pack_a2(p0, a2X);
-    pack_a2(p1, a2Y);
+    pack_a2<SK>(p0, a2X);
+    pack_a2<SK>(p1, a2Y);
 }
 
 // Inverse 1024-point DFT of one region: A operands a2[kt][ks] -> region
 // (engine layout).  i1_base = (16 (g >> 1) + x) * 4 + 2 (g & 1).
+template <bool SK = false>
 __device__ __forceinline__ void inverse(const uint4 (&a2)[2][2], const uint4* s_i1a, const Regs& E,
                                         int lane, int i1_base, uint32_t* region) {
     // inverse 32-point DFT over k_b (data as A), then the conjugate twiddle
@@ -434,6 +457,7 @@ __device__ __forceinline__ void inverse(const uint4 (&a2)[2][2], const uint4* s_
             rfloat4 re = {0.f, 0.f, 0.f, 0.f}, im = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks) {
+                if (SK && ks == 1) continue;
                 re = mma_f16(a2[kt][ks], E.i2b[ks][2 * nt], re);
                 im = mma_f16(a2[kt][ks], E.i2b[ks][2 * nt + 1], im);
             }

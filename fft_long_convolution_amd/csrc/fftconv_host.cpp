@@ -875,7 +875,8 @@ fftconv_status build_device_tables(fftconv_plan_s* pl) {
     }
     if (s.wide_P) {
         const int P = s.wide_P;
-        std::vector<uint16_t> f1b = wide_f1b(P), i1a = wide_i1a(P), i2b = row_i2b(32);
+        std::vector<uint16_t> f1b = wide_f1b(P), i1a = wide_i1a(P), i2b = row_i2b(32),
+                              i2bs = row_i2b(32, true);
         std::vector<uint8_t> f2a = row_f2a(32);
         std::vector<uint16_t> twf = row_twiddles(32, false), two = wide_outer_twiddles(P);
         WideParams& W = pl->wide;
@@ -886,6 +887,8 @@ fftconv_status build_device_tables(fftconv_plan_s* pl) {
         W.i1a = d;
         if (upload(pl, i2b.data(), i2b.size() * 2, &d) != hipSuccess) return FFTCONV_ERR_HIP;
         W.i2b = d;
+        if (upload(pl, i2bs.data(), i2bs.size() * 2, &d) != hipSuccess) return FFTCONV_ERR_HIP;
+        W.i2bs = d;
         if (upload(pl, f2a.data(), f2a.size(), &d) != hipSuccess) return FFTCONV_ERR_HIP;
         W.f2a = d;
         if (upload(pl, twf.data(), twf.size() * 2, &d) != hipSuccess) return FFTCONV_ERR_HIP;
@@ -910,7 +913,8 @@ fftconv_status build_device_tables(fftconv_plan_s* pl) {
 
 fftconv_status build_mp_tables(fftconv_plan_s* pl) {
     const Shape& s = pl->s;
-    std::vector<uint16_t> f1b = wide_f1b(4), i1a = wide_i1a(4), i2b = row_i2b(32);
+    std::vector<uint16_t> f1b = wide_f1b(4), i1a = wide_i1a(4), i2b = row_i2b(32),
+                          i2bs = row_i2b(32, true);
     std::vector<uint8_t> f2a = row_f2a(32);
     std::vector<uint16_t> twf = row_twiddles(32, false), two = mp_inner_twiddles();
     MpInnerParams& I = pl->mp;
@@ -921,6 +925,8 @@ fftconv_status build_mp_tables(fftconv_plan_s* pl) {
     I.i1a = d;
     if (upload(pl, i2b.data(), i2b.size() * 2, &d) != hipSuccess) return FFTCONV_ERR_HIP;
     I.i2b = d;
+    if (upload(pl, i2bs.data(), i2bs.size() * 2, &d) != hipSuccess) return FFTCONV_ERR_HIP;
+    I.i2bs = d;
     if (upload(pl, f2a.data(), f2a.size(), &d) != hipSuccess) return FFTCONV_ERR_HIP;
     I.f2a = d;
     if (upload(pl, twf.data(), twf.size() * 2, &d) != hipSuccess) return FFTCONV_ERR_HIP;
@@ -1354,6 +1360,7 @@ fftconv_status forward_impl(fftconv_plan_t plan, const void* u, const void* w,
         C2.S = 4096;
         C2.tw = plan->mp_tw2;
         MpInnerParams I = plan->mp;
+        I.skip_hi = skip_hi;
         I.B = (int)B;
         I.H = (int)H;
         I.ws = workspace;
@@ -1449,6 +1456,7 @@ fftconv_status forward_impl(fftconv_plan_t plan, const void* u, const void* w,
         W.kf = k_f;
         W.w = w;
         W.v = v;
+        W.skip_hi = skip_hi;
         W.ctr = (uint32_t*)workspace;
         e = launch_claim_reset(W.ctr, st);
         if (e == hipSuccess) e = launch_wide(io, s.wide_P, W, plan->lds_wide, st);
@@ -1497,9 +1505,12 @@ fftconv_status fftconv_forward_lowpass(fftconv_plan_t plan, const void* u,
                                        size_t workspace_bytes, void* stream) {
     if (!plan) return FFTCONV_ERR_INVALID_ARG;
     if (cutoff > plan->s.N) return FFTCONV_ERR_INVALID_ARG;
-    // the row kernel at N = 32 x 32 skips the tiles of k_b = 8..23, whose
-    // packed bins k in [256, 768) all lie beyond a cutoff below M/4
-    const int skip = (plan->use_row && plan->row_nb == 32 && cutoff < plan->s.M / 4) ? 1 : 0;
+    // the 32 x 32 engine (row kernel at N = 1024, wide kernel, multi-pass
+    // inner pass) skips the tiles of k_b = 8..23: the top digit of the bin,
+    // so those packed bins k lie in [M/4, 3M/4), all beyond a cutoff below
+    // M/4
+    const bool engine = (plan->use_row && plan->row_nb == 32) || plan->s.wide_P || plan->s.mp_P1;
+    const int skip = (engine && cutoff < plan->s.M / 4) ? 1 : 0;
     return forward_impl(plan, u, nullptr, nullptr, k_f, y, B, H, N, workspace,
                         workspace_bytes, stream, skip);
 }

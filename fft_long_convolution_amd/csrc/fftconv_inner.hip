@@ -85,7 +85,7 @@ __device__ __forceinline__ rfloat4 mma16_f16(uint2 a, uint2 b) {
                                                  __builtin_bit_cast(rhalf4, b), z, 0, 0, 0);
 }
 
-template <int IO>
+template <int IO, bool SK>
 __global__ void __launch_bounds__(256, 2) mp_inner_kernel(MpInnerParams prm) {
     constexpr int Q = 1024, T = 256, SLAB = 4096;
 
@@ -122,7 +122,7 @@ __global__ void __launch_bounds__(256, 2) mp_inner_kernel(MpInnerParams prm) {
         s_claim[1] = (int)(c1 < total ? c1 : total);
     }
     Regs E;
-    load_regs(E, prm.f2a, prm.i2b, prm.twf, lane);
+    load_regs(E, prm.f2a, SK ? prm.i2bs : prm.i2b, prm.twf, lane);
 
     // outer stage: each wave takes 16 column tiles of 16 columns; lane (g, x)
     // holds slab g / 2, rows n1 = 2 (g % 2) + e of column x, and after the
@@ -257,13 +257,13 @@ __global__ void __launch_bounds__(256, 2) mp_inner_kernel(MpInnerParams prm) {
 #pragma unroll
                 for (int mt = 0; mt < 4; ++mt) cfr[s][0][mt] = cf[(s * 2) * 256 + mt * 64 + lane];
             uint32_t z[2][2][4][2];
-            forward(s_buf + (2 * wave) * Q, s_f1b, E, lane, z[0]);
+            forward<SK>(s_buf + (2 * wave) * Q, s_f1b, E, lane, z[0]);
 #pragma unroll
             for (int s = 0; s < 2; ++s)
 #pragma unroll
                 for (int mt = 0; mt < 4; ++mt) cfr[s][1][mt] = cf[(s * 2 + 1) * 256 + mt * 64 + lane];
             __builtin_amdgcn_sched_barrier(0);
-            forward(s_buf + (2 * wave + 1) * Q, s_f1b, E, lane, z[1]);
+            forward<SK>(s_buf + (2 * wave + 1) * Q, s_f1b, E, lane, z[1]);
             __builtin_amdgcn_sched_barrier(0);
 
             uint4 a2[2][2][2];
@@ -272,13 +272,13 @@ __global__ void __launch_bounds__(256, 2) mp_inner_kernel(MpInnerParams prm) {
                 self_exchange(z[0], scr, g, zq);
 #pragma unroll
                 for (int kt = 0; kt < 2; ++kt) {
-                    pair_self(kt, x == 0, z[0], z[1], zq, cfr[0][kt], cfr[1][kt], a2[0][kt], a2[1][kt]);
+                    pair_self<SK>(kt, x == 0, z[0], z[1], zq, cfr[0][kt], cfr[1][kt], a2[0][kt], a2[1][kt]);
                     __builtin_amdgcn_sched_barrier(0);
                 }
             } else {
 #pragma unroll
                 for (int kt = 0; kt < 2; ++kt) {
-                    pair_elem(kt, z[0], z[1], cfr[0][kt], cfr[1][kt], a2[0][kt], a2[1][kt]);
+                    pair_elem<SK>(kt, z[0], z[1], cfr[0][kt], cfr[1][kt], a2[0][kt], a2[1][kt]);
                     __builtin_amdgcn_sched_barrier(0);
                 }
             }
@@ -287,9 +287,9 @@ __global__ void __launch_bounds__(256, 2) mp_inner_kernel(MpInnerParams prm) {
             if (tid == 0) s_claim[0] = (int)(c2 < total ? c2 : total);
             load_in(inext);
 
-            inverse(a2[0], s_i1a, E, lane, i1_base, s_buf + (2 * wave) * Q);
+            inverse<SK>(a2[0], s_i1a, E, lane, i1_base, s_buf + (2 * wave) * Q);
             __builtin_amdgcn_sched_barrier(0);
-            inverse(a2[1], s_i1a, E, lane, i1_base, s_buf + (2 * wave + 1) * Q);
+            inverse<SK>(a2[1], s_i1a, E, lane, i1_base, s_buf + (2 * wave + 1) * Q);
             __builtin_amdgcn_sched_barrier(0);
         }
         __syncthreads();
@@ -348,24 +348,21 @@ __global__ void __launch_bounds__(256, 2) mp_inner_kernel(MpInnerParams prm) {
 
 // ---------------------------------------------------------------------------
 
-hipError_t launch_mp_inner(int io, const MpInnerParams& p, int lds, hipStream_t s) {
-    const dim3 grid((unsigned)p.grid), blk(256);
-    if (io == IO_BF16) {
-        if (lds > 64 * 1024) {
-            hipError_t e = hipFuncSetAttribute((const void*)mp_inner_kernel<IO_BF16>,
-                                               hipFuncAttributeMaxDynamicSharedMemorySize, lds);
-            if (e != hipSuccess) return e;
-        }
-        hipLaunchKernelGGL(mp_inner_kernel<IO_BF16>, grid, blk, lds, s, p);
-    } else {
-        if (lds > 64 * 1024) {
-            hipError_t e = hipFuncSetAttribute((const void*)mp_inner_kernel<IO_F16>,
-                                               hipFuncAttributeMaxDynamicSharedMemorySize, lds);
-            if (e != hipSuccess) return e;
-        }
-        hipLaunchKernelGGL(mp_inner_kernel<IO_F16>, grid, blk, lds, s, p);
+template <int IO, bool SK>
+static hipError_t mp_inner_t(const MpInnerParams& p, int lds, hipStream_t s) {
+    if (lds > 64 * 1024) {
+        const hipError_t e = hipFuncSetAttribute((const void*)mp_inner_kernel<IO, SK>,
+                                                 hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+        if (e != hipSuccess) return e;
     }
+    hipLaunchKernelGGL((mp_inner_kernel<IO, SK>), dim3((unsigned)p.grid), dim3(256), lds, s, p);
     return hipGetLastError();
+}
+
+hipError_t launch_mp_inner(int io, const MpInnerParams& p, int lds, hipStream_t s) {
+    if (io == IO_BF16)
+        return p.skip_hi ? mp_inner_t<IO_BF16, true>(p, lds, s) : mp_inner_t<IO_BF16, false>(p, lds, s);
+    return p.skip_hi ? mp_inner_t<IO_F16, true>(p, lds, s) : mp_inner_t<IO_F16, false>(p, lds, s);
 }
 
 }  // namespace fftconv

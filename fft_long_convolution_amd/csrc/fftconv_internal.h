@@ -214,8 +214,10 @@ struct WideParams {
     const void* i1a;         // its inverse, A tiles [mt 4][ks 2][64]
     const void* f2a;         // 32-point stage over n_b, A tiles [mt 4][ks 2][64]
     const void* i2b;         // its inverse, B tiles [ks 2][jt 4][64]
+    const void* i2bs;        // the same with the band-limited K-step grouping
     const uint32_t* twf;     // per-lane W_1024 twiddles (packed f16)
     const uint32_t* two;     // outer twiddles W_M^{n' k1}, [k1-1][thread][column]
+    int skip_hi;             // band limit below M/4: skip the tiles of k_b = 8..23
 };
 hipError_t launch_wide(int io, int P, const WideParams& p, int lds_bytes,
                        hipStream_t s);
@@ -288,8 +290,10 @@ struct MpInnerParams {
     const void* i1a;
     const void* f2a;
     const void* i2b;
+    const void* i2bs;      // the same with the band-limited K-step grouping
     const uint32_t* twf;
     const uint32_t* two;   // W_4096^{n' m}, m = 0..4, [m][engine position of n'] (packed f16)
+    int skip_hi;           // band limit below M/4: skip the tiles of k_b = 8..23
 };
 hipError_t launch_mp_inner(int io, const MpInnerParams& p, int lds_bytes, hipStream_t s);
 

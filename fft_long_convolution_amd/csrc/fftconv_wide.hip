@@ -40,7 +40,7 @@ namespace fftconv {
 
 using namespace eng;
 
-template <int IO, int P, bool G>
+template <int IO, int P, bool G, bool SK>
 __global__ void __launch_bounds__(32 * P, 2) wide_kernel(WideParams prm) {
     constexpr int Q = 1024, M = P * Q, HALF = P / 2, T = 32 * P;
     constexpr int CPT = Q / T;   // outer-stage columns per thread
@@ -73,7 +73,7 @@ __global__ void __launch_bounds__(32 * P, 2) wide_kernel(WideParams prm) {
         s_claim[1] = (int)(c1 < total ? c1 : total);
     }
     Regs E;
-    load_regs(E, prm.f2a, prm.i2b, prm.twf, lane);
+    load_regs(E, prm.f2a, SK ? prm.i2bs : prm.i2b, prm.twf, lane);
 
     // ---- outer-stage geometry: n_b = tid & 31, n_a = na0 + j (j < CPT)
     const int nb = tid & 31, na0 = CPT * (tid >> 5);
@@ -194,13 +194,13 @@ __global__ void __launch_bounds__(32 * P, 2) wide_kernel(WideParams prm) {
 #pragma unroll
                 for (int mt = 0; mt < 4; ++mt) cfr[sub][0][mt] = cf[(sub * 2) * 256 + mt * 64 + lane];
             uint32_t z[2][2][4][2];   // [sub][kt][mt][e] packed f16 bins
-            forward(s_buf + (2 * wave) * Q, s_f1b, E, lane, z[0]);
+            forward<SK>(s_buf + (2 * wave) * Q, s_f1b, E, lane, z[0]);
 #pragma unroll
             for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
                 for (int mt = 0; mt < 4; ++mt) cfr[s2][1][mt] = cf[(s2 * 2 + 1) * 256 + mt * 64 + lane];
             __builtin_amdgcn_sched_barrier(0);
-            forward(s_buf + (2 * wave + 1) * Q, s_f1b, E, lane, z[1]);
+            forward<SK>(s_buf + (2 * wave + 1) * Q, s_f1b, E, lane, z[1]);
             __builtin_amdgcn_sched_barrier(0);
 
             // ---------------- spectrum product
@@ -208,7 +208,7 @@ __global__ void __launch_bounds__(32 * P, 2) wide_kernel(WideParams prm) {
             if (wave != 0) {
 #pragma unroll
                 for (int kt = 0; kt < 2; ++kt) {
-                    pair_elem(kt, z[0], z[1], cfr[0][kt], cfr[1][kt], a2[0][kt], a2[1][kt]);
+                    pair_elem<SK>(kt, z[0], z[1], cfr[0][kt], cfr[1][kt], a2[0][kt], a2[1][kt]);
                     __builtin_amdgcn_sched_barrier(0);
                 }
             } else {
@@ -217,7 +217,7 @@ __global__ void __launch_bounds__(32 * P, 2) wide_kernel(WideParams prm) {
                 self_exchange(z[0], scr, g, zq);
 #pragma unroll
                 for (int kt = 0; kt < 2; ++kt) {
-                    pair_self(kt, x == 0, z[0], z[1], zq, cfr[0][kt], cfr[1][kt], a2[0][kt], a2[1][kt]);
+                    pair_self<SK>(kt, x == 0, z[0], z[1], zq, cfr[0][kt], cfr[1][kt], a2[0][kt], a2[1][kt]);
                     __builtin_amdgcn_sched_barrier(0);
                 }
             }
@@ -228,9 +228,9 @@ __global__ void __launch_bounds__(32 * P, 2) wide_kernel(WideParams prm) {
             load_u(inext);
 
             // ---------------- inverse 1024-point DFT of both sub-rows
-            inverse(a2[0], s_i1a, E, lane, i1_base, s_buf + (2 * wave) * Q);
+            inverse<SK>(a2[0], s_i1a, E, lane, i1_base, s_buf + (2 * wave) * Q);
             __builtin_amdgcn_sched_barrier(0);
-            inverse(a2[1], s_i1a, E, lane, i1_base, s_buf + (2 * wave + 1) * Q);
+            inverse<SK>(a2[1], s_i1a, E, lane, i1_base, s_buf + (2 * wave + 1) * Q);
             __builtin_amdgcn_sched_barrier(0);
         }
         __syncthreads();
@@ -302,18 +302,18 @@ hipError_t launch_claim_reset(uint32_t* ctr, hipStream_t s) {
     return hipGetLastError();
 }
 
-template <bool G>
+template <bool G, bool SK>
 static hipError_t launch_wide_g(int io, int P, const WideParams& p, int lds, hipStream_t s) {
     const dim3 grid((unsigned)p.grid), blk((unsigned)(32 * P));
 #define FFTCONV_WIDE(IOT, PP)                                                              \
     do {                                                                                   \
         if (lds > 64 * 1024) {                                                             \
-            hipError_t e_ = hipFuncSetAttribute((const void*)wide_kernel<IOT, PP, G>,      \
+            hipError_t e_ = hipFuncSetAttribute((const void*)wide_kernel<IOT, PP, G, SK>,  \
                                                 hipFuncAttributeMaxDynamicSharedMemorySize, \
                                                 lds);                                      \
             if (e_ != hipSuccess) return e_;                                               \
         }                                                                                  \
-        hipLaunchKernelGGL((wide_kernel<IOT, PP, G>), grid, blk, lds, s, p);               \
+        hipLaunchKernelGGL((wide_kernel<IOT, PP, G, SK>), grid, blk, lds, s, p);           \
     } while (0)
     if (io == IO_BF16) {
         if (P == 4) FFTCONV_WIDE(IO_BF16, 4);
@@ -329,7 +329,9 @@ static hipError_t launch_wide_g(int io, int P, const WideParams& p, int lds, hip
 }
 
 hipError_t launch_wide(int io, int P, const WideParams& p, int lds, hipStream_t s) {
-    return p.w ? launch_wide_g<true>(io, P, p, lds, s) : launch_wide_g<false>(io, P, p, lds, s);
+    if (p.w) return launch_wide_g<true, false>(io, P, p, lds, s);
+    if (p.skip_hi) return launch_wide_g<false, true>(io, P, p, lds, s);
+    return launch_wide_g<false, false>(io, P, p, lds, s);
 }
 
 // Spectrum coefficients in the wide kernel's engine order:

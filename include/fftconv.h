@@ -195,9 +195,11 @@ fftconv_status fftconv_forward(fftconv_plan_t plan, const void *u,
 
 /* fftconv_forward for a spectrum from fftconv_kernel_spectrum_lowpass with
  * the same cutoff: the frequency-sparse convolution.  Kernels may skip the
- * blocks whose bins the cutoff zeroes (the register-resident kernel at
- * N = 1024 skips half of its innermost matrix products and pairing work when
- * cutoff < N/4); other kernels compute the zero bins.  A spectrum built with
+ * blocks whose bins the cutoff zeroes: with 16-bit data at N = 1024 and at
+ * N >= 4096, the 32 x 32 matrix-core stage (the whole transform at 1024,
+ * the innermost one at larger N) skips half of its second forward product,
+ * of its pairing work and of its first inverse product when cutoff < N/4;
+ * other kernels, and larger cutoffs, compute the zero bins.  A spectrum built with
  * a larger cutoff (or none) is not valid here.  Arguments and errors as
  * fftconv_forward; cutoff > N -> FFTCONV_ERR_INVALID_ARG. */
 fftconv_status fftconv_forward_lowpass(fftconv_plan_t plan, const void *u,

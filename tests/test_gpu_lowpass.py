@@ -1,8 +1,9 @@
 """GPU parity of the frequency-sparse (band-limited) convolution:
 fftconv_kernel_spectrum_lowpass + fftconv_forward_lowpass against the fp64
-oracle's band-limited FFT route.  At N = 1024 a cutoff below N/4 runs the
-register-resident kernel's variant that skips the matrix-core tiles of the
-zeroed bins; other lengths compute the zero bins."""
+oracle's band-limited FFT route.  A cutoff below N/4 runs the variants of
+the 32 x 32 engine (row kernel at N = 1024, wide kernel at 4K..16K,
+multi-pass inner pass at >= 32K) that skip the matrix-core tiles of the
+zeroed bins; other cutoffs and lengths compute the zero bins."""
 import sys
 
 import numpy as np
@@ -40,7 +41,10 @@ def _run(w, cutoff):
     (1024, "bf16", 3, 5, 255), (1024, "f16", 64, 3, 128),
     (1024, "bf16", 2, 7, 31), (1024, "bf16", 3, 5, 256),
     (1024, "f16", 3, 5, 700), (8192, "bf16", 2, 3, 1000),
-    (65536, "f16", 1, 3, 20000), (4194304, "bf16", 1, 1, 500000)])
+    (4096, "f16", 3, 2, 500), (16384, "bf16", 2, 3, 4095),
+    (8192, "f16", 2, 2, 2048), (65536, "f16", 1, 3, 20000),
+    (65536, "bf16", 2, 2, 16383), (262144, "f16", 1, 2, 3000),
+    (1048576, "bf16", 1, 1, 200000), (4194304, "bf16", 1, 1, 500000)])
 def test_lowpass(N, dtype, B, H, cutoff):
     w = inputs.Workload("lowpass", 260 + N.bit_length() + B, B, H, N, dtype,
                         "normal", "decay", "band-limited")
