@@ -240,6 +240,30 @@ __device__ __forceinline__ uint32_t rot_down(uint32_t v) {
 }
 
 
+// Kernel gradient, 4 Z_g for one bin from its value and its mirror partner
+// (not conjugated) of u and dy; W = exp(2 pi i k / M)
+__device__ __forceinline__ rhalf2 kg_self(uint32_t a, uint32_t ap, uint32_t d, uint32_t dp, rhalf2 W) {
+    const rhalf2 A = as_h2(a), Ap = as_h2(ap), Dv = as_h2(d), Dp = as_h2(dp);
+    const rhalf2 cAp = {Ap.x, -Ap.y}, cDp = {Dp.x, -Dp.y};
+    const rhalf2 E2 = A + cAp, O2 = A - cAp, Ed = Dv + cDp, Od = Dv - cDp;
+    const rhalf2 T = Od - hmul(Ed, W);
+    const rhalf2 two = {(_Float16)2.f, (_Float16)2.f};
+    return __builtin_elementwise_fma(hmulc(Dv, E2), two, hmulc(T, O2));
+}
+
+// The same for an element-wise pair: a, d the bin's values of u and dy, c, e
+// the conjugated mirror values held at the same position; returns 4 Z_g[k]
+// and, in the conjugated form of the partner region, 4 conj Z_g[-k].
+__device__ __forceinline__ void kg_pair(uint32_t a_, uint32_t c_, uint32_t d_, uint32_t e_, rhalf2 W,
+                                        rhalf2& RX, rhalf2& RY) {
+    const rhalf2 a = as_h2(a_), c = as_h2(c_), d = as_h2(d_), ee = as_h2(e_);
+    const rhalf2 E2 = a + c, O2 = a - c, Ed = d + ee, Od = d - ee;
+    const rhalf2 WE = hmul(Ed, W);
+    const rhalf2 two = {(_Float16)2.f, (_Float16)2.f};
+    RX = __builtin_elementwise_fma(hmulc(d, E2), two, hmulc(Od - WE, O2));
+    RY = __builtin_elementwise_fma(hmulc(ee, E2), two, hmulc(Od + WE, O2));
+}
+
 // LDS word address of (n_a, n_b) within a sub-row region: the engine reads
 // uint4 (it*2 + ks)*64 + lane holding n_a = 16 ks + 4 g + 0..3 and
 // n_b = kmap32(it, x).

@@ -1041,8 +1041,30 @@ int kgrad_wide_slices(const fftconv_plan_s* pl, size_t B, size_t H) {
     return n < 1 ? 1 : (int)n;
 }
 
+// The multi-pass engine kernel gradient (N >= 32K, 16-bit I/O): channel
+// chunks whose outer-transformed rows of u and of dy (all B of a channel)
+// each fit one workspace chunk; batches with more rows per channel take the
+// generic passes.
+bool kgrad_on_mp(const fftconv_plan_s* pl, size_t B) {
+    return pl->s.mp_P1 && pl->s.dtype != FFTCONV_F32 && B * pl->s.M * 4 <= kMpChunkBytes;
+}
+
+size_t kgrad_mp_channels(const fftconv_plan_s* pl, size_t B, size_t H) {
+    const size_t per_ch = (B ? B : 1) * pl->s.M * 4;
+    size_t hc = kMpChunkBytes / per_ch;
+    if (hc > H) hc = H;
+    return hc < 1 ? 1 : hc;
+}
+
 size_t kgrad_workspace_bytes(const fftconv_plan_s* pl, size_t B, size_t H) {
     if (kgrad_on_row(pl)) return (size_t)kgrad_row_slices(pl, B, H) * H * 64 * 32 * 4;
+    if (kgrad_on_mp(pl, B)) {
+        // rows of u and dy after the forward column passes, and one result
+        // row per channel of the chunk; the claim counters the column passes
+        // clear
+        const size_t hc = kgrad_mp_channels(pl, B, H);
+        return (2 * B + 1) * hc * pl->s.M * 4 + kClaimBytes;
+    }
     if (pl->s.wide_P)
         return (size_t)kgrad_wide_slices(pl, B, H) * H * (pl->s.wide_P / 2) * 64 * 64 * 4;
     const Shape& g = pl->grad->s;
@@ -1060,6 +1082,51 @@ int kgrad_lds(const Shape& g) {
 }
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+// Forward column pass(es) of the multi-pass path for one channel chunk:
+// channels h0 .. h0 + hc - 1 of all B rows of src ([B][H][N]) into
+// workspace rows b * hc + (h - h0), in the layout the inner passes read.
+hipError_t mp_cols_fwd(const fftconv_plan_s* plan, int io, const void* src, void* ws,
+                       uint32_t* ctr, size_t B, size_t H, size_t h0, size_t hc,
+                       hipStream_t st) {
+    const Shape& s = plan->s;
+    const long long rows = (long long)B * (long long)hc;
+    if (s.mp_P2 > 1) {
+        MpCol2Params D{};
+        D.rows = rows;
+        D.H = (int)H;
+        D.h0 = (int)h0;
+        D.hc = (int)hc;
+        D.M = (int)s.M;
+        D.tw1 = plan->mp_tw1;
+        D.tw2 = plan->mp_tw2;
+        D.u = src;
+        D.ws = ws;
+        D.ctr = ctr;
+        D.grid = (int)std::min<long long>(mp_col2_tiles(s.mp_P2, rows),
+                                          std::max<long long>(16, (2LL * plan->num_cu) & ~15LL));
+        if (plan->mp2m_a1) {
+            D.a1 = plan->mp2m_a1;
+            D.a2 = plan->mp2m_a2;
+            D.tm = plan->mp2m_tm;
+            D.grid = (int)std::min<long long>(rows * 128, plan->num_cu);
+            return launch_mp_col2m_fwd(io, D, st);
+        }
+        return launch_mp_col2(io, s.mp_P1, s.mp_P2, false, D, st);
+    }
+    MpColParams C{};
+    C.rows = rows;
+    C.H = (int)H;
+    C.h0 = (int)h0;
+    C.hc = (int)hc;
+    C.M = (int)s.M;
+    C.S = (int)(s.M / s.mp_P1);
+    C.tw = plan->mp_tw1;
+    C.u = src;
+    C.ws = ws;
+    C.ctr = ctr;
+    return launch_mp_col(io, s.mp_P1, 0, C, st);
+}
 
 // Channels per chunk of the multi-pass path: the passes run chunk by chunk
 // to bound the workspace (B * hc * M f16 complex, at most 1 GB).  Every
@@ -1618,6 +1685,67 @@ fftconv_status fftconv_backward(fftconv_plan_t plan, const void* u,
         W.pre = 0.25f / sqrtf((float)s.M);
         W.post = (float)s.M;
         e = launch_kgrad_wide(io, s.wide_P, W, st);
+        return e == hipSuccess ? FFTCONV_OK : FFTCONV_ERR_HIP;
+    }
+    if (kgrad_on_mp(plan, B)) {
+        const size_t hcm = kgrad_mp_channels(plan, B, H);
+        const size_t per = B * hcm * s.M * 4;
+        char* base = (char*)workspace;
+        void* wsu = base;
+        void* wsd = base + per;
+        void* wsg = base + 2 * per;
+        uint32_t* ctr = (uint32_t*)(base + 2 * per + hcm * s.M * 4);
+        const MpInnerParams& T = plan->mp;
+        e = hipSuccess;
+        for (size_t h0 = 0; h0 < H && e == hipSuccess; h0 += hcm) {
+            const size_t hc = H - h0 < hcm ? H - h0 : hcm;
+            e = mp_cols_fwd(plan, io, u, wsu, ctr, B, H, h0, hc, st);
+            if (e == hipSuccess) e = mp_cols_fwd(plan, io, dy, wsd, ctr, B, H, h0, hc, st);
+            if (e == hipSuccess) {
+                KgMpParams P{};
+                P.B = (int)B;
+                P.hc = (int)hc;
+                P.M = (int)s.M;
+                P.Po = T.Po;
+                P.P1 = T.P1;
+                P.P2 = T.P2;
+                P.wsu = wsu;
+                P.wsd = wsd;
+                P.wsg = wsg;
+                P.f1b = T.f1b;
+                P.i1a = T.i1a;
+                P.f2a = T.f2a;
+                P.i2b = T.i2b;
+                P.twf = T.twf;
+                P.two = T.two;
+                // accumulated 4 Z_g in unitary units (as the row engine)
+                P.pre = 0.25f / sqrtf((float)s.M);
+                e = launch_kgrad_mp(io, P, st);
+            }
+            if (e == hipSuccess) {
+                // inverse column passes of the channels' result rows into
+                // fp32 dk: the second level in place, then the first
+                MpColParams C{};
+                C.rows = (long long)hc;
+                C.H = (int)H;
+                C.h0 = (int)h0;
+                C.hc = (int)hc;
+                C.M = (int)s.M;
+                C.ws = wsg;
+                C.y = dk;
+                C.ctr = ctr;
+                C.post = (float)s.M;
+                if (s.mp_P2 > 1) {
+                    MpColParams C2 = C;
+                    C2.S = 4096;
+                    C2.tw = plan->mp_tw2;
+                    e = launch_mp_col(io, s.mp_P2, 2, C2, st);
+                }
+                C.S = (int)(s.M / s.mp_P1);
+                C.tw = plan->mp_tw1;
+                if (e == hipSuccess) e = launch_mp_col(io, s.mp_P1, 4, C, st);
+            }
+        }
         return e == hipSuccess ? FFTCONV_OK : FFTCONV_ERR_HIP;
     }
     KgradParams K{};

@@ -347,6 +347,363 @@ __global__ void __launch_bounds__(256, 2) mp_inner_kernel(MpInnerParams prm) {
 }
 
 // ---------------------------------------------------------------------------
+// Kernel gradient on the same units (page "FlashFFTConv: Efficient
+// Convolutions for Long Sequences with Tensor Cores", section 3: gradients
+// of an FFT convolution multiply by conjugate spectra; the input spectra are
+// recomputed, not kept).  One workgroup per (local channel hl, unit q): for
+// every batch row b the unit of u and of dy (workspace rows b * hc + hl,
+// after the forward column passes) goes through the 4-point stage and the
+// engine's forward transform, exactly as in the inner pass; the packed
+// gradient spectrum G = sum_b conj(U_b) DY_b is accumulated in fp32
+// registers, in the same element-wise pair form as the forward pairing:
+// with a, d the values of u and dy at a bin k of the wave's first region
+// and c, e the conjugated mirror values its second region holds there,
+//   4 Z_g[k]       = 2 conj(E2) d + conj(O') (Od' - W Ed2)
+//   4 conj Z_g[-k] = 2 conj(E2) e + conj(O') (Od' + W Ed2)
+// (E2 = a + c, O' = a - c, Ed2 = d + e, Od' = d - e, W = exp(2 pi i k / M)),
+// and wave 0 of the self unit pairs within its regions (k' <-> -k' through
+// LDS, k' <-> 1023 - k' one lane over).  Bin k of a position is
+// k_o + P_o (j + 4 k'), so W is the position's exp(2 pi i k' / 1024) times a
+// factor of the (unit, wave, region).  The result goes through the engine's
+// inverse and the inverse 4-point stage into result row hl.
+template <int IO, bool ONE, bool SELF>
+__global__ void __launch_bounds__(256, 2) kgrad_mp_kernel(KgMpParams prm) {
+    constexpr int Q = 1024, T = 256, SLAB = 4096;
+
+    extern __shared__ uint4 s_lds[];
+    uint4* s_f1b = s_lds;                              // [ks 2][jt 4][64]
+    uint4* s_i1a = s_f1b + 8 * 64;                     // [mt 4][ks 2][64]
+    uint32_t* s_two = (uint32_t*)(s_i1a + 8 * 64);     // W_4096^{n' m}, [m 5][engine position]
+    uint32_t* s_buf = s_two + 5 * Q;                   // [8 regions][Q]
+    uint32_t* s_scr = s_buf + 8 * Q;                   // [u, dy][39 k_b slots][16 x]
+    uint32_t* s_wb = s_scr + 2 * 39 * 16;              // [kt][mt][e][lane] exp(2 pi i k'/1024)
+    uint2* s_aop = (uint2*)(s_wb + 16 * 64);           // outer-stage A operands [4][64]
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int g = lane >> 4, x = lane & 15;
+    const int upr = prm.Po / 2;
+    const int lg_p1 = __builtin_ctz((unsigned)prm.P1);
+    // SELF: the self units (q = 0, one per channel); otherwise units 1 ..
+    // P_o/2 - 1 of every channel
+    int hl = (int)blockIdx.x, q = 0;
+    if constexpr (!SELF) {
+        hl = (int)(blockIdx.x / (unsigned)(upr - 1));
+        q = 1 + (int)blockIdx.x - hl * (upr - 1);
+    }
+    constexpr bool self = SELF;
+    auto sigma = [&](int ko) { return (ko & (prm.P1 - 1)) * prm.P2 + (ko >> lg_p1); };
+    const int sa = sigma(q), sb = sigma(q == 0 ? prm.Po / 2 : prm.Po - q);
+    const __amdgpu_buffer_rsrc_t ru = buf_rsrc(prm.wsu, -1), rd = buf_rsrc(prm.wsd, -1),
+                                 rg = buf_rsrc(prm.wsg, -1);
+
+    for (int i = tid; i < 8 * 64; i += T) {
+        s_f1b[i] = ((const uint4*)prm.f1b)[i];
+        s_i1a[i] = ((const uint4*)prm.i1a)[i];
+    }
+    for (int i = tid; i < 5 * Q / 4; i += T) ((uint4*)s_two)[i] = ((const uint4*)prm.two)[i];
+    if (tid < 64) {
+#pragma unroll
+        for (int v = 0; v < 4; ++v) s_aop[v * 64 + lane] = outer4_a(v & 1, v >> 1, g, x);
+    } else if (tid < 128) {
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+                for (int e = 0; e < 2; ++e) {
+                    const int kp = kmap32(kt, x) + 32 * rmid_perm(8 * mt + 2 * g + e, 32);
+                    float sn, cs;
+                    sincospif(2.f * (float)kp / (float)Q, &sn, &cs);
+                    s_wb[((kt * 4 + mt) * 2 + e) * 64 + lane] = pk2(cs, sn);
+                }
+    }
+    Regs E;
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) E.f2a[mt][ks] = ((const uint4*)prm.f2a)[(mt * 2 + ks) * 64 + lane];
+#pragma unroll
+    for (int it = 0; it < 2; ++it)
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) E.twf[it][kt][r] = prm.twf[lane * 16 + (it * 2 + kt) * 4 + r];
+
+    // W factor of the wave's regions: bin k = k_o + P_o (j + 4 k') with
+    // (k_o, j) the wave's (slab outer bin, 4-point output); wave 0 of the
+    // self unit: k = P_o (0 + 4 k') and P_o (2 + 4 k')
+    uint32_t wsub[2];
+    {
+        int ko = q, j = wave;
+        if (self) {
+            if (wave == 1) {
+                ko = 0;
+                j = 1;
+            } else if (wave >= 2) {
+                ko = prm.Po / 2;
+                j = wave - 2;
+            }
+        }
+        const float inv_m = 1.f / (float)prm.M;
+        float sn, cs;
+        if (self && wave == 0) {
+            sincospif(2.f * (float)(2 * prm.Po) * inv_m, &sn, &cs);
+            wsub[0] = pk2(1.f, 0.f);
+            wsub[1] = pk2(cs, sn);
+        } else {
+            sincospif(2.f * (float)(ko + prm.Po * j) * inv_m, &sn, &cs);
+            wsub[0] = wsub[1] = pk2(cs, sn);
+        }
+    }
+
+    // ---- geometry of the 4-point stage (as the inner pass)
+    const int sl_g = g >> 1;
+    constexpr int TPW = 16;
+    auto buf_word = [&](int blk) {
+        int xv = x;
+        asm volatile("" : "+v"(xv));
+        const int xx1 = xv == 0 ? 0 : 16 - xv;
+        return eng_addr(8 * wave + 4 * (blk >> 1), blk & 1, (blk & 1) ? xx1 : xv) >> 2;
+    };
+    auto col_of = [&](int i) { return 32 * (8 * wave + 4 * (i >> 3) + (i & 3)) + 16 * ((i >> 2) & 1) + x; };
+    const unsigned vs = (unsigned)(((sl_g ? sb : sa) * SLAB + col_of(0) + 16 * (g & 1)) * 4);
+    // forward 4-point stage of workspace row `row` of buffer r into s_buf
+    auto outer_fwd = [&](__amdgpu_buffer_rsrc_t r, int row) {
+        uint2 xin[TPW];
+        const int srow = (int)(row * prm.M * 4);
+#pragma unroll
+        for (int i = 0; i < TPW; ++i) {
+            if ((i >> 2) & 1) continue;
+            const int d = 4 * (col_of(i) - col_of(0));
+            xin[i].x = __builtin_amdgcn_raw_buffer_load_b32(r, vs + d, srow, 2);
+            xin[i].y = __builtin_amdgcn_raw_buffer_load_b32(r, vs + d, srow + 4 * Q, 2);
+            xin[i + 4].x = __builtin_amdgcn_raw_buffer_load_b32(r, vs + d, srow + 8 * Q, 2);
+            xin[i + 4].y = __builtin_amdgcn_raw_buffer_load_b32(r, vs + d, srow + 12 * Q, 2);
+        }
+#pragma unroll
+        for (int i = 0; i < TPW; ++i) {
+            if ((i >> 2) & 1) continue;
+            swap16(xin[i].x, xin[i + 4].x);
+            swap16(xin[i].y, xin[i + 4].y);
+        }
+        const uint2 af = s_aop[(self ? 1 : 0) * 64 + lane];
+        const uint4* tw0 = (const uint4*)(s_two + region_twiddle(self, 2 * g) * Q);
+        const uint4* tw1 = (const uint4*)(s_two + region_twiddle(self, 2 * g + 1) * Q);
+        uint4* b0 = (uint4*)(s_buf + 2 * g * Q);
+        uint4* b1 = (uint4*)(s_buf + (2 * g + 1) * Q);
+#pragma unroll
+        for (int blk = 0; blk < 4; ++blk) {
+            uint32_t v0[4], v1[4];
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const rfloat4 c = mma16_f16(af, xin[4 * blk + k]);
+                v0[k] = pk2(c[0], c[1]);
+                v1[k] = pk2(c[2], c[3]);
+            }
+            const int w4 = buf_word(blk);
+            const uint4 t0 = tw0[w4], t1 = tw1[w4];
+            const uint32_t t0a[4] = {t0.x, t0.y, t0.z, t0.w}, t1a[4] = {t1.x, t1.y, t1.z, t1.w};
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                v0[k] = as_u32(hmul(as_h2(v0[k]), as_h2(t0a[k])));
+                v1[k] = as_u32(hmul(as_h2(v1[k]), as_h2(t1a[k])));
+            }
+            b0[w4] = make_uint4(v0[0], v0[1], v0[2], v0[3]);
+            b1[w4] = make_uint4(v1[0], v1[1], v1[2], v1[3]);
+        }
+    };
+    __syncthreads();
+
+    // fp32 sums over the batch, or with a batch of one the scaled products
+    // straight into the inverse operands
+    float2 acc[ONE ? 1 : 2][2][4][2];   // [region][kt][mt][e]
+    uint32_t pz1[ONE ? 2 : 1][2][4][2];
+    if constexpr (!ONE) {
+#pragma unroll
+        for (int r = 0; r < 2; ++r)
+#pragma unroll
+            for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+                for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+                    for (int e = 0; e < 2; ++e) acc[r][kt][mt][e] = make_float2(0.f, 0.f);
+    }
+    auto add = [&](int r, int kt, int mt, int e, rhalf2 R) {
+        if constexpr (ONE) {
+            pz1[r][kt][mt][e] = pk2((float)R.x * prm.pre, (float)R.y * prm.pre);
+        } else {
+            acc[r][kt][mt][e].x += (float)R.x;
+            acc[r][kt][mt][e].y += (float)R.y;
+        }
+    };
+    uint32_t* scr_u = s_scr + x;
+    uint32_t* scr_d = s_scr + 39 * 16 + x;
+    for (int b = 0; b < (ONE ? 1 : prm.B); ++b) {
+        const int row = b * prm.hc + hl;
+        uint32_t zu[2][2][4][2], zd[2][2][4][2];   // [region][kt][mt][e]
+        outer_fwd(ru, row);
+        __syncthreads();
+        forward(s_buf + (2 * wave) * Q, s_f1b, E, lane, zu[0]);
+        forward(s_buf + (2 * wave + 1) * Q, s_f1b, E, lane, zu[1]);
+        __syncthreads();
+        outer_fwd(rd, row);
+        __syncthreads();
+        forward(s_buf + (2 * wave) * Q, s_f1b, E, lane, zd[0]);
+        forward(s_buf + (2 * wave + 1) * Q, s_f1b, E, lane, zd[1]);
+        if (!(self && wave == 0)) {
+#pragma unroll
+            for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+                for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+                    for (int e = 0; e < 2; ++e) {
+                        const rhalf2 W = hmul(as_h2(s_wb[((kt * 4 + mt) * 2 + e) * 64 + lane]), as_h2(wsub[0]));
+                        rhalf2 RX, RY;
+                        kg_pair(zu[0][kt][mt][e], zu[1][kt][mt][e], zd[0][kt][mt][e], zd[1][kt][mt][e], W,
+                                RX, RY);
+                        add(0, kt, mt, e, RX);
+                        add(1, kt, mt, e, RY);
+                    }
+        } else {
+            uint32_t qu[4][2], qd[4][2];
+            self_exchange(zu[0], scr_u, g, qu);
+            self_exchange(zd[0], scr_d, g, qd);
+            const bool l0 = (x == 0);
+#pragma unroll
+            for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+                for (int mt = 0; mt < 4; ++mt) {
+                    const int pm = (mt + 2) & 3;
+#pragma unroll
+                    for (int e = 0; e < 2; ++e) {
+                        uint32_t nu, nd;
+                        if (kt == 0) {
+                            nu = l0 ? qu[mt][e] : zu[0][1][pm][e];
+                            nd = l0 ? qd[mt][e] : zd[0][1][pm][e];
+                        } else {
+                            nu = l0 ? zu[0][1][pm][e] : zu[0][0][pm][e];
+                            nd = l0 ? zd[0][1][pm][e] : zd[0][0][pm][e];
+                        }
+                        const uint32_t rpu = kt == 0 ? rot_up(zu[1][1][pm][e]) : rot_down(zu[1][0][pm][e]);
+                        const uint32_t rpd = kt == 0 ? rot_up(zd[1][1][pm][e]) : rot_down(zd[1][0][pm][e]);
+                        const rhalf2 W0 = as_h2(s_wb[((kt * 4 + mt) * 2 + e) * 64 + lane]);
+                        const rhalf2 W1 = hmul(W0, as_h2(wsub[1]));
+                        const rhalf2 R0 = kg_self(zu[0][kt][mt][e], nu, zd[0][kt][mt][e], nd, W0);
+                        const rhalf2 R1 = kg_self(zu[1][kt][mt][e], rpu, zd[1][kt][mt][e], rpd, W1);
+                        add(0, kt, mt, e, R0);
+                        add(1, kt, mt, e, R1);
+                    }
+                }
+        }
+        __syncthreads();
+    }
+
+    // ---- inverse of the accumulated spectrum: engine, then the 4-point stage
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+        for (int jt = 0; jt < 4; ++jt) E.i2b[ks][jt] = ((const uint4*)prm.i2b)[(ks * 4 + jt) * 64 + lane];
+    uint4 a2[2][2][2];   // [region][kt][ks]
+#pragma unroll
+    for (int r = 0; r < 2; ++r)
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt) {
+            uint32_t pz[4][2];
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+                for (int e = 0; e < 2; ++e) {
+                    if constexpr (ONE)
+                        pz[mt][e] = pz1[r][kt][mt][e];
+                    else
+                        pz[mt][e] = pk2(acc[r][kt][mt][e].x * prm.pre, acc[r][kt][mt][e].y * prm.pre);
+                }
+            pack_a2(pz, a2[r][kt]);
+        }
+    const int i1_base = (16 * (g >> 1) + x) * 4 + 2 * (g & 1);
+    inverse(a2[0], s_i1a, E, lane, i1_base, s_buf + (2 * wave) * Q);
+    inverse(a2[1], s_i1a, E, lane, i1_base, s_buf + (2 * wave + 1) * Q);
+    __syncthreads();
+    {
+        const uint2 ai = s_aop[(self ? 3 : 2) * 64 + lane];
+        const uint4* tw0 = (const uint4*)(s_two + region_twiddle(self, 2 * g) * Q);
+        const uint4* tw1 = (const uint4*)(s_two + region_twiddle(self, 2 * g + 1) * Q);
+        const uint4* b0 = (const uint4*)(s_buf + 2 * g * Q);
+        const uint4* b1 = (const uint4*)(s_buf + (2 * g + 1) * Q);
+        const int srow = (int)(hl * prm.M * 4);
+#pragma unroll
+        for (int nah = 0; nah < 2; ++nah) {
+            uint32_t o[2][4][2];   // [n_b half][k][e]
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int blk = 2 * nah + h;
+                const int w4 = buf_word(blk);
+                const uint4 r0 = b0[w4], r1 = b1[w4], t0 = tw0[w4], t1 = tw1[w4];
+                const uint32_t r0a[4] = {r0.x, r0.y, r0.z, r0.w}, r1a[4] = {r1.x, r1.y, r1.z, r1.w};
+                const uint32_t t0a[4] = {t0.x, t0.y, t0.z, t0.w}, t1a[4] = {t1.x, t1.y, t1.z, t1.w};
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    uint2 bv;
+                    bv.x = as_u32(hmulc(as_h2(r0a[k]), as_h2(t0a[k])));
+                    bv.y = as_u32(hmulc(as_h2(r1a[k]), as_h2(t1a[k])));
+                    const rfloat4 c = mma16_f16(ai, bv);
+                    o[h][k][0] = pk2(c[0], c[1]);
+                    o[h][k][1] = pk2(c[2], c[3]);
+                }
+            }
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                swap16(o[0][k][0], o[1][k][0]);
+                swap16(o[0][k][1], o[1][k][1]);
+                const int d = col_of(8 * nah + k) - col_of(0);
+                __builtin_amdgcn_raw_buffer_store_b32(o[0][k][0], rg, vs + 4 * d, srow, 2);
+                __builtin_amdgcn_raw_buffer_store_b32(o[0][k][1], rg, vs + 4 * d, srow + 4 * Q, 2);
+                __builtin_amdgcn_raw_buffer_store_b32(o[1][k][0], rg, vs + 4 * d, srow + 8 * Q, 2);
+                __builtin_amdgcn_raw_buffer_store_b32(o[1][k][1], rg, vs + 4 * d, srow + 12 * Q, 2);
+            }
+        }
+    }
+}
+
+int kgrad_mp_lds() {
+    return 16 * 64 * 16 + (5 + 8) * 1024 * 4 + 2 * 39 * 16 * 4 + 16 * 64 * 4 + 4 * 64 * 8;
+}
+
+template <int IO, bool ONE>
+static hipError_t kgrad_mp_t(const KgMpParams& p, long long grid, hipStream_t s) {
+    const int lds = kgrad_mp_lds();
+    hipError_t e = hipFuncSetAttribute((const void*)kgrad_mp_kernel<IO, ONE, true>,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+    if (e == hipSuccess)
+        e = hipFuncSetAttribute((const void*)kgrad_mp_kernel<IO, ONE, false>,
+                                hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+    if (e != hipSuccess) return e;
+    // the self units (one per channel, the longer workgroups: their wave 0
+    // pairs within its regions) first, then the pair units
+    hipLaunchKernelGGL((kgrad_mp_kernel<IO, ONE, true>), dim3((unsigned)p.hc), dim3(256), lds, s, p);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const long long npair = grid - p.hc;
+    hipLaunchKernelGGL((kgrad_mp_kernel<IO, ONE, false>), dim3((unsigned)npair), dim3(256), lds, s, p);
+    return hipGetLastError();
+}
+
+hipError_t launch_kgrad_mp(int io, const KgMpParams& p, hipStream_t s) {
+    if (p.hc <= 0 || p.B <= 0) return hipSuccess;
+    const int upr = p.Po / 2;
+    if (p.Po < 8 || (p.Po & (p.Po - 1)) || (p.P1 & (p.P1 - 1)) || p.P1 * p.P2 != p.Po ||
+        p.M != p.Po * 4096)
+        return hipErrorInvalidValue;
+    const long long grid = (long long)p.hc * upr;
+    // buffer offsets of the workspace rows stay within 31 bits
+    if (grid > 0x7fffffffLL || (long long)p.B * p.hc * p.M * 4 > 0x7fffffffLL) return hipErrorInvalidValue;
+    if (io == IO_BF16)
+        return p.B == 1 ? kgrad_mp_t<IO_BF16, true>(p, grid, s) : kgrad_mp_t<IO_BF16, false>(p, grid, s);
+    return p.B == 1 ? kgrad_mp_t<IO_F16, true>(p, grid, s) : kgrad_mp_t<IO_F16, false>(p, grid, s);
+}
+
+// ---------------------------------------------------------------------------
 
 template <int IO, bool SK>
 static hipError_t mp_inner_t(const MpInnerParams& p, int lds, hipStream_t s) {

@@ -245,7 +245,11 @@ struct MpColParams {
     const void* v;         // output gate (layout of y) or null
     void* ws;
     uint32_t* ctr;         // first pass: clears the inner pass's counters
+    float post;            // mode 4 (inverse, fp32 output): output scale
 };
+// mode 0: forward first level from u; 1: forward second level (in place);
+// 2: inverse second level (in place); 3: inverse first level into y (I/O
+// type); 4: the same into fp32 rows y scaled by post
 hipError_t launch_mp_col(int io, int P, int mode, const MpColParams& p, hipStream_t s);
 
 // Both outer levels of a two-level plan in one pass (tiles of 512 / P2
@@ -296,6 +300,28 @@ struct MpInnerParams {
     int skip_hi;           // band limit below M/4: skip the tiles of k_b = 8..23
 };
 hipError_t launch_mp_inner(int io, const MpInnerParams& p, int lds_bytes, hipStream_t s);
+
+// Kernel gradient on the multi-pass engine: one workgroup per (local
+// channel, unit of two slabs); reads the outer-transformed rows of u and dy
+// (workspace rows b * hc + hl) and writes the channel's packed gradient
+// spectrum, inverse-transformed by the engine and the 4-point stage, to
+// result row hl (the layout the inverse column passes read).
+struct KgMpParams {
+    int B, hc, M;
+    int Po, P1, P2;
+    const void* wsu;
+    const void* wsd;
+    void* wsg;
+    const void* f1b;       // the multi-pass plan's engine tables
+    const void* i1a;
+    const void* f2a;
+    const void* i2b;
+    const uint32_t* twf;
+    const uint32_t* two;
+    float pre;             // scale of the accumulated 4 Z_g before the inverse
+};
+int kgrad_mp_lds();
+hipError_t launch_kgrad_mp(int io, const KgMpParams& p, hipStream_t s);
 
 struct MpCoefParams {
     int M, L, Po;

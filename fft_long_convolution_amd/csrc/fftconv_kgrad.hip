@@ -339,17 +339,6 @@ hipError_t launch_kgrad_row(int io, const KgRowParams& p, hipStream_t s) {
 // ---------------------------------------------------------------------------
 using namespace eng;
 
-// 4 Z_g for one bin from its value and its mirror partner (not conjugated)
-// of u and dy; W = exp(2 pi i k / M)
-__device__ __forceinline__ rhalf2 kg_self(uint32_t a, uint32_t ap, uint32_t d, uint32_t dp, rhalf2 W) {
-    const rhalf2 A = as_h2(a), Ap = as_h2(ap), Dv = as_h2(d), Dp = as_h2(dp);
-    const rhalf2 cAp = {Ap.x, -Ap.y}, cDp = {Dp.x, -Dp.y};
-    const rhalf2 E2 = A + cAp, O2 = A - cAp, Ed = Dv + cDp, Od = Dv - cDp;
-    const rhalf2 T = Od - hmul(Ed, W);
-    const rhalf2 two = {(_Float16)2.f, (_Float16)2.f};
-    return __builtin_elementwise_fma(hmulc(Dv, E2), two, hmulc(T, O2));
-}
-
 template <int IO, int P>
 __global__ void __launch_bounds__(32 * P, 2) kgrad_wide_kernel(KgWideParams K) {
     constexpr int Q = 1024, M = P * Q, HALF = P / 2, T = 32 * P;

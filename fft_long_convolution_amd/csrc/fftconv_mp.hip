@@ -109,9 +109,18 @@ __global__ void __launch_bounds__(256) mp_col_kernel(MpColParams prm) {
             for (int n = 0; n < P / 2; ++n)
                 z[n] = z[n] * f2_from_io<IO>(__builtin_nontemporal_load(&g[(long long)n * prm.S]));
         }
-        uint32_t* y = (uint32_t*)prm.y + mrow * (long long)(prm.M / 2) + c;
+        if constexpr (MODE == 4) {
+            // fp32 rows (the kernel gradient): t = 2m, 2m + 1 as one float2
+            float2* y = (float2*)prm.y + mrow * (long long)(prm.M / 2) + c;
 #pragma unroll
-        for (int n = 0; n < P / 2; ++n) __builtin_nontemporal_store(pk2io<IO>(z[n].x, z[n].y), &y[(long long)n * prm.S]);
+            for (int n = 0; n < P / 2; ++n)
+                y[(long long)n * prm.S] = make_float2(z[n].x * prm.post, z[n].y * prm.post);
+        } else {
+            uint32_t* y = (uint32_t*)prm.y + mrow * (long long)(prm.M / 2) + c;
+#pragma unroll
+            for (int n = 0; n < P / 2; ++n)
+                __builtin_nontemporal_store(pk2io<IO>(z[n].x, z[n].y), &y[(long long)n * prm.S]);
+        }
     }
 }
 
@@ -895,6 +904,7 @@ hipError_t col_launch(int mode, const MpColParams& p, hipStream_t s) {
     case 0: hipLaunchKernelGGL((mp_col_kernel<IO, P, 0>), grid, blk, 0, s, p); break;
     case 1: hipLaunchKernelGGL((mp_col_kernel<IO, P, 1>), grid, blk, 0, s, p); break;
     case 2: hipLaunchKernelGGL((mp_col_kernel<IO, P, 2>), grid, blk, 0, s, p); break;
+    case 4: hipLaunchKernelGGL((mp_col_kernel<IO, P, 4>), grid, blk, 0, s, p); break;
     default: hipLaunchKernelGGL((mp_col_kernel<IO, P, 3>), grid, blk, 0, s, p); break;
     }
     return hipGetLastError();

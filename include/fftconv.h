@@ -230,9 +230,13 @@ fftconv_status fftconv_forward_gated(fftconv_plan_t plan, const void *u,
                                      size_t H, size_t N, void *workspace,
                                      size_t workspace_bytes, void *stream);
 
-/* Bytes of the workspace fftconv_backward needs for B x H rows (the
- * larger of the forward call's and the kernel gradient's: 0 up to N = 8192,
- * else two B*H x N and one H x N fp32 complex rows). */
+/* Bytes of the workspace fftconv_backward needs for B x H rows: the larger
+ * of the forward call's and the kernel gradient's.  The gradient needs
+ * per-slice partial spectra on the row and wide engines (N = 1K..16K,
+ * 16-bit I/O), for N >= 32K with 16-bit I/O the outer-transformed rows of
+ * u and dy of one channel chunk plus one result row per channel (f16
+ * complex, chunks of at most 1 GB per buffer), and otherwise two B*H x N
+ * and one H x N fp32 complex rows (0 for fused fp32 plans). */
 size_t fftconv_backward_workspace_bytes(fftconv_plan_t plan, size_t B, size_t H);
 
 /* Backward pass of the causal convolution y = (u * k)[0:N] (page
@@ -250,9 +254,13 @@ size_t fftconv_backward_workspace_bytes(fftconv_plan_t plan, size_t B, size_t H)
  *     or NULL to skip the kernel gradient; not both NULL.
  *  workspace: fftconv_backward_workspace_bytes(plan, B, H) bytes.
  * du runs the forward kernels on dy with the adjoint spectrum (the same
- * cost as a forward call); dk runs the LDS-staged kernels on u and dy,
- * accumulating conj(U) DY over the batch per channel in registers, then
- * one inverse transform per channel.  B = 0 gives dk = 0.  The input
+ * cost as a forward call); dk recomputes the spectra of u and dy,
+ * accumulates conj(U) DY over the batch per channel in fp32 registers and
+ * runs one inverse transform per channel: on the matrix-core engine of the
+ * forward kernels for 16-bit I/O (the row kernel's at N = 1024, the wide
+ * kernel's at 4K..16K, the multi-pass column and inner passes at N >= 32K
+ * when one channel's B rows fit 1 GB of f16 complex), on the LDS-staged
+ * kernels otherwise.  B = 0 gives dk = 0.  The input
  * gradient of the other kinds is fftconv_forward with the matching adjoint
  * spectrum.  Errors as fftconv_forward. */
 fftconv_status fftconv_backward(fftconv_plan_t plan, const void *u,

@@ -1,8 +1,9 @@
 """GPU parity of the backward pass of the causal convolution through the C
 ABI entry point fftconv_backward: the input gradient (the forward kernels
-with the adjoint spectrum) and the kernel gradient (LDS-staged kernels
-accumulating conj(U) DY per channel), against the fp64 oracle's
-definitions and convolution-theorem routes.  dk is fp32 for every I/O
+with the adjoint spectrum) and the kernel gradient (conj(U) DY accumulated
+per channel: on the row, wide and multi-pass engines for 16-bit I/O, on
+LDS-staged kernels otherwise), against the fp64 oracle's definitions and
+convolution-theorem routes.  dk is fp32 for every I/O
 type; its bar is the I/O type's (the inputs' quantisation is exact in the
 oracle, the error is the transforms').
 """
@@ -29,15 +30,17 @@ def _say(*a):
     (1024, "f32", 2, 2), (2048, "f16", 3, 2),
     (4096, "bf16", 2, 3), (4096, "f16", 1, 1), (8192, "f16", 3, 2),
     (8192, "bf16", 17, 5), (16384, "bf16", 2, 3), (16384, "f16", 4, 2),
-    (32768, "f32", 1, 2), (65536, "f16", 2, 1), (262144, "bf16", 1, 2),
-    (1048576, "f16", 1, 1), (4194304, "bf16", 1, 1)])
+    (32768, "f32", 1, 2), (32768, "bf16", 3, 2), (65536, "f16", 2, 1),
+    (131072, "f16", 2, 3), (262144, "bf16", 1, 2), (524288, "bf16", 2, 1),
+    (1048576, "f16", 1, 1), (2097152, "f16", 1, 2), (4194304, "bf16", 1, 1)])
 def test_backward(N, dtype, B, H):
     # the row engine at N = 1024 and the wide engine at N = 4K..16K with
     # 16-bit I/O (batch slices of one row up to more rows than slices), the
-    # LDS-staged kernel-gradient kernel elsewhere up to N = 8192 (two lines
-    # per workgroup), multi-pass (outer
-    # passes + accumulating inner pass + outer inverse) above; the input
-    # gradient through every forward family
+    # multi-pass engine at N >= 32K with 16-bit I/O (forward column passes
+    # of u and dy, the accumulating inner pass on one- and two-level outer
+    # factors, the inverse column passes into fp32 dk), the LDS-staged
+    # kernel-gradient kernels for fp32; the input gradient through every
+    # forward family
     w = inputs.Workload("bwd", 240 + N.bit_length() + B, B, H, N, dtype,
                         "normal", "decay", "backward")
     du, dk, u, dy, k = run_gpu_backward(w)
@@ -80,12 +83,13 @@ def test_backward_pieces_and_errors():
     assert L.fftconv_backward(conv._plan, u.data_ptr(), dy.data_ptr(), None,
                               None, dk.data_ptr() + 4, 3, 2, 1024, None, 0,
                               None) == 3
-    # a multi-pass kernel gradient needs its workspace
+    # a multi-pass kernel gradient needs its workspace (rows of u, dy and the
+    # result in f16 complex)
     conv2 = fc.FFTConv(32768, dtype="f16")
     u2 = torch.randn(1, 1, 32768, device="cuda").half()
     dk2 = torch.empty(1, 32768, device="cuda")
     need = conv2.backward_workspace_bytes(1, 1)
-    assert need >= 3 * 32768 * 8
+    assert need >= 3 * 32768 * 4
     assert L.fftconv_backward(conv2._plan, u2.data_ptr(), u2.data_ptr(), None,
                               None, dk2.data_ptr(), 1, 1, 32768, None, 0,
                               None) == 4
@@ -103,3 +107,34 @@ def test_backward_full_size(name):
     _say("  du rel_l2", edu, "dk rel_l2", edk)
     assert edu < TOL[w.dtype]
     assert edk < TOL[w.dtype]
+
+
+def test_backward_channel_chunks():
+    # the multi-pass kernel gradient runs over chunks of channels whose rows
+    # of u and dy fit the 1 GB workspace chunk (here two channels of 128
+    # rows at N = 1M): channels on both sides of the chunk boundary are
+    # checked at sampled lags by the definition
+    import torch
+    from fft_long_convolution_amd.fftconv import FFTConv
+    N, B, H, dtype = 1048576, 128, 3, "f16"
+    w = inputs.Workload("kchunk", 261, B, H, N, dtype, "normal", "decay", "kgrad chunks")
+    conv = FFTConv(N, dtype=dtype)
+    u = inputs.input_rows(w)
+    dy = inputs.dy_rows(w)
+    _say("kgrad channel chunks", N, B, H, dtype)
+    du, dk = conv.backward(to_torch(u, dtype).view(B, H, N), to_torch(dy, dtype).view(B, H, N),
+                           None, need_du=False)
+    torch.cuda.synchronize()
+    assert du is None
+    got = dk.cpu().numpy().astype(np.float64)
+    del dk
+    rng = np.random.default_rng(7)
+    js = np.concatenate([[0, 1, N - 1], rng.integers(0, N, 5)])
+    hs = np.repeat(np.arange(H), len(js))
+    jj = np.tile(js, H)
+    u64 = oracle.to_f64(u, dtype).reshape(B * H, N)
+    dy64 = oracle.to_f64(dy, dtype).reshape(B * H, N)
+    want = oracle.kgrad_points(u64, dy64, H, hs, jj, "causal", np.arange(B * H) % H)
+    err = oracle.rel_l2(got[hs, jj], want)
+    _say("  sampled dk rel_l2", err)
+    assert err < 1.5 * TOL[dtype]
