@@ -1017,28 +1017,40 @@ int kgrad_splits(const fftconv_plan_s* pl, size_t B, size_t H) {
     return n < 1 ? 1 : (int)n;
 }
 
-// The row-engine kernel gradient (N = 1024, 16-bit I/O): batch slices per
-// channel so that the (channel, slice) waves cover the GPU a few times.
+// The row-engine kernel gradient (N = 1024, 16-bit I/O).
 bool kgrad_on_row(const fftconv_plan_s* pl) {
     return pl->use_row && pl->row_nb == 32 && pl->s.dtype != FFTCONV_F32;
 }
 
+// Batch slices per channel for the engine kernel gradients: the (channel,
+// slice) tasks run `at_once` at a time, each over ceil(B / S) rows, so the
+// time goes as rounds x rows per task; the smallest S (fewest partial rows
+// to sum) of the minimum, at most 64.
+int kgrad_best_slices(size_t B, size_t H, long long at_once) {
+    if (B == 0 || H == 0 || at_once <= 0) return 1;
+    const long long smax = std::min<long long>((long long)B, 64);
+    long long best = 1, best_cost = -1;
+    for (long long sl = 1; sl <= smax; ++sl) {
+        const long long rounds = ((long long)H * sl + at_once - 1) / at_once;
+        const long long rows = ((long long)B + sl - 1) / sl;
+        const long long cost = rounds * rows;
+        if (best_cost < 0 || cost < best_cost) {
+            best_cost = cost;
+            best = sl;
+        }
+    }
+    return (int)best;
+}
+
+// Row engine: one wave per task, eight-wave workgroups, one per CU.
 int kgrad_row_slices(const fftconv_plan_s* pl, size_t B, size_t H) {
-    if (B == 0 || H == 0) return 1;
-    long long n = (16LL * pl->num_cu + (long long)H - 1) / (long long)H;
-    if (n > (long long)B) n = (long long)B;
-    if (n > 64) n = 64;
-    return n < 1 ? 1 : (int)n;
+    return kgrad_best_slices(B, H, 8LL * pl->num_cu);
 }
 
 // The wide-engine kernel gradient (N = P x 1024, 16-bit I/O): a workgroup
 // per (channel, slice), two per CU.
 int kgrad_wide_slices(const fftconv_plan_s* pl, size_t B, size_t H) {
-    if (B == 0 || H == 0) return 1;
-    long long n = (4LL * pl->num_cu + (long long)H - 1) / (long long)H;
-    if (n > (long long)B) n = (long long)B;
-    if (n > 64) n = 64;
-    return n < 1 ? 1 : (int)n;
+    return kgrad_best_slices(B, H, 2LL * pl->num_cu);
 }
 
 // The multi-pass engine kernel gradient (N >= 32K, 16-bit I/O): channel
