@@ -1053,16 +1053,22 @@ int kgrad_wide_slices(const fftconv_plan_s* pl, size_t B, size_t H) {
     return kgrad_best_slices(B, H, 2LL * pl->num_cu);
 }
 
-// The multi-pass engine kernel gradient (N >= 32K, 16-bit I/O): channel
-// chunks whose outer-transformed rows of u and of dy (all B of a channel)
-// each fit one workspace chunk; batches with more rows per channel take the
-// generic passes.
-bool kgrad_on_mp(const fftconv_plan_s* pl, size_t B) {
-    return pl->s.mp_P1 && pl->s.dtype != FFTCONV_F32 && B * pl->s.M * 4 <= kMpChunkBytes;
+// The multi-pass engine kernel gradient (N >= 32K, 16-bit I/O): chunks of
+// channels x batch rows whose outer-transformed rows of u and of dy each
+// fit one workspace chunk (1 GB); every batch chunk runs the whole pipeline
+// and adds its share to dk (the inverse transform is linear).
+bool kgrad_on_mp(const fftconv_plan_s* pl, size_t) {
+    return pl->s.mp_P1 && pl->s.dtype != FFTCONV_F32;
+}
+
+size_t kgrad_mp_batch(const fftconv_plan_s* pl, size_t B) {
+    size_t bc = kMpChunkBytes / (pl->s.M * 4);
+    if (bc > B) bc = B;
+    return bc < 1 ? 1 : bc;
 }
 
 size_t kgrad_mp_channels(const fftconv_plan_s* pl, size_t B, size_t H) {
-    const size_t per_ch = (B ? B : 1) * pl->s.M * 4;
+    const size_t per_ch = kgrad_mp_batch(pl, B) * pl->s.M * 4;
     size_t hc = kMpChunkBytes / per_ch;
     if (hc > H) hc = H;
     return hc < 1 ? 1 : hc;
@@ -1074,8 +1080,8 @@ size_t kgrad_workspace_bytes(const fftconv_plan_s* pl, size_t B, size_t H) {
         // rows of u and dy after the forward column passes, and one result
         // row per channel of the chunk; the claim counters the column passes
         // clear
-        const size_t hc = kgrad_mp_channels(pl, B, H);
-        return (2 * B + 1) * hc * pl->s.M * 4 + kClaimBytes;
+        const size_t bc = kgrad_mp_batch(pl, B), hc = kgrad_mp_channels(pl, B, H);
+        return (2 * bc + 1) * hc * pl->s.M * 4 + kClaimBytes;
     }
     if (pl->s.wide_P)
         return (size_t)kgrad_wide_slices(pl, B, H) * H * (pl->s.wide_P / 2) * 64 * 64 * 4;
@@ -1700,22 +1706,27 @@ fftconv_status fftconv_backward(fftconv_plan_t plan, const void* u,
         return e == hipSuccess ? FFTCONV_OK : FFTCONV_ERR_HIP;
     }
     if (kgrad_on_mp(plan, B)) {
-        const size_t hcm = kgrad_mp_channels(plan, B, H);
-        const size_t per = B * hcm * s.M * 4;
+        const size_t bcm = kgrad_mp_batch(plan, B), hcm = kgrad_mp_channels(plan, B, H);
+        const size_t per = bcm * hcm * s.M * 4;
         char* base = (char*)workspace;
         void* wsu = base;
         void* wsd = base + per;
         void* wsg = base + 2 * per;
         uint32_t* ctr = (uint32_t*)(base + 2 * per + hcm * s.M * 4);
         const MpInnerParams& T = plan->mp;
+        const size_t row_bytes = H * N * esz;
         e = hipSuccess;
-        for (size_t h0 = 0; h0 < H && e == hipSuccess; h0 += hcm) {
+        for (size_t h0 = 0; h0 < H && e == hipSuccess; h0 += hcm)
+        for (size_t b0 = 0; b0 < B && e == hipSuccess; b0 += bcm) {
             const size_t hc = H - h0 < hcm ? H - h0 : hcm;
-            e = mp_cols_fwd(plan, io, u, wsu, ctr, B, H, h0, hc, st);
-            if (e == hipSuccess) e = mp_cols_fwd(plan, io, dy, wsd, ctr, B, H, h0, hc, st);
+            const size_t bc = B - b0 < bcm ? B - b0 : bcm;
+            const void* ub = (const char*)u + b0 * row_bytes;
+            const void* dyb = (const char*)dy + b0 * row_bytes;
+            e = mp_cols_fwd(plan, io, ub, wsu, ctr, bc, H, h0, hc, st);
+            if (e == hipSuccess) e = mp_cols_fwd(plan, io, dyb, wsd, ctr, bc, H, h0, hc, st);
             if (e == hipSuccess) {
                 KgMpParams P{};
-                P.B = (int)B;
+                P.B = (int)bc;
                 P.hc = (int)hc;
                 P.M = (int)s.M;
                 P.Po = T.Po;
@@ -1755,7 +1766,7 @@ fftconv_status fftconv_backward(fftconv_plan_t plan, const void* u,
                 }
                 C.S = (int)(s.M / s.mp_P1);
                 C.tw = plan->mp_tw1;
-                if (e == hipSuccess) e = launch_mp_col(io, s.mp_P1, 4, C, st);
+                if (e == hipSuccess) e = launch_mp_col(io, s.mp_P1, b0 == 0 ? 4 : 5, C, st);
             }
         }
         return e == hipSuccess ? FFTCONV_OK : FFTCONV_ERR_HIP;

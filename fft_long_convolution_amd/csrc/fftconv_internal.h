@@ -249,7 +249,7 @@ struct MpColParams {
 };
 // mode 0: forward first level from u; 1: forward second level (in place);
 // 2: inverse second level (in place); 3: inverse first level into y (I/O
-// type); 4: the same into fp32 rows y scaled by post
+// type); 4: the same into fp32 rows y scaled by post; 5: added to them
 hipError_t launch_mp_col(int io, int P, int mode, const MpColParams& p, hipStream_t s);
 
 // Both outer levels of a two-level plan in one pass (tiles of 512 / P2

@@ -109,12 +109,20 @@ __global__ void __launch_bounds__(256) mp_col_kernel(MpColParams prm) {
             for (int n = 0; n < P / 2; ++n)
                 z[n] = z[n] * f2_from_io<IO>(__builtin_nontemporal_load(&g[(long long)n * prm.S]));
         }
-        if constexpr (MODE == 4) {
-            // fp32 rows (the kernel gradient): t = 2m, 2m + 1 as one float2
+        if constexpr (MODE >= 4) {
+            // fp32 rows (the kernel gradient): t = 2m, 2m + 1 as one float2;
+            // mode 5 adds to them (batch chunks after the first)
             float2* y = (float2*)prm.y + mrow * (long long)(prm.M / 2) + c;
 #pragma unroll
-            for (int n = 0; n < P / 2; ++n)
-                y[(long long)n * prm.S] = make_float2(z[n].x * prm.post, z[n].y * prm.post);
+            for (int n = 0; n < P / 2; ++n) {
+                float2 o = make_float2(z[n].x * prm.post, z[n].y * prm.post);
+                if constexpr (MODE == 5) {
+                    const float2 p = y[(long long)n * prm.S];
+                    o.x += p.x;
+                    o.y += p.y;
+                }
+                y[(long long)n * prm.S] = o;
+            }
         } else {
             uint32_t* y = (uint32_t*)prm.y + mrow * (long long)(prm.M / 2) + c;
 #pragma unroll
@@ -905,6 +913,7 @@ hipError_t col_launch(int mode, const MpColParams& p, hipStream_t s) {
     case 1: hipLaunchKernelGGL((mp_col_kernel<IO, P, 1>), grid, blk, 0, s, p); break;
     case 2: hipLaunchKernelGGL((mp_col_kernel<IO, P, 2>), grid, blk, 0, s, p); break;
     case 4: hipLaunchKernelGGL((mp_col_kernel<IO, P, 4>), grid, blk, 0, s, p); break;
+    case 5: hipLaunchKernelGGL((mp_col_kernel<IO, P, 5>), grid, blk, 0, s, p); break;
     default: hipLaunchKernelGGL((mp_col_kernel<IO, P, 3>), grid, blk, 0, s, p); break;
     }
     return hipGetLastError();

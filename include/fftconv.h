@@ -234,9 +234,9 @@ fftconv_status fftconv_forward_gated(fftconv_plan_t plan, const void *u,
  * of the forward call's and the kernel gradient's.  The gradient needs
  * per-slice partial spectra on the row and wide engines (N = 1K..16K,
  * 16-bit I/O), for N >= 32K with 16-bit I/O the outer-transformed rows of
- * u and dy of one channel chunk plus one result row per channel (f16
- * complex, chunks of at most 1 GB per buffer), and otherwise two B*H x N
- * and one H x N fp32 complex rows (0 for fused fp32 plans). */
+ * u and dy of one chunk of channels x batch rows plus one result row per
+ * channel (f16 complex, at most 1 GB per buffer), and for fp32 plans two
+ * B*H x N and one H x N fp32 complex rows (0 when fused). */
 size_t fftconv_backward_workspace_bytes(fftconv_plan_t plan, size_t B, size_t H);
 
 /* Backward pass of the causal convolution y = (u * k)[0:N] (page
@@ -258,9 +258,9 @@ size_t fftconv_backward_workspace_bytes(fftconv_plan_t plan, size_t B, size_t H)
  * accumulates conj(U) DY over the batch per channel in fp32 registers and
  * runs one inverse transform per channel: on the matrix-core engine of the
  * forward kernels for 16-bit I/O (the row kernel's at N = 1024, the wide
- * kernel's at 4K..16K, the multi-pass column and inner passes at N >= 32K
- * when one channel's B rows fit 1 GB of f16 complex), on the LDS-staged
- * kernels otherwise.  B = 0 gives dk = 0.  The input
+ * kernel's at 4K..16K, the multi-pass column and inner passes at N >= 32K,
+ * batch chunks adding their share to dk), on the LDS-staged kernels for
+ * fp32 plans.  B = 0 gives dk = 0.  The input
  * gradient of the other kinds is fftconv_forward with the matching adjoint
  * spectrum.  Errors as fftconv_forward. */
 fftconv_status fftconv_backward(fftconv_plan_t plan, const void *u,

@@ -138,3 +138,31 @@ def test_backward_channel_chunks():
     err = oracle.rel_l2(got[hs, jj], want)
     _say("  sampled dk rel_l2", err)
     assert err < 1.5 * TOL[dtype]
+
+
+def test_backward_batch_chunks():
+    # more batch rows of one channel than the 1 GB workspace chunk holds (256
+    # rows at N = 1M): the multi-pass kernel gradient runs per batch chunk and
+    # the second chunk adds its share to dk; sampled lags by the definition
+    import torch
+    from fft_long_convolution_amd.fftconv import FFTConv
+    N, B, H, dtype = 1048576, 257, 1, "bf16"
+    w = inputs.Workload("kbchunk", 262, B, H, N, dtype, "normal", "decay", "kgrad batch chunks")
+    conv = FFTConv(N, dtype=dtype)
+    u = inputs.input_rows(w)
+    dy = inputs.dy_rows(w)
+    _say("kgrad batch chunks", N, B, H, dtype)
+    _, dk = conv.backward(to_torch(u, dtype).view(B, H, N), to_torch(dy, dtype).view(B, H, N),
+                          None, need_du=False)
+    torch.cuda.synchronize()
+    got = dk.cpu().numpy().astype(np.float64)
+    del dk
+    rng = np.random.default_rng(9)
+    js = np.concatenate([[0, 1, N - 1], rng.integers(0, N, 9)])
+    hs = np.zeros(len(js), dtype=np.int64)
+    want = oracle.kgrad_points(oracle.to_f64(u, dtype).reshape(B, N),
+                               oracle.to_f64(dy, dtype).reshape(B, N), H, hs, js, "causal",
+                               np.zeros(B, dtype=np.int64))
+    err = oracle.rel_l2(got[hs, js], want)
+    _say("  sampled dk rel_l2", err)
+    assert err < 1.5 * TOL[dtype]
