@@ -100,9 +100,9 @@ def to_torch(a, dtype, torch):
 def main():
     args = parse()
     if args.gpus != 1:
-        print("bench.py: this build runs on exactly one GPU; a run on %d GPUs "
-              "is not part of it (rows would shard by channel with no "
-              "communication)" % args.gpus, file=sys.stderr)
+        print("bench.py: measures one GPU only; %d GPUs were requested (rows "
+              "would shard by channel with no communication, each GPU "
+              "running this path on its channels)" % args.gpus, file=sys.stderr)
         sys.exit(2)
     import torch
     from fft_long_convolution_amd import inputs
