@@ -27,7 +27,76 @@ namespace fftconv {
 
 constexpr int kKgWaves = 8;
 
-template <int IO>
+// The channel's accumulated spectrum (times 4; s4[kt * 4 + mt] holds bins
+// (kt, mt, e = 0, 1) of the lane) through I2, the conjugate twiddle and I1
+// into fp32 dk, as the row kernel's inverse; `pre` scales the f16 operands
+// so that they stay in range however concentrated the spectrum is.
+__device__ __forceinline__ void kg_row_inverse(const float4 (&s4)[8], const uint4* s_i2b,
+                                               const uint4* s_i1a, const uint32_t (&twf)[2][2][4],
+                                               const KgRowParams& P, int h, int lane) {
+    constexpr int NB = 32, MT2 = 4, KS2 = 2, NT = 2;
+    const int g = lane >> 4, x = lane & 15;
+    uint4 a2[2][KS2];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+        uint32_t zp[MT2][2];
+#pragma unroll
+        for (int mt = 0; mt < MT2; ++mt) {
+            const float4 v = s4[kt * MT2 + mt];
+            zp[mt][0] = pk2(v.x * P.pre, v.y * P.pre);
+            zp[mt][1] = pk2(v.z * P.pre, v.w * P.pre);
+        }
+#pragma unroll
+        for (int ks = 0; ks < KS2; ++ks)
+            a2[kt][ks] = make_uint4(zp[2 * ks][0], zp[2 * ks][1], zp[2 * ks + 1][0], zp[2 * ks + 1][1]);
+    }
+    // I2 and the conjugate twiddle, as the row kernel
+    uint4 b1v[2][NT];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+            rfloat4 re = {0.f, 0.f, 0.f, 0.f}, im = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < KS2; ++ks) {
+                re = mma_f16(a2[kt][ks], s_i2b[(ks * 2 * NT + 2 * nt) * 64 + lane], re);
+                im = mma_f16(a2[kt][ks], s_i2b[(ks * 2 * NT + 2 * nt + 1) * 64 + lane], im);
+            }
+            uint32_t w[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) w[r] = as_u32(hmulc(as_h2(pk2(re[r], im[r])), as_h2(twf[kt][nt][r])));
+            b1v[kt][nt] = make_uint4(w[0], w[1], w[2], w[3]);
+        }
+    // I1 into fp32 points (t even, t odd), whole lines as the row kernel
+    float2* dk = (float2*)(P.dk + (long long)h * (32 * NB));
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) {
+        float2 o[NT][2];
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+            rfloat4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) acc = mma_f16(s_i1a[(mt * 2 + ks) * 64 + lane], b1v[ks][nt], acc);
+#pragma unroll
+            for (int e = 0; e < 2; ++e) o[nt][e] = make_float2(acc[2 * e] * P.post, acc[2 * e + 1] * P.post);
+        }
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+            uint32_t ax = __float_as_uint(o[0][e].x), bx = __float_as_uint(o[1][e].x);
+            uint32_t ay = __float_as_uint(o[0][e].y), by = __float_as_uint(o[1][e].y);
+            swap16(ax, bx);
+            swap16(ay, by);
+            const int na = 8 * mt + 4 * (g >> 1) + e, w = (g & 1) ? kmap32(1, x) : x;
+            dk[NB * na + w] = make_float2(__uint_as_float(ax), __uint_as_float(ay));
+            dk[NB * (na + 2) + w] = make_float2(__uint_as_float(bx), __uint_as_float(by));
+        }
+    }
+}
+
+// FUSE (S = kKgWaves: a workgroup's waves are the slices of one channel):
+// the slices' sums meet in LDS and wave 0 runs the inverse into dk, with no
+// partial rows in memory and no second kernel.
+template <int IO, bool FUSE>
 __global__ void __launch_bounds__(64 * kKgWaves, 1) kgrad_row_kernel(KgRowParams P) {
     constexpr int NB = 32, IT = 2, MT2 = 4, KS2 = 2, M = 1024;
     constexpr bool BF = (IO == IO_BF16);
@@ -36,6 +105,9 @@ __global__ void __launch_bounds__(64 * kKgWaves, 1) kgrad_row_kernel(KgRowParams
     uint4* s_f1b = s_lds;                                   // [F1T][64]
     uint4* s_f2a = s_f1b + F1T * 64;                        // [MT2][KS2][64]
     uint32_t* s_scr = (uint32_t*)(s_f2a + MT2 * KS2 * 64);  // [waves][2][NB][16]
+    uint4* s_i2b = (uint4*)(s_scr + kKgWaves * 2 * NB * 16);  // FUSE: [KS2][4][64]
+    uint4* s_i1a = s_i2b + 8 * 64;                             // FUSE: [4][64]
+    float4* s_red = (float4*)(s_i1a + 4 * 64);                 // FUSE: [waves][64][8]
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -43,6 +115,10 @@ __global__ void __launch_bounds__(64 * kKgWaves, 1) kgrad_row_kernel(KgRowParams
     constexpr int TH = 64 * kKgWaves;
     for (int i = tid; i < F1T * 64; i += TH) s_f1b[i] = ((const uint4*)P.f1b)[i];
     for (int i = tid; i < MT2 * KS2 * 64; i += TH) s_f2a[i] = ((const uint4*)P.f2a)[i];
+    if constexpr (FUSE) {
+        for (int i = tid; i < 8 * 64; i += TH) s_i2b[i] = ((const uint4*)P.i2b)[i];
+        for (int i = tid; i < 4 * 64; i += TH) s_i1a[i] = ((const uint4*)P.i1a)[i];
+    }
     uint32_t twf[IT][2][4];
 #pragma unroll
     for (int it = 0; it < IT; ++it)
@@ -51,11 +127,15 @@ __global__ void __launch_bounds__(64 * kKgWaves, 1) kgrad_row_kernel(KgRowParams
 #pragma unroll
             for (int r = 0; r < 4; ++r) twf[it][kt][r] = P.twf[lane * (IT * 8) + (it * 2 + kt) * 4 + r];
     __syncthreads();
-    // no workgroup barrier below: a wave without a task may leave
+    // without FUSE no workgroup barrier follows: a wave without a task may
+    // leave; with FUSE every wave has one (the grid is one workgroup per
+    // channel) and an idle one would still reach the barrier
     const int task = blockIdx.x * kKgWaves + wave;
-    if (task >= P.H * P.S) return;
+    const bool has_task = task < P.H * P.S;
+    if (!FUSE && !has_task) return;
     const int h = task / P.S, sl = task - h * P.S;
-    const int b0 = (int)((long long)P.B * sl / P.S), b1 = (int)((long long)P.B * (sl + 1) / P.S);
+    const int b0 = has_task ? (int)((long long)P.B * sl / P.S) : 0;
+    const int b1 = has_task ? (int)((long long)P.B * (sl + 1) / P.S) : 0;
 
     // conj(W_2N^k)^2 = exp(2 pi i k / M) of the lane's bins, packed f16
     uint32_t wc[2][MT2][2];
@@ -198,13 +278,33 @@ __global__ void __launch_bounds__(64 * kKgWaves, 1) kgrad_row_kernel(KgRowParams
                     acc[kt][mt][e].y += (float)R.y;
                 }
     }
-    float4* o = (float4*)P.part + ((long long)(sl * P.H + h) * 64 + lane) * 8;
+    float4* o = FUSE ? s_red + (wave * 64 + lane) * 8
+                     : (float4*)P.part + ((long long)(sl * P.H + h) * 64 + lane) * 8;
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
         for (int mt = 0; mt < MT2; ++mt)
             o[kt * MT2 + mt] = make_float4(acc[kt][mt][0].x, acc[kt][mt][0].y, acc[kt][mt][1].x,
                                            acc[kt][mt][1].y);
+    if constexpr (FUSE) {
+        __syncthreads();
+        if (wave == 0 && has_task) {
+            float4 s4[2 * MT2];
+#pragma unroll
+            for (int i = 0; i < 2 * MT2; ++i) s4[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+            for (int w = 0; w < kKgWaves; ++w) {
+#pragma unroll
+                for (int i = 0; i < 2 * MT2; ++i) {
+                    const float4 v = s_red[(w * 64 + lane) * 8 + i];
+                    s4[i].x += v.x;
+                    s4[i].y += v.y;
+                    s4[i].z += v.z;
+                    s4[i].w += v.w;
+                }
+            }
+            kg_row_inverse(s4, s_i2b, s_i1a, twf, P, h, lane);
+        }
+    }
 }
 
 template <int IO>
@@ -245,72 +345,32 @@ __global__ void __launch_bounds__(64 * kKgWaves, 1) kgrad_row_inv_kernel(KgRowPa
             s4[i].w += v.w;
         }
     }
-    uint4 a2[2][KS2];
-#pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
-        uint32_t zp[MT2][2];
-#pragma unroll
-        for (int mt = 0; mt < MT2; ++mt) {
-            const float4 v = s4[kt * MT2 + mt];
-            zp[mt][0] = pk2(v.x * P.pre, v.y * P.pre);
-            zp[mt][1] = pk2(v.z * P.pre, v.w * P.pre);
-        }
-#pragma unroll
-        for (int ks = 0; ks < KS2; ++ks)
-            a2[kt][ks] = make_uint4(zp[2 * ks][0], zp[2 * ks][1], zp[2 * ks + 1][0], zp[2 * ks + 1][1]);
-    }
-    // I2 and the conjugate twiddle, as the row kernel
-    uint4 b1v[2][NT];
-#pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt) {
-            rfloat4 re = {0.f, 0.f, 0.f, 0.f}, im = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int ks = 0; ks < KS2; ++ks) {
-                re = mma_f16(a2[kt][ks], s_i2b[(ks * 2 * NT + 2 * nt) * 64 + lane], re);
-                im = mma_f16(a2[kt][ks], s_i2b[(ks * 2 * NT + 2 * nt + 1) * 64 + lane], im);
-            }
-            uint32_t w[4];
-#pragma unroll
-            for (int r = 0; r < 4; ++r) w[r] = as_u32(hmulc(as_h2(pk2(re[r], im[r])), as_h2(twf[kt][nt][r])));
-            b1v[kt][nt] = make_uint4(w[0], w[1], w[2], w[3]);
-        }
-    // I1 into fp32 points (t even, t odd), whole lines as the row kernel
-    float2* dk = (float2*)(P.dk + (long long)h * (32 * NB));
-#pragma unroll
-    for (int mt = 0; mt < 2; ++mt) {
-        float2 o[NT][2];
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt) {
-            rfloat4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int ks = 0; ks < 2; ++ks) acc = mma_f16(s_i1a[(mt * 2 + ks) * 64 + lane], b1v[ks][nt], acc);
-#pragma unroll
-            for (int e = 0; e < 2; ++e) o[nt][e] = make_float2(acc[2 * e] * P.post, acc[2 * e + 1] * P.post);
-        }
-#pragma unroll
-        for (int e = 0; e < 2; ++e) {
-            uint32_t ax = __float_as_uint(o[0][e].x), bx = __float_as_uint(o[1][e].x);
-            uint32_t ay = __float_as_uint(o[0][e].y), by = __float_as_uint(o[1][e].y);
-            swap16(ax, bx);
-            swap16(ay, by);
-            const int na = 8 * mt + 4 * (g >> 1) + e, w = (g & 1) ? kmap32(1, x) : x;
-            dk[NB * na + w] = make_float2(__uint_as_float(ax), __uint_as_float(ay));
-            dk[NB * (na + 2) + w] = make_float2(__uint_as_float(bx), __uint_as_float(by));
-        }
-    }
+    kg_row_inverse(s4, s_i2b, s_i1a, twf, P, h, lane);
 }
 
 int kgrad_row_lds(int io) { return ((io == IO_BF16 ? 8 : 4) + 8) * 64 * 16 + kKgWaves * 2 * 32 * 16 * 4; }
+// with FUSE: the inverse's tables and the slices' sums
+int kgrad_row_fused_lds(int io) { return kgrad_row_lds(io) + (8 + 4) * 64 * 16 + kKgWaves * 64 * 8 * 16; }
+
+template <int IO>
+static hipError_t kgrad_row_fused_t(const KgRowParams& p, hipStream_t s) {
+    const int lds = kgrad_row_fused_lds(IO);
+    const hipError_t e = hipFuncSetAttribute((const void*)kgrad_row_kernel<IO, true>,
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((kgrad_row_kernel<IO, true>), dim3((unsigned)p.H), dim3(64 * kKgWaves), lds, s, p);
+    return hipGetLastError();
+}
 
 hipError_t launch_kgrad_row(int io, const KgRowParams& p, hipStream_t s) {
     if (p.H <= 0 || p.S <= 0) return hipSuccess;
+    if (p.S == kKgWaves)
+        return io == IO_BF16 ? kgrad_row_fused_t<IO_BF16>(p, s) : kgrad_row_fused_t<IO_F16>(p, s);
     const unsigned tasks = (unsigned)(p.H * p.S);
     const dim3 grid((tasks + kKgWaves - 1) / kKgWaves), blk(64 * kKgWaves);
     const int lds = kgrad_row_lds(io);
-    if (io == IO_BF16) hipLaunchKernelGGL(kgrad_row_kernel<IO_BF16>, grid, blk, lds, s, p);
-    else hipLaunchKernelGGL(kgrad_row_kernel<IO_F16>, grid, blk, lds, s, p);
+    if (io == IO_BF16) hipLaunchKernelGGL((kgrad_row_kernel<IO_BF16, false>), grid, blk, lds, s, p);
+    else hipLaunchKernelGGL((kgrad_row_kernel<IO_F16, false>), grid, blk, lds, s, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const dim3 grid2((unsigned)((p.H + kKgWaves - 1) / kKgWaves));

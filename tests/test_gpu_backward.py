@@ -27,6 +27,7 @@ def _say(*a):
 @pytest.mark.parametrize("N,dtype,B,H", [
     (256, "f32", 1, 4), (256, "bf16", 3, 5), (512, "f16", 4, 3),
     (1024, "bf16", 5, 3), (1024, "f16", 64, 4), (1024, "bf16", 1, 1),
+    (1024, "bf16", 8, 256), (1024, "f16", 16, 256),
     (1024, "f32", 2, 2), (2048, "f16", 3, 2),
     (4096, "bf16", 2, 3), (4096, "f16", 1, 1), (8192, "f16", 3, 2),
     (8192, "bf16", 17, 5), (16384, "bf16", 2, 3), (16384, "f16", 4, 2),
@@ -34,8 +35,10 @@ def _say(*a):
     (131072, "f16", 2, 3), (262144, "bf16", 1, 2), (524288, "bf16", 2, 1),
     (1048576, "f16", 1, 1), (2097152, "f16", 1, 2), (4194304, "bf16", 1, 1)])
 def test_backward(N, dtype, B, H):
-    # the row engine at N = 1024 and the wide engine at N = 4K..16K with
-    # 16-bit I/O (batch slices of one row up to more rows than slices), the
+    # the row engine at N = 1024 (batch slices of one row up to more rows
+    # than slices; eight slices of a channel -- B = 8 and 16 at H = 256, and
+    # the full-size shape -- sum in one workgroup's LDS) and the wide engine
+    # at N = 4K..16K with 16-bit I/O, the
     # multi-pass engine at N >= 32K with 16-bit I/O (forward column passes
     # of u and dy, the accumulating inner pass on one- and two-level outer
     # factors, the inverse column passes into fp32 dk), the LDS-staged
