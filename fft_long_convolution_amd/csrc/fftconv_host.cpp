@@ -1640,6 +1640,8 @@ fftconv_status fftconv_backward(fftconv_plan_t plan, const void* u,
         if (!workspace || workspace_bytes < ws_need) return FFTCONV_ERR_WORKSPACE;
         if (!aligned16(workspace)) return FFTCONV_ERR_ALIGNMENT;
         if ((u && overlap(workspace, ws_need, u, io_bytes)) ||
+            (dy && overlap(workspace, ws_need, dy, io_bytes)) ||
+            (du && overlap(workspace, ws_need, du, io_bytes)) ||
             (dk && overlap(workspace, ws_need, dk, dk_bytes)))
             return FFTCONV_ERR_INVALID_ARG;
     }

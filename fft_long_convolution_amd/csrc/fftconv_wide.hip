@@ -3,7 +3,8 @@
 // LDS and registers (page "FlashFFTConv: Efficient Convolutions for Long
 // Sequences with Tensor Cores", section 3.4 and Algorithm 1: an order-3
 // Monarch decomposition P x 32 x 32, with the real-input packing and the
-// implicit zero padding of section 3.3).
+// implicit zero padding of section 3.4, "Implicit zero-padding for causal
+// convolutions").
 //
 // Packed row z[n], n = n1*Q + n' (Q = 1024, n1 < P/2 nonzero), bins
 // k = k1 + P*k', k' = k_a + 32*k_b (the 32 x 32 engine of the row kernel).

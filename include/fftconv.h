@@ -138,7 +138,8 @@ fftconv_status fftconv_kernel_spectrum(fftconv_plan_t plan, const float *k,
 /* Which operator a spectrum makes fftconv_forward (and the gated call)
  * compute, for kernel taps k[h, 0:N] (page "FlashFFTConv: Efficient
  * Convolutions for Long Sequences with Tensor Cores": the convolution
- * definition and theorem of section 3.3; the non-causal convolutions of its
+ * definition and theorem of section 3.4, "The FFT Convolution and Its
+ * Hardware Mismatch"; the non-causal convolutions of its
  * benchmark tables use an FFT of size N, i.e. a circular convolution; the
  * gradients multiply by the conjugate spectrum):
  *   FFTCONV_CAUSAL            y[t] = sum_{s<=t} u[s] k[t-s]

@@ -26,7 +26,8 @@
  * Further operators of the same family (same page, section 3: the
  * non-causal convolutions of its benchmark tables use an FFT of size N, a
  * circular convolution; training needs the gradients of the causal one,
- * which section 3.3 writes as products with the conjugate spectra):
+ * which section 3.4, "Recomputation in the backward pass", writes as
+ * products with the conjugate spectra):
  *
  *   kind 0  causal             y[t] = sum_{s<=t} u[s] k[t-s]
  *   kind 1  causal adjoint     y[s] = sum_{t>=s} u[t] k[t-s]

@@ -21,7 +21,15 @@ def _say(*a):
     sys.stdout.flush()
 
 
-def _run(w, cutoff):
+def _round_io(x, dtype):
+    if dtype == "bf16":
+        return oracle.to_f64(inputs.f32_to_bf16_bits(x.astype(np.float32)), "bf16")
+    if dtype == "f16":
+        return x.astype(np.float16).astype(np.float64)
+    return x.astype(np.float32).astype(np.float64)
+
+
+def _run(w, cutoff, with_rounding=False):
     import torch
     from fft_long_convolution_amd.fftconv import FFTConv
     conv = FFTConv(w.N, dtype=w.dtype)
@@ -33,6 +41,8 @@ def _run(w, cutoff):
     got = oracle.to_f64(from_torch(y, w.dtype).reshape(w.rows, w.N), w.dtype)
     ref = oracle.lowpass_fft(oracle.to_f64(u, w.dtype).reshape(w.rows, w.N),
                              k.astype(np.float64), cutoff, np.arange(w.rows) % w.H)
+    if with_rounding:
+        return oracle.rel_l2(got, ref), oracle.rel_l2(_round_io(ref, w.dtype), ref)
     return oracle.rel_l2(got, ref)
 
 
@@ -45,28 +55,25 @@ def _run(w, cutoff):
     (8192, "f16", 2, 2, 2048), (65536, "f16", 1, 3, 20000),
     (65536, "bf16", 2, 2, 16383), (262144, "f16", 1, 2, 3000),
     (1048576, "bf16", 1, 1, 200000), (4194304, "bf16", 1, 1, 500000),
-    # the extremes: the DC bin alone, and no limit (cutoff = N).  With the DC
-    # bin alone every output of a row is one value, so its rounding (bf16:
-    # up to 2^-9 relative) does not average within the row: enough rows
-    # that the whole-tensor rel L2 averages over rows as it does over
-    # elements elsewhere
-    (1024, "bf16", 16, 8, 0), (8192, "f16", 4, 8, 0), (65536, "bf16", 2, 16, 0),
+    # the extremes: the DC bin alone, and no limit (cutoff = N)
+    (1024, "bf16", 64, 64, 0), (8192, "f16", 4, 64, 0), (65536, "bf16", 1, 64, 0),
     (1024, "f16", 2, 3, 1024), (16384, "bf16", 1, 2, 16384), (131072, "f16", 1, 1, 131072)])
 def test_lowpass(N, dtype, B, H, cutoff):
     w = inputs.Workload("lowpass", 260 + N.bit_length() + B, B, H, N, dtype,
                         "normal", "decay", "band-limited")
-    err = _run(w, cutoff)
-    _say("lowpass", N, dtype, B, H, cutoff, "rel_l2", err)
-    assert err < (TOL[dtype] if cutoff > 0 else DC_TOL[dtype])
-
-
-# The DC bin alone (cutoff 0): every output of a row is the one value
-# sum(u) sum(k) / 2N, carried by a single bin through the f16 stages (about
-# six roundings of at most 2^-11 relative: after the first stage, the
-# coefficient, the pairing product, after the inverse stages) and the output
-# rounding (bf16 2^-9, f16 2^-11).  Nothing averages, so the bound is the
-# per-value one: 6 * 2^-11 + 2^-9 = 4.9e-3 (bf16), 7 * 2^-11 = 3.4e-3 (f16).
-DC_TOL = {"f32": 1e-5, "f16": 3.5e-3, "bf16": 5e-3}
+    err, rounding_only = _run(w, cutoff, with_rounding=True)
+    _say("lowpass", N, dtype, B, H, cutoff, "rel_l2", err,
+         "(oracle rounded to the I/O type: %.3e)" % rounding_only)
+    if cutoff == 0:
+        # With the DC bin alone every output of a row is the one value
+        # sum(u) sum(k) / 2N, so the whole-tensor rel L2 averages over rows,
+        # each weighted by (sum k)^2 of its channel, not over elements.  With
+        # few channels one channel carries most of the weight and even the
+        # exact result rounded to bf16 scatters around the bar (16 x 8 rows
+        # at N = 1024: 2.04e-3).  The cases therefore span 64 channels; this
+        # checks that the sample is wide enough for the bar to be meaningful.
+        assert rounding_only < 0.9 * TOL[dtype]
+    assert err < TOL[dtype]
 
 
 def test_lowpass_full_size_hyena():
