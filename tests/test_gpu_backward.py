@@ -96,6 +96,19 @@ def test_backward_pieces_and_errors():
     assert L.fftconv_backward(conv2._plan, u2.data_ptr(), u2.data_ptr(), None,
                               None, dk2.data_ptr(), 1, 1, 32768, None, 0,
                               None) == 4
+    # a workspace overlapping du or dy is rejected before anything launches
+    ws2 = torch.empty(need + 2 * 32768 * 2, dtype=torch.uint8, device="cuda")
+    dy_in_ws = ws2[need:].view(torch.float16)[:32768]
+    du2 = torch.empty(1, 1, 32768, device="cuda").half()
+    kfa2 = conv2.kernel_spectrum(torch.randn(1, 32768, device="cuda"),
+                                 kind="causal_adjoint")
+    assert L.fftconv_backward(conv2._plan, u2.data_ptr(), dy_in_ws.data_ptr(), kfa2.data_ptr(),
+                              du2.data_ptr(), dk2.data_ptr(), 1, 1, 32768,
+                              ws2.data_ptr() + 2 * 32768 * 2, need, None) == 1
+    du_in_ws = ws2.view(torch.float16)[:32768]
+    assert L.fftconv_backward(conv2._plan, u2.data_ptr(), u2.data_ptr(), kfa2.data_ptr(),
+                              du_in_ws.data_ptr(), dk2.data_ptr(), 1, 1, 32768,
+                              ws2.data_ptr(), need, None) == 1
     torch.cuda.synchronize()
 
 
