@@ -17,7 +17,8 @@ SOURCES = [os.path.join(HERE, "csrc", "fftconv_host.cpp"),
            os.path.join(HERE, "csrc", "fftconv_wide.hip"),
            os.path.join(HERE, "csrc", "fftconv_mp.hip"),
            os.path.join(HERE, "csrc", "fftconv_inner.hip"),
-           os.path.join(HERE, "csrc", "fftconv_kgrad.hip")]
+           os.path.join(HERE, "csrc", "fftconv_kgrad.hip"),
+           os.path.join(HERE, "csrc", "fftconv_scratch.hip")]
 # per-source extra flags: the inner multi-pass kernel schedules best with the
 # max-ILP strategy (measured; the other kernels are slower with it)
 EXTRA = {"fftconv_inner.hip": ["-mllvm", "-amdgpu-sched-strategy=max-ilp"]}

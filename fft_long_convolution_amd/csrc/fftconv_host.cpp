@@ -712,12 +712,13 @@ fftconv_status build_mp_tables(fftconv_plan_s* pl);
 fftconv_status spectrum_impl(fftconv_plan_t plan, const float* k, size_t H,
                              fftconv_kernel_kind kind, long long cutoff, void* k_f,
                              void* stream);
+constexpr size_t kMpChunkBytes = (size_t)1024 << 20;
+
 fftconv_status forward_impl(fftconv_plan_t plan, const void* u, const void* w,
                             const void* v, const void* k_f, void* y, size_t B,
                             size_t H, size_t N, void* workspace,
-                            size_t workspace_bytes, void* stream, int skip_hi);
-
-constexpr size_t kMpChunkBytes = (size_t)1024 << 20;
+                            size_t workspace_bytes, void* stream, int skip_hi,
+                            size_t chunk_cap);
 
 fftconv_status build_device_tables(fftconv_plan_s* pl) {
     const Shape& s = pl->s;
@@ -1153,19 +1154,35 @@ hipError_t mp_cols_fwd(const fftconv_plan_s* plan, int io, const void* src, void
 // slower than 1 GB ones, so the cache does not decide the size.
 // Batch rows per chunk: all of them unless one channel's rows alone exceed
 // the bound (then the chunk is one channel of a slice of the batch).
-size_t mp_chunk_batch(const Shape& s, size_t B) {
-    size_t bc = kMpChunkBytes / (s.M * 4);
+// `cap` is the chunk bound in bytes (kMpChunkBytes, or what the static
+// scratch array of the allocation-free call leaves beside the counters).
+size_t mp_chunk_batch(const Shape& s, size_t B, size_t cap = kMpChunkBytes) {
+    size_t bc = cap / (s.M * 4);
     if (bc < 1) bc = 1;
     return B < bc ? (B ? B : 1) : bc;
 }
 
-size_t mp_chunk_channels(const Shape& s, size_t B, size_t H) {
-    B = mp_chunk_batch(s, B);
+size_t mp_chunk_channels(const Shape& s, size_t B, size_t H, size_t cap = kMpChunkBytes) {
+    B = mp_chunk_batch(s, B, cap);
     const size_t per_ch = B * s.M * 4;
-    size_t hc = kMpChunkBytes / per_ch;
+    size_t hc = cap / per_ch;
     if (hc < 1) hc = 1;
     if (hc > H) hc = H;
     return hc;
+}
+
+// Workspace bytes of a forward call whose multi-pass chunks are bounded by
+// `cap` (fftconv_workspace_bytes with the default bound).
+size_t forward_workspace_bytes(const fftconv_plan_s* plan, size_t B, size_t H,
+                               size_t cap = kMpChunkBytes) {
+    // wide kernel: the row-claim counters only
+    if (plan->s.wide_P) return kClaimBytes;
+    if (plan->s.path == 0) return 0;
+    // multi-pass: one channel chunk of f16 complex rows, then the counters
+    if (plan->s.mp_P1)
+        return mp_chunk_batch(plan->s, B, cap) * mp_chunk_channels(plan->s, B, H, cap) *
+                   plan->s.M * 4 + kClaimBytes;
+    return B * H * plan->s.M * 8;
 }
 
 bool overlap(const void* a, size_t na, const void* b, size_t nb) {
@@ -1250,14 +1267,7 @@ size_t fftconv_backward_workspace_bytes(fftconv_plan_t plan, size_t B, size_t H)
 
 size_t fftconv_workspace_bytes(fftconv_plan_t plan, size_t B, size_t H) {
     if (!plan) return 0;
-    // wide kernel: the row-claim counters only
-    if (plan->s.wide_P) return kClaimBytes;
-    if (plan->s.path == 0) return 0;
-    // multi-pass: one channel chunk of f16 complex rows, then the counters
-    if (plan->s.mp_P1)
-        return mp_chunk_batch(plan->s, B) * mp_chunk_channels(plan->s, B, H) * plan->s.M * 4 +
-               kClaimBytes;
-    return B * H * plan->s.M * 8;
+    return forward_workspace_bytes(plan, B, H);
 }
 
 fftconv_status fftconv_kernel_spectrum(fftconv_plan_t plan, const float* k,
@@ -1371,7 +1381,8 @@ fftconv_status spectrum_impl(fftconv_plan_t plan, const float* k, size_t H,
 fftconv_status forward_impl(fftconv_plan_t plan, const void* u, const void* w,
                             const void* v, const void* k_f, void* y, size_t B,
                             size_t H, size_t N, void* workspace,
-                            size_t workspace_bytes, void* stream, int skip_hi) {
+                            size_t workspace_bytes, void* stream, int skip_hi,
+                            size_t chunk_cap) {
     if (!plan) return FFTCONV_ERR_INVALID_ARG;
     const Shape& s = plan->s;
     if (N != s.N) return FFTCONV_ERR_INVALID_ARG;
@@ -1389,7 +1400,7 @@ fftconv_status forward_impl(fftconv_plan_t plan, const void* u, const void* w,
         return FFTCONV_ERR_INVALID_ARG;
     if (w && (overlap(y, io_bytes, w, io_bytes) || overlap(y, io_bytes, v, io_bytes)))
         return FFTCONV_ERR_INVALID_ARG;
-    const size_t ws_need = fftconv_workspace_bytes(plan, B, H);
+    const size_t ws_need = forward_workspace_bytes(plan, B, H, chunk_cap);
     if (ws_need) {
         if (!workspace || workspace_bytes < ws_need) return FFTCONV_ERR_WORKSPACE;
         if (!aligned16(workspace)) return FFTCONV_ERR_ALIGNMENT;
@@ -1428,8 +1439,8 @@ fftconv_status forward_impl(fftconv_plan_t plan, const void* u, const void* w,
         R.skip_hi = skip_hi;
         e = launch_row(io, plan->row_nb, R, plan->lds_row, st);
     } else if (s.mp_P1) {
-        const size_t hc_max = mp_chunk_channels(s, B, H);
-        const size_t bc_max = mp_chunk_batch(s, B);
+        const size_t hc_max = mp_chunk_channels(s, B, H, chunk_cap);
+        const size_t bc_max = mp_chunk_batch(s, B, chunk_cap);
         MpColParams C1{};
         C1.H = (int)H;
         C1.M = (int)s.M;
@@ -1581,7 +1592,29 @@ fftconv_status fftconv_forward(fftconv_plan_t plan, const void* u,
                                size_t N, void* workspace,
                                size_t workspace_bytes, void* stream) {
     return forward_impl(plan, u, nullptr, nullptr, k_f, y, B, H, N, workspace,
-                        workspace_bytes, stream, 0);
+                        workspace_bytes, stream, 0, kMpChunkBytes);
+}
+
+fftconv_status fftconv_forward_noalloc(fftconv_plan_t plan, const void* u,
+                                       const void* k_f, void* y, size_t B, size_t H,
+                                       size_t N, void* stream) {
+    if (!plan) return FFTCONV_ERR_INVALID_ARG;
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess) return FFTCONV_ERR_HIP;
+    if (dev != plan->device) return FFTCONV_ERR_INVALID_ARG;
+    // the library's static scratch array on this device (its address is
+    // looked up once per device)
+    void* scratch = nullptr;
+    size_t scratch_bytes = 0;
+    if (scratch_buffer(dev, &scratch, &scratch_bytes) != hipSuccess) return FFTCONV_ERR_HIP;
+    // multi-pass chunks sized to what the array holds beside the counters;
+    // a single row must fit
+    const size_t cap = scratch_bytes - kClaimBytes;
+    if (plan->s.mp_P1 && plan->s.M * 4 > cap) return FFTCONV_ERR_WORKSPACE;
+    if (B * H != 0 && forward_workspace_bytes(plan, B, H, cap) > scratch_bytes)
+        return FFTCONV_ERR_WORKSPACE;
+    return forward_impl(plan, u, nullptr, nullptr, k_f, y, B, H, N, scratch,
+                        scratch_bytes, stream, 0, cap);
 }
 
 fftconv_status fftconv_forward_lowpass(fftconv_plan_t plan, const void* u,
@@ -1597,7 +1630,7 @@ fftconv_status fftconv_forward_lowpass(fftconv_plan_t plan, const void* u,
     const bool engine = (plan->use_row && plan->row_nb == 32) || plan->s.wide_P || plan->s.mp_P1;
     const int skip = (engine && cutoff < plan->s.M / 4) ? 1 : 0;
     return forward_impl(plan, u, nullptr, nullptr, k_f, y, B, H, N, workspace,
-                        workspace_bytes, stream, skip);
+                        workspace_bytes, stream, skip, kMpChunkBytes);
 }
 
 fftconv_status fftconv_forward_gated(fftconv_plan_t plan, const void* u,
@@ -1607,7 +1640,7 @@ fftconv_status fftconv_forward_gated(fftconv_plan_t plan, const void* u,
                                      size_t workspace_bytes, void* stream) {
     if (B * H != 0 && (!w || !v)) return FFTCONV_ERR_INVALID_ARG;
     return forward_impl(plan, u, w, v, k_f, y, B, H, N, workspace,
-                        workspace_bytes, stream, 0);
+                        workspace_bytes, stream, 0, kMpChunkBytes);
 }
 
 fftconv_status fftconv_backward(fftconv_plan_t plan, const void* u,
@@ -1653,7 +1686,8 @@ fftconv_status fftconv_backward(fftconv_plan_t plan, const void* u,
     // conjugate spectrum); validated like any forward call
     if (du) {
         const fftconv_status fs = forward_impl(plan, dy, nullptr, nullptr, k_f_adj, du, B, H,
-                                               N, workspace, workspace_bytes, stream, 0);
+                                               N, workspace, workspace_bytes, stream, 0,
+                                               kMpChunkBytes);
         if (fs != FFTCONV_OK) return fs;
     }
     if (!dk || H == 0) return FFTCONV_OK;

@@ -199,6 +199,11 @@ constexpr int kRowWavesGated = 12;
 // Row-claim counters of one call: 8 XCD groups, one 128-byte line each.
 constexpr int kClaimWords = 256;
 constexpr size_t kClaimBytes = kClaimWords * 4;
+
+// The static scratch array of the allocation-free forward call
+// (fftconv_scratch.hip): its device address on `device` (which must be the
+// current device; looked up once per device) and its size in bytes.
+hipError_t scratch_buffer(int device, void** ptr, size_t* bytes);
 hipError_t launch_claim_reset(uint32_t* ctr, hipStream_t s);
 
 struct WideParams {

@@ -96,6 +96,8 @@ def lib() -> ctypes.CDLL:
         L.fftconv_kernel_spectrum_kind.restype = i
         L.fftconv_forward.argtypes = [vp, vp, vp, vp, sz, sz, sz, vp, sz, vp]
         L.fftconv_forward.restype = i
+        L.fftconv_forward_noalloc.argtypes = [vp, vp, vp, vp, sz, sz, sz, vp]
+        L.fftconv_forward_noalloc.restype = i
         L.fftconv_forward_gated.argtypes = [vp, vp, vp, vp, vp, vp, sz, sz,
                                             sz, vp, sz, vp]
         L.fftconv_forward_gated.restype = i
@@ -264,6 +266,20 @@ class FFTConv:
                                    _stream_handle(stream))
         if st != 0:
             raise FFTConvError(st, "fftconv_forward")
+        return out
+
+    def forward_noalloc(self, u, k_f, out, stream=None):
+        """fftconv_forward_noalloc: y into the caller's `out` ([B, H, N],
+        plan dtype) with the library's static scratch as the workspace."""
+        u = u.contiguous()
+        if out.shape != u.shape or out.dtype != u.dtype or not out.is_contiguous():
+            raise ValueError("out must be a contiguous tensor of u's shape and dtype")
+        B, H, N = u.shape
+        st = lib().fftconv_forward_noalloc(self._plan, u.data_ptr(), k_f.data_ptr(),
+                                           out.data_ptr(), B, H, N,
+                                           _stream_handle(stream))
+        if st != 0:
+            raise FFTConvError(st, "fftconv_forward_noalloc")
         return out
 
     def forward_gated(self, u, w, v, k_f, out=None, workspace=None,

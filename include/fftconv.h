@@ -194,6 +194,24 @@ fftconv_status fftconv_forward(fftconv_plan_t plan, const void *u,
                                size_t N, void *workspace,
                                size_t workspace_bytes, void *stream);
 
+/* fftconv_forward without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc).  The workspace is a static
+ * device array of the library (64 MiB; each GPU the library runs on holds
+ * its own copy from the first call on it until the process ends); the call
+ * itself allocates nothing.  The multi-pass path (16-bit I/O, N >= 32K) runs
+ * its channel chunks sized to that array, so any B and H fit; an fp32 plan
+ * at N >= 32K needs B*H*N*8 bytes in one piece, and a call needing more
+ * than the array holds returns FFTCONV_ERR_WORKSPACE before launching
+ * anything.  Every call on one GPU uses the same array and leaves its
+ * contents behind (the counters that must start at zero are cleared by each
+ * call's own kernels): calls that overlap in time on one GPU (on different
+ * streams or host threads) race and must not be issued.  Arguments,
+ * results and the other errors as fftconv_forward. */
+fftconv_status fftconv_forward_noalloc(fftconv_plan_t plan, const void *u,
+                                       const void *k_f, void *y, size_t B, size_t H,
+                                       size_t N, void *stream);
+
 /* fftconv_forward for a spectrum from fftconv_kernel_spectrum_lowpass with
  * the same cutoff: the frequency-sparse convolution.  Kernels may skip the
  * blocks whose bins the cutoff zeroes: with 16-bit data at N = 1024 and at
