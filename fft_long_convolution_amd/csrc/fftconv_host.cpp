@@ -19,6 +19,7 @@
 #include <string.h>
 
 #include <complex>
+#include <cmath>
 #include <functional>
 #include <mutex>
 #include <new>
@@ -58,6 +59,8 @@ struct Shape {
     int mp_P1 = 0;       // > 0: multi-pass with outer levels P1 [x mp_P2] and
     int mp_P2 = 1;       //      4096-point inner slabs (4 x 32 x 32)
     bool grad = false;   // the kernel-gradient plan: LDS-staged kernels only
+    bool generic = false;  // LDS-staged kernels even where a register-resident
+                           // (row / wide) or 16-bit multi-pass kernel exists
     fftconv_dtype dtype = FFTCONV_F32;
 };
 
@@ -102,11 +105,14 @@ bool search_factors(int lg, int p, std::vector<int>& out) {
 
 bool generic_forced();
 
-// grad: the shape of the kernel-gradient passes, which hold two lines (u
-// and dy) per workgroup: LDS-staged kernels only, fused up to M = 8192 and
-// multi-pass slabs of at most 4096 points above.
-fftconv_status make_shape(size_t N, int p, fftconv_dtype dtype, Shape& s,
-                          bool grad = false) {
+// The shape of one candidate plan: order p (0: the family's own order for
+// N) on the LDS-staged kernels (generic) or on the kernel family that
+// covers N (row, wide or 16-bit multi-pass), grad: the shape of the
+// kernel-gradient passes, which hold two lines (u and dy) per workgroup:
+// LDS-staged kernels only, fused up to M = 8192 and multi-pass slabs of at
+// most 4096 points above.
+fftconv_status make_shape_fixed(size_t N, int p, fftconv_dtype dtype, Shape& s,
+                                bool grad, bool generic) {
     if (dtype != FFTCONV_F32 && dtype != FFTCONV_F16 && dtype != FFTCONV_BF16)
         return FFTCONV_ERR_UNSUPPORTED;
     if (!is_pow2(N) || N < kMinN || N > kMaxN) return FFTCONV_ERR_UNSUPPORTED;
@@ -118,13 +124,14 @@ fftconv_status make_shape(size_t N, int p, fftconv_dtype dtype, Shape& s,
     const int lg = ilog2(N);
     std::vector<int> fac;
     s.grad = grad;
+    s.generic = generic || grad;
     if (s.M <= (size_t)(grad ? 8192 : kFusedMaxM)) {
         s.path = 0;
         if (!default_fused(lg, fac)) return FFTCONV_ERR_UNSUPPORTED;
         // 16-bit I/O at N = 4K..16K: order 3 as P x 32 x 32 on the
         // one-workgroup-per-row kernel
         if (dtype != FFTCONV_F32 && lg >= 12 && lg <= 14 && (p == 0 || p == 3) &&
-            !generic_forced() && !grad) {
+            !s.generic) {
             s.wide_P = 1 << (lg - 10);
             fac = {s.wide_P, 32, 32};
         }
@@ -137,7 +144,7 @@ fftconv_status make_shape(size_t N, int p, fftconv_dtype dtype, Shape& s,
         const int waves = s.M <= 1024 ? 1 : (s.M <= 4096 ? 4 : 8);
         s.thr_fused = 64 * waves;
         s.lds_fused = (int)(s.M * 8 + waves * 32 * 8);
-    } else if (dtype != FFTCONV_F32 && !generic_forced() && !grad) {
+    } else if (dtype != FFTCONV_F32 && !s.generic) {
         s.path = 1;
         const int Po = (int)(s.M / 4096);
         switch (Po) {
@@ -219,7 +226,140 @@ bool generic_forced() {
 // I/O; FFTCONV_KERNEL=generic keeps such plans on the LDS-staged kernel.
 bool row_kernel_applies(const Shape& s) {
     return s.path == 0 && s.p == 2 && s.f[0] == 32 && (s.f[1] == 16 || s.f[1] == 32) &&
-           s.dtype != FFTCONV_F32 && !generic_forced() && !s.grad;
+           s.dtype != FFTCONV_F32 && !s.generic;
+}
+
+// ------------------------------------------------------------ cost model
+//
+// An MI355X analogue of the page's cost model (FlashFFTConv page, section
+// 3.4, "The GPU Cost Model for Order-p Decompositions", Equation 2): per
+// row, the work of every decomposition level is charged to the unit that
+// runs it -- DFT-matrix products on the matrix cores (tau_M), small DFTs
+// done with butterflies, twiddles and the spectrum pairing on the vector ALU
+// (tau_V), stage data and operand tables through LDS (sigma_S), and the
+// compulsory streams plus any workspace round trips through HBM
+// (sigma_H).  Unlike Equation 2's plain sum, compute and HBM overlap: the
+// matrix, vector and LDS instructions of a wave share its issue stream and
+// are summed, the memory streams run beside them, so the predicted time is
+// max(t_HBM, t_MFMA + t_VALU + t_LDS).  The HBM rate is the practical one a
+// streaming copy reaches on the part (the page likewise measures its
+// constants); the others are the published peaks of MI355X.
+namespace cost {
+constexpr double kHbm = 5.2e12;        // B/s, streaming copy on MI355X
+constexpr double kMfmaF16 = 2.5e15;    // dense f16/bf16 matrix flop/s
+constexpr double kMfmaF32 = 157.3e12;  // dense fp32 matrix flop/s
+constexpr double kValuF16 = 157.3e12;  // packed-f16 vector flop/s
+constexpr double kValuF32 = 78.6e12;   // fp32 vector flop/s (no packed fp32)
+constexpr double kLds = 256 * 128 * 2.4e9;   // B/s: 128 B/clk per CU
+}  // namespace cost
+
+struct CostTerms {
+    double hbm_bytes = 0, mfma_flops = 0, valu_flops_f16 = 0, valu_flops_f32 = 0, lds_bytes = 0;
+    double t_hbm = 0, t_mfma = 0, t_valu = 0, t_lds = 0, t_pred = 0;
+};
+
+// Work of one call over B x H rows of the plan shape s.  B = 0: the per-row
+// cost of a large batch, the spectrum's read amortised away (H rows).
+CostTerms estimate(const Shape& s, size_t B, size_t H) {
+    CostTerms c;
+    const double R = (double)(B ? B : 1) * (double)H, M = (double)s.M, N = (double)s.N;
+    const double sio = s.dtype == FFTCONV_F32 ? 4.0 : 2.0;
+    const double skf = s.dtype == FFTCONV_F32 ? 16.0 : 8.0;
+    const bool f32 = s.dtype == FFTCONV_F32;
+    const bool bf16 = s.dtype == FFTCONV_BF16;
+    const bool row = row_kernel_applies(s);
+    // --- HBM: u, y once; k_f once per channel; workspace round trips
+    double hbm = R * 2.0 * N * sio + (B ? (double)H * M * skf : 0.0);
+    if (s.path == 1) hbm += R * M * (s.mp_P1 ? 16.0 : 32.0);
+    // --- per level: matrix products, or butterflies on the vector ALU
+    double mf = 0, vf16 = 0, vf32 = 0, lds = 0;
+    for (int i = 0; i < s.p; ++i) {
+        const double n = (double)s.f[i];
+        const double half = (i == 0) ? 0.5 : 1.0;   // the zero half / half outputs
+        bool valu_level = false;
+        if (s.wide_P && i == 0) valu_level = true;
+        if (s.mp_P1 && i < s.n_outer && !(s.mp_P1 == 32 && s.mp_P2 == 32)) valu_level = true;
+        if (valu_level) {
+            // radix-2 butterflies, both directions: 5 M log2(n) flops each
+            const double fl = half * 2.0 * 5.0 * M * std::log2(n);
+            if (bf16 || f32) vf32 += fl; else vf16 += fl;
+        } else {
+            double fl = half * 16.0 * M * n;
+            // hi/lo split operands: bf16 rows into the row kernel's first
+            // stage, both 32-point levels of the 4M column passes
+            if (row && bf16 && i == 0) fl *= 2.0;
+            if (s.mp_P1 == 32 && s.mp_P2 == 32 && i < 2) fl *= 2.0;
+            mf += fl;
+        }
+    }
+    // twiddles between levels (both directions) and the spectrum pairing
+    // (two complex multiply-adds per bin)
+    const double tw = (double)(s.p - 1) * 2.0 * 6.0 * M, pair = 16.0 * M;
+    if (f32) vf32 += tw + pair;
+    else vf16 += tw + pair;
+    // --- LDS traffic
+    if (row) {
+        // the four stage tables read at each use, one 16-byte operand per
+        // lane and tile (KB per row: first stage 4, or 8 with the bf16 hi/lo
+        // split; second (NB/8)(NB/16); its inverse 2 (NB/16)^2; last 4),
+        // and the spectrum coefficients (8 B per bin)
+        const double q = (double)s.f[1] / 16.0;
+        const double tabs_kb = (bf16 ? 8.0 : 4.0) + 2.0 * q * q + 2.0 * q * q + 4.0;
+        lds = tabs_kb * 1024.0 + M * 8.0;
+    } else if (s.wide_P || s.mp_P1) {
+        // sub-rows written and read around the engine, both directions;
+        // engine operand tables per 1024-point sub-row; outer twiddles
+        lds = 16.0 * M + 16.0 * M + 4.0 * M;
+        if (s.mp_P1) lds += 16.0 * M;   // column tiles of the outer passes
+    } else {
+        // LDS-staged: every stage reads and writes the row (fp32 complex)
+        // in both directions, as column gathers and scatters that reach
+        // about 1/6 of the LDS peak for 16- and 32-point stages and 1/10
+        // for 8-point ones (measured on MI355X, 16-bit plans at N = 1K..16K;
+        // charged here as extra bytes at the peak rate)
+        for (int i = 0; i < s.p; ++i) lds += 32.0 * M * (s.f[i] >= 16 ? 6.0 : 10.0);
+    }
+    c.hbm_bytes = hbm;
+    c.mfma_flops = R * mf;
+    c.valu_flops_f16 = R * vf16;
+    c.valu_flops_f32 = R * vf32;
+    c.lds_bytes = R * lds;
+    c.t_hbm = hbm / cost::kHbm;
+    c.t_mfma = c.mfma_flops / (f32 ? cost::kMfmaF32 : cost::kMfmaF16);
+    c.t_valu = c.valu_flops_f16 / cost::kValuF16 + c.valu_flops_f32 / cost::kValuF32;
+    c.t_lds = c.lds_bytes / cost::kLds;
+    const double comp = c.t_mfma + c.t_valu + c.t_lds;
+    c.t_pred = c.t_hbm > comp ? c.t_hbm : comp;
+    return c;
+}
+
+// p = 0: the candidate of lowest predicted time among every order the
+// kernels support for N, on the LDS-staged kernels and on the kernel family
+// that covers N (ties: the lower order).  FFTCONV_KERNEL=generic restricts
+// the choice to the LDS-staged kernels.
+fftconv_status make_shape(size_t N, int p, fftconv_dtype dtype, Shape& s,
+                          bool grad = false) {
+    const bool force_generic = generic_forced();
+    if (p != 0 || grad) return make_shape_fixed(N, p, dtype, s, grad, force_generic);
+    fftconv_status first = FFTCONV_ERR_UNSUPPORTED;
+    bool found = false;
+    double best = 0;
+    for (int q = 2; q <= kMaxStages; ++q)
+        for (int gen = force_generic ? 1 : 0; gen <= 1; ++gen) {
+            Shape c;
+            const fftconv_status st = make_shape_fixed(N, q, dtype, c, false, gen != 0);
+            if (st != FFTCONV_OK) {
+                if (first == FFTCONV_ERR_UNSUPPORTED) first = st;
+                continue;
+            }
+            const double t = estimate(c, 0, 1).t_pred;
+            if (!found || t < best * (1.0 - 1e-9)) {
+                best = t;
+                s = c;
+                found = true;
+            }
+        }
+    return found ? FFTCONV_OK : first;
 }
 
 void fill_info(const Shape& s, fftconv_plan_info* info) {
@@ -1217,6 +1357,53 @@ fftconv_status fftconv_plan_query(size_t N, int p, fftconv_dtype dtype,
     fftconv_status st = make_shape(N, p, dtype, s);
     if (st != FFTCONV_OK) return st;
     fill_info(s, info);
+    return FFTCONV_OK;
+}
+
+fftconv_status fftconv_plan_estimate(size_t N, int p, fftconv_dtype dtype, int lds_staged,
+                                     size_t B, size_t H, fftconv_estimate* out) {
+    if (!out) return FFTCONV_ERR_INVALID_ARG;
+    Shape s;
+    fftconv_status st;
+    if (lds_staged) {
+        if (p == 0) {
+            // the LDS-staged kernels' own choice: lowest predicted order
+            st = FFTCONV_ERR_UNSUPPORTED;
+            double best = 0;
+            for (int q = 2; q <= kMaxStages; ++q) {
+                Shape c;
+                if (make_shape_fixed(N, q, dtype, c, false, true) != FFTCONV_OK) continue;
+                const double t = estimate(c, 0, 1).t_pred;
+                if (st != FFTCONV_OK || t < best * (1.0 - 1e-9)) {
+                    best = t;
+                    s = c;
+                    st = FFTCONV_OK;
+                }
+            }
+        } else {
+            st = make_shape_fixed(N, p, dtype, s, false, true);
+        }
+    } else {
+        st = make_shape(N, p, dtype, s);
+    }
+    if (st != FFTCONV_OK) return st;
+    memset(out, 0, sizeof(*out));
+    fftconv_plan_info info;
+    fill_info(s, &info);
+    out->order = s.p;
+    for (int i = 0; i < s.p; ++i) out->factors[i] = s.f[i];
+    out->path = info.path;
+    out->kernel_variant = info.kernel_variant;
+    const CostTerms c = estimate(s, B, H);
+    out->hbm_bytes = c.hbm_bytes;
+    out->mfma_flops = c.mfma_flops;
+    out->valu_flops = c.valu_flops_f16 + c.valu_flops_f32;
+    out->lds_bytes = c.lds_bytes;
+    out->t_hbm = c.t_hbm;
+    out->t_mfma = c.t_mfma;
+    out->t_valu = c.t_valu;
+    out->t_lds = c.t_lds;
+    out->t_pred = c.t_pred;
     return FFTCONV_OK;
 }
 

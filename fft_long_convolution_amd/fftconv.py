@@ -77,6 +77,8 @@ def lib() -> ctypes.CDLL:
         L.fftconv_plan.restype = i
         L.fftconv_plan_query.argtypes = [sz, i, i, ctypes.POINTER(PlanInfo)]
         L.fftconv_plan_query.restype = i
+        L.fftconv_plan_estimate.argtypes = [sz, i, i, i, sz, sz, ctypes.POINTER(Estimate)]
+        L.fftconv_plan_estimate.restype = i
         L.fftconv_plan_get_info.argtypes = [vp, ctypes.POINTER(PlanInfo)]
         L.fftconv_plan_get_info.restype = i
         L.fftconv_plan_destroy.argtypes = [vp]
@@ -121,6 +123,33 @@ def plan_query(N: int, p: int = 0, dtype: str = "bf16") -> dict:
     if st != 0:
         raise FFTConvError(st, "fftconv_plan_query(N=%d, p=%d)" % (N, p))
     return info.as_dict()
+
+
+class Estimate(ctypes.Structure):
+    _fields_ = [("order", ctypes.c_int), ("factors", ctypes.c_int * 8),
+                ("path", ctypes.c_int), ("kernel_variant", ctypes.c_int),
+                ("hbm_bytes", ctypes.c_double), ("mfma_flops", ctypes.c_double),
+                ("valu_flops", ctypes.c_double), ("lds_bytes", ctypes.c_double),
+                ("t_hbm", ctypes.c_double), ("t_mfma", ctypes.c_double),
+                ("t_valu", ctypes.c_double), ("t_lds", ctypes.c_double),
+                ("t_pred", ctypes.c_double)]
+
+    def as_dict(self) -> dict:
+        d = {k: getattr(self, k) for k, _ in self._fields_ if k != "factors"}
+        d["factors"] = list(self.factors[:self.order])
+        return d
+
+
+def plan_estimate(N: int, p: int = 0, dtype: str = "bf16", lds_staged: bool = False,
+                  B: int = 1, H: int = 1) -> dict:
+    """fftconv_plan_estimate: the cost model's prediction for one forward
+    call over B x H rows (no device needed)."""
+    e = Estimate()
+    st = lib().fftconv_plan_estimate(N, p, DTYPES[dtype], 1 if lds_staged else 0,
+                                     B, H, ctypes.byref(e))
+    if st != 0:
+        raise FFTConvError(st, "fftconv_plan_estimate(N=%d, p=%d)" % (N, p))
+    return e.as_dict()
 
 
 def _torch_dtype(dtype: str):

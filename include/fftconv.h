@@ -82,10 +82,46 @@ typedef struct fftconv_plan_info {
                                      (N >= 32K, 16-bit I/O)                */
 } fftconv_plan_info;
 
+/* Predicted cost of one forward call (an MI355X analogue of the page's cost
+ * model: "FlashFFTConv: Efficient Convolutions for Long Sequences with
+ * Tensor Cores", section 3.4, "The GPU Cost Model for Order-p
+ * Decompositions", Equation 2).  Each decomposition level's work is charged
+ * to the unit that runs it: DFT-matrix products to the matrix cores
+ * (2.5 PFLOP/s f16, 157.3 TFLOP/s fp32), butterfly stages, twiddles and the
+ * spectrum pairing to the vector ALU (157.3 TFLOP/s packed f16, 78.6 fp32),
+ * stage data and operand tables to LDS (128 B/clk per CU), the u, y and k_f
+ * streams and any workspace round trips to HBM (5.2 TB/s, what a streaming
+ * copy reaches).  Matrix, vector and LDS work share a wave's issue stream
+ * and add up; HBM runs beside them:
+ *     t_pred = max(t_hbm, t_mfma + t_valu + t_lds).
+ * With p = 0 fftconv_plan picks the candidate (order and kernel family) of
+ * lowest t_pred for N. */
+typedef struct fftconv_estimate {
+    int order;                /* p of the estimated plan                    */
+    int factors[8];
+    int path;                 /* as fftconv_plan_info                       */
+    int kernel_variant;       /* as fftconv_plan_info                       */
+    double hbm_bytes;         /* per call                                   */
+    double mfma_flops;
+    double valu_flops;
+    double lds_bytes;
+    double t_hbm, t_mfma, t_valu, t_lds, t_pred;   /* seconds per call      */
+} fftconv_estimate;
+
+/* Estimate the call over B x H rows of the plan (N, p, dtype) -- the plan
+ * fftconv_plan builds (lds_staged = 0) or the same order on the LDS-staged
+ * kernels (lds_staged = 1).  B = 0 gives the cost per H rows of a large
+ * batch (the spectrum's one read amortised away), which is what the choice
+ * for p = 0 compares.  No device access.  Errors as fftconv_plan_query;
+ * out == NULL -> FFTCONV_ERR_INVALID_ARG. */
+fftconv_status fftconv_plan_estimate(size_t N, int p, fftconv_dtype dtype, int lds_staged,
+                                     size_t B, size_t H, fftconv_estimate *out);
+
 /* Create a plan for length N, Monarch order p and I/O dtype.
  *  N: a power of two in [256, 4194304] (section 3.4 discusses lengths up to
  *     4M; section 4.2's tables span 256..4M).
- *  p: 0 picks the default factorisation for N; p >= 2 requests exactly p
+ *  p: 0 picks the factorisation of lowest predicted time for N
+ *     (fftconv_plan_estimate); p >= 2 requests exactly p
  *     factors and returns FFTCONV_ERR_UNSUPPORTED when N cannot be split
  *     that way.  For the LDS-staged kernels the factors are 8, 16 or 32 (the
  *     last one 16 or 32); 16-bit plans at N = 4K..16K use P x 32 x 32
