@@ -317,6 +317,12 @@ __device__ __forceinline__ void load_regs(Regs& E, const void* f2a, const void* 
             for (int r = 0; r < 4; ++r) E.twf[it][kt][r] = twf[lane * 16 + (it * 2 + kt) * 4 + r];
 }
 
+// The same tables through buffer descriptors (scalar bases, one 32-bit lane
+// offset): for kernels that reload them inside their row loop, where
+// hoisted 64-bit per-lane addresses would stay live across the loop.
+__device__ __forceinline__ void load_regs_buf(Regs& E, const void* f2a, const void* i2b,
+                                              const uint32_t* twf, int lane);
+
 // Forward 1024-point DFT of one region (engine layout) into z[kt][mt][e].
 // SK (a band limit below M/4): the odd M-tiles of the second stage,
 // k_b = 8..23, hold only bins the limit zeroes -- not computed (zero).
@@ -536,6 +542,31 @@ __device__ __forceinline__ uint4 buf_ld16(__amdgpu_buffer_rsrc_t r, unsigned vof
     typedef unsigned v4u __attribute__((ext_vector_type(4)));
     const v4u v = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
     return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+__device__ __forceinline__ void load_regs_buf(Regs& E, const void* f2a, const void* i2b,
+                                              const uint32_t* twf, int lane) {
+    const __amdgpu_buffer_rsrc_t rf = buf_rsrc(f2a, 8 * 64 * 16);
+    const __amdgpu_buffer_rsrc_t ri = buf_rsrc(i2b, 8 * 64 * 16);
+    const __amdgpu_buffer_rsrc_t rt = buf_rsrc(twf, 64 * 16 * 4);
+    const unsigned vo = (unsigned)lane * 16u;
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) E.f2a[mt][ks] = buf_ld16(rf, vo, (mt * 2 + ks) * 64 * 16);
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+        for (int jt = 0; jt < 4; ++jt) E.i2b[ks][jt] = buf_ld16(ri, vo, (ks * 4 + jt) * 64 * 16);
+    // twf: 16 consecutive words per lane, [it][kt][r]
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const uint4 v = buf_ld16(rt, vo * 4u, q * 16);
+        E.twf[q >> 1][q & 1][0] = v.x;
+        E.twf[q >> 1][q & 1][1] = v.y;
+        E.twf[q >> 1][q & 1][2] = v.z;
+        E.twf[q >> 1][q & 1][3] = v.w;
+    }
 }
 
 }  // namespace eng

@@ -125,7 +125,13 @@ fftconv_status make_shape_fixed(size_t N, int p, fftconv_dtype dtype, Shape& s,
     std::vector<int> fac;
     s.grad = grad;
     s.generic = generic || grad;
-    if (s.M <= (size_t)(grad ? 8192 : kFusedMaxM)) {
+    if (dtype != FFTCONV_F32 && lg == 15 && (p == 0 || p == 3) && !s.generic) {
+        // 16-bit I/O at N = 32K: 32 x 32 x 32 on the one-workgroup-per-row
+        // kernel (eight waves, two mirror pairs each), fused
+        s.path = 0;
+        s.wide_P = 32;
+        fac = {32, 32, 32};
+    } else if (s.M <= (size_t)(grad ? 8192 : kFusedMaxM)) {
         s.path = 0;
         if (!default_fused(lg, fac)) return FFTCONV_ERR_UNSUPPORTED;
         // 16-bit I/O at N = 4K..16K: order 3 as P x 32 x 32 on the
@@ -686,8 +692,12 @@ std::vector<uint16_t> wide_i1a(int P) {
 
 // Outer-stage twiddles W_M^{n' k1}, k1 = 1..P/2, for the columns each
 // thread owns: n_b = t & 31, n_a = CPT (t >> 5) + j.
+// Threads of the wide kernel's workgroup: one wave per mirror pair of
+// sub-rows, at most eight.
+int wide_threads(int P) { return 64 * (P / 2 < 8 ? P / 2 : 8); }
+
 std::vector<uint16_t> wide_outer_twiddles(int P) {
-    const int T = 32 * P, CPT = 1024 / T, M = 1024 * P;
+    const int T = wide_threads(P), CPT = 1024 / T, M = 1024 * P;
     std::vector<uint16_t> out((size_t)(P / 2) * T * CPT * 2);
     for (int k1 = 1; k1 <= P / 2; ++k1)
         for (int t = 0; t < T; ++t)
@@ -827,6 +837,10 @@ struct fftconv_plan_s {
     const float2* mp_tw1 = nullptr;   // W_M^c, c < M / P1
     const float2* mp_tw2 = nullptr;   // W_{M/P1}^c, c < 4096 (two levels)
     fftconv_plan_s* grad = nullptr;   // LDS-staged plan of the kernel gradient
+    // the plan whose engine computes the kernel gradient when it is not this
+    // plan's own (N = 32K: the forward is the fused 32 x 32 x 32 kernel, the
+    // gradient the multi-pass engine)
+    fftconv_plan_s* kg = nullptr;
 };
 
 namespace {
@@ -844,6 +858,7 @@ hipError_t upload(fftconv_plan_s* pl, const void* host, size_t bytes, void** dev
 void free_plan(fftconv_plan_s* pl) {
     if (!pl) return;
     free_plan(pl->grad);
+    free_plan(pl->kg);
     for (void* p : pl->allocs) (void)hipFree(p);
     delete pl;
 }
@@ -859,6 +874,9 @@ fftconv_status forward_impl(fftconv_plan_t plan, const void* u, const void* w,
                             size_t H, size_t N, void* workspace,
                             size_t workspace_bytes, void* stream, int skip_hi,
                             size_t chunk_cap);
+fftconv_status backward_dk(const fftconv_plan_s* plan, const void* u, const void* dy,
+                           float* dk, size_t B, size_t H, size_t N, void* workspace,
+                           hipStream_t st);
 
 fftconv_status build_device_tables(fftconv_plan_s* pl) {
     const Shape& s = pl->s;
@@ -1037,11 +1055,12 @@ fftconv_status build_device_tables(fftconv_plan_s* pl) {
         if (upload(pl, two.data(), two.size() * 2, &d) != hipSuccess) return FFTCONV_ERR_HIP;
         W.two = (const uint32_t*)d;
         W.N = (int)s.N;
-        // stage tables (16 KB) + outer twiddles + one row of f16 points +
-        // the k_b exchange
-        pl->lds_wide = 16 * 1024 + (P / 2) * 4096 + (int)s.M * 4 + 39 * 16 * 4 + 16;
+        // stage tables (16 KB) + outer twiddles (read through L2 at P = 32)
+        // + one row of f16 points + the k_b exchange
+        pl->lds_wide = 16 * 1024 + (P <= 16 ? (P / 2) * 4096 : 0) + (int)s.M * 4 +
+                       39 * 16 * 4 + 16;
         // two waves per SIMD (256 registers each), LDS permitting
-        const int by_waves = 8 / (P / 2);
+        const int by_waves = 8 / (wide_threads(P) / 64);
         const int by_lds = (160 * 1024) / pl->lds_wide;
         pl->wide_wgs_per_cu = by_waves < by_lds ? by_waves : by_lds;
         if (pl->wide_wgs_per_cu < 1) pl->wide_wgs_per_cu = 1;
@@ -1123,6 +1142,23 @@ fftconv_status build_mp_tables(fftconv_plan_s* pl) {
 // innermost stage, one for a 32-point one).
 
 fftconv_status build_grad_plan(fftconv_plan_s* pl) {
+    if (pl->s.wide_P == 32) {
+        // the kernel gradient at 32K runs on the multi-pass engine
+        Shape m;
+        fftconv_status st = make_shape_fixed(pl->s.N, 4, pl->s.dtype, m, false, false);
+        if (st != FFTCONV_OK) return st;
+        if (!m.mp_P1) return FFTCONV_ERR_UNSUPPORTED;
+        fftconv_plan_s* kp = new (std::nothrow) fftconv_plan_s();
+        if (!kp) return FFTCONV_ERR_HIP;
+        kp->s = m;
+        kp->device = pl->device;
+        st = build_device_tables(kp);
+        if (st != FFTCONV_OK) {
+            free_plan(kp);
+            return st;
+        }
+        pl->kg = kp;
+    }
     Shape g;
     fftconv_status st = make_shape(pl->s.N, 0, pl->s.dtype, g, true);
     if (st != FFTCONV_OK) return st;
@@ -1216,6 +1252,7 @@ size_t kgrad_mp_channels(const fftconv_plan_s* pl, size_t B, size_t H) {
 }
 
 size_t kgrad_workspace_bytes(const fftconv_plan_s* pl, size_t B, size_t H) {
+    if (pl->kg) return kgrad_workspace_bytes(pl->kg, B, H);
     if (kgrad_on_row(pl)) return (size_t)kgrad_row_slices(pl, B, H) * H * 64 * 32 * 4;
     if (kgrad_on_mp(pl, B)) {
         // rows of u and dy after the forward column passes, and one result
@@ -1878,15 +1915,28 @@ fftconv_status fftconv_backward(fftconv_plan_t plan, const void* u,
         if (fs != FFTCONV_OK) return fs;
     }
     if (!dk || H == 0) return FFTCONV_OK;
-    const fftconv_plan_s* gp = plan->grad;
-    const Shape& g = gp->s;
-    const int io = (int)s.dtype;
-    hipError_t e;
     if (rows == 0) {
         // an empty batch contributes nothing: dk = 0
         return launch_scale_f32(dk, (long long)(H * N), 0.f, st) == hipSuccess
                    ? FFTCONV_OK : FFTCONV_ERR_HIP;
     }
+    return backward_dk(plan->kg ? plan->kg : plan, u, dy, dk, B, H, N, workspace, st);
+}
+
+}  // extern "C"
+
+namespace {
+
+// dk of the causal convolution on the engine of `plan` (the caller's plan,
+// or the one it delegates the kernel gradient to); arguments validated.
+fftconv_status backward_dk(const fftconv_plan_s* plan, const void* u, const void* dy,
+                           float* dk, size_t B, size_t H, size_t N, void* workspace,
+                           hipStream_t st) {
+    const Shape& s = plan->s;
+    const size_t rows = B * H;
+    const size_t esz = s.dtype == FFTCONV_F32 ? 4 : 2;
+    const int io = (int)s.dtype;
+    hipError_t e;
     if (kgrad_on_row(plan)) {
         KgRowParams R{};
         R.B = (int)B;
@@ -1994,6 +2044,8 @@ fftconv_status fftconv_backward(fftconv_plan_t plan, const void* u,
         }
         return e == hipSuccess ? FFTCONV_OK : FFTCONV_ERR_HIP;
     }
+    const fftconv_plan_s* gp = plan->grad;
+    const Shape& g = gp->s;
     KgradParams K{};
     K.B = (int)B;
     K.H = (int)H;
@@ -2044,4 +2096,4 @@ fftconv_status fftconv_backward(fftconv_plan_t plan, const void* u,
     return e == hipSuccess ? FFTCONV_OK : FFTCONV_ERR_HIP;
 }
 
-}  // extern "C"
+}  // namespace

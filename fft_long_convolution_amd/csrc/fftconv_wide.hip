@@ -1,6 +1,6 @@
-// Fused kernel for rows of N = P * 1024 (P = 4, 8, 16) with 16-bit I/O: one
-// workgroup of P/2 wavefronts per row, the whole 2N-point transform held in
-// LDS and registers (page "FlashFFTConv: Efficient Convolutions for Long
+// Fused kernel for rows of N = P * 1024 (P = 4, 8, 16, 32) with 16-bit I/O:
+// one workgroup per row (P/2 wavefronts, at most eight), the whole 2N-point
+// transform held in LDS and registers (page "FlashFFTConv: Efficient Convolutions for Long
 // Sequences with Tensor Cores", section 3.4 and Algorithm 1: an order-3
 // Monarch decomposition P x 32 x 32, with the real-input packing and the
 // implicit zero padding of section 3.4, "Implicit zero-padding for causal
@@ -41,16 +41,32 @@ namespace fftconv {
 
 using namespace eng;
 
+// Waves per workgroup: one per mirror pair of sub-rows up to P = 16; at
+// P = 32 the 16 pairs go to 8 waves, two each in turn (the row's 32 sub-rows
+// fill 128 KB of LDS, which leaves no room for the outer twiddles: those are
+// read through L2 instead).
+template <int P>
+struct WideShape {
+    static constexpr int HALF = P / 2;
+    static constexpr int WAVES = HALF < 8 ? HALF : 8;
+    static constexpr int T = 64 * WAVES;
+    static constexpr int PPW = HALF / WAVES;     // mirror pairs per wave
+    static constexpr bool TWG = P > 16;          // outer twiddles from memory
+};
+
 template <int IO, int P, bool G, bool SK>
-__global__ void __launch_bounds__(32 * P, 2) wide_kernel(WideParams prm) {
-    constexpr int Q = 1024, M = P * Q, HALF = P / 2, T = 32 * P;
+__global__ void __launch_bounds__(WideShape<P>::T, 2) wide_kernel(WideParams prm) {
+    typedef WideShape<P> WS;
+    constexpr int Q = 1024, M = P * Q, HALF = P / 2, T = WS::T;
+    constexpr int WAVES = WS::WAVES, PPW = WS::PPW;
+    constexpr bool TWG = WS::TWG;
     constexpr int CPT = Q / T;   // outer-stage columns per thread
 
     extern __shared__ uint4 s_lds[];
     uint4* s_f1b = s_lds;                              // [ks 2][jt 4][64]
     uint4* s_i1a = s_f1b + 8 * 64;                     // [mt 4][ks 2][64]
     uint32_t* s_two = (uint32_t*)(s_i1a + 8 * 64);     // [k1 - 1][thread][column]
-    uint32_t* s_buf = s_two + HALF * Q;                // [P sub-rows][Q]
+    uint32_t* s_buf = s_two + (TWG ? 0 : HALF * Q);    // [P sub-rows][Q]
     uint32_t* s_scr = s_buf + M;                       // [39 k_b slots][16 x]
     int* s_claim = (int*)(s_scr + 39 * 16);            // [2] claimed row indices
 
@@ -67,14 +83,20 @@ __global__ void __launch_bounds__(32 * P, 2) wide_kernel(WideParams prm) {
         s_f1b[i] = ((const uint4*)prm.f1b)[i];
         s_i1a[i] = ((const uint4*)prm.i1a)[i];
     }
-    for (int i = tid; i < HALF * Q / 4; i += T) ((uint4*)s_two)[i] = ((const uint4*)prm.two)[i];
+    if constexpr (!TWG)
+        for (int i = tid; i < HALF * Q / 4; i += T) ((uint4*)s_two)[i] = ((const uint4*)prm.two)[i];
     if (tid == 0) {
         const long long c0 = claimer.next(), c1 = claimer.next();
         s_claim[0] = (int)(c0 < total ? c0 : total);
         s_claim[1] = (int)(c1 < total ? c1 : total);
     }
+    // engine tables in registers: for the whole kernel up to P = 16; at
+    // P = 32 they are reloaded (from L2) for each row's engine phase, so
+    // that they are not live across the larger outer stages
     Regs E;
-    load_regs(E, prm.f2a, SK ? prm.i2bs : prm.i2b, prm.twf, lane);
+    if constexpr (!TWG) load_regs(E, prm.f2a, SK ? prm.i2bs : prm.i2b, prm.twf, lane);
+    // outer twiddles read from memory (P = 32): [k1 - 1][thread][column]
+    const __amdgpu_buffer_rsrc_t rtwo = buf_rsrc(prm.two, HALF * T * CPT * 4);
 
     // ---- outer-stage geometry: n_b = tid & 31, n_a = na0 + j (j < CPT)
     const int nb = tid & 31, na0 = CPT * (tid >> 5);
@@ -84,6 +106,13 @@ __global__ void __launch_bounds__(32 * P, 2) wide_kernel(WideParams prm) {
     auto load_two = [&](uint32_t (&tw)[HALF][CPT]) {
 #pragma unroll
         for (int k1 = 0; k1 < HALF; ++k1) {
+            if constexpr (TWG) {
+                static_assert(CPT == 2, "memory twiddles are read as pairs");
+                const uint2 v = *(const uint2*)(prm.two + (k1 * T + tid) * CPT);
+                tw[k1][0] = v.x;
+                tw[k1][1] = v.y;
+                continue;
+            }
             const uint32_t* s = s_two + (k1 * T + tid) * CPT;
             if constexpr (CPT == 2) {
                 const uint2 v = *(const uint2*)s;
@@ -141,7 +170,38 @@ __global__ void __launch_bounds__(32 * P, 2) wide_kernel(WideParams prm) {
         // next row of this workgroup (past the end: re-read this row)
         const int inext = nxt < total ? nxt : cur;
         // ---------------- outer forward stage
-        {
+        if constexpr (TWG) {
+            // one column at a time, its twiddles read as it starts and its
+            // P outputs stored to LDS as they come
+            typedef Outer<IO> O;
+            typedef typename O::V C;
+#pragma unroll
+            for (int j = 0; j < CPT; ++j) {
+                uint32_t tw[HALF];
+#pragma unroll
+                for (int k1 = 0; k1 < HALF; ++k1)
+                    tw[k1] = __builtin_amdgcn_raw_buffer_load_b32(rtwo, (unsigned)(tid * CPT + j) * 4u,
+                                                                  k1 * T * CPT * 4, 0);
+                C xin[HALF], A[P];
+#pragma unroll
+                for (int n1 = 0; n1 < HALF; ++n1) {
+                    xin[n1] = O::from_io(uin[n1][j]);
+                    if constexpr (G) xin[n1] = O::emul(xin[n1], win[n1][j]);
+                }
+                dft_half_in<P>(xin, A);
+                uint32_t* dst = s_buf + oa0 + j;
+                dst[0] = O::to_h2(A[0]);
+                dst[Q] = O::to_h2(O::mul(A[HALF], tw[HALF - 1]));
+#pragma unroll
+                for (int k1 = 1; k1 < HALF; ++k1) {
+                    dst[(2 * k1) * Q] = O::to_h2(O::mul(A[k1], tw[k1 - 1]));
+                    dst[(2 * k1 + 1) * Q] = O::to_h2(O::mul(cnj(A[P - k1]), tw[k1 - 1]));
+                }
+                // the columns one after the other (interleaved, their
+                // transforms would not fit the registers together)
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        } else {
             typedef Outer<IO> O;
             typedef typename O::V C;
             uint32_t two[HALF][CPT];
@@ -183,30 +243,34 @@ __global__ void __launch_bounds__(32 * P, 2) wide_kernel(WideParams prm) {
         long long c2 = 0;
         if (tid == 0) c2 = claimer.next();
         __syncthreads();
+        if constexpr (TWG) load_regs_buf(E, prm.f2a, SK ? prm.i2bs : prm.i2b, prm.twf, lane);
 
-        // ---------------- engine: sub-rows 2*wave and 2*wave + 1
-        {
+        // ---------------- engine: mirror pair j = wave + q * WAVES (q < PPW),
+        // sub-rows 2 j and 2 j + 1
+#pragma unroll
+        for (int q = 0; q < PPW; ++q) {
+            const int pr = wave + q * WAVES;
             // spectrum coefficients of this row's bins, in flight while the
             // forward transforms run; kt = 1 is issued after sub-row 0
-            const uint4* cf = (const uint4*)prm.kf + ((long long)h * HALF + wave) * 1024;
+            const uint4* cf = (const uint4*)prm.kf + ((long long)h * HALF + pr) * 1024;
             uint4 cfr[2][2][4];   // [sub][kt][mt]
 #pragma unroll
             for (int sub = 0; sub < 2; ++sub)
 #pragma unroll
                 for (int mt = 0; mt < 4; ++mt) cfr[sub][0][mt] = cf[(sub * 2) * 256 + mt * 64 + lane];
             uint32_t z[2][2][4][2];   // [sub][kt][mt][e] packed f16 bins
-            forward<SK>(s_buf + (2 * wave) * Q, s_f1b, E, lane, z[0]);
+            forward<SK>(s_buf + (2 * pr) * Q, s_f1b, E, lane, z[0]);
 #pragma unroll
             for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
                 for (int mt = 0; mt < 4; ++mt) cfr[s2][1][mt] = cf[(s2 * 2 + 1) * 256 + mt * 64 + lane];
             __builtin_amdgcn_sched_barrier(0);
-            forward<SK>(s_buf + (2 * wave + 1) * Q, s_f1b, E, lane, z[1]);
+            forward<SK>(s_buf + (2 * pr + 1) * Q, s_f1b, E, lane, z[1]);
             __builtin_amdgcn_sched_barrier(0);
 
             // ---------------- spectrum product
             uint4 a2[2][2][2];   // [sub][kt][ks] inverse A operands
-            if (wave != 0) {
+            if (pr != 0) {
 #pragma unroll
                 for (int kt = 0; kt < 2; ++kt) {
                     pair_elem<SK>(kt, z[0], z[1], cfr[0][kt], cfr[1][kt], a2[0][kt], a2[1][kt]);
@@ -222,22 +286,60 @@ __global__ void __launch_bounds__(32 * P, 2) wide_kernel(WideParams prm) {
                     __builtin_amdgcn_sched_barrier(0);
                 }
             }
-            // publish the row after next; then the next row's input, issued
-            // only now because the load counter retires in order and the
-            // coefficient loads above must not wait behind it
-            if (tid == 0) s_claim[0] = (int)(c2 < total ? c2 : total);
-            load_u(inext);
+            if (q == PPW - 1) {
+                // publish the row after next; then the next row's input,
+                // issued only now because the load counter retires in order
+                // and the coefficient loads above must not wait behind it
+                if (tid == 0) s_claim[0] = (int)(c2 < total ? c2 : total);
+                load_u(inext);
+            }
 
             // ---------------- inverse 1024-point DFT of both sub-rows
-            inverse<SK>(a2[0], s_i1a, E, lane, i1_base, s_buf + (2 * wave) * Q);
+            inverse<SK>(a2[0], s_i1a, E, lane, i1_base, s_buf + (2 * pr) * Q);
             __builtin_amdgcn_sched_barrier(0);
-            inverse<SK>(a2[1], s_i1a, E, lane, i1_base, s_buf + (2 * wave + 1) * Q);
+            inverse<SK>(a2[1], s_i1a, E, lane, i1_base, s_buf + (2 * pr + 1) * Q);
             __builtin_amdgcn_sched_barrier(0);
         }
         __syncthreads();
         const int nn = s_claim[0];
         // ---------------- outer inverse stage and store
-        {
+        if constexpr (TWG) {
+            // one column at a time (as the forward stage)
+            typedef Outer<IO> O;
+            typedef typename O::V C;
+            uint32_t* yrow = (uint32_t*)prm.y + mrow * (M / 2);
+#pragma unroll
+            for (int j = 0; j < CPT; ++j) {
+                uint32_t vin[G ? HALF : 1];   // output gate (gated only)
+                if constexpr (G) {
+                    const uint32_t* vr = (const uint32_t*)prm.v + mrow * (M / 2);
+#pragma unroll
+                    for (int n1 = 0; n1 < HALF; ++n1)
+                        vin[n1] = __builtin_nontemporal_load(&vr[n1 * Q + lofs + 32 * j]);
+                }
+                uint32_t tw[HALF];
+#pragma unroll
+                for (int k1 = 0; k1 < HALF; ++k1)
+                    tw[k1] = __builtin_amdgcn_raw_buffer_load_b32(rtwo, (unsigned)(tid * CPT + j) * 4u,
+                                                                  k1 * T * CPT * 4, 0);
+                const uint32_t* src = s_buf + oa0 + j;
+                C Bv[P], zo[HALF];
+                Bv[0] = O::from_h2(src[0]);
+                Bv[HALF] = O::mulc(O::from_h2(src[Q]), tw[HALF - 1]);
+#pragma unroll
+                for (int k1 = 1; k1 < HALF; ++k1) {
+                    Bv[k1] = O::mulc(O::from_h2(src[(2 * k1) * Q]), tw[k1 - 1]);
+                    Bv[P - k1] = cnj(O::mulc(O::from_h2(src[(2 * k1 + 1) * Q]), tw[k1 - 1]));
+                }
+                idft_half_out<P>(Bv, zo);
+#pragma unroll
+                for (int n1 = 0; n1 < HALF; ++n1) {
+                    if constexpr (G) zo[n1] = O::emul(zo[n1], vin[n1]);
+                    __builtin_nontemporal_store(O::to_io(zo[n1]), &yrow[n1 * Q + lofs + 32 * j]);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        } else {
             uint32_t vin[G ? HALF : 1][CPT];   // output gate (gated only)
             if constexpr (G) {
                 const uint32_t* vr = (const uint32_t*)prm.v + mrow * (M / 2);
@@ -305,7 +407,7 @@ hipError_t launch_claim_reset(uint32_t* ctr, hipStream_t s) {
 
 template <bool G, bool SK>
 static hipError_t launch_wide_g(int io, int P, const WideParams& p, int lds, hipStream_t s) {
-    const dim3 grid((unsigned)p.grid), blk((unsigned)(32 * P));
+    const dim3 grid((unsigned)p.grid), blk((unsigned)(P >= 16 ? 512 : 32 * P));
 #define FFTCONV_WIDE(IOT, PP)                                                              \
     do {                                                                                   \
         if (lds > 64 * 1024) {                                                             \
@@ -319,11 +421,15 @@ static hipError_t launch_wide_g(int io, int P, const WideParams& p, int lds, hip
     if (io == IO_BF16) {
         if (P == 4) FFTCONV_WIDE(IO_BF16, 4);
         else if (P == 8) FFTCONV_WIDE(IO_BF16, 8);
-        else FFTCONV_WIDE(IO_BF16, 16);
+        else if (P == 16) FFTCONV_WIDE(IO_BF16, 16);
+        else if (P == 32) FFTCONV_WIDE(IO_BF16, 32);
+        else return hipErrorInvalidValue;
     } else {
         if (P == 4) FFTCONV_WIDE(IO_F16, 4);
         else if (P == 8) FFTCONV_WIDE(IO_F16, 8);
-        else FFTCONV_WIDE(IO_F16, 16);
+        else if (P == 16) FFTCONV_WIDE(IO_F16, 16);
+        else if (P == 32) FFTCONV_WIDE(IO_F16, 32);
+        else return hipErrorInvalidValue;
     }
 #undef FFTCONV_WIDE
     return hipGetLastError();

@@ -77,7 +77,8 @@ typedef struct fftconv_plan_info {
                                      or 32*32, 16-bit I/O),
                                  2 = three-pass, LDS-staged (fp32 I/O),
                                  3 = one-workgroup-per-row kernel
-                                     (N = P*1024, P = 4, 8, 16, 16-bit I/O),
+                                     (N = P*1024, P = 4, 8, 16, 32, 16-bit
+                                     I/O),
                                  4 = column passes + slab-pair inner pass
                                      (N >= 32K, 16-bit I/O)                */
 } fftconv_plan_info;
@@ -124,9 +125,9 @@ fftconv_status fftconv_plan_estimate(size_t N, int p, fftconv_dtype dtype, int l
  *     (fftconv_plan_estimate); p >= 2 requests exactly p
  *     factors and returns FFTCONV_ERR_UNSUPPORTED when N cannot be split
  *     that way.  For the LDS-staged kernels the factors are 8, 16 or 32 (the
- *     last one 16 or 32); 16-bit plans at N = 4K..16K use P x 32 x 32
- *     (P = N/1024, p = 3) and at N >= 32K the outer levels followed by
- *     4 x 32 x 32, whose order is fixed by N.
+ *     last one 16 or 32); 16-bit plans at N = 4K..32K use P x 32 x 32
+ *     (P = N/1024, p = 3, fused) and at N >= 32K also the outer levels
+ *     followed by 4 x 32 x 32 (multi-pass), whose order is fixed by N.
  * Builds the DFT matrices and twiddle tables in fp64 on the host, rounds
  * them to the kernel's operand types and uploads them synchronously.
  * On success *out receives the plan; on failure *out is set to NULL. */
@@ -277,7 +278,7 @@ fftconv_status fftconv_forward_lowpass(fftconv_plan_t plan, const void *u,
  *  fftconv_forward.  Products are formed in fp32 (exact for 16-bit
  *  inputs); with 16-bit I/O the gated input enters the first transform
  *  stage as f16, and the output gate multiplies the fp32 result before the
- *  one rounding to the I/O type (f16 rows of N = 4K..16K multiply in
+ *  one rounding to the I/O type (f16 rows of N = 4K..32K multiply in
  *  packed f16, as that stage computes). */
 fftconv_status fftconv_forward_gated(fftconv_plan_t plan, const void *u,
                                      const void *w, const void *v,
@@ -313,7 +314,9 @@ size_t fftconv_backward_workspace_bytes(fftconv_plan_t plan, size_t B, size_t H)
  * accumulates conj(U) DY over the batch per channel in fp32 registers and
  * runs one inverse transform per channel: on the matrix-core engine of the
  * forward kernels for 16-bit I/O (the row kernel's at N = 1024, the wide
- * kernel's at 4K..16K, the multi-pass column and inner passes at N >= 32K,
+ * kernel's at 4K..16K, the multi-pass column and inner passes at N >= 32K
+ * -- at 32K the forward call is the fused wide kernel and dk still runs on
+ * the multi-pass engine --
  * batch chunks adding their share to dk), on the LDS-staged kernels for
  * fp32 plans.  B = 0 gives dk = 0.  The input
  * gradient of the other kinds is fftconv_forward with the matching adjoint

@@ -58,7 +58,7 @@ def test_gated_generic_kernel(N, dtype, monkeypatch):
 
 
 @pytest.mark.parametrize("N,dtype,B,H", [
-    (512, "f16", 33, 4), (1024, "bf16", 64, 3), (8192, "bf16", 5, 9),
+    (512, "f16", 33, 4), (1024, "bf16", 64, 3), (8192, "bf16", 5, 9), (32768, "bf16", 7, 5),
     (262144, "f16", 1, 3), (524288, "bf16", 1, 2), (1048576, "f16", 1, 2),
     (2097152, "bf16", 1, 1), (4194304, "bf16", 1, 1),
     (4194304, "f16", 1, 1)])

@@ -52,7 +52,8 @@ def _run(w, cutoff, with_rounding=False):
     (1024, "bf16", 2, 7, 31), (1024, "bf16", 3, 5, 256),
     (1024, "f16", 3, 5, 700), (8192, "bf16", 2, 3, 1000),
     (4096, "f16", 3, 2, 500), (16384, "bf16", 2, 3, 4095),
-    (8192, "f16", 2, 2, 2048), (65536, "f16", 1, 3, 20000),
+    (8192, "f16", 2, 2, 2048), (32768, "bf16", 2, 3, 8191), (32768, "f16", 3, 2, 5000),
+    (65536, "f16", 1, 3, 20000),
     (65536, "bf16", 2, 2, 16383), (262144, "f16", 1, 2, 3000),
     (1048576, "bf16", 1, 1, 200000), (4194304, "bf16", 1, 1, 500000),
     # the extremes: the DC bin alone, and no limit (cutoff = N)

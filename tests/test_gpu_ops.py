@@ -26,7 +26,7 @@ def _say(*a):
 @pytest.mark.parametrize("N,dtype,B,H", [
     (256, "f32", 1, 4), (256, "bf16", 3, 5), (1024, "bf16", 3, 5),
     (512, "f16", 2, 3), (2048, "f32", 2, 3), (8192, "f16", 3, 5),
-    (16384, "bf16", 2, 3), (65536, "bf16", 1, 3), (131072, "f32", 1, 2),
+    (16384, "bf16", 2, 3), (32768, "f16", 2, 3), (65536, "bf16", 1, 3), (131072, "f32", 1, 2),
     (1048576, "f16", 1, 2), (4194304, "bf16", 1, 1)])
 def test_operator_kinds(kind, N, dtype, B, H):
     # every kernel family: LDS-staged (256, 2048 fp32), row (512, 1024),

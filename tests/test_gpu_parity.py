@@ -84,7 +84,8 @@ def test_row_kernel_batch_shapes(B, H):
 @pytest.mark.parametrize("N,dtype,B,H", [
     (4096, "f16", 1, 1), (4096, "bf16", 7, 3), (8192, "f16", 1, 1),
     (8192, "f16", 5, 9), (8192, "bf16", 33, 2), (16384, "f16", 3, 1),
-    (16384, "bf16", 2, 7)])
+    (16384, "bf16", 2, 7), (32768, "f16", 1, 1), (32768, "bf16", 3, 5),
+    (32768, "f16", 17, 3), (32768, "bf16", 64, 9)])
 def test_wide_kernel_batch_shapes(N, dtype, B, H):
     # row counts that leave the persistent workgroups' slices ragged and
     # cross channel boundaries inside a slice
@@ -160,20 +161,20 @@ def test_error_paths():
     assert L.fftconv_forward(conv._plan, u.data_ptr(), None, y.data_ptr(),
                              2, 3, 1024, None, 0, s) == 1
     # multi-pass plan with a missing / short workspace
-    conv2, kf2 = _plan_and_spectrum(32768, "bf16", H=1)
-    u2 = torch.randn(1, 1, 32768, device="cuda").to(torch.bfloat16)
+    conv2, kf2 = _plan_and_spectrum(65536, "bf16", H=1)
+    u2 = torch.randn(1, 1, 65536, device="cuda").to(torch.bfloat16)
     y2 = torch.empty_like(u2)
     need = conv2.workspace_bytes(1, 1)
     # one f16 complex row (a single-channel chunk) and the claim counters
-    assert need == 32768 * 4 + 1024
+    assert need == 65536 * 4 + 1024
     ws = torch.empty(need, dtype=torch.uint8, device="cuda")
     assert L.fftconv_forward(conv2._plan, u2.data_ptr(), kf2.data_ptr(),
-                             y2.data_ptr(), 1, 1, 32768, None, 0, s) == 4
+                             y2.data_ptr(), 1, 1, 65536, None, 0, s) == 4
     assert L.fftconv_forward(conv2._plan, u2.data_ptr(), kf2.data_ptr(),
-                             y2.data_ptr(), 1, 1, 32768, ws.data_ptr(),
+                             y2.data_ptr(), 1, 1, 65536, ws.data_ptr(),
                              need - 16, s) == 4
     assert L.fftconv_forward(conv2._plan, u2.data_ptr(), kf2.data_ptr(),
-                             y2.data_ptr(), 1, 1, 32768, ws.data_ptr(),
+                             y2.data_ptr(), 1, 1, 65536, ws.data_ptr(),
                              need, s) == 0
     torch.cuda.synchronize()
     with pytest.raises(fc.FFTConvError):

@@ -43,8 +43,8 @@ def test_plan_query_every_length(lg, dtype):
     fac = info["factors"]
     for i, f in enumerate(fac):
         if info["kernel"] == "wide_kernel" and i == 0:
-            # vector-ALU outer stage of radix 4..16 before the 32 x 32 engine
-            assert f in (4, 8, 16)
+            # vector-ALU outer stage of radix 4..32 before the 32 x 32 engine
+            assert f in (4, 8, 16, 32)
         elif info["kernel"].startswith("mp_") and i == len(fac) - 3:
             # multi-pass: 4096-point inner slabs, 4 x 32 x 32
             assert f == 4
@@ -53,13 +53,18 @@ def test_plan_query_every_length(lg, dtype):
         prod *= f
     assert prod == N and info["M"] == N
     assert info["factors"][-1] in (16, 32)
-    assert info["path"] == ("fused" if N <= 16384 else "multipass")
+    # fused up to 16K, and at 32K for 16-bit I/O (the 32 x 32 x 32 wide
+    # kernel)
+    fused_max = 16384 if dtype == "f32" else 32768
+    assert info["path"] == ("fused" if N <= fused_max else "multipass")
     entry = 16 if dtype == "f32" else 8
     assert info["spectrum_bytes_per_channel"] == N * entry
     # workspace: f16 complex on the 16-bit multi-pass path, fp32 otherwise
-    ws = 0 if N <= 16384 else (8 * N if dtype == "f32" else 4 * N)
+    ws = 0 if N <= fused_max else (8 * N if dtype == "f32" else 4 * N)
     assert info["workspace_bytes_per_row"] == ws
-    if N > 16384 and dtype != "f32":
+    if N == 32768 and dtype != "f32":
+        assert fac == [32, 32, 32] and info["kernel"] == "wide_kernel"
+    if N > 32768 and dtype != "f32":
         # one outer level up to P_o = 32 (N = 128K), two above
         two = N > 131072
         assert info["outer_factors"] == (2 if two else 1)
@@ -150,7 +155,7 @@ def test_python_binding_marshals_only():
 MEASURED_BEST = {
     "16bit": {256: [16, 16], 512: [32, 16], 1024: [32, 32], 2048: [8, 16, 16],
               4096: [4, 32, 32], 8192: [8, 32, 32], 16384: [16, 32, 32],
-              32768: [8, 4, 32, 32], 65536: [16, 4, 32, 32], 131072: [32, 4, 32, 32],
+              32768: [32, 32, 32], 65536: [16, 4, 32, 32], 131072: [32, 4, 32, 32],
               262144: [8, 8, 4, 32, 32], 524288: [16, 8, 4, 32, 32],
               1048576: [16, 16, 4, 32, 32], 2097152: [32, 16, 4, 32, 32],
               4194304: [32, 32, 4, 32, 32]},
@@ -207,7 +212,7 @@ def test_cost_model_terms():
     assert z["hbm_bytes"] == pytest.approx(1024 * 2 * 2)
     # at the multi-pass lengths the kernels fix the order: a requested
     # order other than the plan's is refused
-    for N in (32768, 1 << 22):
+    for N in (65536, 1 << 22):
         p0 = fc.plan_query(N)["order"]
         for p in (2, 3, p0 + 1):
             if p == p0:

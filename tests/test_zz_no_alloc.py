@@ -34,6 +34,7 @@ def _inputs(N, dtype, B, H, wid):
     # LDS-staged fused kernel and the fp32 three-pass path
     (1024, "bf16", [(4, 96), (1, 5)]),
     (8192, "f16", [(3, 40), (2, 3)]),
+    (32768, "bf16", [(4, 24), (1, 3)]),
     (65536, "bf16", [(4, 96), (1, 3)]),
     (4194304, "bf16", [(1, 6), (1, 1)]),
     (2048, "f16", [(2, 9), (1, 2)]),
