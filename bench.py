@@ -86,8 +86,19 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU time of the oracle sample")
     ap.add_argument("--copy-calibration", action="store_true",
-                    help="run only a plain device copy of the workload's "
-                         "input size (reference for HBM byte counters)")
+                    help="run only the library's streaming copy of the "
+                         "workload's input size (reference for HBM byte "
+                         "counters)")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="time only the selected workload (no 'workloads' key)")
+    ap.add_argument("--profile", action="store_true",
+                    help="profile the selected workload and operator under "
+                         "rocprofv3 (kernel trace, HBM byte and instruction "
+                         "counters) and write its summary to profiles/")
+    ap.add_argument("--profile-dir", default=os.path.join(ROOT, "gpurun_out", "prof"),
+                    help="where rocprofv3 writes its raw output")
+    ap.add_argument("--profile-out", default=os.path.join(ROOT, "profiles"),
+                    help="where the summary and traffic.json are written")
     return ap.parse_args()
 
 
@@ -104,6 +115,10 @@ def main():
               "would shard by channel with no communication, each GPU "
               "running this path on its channels)" % args.gpus, file=sys.stderr)
         sys.exit(2)
+    if args.profile:
+        # drives rocprofv3 runs of this script as child processes; touches
+        # no GPU itself
+        return profile(args)
     import torch
     from fft_long_convolution_amd import inputs
     from fft_long_convolution_amd.fftconv import FFTConv
@@ -112,11 +127,15 @@ def main():
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
     if args.copy_calibration:
+        # the library's streaming copy (16-byte non-temporal loads and
+        # stores, the access pattern of the kernels) over the workload's
+        # input size: the reference of the HBM byte counters
+        from fft_long_convolution_amd.fftconv import stream_copy
         esz = 4 if w.dtype == "f32" else 2
         a = torch.ones(w.rows * w.N * esz // 4, dtype=torch.float32, device=dev)
         b = torch.empty_like(a)
         for _ in range(args.steps or 100):
-            b.copy_(a)
+            stream_copy(a, b)
         torch.cuda.synchronize()
         print(json.dumps({"copy_calibration_bytes_each_way": a.numel() * 4,
                           "copies": args.steps or 100}))
@@ -259,6 +278,11 @@ def main():
     roof["mfma_flops"] = float(flops)
     roof["mfma_frac"] = round(achieved_tf / MFMA_PEAK_TFLOPS[w.dtype], 4)
     roof["launch_ms"] = round(ms_kernel, 5)
+    # the practical roof: the library's streaming copy (read + write) on
+    # this GPU, measured in the same run
+    copy_gbs = stream_copy_rate(torch, dev)
+    roof["copy_gbs"] = round(copy_gbs, 1)
+    roof["frac_of_copy"] = round(achieved_gbs / copy_gbs, 4) if bound == "hbm" else None
 
     # ---- sampled correctness of the timed output against the oracle
     import oracle
@@ -376,7 +400,265 @@ def main():
                    "sampled_max_err_over_rms": sample_err,
                    "input_gen_s": round(gen_s, 2)},
     }
+    if op == "plain" and not args.no_extra:
+        # the other workloads, each timed the same way (one call per step,
+        # inputs resident, HIP events around back-to-back calls)
+        del us, gs, ys, ws, u0, g0, kf, k, dks
+        torch.cuda.empty_cache()
+        line["workloads"] = {n: time_workload(n, torch, dev)
+                             for n in inputs.WORKLOADS if n != w.name}
     print(json.dumps(line), flush=True)
+
+
+def stream_copy_rate(torch, dev, nbytes=1 << 30, reps=20) -> float:
+    """GB/s (bytes read + written) of fftconv_stream_copy over 1 GB."""
+    from fft_long_convolution_amd.fftconv import stream_copy
+    a = torch.ones(nbytes // 4, dtype=torch.float32, device=dev)
+    b = torch.empty_like(a)
+    for _ in range(5):
+        stream_copy(a, b)
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    st = torch.cuda.current_stream()
+    e0.record(st)
+    for _ in range(reps):
+        stream_copy(a, b)
+    e1.record(st)
+    torch.cuda.synchronize()
+    return 2.0 * nbytes * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9
+
+
+def time_workload(name: str, torch, dev) -> dict:
+    """One workload's forward call timed as the main line (>= 0.2 s warmup,
+    ~0.5 s timed); its roofline fraction against the spec HBM peak."""
+    from fft_long_convolution_amd import inputs
+    from fft_long_convolution_amd.fftconv import FFTConv
+    w = inputs.WORKLOADS[name]
+    conv = FFTConv(w.N, dtype=w.dtype)
+    u = to_torch(inputs.input_rows(w), w.dtype, torch).view(w.B, w.H, w.N).to(dev)
+    k = torch.from_numpy(inputs.kernel_rows(w)).to(dev)
+    kf = conv.kernel_spectrum(k)
+    y = torch.empty_like(u)
+    ws = torch.empty(max(conv.workspace_bytes(w.B, w.H), 16), dtype=torch.uint8, device=dev)
+    st = torch.cuda.current_stream()
+
+    def region(n):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(st)
+        for _ in range(n):
+            conv.forward(u, kf, out=y, workspace=ws)
+        e1.record(st)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n
+
+    est = max(region(3), 1e-3)
+    region(max(5, int(math.ceil(200.0 / est))))
+    steps = max(20, int(math.ceil(500.0 / est)))
+    ms = region(steps)
+    esz = 4 if w.dtype == "f32" else 2
+    alg = 2 * w.rows * w.N * esz + conv.spectrum_bytes(w.H)
+    gbs = alg / (ms * 1e-3) / 1e9
+    out = {"ms_per_step": round(ms, 5), "steps": steps,
+           "outputs_per_s": round(w.rows * w.N / (ms * 1e-3), 1),
+           "kernel": conv.info["kernel"], "factors": conv.info["factors"],
+           "algorithmic_bytes": int(alg), "achieved_gbs": round(gbs, 1),
+           "frac": round(gbs / HBM_PEAK_GBS, 4)}
+    del conv, u, k, kf, y, ws
+    torch.cuda.empty_cache()
+    return out
+
+
+# ---------------------------------------------------------------- profiling
+#
+# --profile runs this script under rocprofv3 as child processes (the
+# profiler's own program after "--", never through a shell): one kernel
+# trace at the default lengths, then one counter pass per group below on a
+# short run (1 warmup + 4 timed + 4 bracketed calls = 9 calls), and the same
+# HBM byte counters on the library's streaming copy of the workload's input
+# size, whose known bytes calibrate them.  It writes
+# profiles/<kernel>_<workload>[_<op>].md and the HBM traffic record of
+# profiles/traffic.json (tied to the sha1 of the library sources).
+
+PMC_PASSES = [
+    ["FETCH_SIZE"],
+    ["WRITE_SIZE"],
+    ["SQ_INSTS_VALU", "SQ_INSTS_MFMA", "SQ_INSTS_LDS", "SQ_INSTS_SALU", "SQ_WAVES",
+     "SQ_BUSY_CU_CYCLES", "SQ_WAVE_CYCLES", "SQ_WAIT_INST_ANY", "GRBM_GUI_ACTIVE"],
+    ["SQ_VALU_MFMA_BUSY_CYCLES", "SQ_ACTIVE_INST_VALU", "SQ_LDS_BANK_CONFLICT",
+     "SQ_LDS_IDX_ACTIVE", "SQ_ACTIVE_INST_LDS", "SQ_WAIT_ANY", "GRBM_GUI_ACTIVE"],
+]
+# kernels of the untimed set-up (kernel spectrum), not of a call
+SETUP_KERNELS = ("kpad_kernel", "stockham_kernel", "alphabeta_kernel", "coef_kernel",
+                 "band_limit_kernel")
+
+
+def _op_flags(args):
+    if args.gated:
+        return ["--gated"], "gated"
+    if args.circular:
+        return ["--circular"], "circular"
+    if args.backward:
+        return ["--backward"], "backward"
+    if args.lowpass is not None:
+        return ["--lowpass", str(args.lowpass)], "lowpass"
+    return [], "plain"
+
+
+def _is_call_kernel(name: str) -> bool:
+    return "fftconv::" in name and not any(k in name for k in SETUP_KERNELS) \
+        and "stream_copy" not in name
+
+
+def _run(cmd, log):
+    import subprocess
+    env = dict(os.environ, TMPDIR="/tmp")
+    print("profile: " + " ".join(cmd), flush=True)
+    r = subprocess.run(cmd, cwd="/tmp", env=env, capture_output=True, text=True, timeout=900)
+    with open(log, "w") as f:
+        f.write(r.stdout + "\n---- stderr ----\n" + r.stderr)
+    if r.returncode != 0:
+        raise RuntimeError("%s exited with %d (log %s)" % (cmd[0], r.returncode, log))
+    lines = [l for l in r.stdout.splitlines() if l.startswith("{")]
+    return json.loads(lines[-1]) if lines else None
+
+
+def _csv_rows(root: str, suffix: str):
+    import csv
+    import glob
+    rows = []
+    for path in glob.glob(os.path.join(root, "**", "*" + suffix), recursive=True):
+        with open(path, newline="") as f:
+            rows.extend(csv.DictReader(f))
+    return rows
+
+
+def _counters(root: str, pred) -> dict:
+    tot = {}
+    for r in _csv_rows(root, "counter_collection.csv"):
+        if not pred(r.get("Kernel_Name", "")):
+            continue
+        n = r["Counter_Name"]
+        tot[n] = tot.get(n, 0.0) + float(r["Counter_Value"])
+    return tot
+
+
+def profile(args):
+    from fft_long_convolution_amd import inputs
+    from fft_long_convolution_amd.fftconv import plan_query
+    w = inputs.WORKLOADS[args.workload]
+    flags, op = _op_flags(args)
+    tag = w.name + ("" if op == "plain" else "_" + op)
+    info = plan_query(w.N, 0, w.dtype)
+    out = os.path.join(os.path.abspath(args.profile_dir), tag)
+    os.makedirs(out, exist_ok=True)
+    me = [sys.executable, os.path.abspath(__file__), "--workload", w.name, "--no-extra"] + flags
+    short = ["--steps", "4", "--warmup", "1", "--no-cpu"]
+    calls_short = 1 + 4 + 4
+    # 1. kernel trace at the default lengths
+    tcmd = ["rocprofv3", "--kernel-trace", "--stats", "--output-format", "csv",
+            "-d", os.path.join(out, "trace"), "-o", "trace", "--"] + me + ["--no-cpu"]
+    tline = _run(tcmd, os.path.join(out, "trace.log"))
+    calls = 13 + tline["warmup"] + tline["steps"] + min(tline["steps"], 20)
+    stats = [r for r in _csv_rows(os.path.join(out, "trace"), "kernel_stats.csv")
+             if _is_call_kernel(r["Name"])]
+    trace_ns = sum(float(r["TotalDurationNs"]) for r in stats) / calls
+    # 2. counters on short runs, and on the calibration copy
+    pmc = {}
+    for i, group in enumerate(PMC_PASSES):
+        d = os.path.join(out, "pmc%d" % i)
+        _run(["rocprofv3", "--pmc"] + group + ["--output-format", "csv", "-d", d, "-o", "pmc", "--"]
+             + me + short, d + ".log")
+        for k, v in _counters(d, _is_call_kernel).items():
+            pmc[k] = v / calls_short
+    cal = {}
+    for c in ("FETCH_SIZE", "WRITE_SIZE"):
+        d = os.path.join(out, "copy_" + c)
+        _run(["rocprofv3", "--pmc", c, "--output-format", "csv", "-d", d, "-o", "pmc", "--",
+              sys.executable, os.path.abspath(__file__), "--workload", w.name,
+              "--steps", "4", "--copy-calibration"], d + ".log")
+        cal.update({k: v / 4 for k, v in _counters(d, lambda n: "stream_copy" in n).items()})
+    esz = 4 if w.dtype == "f32" else 2
+    copy_bytes = w.rows * w.N * esz
+    f_scale = copy_bytes / (cal["FETCH_SIZE"] * 1024.0)
+    w_scale = copy_bytes / (cal["WRITE_SIZE"] * 1024.0)
+    traffic = int(round(pmc["FETCH_SIZE"] * 1024.0 * f_scale + pmc["WRITE_SIZE"] * 1024.0 * w_scale))
+    alg = tline["roofline"]["algorithmic_bytes"]
+    rows = w.rows
+    # 3. summary
+    kern = info["kernel"].split("+")[0] if op != "backward" else info["kernel"].split("+")[0] + "_kgrad"
+    name = "%s_%s%s.md" % (kern, w.name, "" if op == "plain" else "_" + op)
+    # GRBM_GUI_ACTIVE is reported once per XCD (8 on MI355X): the call's
+    # busy cycles are the per-XCD value
+    gui = pmc.get("GRBM_GUI_ACTIVE", 0.0) / 8.0
+    simd = 4 * 256
+    lines = [
+        "# %s -- workload %s%s" % (kern, w.name, "" if op == "plain" else " (%s)" % op), "",
+        "Workload %s: B=%d, H=%d, N=%d, %s I/O, factors %s, %s path; kernels of a call: %s." % (
+            w.name, w.B, w.H, w.N, w.dtype, info["factors"], info["path"], info["kernel"]), "",
+        "Generated by `python3 bench.py --profile --workload %s%s` (rocprofv3 runs of bench.py "
+        "as child processes, from /tmp with TMPDIR=/tmp; `<repo>` is the repository root)." % (
+            w.name, (" " + " ".join(flags)) if flags else ""), "",
+        "## Kernel trace", "", "```",
+        " ".join(tcmd).replace(os.path.dirname(os.path.abspath(__file__)), "<repo>")
+        .replace(out, "<out>"), "```", "",
+        "| kernel | calls | average ns | min ns | max ns |", "|---|---|---|---|---|"]
+    for r in sorted(stats, key=lambda r: -float(r["TotalDurationNs"])):
+        lines.append("| `%s` | %s | %.0f | %s | %s |" % (r["Name"], r["Calls"], float(r["AverageNs"]),
+                                                      r["MinNs"], r["MaxNs"]))
+    lines += ["", "Kernel time per call in the trace: %.2f us over %d calls; the traced run's own "
+              "line reports ms_per_step %.5f (%.2f us per call, the gaps between launches "
+              "included)." % (trace_ns / 1e3, calls, tline["ms_per_step"], tline["ms_per_step"] * 1e3),
+              "", "## bench.py line of the traced run", "", "```", json.dumps(tline), "```", "",
+              "## Counters per call (rocprofv3 --pmc, one pass per group, %d calls per run)" % calls_short,
+              "", "```"]
+    for i, group in enumerate(PMC_PASSES):
+        lines.append("rocprofv3 --pmc %s -- python3 <repo>/bench.py --workload %s%s %s" % (
+            " ".join(group), w.name, (" " + " ".join(flags)) if flags else "", " ".join(short)))
+    lines += ["rocprofv3 --pmc FETCH_SIZE (and WRITE_SIZE) -- python3 <repo>/bench.py --workload %s "
+              "--steps 4 --copy-calibration" % w.name, "```", "",
+              "| counter | per call |", "|---|---|"]
+    for k in sorted(pmc):
+        lines.append("| %s | %.6g |" % (k, pmc[k]))
+    lines += ["",
+              "| HBM bytes | FETCH_SIZE KiB | WRITE_SIZE KiB |", "|---|---|---|",
+              "| streaming copy of %d B | %.1f | %.1f |" % (copy_bytes, cal["FETCH_SIZE"], cal["WRITE_SIZE"]),
+              "| scale factor (true bytes / counter) | %.4f | %.4f |" % (f_scale, w_scale),
+              "| one call | %.1f | %.1f |" % (pmc["FETCH_SIZE"], pmc["WRITE_SIZE"]), "",
+              "HBM traffic per call %d B vs algorithmic %d B: ratio %.3f." % (traffic, alg, traffic / alg), ""]
+    if gui > 0:
+        lines += ["Derived (GRBM_GUI_ACTIVE = %.0f cycles per call per XCD, %d SIMDs):" % (gui, simd), "",
+                  "* matrix cores busy: %.1f%% of SIMD cycles (SQ_VALU_MFMA_BUSY_CYCLES)" % (
+                      100.0 * pmc.get("SQ_VALU_MFMA_BUSY_CYCLES", 0) / (gui * simd)),
+                  "* vector instructions per row: %.1f wave-instructions (SQ_INSTS_VALU / rows)" % (
+                      pmc.get("SQ_INSTS_VALU", 0) / rows),
+                  "* matrix instructions per row: %.1f (SQ_INSTS_MFMA / rows)" % (
+                      pmc.get("SQ_INSTS_MFMA", 0) / rows),
+                  "* LDS instructions per row: %.1f; bank-conflict cycles / LDS-active cycles: %.3f" % (
+                      pmc.get("SQ_INSTS_LDS", 0) / rows,
+                      pmc.get("SQ_LDS_BANK_CONFLICT", 0) / max(pmc.get("SQ_LDS_IDX_ACTIVE", 1), 1)),
+                  "* waves waiting for an issue slot: %.1f%% of wave cycles (SQ_WAIT_INST_ANY / "
+                  "SQ_WAVE_CYCLES)" % (100.0 * pmc.get("SQ_WAIT_INST_ANY", 0) /
+                                       max(pmc.get("SQ_WAVE_CYCLES", 1), 1)), ""]
+    os.makedirs(args.profile_out, exist_ok=True)
+    with open(os.path.join(args.profile_out, name), "w") as f:
+        f.write("\n".join(lines) + "\n")
+    tfile = os.path.join(args.profile_out, "traffic.json")
+    rec = {}
+    for src in (tfile, TRAFFIC_FILE):
+        try:
+            with open(src) as f:
+                rec = json.load(f)
+            break
+        except (OSError, ValueError):
+            continue
+    rec[tag] = {"traffic_bytes": traffic, "algorithmic_bytes": alg,
+                "source_sha1": kernel_source_hash(), "summary": "profiles/" + name}
+    with open(tfile, "w") as f:
+        json.dump(rec, f, indent=1, sort_keys=True)
+    print(json.dumps({"profile": "profiles/" + name, "traffic_bytes": traffic,
+                      "algorithmic_bytes": alg, "trace_us_per_call": round(trace_ns / 1e3, 3)}),
+          flush=True)
 
 
 if __name__ == "__main__":

@@ -1373,7 +1373,21 @@ bool overlap(const void* a, size_t na, const void* b, size_t nb) {
 
 extern "C" {
 
-const char* fftconv_version(void) { return "fftconv-gfx950 0.1"; }
+const char* fftconv_version(void) { return "fftconv-gfx950 0.2"; }
+
+fftconv_status fftconv_stream_copy(const void* src, void* dst, size_t bytes, void* stream) {
+    if (!src || !dst || (bytes & 15)) return FFTCONV_ERR_INVALID_ARG;
+    if (!aligned16(src) || !aligned16(dst)) return FFTCONV_ERR_ALIGNMENT;
+    if (overlap(src, bytes, dst, bytes)) return FFTCONV_ERR_INVALID_ARG;
+    if (bytes == 0) return FFTCONV_OK;
+    int dev = 0, cu = 256;
+    if (hipGetDevice(&dev) != hipSuccess) return FFTCONV_ERR_HIP;
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) == hipSuccess && prop.multiProcessorCount > 0)
+        cu = prop.multiProcessorCount;
+    return launch_stream_copy(src, dst, (long long)(bytes / 16), cu, (hipStream_t)stream) == hipSuccess
+               ? FFTCONV_OK : FFTCONV_ERR_HIP;
+}
 
 const char* fftconv_status_string(fftconv_status st) {
     switch (st) {

@@ -118,6 +118,7 @@ hipError_t launch_kgrad_inner(int io, const KgradParams& p, int lds_bytes,
 hipError_t launch_outer_inv_f32out(int io, const FwdParams& p, int lds_bytes,
                                    hipStream_t s);
 hipError_t launch_scale_f32(float* x, long long n, float a, hipStream_t s);
+hipError_t launch_stream_copy(const void* src, void* dst, long long n16, int num_cu, hipStream_t s);
 
 // Kernel gradient on the row engine (N = 1024, 16-bit I/O,
 // fftconv_kgrad.hip): one wave per (channel, batch slice) accumulates the

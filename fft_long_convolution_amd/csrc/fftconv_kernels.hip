@@ -1274,6 +1274,35 @@ hipError_t launch_outer_inv_f32out(int io, const FwdParams& p, int lds, hipStrea
     return hipGetLastError();
 }
 
+// Streaming copy through 16-byte non-temporal loads and stores: each
+// workgroup moves contiguous chunks of 4 x 256 x 16 bytes, four loads in
+// flight per thread before the stores.  Its rate is the one a pure
+// read+write stream reaches on the part (the practical HBM roof), and its
+// byte counters are the reference for kernels that stream the same way.
+typedef unsigned int stream_v4 __attribute__((ext_vector_type(4)));
+__global__ void __launch_bounds__(256) stream_copy_kernel(const stream_v4* __restrict__ src,
+                                                          stream_v4* __restrict__ dst,
+                                                          long long n16) {
+    constexpr long long PER = 4 * 256;
+    for (long long base = (long long)blockIdx.x * PER; base < n16;
+         base += (long long)gridDim.x * PER) {
+        const long long i0 = base + threadIdx.x;
+        stream_v4 r[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+            if (i0 + k * 256 < n16) r[k] = __builtin_nontemporal_load(&src[i0 + k * 256]);
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+            if (i0 + k * 256 < n16) __builtin_nontemporal_store(r[k], &dst[i0 + k * 256]);
+    }
+}
+
+hipError_t launch_stream_copy(const void* src, void* dst, long long n16, int num_cu, hipStream_t s) {
+    hipLaunchKernelGGL(stream_copy_kernel, dim3((unsigned)(32 * num_cu)), dim3(256), 0, s,
+                       (const stream_v4*)src, (stream_v4*)dst, n16);
+    return hipGetLastError();
+}
+
 hipError_t launch_scale_f32(float* x, long long n, float a, hipStream_t s) {
     if (n <= 0) return hipSuccess;
     hipLaunchKernelGGL(scale_f32_kernel, dim3(1024), dim3(256), 0, s, x, n, a);

@@ -108,6 +108,8 @@ def lib() -> ctypes.CDLL:
         L.fftconv_backward.argtypes = [vp, vp, vp, vp, vp, vp, sz, sz, sz,
                                        vp, sz, vp]
         L.fftconv_backward.restype = i
+        L.fftconv_stream_copy.argtypes = [vp, vp, sz, vp]
+        L.fftconv_stream_copy.restype = i
         L.fftconv_status_string.argtypes = [i]
         L.fftconv_status_string.restype = ctypes.c_char_p
         L.fftconv_version.argtypes = []
@@ -150,6 +152,19 @@ def plan_estimate(N: int, p: int = 0, dtype: str = "bf16", lds_staged: bool = Fa
     if st != 0:
         raise FFTConvError(st, "fftconv_plan_estimate(N=%d, p=%d)" % (N, p))
     return e.as_dict()
+
+
+def stream_copy(src, dst, stream=None):
+    """fftconv_stream_copy of a contiguous CUDA tensor into another of the
+    same byte size (non-temporal 16-byte loads and stores)."""
+    nbytes = src.numel() * src.element_size()
+    if dst.numel() * dst.element_size() != nbytes:
+        raise ValueError("src and dst must have the same size in bytes")
+    st = lib().fftconv_stream_copy(src.data_ptr(), dst.data_ptr(), nbytes,
+                                   _stream_handle(stream))
+    if st != 0:
+        raise FFTConvError(st, "fftconv_stream_copy")
+    return dst
 
 
 def _torch_dtype(dtype: str):

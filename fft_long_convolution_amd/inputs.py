@@ -55,6 +55,10 @@ WORKLOADS = {
         Workload("m2bert_f16_n8k", 3, 16, 768, 8192, "f16", "normal",
                  "decay",
                  "M2-BERT/Hyena long context: u ~ N(0,1) in fp16"),
+        Workload("longconv_bf16_n32k", 6, 4, 512, 32768, "bf16", "normal",
+                 "decay",
+                 "32K-sample long convolution, the longest length the page "
+                 "runs fully fused: u ~ N(0,1) in bf16"),
         Workload("audio_bf16_n64k", 4, 4, 256, 65536, "bf16", "sines",
                  "decay",
                  "raw-audio shaped: 8 random tones at 64 kHz + 0.1 N(0,1)"),

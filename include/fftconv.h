@@ -333,6 +333,16 @@ const char *fftconv_status_string(fftconv_status status);
 /* Version string of the library build. */
 const char *fftconv_version(void);
 
+/* Measurement aid, not part of the convolution: copies `bytes` (a multiple
+ * of 16; src and dst device pointers, 16-B aligned, not overlapping) with
+ * 16-byte non-temporal loads and stores on the current device, the access
+ * pattern the convolution kernels stream their rows with.  Its rate is the
+ * practical HBM roof of the part, and its byte counters calibrate the
+ * kernels' (bench.py --copy-calibration).  Asynchronous on `stream`.
+ * Errors: null or misaligned pointers, a size not a multiple of 16, or
+ * overlap -> FFTCONV_ERR_INVALID_ARG / FFTCONV_ERR_ALIGNMENT. */
+fftconv_status fftconv_stream_copy(const void *src, void *dst, size_t bytes, void *stream);
+
 #ifdef __cplusplus
 }
 #endif
