@@ -24,6 +24,9 @@ Cores", section 3.4):
   the circular kinds);
 * ``lowpass_fft`` -- the frequency-sparse (band-limited) convolution: the
   2N-point kernel spectrum zeroed beyond a cutoff frequency F;
+* ``masked_fft`` / ``blocksparse_mask`` / ``blocksparse_fft`` -- the
+  frequency-sparse convolution whose zero blocks follow the transform's
+  digits (a bins of the top digit, d outer classes);
 * ``gated_direct`` / ``gated_fft`` / ``gated_points`` -- the gated
   convolution ``y = v * ((u * w) conv k)`` (elementwise gates on the input
   and on the output; same page, section 3 "Technical Approach",
@@ -94,6 +97,8 @@ def _load():
         lib.oracle_kgrad_points.restype = None
         lib.oracle_lowpass_fft.argtypes = [d, d, lp, d, L, L, L, L]
         lib.oracle_lowpass_fft.restype = ctypes.c_int
+        lib.oracle_masked_fft.argtypes = [d, d, lp, d, L, L, L, d]
+        lib.oracle_masked_fft.restype = ctypes.c_int
         _lib = lib
     return _lib
 
@@ -293,6 +298,66 @@ def lowpass_fft(u, k, F: int, hidx=None) -> np.ndarray:
                                   k.shape[0], N, int(F)) != 0:
         raise MemoryError("oracle_lowpass_fft: allocation failed")
     return y
+
+
+def masked_fft(u, k, mask, hidx=None) -> np.ndarray:
+    """Causal convolution with a masked kernel spectrum:
+    IFFT_2N(U . K . mask)[0:N], mask[f] in {0, 1} for f in [0, 2N)."""
+    u, k, hidx, R, N = _rows(u, k, hidx)
+    mask = np.ascontiguousarray(mask, dtype=np.float64)
+    if mask.shape != (2 * N,):
+        raise ValueError("mask needs 2N entries")
+    if N & (N - 1):
+        raise ValueError("masked_fft needs a power-of-two N")
+    y = np.empty((R, N), dtype=np.float64)
+    if _load().oracle_masked_fft(_dp(u), _dp(k), _lp(hidx), _dp(y), R,
+                                 k.shape[0], N, _dp(mask)) != 0:
+        raise MemoryError("oracle_masked_fft: allocation failed")
+    return y
+
+
+def blocksparse_mask(N: int, P: int, a: int, d: int) -> np.ndarray:
+    """Kept (1) and zeroed (0) frequencies f in [0, 2N) of the frequency-
+    sparse convolution whose zero blocks follow the digits of the transform
+    (FlashFFTConv page, section 3.4, "Frequency-sparse convolutions": the
+    kernel spectrum reshaped along the decomposition's factors, a whole
+    number of rows zeroed along each one).  Reading taken here:
+
+    * the 2N-point spectrum is used through N packed bins; frequencies f and
+      f + N share the bin k = f mod N (the real-input packing), so the mask
+      is a mask of bins;
+    * a bin is written k = k_out + P k_in, k_out < P the outer digit of a
+      P x (N / P) decomposition, and its top digit of 32 is
+      k_b = floor(32 k_in P / N);
+    * a: the a middle values of k_b are zeroed (16 - a/2 <= k_b < 16 + a/2;
+      a even) -- the highest frequencies of every outer class;
+    * d: the d outer classes nearest P/2 are zeroed (0 < |k_out - P/2| <=
+      d // 2, and k_out = P/2 itself when d is odd);
+    * a bin is also zeroed when its mirror bin -k mod N is, which keeps the
+      spectrum Hermitian (the output real).
+    """
+    if N < 2 or N & (N - 1) or P < 1 or N % P:
+        raise ValueError("bad N or P")
+    if a < 0 or a > 32 or a % 2 or d < 0 or d >= max(P, 1) or (P == 1 and d):
+        raise ValueError("bad a or d")
+    k = np.arange(N)
+    k_out = k % P
+    k_in = k // P
+    k_b = (k_in * 32 * P) // N
+    zero_b = (k_b >= 16 - a // 2) & (k_b < 16 + a // 2)
+    dist = np.abs(k_out - P / 2.0)
+    zero_out = (dist > 0) & (dist <= d // 2)
+    if d % 2:
+        zero_out |= (k_out * 2 == P)
+    z = zero_b | zero_out
+    z = z | z[(-k) % N]
+    return np.concatenate([~z, ~z]).astype(np.float64)
+
+
+def blocksparse_fft(u, k, P: int, a: int, d: int, hidx=None) -> np.ndarray:
+    """The frequency-sparse causal convolution of blocksparse_mask."""
+    N = np.asarray(u).shape[-1]
+    return masked_fft(u, k, blocksparse_mask(N, P, a, d), hidx)
 
 
 def _gates(u, w, v):

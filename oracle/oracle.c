@@ -518,3 +518,59 @@ int oracle_lowpass_fft(const double *u, const double *kern, const long *hidx,
     free(kim);
     return fail ? -1 : 0;
 }
+
+/* Causal convolution with a masked kernel spectrum: y = IFFT_2N(U . K m)[0:N]
+ * with m[f] in {0, 1} given for every f in [0, 2N) (mask[f] != 0 keeps the
+ * frequency).  The frequency-sparse convolutions are such masks. */
+int oracle_masked_fft(const double *u, const double *kern, const long *hidx,
+                      double *y, long R, long Hk, long N, const double *mask)
+{
+    const long L = 2 * N;
+    double *kre = (double *)malloc(sizeof(double) * (size_t)(Hk * L));
+    double *kim = (double *)malloc(sizeof(double) * (size_t)(Hk * L));
+    if (!kre || !kim) {
+        free(kre);
+        free(kim);
+        return -1;
+    }
+    oracle_kernel_spectrum(kern, Hk, N, kre, kim);
+    for (long h = 0; h < Hk; ++h)
+        for (long f = 0; f < L; ++f) {
+            kre[h * L + f] *= mask[f];
+            kim[h * L + f] *= mask[f];
+        }
+    int fail = 0;
+#pragma omp parallel
+    {
+        double *re = (double *)malloc(sizeof(double) * (size_t)L);
+        double *im = (double *)malloc(sizeof(double) * (size_t)L);
+        if (!re || !im) {
+#pragma omp atomic write
+            fail = 1;
+        } else {
+            long r;
+#pragma omp for schedule(dynamic, 1)
+            for (r = 0; r < R; ++r) {
+                const double *Kr = kre + hidx[r] * L, *Ki = kim + hidx[r] * L;
+                for (long t = 0; t < L; ++t) {
+                    re[t] = t < N ? u[r * N + t] : 0.0;
+                    im[t] = 0.0;
+                }
+                fft_radix2(re, im, L, -1);
+                for (long f = 0; f < L; ++f) {
+                    double a = re[f], b = im[f];
+                    re[f] = a * Kr[f] - b * Ki[f];
+                    im[f] = a * Ki[f] + b * Kr[f];
+                }
+                fft_radix2(re, im, L, +1);
+                for (long t = 0; t < N; ++t)
+                    y[r * N + t] = re[t] / (double)L;
+            }
+        }
+        free(re);
+        free(im);
+    }
+    free(kre);
+    free(kim);
+    return fail ? -1 : 0;
+}

@@ -570,3 +570,78 @@ def test_lowpass_special_cases():
     mask = np.minimum(f, L - f) <= 9
     want = np.fft.ifft(np.fft.fft(u, n=L) * np.fft.fft(k, n=L) * mask).real[:, :N]
     np.testing.assert_allclose(oracle.lowpass_fft(u, k, 9), want, atol=1e-12)
+
+
+# ---- frequency-sparse convolution with zero blocks along the digits
+
+def _blocksparse_cases():
+    out = []
+    for line in open(golden_path("blocksparse_mask_hand.txt")):
+        line = line.strip()
+        if not line or line.startswith("#"):
+            continue
+        head, _, kept = line.partition(":")
+        N, P, a, d = (int(x) for x in head.split())
+        out.append((N, P, a, d, [int(x) for x in kept.split()]))
+    return out
+
+
+def test_blocksparse_mask_hand_worked():
+    cases = _blocksparse_cases()
+    assert len(cases) == 5
+    for N, P, a, d, kept in cases:
+        m = oracle.blocksparse_mask(N, P, a, d)
+        assert m.shape == (2 * N,)
+        assert sorted(np.flatnonzero(m).tolist()) == kept, (N, P, a, d)
+
+
+@pytest.mark.parametrize("N,P", [(1024, 1), (8192, 8), (32768, 32), (65536, 16)])
+def test_blocksparse_mask_structure(N, P):
+    # Hermitian (f and 2N - f kept together), bins f and f + N together,
+    # and the zeroed fraction of the digit sets plus only the mirror closure
+    for a in (0, 8, 16, 24):
+        for d in ((0, 1, 2, P // 2, P - 2) if P > 2 else (0,)):
+            m = oracle.blocksparse_mask(N, P, a, d)
+            f = np.arange(2 * N)
+            assert np.array_equal(m, m[(2 * N - f) % (2 * N)])
+            assert np.array_equal(m[:N], m[N:])
+            kept = m[:N].mean()
+            want = (32 - a) / 32.0 * (P - d) / P
+            # the mirror closure only adds zeros in outer class 0 (at most
+            # the bins of its k_a = 0 column: N / (32 P) of N)
+            assert want - 1.0 / (32 * P) - 1e-12 <= kept <= want + 1e-12
+
+
+def test_blocksparse_special_cases():
+    rng = np.random.default_rng(3)
+    N, P = 512, 4
+    u = rng.standard_normal((3, N))
+    k = rng.standard_normal((2, N)) * np.exp(-0.01 * np.arange(N))
+    hidx = np.array([0, 1, 1])
+    # no zero blocks: the causal convolution
+    np.testing.assert_allclose(oracle.blocksparse_fft(u, k, P, 0, 0, hidx),
+                               oracle.conv_direct(u, k, hidx), rtol=0, atol=1e-10)
+    # every bin zero: no output
+    assert np.max(np.abs(oracle.blocksparse_fft(u, k, P, 32, 0, hidx))) < 1e-12
+    # the masked route with the band-limit mask is the band-limited route
+    F = 100
+    f = np.arange(2 * N)
+    band = (np.minimum(f, 2 * N - f) <= F).astype(np.float64)
+    np.testing.assert_allclose(oracle.masked_fft(u, k, band, hidx),
+                               oracle.lowpass_fft(u, k, F, hidx), rtol=0, atol=1e-10)
+    # numpy's FFT with the same mask (an independent transform)
+    for a, d in ((16, 0), (8, 1), (0, 2), (24, 3)):
+        m = oracle.blocksparse_mask(N, P, a, d)
+        U = np.fft.fft(u, 2 * N)
+        K = np.fft.fft(k, 2 * N)
+        want = np.fft.ifft(U * K[hidx] * m)[:, :N]
+        assert np.max(np.abs(want.imag)) < 1e-9     # the mask keeps it real
+        np.testing.assert_allclose(oracle.blocksparse_fft(u, k, P, a, d, hidx),
+                                   want.real, rtol=0, atol=1e-9)
+
+
+def test_blocksparse_mask_rejects_bad_counts():
+    for args in ((1024, 1, 0, 1), (1024, 4, 3, 0), (1024, 4, 34, 0), (1000, 4, 0, 0),
+                 (1024, 4, 0, 4)):
+        with pytest.raises(ValueError):
+            oracle.blocksparse_mask(*args)
