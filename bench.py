@@ -81,6 +81,10 @@ def parse():
     ap.add_argument("--lowpass", type=int, default=None, metavar="F",
                     help="time the frequency-sparse convolution whose kernel "
                          "spectrum keeps frequencies within F of zero")
+    ap.add_argument("--blocksparse", default=None, metavar="A,D",
+                    help="time the frequency-sparse convolution with zero "
+                         "blocks along the transform's digits (a middle values "
+                         "of the top digit, d outer classes)")
     ap.add_argument("--no-cpu", action="store_true",
                     help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
@@ -140,13 +144,17 @@ def main():
         print(json.dumps({"copy_calibration_bytes_each_way": a.numel() * 4,
                           "copies": args.steps or 100}))
         return
-    if args.gated + args.circular + args.backward + (args.lowpass is not None) > 1:
+    if (args.gated + args.circular + args.backward + (args.lowpass is not None)
+            + (args.blocksparse is not None)) > 1:
         print("bench.py: choose one of --gated, --circular, --backward, "
-              "--lowpass", file=sys.stderr)
+              "--lowpass, --blocksparse", file=sys.stderr)
         sys.exit(2)
     op = ("gated" if args.gated else "circular" if args.circular
           else "backward" if args.backward
-          else "lowpass" if args.lowpass is not None else "plain")
+          else "lowpass" if args.lowpass is not None
+          else "blocksparse" if args.blocksparse is not None else "plain")
+    bs_a, bs_d = ((int(x) for x in args.blocksparse.split(","))
+                  if args.blocksparse is not None else (0, 0))
     conv = FFTConv(w.N, dtype=w.dtype)
     info = conv.info
 
@@ -167,6 +175,8 @@ def main():
     kind = {"circular": "circular", "backward": "causal_adjoint"}.get(op, "causal")
     if op == "lowpass":
         kf = conv.kernel_spectrum_lowpass(k, args.lowpass)
+    elif op == "blocksparse":
+        kf = conv.kernel_spectrum_blocksparse(k, bs_a, bs_d)
     else:
         kf = conv.kernel_spectrum(k, kind=kind)
     esz = 4 if w.dtype == "f32" else 2
@@ -195,6 +205,8 @@ def main():
                           out_dk=dks[j])
         elif op == "lowpass":
             conv.forward_lowpass(us[j], kf, args.lowpass, out=ys[j], workspace=ws)
+        elif op == "blocksparse":
+            conv.forward_blocksparse(us[j], kf, bs_a, bs_d, out=ys[j], workspace=ws)
         else:
             conv.forward(us[j], kf, out=ys[j], workspace=ws)
 
@@ -311,6 +323,10 @@ def main():
         uh, inv = np.unique(rows % w.H, return_inverse=True)
         full = oracle.lowpass_fft(sel_u, sel_k[uh], args.lowpass, inv)
         want = full[np.arange(48), ts]
+    elif op == "blocksparse":
+        uh, inv = np.unique(rows % w.H, return_inverse=True)
+        full = oracle.blocksparse_fft(sel_u, sel_k[uh], info["sparse_outer"], bs_a, bs_d, inv)
+        want = full[np.arange(48), ts]
     else:
         want = oracle.conv_points(sel_u, sel_k, np.arange(48), ts, rows % w.H)
     scale = float(np.sqrt(np.mean(want ** 2))) or 1.0
@@ -356,6 +372,8 @@ def main():
                     oracle.kgrad_fft(usel, gsel[0], len(uh), "causal", inv)
                 elif op == "lowpass":
                     oracle.lowpass_fft(usel, ksel, args.lowpass, inv)
+                elif op == "blocksparse":
+                    oracle.blocksparse_fft(usel, ksel, info["sparse_outer"], bs_a, bs_d, inv)
                 else:
                     oracle.conv_fft(usel, ksel, inv)
             return time.perf_counter() - t0
@@ -372,7 +390,8 @@ def main():
         what = {"gated": " with both gates", "circular": " (circular kind)",
                 "backward": " (du by the adjoint and dk by the gradient "
                             "routes)",
-                "lowpass": " (band-limited spectrum)"}.get(op, "")
+                "lowpass": " (band-limited spectrum)",
+                "blocksparse": " (digit-block sparse spectrum)"}.get(op, "")
         cpu = {"value": round(passes * n * w.N / tc, 1), "unit": "outputs/s",
                "cores": cores, "kind": "oracle",
                "sample": "%s%d of %d rows (B*H) at N=%d through the fp64 "
@@ -388,6 +407,11 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name + ("" if op == "plain" else " " + op),
                    "op": op, "cutoff": args.lowpass,
+                   "blocksparse": ({"a": bs_a, "d": bs_d, "P": info["sparse_outer"],
+                                    "sparsity": round(1.0 - float(
+                                        __import__("oracle").blocksparse_mask(
+                                            w.N, info["sparse_outer"], bs_a, bs_d).mean()), 4)}
+                                   if op == "blocksparse" else None),
                    "B": w.B, "H": w.H, "N": w.N,
                    "io_dtype": w.dtype, "factors": info["factors"],
                    "path": info["path"], "global_batch": w.B,
@@ -502,6 +526,8 @@ def _op_flags(args):
         return ["--backward"], "backward"
     if args.lowpass is not None:
         return ["--lowpass", str(args.lowpass)], "lowpass"
+    if args.blocksparse is not None:
+        return ["--blocksparse", args.blocksparse], "blocksparse"
     return [], "plain"
 
 

@@ -368,6 +368,15 @@ fftconv_status make_shape(size_t N, int p, fftconv_dtype dtype, Shape& s,
     return found ? FFTCONV_OK : first;
 }
 
+// The outer factor P of the digit-block sparsity pattern: the outer stage
+// before the 1024- or 4096-point inner transform (wide and multi-pass
+// kernels); 1 where the kernels have no such outer stage.
+int sparse_outer(const Shape& s) {
+    if (s.wide_P) return s.wide_P;
+    if (s.mp_P1) return (int)(s.M / 4096);
+    return 1;
+}
+
 void fill_info(const Shape& s, fftconv_plan_info* info) {
     memset(info, 0, sizeof(*info));
     info->N = s.N;
@@ -381,6 +390,7 @@ void fill_info(const Shape& s, fftconv_plan_info* info) {
     info->workspace_bytes_per_row = s.path ? s.M * (s.mp_P1 ? 4 : 8) : 0;
     info->mfma_flops_per_row = mfma_flops_per_row(s);
     info->kernel_variant = s.mp_P1 ? 4 : s.path ? 2 : (s.wide_P ? 3 : (row_kernel_applies(s) ? 1 : 0));
+    info->sparse_outer = sparse_outer(s);
 }
 
 // ------------------------------------------------------- table construction
@@ -866,14 +876,14 @@ void free_plan(fftconv_plan_s* pl) {
 fftconv_status build_mp_tables(fftconv_plan_s* pl);
 fftconv_status spectrum_impl(fftconv_plan_t plan, const float* k, size_t H,
                              fftconv_kernel_kind kind, long long cutoff, void* k_f,
-                             void* stream);
+                             void* stream, int blk_a = 0, int blk_d = 0);
 constexpr size_t kMpChunkBytes = (size_t)1024 << 20;
 
 fftconv_status forward_impl(fftconv_plan_t plan, const void* u, const void* w,
                             const void* v, const void* k_f, void* y, size_t B,
                             size_t H, size_t N, void* workspace,
                             size_t workspace_bytes, void* stream, int skip_hi,
-                            size_t chunk_cap);
+                            size_t chunk_cap, int outer_keep = 0);
 fftconv_status backward_dk(const fftconv_plan_s* plan, const void* u, const void* dy,
                            float* dk, size_t B, size_t H, size_t N, void* workspace,
                            hipStream_t st);
@@ -1055,6 +1065,7 @@ fftconv_status build_device_tables(fftconv_plan_s* pl) {
         if (upload(pl, two.data(), two.size() * 2, &d) != hipSuccess) return FFTCONV_ERR_HIP;
         W.two = (const uint32_t*)d;
         W.N = (int)s.N;
+        W.pairs = P / 2;
         // stage tables (16 KB) + outer twiddles (read through L2 at P = 32)
         // + one row of f16 points + the k_b exchange
         pl->lds_wide = 16 * 1024 + (P <= 16 ? (P / 2) * 4096 : 0) + (int)s.M * 4 +
@@ -1095,6 +1106,7 @@ fftconv_status build_mp_tables(fftconv_plan_s* pl) {
     I.two = (const uint32_t*)d;
     I.M = (int)s.M;
     I.Po = (int)(s.M / 4096);
+    I.upr_active = I.Po / 2;
     I.P1 = s.mp_P1;
     I.P2 = s.mp_P2;
     std::vector<float> t1 = col_twiddles((long long)s.M, (long long)s.M / s.mp_P1);
@@ -1535,7 +1547,7 @@ namespace {
 // `cutoff` of zero when cutoff >= 0.
 fftconv_status spectrum_impl(fftconv_plan_t plan, const float* k, size_t H,
                              fftconv_kernel_kind kind, long long cutoff, void* k_f,
-                             void* stream) {
+                             void* stream, int blk_a, int blk_d) {
     if (!plan) return FFTCONV_ERR_INVALID_ARG;
     if ((int)kind < 0 || (int)kind > 3) return FFTCONV_ERR_INVALID_ARG;
     if (H == 0) return FFTCONV_OK;
@@ -1572,6 +1584,8 @@ fftconv_status spectrum_impl(fftconv_plan_t plan, const float* k, size_t H,
             b = t;
         }
         if (e == hipSuccess && cutoff >= 0) e = launch_band_limit(a, cnt, (int)L, (int)cutoff, st);
+        if (e == hipSuccess && (blk_a > 0 || blk_d > 0))
+            e = launch_block_mask(a, cnt, (int)L, (int)s.M, sparse_outer(s), blk_a, blk_d, st);
         if (e != hipSuccess) break;
         if (s.mp_P1) {
             MpCoefParams mp{};
@@ -1620,7 +1634,7 @@ fftconv_status forward_impl(fftconv_plan_t plan, const void* u, const void* w,
                             const void* v, const void* k_f, void* y, size_t B,
                             size_t H, size_t N, void* workspace,
                             size_t workspace_bytes, void* stream, int skip_hi,
-                            size_t chunk_cap) {
+                            size_t chunk_cap, int outer_keep) {
     if (!plan) return FFTCONV_ERR_INVALID_ARG;
     const Shape& s = plan->s;
     if (N != s.N) return FFTCONV_ERR_INVALID_ARG;
@@ -1695,6 +1709,7 @@ fftconv_status forward_impl(fftconv_plan_t plan, const void* u, const void* w,
         C2.tw = plan->mp_tw2;
         MpInnerParams I = plan->mp;
         I.skip_hi = skip_hi;
+        I.upr_active = outer_keep > 0 && outer_keep < I.Po / 2 ? outer_keep : I.Po / 2;
         I.B = (int)B;
         I.H = (int)H;
         I.ws = workspace;
@@ -1718,7 +1733,7 @@ fftconv_status forward_impl(fftconv_plan_t plan, const void* u, const void* w,
             C1.h0 = C2.h0 = I.h0 = (int)h0;
             C1.hc = C2.hc = I.hc = (int)hc;
             C1.rows = C2.rows = (long long)bcur * (long long)hc;
-            const long long units = C1.rows * (I.Po / 2);
+            const long long units = C1.rows * I.upr_active;
             long long G = 2LL * plan->num_cu;
             G = G < 8 ? 8 : G & ~7LL;
             const long long need = (units + 7) & ~7LL;
@@ -1756,6 +1771,9 @@ fftconv_status forward_impl(fftconv_plan_t plan, const void* u, const void* w,
                     e = launch_mp_col2(io, s.mp_P1, s.mp_P2, false, D, st);
                 }
                 if (e == hipSuccess) e = launch_mp_inner(io, I, plan->lds_mp, st);
+                if (e == hipSuccess)
+                    e = launch_mp_zero_units(workspace, C1.rows, (int)s.M, I.Po, I.P1, I.P2,
+                                             I.upr_active, st);
                 if (e == hipSuccess) {
                     if (plan->mp2m_ia1) {
                         MpCol2Params F = D;
@@ -1771,6 +1789,9 @@ fftconv_status forward_impl(fftconv_plan_t plan, const void* u, const void* w,
             } else {
                 e = launch_mp_col(io, s.mp_P1, 0, C1, st);
                 if (e == hipSuccess) e = launch_mp_inner(io, I, plan->lds_mp, st);
+                if (e == hipSuccess)
+                    e = launch_mp_zero_units(workspace, C1.rows, (int)s.M, I.Po, I.P1, I.P2,
+                                             I.upr_active, st);
                 if (e == hipSuccess) e = launch_mp_col(io, s.mp_P1, 3, C1, st);
             }
         }
@@ -1791,6 +1812,7 @@ fftconv_status forward_impl(fftconv_plan_t plan, const void* u, const void* w,
         W.w = w;
         W.v = v;
         W.skip_hi = skip_hi;
+        W.pairs = outer_keep > 0 && outer_keep < s.wide_P / 2 ? outer_keep : s.wide_P / 2;
         W.ctr = (uint32_t*)workspace;
         e = launch_claim_reset(W.ctr, st);
         if (e == hipSuccess) e = launch_wide(io, s.wide_P, W, plan->lds_wide, st);
@@ -1869,6 +1891,38 @@ fftconv_status fftconv_forward_lowpass(fftconv_plan_t plan, const void* u,
     const int skip = (engine && cutoff < plan->s.M / 4) ? 1 : 0;
     return forward_impl(plan, u, nullptr, nullptr, k_f, y, B, H, N, workspace,
                         workspace_bytes, stream, skip, kMpChunkBytes);
+}
+
+// a and d of the digit-block pattern: a even in [0, 32]; d in [0, P) with P
+// the plan's outer factor (d = 0 when P = 1)
+bool blocksparse_args_ok(const fftconv_plan_s* plan, int a, int d) {
+    const int P = sparse_outer(plan->s);
+    return a >= 0 && a <= 32 && (a % 2) == 0 && d >= 0 && d < P;
+}
+
+fftconv_status fftconv_kernel_spectrum_blocksparse(fftconv_plan_t plan, const float* k,
+                                                   size_t H, int a, int d, void* k_f,
+                                                   void* stream) {
+    if (!plan) return FFTCONV_ERR_INVALID_ARG;
+    if (!blocksparse_args_ok(plan, a, d)) return FFTCONV_ERR_INVALID_ARG;
+    return spectrum_impl(plan, k, H, FFTCONV_CAUSAL, -1, k_f, stream, a, d);
+}
+
+fftconv_status fftconv_forward_blocksparse(fftconv_plan_t plan, const void* u,
+                                           const void* k_f, int a, int d, void* y,
+                                           size_t B, size_t H, size_t N, void* workspace,
+                                           size_t workspace_bytes, void* stream) {
+    if (!plan) return FFTCONV_ERR_INVALID_ARG;
+    if (!blocksparse_args_ok(plan, a, d)) return FFTCONV_ERR_INVALID_ARG;
+    // the 32 x 32 engine skips the tiles of k_b = 8..23 (a >= 16 zeroes
+    // them all); the wide and multi-pass kernels skip the mirror pairs of
+    // outer classes j >= P/2 - d/2, whose bins are all zero
+    const bool engine = (plan->use_row && plan->row_nb == 32) || plan->s.wide_P || plan->s.mp_P1;
+    const int skip = (engine && a >= 16) ? 1 : 0;
+    const int P = sparse_outer(plan->s);
+    const int keep = P > 1 ? P / 2 - d / 2 : 0;
+    return forward_impl(plan, u, nullptr, nullptr, k_f, y, B, H, N, workspace,
+                        workspace_bytes, stream, skip, kMpChunkBytes, keep);
 }
 
 fftconv_status fftconv_forward_gated(fftconv_plan_t plan, const void* u,

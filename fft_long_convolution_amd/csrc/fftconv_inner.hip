@@ -102,7 +102,10 @@ __global__ void __launch_bounds__(256, 2) mp_inner_kernel(MpInnerParams prm) {
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int g = lane >> 4, x = lane & 15;
     const int upr = prm.Po / 2;                        // units per row
-    const int total = prm.B * prm.hc * upr;
+    // units q >= upr_active hold only zeroed bins (a frequency-sparse call)
+    // and are not computed: the claimed index runs over the others
+    const int upa = prm.upr_active;
+    const int total = prm.B * prm.hc * upa;
     // unit index (hl * upr + q) * B + b: the B units that share spectrum
     // coefficients are neighbours; units are claimed one ahead from the
     // counters of this workgroup's XCD group (as in the wide kernel)
@@ -157,8 +160,14 @@ __global__ void __launch_bounds__(256, 2) mp_inner_kernel(MpInnerParams prm) {
     // channel (its spectrum coefficients)
     auto unit_rows = [&](int idx, long long& row, int& h, int& q, int& sa, int& sb) {
         const int hq = (int)((unsigned)idx / (unsigned)prm.B), b = idx - hq * prm.B;
-        const int hl = hq >> lg_upr;
-        q = hq & (upr - 1);
+        int hl;
+        if (upa == upr) {
+            hl = hq >> lg_upr;
+            q = hq & (upr - 1);
+        } else {
+            hl = (int)((unsigned)hq / (unsigned)upa);
+            q = hq - hl * upa;
+        }
         h = prm.h0 + hl;
         row = (long long)b * prm.hc + hl;
         sa = sigma(q);

@@ -224,6 +224,8 @@ struct WideParams {
     const uint32_t* twf;     // per-lane W_1024 twiddles (packed f16)
     const uint32_t* two;     // outer twiddles W_M^{n' k1}, [k1-1][thread][column]
     int skip_hi;             // band limit below M/4: skip the tiles of k_b = 8..23
+    int pairs;               // mirror pairs of sub-rows computed (the rest
+                             // hold only zeroed bins: their sub-rows are zero)
 };
 hipError_t launch_wide(int io, int P, const WideParams& p, int lds_bytes,
                        hipStream_t s);
@@ -304,6 +306,8 @@ struct MpInnerParams {
     const uint32_t* twf;
     const uint32_t* two;   // W_4096^{n' m}, m = 0..4, [m][engine position of n'] (packed f16)
     int skip_hi;           // band limit below M/4: skip the tiles of k_b = 8..23
+    int upr_active;        // units q < upr_active of a row are computed (the
+                           // others hold only zeroed bins)
 };
 hipError_t launch_mp_inner(int io, const MpInnerParams& p, int lds_bytes, hipStream_t s);
 
@@ -350,6 +354,15 @@ hipError_t launch_outer_inv(int io, const FwdParams& p, int lds_bytes,
 hipError_t launch_kpad(const float* k, float2* X, int hcount, int N, int kind,
                        hipStream_t s);
 hipError_t launch_band_limit(float2* X, int hcount, int L, int F, hipStream_t s);
+// Zero blocks along the transform's digits: frequencies f whose packed bin
+// k = f mod M (or its mirror -k) has its top digit of 32 among the a
+// middle values or its outer digit k mod P among the d classes nearest P/2.
+hipError_t launch_block_mask(float2* X, int hcount, int L, int M, int P, int a, int d,
+                             hipStream_t s);
+// Zero the workspace slabs of the multi-pass units q in [q_from, Po/2)
+// (slabs sigma(q) and sigma(Po - q) of every row).
+hipError_t launch_mp_zero_units(void* ws, long long rows, int M, int Po, int P1, int P2,
+                                int q_from, hipStream_t s);
 hipError_t launch_stockham(const float2* in, float2* out, int hcount, int L,
                            int Ns, hipStream_t s);
 hipError_t launch_alphabeta(int io, const SpecParams& p, hipStream_t s);

@@ -1181,6 +1181,65 @@ hipError_t launch_kpad(const float* k, float2* X, int hcount, int N, int kind,
     return hipGetLastError();
 }
 
+__device__ __forceinline__ bool block_zero(long long k, int M, int P, int a, int d) {
+    const long long kin = k / P;
+    const int kout = (int)(k - kin * P);
+    const int kb = (int)((kin * 32 * P) / M);
+    if (kb >= 16 - a / 2 && kb < 16 + a / 2) return true;
+    // 0 < |kout - P/2| <= d/2, or kout = P/2 when d is odd
+    const int twice = 2 * kout - P;
+    const int dist2 = twice < 0 ? -twice : twice;
+    if (dist2 > 0 && dist2 <= 2 * (d / 2)) return true;
+    return (d & 1) && dist2 == 0;
+}
+
+__global__ void block_mask_kernel(float2* __restrict__ X, int hcount, int L, int M, int P,
+                                  int a, int d) {
+    const long long total = (long long)hcount * L;
+    for (long long i = blockIdx.x * (long long)blockDim.x + threadIdx.x; i < total;
+         i += (long long)gridDim.x * blockDim.x) {
+        const long long f = i % L;
+        const long long k = f % M, km = (M - k) % M;
+        if (block_zero(k, M, P, a, d) || block_zero(km, M, P, a, d)) X[i] = make_float2(0.f, 0.f);
+    }
+}
+
+hipError_t launch_block_mask(float2* X, int hcount, int L, int M, int P, int a, int d,
+                             hipStream_t s) {
+    hipLaunchKernelGGL(block_mask_kernel, dim3(1024), dim3(256), 0, s, X, hcount, L, M, P, a, d);
+    return hipGetLastError();
+}
+
+// Multi-pass workspace rows hold, per outer digit k_o, a slab of 4096 f16
+// complex words at slab position sigma(k_o) (the column passes' digit
+// order); zero the slabs of the units q >= q_from.
+__global__ void mp_zero_units_kernel(uint4* __restrict__ ws, long long rows, int M, int Po,
+                                     int P1, int P2, int q_from) {
+    const int per_slab = 4096 / 4;   // uint4 per slab
+    const int nq = Po / 2 - q_from;
+    const long long total = rows * (long long)nq * 2 * per_slab;
+    for (long long i = blockIdx.x * (long long)blockDim.x + threadIdx.x; i < total;
+         i += (long long)gridDim.x * blockDim.x) {
+        const int w = (int)(i % per_slab);
+        long long rest = i / per_slab;
+        const int side = (int)(rest & 1);
+        rest >>= 1;
+        const int q = q_from + (int)(rest % nq);
+        const long long r = rest / nq;
+        const int ko = side ? Po - q : q;
+        const int slab = (ko % P1) * P2 + ko / P1;
+        ws[(r * M + (long long)slab * 4096) / 4 + w] = make_uint4(0u, 0u, 0u, 0u);
+    }
+}
+
+hipError_t launch_mp_zero_units(void* ws, long long rows, int M, int Po, int P1, int P2,
+                                int q_from, hipStream_t s) {
+    if (q_from >= Po / 2) return hipSuccess;
+    hipLaunchKernelGGL(mp_zero_units_kernel, dim3(2048), dim3(256), 0, s, (uint4*)ws, rows, M,
+                       Po, P1, P2, q_from);
+    return hipGetLastError();
+}
+
 hipError_t launch_band_limit(float2* X, int hcount, int L, int F, hipStream_t s) {
     hipLaunchKernelGGL(band_limit_kernel, dim3(1024), dim3(256), 0, s, X, hcount, L, F);
     return hipGetLastError();

@@ -250,6 +250,18 @@ __global__ void __launch_bounds__(WideShape<P>::T, 2) wide_kernel(WideParams prm
 #pragma unroll
         for (int q = 0; q < PPW; ++q) {
             const int pr = wave + q * WAVES;
+            if (pr >= prm.pairs) {
+                // a frequency-sparse call whose pair holds only zeroed bins:
+                // its sub-rows are zero
+                if (q == PPW - 1) {
+                    if (tid == 0) s_claim[0] = (int)(c2 < total ? c2 : total);
+                    load_u(inext);
+                }
+                uint4* z0 = (uint4*)(s_buf + (2 * pr) * Q);
+#pragma unroll
+                for (int i = 0; i < 8; ++i) z0[i * 64 + lane] = make_uint4(0u, 0u, 0u, 0u);
+                continue;
+            }
             // spectrum coefficients of this row's bins, in flight while the
             // forward transforms run; kt = 1 is issued after sub-row 0
             const uint4* cf = (const uint4*)prm.kf + ((long long)h * HALF + pr) * 1024;

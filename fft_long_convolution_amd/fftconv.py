@@ -34,7 +34,8 @@ class PlanInfo(ctypes.Structure):
                 ("spectrum_bytes_per_channel", ctypes.c_size_t),
                 ("workspace_bytes_per_row", ctypes.c_size_t),
                 ("mfma_flops_per_row", ctypes.c_double),
-                ("kernel_variant", ctypes.c_int)]
+                ("kernel_variant", ctypes.c_int),
+                ("sparse_outer", ctypes.c_int)]
 
     def as_dict(self) -> dict:
         return {"N": self.N, "M": self.M, "order": self.order,
@@ -45,6 +46,7 @@ class PlanInfo(ctypes.Structure):
                 "spectrum_bytes_per_channel": self.spectrum_bytes_per_channel,
                 "workspace_bytes_per_row": self.workspace_bytes_per_row,
                 "mfma_flops_per_row": self.mfma_flops_per_row,
+                "sparse_outer": self.sparse_outer,
                 "kernel": {0: "fused_kernel", 1: "row_kernel", 3: "wide_kernel",
                            # one outer level: per-column passes; two: both
                            # levels in one column pass each way (on the
@@ -94,6 +96,10 @@ def lib() -> ctypes.CDLL:
         L.fftconv_forward_lowpass.argtypes = [vp, vp, vp, sz, vp, sz, sz, sz,
                                               vp, sz, vp]
         L.fftconv_forward_lowpass.restype = i
+        L.fftconv_kernel_spectrum_blocksparse.argtypes = [vp, vp, sz, i, i, vp, vp]
+        L.fftconv_kernel_spectrum_blocksparse.restype = i
+        L.fftconv_forward_blocksparse.argtypes = [vp, vp, vp, i, i, vp, sz, sz, sz, vp, sz, vp]
+        L.fftconv_forward_blocksparse.restype = i
         L.fftconv_kernel_spectrum_kind.argtypes = [vp, vp, sz, i, vp, vp]
         L.fftconv_kernel_spectrum_kind.restype = i
         L.fftconv_forward.argtypes = [vp, vp, vp, vp, sz, sz, sz, vp, sz, vp]
@@ -253,6 +259,37 @@ class FFTConv:
                                            ws_bytes, _stream_handle(stream))
         if st != 0:
             raise FFTConvError(st, "fftconv_forward_lowpass")
+        return out
+
+    def kernel_spectrum_blocksparse(self, k, a: int, d: int, out=None, stream=None):
+        """Spectrum of the causal kernel k ([H, N] fp32) with the digit-block
+        zero pattern (a middle values of the top digit, d outer classes)."""
+        import torch
+        if k.dtype != torch.float32 or k.dim() != 2 or k.shape[1] != self.N:
+            raise ValueError("k must be fp32 [H, %d]" % self.N)
+        k = k.contiguous()
+        H = k.shape[0]
+        if out is None:
+            out = torch.empty(self.spectrum_bytes(H), dtype=torch.uint8, device=k.device)
+        st = lib().fftconv_kernel_spectrum_blocksparse(self._plan, k.data_ptr(), H, int(a),
+                                                       int(d), out.data_ptr(),
+                                                       _stream_handle(stream))
+        if st != 0:
+            raise FFTConvError(st, "fftconv_kernel_spectrum_blocksparse")
+        return out
+
+    def forward_blocksparse(self, u, k_f, a: int, d: int, out=None, workspace=None,
+                            stream=None):
+        """The frequency-sparse convolution with zero blocks along the digits
+        (k_f from kernel_spectrum_blocksparse with the same a, d)."""
+        u = u.contiguous()
+        out, ws_ptr, ws_bytes = self._prepare(u, out, workspace)
+        B, H, N = u.shape
+        st = lib().fftconv_forward_blocksparse(self._plan, u.data_ptr(), k_f.data_ptr(),
+                                               int(a), int(d), out.data_ptr(), B, H, N,
+                                               ws_ptr, ws_bytes, _stream_handle(stream))
+        if st != 0:
+            raise FFTConvError(st, "fftconv_forward_blocksparse")
         return out
 
     def kernel_spectrum(self, k, out=None, stream=None, kind="causal"):

@@ -81,6 +81,10 @@ typedef struct fftconv_plan_info {
                                      I/O),
                                  4 = column passes + slab-pair inner pass
                                      (N >= 32K, 16-bit I/O)                */
+    int sparse_outer;         /* outer factor P of the digit-block sparsity
+                                 (fftconv_forward_blocksparse): P of the
+                                 wide kernel, N/4096 on the multi-pass path,
+                                 1 otherwise                                */
 } fftconv_plan_info;
 
 /* Predicted cost of one forward call (an MI355X analogue of the page's cost
@@ -262,6 +266,36 @@ fftconv_status fftconv_forward_lowpass(fftconv_plan_t plan, const void *u,
                                        const void *k_f, size_t cutoff, void *y,
                                        size_t B, size_t H, size_t N, void *workspace,
                                        size_t workspace_bytes, void *stream);
+
+/* Frequency-sparse convolution with zero blocks along the transform's
+ * digits (page "FlashFFTConv: Efficient Convolutions for Long Sequences
+ * with Tensor Cores", section 3.4, "Frequency-sparse convolutions": the
+ * kernel spectrum reshaped along the decomposition's factors with whole
+ * rows zeroed along each, so that whole blocks of the transform can be
+ * skipped).  The 2N-point spectrum is used through N packed bins (f and
+ * f + N share bin f mod N); a bin k = k_out + P k_in (P = the plan's
+ * sparse_outer, k_out < P) is zeroed when
+ *   - its top digit of 32, floor(32 k_in P / N), is one of the a middle
+ *     values 16 - a/2 .. 15 + a/2 (a even, 0..32), or
+ *   - its outer digit k_out is one of the d classes nearest P/2
+ *     (0 < |k_out - P/2| <= d/2, and P/2 itself when d is odd; d < P),
+ * or when its mirror bin -k mod N is (so the output stays real).  The
+ * sparsity is about 1 - (32 - a)(P - d) / (32 P).
+ * fftconv_kernel_spectrum_blocksparse builds that spectrum (arguments as
+ * fftconv_kernel_spectrum); fftconv_forward_blocksparse convolves with it
+ * (arguments as fftconv_forward, a and d as given to the spectrum), skipping
+ * the work of zero blocks: the matrix-core tiles of the top digit's middle
+ * 16 values when a >= 16 (1024-point row kernel, wide and multi-pass
+ * engines), and the whole engine passes of the outer classes' mirror pairs
+ * (wide kernel: pairs of sub-rows; multi-pass: units of two slabs).  Bad a
+ * or d -> FFTCONV_ERR_INVALID_ARG. */
+fftconv_status fftconv_kernel_spectrum_blocksparse(fftconv_plan_t plan, const float *k,
+                                                   size_t H, int a, int d, void *k_f,
+                                                   void *stream);
+fftconv_status fftconv_forward_blocksparse(fftconv_plan_t plan, const void *u,
+                                           const void *k_f, int a, int d, void *y,
+                                           size_t B, size_t H, size_t N, void *workspace,
+                                           size_t workspace_bytes, void *stream);
 
 /* Gated causal long convolution, y = v (.) ((u (.) w) * k)[0:N], for all
  * B x H rows: the input gate w multiplies u element-wise before the
