@@ -14,8 +14,11 @@ as a baseline.
 --gated times the gated form y = v * ((u * w) conv k) instead (one
 fftconv_forward_gated per step; the gates are seeded N(0,1) tensors of the
 shape of u, resident in HBM like u).  --circular times the non-causal
-(circular) convolution, --backward one fftconv_backward (du and dk of the
-causal convolution for a seeded N(0,1) dy).
+(circular) convolution on the plan at FFT size N (fftconv_plan_circular),
+and beside it, under "compare", the causal call and the circular operator
+through the causal plan's 2N-point transform; --backward one
+fftconv_backward (du and dk of the causal convolution for a seeded N(0,1)
+dy).
 """
 from __future__ import annotations
 
@@ -155,7 +158,8 @@ def main():
           else "blocksparse" if args.blocksparse is not None else "plain")
     bs_a, bs_d = ((int(x) for x in args.blocksparse.split(","))
                   if args.blocksparse is not None else (0, 0))
-    conv = FFTConv(w.N, dtype=w.dtype)
+    # the circular operator runs on the plan at FFT size N
+    conv = FFTConv(w.N, dtype=w.dtype, circular=(op == "circular"))
     info = conv.info
 
     # ---- inputs (seeded, synthetic) resident in HBM before timing
@@ -431,6 +435,15 @@ def main():
         torch.cuda.empty_cache()
         line["workloads"] = {n: time_workload(n, torch, dev)
                              for n in inputs.WORKLOADS if n != w.name}
+    if op == "circular" and not args.no_extra:
+        # the same workload on the causal plan (2N-point transform): its
+        # causal call, and the circular operator through it (the doubled
+        # kernel), each timed the same way
+        del us, gs, ys, ws, u0, g0, kf, k, dks
+        torch.cuda.empty_cache()
+        line["compare"] = {
+            "causal_plan_causal": time_workload(w.name, torch, dev),
+            "causal_plan_circular_2n": time_workload(w.name, torch, dev, kind="circular")}
     print(json.dumps(line), flush=True)
 
 
@@ -452,16 +465,17 @@ def stream_copy_rate(torch, dev, nbytes=1 << 30, reps=20) -> float:
     return 2.0 * nbytes * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9
 
 
-def time_workload(name: str, torch, dev) -> dict:
-    """One workload's forward call timed as the main line (>= 0.2 s warmup,
-    ~0.5 s timed); its roofline fraction against the spec HBM peak."""
+def time_workload(name: str, torch, dev, kind: str = "causal") -> dict:
+    """One workload's forward call on the plan of fftconv_plan, its spectrum
+    of operator `kind`, timed as the main line (>= 0.2 s warmup, ~0.5 s
+    timed); its roofline fraction against the spec HBM peak."""
     from fft_long_convolution_amd import inputs
     from fft_long_convolution_amd.fftconv import FFTConv
     w = inputs.WORKLOADS[name]
     conv = FFTConv(w.N, dtype=w.dtype)
     u = to_torch(inputs.input_rows(w), w.dtype, torch).view(w.B, w.H, w.N).to(dev)
     k = torch.from_numpy(inputs.kernel_rows(w)).to(dev)
-    kf = conv.kernel_spectrum(k)
+    kf = conv.kernel_spectrum(k, kind=kind)
     y = torch.empty_like(u)
     ws = torch.empty(max(conv.workspace_bytes(w.B, w.H), 16), dtype=torch.uint8, device=dev)
     st = torch.cuda.current_stream()

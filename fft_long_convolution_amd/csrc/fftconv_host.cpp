@@ -35,6 +35,9 @@ namespace {
 constexpr size_t kMinN = 256;
 constexpr size_t kMaxN = 4194304;
 constexpr int kFusedMaxM = 16384;
+// full plans on the wide and 16-bit multi-pass kernels (else on the
+// LDS-staged ones)
+constexpr bool kFullWide = true, kFullMp = true;
 
 bool is_pow2(size_t v) { return v && !(v & (v - 1)); }
 int ilog2(size_t v) {
@@ -61,6 +64,8 @@ struct Shape {
     bool grad = false;   // the kernel-gradient plan: LDS-staged kernels only
     bool generic = false;  // LDS-staged kernels even where a register-resident
                            // (row / wide) or 16-bit multi-pass kernel exists
+    bool full = false;     // circular operators at FFT size N: M = N/2, no
+                           // zero half (every packed point in and out)
     fftconv_dtype dtype = FFTCONV_F32;
 };
 
@@ -110,22 +115,29 @@ bool generic_forced();
 // covers N (row, wide or 16-bit multi-pass), grad: the shape of the
 // kernel-gradient passes, which hold two lines (u and dy) per workgroup:
 // LDS-staged kernels only, fused up to M = 8192 and multi-pass slabs of at
-// most 4096 points above.
+// most 4096 points above.  full: the circular operators at FFT size N (an
+// N-point real transform, M = N/2 packed points, none of them zero), N in
+// [512, 4M]; the kernel families are the same, chosen by M.
 fftconv_status make_shape_fixed(size_t N, int p, fftconv_dtype dtype, Shape& s,
-                                bool grad, bool generic) {
+                                bool grad, bool generic, bool full = false) {
     if (dtype != FFTCONV_F32 && dtype != FFTCONV_F16 && dtype != FFTCONV_BF16)
         return FFTCONV_ERR_UNSUPPORTED;
-    if (!is_pow2(N) || N < kMinN || N > kMaxN) return FFTCONV_ERR_UNSUPPORTED;
+    if (!is_pow2(N) || N < (full ? 2 * kMinN : kMinN) || N > kMaxN) return FFTCONV_ERR_UNSUPPORTED;
     if (p < 0 || p == 1 || p > kMaxStages) return FFTCONV_ERR_UNSUPPORTED;
+    if (full && grad) return FFTCONV_ERR_UNSUPPORTED;
     s = Shape();
     s.N = N;
-    s.M = N;
+    s.M = full ? N / 2 : N;
+    s.full = full;
     s.dtype = dtype;
-    const int lg = ilog2(N);
+    const int lg = ilog2(s.M);
     std::vector<int> fac;
     s.grad = grad;
     s.generic = generic || grad;
-    if (dtype != FFTCONV_F32 && lg == 15 && (p == 0 || p == 3) && !s.generic) {
+    if (full && dtype != FFTCONV_F32 &&
+        ((lg >= 12 && lg <= 14 && !kFullWide) || (lg >= 15 && !kFullMp)))
+        s.generic = true;
+    if (dtype != FFTCONV_F32 && lg == 15 && (p == 0 || p == 3) && !s.generic && !full) {
         // 16-bit I/O at N = 32K: 32 x 32 x 32 on the one-workgroup-per-row
         // kernel (eight waves, two mirror pairs each), fused
         s.path = 0;
@@ -214,11 +226,11 @@ size_t kf_entry_bytes(fftconv_dtype dt) { return dt == FFTCONV_F32 ? 16 : 8; }
 double mfma_flops_per_row(const Shape& s) {
     // real flops of the complex DFT-matrix products (8 per complex MAC):
     // forward stage 1 contracts half its digits, the last inverse stage
-    // produces half its outputs.
+    // produces half its outputs (both whole on full plans).
     double f = 0;
     for (int i = 0; i < s.p; ++i) {
         const double per = 8.0 * (double)s.M * s.f[i];
-        f += (i == 0) ? per : 2.0 * per;
+        f += (i == 0 && !s.full) ? per : 2.0 * per;
     }
     return f;
 }
@@ -344,9 +356,11 @@ CostTerms estimate(const Shape& s, size_t B, size_t H) {
 // that covers N (ties: the lower order).  FFTCONV_KERNEL=generic restricts
 // the choice to the LDS-staged kernels.
 fftconv_status make_shape(size_t N, int p, fftconv_dtype dtype, Shape& s,
-                          bool grad = false) {
+                          bool grad = false, bool full = false) {
     const bool force_generic = generic_forced();
-    if (p != 0 || grad) return make_shape_fixed(N, p, dtype, s, grad, force_generic);
+    // full plans take the family's own factorisation (the cost model
+    // prices the causal kernels)
+    if (p != 0 || grad || full) return make_shape_fixed(N, p, dtype, s, grad, force_generic, full);
     fftconv_status first = FFTCONV_ERR_UNSUPPORTED;
     bool found = false;
     double best = 0;
@@ -391,6 +405,7 @@ void fill_info(const Shape& s, fftconv_plan_info* info) {
     info->mfma_flops_per_row = mfma_flops_per_row(s);
     info->kernel_variant = s.mp_P1 ? 4 : s.path ? 2 : (s.wide_P ? 3 : (row_kernel_applies(s) ? 1 : 0));
     info->sparse_outer = sparse_outer(s);
+    info->circular = s.full ? 1 : 0;
 }
 
 // ------------------------------------------------------- table construction
@@ -554,10 +569,13 @@ float bf16_bits_to_f32(uint16_t h) {
 // First stage as the B operand: K = (n_a < 16, part d), columns
 // (k_a tile, part c), k_a = kmap32(tile, x).  bf16 plans get a hi/lo split
 // so the bf16 input feeds the matrix core directly at ~2^-16 accuracy.
-std::vector<uint16_t> row_f1b(bool bf16) {
-    const int T = bf16 ? 8 : 4;
-    std::vector<uint16_t> out((size_t)T * 64 * 8);
+// full: a second set of tiles for n_a = 16..31 (the K-step of the upper
+// half), [half][tile][lane].
+std::vector<uint16_t> row_f1b(bool bf16, bool full = false) {
+    const int T = bf16 ? 8 : 4, NH = full ? 2 : 1;
+    std::vector<uint16_t> out((size_t)NH * T * 64 * 8);
     const double sc = 1.0 / sqrt(32.0);
+    for (int hf = 0; hf < NH; ++hf)
     for (int tt = 0; tt < T; ++tt) {
         const int jt = tt & 3;
         const bool lo = tt >= 4;
@@ -565,7 +583,7 @@ std::vector<uint16_t> row_f1b(bool bf16) {
             const int g = lane >> 4, x = lane & 15;
             const int kt = jt >> 1, c = jt & 1, ka = kmap32h(kt, x);
             for (int j = 0; j < 8; ++j) {
-                const int na = 4 * g + (j >> 1), d = j & 1;
+                const int na = 16 * hf + 4 * g + (j >> 1), d = j & 1;
                 const double ang = -2.0 * M_PI * (double)((na * ka) % 32) / 32.0;
                 const double v = emb(cos(ang) * sc, sin(ang) * sc, c, d);
                 uint16_t bits;
@@ -575,19 +593,21 @@ std::vector<uint16_t> row_f1b(bool bf16) {
                 } else {
                     bits = f32_to_f16_bits((float)v);
                 }
-                out[((size_t)tt * 64 + lane) * 8 + j] = bits;
+                out[((size_t)(hf * T + tt) * 64 + lane) * 8 + j] = bits;
             }
         }
     }
     return out;
 }
 
-// Last inverse stage as the A operand: rows (n_a < 16, part c), K the
-// accumulator order of the preceding stage: k_a = kmap32(ks, 4g + j/2).
-std::vector<uint16_t> row_i1a() {
-    std::vector<uint16_t> out((size_t)4 * 64 * 8);
+// Last inverse stage as the A operand: rows (n_a < 16, part c; all 32 n_a
+// when full), K the accumulator order of the preceding stage:
+// k_a = kmap32(ks, 4g + j/2).
+std::vector<uint16_t> row_i1a(bool full = false) {
+    const int MT = full ? 4 : 2;
+    std::vector<uint16_t> out((size_t)MT * 2 * 64 * 8);
     const double sc = 1.0 / sqrt(32.0);
-    for (int mt = 0; mt < 2; ++mt)
+    for (int mt = 0; mt < MT; ++mt)
         for (int ks = 0; ks < 2; ++ks)
             for (int lane = 0; lane < 64; ++lane) {
                 const int g = lane >> 4, x = lane & 15;
@@ -874,6 +894,8 @@ void free_plan(fftconv_plan_s* pl) {
 }
 
 fftconv_status build_mp_tables(fftconv_plan_s* pl);
+fftconv_status plan_create(size_t N, int p, fftconv_dtype dtype, bool full,
+                           fftconv_plan_t* out);
 fftconv_status spectrum_impl(fftconv_plan_t plan, const float* k, size_t H,
                              fftconv_kernel_kind kind, long long cutoff, void* k_f,
                              void* stream, int blk_a = 0, int blk_d = 0);
@@ -910,8 +932,9 @@ fftconv_status build_device_tables(fftconv_plan_s* pl) {
         std::vector<float> tw = build_twiddles(n, S[i]);
         void *dtw = nullptr, *dmf = nullptr, *dmi = nullptr;
         if (upload(pl, tw.data(), tw.size() * 4, &dtw) != hipSuccess) return FFTCONV_ERR_HIP;
-        std::vector<uint8_t> mf = build_matrix(n, false, outermost, false, MAT_REG, f32);
-        std::vector<uint8_t> mi = build_matrix(n, true, false, outermost, MAT_REG, f32);
+        const bool half = outermost && !s.full;
+        std::vector<uint8_t> mf = build_matrix(n, false, half, false, MAT_REG, f32);
+        std::vector<uint8_t> mi = build_matrix(n, true, false, half, MAT_REG, f32);
         if (upload(pl, mf.data(), mf.size(), &dmf) != hipSuccess) return FFTCONV_ERR_HIP;
         if (upload(pl, mi.data(), mi.size(), &dmi) != hipSuccess) return FFTCONV_ERR_HIP;
         reg[i].n = n;
@@ -946,7 +969,7 @@ fftconv_status build_device_tables(fftconv_plan_s* pl) {
         P.M = (int)s.M;
         P.N = (int)s.N;
         P.nst = s.p - 1;
-        P.outer_half = 1;
+        P.outer_half = s.full ? 0 : 1;
         for (int i = 0; i < P.nst; ++i) {
             P.st[i] = reg[i];
             P.st[i].Sb = (int)S[i];
@@ -964,7 +987,7 @@ fftconv_status build_device_tables(fftconv_plan_s* pl) {
         O.M = (int)s.M;
         O.N = (int)s.N;
         O.nst = s.n_outer;
-        O.outer_half = 1;
+        O.outer_half = s.full ? 0 : 1;
         for (int i = 0; i < s.n_outer; ++i) {
             O.st[i] = reg[i];
             O.st[i].Sb = (int)(S[i] / s.Min);
@@ -1004,8 +1027,8 @@ fftconv_status build_device_tables(fftconv_plan_s* pl) {
     if (row_kernel_applies(s)) {
         const int NB = s.f[1];
         const bool bf = s.dtype == FFTCONV_BF16;
-        std::vector<uint16_t> f1b = row_f1b(bf), i1a = row_i1a(), i2b = row_i2b(NB),
-                              i2bs = row_i2b(NB, true);
+        std::vector<uint16_t> f1b = row_f1b(bf, s.full), i1a = row_i1a(s.full),
+                              i2b = row_i2b(NB), i2bs = row_i2b(NB, true);
         std::vector<uint8_t> f2a = row_f2a(NB);
         std::vector<uint16_t> twf = row_twiddles(NB, false), twi = row_twiddles(NB, true);
         RowParams& R = pl->row;
@@ -1015,7 +1038,7 @@ fftconv_status build_device_tables(fftconv_plan_s* pl) {
         R.f1h = d;
         if (bf) {
             // gated rows feed u (.) w to the first stage as f16
-            std::vector<uint16_t> f1h = row_f1b(false);
+            std::vector<uint16_t> f1h = row_f1b(false, s.full);
             if (upload(pl, f1h.data(), f1h.size() * 2, &d) != hipSuccess) return FFTCONV_ERR_HIP;
             R.f1h = d;
         }
@@ -1032,12 +1055,14 @@ fftconv_status build_device_tables(fftconv_plan_s* pl) {
         if (upload(pl, twi.data(), twi.size() * 2, &d) != hipSuccess) return FFTCONV_ERR_HIP;
         R.twi = (const uint32_t*)d;
         R.N = (int)s.N;
+        R.full = s.full ? 1 : 0;
         pl->use_row = true;
         pl->row_nb = NB;
         // fixed part: the four stage tables, claim counter, exchange
         // scratch of every wave; the rest of a 144 KB budget (one
         // workgroup per CU) holds spectra
-        const int tables = (bf ? 8 : 4) + 4 + (NB / 8) * (NB / 16) + (NB / 16) * 2 * (NB / 16);
+        const int NH = s.full ? 2 : 1;
+        const int tables = NH * ((bf ? 8 : 4) + 4) + (NB / 8) * (NB / 16) + (NB / 16) * 2 * (NB / 16);
         const int fixed = tables * 64 * 16 + 16 + kRowWaves * 16 * NB * 4;
         pl->row_max_channels = (144 * 1024 - fixed) / ((int)s.M * 8);
         pl->lds_row = fixed + (int)pl->row_max_channels * (int)s.M * 8;
@@ -1066,6 +1091,7 @@ fftconv_status build_device_tables(fftconv_plan_s* pl) {
         W.two = (const uint32_t*)d;
         W.N = (int)s.N;
         W.pairs = P / 2;
+        W.full = s.full ? 1 : 0;
         // stage tables (16 KB) + outer twiddles (read through L2 at P = 32)
         // + one row of f16 points + the k_b exchange
         pl->lds_wide = 16 * 1024 + (P <= 16 ? (P / 2) * 4096 : 0) + (int)s.M * 4 +
@@ -1154,6 +1180,8 @@ fftconv_status build_mp_tables(fftconv_plan_s* pl) {
 // innermost stage, one for a 32-point one).
 
 fftconv_status build_grad_plan(fftconv_plan_s* pl) {
+    // plans at FFT size N (circular operators) have no kernel gradient
+    if (pl->s.full) return FFTCONV_OK;
     if (pl->s.wide_P == 32) {
         // the kernel gradient at 32K runs on the multi-pass engine
         Shape m;
@@ -1472,10 +1500,32 @@ fftconv_status fftconv_plan_estimate(size_t N, int p, fftconv_dtype dtype, int l
 
 fftconv_status fftconv_plan(size_t N, int p, fftconv_dtype dtype,
                             fftconv_plan_t* out) {
+    return plan_create(N, p, dtype, false, out);
+}
+
+fftconv_status fftconv_plan_circular(size_t N, int p, fftconv_dtype dtype,
+                                     fftconv_plan_t* out) {
+    return plan_create(N, p, dtype, true, out);
+}
+
+fftconv_status fftconv_plan_circular_query(size_t N, int p, fftconv_dtype dtype,
+                                           fftconv_plan_info* info) {
+    if (!info) return FFTCONV_ERR_INVALID_ARG;
+    Shape s;
+    fftconv_status st = make_shape(N, p, dtype, s, false, true);
+    if (st != FFTCONV_OK) return st;
+    fill_info(s, info);
+    return FFTCONV_OK;
+}
+}  // extern "C"
+
+namespace {
+fftconv_status plan_create(size_t N, int p, fftconv_dtype dtype, bool full,
+                           fftconv_plan_t* out) {
     if (!out) return FFTCONV_ERR_INVALID_ARG;
     *out = nullptr;
     Shape s;
-    fftconv_status st = make_shape(N, p, dtype, s);
+    fftconv_status st = make_shape(N, p, dtype, s, false, full);
     if (st != FFTCONV_OK) return st;
     fftconv_plan_s* pl = new (std::nothrow) fftconv_plan_s();
     if (!pl) return FFTCONV_ERR_HIP;
@@ -1493,6 +1543,9 @@ fftconv_status fftconv_plan(size_t N, int p, fftconv_dtype dtype,
     *out = pl;
     return FFTCONV_OK;
 }
+}  // namespace
+
+extern "C" {
 
 fftconv_status fftconv_plan_get_info(fftconv_plan_t plan,
                                      fftconv_plan_info* info) {
@@ -1550,6 +1603,10 @@ fftconv_status spectrum_impl(fftconv_plan_t plan, const float* k, size_t H,
                              void* stream, int blk_a, int blk_d) {
     if (!plan) return FFTCONV_ERR_INVALID_ARG;
     if ((int)kind < 0 || (int)kind > 3) return FFTCONV_ERR_INVALID_ARG;
+    // a plan at FFT size N computes the circular kinds only, unmasked
+    if (plan->s.full && (kind == FFTCONV_CAUSAL || kind == FFTCONV_CAUSAL_ADJOINT ||
+                         cutoff >= 0 || blk_a > 0 || blk_d > 0))
+        return FFTCONV_ERR_UNSUPPORTED;
     if (H == 0) return FFTCONV_OK;
     if (!k || !k_f) return FFTCONV_ERR_INVALID_ARG;
     if (!aligned16(k) || !aligned16(k_f)) return FFTCONV_ERR_ALIGNMENT;
@@ -1561,7 +1618,8 @@ fftconv_status spectrum_impl(fftconv_plan_t plan, const float* k, size_t H,
     if (hipGetDevice(&dev) != hipSuccess) return FFTCONV_ERR_HIP;
     if (dev != plan->device) return FFTCONV_ERR_INVALID_ARG;
     hipStream_t st = (hipStream_t)stream;
-    const long long L = 2LL * (long long)s.N;
+    // the real transform's length: 2N (causal padding) or N (full plans)
+    const long long L = 2LL * (long long)s.M;
     const size_t per_ch = (size_t)L * sizeof(float2) * 2;
     size_t hc = (size_t)512 << 20;
     hc = hc / per_ch;
@@ -1575,7 +1633,7 @@ fftconv_status spectrum_impl(fftconv_plan_t plan, const float* k, size_t H,
     const int io = (int)s.dtype;
     for (size_t h0 = 0; h0 < H && e == hipSuccess; h0 += hc) {
         const int cnt = (int)((H - h0) < hc ? (H - h0) : hc);
-        e = launch_kpad(k + h0 * s.N, X0, cnt, (int)s.N, (int)kind, st);
+        e = launch_kpad(k + h0 * s.N, X0, cnt, (int)s.N, (int)L, (int)kind, st);
         float2 *a = X0, *b = X1;
         for (long long Ns = 1; Ns < L && e == hipSuccess; Ns *= 2) {
             e = launch_stockham(a, b, cnt, (int)L, (int)Ns, st);
@@ -1704,6 +1762,7 @@ fftconv_status forward_impl(fftconv_plan_t plan, const void* u, const void* w,
         C1.v = v;
         C1.ws = workspace;
         C1.ctr = (uint32_t*)((char*)workspace + (ws_need - kClaimBytes));
+        C1.full = s.full ? 1 : 0;
         MpColParams C2 = C1;
         C2.S = 4096;
         C2.tw = plan->mp_tw2;
@@ -1754,6 +1813,7 @@ fftconv_status forward_impl(fftconv_plan_t plan, const void* u, const void* w,
                 D.v = C1.v;
                 D.ws = workspace;
                 D.ctr = C1.ctr;
+                D.full = C1.full;
                 // persistent workgroups, two per CU, a multiple of 16 (the
                 // tile count is a multiple of 64)
                 D.grid = (int)std::min<long long>(mp_col2_tiles(s.mp_P2, D.rows),
@@ -1882,6 +1942,7 @@ fftconv_status fftconv_forward_lowpass(fftconv_plan_t plan, const void* u,
                                        size_t B, size_t H, size_t N, void* workspace,
                                        size_t workspace_bytes, void* stream) {
     if (!plan) return FFTCONV_ERR_INVALID_ARG;
+    if (plan->s.full) return FFTCONV_ERR_UNSUPPORTED;
     if (cutoff > plan->s.N) return FFTCONV_ERR_INVALID_ARG;
     // the 32 x 32 engine (row kernel at N = 1024, wide kernel, multi-pass
     // inner pass) skips the tiles of k_b = 8..23: the top digit of the bin,
@@ -1904,6 +1965,7 @@ fftconv_status fftconv_kernel_spectrum_blocksparse(fftconv_plan_t plan, const fl
                                                    size_t H, int a, int d, void* k_f,
                                                    void* stream) {
     if (!plan) return FFTCONV_ERR_INVALID_ARG;
+    if (plan->s.full) return FFTCONV_ERR_UNSUPPORTED;
     if (!blocksparse_args_ok(plan, a, d)) return FFTCONV_ERR_INVALID_ARG;
     return spectrum_impl(plan, k, H, FFTCONV_CAUSAL, -1, k_f, stream, a, d);
 }
@@ -1913,6 +1975,7 @@ fftconv_status fftconv_forward_blocksparse(fftconv_plan_t plan, const void* u,
                                            size_t B, size_t H, size_t N, void* workspace,
                                            size_t workspace_bytes, void* stream) {
     if (!plan) return FFTCONV_ERR_INVALID_ARG;
+    if (plan->s.full) return FFTCONV_ERR_UNSUPPORTED;
     if (!blocksparse_args_ok(plan, a, d)) return FFTCONV_ERR_INVALID_ARG;
     // the 32 x 32 engine skips the tiles of k_b = 8..23 (a >= 16 zeroes
     // them all); the wide and multi-pass kernels skip the mirror pairs of
@@ -1940,6 +2003,7 @@ fftconv_status fftconv_backward(fftconv_plan_t plan, const void* u,
                                 float* dk, size_t B, size_t H, size_t N,
                                 void* workspace, size_t workspace_bytes,
                                 void* stream) {
+    if (plan && plan->s.full) return FFTCONV_ERR_UNSUPPORTED;
     if (!plan || !plan->grad) return FFTCONV_ERR_INVALID_ARG;
     const Shape& s = plan->s;
     if (N != s.N) return FFTCONV_ERR_INVALID_ARG;

@@ -5,7 +5,9 @@
 // Long Sequences with Tensor Cores", section 3.4):
 //  * A row u[0:N] is packed into M = N complex points z[m] = u[2m] + i u[2m+1]
 //    for m < N/2; z[m] = 0 for m >= N/2 is the causal zero padding, never
-//    stored and never multiplied ("Implicit zero-padding").
+//    stored and never multiplied ("Implicit zero-padding").  Plans of the
+//    circular operators at FFT size N ("full" plans) have M = N/2 and no
+//    zero half: every packed point is loaded and every output stored.
 //  * The M-point DFT is factored M = N_1 * ... * N_p (order-p Monarch).
 //    Forward stage i (decimation in frequency, in place): within blocks of
 //    S_i = N_i * ... * N_p points, each of the s_i = S_i / N_i columns gets an
@@ -70,7 +72,9 @@ struct FwdParams {
     int M;              // packed transform length (= N)
     int N;              // sequence length
     int nst;            // regular stages handled by this kernel
-    int outer_half;     // stage 0 is the outermost stage (zero half)
+    int outer_half;     // stage 0 is the outermost stage with a zero half
+                        // (0 on full plans: all of stage 0's inputs are
+                        // loaded and all its outputs stored)
     StageDev st[kMaxStages];
     MidDev mid;
     // rows
@@ -172,6 +176,8 @@ struct RowParams {
     int B, H, N;
     int skip_hi;             // band limit below M/4 (NB = 32): skip the
                              // matrix-core tiles of k_b = 8..23
+    int full;                // FFT size 2M (circular operators): all 32 n_a
+                             // in and out, rows of M 32-bit words
     long long rows_per_wg;   // contiguous slice of channel-major rows
     int grid;                // workgroups
     const void* u;
@@ -179,9 +185,9 @@ struct RowParams {
     const void* w;      // input gate (layout of u) or null
     const void* v;      // output gate (layout of y) or null
     const void* kf;     // alpha/beta, [H][M] (4 x f16 each)
-    const void* f1b;    // first stage, B-operand tiles [hi 4][lo 4][64]
-    const void* f1h;    // first stage in f16 [4][64] (gated rows)
-    const void* i1a;    // last inverse stage, A-operand tiles [2][2][64]
+    const void* f1b;    // first stage, B-operand tiles [n_a half][hi 4][lo 4][64]
+    const void* f1h;    // first stage in f16 [n_a half][4][64] (gated rows)
+    const void* i1a;    // last inverse stage, A-operand tiles [2 or 4][2][64]
     const void* f2a;    // inner forward stage, A-operand tiles
     const void* i2b;    // inner inverse stage, B-operand tiles
     const void* i2bs;   // the same with the band-limited K-step grouping
@@ -226,6 +232,8 @@ struct WideParams {
     int skip_hi;             // band limit below M/4: skip the tiles of k_b = 8..23
     int pairs;               // mirror pairs of sub-rows computed (the rest
                              // hold only zeroed bins: their sub-rows are zero)
+    int full;                // FFT size 2M (circular operators, P <= 16): all
+                             // P sub-rows in and out, rows of M 32-bit words
 };
 hipError_t launch_wide(int io, int P, const WideParams& p, int lds_bytes,
                        hipStream_t s);
@@ -254,6 +262,8 @@ struct MpColParams {
     void* ws;
     uint32_t* ctr;         // first pass: clears the inner pass's counters
     float post;            // mode 4 (inverse, fp32 output): output scale
+    int full;              // modes 0 and 3 at FFT size 2M: all P points of
+                           // u / y, rows of M 32-bit words
 };
 // mode 0: forward first level from u; 1: forward second level (in place);
 // 2: inverse second level (in place); 3: inverse first level into y (I/O
@@ -275,6 +285,7 @@ struct MpCol2Params {
     const void* v;         // output gate (layout of y) or null
     void* ws;
     uint32_t* ctr;         // forward pass: clears the inner pass's counters
+    int full;              // FFT size 2M: all P1 first-level points of u / y
     // matrix-core forward pass (P1 = P2 = 32)
     const uint4* a1;       // forward level-1 DFT A operands, [mt 4][hi/lo 2][64];
                            // inverse: level-1 inverse DFT, [mt 2][ks 2][hi/lo 2][64]
@@ -351,7 +362,9 @@ hipError_t launch_inner(int io, const FwdParams& p, int lds_bytes,
                         hipStream_t s);
 hipError_t launch_outer_inv(int io, const FwdParams& p, int lds_bytes,
                             hipStream_t s);
-hipError_t launch_kpad(const float* k, float2* X, int hcount, int N, int kind,
+// X[h][0:L] = the L-periodic kernel of operator `kind` built from k[h][0:N]
+// (L = 2N: every kind; L = N: the circular kinds at FFT size N)
+hipError_t launch_kpad(const float* k, float2* X, int hcount, int N, int L, int kind,
                        hipStream_t s);
 hipError_t launch_band_limit(float2* X, int hcount, int L, int F, hipStream_t s);
 // Zero blocks along the transform's digits: frequencies f whose packed bin

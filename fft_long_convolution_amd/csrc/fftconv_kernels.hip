@@ -543,11 +543,13 @@ __global__ void __launch_bounds__(512) outer_fwd_kernel(FwdParams P) {
     const int c0 = blockIdx.y * P.ct;
     const int slab = P.M / P.Qo;
     float2* line = smem;
-    // the nonzero half of the outer digits: n_o < Qo/2, every thread over
-    // (digit, vector) pairs -- a tile's run per digit is only ct points
+    // the nonzero half of the outer digits: n_o < Qo/2 (all Qo digits for
+    // a plan at FFT size N: no zero half), every thread over (digit,
+    // vector) pairs -- a tile's run per digit is only ct points
+    const int nload = P.outer_half ? (P.Qo >> 1) : P.Qo;
     {
         const int per = P.ct / pts_per_vec<IO>();
-        for (int i = threadIdx.x; i < (P.Qo >> 1) * per; i += blockDim.x) {
+        for (int i = threadIdx.x; i < nload * per; i += blockDim.x) {
             const int no = i / per, j = i - no * per;
             const long long e0 = row * P.N + 2LL * ((long long)no * slab + c0);
             load_vec<IO>(io_ptr<IO>(P.u, e0), gate_ptr<IO>(P.w, e0), line + no * P.ct, j);
@@ -555,7 +557,7 @@ __global__ void __launch_bounds__(512) outer_fwd_kernel(FwdParams P) {
     }
     __syncthreads();
     for (int i = 0; i < P.nst; ++i) {
-        dispatch_stage<MF, false>(i == 0, P.st[i], line, P.Qo * P.ct, c0,
+        dispatch_stage<MF, false>(i == 0 && P.outer_half, P.st[i], line, P.Qo * P.ct, c0,
                                   wave, nwaves, lane);
         __syncthreads();
     }
@@ -634,13 +636,14 @@ __global__ void __launch_bounds__(512) outer_inv_kernel(FwdParams P) {
     }
     __syncthreads();
     for (int i = P.nst - 1; i >= 0; --i) {
-        dispatch_stage<MF, true>(i == 0, P.st[i], line, P.Qo * P.ct, c0,
+        dispatch_stage<MF, true>(i == 0 && P.outer_half, P.st[i], line, P.Qo * P.ct, c0,
                                  wave, nwaves, lane);
         __syncthreads();
     }
     {
         const int per = P.ct / pts_per_vec<IO>();
-        for (int i = threadIdx.x; i < (P.Qo >> 1) * per; i += blockDim.x) {
+        const int nstore = P.outer_half ? (P.Qo >> 1) : P.Qo;
+        for (int i = threadIdx.x; i < nstore * per; i += blockDim.x) {
             const int no = i / per, j = i - no * per;
             const long long e0 = row * P.N + 2LL * ((long long)no * slab + c0);
             store_vec<IO>(line + no * P.ct, gate_ptr<IO>(P.v, e0), (void*)io_ptr<IO>(P.y, e0), j);
@@ -1024,17 +1027,21 @@ __global__ void scale_f32_kernel(float* x, long long n, float a) {
 //                       (y[s] = sum_{t>=s} u[t] k[t-s])
 //   2 circular          c[t] = k[t mod N]  (y[t] = sum_s u[s] k[(t-s) mod N])
 //   3 circular adjoint  c[t] = k[(-t) mod N]
+// L = 2N: the 2N-periodic kernel of each operator kind (the causal
+// transform size); L = N: the N-periodic kernel of the circular kinds
+// (k itself, or k reversed: k[-t mod N]) for plans at FFT size N.
 __global__ void kpad_kernel(const float* __restrict__ k, float2* __restrict__ X,
-                            int hcount, int N, int kind) {
-    const long long L = 2LL * N;
-    const long long total = hcount * L;
+                            int hcount, int N, int L, int kind) {
+    const long long total = (long long)hcount * L;
     for (long long i = blockIdx.x * (long long)blockDim.x + threadIdx.x; i < total;
          i += (long long)gridDim.x * blockDim.x) {
         const long long h = i / L;
         const int t = (int)(i - h * L);
         const float* kr = k + h * N;
         float v = 0.f;
-        if (kind == 0) {
+        if (L == N) {
+            v = kr[kind == 2 ? t : ((N - t) & (N - 1))];
+        } else if (kind == 0) {
             if (t < N) v = kr[t];
         } else if (kind == 1) {
             if (t == 0) v = kr[0];
@@ -1175,9 +1182,11 @@ hipError_t launch_outer_inv(int io, const FwdParams& p, int lds, hipStream_t s) 
     FFTCONV_LAUNCH(outer_inv_kernel, dim3((unsigned)p.rows, slab / p.ct));
 }
 
-hipError_t launch_kpad(const float* k, float2* X, int hcount, int N, int kind,
+hipError_t launch_kpad(const float* k, float2* X, int hcount, int N, int L, int kind,
                        hipStream_t s) {
-    hipLaunchKernelGGL(kpad_kernel, dim3(1024), dim3(256), 0, s, k, X, hcount, N, kind);
+    if (L != N && L != 2 * N) return hipErrorInvalidValue;
+    if (L == N && kind != 2 && kind != 3) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(kpad_kernel, dim3(1024), dim3(256), 0, s, k, X, hcount, N, L, kind);
     return hipGetLastError();
 }
 

@@ -35,9 +35,13 @@ using namespace eng;
 // Column passes.  One thread per column c of a block: MODE 0 reads u (first
 // level, P/2 nonzero inputs) and writes the workspace; MODE 1 is a forward
 // level in place; MODE 2 an inverse level in place; MODE 3 the last inverse
-// level, writing the P/2 outputs t < N to y.
-template <int IO, int P, int MODE>
+// level, writing the P/2 outputs t < N to y.  FULL (modes 0 and 3; the
+// circular operators at FFT size 2M): all P inputs and outputs, rows of M
+// 32-bit words.
+template <int IO, int P, int MODE, bool FULL = false>
 __global__ void __launch_bounds__(256) mp_col_kernel(MpColParams prm) {
+    constexpr int NIN = FULL ? P : P / 2;     // first-level points in u / y
+    const long long roww = FULL ? (long long)prm.M : (long long)(prm.M / 2);
     // the first pass of a chunk clears the inner pass's claim counters
     if (MODE == 0 && blockIdx.x == 0 && threadIdx.x < kClaimWords) prm.ctr[threadIdx.x] = 0u;
     // M / P columns per row and S are powers of two and M / P is a multiple
@@ -60,19 +64,25 @@ __global__ void __launch_bounds__(256) mp_col_kernel(MpColParams prm) {
     rfloat2 v[P];
     uint32_t* ws = (uint32_t*)prm.ws + row * (long long)prm.M + (long long)blk * P * prm.S + c;
     if constexpr (MODE == 0) {
-        const uint32_t* u = (const uint32_t*)prm.u + mrow * (long long)(prm.M / 2) + c;
-        rfloat2 xin[P / 2];
+        const uint32_t* u = (const uint32_t*)prm.u + mrow * roww + c;
+        rfloat2 xin[NIN];
 #pragma unroll
-        for (int n = 0; n < P / 2; ++n)
+        for (int n = 0; n < NIN; ++n)
             xin[n] = f2_from_io<IO>(__builtin_nontemporal_load(&u[(long long)n * prm.S])) * sc;
         if (prm.w) {
             // input gate: u (.) w, exact in fp32
-            const uint32_t* w = (const uint32_t*)prm.w + mrow * (long long)(prm.M / 2) + c;
+            const uint32_t* w = (const uint32_t*)prm.w + mrow * roww + c;
 #pragma unroll
-            for (int n = 0; n < P / 2; ++n)
+            for (int n = 0; n < NIN; ++n)
                 xin[n] = xin[n] * f2_from_io<IO>(__builtin_nontemporal_load(&w[(long long)n * prm.S]));
         }
-        dft_half_in<P>(xin, v);
+        if constexpr (FULL) {
+#pragma unroll
+            for (int n = 0; n < P; ++n) v[n] = xin[n];
+            dft_small<P, false>(v);
+        } else {
+            dft_half_in<P>(xin, v);
+        }
     } else if constexpr (MODE == 1) {
 #pragma unroll
         for (int n = 0; n < P; ++n) v[n] = f2_from_h2(__builtin_nontemporal_load(&ws[(long long)n * prm.S])) * sc;
@@ -100,13 +110,19 @@ __global__ void __launch_bounds__(256) mp_col_kernel(MpColParams prm) {
 #pragma unroll
         for (int n = 0; n < P; ++n) __builtin_nontemporal_store(pk2(v[n].x, v[n].y), &ws[(long long)n * prm.S]);
     } else {
-        rfloat2 z[P / 2];
-        idft_half_out<P>(v, z);
+        rfloat2 z[NIN];
+        if constexpr (FULL) {
+            dft_small<P, true>(v);
+#pragma unroll
+            for (int n = 0; n < P; ++n) z[n] = v[n];
+        } else {
+            idft_half_out<P>(v, z);
+        }
         if (prm.v) {
             // output gate, in fp32 before the one rounding to the I/O type
-            const uint32_t* g = (const uint32_t*)prm.v + mrow * (long long)(prm.M / 2) + c;
+            const uint32_t* g = (const uint32_t*)prm.v + mrow * roww + c;
 #pragma unroll
-            for (int n = 0; n < P / 2; ++n)
+            for (int n = 0; n < NIN; ++n)
                 z[n] = z[n] * f2_from_io<IO>(__builtin_nontemporal_load(&g[(long long)n * prm.S]));
         }
         if constexpr (MODE >= 4) {
@@ -124,9 +140,9 @@ __global__ void __launch_bounds__(256) mp_col_kernel(MpColParams prm) {
                 y[(long long)n * prm.S] = o;
             }
         } else {
-            uint32_t* y = (uint32_t*)prm.y + mrow * (long long)(prm.M / 2) + c;
+            uint32_t* y = (uint32_t*)prm.y + mrow * roww + c;
 #pragma unroll
-            for (int n = 0; n < P / 2; ++n)
+            for (int n = 0; n < NIN; ++n)
                 __builtin_nontemporal_store(pk2io<IO>(z[n].x, z[n].y), &y[(long long)n * prm.S]);
         }
     }
@@ -153,9 +169,11 @@ __global__ void __launch_bounds__(256) mp_col_kernel(MpColParams prm) {
 constexpr int kCol2Threads = 256;
 constexpr int col2_cols(int P2) { return 512 / P2; }
 
-template <int IO, int P1, int P2, bool INV, bool G>
+template <int IO, int P1, int P2, bool INV, bool G, bool FULL>
 __global__ void __launch_bounds__(kCol2Threads, 2) mp_col2_kernel(MpCol2Params prm) {
     constexpr int TC = col2_cols(P2), SLAB = 4096, TPR = SLAB / TC;
+    // first-level points in u / y: P1 / 2, or all P1 at FFT size 2M (FULL)
+    constexpr int NIN = FULL ? P1 : P1 / 2;
     constexpr int NT = kCol2Threads;
     constexpr int L1T = P2 * TC / NT;             // level-1 tasks per thread (2)
     constexpr int L2T = P1 * TC / NT;             // level-2 tasks per thread (2 or 4)
@@ -166,6 +184,7 @@ __global__ void __launch_bounds__(kCol2Threads, 2) mp_col2_kernel(MpCol2Params p
     auto lidx = [](int k1, int n2, int c) { return (k1 * P2 + ((n2 + k1) & (P2 - 1))) * TC + c; };
     const int tid = threadIdx.x;
     const long long M2 = (long long)P2 * SLAB, M = (long long)P1 * M2;
+    const long long roww = FULL ? M : M / 2;   // 32-bit words per I/O row
     const long long ntiles = prm.rows * TPR;
     const float sc1 = rsqrtf((float)P1), sc2 = rsqrtf((float)P2);
     // the first pass of a chunk clears the inner pass's claim counters
@@ -188,18 +207,18 @@ __global__ void __launch_bounds__(kCol2Threads, 2) mp_col2_kernel(MpCol2Params p
     };
 
     if constexpr (!INV) {
-        uint32_t raw[L1T][P1 / 2];
+        uint32_t raw[L1T][NIN];
         float2 tw1[L1T], tw2[L2T];
         auto fetch = [&](long long t) {
             int c0;
             const long long r = row_of(t, c0);
-            const uint32_t* u = (const uint32_t*)prm.u + mem_row(r) * (M / 2) + c0;
+            const uint32_t* u = (const uint32_t*)prm.u + mem_row(r) * roww + c0;
 #pragma unroll
             for (int i = 0; i < L1T; ++i) {
                 const int task = tid + i * NT;
                 const long long col = (long long)(task / TC) * SLAB + task % TC;
 #pragma unroll
-                for (int n1 = 0; n1 < P1 / 2; ++n1)
+                for (int n1 = 0; n1 < NIN; ++n1)
                     raw[i][n1] = __builtin_nontemporal_load(&u[(long long)n1 * M2 + col]);
                 tw1[i] = prm.tw1[col + c0];
             }
@@ -212,15 +231,15 @@ __global__ void __launch_bounds__(kCol2Threads, 2) mp_col2_kernel(MpCol2Params p
         for (; t < ntiles; t += gridDim.x) {
             int c0;
             const long long r = row_of(t, c0);
-            uint32_t graw[G ? L1T : 1][P1 / 2];   // input gate of this tile
+            uint32_t graw[G ? L1T : 1][NIN];   // input gate of this tile
             if constexpr (G) {
-                const uint32_t* w = (const uint32_t*)prm.w + mem_row(r) * (M / 2) + c0;
+                const uint32_t* w = (const uint32_t*)prm.w + mem_row(r) * roww + c0;
 #pragma unroll
                 for (int i = 0; i < L1T; ++i) {
                     const int task = tid + i * NT;
                     const long long col = (long long)(task / TC) * SLAB + task % TC;
 #pragma unroll
-                    for (int n1 = 0; n1 < P1 / 2; ++n1)
+                    for (int n1 = 0; n1 < NIN; ++n1)
                         graw[i][n1] = __builtin_nontemporal_load(&w[(long long)n1 * M2 + col]);
                 }
             }
@@ -230,13 +249,19 @@ __global__ void __launch_bounds__(kCol2Threads, 2) mp_col2_kernel(MpCol2Params p
                 // one task at a time: interleaved tasks would not fit the registers
                 __builtin_amdgcn_sched_barrier(0);
                 const int task = tid + i * NT, c = task % TC, n2 = task / TC;
-                rfloat2 xin[P1 / 2], v[P1];
+                rfloat2 xin[NIN], v[P1];
 #pragma unroll
-                for (int n1 = 0; n1 < P1 / 2; ++n1) {
+                for (int n1 = 0; n1 < NIN; ++n1) {
                     xin[n1] = f2_from_io<IO>(raw[i][n1]) * sc1;
                     if constexpr (G) xin[n1] = xin[n1] * f2_from_io<IO>(graw[i][n1]);
                 }
-                dft_half_in<P1>(xin, v);
+                if constexpr (FULL) {
+#pragma unroll
+                    for (int n1 = 0; n1 < P1; ++n1) v[n1] = xin[n1];
+                    dft_small<P1, false>(v);
+                } else {
+                    dft_half_in<P1>(xin, v);
+                }
                 const rfloat2 t1 = {tw1[i].x, tw1[i].y};
                 rfloat2 w = t1;
                 s_t[lidx(0, n2, c)] = pk2(v[0].x, v[0].y);
@@ -330,18 +355,18 @@ __global__ void __launch_bounds__(kCol2Threads, 2) mp_col2_kernel(MpCol2Params p
             }
             // inverse level 1: conjugate twiddle, P1-point inverse DFT, the
             // P1/2 outputs t < N to y
-            uint32_t* y = (uint32_t*)prm.y + mem_row(r) * (M / 2) + c0;
+            uint32_t* y = (uint32_t*)prm.y + mem_row(r) * roww + c0;
 #pragma unroll
             for (int i = 0; i < L1T; ++i) {
                 // one task at a time: interleaved tasks would not fit the registers
                 __builtin_amdgcn_sched_barrier(0);
                 const int task = tid + i * NT, c = task % TC, n2 = task / TC;
-                uint32_t graw[G ? P1 / 2 : 1];   // output gate of this task
+                uint32_t graw[G ? NIN : 1];   // output gate of this task
                 if constexpr (G) {
-                    const uint32_t* gv = (const uint32_t*)prm.v + mem_row(r) * (M / 2) + c0 +
+                    const uint32_t* gv = (const uint32_t*)prm.v + mem_row(r) * roww + c0 +
                                          (long long)n2 * SLAB + c;
 #pragma unroll
-                    for (int n1 = 0; n1 < P1 / 2; ++n1)
+                    for (int n1 = 0; n1 < NIN; ++n1)
                         graw[n1] = __builtin_nontemporal_load(&gv[(long long)n1 * M2]);
                 }
                 const rfloat2 t1 = {tw1c[i].x, tw1c[i].y};
@@ -352,15 +377,21 @@ __global__ void __launch_bounds__(kCol2Threads, 2) mp_col2_kernel(MpCol2Params p
                     v[k1] = fmulc(f2_from_h2(s_t[lidx(k1, n2, c)]) * sc1, w);
                     w = fmul(w, t1);
                 }
-                rfloat2 z[P1 / 2];
-                idft_half_out<P1>(v, z);
+                rfloat2 z[NIN];
+                if constexpr (FULL) {
+                    dft_small<P1, true>(v);
+#pragma unroll
+                    for (int n1 = 0; n1 < P1; ++n1) z[n1] = v[n1];
+                } else {
+                    idft_half_out<P1>(v, z);
+                }
                 if constexpr (G) {
 #pragma unroll
-                    for (int n1 = 0; n1 < P1 / 2; ++n1) z[n1] = z[n1] * f2_from_io<IO>(graw[n1]);
+                    for (int n1 = 0; n1 < NIN; ++n1) z[n1] = z[n1] * f2_from_io<IO>(graw[n1]);
                 }
                 uint32_t* o = y + (long long)n2 * SLAB + c;
 #pragma unroll
-                for (int n1 = 0; n1 < P1 / 2; ++n1)
+                for (int n1 = 0; n1 < NIN; ++n1)
                     __builtin_nontemporal_store(pk2io<IO>(z[n1].x, z[n1].y), &o[(long long)n1 * M2]);
             }
             if constexpr (G) {
@@ -908,6 +939,13 @@ template <int IO, int P>
 hipError_t col_launch(int mode, const MpColParams& p, hipStream_t s) {
     const long long threads = p.rows * (long long)(p.M / P);
     const dim3 grid((unsigned)((threads + 255) / 256)), blk(256);
+    if (p.full) {
+        // rows at FFT size 2M: the first forward and the last inverse level
+        if (mode == 0) hipLaunchKernelGGL((mp_col_kernel<IO, P, 0, true>), grid, blk, 0, s, p);
+        else if (mode == 3) hipLaunchKernelGGL((mp_col_kernel<IO, P, 3, true>), grid, blk, 0, s, p);
+        else return hipErrorInvalidValue;
+        return hipGetLastError();
+    }
     switch (mode) {
     case 0: hipLaunchKernelGGL((mp_col_kernel<IO, P, 0>), grid, blk, 0, s, p); break;
     case 1: hipLaunchKernelGGL((mp_col_kernel<IO, P, 1>), grid, blk, 0, s, p); break;
@@ -948,17 +986,26 @@ template <int IO, int P1, int P2>
 hipError_t col2_launch(bool inv, const MpCol2Params& p, hipStream_t s) {
     const dim3 grid((unsigned)p.grid), blk(kCol2Threads);
     // 32 x 32 plans take the matrix-core passes; only their plain variant
-    // of this kernel is kept
+    // of this kernel is kept (and no FFT-size variant: M = 4M is beyond the
+    // longest circular plan)
     if constexpr (P1 == 32 && P2 == 32) {
-        if (p.w) return hipErrorInvalidValue;
-        if (inv) hipLaunchKernelGGL((mp_col2_kernel<IO, P1, P2, true, false>), grid, blk, 0, s, p);
-        else hipLaunchKernelGGL((mp_col2_kernel<IO, P1, P2, false, false>), grid, blk, 0, s, p);
+        if (p.w || p.full) return hipErrorInvalidValue;
+        if (inv) hipLaunchKernelGGL((mp_col2_kernel<IO, P1, P2, true, false, false>), grid, blk, 0, s, p);
+        else hipLaunchKernelGGL((mp_col2_kernel<IO, P1, P2, false, false, false>), grid, blk, 0, s, p);
+    } else if (p.full) {
+        if (p.w) {
+            if (inv) hipLaunchKernelGGL((mp_col2_kernel<IO, P1, P2, true, true, true>), grid, blk, 0, s, p);
+            else hipLaunchKernelGGL((mp_col2_kernel<IO, P1, P2, false, true, true>), grid, blk, 0, s, p);
+        } else {
+            if (inv) hipLaunchKernelGGL((mp_col2_kernel<IO, P1, P2, true, false, true>), grid, blk, 0, s, p);
+            else hipLaunchKernelGGL((mp_col2_kernel<IO, P1, P2, false, false, true>), grid, blk, 0, s, p);
+        }
     } else if (p.w) {
-        if (inv) hipLaunchKernelGGL((mp_col2_kernel<IO, P1, P2, true, true>), grid, blk, 0, s, p);
-        else hipLaunchKernelGGL((mp_col2_kernel<IO, P1, P2, false, true>), grid, blk, 0, s, p);
+        if (inv) hipLaunchKernelGGL((mp_col2_kernel<IO, P1, P2, true, true, false>), grid, blk, 0, s, p);
+        else hipLaunchKernelGGL((mp_col2_kernel<IO, P1, P2, false, true, false>), grid, blk, 0, s, p);
     } else {
-        if (inv) hipLaunchKernelGGL((mp_col2_kernel<IO, P1, P2, true, false>), grid, blk, 0, s, p);
-        else hipLaunchKernelGGL((mp_col2_kernel<IO, P1, P2, false, false>), grid, blk, 0, s, p);
+        if (inv) hipLaunchKernelGGL((mp_col2_kernel<IO, P1, P2, true, false, false>), grid, blk, 0, s, p);
+        else hipLaunchKernelGGL((mp_col2_kernel<IO, P1, P2, false, false, false>), grid, blk, 0, s, p);
     }
     return hipGetLastError();
 }

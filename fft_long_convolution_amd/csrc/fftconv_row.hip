@@ -8,13 +8,16 @@
 //
 // Packed row z[m] = u[2m] + i u[2m+1], m = NB*n_a + n_b (n_a < 16 nonzero:
 // the causal zero half is never touched).  Bins k = k_a + 32 k_b.
+// FULL (the circular operators at FFT size 2M = 64 NB, no padding): all 32
+// n_a are loaded, F1 contracts them in two K-steps and I1 produces all 32.
 //
 // The four matrix-core products alternate the role of the data so that the
 // index the next stage contracts is always the one held inside a lane:
 //   F1  C[n_b][(c,k_a)] = data(A: rows n_b, K n_a) x F32       (k_a -> lanes)
 //   F2  C[(k_b,c)][k_a] = F_NB x data(B: K n_b, cols k_a)      (k_b in-lane)
 //   I2  C[k_a][(c,n_b)] = data(A: rows k_a, K k_b) x F_NB^-1   (k_a in-lane)
-//   I1  C[(n_a,c)][n_b] = F32^-1 x data(B: K k_a, cols n_b)    (n_a < 16)
+//   I1  C[(n_a,c)][n_b] = F32^-1 x data(B: K k_a, cols n_b)    (n_a < 16;
+//                                                               all: FULL)
 // Real and imaginary parts of a point always sit in the same lane (the
 // complex index goes to rows, or to separate column tiles).  Lane x holds
 // k_a = x and its mirror 32-x (lane 0: 0 and 16), and the F_NB row order
@@ -48,12 +51,19 @@ namespace fftconv {
 // accumulators before the one rounding to the I/O type.  The extra registers
 // take the workgroup down to twelve waves.
 constexpr int kRowDepth = 2;
+// Rows of 32 n_a at NB = 32 (FULL) hold twice the input registers: twelve
+// waves, like gated rows; gated FULL rows also prefetch one row less.
+template <bool G, bool FULL, int NB>
+constexpr int row_waves() { return (G || (FULL && NB == 32)) ? kRowWavesGated : kRowWaves; }
 
-template <int IO, int NB, bool G, bool SK>
-__global__ void __launch_bounds__(64 * (G ? kRowWavesGated : kRowWaves), 1)
+template <int IO, int NB, bool G, bool SK, bool FULL>
+__global__ void __launch_bounds__((64 * row_waves<G, FULL, NB>()), 1)
 row_kernel(RowParams P) {
-    constexpr int WAVES = G ? kRowWavesGated : kRowWaves;
+    constexpr int WAVES = row_waves<G, FULL, NB>();
     constexpr int M = 32 * NB;
+    constexpr int NH = FULL ? 2 : 1;      // halves of n_a loaded (16 each)
+    constexpr int ROWW = NH * M / 2;      // 32-bit words per I/O row
+    constexpr int MTO = 2 * NH;           // I1 output tiles (8 n_a each)
     constexpr int IT = NB / 16;    // n_b tiles
     constexpr int MT2 = NB / 8;    // k_b slot tiles
     constexpr int KS2 = NB / 16;   // K-steps over n_b / k_b
@@ -62,12 +72,12 @@ row_kernel(RowParams P) {
     constexpr int F1R = BF ? 8 : 4;       // first-stage region (plan layout)
     constexpr bool BFA = BF && !G;        // bf16 first-stage operands
     constexpr int F1T = BFA ? 8 : 4;      // first-stage tiles used
-    constexpr int D = kRowDepth;
+    constexpr int D = (G && FULL && NB == 32) ? 1 : kRowDepth;
 
     extern __shared__ uint4 s_lds[];
-    uint4* s_f1b = s_lds;                            // [F1R][64]
-    uint4* s_i1a = s_f1b + F1R * 64;                 // [4][64]
-    uint4* s_f2a = s_i1a + 4 * 64;                   // [MT2][KS2][64]
+    uint4* s_f1b = s_lds;                            // [NH][F1R][64]
+    uint4* s_i1a = s_f1b + NH * F1R * 64;            // [MTO][2][64]
+    uint4* s_f2a = s_i1a + MTO * 2 * 64;             // [MT2][KS2][64]
     uint4* s_i2b = s_f2a + MT2 * KS2 * 64;           // [KS2][2 NT][64]
     uint32_t* s_ctr = (uint32_t*)(s_i2b + KS2 * 2 * NT * 64);   // row claim counter (16 B)
     uint32_t* s_scr = s_ctr + 4;                     // [waves][NB][16]
@@ -86,8 +96,12 @@ row_kernel(RowParams P) {
 
     constexpr int TH = 64 * WAVES;
     const uint4* f1src = (const uint4*)(G ? P.f1h : P.f1b);
-    for (int i = tid; i < F1T * 64; i += TH) s_f1b[i] = f1src[i];
-    for (int i = tid; i < 4 * 64; i += TH) s_i1a[i] = ((const uint4*)P.i1a)[i];
+    // the table holds F1T tiles per half; the LDS region F1R per half
+    for (int i = tid; i < NH * F1T * 64; i += TH) {
+        const int hf = i / (F1T * 64);
+        s_f1b[hf * F1R * 64 + (i - hf * F1T * 64)] = f1src[i];
+    }
+    for (int i = tid; i < MTO * 2 * 64; i += TH) s_i1a[i] = ((const uint4*)P.i1a)[i];
     for (int i = tid; i < MT2 * KS2 * 64; i += TH) s_f2a[i] = ((const uint4*)P.f2a)[i];
     const uint4* i2src = (const uint4*)(skip_hi ? P.i2bs : P.i2b);
     for (int i = tid; i < KS2 * 2 * NT * 64; i += TH) s_i2b[i] = i2src[i];
@@ -151,30 +165,34 @@ row_kernel(RowParams P) {
         h = hh;
         b = off;
     };
-    auto load_row = [&](uint32_t (&dst)[IT][4], const void* base, int c) {
+    auto load_row = [&](uint32_t (&dst)[NH][IT][4], const void* base, int c) {
         int h, b;
         row_of(c, h, b);
         const uint32_t* u =
-            (const uint32_t*)base + ((long long)b * P.H + h) * (M / 2);
-        if constexpr (NB == 32) {
-            // whole 128-byte rows per load: lane groups g and g + 1 take the
-            // two halves of rows 8 (g / 2) + q; the exchange into the
-            // operand layout happens where the row is consumed
+            (const uint32_t*)base + ((long long)b * P.H + h) * ROWW;
 #pragma unroll
-            for (int q = 0; q < 8; ++q)
-                dst[q >> 2][q & 3] = __builtin_nontemporal_load(
-                    &u[NB * (8 * (g >> 1) + q) + ((g & 1) ? kmap32(1, x) : x)]);
-        } else {
+        for (int hf = 0; hf < NH; ++hf) {
+            const uint32_t* uh = u + hf * 16 * NB;
+            if constexpr (NB == 32) {
+                // whole 128-byte rows per load: lane groups g and g + 1 take
+                // the two halves of rows 8 (g / 2) + q; the exchange into the
+                // operand layout happens where the row is consumed
 #pragma unroll
-            for (int it = 0; it < IT; ++it)
+                for (int q = 0; q < 8; ++q)
+                    dst[hf][q >> 2][q & 3] = __builtin_nontemporal_load(
+                        &uh[NB * (8 * (g >> 1) + q) + ((g & 1) ? kmap32(1, x) : x)]);
+            } else {
 #pragma unroll
-                for (int jj = 0; jj < 4; ++jj)
-                    dst[it][jj] = __builtin_nontemporal_load(&u[NB * (4 * g + jj) + nbmap<NB>(it, x)]);
+                for (int it = 0; it < IT; ++it)
+#pragma unroll
+                    for (int jj = 0; jj < 4; ++jj)
+                        dst[hf][it][jj] = __builtin_nontemporal_load(&uh[NB * (4 * g + jj) + nbmap<NB>(it, x)]);
+            }
         }
     };
 
-    uint32_t ring[D][IT][4];
-    uint32_t wring[G ? D : 1][IT][4];   // input gate rows (gated only)
+    uint32_t ring[D][NH][IT][4];
+    uint32_t wring[G ? D : 1][NH][IT][4];   // input gate rows (gated only)
     int cl[D];
     if (nslice > 0) {
 #pragma unroll
@@ -189,7 +207,7 @@ row_kernel(RowParams P) {
     uint32_t* scr = s_scr + wave * 16 * NB + x;
 
     {
-        auto row_body = [&](uint32_t (&cur)[IT][4], uint32_t (&wcur)[IT][4], const int m) {
+        auto row_body = [&](uint32_t (&cur)[NH][IT][4], uint32_t (&wcur)[NH][IT][4], const int m) {
             int h, b;
             row_of(m, h, b);
             const long long row = (long long)b * P.H + h;
@@ -197,11 +215,11 @@ row_kernel(RowParams P) {
             // output gate at the stores' addresses: [mt][nt][e] is the word
             // stored from o[nt][e] of tile mt (for NB = 32 after the
             // exchange, which is undone below)
-            uint32_t vg[G ? 2 : 1][NT][2];
+            uint32_t vg[G ? MTO : 1][NT][2];
             if constexpr (G) {
-                const uint32_t* vrow = (const uint32_t*)P.v + row * (long long)(M / 2);
+                const uint32_t* vrow = (const uint32_t*)P.v + row * (long long)ROWW;
 #pragma unroll
-                for (int mt = 0; mt < 2; ++mt)
+                for (int mt = 0; mt < MTO; ++mt)
 #pragma unroll
                     for (int e = 0; e < 2; ++e) {
                         if constexpr (NB == 32) {
@@ -216,33 +234,43 @@ row_kernel(RowParams P) {
                         }
                     }
             }
-            if constexpr (NB == 32) {
 #pragma unroll
-                for (int jj = 0; jj < 4; ++jj) {
-                    swap16(cur[0][jj], cur[1][jj]);
-                    if constexpr (G) swap16(wcur[0][jj], wcur[1][jj]);
+            for (int hf = 0; hf < NH; ++hf) {
+                if constexpr (NB == 32) {
+#pragma unroll
+                    for (int jj = 0; jj < 4; ++jj) {
+                        swap16(cur[hf][0][jj], cur[hf][1][jj]);
+                        if constexpr (G) swap16(wcur[hf][0][jj], wcur[hf][1][jj]);
+                    }
+                }
+                if constexpr (G) {
+#pragma unroll
+                    for (int it = 0; it < IT; ++it)
+#pragma unroll
+                        for (int jj = 0; jj < 4; ++jj)
+                            cur[hf][it][jj] = gate_in<IO>(cur[hf][it][jj], wcur[hf][it][jj]);
                 }
             }
-            if constexpr (G) {
-#pragma unroll
-                for (int it = 0; it < IT; ++it)
-#pragma unroll
-                    for (int jj = 0; jj < 4; ++jj) cur[it][jj] = gate_in<IO>(cur[it][jj], wcur[it][jj]);
-            }
-            // ---- F1: 32-point DFT over n_a (16 nonzero), k_a to the lanes
+            // ---- F1: 32-point DFT over n_a (16 nonzero; all 32 in two
+            // K-steps when FULL), k_a to the lanes
             uint4 b2[KS2][2];
 #pragma unroll
             for (int it = 0; it < IT; ++it) {
-                const uint4 a = make_uint4(cur[it][0], cur[it][1], cur[it][2], cur[it][3]);
                 rfloat4 c1[4];
 #pragma unroll
                 for (int jt = 0; jt < 4; ++jt) {
                     rfloat4 acc = {0.f, 0.f, 0.f, 0.f};
-                    if (BFA) {
-                        acc = mma_bf16(a, s_f1b[jt * 64 + lane], acc);
-                        acc = mma_bf16(a, s_f1b[(4 + jt) * 64 + lane], acc);
-                    } else {
-                        acc = mma_f16(a, s_f1b[jt * 64 + lane], acc);
+#pragma unroll
+                    for (int hf = 0; hf < NH; ++hf) {
+                        const uint4 a = make_uint4(cur[hf][it][0], cur[hf][it][1], cur[hf][it][2],
+                                                   cur[hf][it][3]);
+                        const uint4* tb = s_f1b + hf * F1R * 64;
+                        if (BFA) {
+                            acc = mma_bf16(a, tb[jt * 64 + lane], acc);
+                            acc = mma_bf16(a, tb[(4 + jt) * 64 + lane], acc);
+                        } else {
+                            acc = mma_f16(a, tb[jt * 64 + lane], acc);
+                        }
                     }
                     c1[jt] = acc;
                 }
@@ -354,10 +382,11 @@ row_kernel(RowParams P) {
                     }
                     b1v[kt][nt] = make_uint4(w[0], w[1], w[2], w[3]);
                 }
-            // ---- I1: inverse 32-point DFT over k_a, only n_a < 16 (t < N)
-            uint32_t* yrow = (uint32_t*)P.y + row * (long long)(M / 2);
+            // ---- I1: inverse 32-point DFT over k_a, only n_a < 16 (t < N;
+            // all 32 when FULL)
+            uint32_t* yrow = (uint32_t*)P.y + row * (long long)ROWW;
 #pragma unroll
-            for (int mt = 0; mt < 2; ++mt) {
+            for (int mt = 0; mt < MTO; ++mt) {
                 uint32_t o[NT][2];
                 if constexpr (G && NB == 32) {
 #pragma unroll
@@ -415,36 +444,41 @@ row_kernel(RowParams P) {
     }
 }
 
-template <int IO, int NB, bool G, bool SK>
+template <int IO, int NB, bool G, bool SK, bool FULL>
 static hipError_t launch_row_t(const RowParams& p, int lds, hipStream_t s) {
     if (lds > 64 * 1024) {
-        const hipError_t e = hipFuncSetAttribute((const void*)row_kernel<IO, NB, G, SK>,
+        const hipError_t e = hipFuncSetAttribute((const void*)row_kernel<IO, NB, G, SK, FULL>,
                                                  hipFuncAttributeMaxDynamicSharedMemorySize, lds);
         if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL((row_kernel<IO, NB, G, SK>), dim3((unsigned)p.grid),
-                       dim3(64 * (G ? kRowWavesGated : kRowWaves)), lds, s, p);
+    hipLaunchKernelGGL((row_kernel<IO, NB, G, SK, FULL>), dim3((unsigned)p.grid),
+                       dim3(64 * row_waves<G, FULL, NB>()), lds, s, p);
     return hipGetLastError();
 }
 
-template <bool G>
+template <bool G, bool FULL>
 static hipError_t launch_row_g(int io, int nb, const RowParams& p, int lds, hipStream_t s) {
     if (io == IO_BF16)
-        return nb == 32 ? launch_row_t<IO_BF16, 32, G, false>(p, lds, s)
-                        : launch_row_t<IO_BF16, 16, G, false>(p, lds, s);
-    return nb == 32 ? launch_row_t<IO_F16, 32, G, false>(p, lds, s)
-                    : launch_row_t<IO_F16, 16, G, false>(p, lds, s);
+        return nb == 32 ? launch_row_t<IO_BF16, 32, G, false, FULL>(p, lds, s)
+                        : launch_row_t<IO_BF16, 16, G, false, FULL>(p, lds, s);
+    return nb == 32 ? launch_row_t<IO_F16, 32, G, false, FULL>(p, lds, s)
+                    : launch_row_t<IO_F16, 16, G, false, FULL>(p, lds, s);
 }
 
 hipError_t launch_row(int io, int nb, const RowParams& p, int lds, hipStream_t s) {
-    if (p.w) return launch_row_g<true>(io, nb, p, lds, s);
+    if (p.full) {
+        if (p.skip_hi) return hipErrorInvalidValue;
+        return p.w ? launch_row_g<true, true>(io, nb, p, lds, s)
+                   : launch_row_g<false, true>(io, nb, p, lds, s);
+    }
+    if (p.w) return launch_row_g<true, false>(io, nb, p, lds, s);
     if (p.skip_hi) {
         // band-limited rows (N = 1024 only)
         if (nb != 32) return hipErrorInvalidValue;
-        return io == IO_BF16 ? launch_row_t<IO_BF16, 32, false, true>(p, lds, s)
-                             : launch_row_t<IO_F16, 32, false, true>(p, lds, s);
+        return io == IO_BF16 ? launch_row_t<IO_BF16, 32, false, true, false>(p, lds, s)
+                             : launch_row_t<IO_F16, 32, false, true, false>(p, lds, s);
     }
-    return launch_row_g<false>(io, nb, p, lds, s);
+    return launch_row_g<false, false>(io, nb, p, lds, s);
 }
 
 }  // namespace fftconv

@@ -27,6 +27,10 @@
 // before the store (fp32 for bf16 rows, packed f16 for f16 rows, as the
 // stage itself computes).
 //
+// FULL (the circular operators at FFT size 2M, P <= 16): no zero half; the
+// outer stage takes all P sub-rows of the row (a whole P-point DFT) and the
+// outer inverse stores all P.
+//
 // Mirror pairing.  Bin k pairs with -k.  For 0 < k1 < P/2 the partner bins
 // live in sub-row P - k1.  That sub-row is pushed through the engine as
 // w_k1 * conj(A_{P-k1}) -- the same twiddle as sub-row k1 -- which returns
@@ -54,13 +58,16 @@ struct WideShape {
     static constexpr bool TWG = P > 16;          // outer twiddles from memory
 };
 
-template <int IO, int P, bool G, bool SK>
+template <int IO, int P, bool G, bool SK, bool FULL>
 __global__ void __launch_bounds__(WideShape<P>::T, 2) wide_kernel(WideParams prm) {
     typedef WideShape<P> WS;
     constexpr int Q = 1024, M = P * Q, HALF = P / 2, T = WS::T;
+    constexpr int NIN = FULL ? P : HALF;      // sub-rows loaded and stored
+    constexpr int ROWW = NIN * Q;             // 32-bit words per I/O row
     constexpr int WAVES = WS::WAVES, PPW = WS::PPW;
     constexpr bool TWG = WS::TWG;
     constexpr int CPT = Q / T;   // outer-stage columns per thread
+    static_assert(!(FULL && TWG), "FFT-size rows on the P <= 16 kernels only");
 
     extern __shared__ uint4 s_lds[];
     uint4* s_f1b = s_lds;                              // [ks 2][jt 4][64]
@@ -134,14 +141,14 @@ __global__ void __launch_bounds__(WideShape<P>::T, 2) wide_kernel(WideParams prm
     // word offset of this thread's first column; the rest are immediates
     // on a per-n1 scalar base
     const int lofs = 32 * na0 + nb;
-    uint32_t uin[HALF][CPT];
-    uint32_t win[G ? HALF : 1][CPT];   // input gate (gated only)
+    uint32_t uin[NIN][CPT];
+    uint32_t win[G ? NIN : 1][CPT];   // input gate (gated only)
     auto load_u = [&](int idx) {
         const int hh = idx / prm.B, bb = idx - hh * prm.B;
-        const long long off = ((long long)bb * prm.H + hh) * (M / 2);
+        const long long off = ((long long)bb * prm.H + hh) * ROWW;
         const uint32_t* u = (const uint32_t*)prm.u + off;
 #pragma unroll
-        for (int n1 = 0; n1 < HALF; ++n1) {
+        for (int n1 = 0; n1 < NIN; ++n1) {
             const uint32_t* un = u + n1 * Q + lofs;
 #pragma unroll
             for (int j = 0; j < CPT; ++j) uin[n1][j] = __builtin_nontemporal_load(&un[32 * j]);
@@ -149,7 +156,7 @@ __global__ void __launch_bounds__(WideShape<P>::T, 2) wide_kernel(WideParams prm
         if constexpr (G) {
             const uint32_t* w = (const uint32_t*)prm.w + off;
 #pragma unroll
-            for (int n1 = 0; n1 < HALF; ++n1) {
+            for (int n1 = 0; n1 < NIN; ++n1) {
                 const uint32_t* wn = w + n1 * Q + lofs;
 #pragma unroll
                 for (int j = 0; j < CPT; ++j) win[n1][j] = __builtin_nontemporal_load(&wn[32 * j]);
@@ -209,13 +216,19 @@ __global__ void __launch_bounds__(WideShape<P>::T, 2) wide_kernel(WideParams prm
             uint32_t V[P][CPT];
 #pragma unroll
             for (int j = 0; j < CPT; ++j) {
-                C xin[HALF], A[P];
+                C xin[NIN], A[P];
 #pragma unroll
-                for (int n1 = 0; n1 < HALF; ++n1) {
+                for (int n1 = 0; n1 < NIN; ++n1) {
                     xin[n1] = O::from_io(uin[n1][j]);
                     if constexpr (G) xin[n1] = O::emul(xin[n1], win[n1][j]);
                 }
-                dft_half_in<P>(xin, A);
+                if constexpr (FULL) {
+#pragma unroll
+                    for (int n1 = 0; n1 < P; ++n1) A[n1] = xin[n1];
+                    dft_small<P, false>(A);
+                } else {
+                    dft_half_in<P>(xin, A);
+                }
                 V[0][j] = O::to_h2(A[0]);
                 V[1][j] = O::to_h2(O::mul(A[HALF], two[HALF - 1][j]));
 #pragma unroll
@@ -352,11 +365,11 @@ __global__ void __launch_bounds__(WideShape<P>::T, 2) wide_kernel(WideParams prm
                 __builtin_amdgcn_sched_barrier(0);
             }
         } else {
-            uint32_t vin[G ? HALF : 1][CPT];   // output gate (gated only)
+            uint32_t vin[G ? NIN : 1][CPT];   // output gate (gated only)
             if constexpr (G) {
-                const uint32_t* vr = (const uint32_t*)prm.v + mrow * (M / 2);
+                const uint32_t* vr = (const uint32_t*)prm.v + mrow * ROWW;
 #pragma unroll
-                for (int n1 = 0; n1 < HALF; ++n1)
+                for (int n1 = 0; n1 < NIN; ++n1)
 #pragma unroll
                     for (int j = 0; j < CPT; ++j)
                         vin[n1][j] = __builtin_nontemporal_load(&vr[n1 * Q + lofs + 32 * j]);
@@ -380,14 +393,14 @@ __global__ void __launch_bounds__(WideShape<P>::T, 2) wide_kernel(WideParams prm
                     }
                 }
             }
-            uint32_t* yrow = (uint32_t*)prm.y + mrow * (M / 2);
+            uint32_t* yrow = (uint32_t*)prm.y + mrow * ROWW;
             uint32_t two[HALF][CPT];
             load_two(two);
 #pragma unroll
             for (int j = 0; j < CPT; ++j) {
                 typedef Outer<IO> O;
                 typedef typename O::V C;
-                C Bv[P], zo[HALF];
+                C Bv[P], zo[NIN];
                 Bv[0] = O::from_h2(R[0][j]);
                 Bv[HALF] = O::mulc(O::from_h2(R[1][j]), two[HALF - 1][j]);
 #pragma unroll
@@ -395,9 +408,15 @@ __global__ void __launch_bounds__(WideShape<P>::T, 2) wide_kernel(WideParams prm
                     Bv[k1] = O::mulc(O::from_h2(R[2 * k1][j]), two[k1 - 1][j]);
                     Bv[P - k1] = cnj(O::mulc(O::from_h2(R[2 * k1 + 1][j]), two[k1 - 1][j]));
                 }
-                idft_half_out<P>(Bv, zo);
+                if constexpr (FULL) {
+                    dft_small<P, true>(Bv);
 #pragma unroll
-                for (int n1 = 0; n1 < HALF; ++n1) {
+                    for (int n1 = 0; n1 < P; ++n1) zo[n1] = Bv[n1];
+                } else {
+                    idft_half_out<P>(Bv, zo);
+                }
+#pragma unroll
+                for (int n1 = 0; n1 < NIN; ++n1) {
                     if constexpr (G) zo[n1] = O::emul(zo[n1], vin[n1][j]);
                     __builtin_nontemporal_store(O::to_io(zo[n1]), &yrow[n1 * Q + lofs + 32 * j]);
                 }
@@ -417,30 +436,30 @@ hipError_t launch_claim_reset(uint32_t* ctr, hipStream_t s) {
     return hipGetLastError();
 }
 
-template <bool G, bool SK>
+template <bool G, bool SK, bool FULL>
 static hipError_t launch_wide_g(int io, int P, const WideParams& p, int lds, hipStream_t s) {
     const dim3 grid((unsigned)p.grid), blk((unsigned)(P >= 16 ? 512 : 32 * P));
-#define FFTCONV_WIDE(IOT, PP)                                                              \
-    do {                                                                                   \
-        if (lds > 64 * 1024) {                                                             \
-            hipError_t e_ = hipFuncSetAttribute((const void*)wide_kernel<IOT, PP, G, SK>,  \
-                                                hipFuncAttributeMaxDynamicSharedMemorySize, \
-                                                lds);                                      \
-            if (e_ != hipSuccess) return e_;                                               \
-        }                                                                                  \
-        hipLaunchKernelGGL((wide_kernel<IOT, PP, G, SK>), grid, blk, lds, s, p);           \
+#define FFTCONV_WIDE(IOT, PP)                                                                  \
+    do {                                                                                       \
+        if (lds > 64 * 1024) {                                                                 \
+            hipError_t e_ = hipFuncSetAttribute((const void*)wide_kernel<IOT, PP, G, SK, FULL>, \
+                                                hipFuncAttributeMaxDynamicSharedMemorySize,     \
+                                                lds);                                          \
+            if (e_ != hipSuccess) return e_;                                                   \
+        }                                                                                      \
+        hipLaunchKernelGGL((wide_kernel<IOT, PP, G, SK, FULL>), grid, blk, lds, s, p);         \
     } while (0)
     if (io == IO_BF16) {
         if (P == 4) FFTCONV_WIDE(IO_BF16, 4);
         else if (P == 8) FFTCONV_WIDE(IO_BF16, 8);
         else if (P == 16) FFTCONV_WIDE(IO_BF16, 16);
-        else if (P == 32) FFTCONV_WIDE(IO_BF16, 32);
+        else if (P == 32 && !FULL) FFTCONV_WIDE(IO_BF16, 32 - 16 * FULL);
         else return hipErrorInvalidValue;
     } else {
         if (P == 4) FFTCONV_WIDE(IO_F16, 4);
         else if (P == 8) FFTCONV_WIDE(IO_F16, 8);
         else if (P == 16) FFTCONV_WIDE(IO_F16, 16);
-        else if (P == 32) FFTCONV_WIDE(IO_F16, 32);
+        else if (P == 32 && !FULL) FFTCONV_WIDE(IO_F16, 32 - 16 * FULL);
         else return hipErrorInvalidValue;
     }
 #undef FFTCONV_WIDE
@@ -448,9 +467,15 @@ static hipError_t launch_wide_g(int io, int P, const WideParams& p, int lds, hip
 }
 
 hipError_t launch_wide(int io, int P, const WideParams& p, int lds, hipStream_t s) {
-    if (p.w) return launch_wide_g<true, false>(io, P, p, lds, s);
-    if (p.skip_hi) return launch_wide_g<false, true>(io, P, p, lds, s);
-    return launch_wide_g<false, false>(io, P, p, lds, s);
+    if (p.full) {
+        // FFT-size rows: P <= 16, no band limit or digit blocks
+        if (p.skip_hi || P > 16 || p.pairs != P / 2) return hipErrorInvalidValue;
+        return p.w ? launch_wide_g<true, false, true>(io, P, p, lds, s)
+                   : launch_wide_g<false, false, true>(io, P, p, lds, s);
+    }
+    if (p.w) return launch_wide_g<true, false, false>(io, P, p, lds, s);
+    if (p.skip_hi) return launch_wide_g<false, true, false>(io, P, p, lds, s);
+    return launch_wide_g<false, false, false>(io, P, p, lds, s);
 }
 
 // Spectrum coefficients in the wide kernel's engine order:

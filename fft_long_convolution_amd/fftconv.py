@@ -35,7 +35,8 @@ class PlanInfo(ctypes.Structure):
                 ("workspace_bytes_per_row", ctypes.c_size_t),
                 ("mfma_flops_per_row", ctypes.c_double),
                 ("kernel_variant", ctypes.c_int),
-                ("sparse_outer", ctypes.c_int)]
+                ("sparse_outer", ctypes.c_int),
+                ("circular", ctypes.c_int)]
 
     def as_dict(self) -> dict:
         return {"N": self.N, "M": self.M, "order": self.order,
@@ -47,6 +48,7 @@ class PlanInfo(ctypes.Structure):
                 "workspace_bytes_per_row": self.workspace_bytes_per_row,
                 "mfma_flops_per_row": self.mfma_flops_per_row,
                 "sparse_outer": self.sparse_outer,
+                "circular": bool(self.circular),
                 "kernel": {0: "fused_kernel", 1: "row_kernel", 3: "wide_kernel",
                            # one outer level: per-column passes; two: both
                            # levels in one column pass each way (on the
@@ -79,6 +81,10 @@ def lib() -> ctypes.CDLL:
         L.fftconv_plan.restype = i
         L.fftconv_plan_query.argtypes = [sz, i, i, ctypes.POINTER(PlanInfo)]
         L.fftconv_plan_query.restype = i
+        L.fftconv_plan_circular.argtypes = [sz, i, i, ctypes.POINTER(vp)]
+        L.fftconv_plan_circular.restype = i
+        L.fftconv_plan_circular_query.argtypes = [sz, i, i, ctypes.POINTER(PlanInfo)]
+        L.fftconv_plan_circular_query.restype = i
         L.fftconv_plan_estimate.argtypes = [sz, i, i, i, sz, sz, ctypes.POINTER(Estimate)]
         L.fftconv_plan_estimate.restype = i
         L.fftconv_plan_get_info.argtypes = [vp, ctypes.POINTER(PlanInfo)]
@@ -124,12 +130,14 @@ def lib() -> ctypes.CDLL:
     return _lib
 
 
-def plan_query(N: int, p: int = 0, dtype: str = "bf16") -> dict:
-    """What fftconv_plan(N, p, dtype) would build (no device needed)."""
+def plan_query(N: int, p: int = 0, dtype: str = "bf16", circular: bool = False) -> dict:
+    """What fftconv_plan(N, p, dtype) -- or, circular=True,
+    fftconv_plan_circular -- would build (no device needed)."""
     info = PlanInfo()
-    st = lib().fftconv_plan_query(N, p, DTYPES[dtype], ctypes.byref(info))
+    fn = lib().fftconv_plan_circular_query if circular else lib().fftconv_plan_query
+    st = fn(N, p, DTYPES[dtype], ctypes.byref(info))
     if st != 0:
-        raise FFTConvError(st, "fftconv_plan_query(N=%d, p=%d)" % (N, p))
+        raise FFTConvError(st, "plan query (N=%d, p=%d, circular=%s)" % (N, p, circular))
     return info.as_dict()
 
 
@@ -187,24 +195,29 @@ def _stream_handle(stream):
 
 
 class FFTConv:
-    """Causal FFT long convolution for one (N, order, dtype) plan.
+    """FFT long convolution for one (N, order, dtype) plan.
 
     >>> conv = FFTConv(1024, dtype="bf16")
     >>> k_f = conv.kernel_spectrum(k)          # k: [H, N] fp32, once
     >>> y = conv.forward(u, k_f)               # u: [B, H, N] bf16
+
+    circular=True builds the plan of the circular operators at FFT size N
+    (fftconv_plan_circular): kernel_spectrum then takes kind="circular" or
+    "circular_adjoint".
     """
 
-    def __init__(self, N: int, p: int = 0, dtype: str = "bf16"):
+    def __init__(self, N: int, p: int = 0, dtype: str = "bf16", circular: bool = False):
         if dtype not in DTYPES:
             raise ValueError("dtype must be one of %s" % list(DTYPES))
         import torch
         if not torch.cuda.is_available():
             raise RuntimeError("FFTConv needs a ROCm GPU")
-        self.N, self.dtype = N, dtype
+        self.N, self.dtype, self.circular = N, dtype, circular
         h = ctypes.c_void_p()
-        st = lib().fftconv_plan(N, p, DTYPES[dtype], ctypes.byref(h))
+        fn = lib().fftconv_plan_circular if circular else lib().fftconv_plan
+        st = fn(N, p, DTYPES[dtype], ctypes.byref(h))
         if st != 0:
-            raise FFTConvError(st, "fftconv_plan(N=%d, p=%d, %s)" % (N, p, dtype))
+            raise FFTConvError(st, "plan (N=%d, p=%d, %s, circular=%s)" % (N, p, dtype, circular))
         self._plan = h
         info = PlanInfo()
         lib().fftconv_plan_get_info(h, ctypes.byref(info))
@@ -292,11 +305,14 @@ class FFTConv:
             raise FFTConvError(st, "fftconv_forward_blocksparse")
         return out
 
-    def kernel_spectrum(self, k, out=None, stream=None, kind="causal"):
+    def kernel_spectrum(self, k, out=None, stream=None, kind=None):
         """k: [H, N] fp32 CUDA tensor -> opaque k_f (uint8 CUDA tensor).
         kind: "causal", "causal_adjoint", "circular" or "circular_adjoint"
-        (the operator fftconv_forward then computes)."""
+        (the operator fftconv_forward then computes); by default "causal",
+        or "circular" on a circular plan."""
         import torch
+        if kind is None:
+            kind = "circular" if self.circular else "causal"
         if k.dtype != torch.float32 or k.dim() != 2 or k.shape[1] != self.N:
             raise ValueError("k must be fp32 [H, %d]" % self.N)
         k = k.contiguous()

@@ -62,7 +62,8 @@ typedef struct fftconv_plan_s *fftconv_plan_t;
 /* Description of what a plan does (filled without touching the device). */
 typedef struct fftconv_plan_info {
     size_t N;                 /* sequence length                            */
-    size_t M;                 /* packed complex transform length (= N)     */
+    size_t M;                 /* packed complex transform length (N; N/2
+                                 on a plan of fftconv_plan_circular)       */
     int order;                /* number of Monarch factors p                */
     int factors[8];           /* N_1 (outermost, sees the zero half) ...    */
     int path;                 /* 0 = fused (one launch per call),
@@ -83,8 +84,10 @@ typedef struct fftconv_plan_info {
                                      (N >= 32K, 16-bit I/O)                */
     int sparse_outer;         /* outer factor P of the digit-block sparsity
                                  (fftconv_forward_blocksparse): P of the
-                                 wide kernel, N/4096 on the multi-pass path,
+                                 wide kernel, M/4096 on the multi-pass path,
                                  1 otherwise                                */
+    int circular;             /* 1: a plan of fftconv_plan_circular (FFT
+                                 size N, M = N/2, circular kinds only)     */
 } fftconv_plan_info;
 
 /* Predicted cost of one forward call (an MI355X analogue of the page's cost
@@ -138,6 +141,36 @@ fftconv_status fftconv_plan_estimate(size_t N, int p, fftconv_dtype dtype, int l
 fftconv_status fftconv_plan(size_t N, int p, fftconv_dtype dtype,
                             fftconv_plan_t *out);
 
+/* Plan for the circular (non-causal) operators at FFT size N (page
+ * "FlashFFTConv: Efficient Convolutions for Long Sequences with Tensor
+ * Cores", section 5, "Convolution Micro-Benchmarks": the standard
+ * convolutions of its Tables 3 and 4 transform the input at its own length
+ * N, while the causal ones of Tables 13 and 14 pad it to twice that; the
+ * real-valued FFT of section 3.4, "Domain-Specific Optimizations", packs the
+ * N real points into M = N/2 complex ones).  The forward kernels of such a
+ * plan load and store every packed point (none is padding) and run the
+ * M-point transform: half the transform length of the 2N-point route that
+ * fftconv_plan takes for the same kinds.
+ *  N: a power of two in [512, 4194304]; M = N/2 picks the kernel family
+ *     and factorisation exactly as fftconv_plan does for a transform of M
+ *     points (p = 0: the family's own factors; p >= 2: exactly p factors
+ *     of M, as there).
+ * On such a plan fftconv_kernel_spectrum_kind accepts FFTCONV_CIRCULAR and
+ * FFTCONV_CIRCULAR_ADJOINT (the causal kinds, fftconv_kernel_spectrum, the
+ * band-limited and digit-block calls return FFTCONV_ERR_UNSUPPORTED);
+ * fftconv_forward, fftconv_forward_noalloc and fftconv_forward_gated work
+ * as on any plan; fftconv_backward returns FFTCONV_ERR_UNSUPPORTED (the
+ * input gradient of a circular convolution is fftconv_forward with the
+ * FFTCONV_CIRCULAR_ADJOINT spectrum; no kernel gradient is provided).
+ * Errors and ownership as fftconv_plan. */
+fftconv_status fftconv_plan_circular(size_t N, int p, fftconv_dtype dtype,
+                                     fftconv_plan_t *out);
+
+/* Describe the plan fftconv_plan_circular(N, p, dtype) would build,
+ * without touching the device. */
+fftconv_status fftconv_plan_circular_query(size_t N, int p, fftconv_dtype dtype,
+                                           fftconv_plan_info *info);
+
 /* Describe the plan fftconv_plan(N, p, dtype) would build, without
  * allocating anything on the device. */
 fftconv_status fftconv_plan_query(size_t N, int p, fftconv_dtype dtype,
@@ -188,10 +221,12 @@ fftconv_status fftconv_kernel_spectrum(fftconv_plan_t plan, const float *k,
  *                             (the transpose: du from dy)
  *   FFTCONV_CIRCULAR          y[t] = sum_s u[s] k[(t-s) mod N]
  *   FFTCONV_CIRCULAR_ADJOINT  y[s] = sum_t u[t] k[(t-s) mod N]
- * Every kind runs the same kernels at the same cost: each is the first N
- * outputs of a 2N-point circular convolution of the zero-padded input with
- * a 2N-periodic kernel built from k (k followed by zeros; k[0] and the
- * reversed taps; k twice; k reversed twice). */
+ * On a plan of fftconv_plan every kind runs the same kernels at the same
+ * cost: each is the first N outputs of a 2N-point circular convolution of
+ * the zero-padded input with a 2N-periodic kernel built from k (k followed
+ * by zeros; k[0] and the reversed taps; k twice; k reversed twice).  A plan
+ * of fftconv_plan_circular computes the two circular kinds at FFT size N
+ * (the N-periodic kernel k, or k reversed). */
 typedef enum fftconv_kernel_kind {
     FFTCONV_CAUSAL = 0,
     FFTCONV_CAUSAL_ADJOINT = 1,

@@ -155,3 +155,45 @@ def oracle_backward(w: inputs.Workload, u, dy, k):
         du = oracle.op_fft(dy64, k64, "causal_adjoint", hidx)
         dk = oracle.kgrad_fft(u64, dy64, w.H, "causal", hidx)
     return du, dk
+
+
+def run_gpu_circular(w: inputs.Workload, kind: str = "circular", conv=None, gated: bool = False,
+                     p: int = 0):
+    """GPU result of a plan at FFT size N (fftconv_plan_circular) for all
+    rows of w, operator ``kind`` (circular or circular_adjoint), as fp64;
+    gated: v * op(u * w)."""
+    import torch
+    from fft_long_convolution_amd.fftconv import FFTConv
+    if conv is None:
+        conv = FFTConv(w.N, p=p, dtype=w.dtype, circular=True)
+    u = inputs.input_rows(w)
+    k = inputs.kernel_rows(w)
+    kf = conv.kernel_spectrum(torch.from_numpy(k).cuda(), kind=kind)
+    ins = (u,)
+    if gated:
+        ins = (u, inputs.gate_rows(w, "w"), inputs.gate_rows(w, "v"))
+        dev = [to_torch(a, w.dtype).view(w.B, w.H, w.N) for a in ins]
+        y = conv.forward_gated(dev[0], dev[1], dev[2], kf)
+    else:
+        y = conv.forward(to_torch(u, w.dtype).view(w.B, w.H, w.N), kf)
+    torch.cuda.synchronize()
+    y64 = oracle.to_f64(from_torch(y, w.dtype).reshape(w.rows, w.N), w.dtype)
+    return y64, ins, k
+
+
+def oracle_circular(w: inputs.Workload, ins, k, kind: str = "circular"):
+    """fp64 oracle of the same rows: the operator by its definition (small
+    N) or the oracle's FFT route; with three inputs the gated form."""
+    u64 = oracle.to_f64(ins[0], w.dtype).reshape(w.rows, w.N)
+    k64 = k.astype(np.float64)
+    hidx = np.arange(w.rows) % w.H
+    if len(ins) == 3:
+        g = [oracle.to_f64(a, w.dtype).reshape(w.rows, w.N) for a in ins[1:]]
+        u64 = u64 * g[0]
+    if w.N <= 512:
+        ref = oracle.op_direct(u64, k64, kind, hidx)
+    else:
+        ref = oracle.op_fft(u64, k64, kind, hidx)
+    if len(ins) == 3:
+        ref = g[1] * ref
+    return ref

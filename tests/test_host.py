@@ -219,3 +219,45 @@ def test_cost_model_terms():
                 continue
             with pytest.raises(fc.FFTConvError):
                 fc.plan_estimate(N, p, "bf16")
+
+
+@pytest.mark.parametrize("lg", range(9, 23))
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
+def test_circular_plan_query(lg, dtype):
+    # plans at FFT size N: an M = N/2 transform with every factor whole (no
+    # zero half), the kernel family of that M, spectra and workspace sized
+    # by M
+    N = 1 << lg
+    info = fc.plan_query(N, 0, dtype, circular=True)
+    M = N // 2
+    assert info["circular"] and info["N"] == N and info["M"] == M
+    prod = 1
+    for f in info["factors"]:
+        prod *= f
+    assert prod == M
+    entry = 16 if dtype == "f32" else 8
+    assert info["spectrum_bytes_per_channel"] == M * entry
+    f = info["factors"]
+    assert info["mfma_flops_per_row"] == pytest.approx(16.0 * M * sum(f))
+    causal = fc.plan_query(M, 0, dtype) if M >= 256 else None
+    if causal is not None and not (M == 32768 and dtype != "f32"):
+        # the same family and factors as the causal plan of length M
+        assert f == causal["factors"]
+        assert info["kernel"] == causal["kernel"]
+    if M == 32768 and dtype != "f32":
+        # the 32 x 32 x 32 wide kernel exists for the causal half only: M =
+        # 32K runs the 16-bit multi-pass kernels
+        assert info["path"] == "multipass" and f == [8, 4, 32, 32]
+
+
+def test_circular_plan_limits():
+    for N in (256, 128, 1000, 1 << 23):
+        with pytest.raises(fc.FFTConvError) as e:
+            fc.plan_query(N, 0, "bf16", circular=True)
+        assert e.value.status == 2
+    assert fc.plan_query(4096, 3, "bf16", circular=True)["factors"] == [8, 16, 16]
+    with pytest.raises(fc.FFTConvError):
+        fc.plan_query(1024, 5, "bf16", circular=True)
+    L = fc.lib()
+    assert L.fftconv_plan_circular_query(1024, 0, 2, None) == 1
+    assert L.fftconv_plan_circular(1024, 0, 2, None) == 1
