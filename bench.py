@@ -573,13 +573,25 @@ def _csv_rows(root: str, suffix: str):
     return rows
 
 
-def _counters(root: str, pred) -> dict:
+def _kernel_short(name: str) -> str:
+    import re
+    m = re.search(r"fftconv::(\w+)", name)
+    return m.group(1) if m else name
+
+
+def _counters(root: str, pred, by_kernel=None) -> dict:
+    """Counter totals over the kernels `pred` accepts; with a dict
+    `by_kernel`, also the totals per kernel (short name) added into it."""
     tot = {}
     for r in _csv_rows(root, "counter_collection.csv"):
         if not pred(r.get("Kernel_Name", "")):
             continue
         n = r["Counter_Name"]
-        tot[n] = tot.get(n, 0.0) + float(r["Counter_Value"])
+        v = float(r["Counter_Value"])
+        tot[n] = tot.get(n, 0.0) + v
+        if by_kernel is not None:
+            d = by_kernel.setdefault(_kernel_short(r["Kernel_Name"]), {})
+            d[n] = d.get(n, 0.0) + v
     return tot
 
 
@@ -605,11 +617,12 @@ def profile(args):
     trace_ns = sum(float(r["TotalDurationNs"]) for r in stats) / calls
     # 2. counters on short runs, and on the calibration copy
     pmc = {}
+    per_k = {}
     for i, group in enumerate(PMC_PASSES):
         d = os.path.join(out, "pmc%d" % i)
         _run(["rocprofv3", "--pmc"] + group + ["--output-format", "csv", "-d", d, "-o", "pmc", "--"]
              + me + short, d + ".log")
-        for k, v in _counters(d, _is_call_kernel).items():
+        for k, v in _counters(d, _is_call_kernel, per_k).items():
             pmc[k] = v / calls_short
     cal = {}
     for c in ("FETCH_SIZE", "WRITE_SIZE"):
@@ -666,6 +679,26 @@ def profile(args):
               "| scale factor (true bytes / counter) | %.4f | %.4f |" % (f_scale, w_scale),
               "| one call | %.1f | %.1f |" % (pmc["FETCH_SIZE"], pmc["WRITE_SIZE"]), "",
               "HBM traffic per call %d B vs algorithmic %d B: ratio %.3f." % (traffic, alg, traffic / alg), ""]
+    if len(per_k) > 1:
+        # the same counters kernel by kernel (per call), with each kernel's
+        # HBM bytes and rate over its traced time per call
+        ks = sorted(per_k)
+        tper = {_kernel_short(r["Name"]): float(r["TotalDurationNs"]) / calls for r in stats}
+        lines += ["Per kernel (per call):", "",
+                  "| counter | " + " | ".join("`%s`" % k for k in ks) + " |",
+                  "|---|" + "---|" * len(ks)]
+        for c in sorted({c for k in ks for c in per_k[k]}):
+            lines.append("| %s | " % c + " | ".join("%.6g" % (per_k[k].get(c, 0.0) / calls_short)
+                                                  for k in ks) + " |")
+        hb = {k: (per_k[k].get("FETCH_SIZE", 0.0) * f_scale + per_k[k].get("WRITE_SIZE", 0.0) * w_scale)
+              * 1024.0 / calls_short for k in ks}
+        lines.append("| HBM bytes (scaled) | " + " | ".join("%.4g" % hb[k] for k in ks) + " |")
+        lines.append("| traced us per call | " + " | ".join("%.2f" % (tper.get(k, 0.0) / 1e3) for k in ks) + " |")
+        lines.append("| HBM TB/s | " + " | ".join(
+            "%.2f" % (hb[k] / (tper[k] * 1e-9) / 1e12 if tper.get(k) else 0.0) for k in ks) + " |")
+        lines.append("| vector instructions per row | " + " | ".join(
+            "%.1f" % (per_k[k].get("SQ_INSTS_VALU", 0.0) / calls_short / rows) for k in ks) + " |")
+        lines.append("")
     if gui > 0:
         lines += ["Derived (GRBM_GUI_ACTIVE = %.0f cycles per call per XCD, %d SIMDs):" % (gui, simd), "",
                   "* matrix cores busy: %.1f%% of SIMD cycles (SQ_VALU_MFMA_BUSY_CYCLES)" % (

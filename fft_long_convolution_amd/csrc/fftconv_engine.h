@@ -280,14 +280,25 @@ __device__ __forceinline__ int eng_addr(int na, int it, int x) {
 // which then stay in that XCD's L2 -- and its workgroups claim them in
 // order from their own counter (ctr[32 x], a 128-byte line each).  A
 // workgroup that the CU's arbitration favours simply claims more.
+// With no counters (c == nullptr) the claims are static: the workgroup at
+// position p of its group takes the group's indices p, p + G/8, p + 2 G/8,
+// ... (the same order, without atomics or counters to clear).
 struct XcdClaim {
     uint32_t* ctr;
     int G, gx, x;
+    mutable uint32_t ks;   // static claims: the next one of this workgroup
     __device__ __forceinline__ XcdClaim(uint32_t* c, int grid, int bid)
-        : ctr(c + 32 * (bid & 7)), G(grid), gx(grid >> 3), x(bid & 7) {}
+        : ctr(c ? c + 32 * (bid & 7) : nullptr), G(grid), gx(grid >> 3), x(bid & 7),
+          ks((uint32_t)(bid >> 3)) {}
     // next index of this group (monotonic; >= total means done)
     __device__ __forceinline__ long long next() const {
-        const uint32_t k = atomicAdd(ctr, 1u);
+        uint32_t k;
+        if (ctr) {
+            k = atomicAdd(ctr, 1u);
+        } else {
+            k = ks;
+            ks += (uint32_t)gx;
+        }
         return (long long)(k / gx) * G + (long long)x * gx + (k % gx);
     }
 };

@@ -1392,8 +1392,6 @@ size_t mp_chunk_channels(const Shape& s, size_t B, size_t H, size_t cap = kMpChu
 // `cap` (fftconv_workspace_bytes with the default bound).
 size_t forward_workspace_bytes(const fftconv_plan_s* plan, size_t B, size_t H,
                                size_t cap = kMpChunkBytes) {
-    // wide kernel: the row-claim counters only
-    if (plan->s.wide_P) return kClaimBytes;
     if (plan->s.path == 0) return 0;
     // multi-pass: one channel chunk of f16 complex rows, then the counters
     if (plan->s.mp_P1)
@@ -1873,9 +1871,11 @@ fftconv_status forward_impl(fftconv_plan_t plan, const void* u, const void* w,
         W.v = v;
         W.skip_hi = skip_hi;
         W.pairs = outer_keep > 0 && outer_keep < s.wide_P / 2 ? outer_keep : s.wide_P / 2;
-        W.ctr = (uint32_t*)workspace;
-        e = launch_claim_reset(W.ctr, st);
-        if (e == hipSuccess) e = launch_wide(io, s.wide_P, W, plan->lds_wide, st);
+        // static row claims (no counters: measured as fast as claiming
+        // from per-XCD counters at the workload sizes, and faster for small
+        // calls, which no longer pay a counter-clearing launch)
+        W.ctr = nullptr;
+        e = launch_wide(io, s.wide_P, W, plan->lds_wide, st);
     } else if (s.path == 0) {
         FwdParams P = plan->fused;
         P.rows = (long long)rows;

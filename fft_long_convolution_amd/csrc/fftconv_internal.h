@@ -211,12 +211,11 @@ constexpr size_t kClaimBytes = kClaimWords * 4;
 // (fftconv_scratch.hip): its device address on `device` (which must be the
 // current device; looked up once per device) and its size in bytes.
 hipError_t scratch_buffer(int device, void** ptr, size_t* bytes);
-hipError_t launch_claim_reset(uint32_t* ctr, hipStream_t s);
 
 struct WideParams {
     int B, H, N;
     int grid;                // persistent workgroups, a multiple of 8
-    uint32_t* ctr;           // claim counters (workspace, cleared per call)
+    uint32_t* ctr;           // claim counters, or null: static claims
     const void* u;
     void* y;
     const void* w;           // input gate (layout of u) or null

@@ -81,9 +81,10 @@ __global__ void __launch_bounds__(WideShape<P>::T, 2) wide_kernel(WideParams prm
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int g = lane >> 4, x = lane & 15;
     const int total = prm.B * prm.H;
-    // Rows are taken in channel-major order (index h * B + b), claimed one
-    // row ahead by thread 0 from the counters of this workgroup's XCD group
-    // and published through LDS at the row's barriers.
+    // Rows are taken in channel-major order (index h * B + b), in the order
+    // of this workgroup's XCD group (with counters: claimed from them; the
+    // library passes none: each workgroup takes its fixed share), one row
+    // ahead by thread 0 and published through LDS at the row's barriers.
     const XcdClaim claimer(prm.ctr, gridDim.x, blockIdx.x);
 
     for (int i = tid; i < 8 * 64; i += T) {
@@ -425,15 +426,6 @@ __global__ void __launch_bounds__(WideShape<P>::T, 2) wide_kernel(WideParams prm
         cur = nxt;
         nxt = nn;
     }
-}
-
-// Clears the row-claim counters of one call (a kernel rather than a memset,
-// so the call can be captured in a graph).
-__global__ void claim_reset_kernel(uint32_t* ctr) { ctr[threadIdx.x] = 0u; }
-
-hipError_t launch_claim_reset(uint32_t* ctr, hipStream_t s) {
-    hipLaunchKernelGGL(claim_reset_kernel, dim3(1), dim3(kClaimWords), 0, s, ctr);
-    return hipGetLastError();
 }
 
 template <bool G, bool SK, bool FULL>

@@ -187,8 +187,8 @@ void fftconv_plan_destroy(fftconv_plan_t plan);
 size_t fftconv_spectrum_bytes(fftconv_plan_t plan, size_t H);
 
 /* Bytes of the workspace fftconv_forward needs for B x H rows; the caller
- * allocates it.  0 for the row and LDS-staged fused kernels; 1 KB of work
- * counters for the one-workgroup-per-row kernel; for the 16-bit multi-pass
+ * allocates it.  0 for the fused kernels (row, one-workgroup-per-row and
+ * LDS-staged); for the 16-bit multi-pass
  * path one channel chunk of f16 complex rows (at most 1 GB unless a single
  * channel is larger) plus the counters; B*H rows of fp32 complex for the
  * fp32 multi-pass path.  A call owns its workspace until it completes: two
