@@ -109,6 +109,15 @@ def parse():
     return ap.parse_args()
 
 
+def kf_min_bytes(info: dict, H: int) -> int:
+    """The kernel spectrum at its information content: a real kernel's
+    spectrum of length L = 2M is Hermitian, so M + 1 complex bins per
+    channel carry it (f16 complex for 16-bit plans, fp32 complex for fp32
+    plans).  The plans store 8 (16) B per bin, twice that, as per-bin
+    coefficients; the roofline counts the minimum."""
+    return H * (info["M"] + 1) * (8 if info["dtype"] == "f32" else 4)
+
+
 def to_torch(a, dtype, torch):
     if dtype == "bf16":
         return torch.from_numpy(a.view(np.int16).copy()).view(torch.bfloat16)
@@ -267,7 +276,7 @@ def main():
     # average agrees up to the gaps between launches).  Individually
     # bracketed launches (ms_median_single_launch) also carry the events' own
     # overhead.
-    kf_bytes = conv.spectrum_bytes(w.H)
+    kf_bytes = kf_min_bytes(info, w.H)
     alg_bytes = nstream * w.rows * w.N * esz + kf_bytes
     if op == "backward":
         alg_bytes += w.H * w.N * 4
@@ -291,6 +300,7 @@ def main():
     roof["traffic"] = measured_traffic(w.name + ("" if op == "plain" else "_" + op))
     roof["kernel"] = info["kernel"] + ("+kgrad" if op == "backward" else "")
     roof["algorithmic_bytes"] = int(alg_bytes)
+    roof["kf_stored_bytes"] = int(conv.spectrum_bytes(w.H))
     roof["mfma_flops"] = float(flops)
     roof["mfma_frac"] = round(achieved_tf / MFMA_PEAK_TFLOPS[w.dtype], 4)
     roof["launch_ms"] = round(ms_kernel, 5)
@@ -495,7 +505,7 @@ def time_workload(name: str, torch, dev, kind: str = "causal") -> dict:
     steps = max(20, int(math.ceil(500.0 / est)))
     ms = region(steps)
     esz = 4 if w.dtype == "f32" else 2
-    alg = 2 * w.rows * w.N * esz + conv.spectrum_bytes(w.H)
+    alg = 2 * w.rows * w.N * esz + kf_min_bytes(conv.info, w.H)
     gbs = alg / (ms * 1e-3) / 1e9
     out = {"ms_per_step": round(ms, 5), "steps": steps,
            "outputs_per_s": round(w.rows * w.N / (ms * 1e-3), 1),
@@ -601,7 +611,7 @@ def profile(args):
     w = inputs.WORKLOADS[args.workload]
     flags, op = _op_flags(args)
     tag = w.name + ("" if op == "plain" else "_" + op)
-    info = plan_query(w.N, 0, w.dtype)
+    info = plan_query(w.N, 0, w.dtype, circular=(op == "circular"))
     out = os.path.join(os.path.abspath(args.profile_dir), tag)
     os.makedirs(out, exist_ok=True)
     me = [sys.executable, os.path.abspath(__file__), "--workload", w.name, "--no-extra"] + flags
@@ -683,7 +693,10 @@ def profile(args):
         # the same counters kernel by kernel (per call), with each kernel's
         # HBM bytes and rate over its traced time per call
         ks = sorted(per_k)
-        tper = {_kernel_short(r["Name"]): float(r["TotalDurationNs"]) / calls for r in stats}
+        tper = {}
+        for r in stats:
+            k = _kernel_short(r["Name"])
+            tper[k] = tper.get(k, 0.0) + float(r["TotalDurationNs"]) / calls
         lines += ["Per kernel (per call):", "",
                   "| counter | " + " | ".join("`%s`" % k for k in ks) + " |",
                   "|---|" + "---|" * len(ks)]

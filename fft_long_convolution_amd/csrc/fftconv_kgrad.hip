@@ -309,13 +309,12 @@ __global__ void __launch_bounds__(64 * kKgWaves, 1) kgrad_row_kernel(KgRowParams
 
 template <int IO>
 __global__ void __launch_bounds__(64 * kKgWaves, 1) kgrad_row_inv_kernel(KgRowParams P) {
-    constexpr int NB = 32, MT2 = 4, KS2 = 2, NT = 2, IT = 2;
+    constexpr int MT2 = 4, KS2 = 2, NT = 2, IT = 2;
     extern __shared__ uint4 s_lds[];
     uint4* s_i2b = s_lds;                       // [KS2][2 NT][64]
     uint4* s_i1a = s_i2b + KS2 * 2 * NT * 64;   // [4][64]
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int g = lane >> 4, x = lane & 15;
     constexpr int TH = 64 * kKgWaves;
     for (int i = tid; i < KS2 * 2 * NT * 64; i += TH) s_i2b[i] = ((const uint4*)P.i2b)[i];
     for (int i = tid; i < 4 * 64; i += TH) s_i1a[i] = ((const uint4*)P.i1a)[i];
