@@ -663,8 +663,8 @@ def profile(args):
         "as child processes, from /tmp with TMPDIR=/tmp; `<repo>` is the repository root)." % (
             w.name, (" " + " ".join(flags)) if flags else ""), "",
         "## Kernel trace", "", "```",
-        " ".join(tcmd).replace(os.path.dirname(os.path.abspath(__file__)), "<repo>")
-        .replace(out, "<out>"), "```", "",
+        " ".join(tcmd).replace(os.path.join(out, "trace"), "<out>/trace")
+        .replace(os.path.dirname(os.path.abspath(__file__)), "<repo>"), "```", "",
         "| kernel | calls | average ns | min ns | max ns |", "|---|---|---|---|---|"]
     for r in sorted(stats, key=lambda r: -float(r["TotalDurationNs"])):
         lines.append("| `%s` | %s | %.0f | %s | %s |" % (r["Name"], r["Calls"], float(r["AverageNs"]),
