@@ -901,6 +901,10 @@ fftconv_status spectrum_impl(fftconv_plan_t plan, const float* k, size_t H,
                              void* stream, int blk_a = 0, int blk_d = 0);
 constexpr size_t kMpChunkBytes = (size_t)1024 << 20;
 
+fftconv_status forward_check(fftconv_plan_t plan, const void* u, const void* w,
+                             const void* v, const void* k_f, void* y, size_t B,
+                             size_t H, size_t N, void* workspace,
+                             size_t workspace_bytes, size_t chunk_cap);
 fftconv_status forward_impl(fftconv_plan_t plan, const void* u, const void* w,
                             const void* v, const void* k_f, void* y, size_t B,
                             size_t H, size_t N, void* workspace,
@@ -908,7 +912,8 @@ fftconv_status forward_impl(fftconv_plan_t plan, const void* u, const void* w,
                             size_t chunk_cap, int outer_keep = 0);
 fftconv_status backward_dk(const fftconv_plan_s* plan, const void* u, const void* dy,
                            float* dk, size_t B, size_t H, size_t N, void* workspace,
-                           hipStream_t st);
+                           hipStream_t st, const void* k_f_adj = nullptr,
+                           void* du = nullptr);
 
 fftconv_status build_device_tables(fftconv_plan_s* pl) {
     const Shape& s = pl->s;
@@ -1364,6 +1369,66 @@ hipError_t mp_cols_fwd(const fftconv_plan_s* plan, int io, const void* src, void
     return launch_mp_col(io, s.mp_P1, 0, C, st);
 }
 
+// Both outer levels' pass parameters of one chunk, from its one-level
+// column-pass parameters: persistent workgroups, two per CU, a multiple of
+// 16 (the tile count is a multiple of 64).
+MpCol2Params mp_col2_params(const fftconv_plan_s* plan, const MpColParams& C) {
+    MpCol2Params D{};
+    D.rows = C.rows;
+    D.H = C.H;
+    D.h0 = C.h0;
+    D.hc = C.hc;
+    D.M = C.M;
+    D.tw1 = plan->mp_tw1;
+    D.tw2 = plan->mp_tw2;
+    D.u = C.u;
+    D.y = C.y;
+    D.w = C.w;
+    D.v = C.v;
+    D.ws = C.ws;
+    D.ctr = C.ctr;
+    D.full = C.full;
+    D.grid = (int)std::min<long long>(mp_col2_tiles(plan->s.mp_P2, D.rows),
+                                      std::max<long long>(16, (2LL * plan->num_cu) & ~15LL));
+    return D;
+}
+
+// Workgroups of the inner pass for `units` slab-pair units: two per CU, a
+// multiple of 8 (every XCD the same share), no more than the units need.
+int mp_inner_grid(const fftconv_plan_s* plan, long long units) {
+    long long G = 2LL * plan->num_cu;
+    G = G < 8 ? 8 : G & ~7LL;
+    const long long need = (units + 7) & ~7LL;
+    return (int)(G < need ? G : need);
+}
+
+// The rest of one multi-pass chunk once its workspace holds the forward
+// column passes' output: the inner pass (the spectrum product included),
+// the clearing of the units it skips, and the inverse column pass(es) into
+// the chunk's output rows.  C: the chunk's one-level column-pass parameters
+// (workspace, counters, output rows and gate).
+hipError_t mp_inner_inverse(const fftconv_plan_s* plan, int io, const MpInnerParams& I,
+                            const MpColParams& C, hipStream_t st) {
+    const Shape& s = plan->s;
+    hipError_t e = launch_mp_inner(io, I, plan->lds_mp, st);
+    if (e == hipSuccess)
+        e = launch_mp_zero_units(C.ws, C.rows, (int)s.M, I.Po, I.P1, I.P2, I.upr_active, st);
+    if (e != hipSuccess) return e;
+    if (s.mp_P2 > 1) {
+        const MpCol2Params D = mp_col2_params(plan, C);
+        if (plan->mp2m_ia1) {
+            MpCol2Params F = D;
+            F.a1 = plan->mp2m_ia1;
+            F.a2 = plan->mp2m_ia2;
+            F.tm = plan->mp2m_tm;
+            F.grid = (int)std::min<long long>(D.rows * 128, plan->num_cu);
+            return launch_mp_col2m_inv(io, F, st);
+        }
+        return launch_mp_col2(io, s.mp_P1, s.mp_P2, true, D, st);
+    }
+    return launch_mp_col(io, s.mp_P1, 3, C, st);
+}
+
 // Channels per chunk of the multi-pass path: the passes run chunk by chunk
 // to bound the workspace (B * hc * M f16 complex, at most 1 GB).  Every
 // chunk costs three launches with their ramp-up and tail; measured at
@@ -1686,11 +1751,12 @@ fftconv_status spectrum_impl(fftconv_plan_t plan, const float* k, size_t H,
 
 // Shared body of the plain and the gated forward call; w and v are both
 // null (plain) or both set (gated), which the callers guarantee.
-fftconv_status forward_impl(fftconv_plan_t plan, const void* u, const void* w,
-                            const void* v, const void* k_f, void* y, size_t B,
-                            size_t H, size_t N, void* workspace,
-                            size_t workspace_bytes, void* stream, int skip_hi,
-                            size_t chunk_cap, int outer_keep) {
+// Argument checks of a forward call (the plan's length, pointers,
+// alignment, aliasing, workspace size); FFTCONV_OK when the call may run.
+fftconv_status forward_check(fftconv_plan_t plan, const void* u, const void* w,
+                             const void* v, const void* k_f, void* y, size_t B,
+                             size_t H, size_t N, void* workspace,
+                             size_t workspace_bytes, size_t chunk_cap) {
     if (!plan) return FFTCONV_ERR_INVALID_ARG;
     const Shape& s = plan->s;
     if (N != s.N) return FFTCONV_ERR_INVALID_ARG;
@@ -1723,6 +1789,22 @@ fftconv_status forward_impl(fftconv_plan_t plan, const void* u, const void* w,
     int dev = -1;
     if (hipGetDevice(&dev) != hipSuccess) return FFTCONV_ERR_HIP;
     if (dev != plan->device) return FFTCONV_ERR_INVALID_ARG;
+    return FFTCONV_OK;
+}
+
+fftconv_status forward_impl(fftconv_plan_t plan, const void* u, const void* w,
+                            const void* v, const void* k_f, void* y, size_t B,
+                            size_t H, size_t N, void* workspace,
+                            size_t workspace_bytes, void* stream, int skip_hi,
+                            size_t chunk_cap, int outer_keep) {
+    const fftconv_status chk =
+        forward_check(plan, u, w, v, k_f, y, B, H, N, workspace, workspace_bytes, chunk_cap);
+    if (chk != FFTCONV_OK) return chk;
+    const Shape& s = plan->s;
+    const size_t rows = B * H;
+    if (rows == 0) return FFTCONV_OK;
+    const size_t esz = s.dtype == FFTCONV_F32 ? 4 : 2;
+    const size_t ws_need = forward_workspace_bytes(plan, B, H, chunk_cap);
     hipStream_t st = (hipStream_t)stream;
     const int io = (int)s.dtype;
     hipError_t e;
@@ -1761,9 +1843,6 @@ fftconv_status forward_impl(fftconv_plan_t plan, const void* u, const void* w,
         C1.ws = workspace;
         C1.ctr = (uint32_t*)((char*)workspace + (ws_need - kClaimBytes));
         C1.full = s.full ? 1 : 0;
-        MpColParams C2 = C1;
-        C2.S = 4096;
-        C2.tw = plan->mp_tw2;
         MpInnerParams I = plan->mp;
         I.skip_hi = skip_hi;
         I.upr_active = outer_keep > 0 && outer_keep < I.Po / 2 ? outer_keep : I.Po / 2;
@@ -1782,40 +1861,18 @@ fftconv_status forward_impl(fftconv_plan_t plan, const void* u, const void* w,
         for (size_t h0 = 0; h0 < H && e == hipSuccess; h0 += hc_max) {
             const size_t bcur = B - b0 < bc_max ? B - b0 : bc_max;
             const size_t hc = H - h0 < hc_max ? H - h0 : hc_max;
-            C1.u = C2.u = (const char*)u + b0 * row_bytes;
-            C1.y = C2.y = (char*)y + b0 * row_bytes;
-            C1.w = C2.w = w ? (const char*)w + b0 * row_bytes : nullptr;
-            C1.v = C2.v = v ? (const char*)v + b0 * row_bytes : nullptr;
+            C1.u = (const char*)u + b0 * row_bytes;
+            C1.y = (char*)y + b0 * row_bytes;
+            C1.w = w ? (const char*)w + b0 * row_bytes : nullptr;
+            C1.v = v ? (const char*)v + b0 * row_bytes : nullptr;
             I.B = (int)bcur;
-            C1.h0 = C2.h0 = I.h0 = (int)h0;
-            C1.hc = C2.hc = I.hc = (int)hc;
-            C1.rows = C2.rows = (long long)bcur * (long long)hc;
-            const long long units = C1.rows * I.upr_active;
-            long long G = 2LL * plan->num_cu;
-            G = G < 8 ? 8 : G & ~7LL;
-            const long long need = (units + 7) & ~7LL;
-            I.grid = (int)(G < need ? G : need);
+            C1.h0 = I.h0 = (int)h0;
+            C1.hc = I.hc = (int)hc;
+            C1.rows = (long long)bcur * (long long)hc;
+            I.grid = mp_inner_grid(plan, C1.rows * I.upr_active);
             if (s.mp_P2 > 1) {
                 // both outer levels in one pass each way
-                MpCol2Params D{};
-                D.rows = C1.rows;
-                D.H = C1.H;
-                D.h0 = C1.h0;
-                D.hc = C1.hc;
-                D.M = C1.M;
-                D.tw1 = C1.tw;
-                D.tw2 = C2.tw;
-                D.u = C1.u;
-                D.y = C1.y;
-                D.w = C1.w;
-                D.v = C1.v;
-                D.ws = workspace;
-                D.ctr = C1.ctr;
-                D.full = C1.full;
-                // persistent workgroups, two per CU, a multiple of 16 (the
-                // tile count is a multiple of 64)
-                D.grid = (int)std::min<long long>(mp_col2_tiles(s.mp_P2, D.rows),
-                                                  std::max<long long>(16, (2LL * plan->num_cu) & ~15LL));
+                const MpCol2Params D = mp_col2_params(plan, C1);
                 if (plan->mp2m_a1) {
                     // P1 = P2 = 32: the forward pass on the matrix cores,
                     // one workgroup per CU
@@ -1828,30 +1885,10 @@ fftconv_status forward_impl(fftconv_plan_t plan, const void* u, const void* w,
                 } else {
                     e = launch_mp_col2(io, s.mp_P1, s.mp_P2, false, D, st);
                 }
-                if (e == hipSuccess) e = launch_mp_inner(io, I, plan->lds_mp, st);
-                if (e == hipSuccess)
-                    e = launch_mp_zero_units(workspace, C1.rows, (int)s.M, I.Po, I.P1, I.P2,
-                                             I.upr_active, st);
-                if (e == hipSuccess) {
-                    if (plan->mp2m_ia1) {
-                        MpCol2Params F = D;
-                        F.a1 = plan->mp2m_ia1;
-                        F.a2 = plan->mp2m_ia2;
-                        F.tm = plan->mp2m_tm;
-                        F.grid = (int)std::min<long long>(D.rows * 128, plan->num_cu);
-                        e = launch_mp_col2m_inv(io, F, st);
-                    } else {
-                        e = launch_mp_col2(io, s.mp_P1, s.mp_P2, true, D, st);
-                    }
-                }
             } else {
                 e = launch_mp_col(io, s.mp_P1, 0, C1, st);
-                if (e == hipSuccess) e = launch_mp_inner(io, I, plan->lds_mp, st);
-                if (e == hipSuccess)
-                    e = launch_mp_zero_units(workspace, C1.rows, (int)s.M, I.Po, I.P1, I.P2,
-                                             I.upr_active, st);
-                if (e == hipSuccess) e = launch_mp_col(io, s.mp_P1, 3, C1, st);
             }
+            if (e == hipSuccess) e = mp_inner_inverse(plan, io, I, C1, st);
         }
     } else if (s.wide_P) {
         WideParams W = plan->wide;
@@ -2038,13 +2075,22 @@ fftconv_status fftconv_backward(fftconv_plan_t plan, const void* u,
     if (hipGetDevice(&dev) != hipSuccess) return FFTCONV_ERR_HIP;
     if (dev != plan->device) return FFTCONV_ERR_INVALID_ARG;
     hipStream_t st = (hipStream_t)stream;
+    // On the multi-pass engine both gradients start from the same forward
+    // column pass of dy: dk's gradient pass only reads it, so du's inner and
+    // inverse passes then run on that workspace in place of a second column
+    // pass of dy of their own.
+    const bool share_dy = du && dk && rows && !plan->kg && kgrad_on_mp(plan, B);
     // du = the adjoint operator applied to dy (the forward kernels with the
     // conjugate spectrum); validated like any forward call
     if (du) {
-        const fftconv_status fs = forward_impl(plan, dy, nullptr, nullptr, k_f_adj, du, B, H,
-                                               N, workspace, workspace_bytes, stream, 0,
-                                               kMpChunkBytes);
+        const fftconv_status fs =
+            share_dy ? forward_check(plan, dy, nullptr, nullptr, k_f_adj, du, B, H, N, workspace,
+                                     workspace_bytes, kMpChunkBytes)
+                     : forward_impl(plan, dy, nullptr, nullptr, k_f_adj, du, B, H, N, workspace,
+                                    workspace_bytes, stream, 0, kMpChunkBytes);
         if (fs != FFTCONV_OK) return fs;
+        if (share_dy && overlap(workspace, ws_need, k_f_adj, fftconv_spectrum_bytes(plan, H)))
+            return FFTCONV_ERR_INVALID_ARG;
     }
     if (!dk || H == 0) return FFTCONV_OK;
     if (rows == 0) {
@@ -2052,7 +2098,8 @@ fftconv_status fftconv_backward(fftconv_plan_t plan, const void* u,
         return launch_scale_f32(dk, (long long)(H * N), 0.f, st) == hipSuccess
                    ? FFTCONV_OK : FFTCONV_ERR_HIP;
     }
-    return backward_dk(plan->kg ? plan->kg : plan, u, dy, dk, B, H, N, workspace, st);
+    return backward_dk(plan->kg ? plan->kg : plan, u, dy, dk, B, H, N, workspace, st,
+                       share_dy ? k_f_adj : nullptr, share_dy ? du : nullptr);
 }
 
 }  // extern "C"
@@ -2061,9 +2108,11 @@ namespace {
 
 // dk of the causal convolution on the engine of `plan` (the caller's plan,
 // or the one it delegates the kernel gradient to); arguments validated.
+// With du set (multi-pass engine only), du = the adjoint spectrum k_f_adj
+// applied to dy is computed from the same column pass of dy.
 fftconv_status backward_dk(const fftconv_plan_s* plan, const void* u, const void* dy,
                            float* dk, size_t B, size_t H, size_t N, void* workspace,
-                           hipStream_t st) {
+                           hipStream_t st, const void* k_f_adj, void* du) {
     const Shape& s = plan->s;
     const size_t rows = B * H;
     const size_t esz = s.dtype == FFTCONV_F32 ? 4 : 2;
@@ -2120,6 +2169,8 @@ fftconv_status backward_dk(const fftconv_plan_s* plan, const void* u, const void
         uint32_t* ctr = (uint32_t*)(base + 2 * per + hcm * s.M * 4);
         const MpInnerParams& T = plan->mp;
         const size_t row_bytes = H * N * esz;
+        if (du && (long long)bcm * (long long)hcm * (T.Po / 2) > 0x7fffffffLL)
+            return FFTCONV_ERR_UNSUPPORTED;
         e = hipSuccess;
         for (size_t h0 = 0; h0 < H && e == hipSuccess; h0 += hcm)
         for (size_t b0 = 0; b0 < B && e == hipSuccess; b0 += bcm) {
@@ -2149,6 +2200,33 @@ fftconv_status backward_dk(const fftconv_plan_s* plan, const void* u, const void
                 // accumulated 4 Z_g in unitary units (as the row engine)
                 P.pre = 0.25f / sqrtf((float)s.M);
                 e = launch_kgrad_mp(io, P, st);
+            }
+            if (e == hipSuccess && du) {
+                // du: the forward call's inner and inverse passes on the
+                // transformed dy rows, which the gradient pass left intact
+                MpColParams C{};
+                C.rows = (long long)bc * (long long)hc;
+                C.H = (int)H;
+                C.h0 = (int)h0;
+                C.hc = (int)hc;
+                C.M = (int)s.M;
+                C.S = (int)(s.M / s.mp_P1);
+                C.tw = plan->mp_tw1;
+                C.y = (char*)du + b0 * row_bytes;
+                C.ws = wsd;
+                C.ctr = ctr;
+                MpInnerParams I = T;
+                I.skip_hi = 0;
+                I.upr_active = I.Po / 2;
+                I.B = (int)bc;
+                I.H = (int)H;
+                I.h0 = (int)h0;
+                I.hc = (int)hc;
+                I.ws = wsd;
+                I.ctr = ctr;
+                I.kf = k_f_adj;
+                I.grid = mp_inner_grid(plan, C.rows * I.upr_active);
+                e = mp_inner_inverse(plan, io, I, C, st);
             }
             if (e == hipSuccess) {
                 // inverse column passes of the channels' result rows into

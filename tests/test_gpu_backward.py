@@ -109,7 +109,48 @@ def test_backward_pieces_and_errors():
     assert L.fftconv_backward(conv2._plan, u2.data_ptr(), u2.data_ptr(), kfa2.data_ptr(),
                               du_in_ws.data_ptr(), dk2.data_ptr(), 1, 1, 32768,
                               ws2.data_ptr(), need, None) == 1
+    # where du runs from dk's workspace, an adjoint spectrum inside any part
+    # of that workspace is rejected too
+    conv3 = fc.FFTConv(65536, dtype="f16")
+    u3 = torch.randn(1, 1, 65536, device="cuda").half()
+    du3 = torch.empty_like(u3)
+    dk3 = torch.empty(1, 65536, device="cuda")
+    need3 = conv3.backward_workspace_bytes(1, 1)
+    ws3 = torch.empty(need3, dtype=torch.uint8, device="cuda")
+    kf_in_ws = ws3.data_ptr() + ((need3 - conv3.spectrum_bytes(1)) & ~255)
+    assert L.fftconv_backward(conv3._plan, u3.data_ptr(), u3.data_ptr(), kf_in_ws,
+                              du3.data_ptr(), dk3.data_ptr(), 1, 1, 65536,
+                              ws3.data_ptr(), need3, None) == 1
     torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("N,dtype,B,H", [(65536, "f16", 2, 3), (1048576, "bf16", 1, 2),
+                                         (4194304, "bf16", 1, 1)])
+def test_backward_pieces_multipass(N, dtype, B, H):
+    # on the multi-pass engine a call that asks for both gradients runs du
+    # from dk's column pass of dy: it must give the bits of the separate calls
+    # (one-level passes, two-level passes, the matrix-core pair at 4M)
+    import torch
+    from fft_long_convolution_amd import fftconv as fc
+    w = inputs.Workload("bwdm", 260 + N.bit_length(), B, H, N, dtype, "normal", "decay", "")
+    _say("backward pieces", N, dtype, B, H)
+    conv = fc.FFTConv(N, dtype=dtype)
+    u_h, dy_h, k = inputs.input_rows(w), inputs.dy_rows(w), inputs.kernel_rows(w)
+    u = to_torch(u_h, dtype).view(B, H, N)
+    dy = to_torch(dy_h, dtype).view(B, H, N)
+    kfa = conv.kernel_spectrum(torch.from_numpy(k).cuda(), kind="causal_adjoint")
+    du_all, dk_all = conv.backward(u, dy, kfa)
+    du_only, _ = conv.backward(None, dy, kfa, need_dk=False)
+    _, dk_only = conv.backward(u, dy, None, need_du=False)
+    torch.cuda.synchronize()
+    assert torch.equal(du_all.view(torch.int16), du_only.view(torch.int16))
+    assert torch.equal(dk_all, dk_only)
+    rdu, rdk = oracle_backward(w, u_h, dy_h, k)
+    edu = oracle.rel_l2(oracle.to_f64(from_torch(du_all, dtype).reshape(B * H, N), dtype), rdu)
+    edk = oracle.rel_l2(dk_all.cpu().numpy().astype(np.float64), rdk)
+    _say("  du rel_l2", edu, "dk rel_l2", edk)
+    assert edu < TOL[dtype]
+    assert edk < TOL[dtype]
 
 
 @pytest.mark.parametrize("name", ["hyena_bf16_n1k", "m2bert_f16_n8k",
