@@ -81,6 +81,25 @@ def test_row_kernel_batch_shapes(B, H):
     assert err < TOL["bf16"]
 
 
+@pytest.mark.parametrize("dtype,B,H", [("bf16", 5, 77), ("f16", 64, 7), ("bf16", 3, 512),
+                                         ("f16", 1, 1000), ("bf16", 7, 1)])
+def test_row_pairs_every_row(dtype, B, H):
+    # plain N = 1024 rows go two per wave: odd slices (the last pair holds
+    # one row), pairs that straddle a channel boundary, slices over several
+    # channels; every row held to the bar relative to its conditioning, so
+    # that one wrong row of a pair cannot hide in the whole-tensor norm
+    w = inputs.Workload("rowpairs", 90 + B + H, B, H, 1024, dtype, "normal", "decay",
+                        "paired rows")
+    err, y, ref = parity(w)
+    u64 = oracle.to_f64(inputs.input_rows(w), dtype).reshape(w.rows, w.N)
+    kmax = np.max(np.abs(oracle.kernel_spectrum(inputs.kernel_rows(w).astype(np.float64))), axis=1)
+    scale = np.linalg.norm(u64, axis=1) * kmax[np.arange(w.rows) % H]
+    worst = float(np.max(np.linalg.norm(y - ref, axis=1) / scale))
+    _say("row pairs", dtype, B, H, "rel_l2", err, "worst row (conditioned)", worst)
+    assert err < TOL[dtype]
+    assert worst < TOL[dtype]
+
+
 @pytest.mark.parametrize("N,dtype,B,H", [
     (4096, "f16", 1, 1), (4096, "bf16", 7, 3), (8192, "f16", 1, 1),
     (8192, "f16", 5, 9), (8192, "bf16", 33, 2), (16384, "f16", 3, 1),
