@@ -387,7 +387,11 @@ size_t fftconv_backward_workspace_bytes(fftconv_plan_t plan, size_t B, size_t H)
  * -- at 32K the forward call is the fused wide kernel and dk still runs on
  * the multi-pass engine --
  * batch chunks adding their share to dk), on the LDS-staged kernels for
- * fp32 plans.  B = 0 gives dk = 0.  The input
+ * fp32 plans.  When both gradients are requested on the multi-pass engine,
+ * du's inner and inverse passes start from dk's forward column pass of dy
+ * (one column pass fewer; the same bits as two separate calls), and
+ * k_f_adj must not overlap any part of the workspace.  B = 0 gives dk = 0.
+ * The input
  * gradient of the other kinds is fftconv_forward with the matching adjoint
  * spectrum.  Errors as fftconv_forward. */
 fftconv_status fftconv_backward(fftconv_plan_t plan, const void *u,
