@@ -194,6 +194,45 @@ def test_backward_channel_chunks():
         assert err < TOL[dtype]
 
 
+@pytest.mark.parametrize("B,H,dtype", [(128, 3, "f16"), (257, 1, "bf16")])
+def test_backward_shared_dy_chunks(B, H, dtype):
+    # both gradients at once across workspace chunks (two channels per
+    # chunk at B = 128, 256 batch rows per chunk at B = 257): du runs from dk's
+    # column pass of dy chunk by chunk; its bits must equal the du-only
+    # call's, and the rows on both sides of each chunk boundary are held to
+    # the bar against the oracle
+    import torch
+    from fft_long_convolution_amd.fftconv import FFTConv
+    N = 1048576
+    w = inputs.Workload("sdchunk", 263 + B, B, H, N, dtype, "normal", "decay", "shared dy chunks")
+    conv = FFTConv(N, dtype=dtype)
+    u_h, dy_h, k = inputs.input_rows(w), inputs.dy_rows(w), inputs.kernel_rows(w)
+    _say("shared dy chunks", N, B, H, dtype)
+    u = to_torch(u_h, dtype).view(B, H, N)
+    dy = to_torch(dy_h, dtype).view(B, H, N)
+    del u_h
+    kfa = conv.kernel_spectrum(torch.from_numpy(k).cuda(), kind="causal_adjoint")
+    du_all, dk_all = conv.backward(u, dy, kfa)
+    del dk_all
+    du_only, _ = conv.backward(None, dy, kfa, need_dk=False)
+    torch.cuda.synchronize()
+    assert torch.equal(du_all.view(torch.int16), du_only.view(torch.int16))
+    del du_only
+    # rows r = b * H + h around the boundaries: channels 1 | 2 of batch rows
+    # 0 and B - 1, or batch rows 255 | 256
+    rows = [1, 2, (B - 1) * H + 1, (B - 1) * H + 2] if H == 3 else [0, 255, 256]
+    got = from_torch(du_all.view(B * H, N)[rows], dtype)
+    del du_all
+    hidx = np.array(rows) % H
+    uh, inv = np.unique(hidx, return_inverse=True)
+    ref = oracle.op_fft(oracle.to_f64(dy_h[rows], dtype), k[uh].astype(np.float64),
+                        "causal_adjoint", inv)
+    for i, r in enumerate(rows):
+        err = oracle.rel_l2(oracle.to_f64(got[i:i + 1], dtype), ref[i:i + 1])
+        _say("  du row", r, "rel_l2", err)
+        assert err < TOL[dtype]
+
+
 def test_backward_batch_chunks():
     # more batch rows of one channel than the 1 GB workspace chunk holds (256
     # rows at N = 1M): the multi-pass kernel gradient runs per batch chunk and
