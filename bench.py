@@ -27,6 +27,7 @@ import json
 import math
 import os
 import sys
+import tempfile
 import time
 
 import numpy as np
@@ -102,7 +103,7 @@ def parse():
                     help="profile the selected workload and operator under "
                          "rocprofv3 (kernel trace, HBM byte and instruction "
                          "counters) and write its summary to profiles/")
-    ap.add_argument("--profile-dir", default=os.path.join(ROOT, "gpurun_out", "prof"),
+    ap.add_argument("--profile-dir", default=os.path.join(tempfile.gettempdir(), "fftconv_prof"),
                     help="where rocprofv3 writes its raw output")
     ap.add_argument("--profile-out", default=os.path.join(ROOT, "profiles"),
                     help="where the summary and traffic.json are written")
