@@ -148,6 +148,20 @@ def test_python_binding_marshals_only():
         assert bad not in src
 
 
+def test_product_never_reaches_the_oracle():
+    # no module of the package and no library source imports, includes or
+    # loads the oracle (it is test infrastructure only)
+    import glob
+    import os
+    pkg = os.path.dirname(fc.__file__)
+    files = glob.glob(os.path.join(pkg, "*.py")) + glob.glob(os.path.join(pkg, "csrc", "*"))
+    assert len(files) > 5
+    for f in files:
+        src = open(f).read()
+        for bad in ("import oracle", "from oracle", "liboracle", "oracle.c", "oracle/"):
+            assert bad not in src, (f, bad)
+
+
 # The plans measured fastest on MI355X per length and I/O type (kernel
 # family and factors; the alternatives each length admits were timed on the
 # GPU).  With p = 0 the library picks the candidate of lowest predicted time
