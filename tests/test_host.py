@@ -275,3 +275,14 @@ def test_circular_plan_limits():
     L = fc.lib()
     assert L.fftconv_plan_circular_query(1024, 0, 2, None) == 1
     assert L.fftconv_plan_circular(1024, 0, 2, None) == 1
+
+
+def test_missing_library_fails_loudly(monkeypatch):
+    # without the built HIP library every entry point raises: there is no
+    # fallback path
+    monkeypatch.setattr(fc, "_lib", None)
+    monkeypatch.setattr(fc, "LIB_PATH", "/nonexistent/libfftconv.so")
+    with pytest.raises(RuntimeError, match="not built"):
+        fc.lib()
+    with pytest.raises(RuntimeError):
+        fc.plan_query(1024, 0, "bf16")
